@@ -1,0 +1,140 @@
+"""CPU oracle for one decode step of one hybrid-sparse-attention layer.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may
+import this package. The GPU library never calls it, and it never calls the GPU library.
+
+The arithmetic lives in oracle.c (plain C loops in double precision). This module marshals
+numpy arrays and assembles the key set of one decode step (window rows plus the selected
+compressed entries), which is a matter of choosing rows, not of arithmetic.
+
+Sources (web pages, cited by title and section):
+  "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (SWA of 128 tokens plus C4 top-512 or
+  C128 dense per layer) and Kernel 層一堆狠活 (one attention call over window and compressed
+  entries); "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 2 (compressor stages;
+  threshold top-k) and 创新 3 (every C128 entry is read each step).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+_p = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = os.path.join(HERE, "liboracle.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run oracle/build.py")
+        lib = ctypes.CDLL(path)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_compress.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p, _p, _p, _p, _p]
+        lib.oracle_index_scores.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, _p, ctypes.c_int64, _p, _p]
+        lib.oracle_topk.argtypes = [_p, ctypes.c_int64, ctypes.c_int32, _p]
+        lib.oracle_topk.restype = ctypes.c_int32
+        lib.oracle_attend.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, ctypes.c_int64, _p, ctypes.c_double,
+                                      _p, _p]
+        lib.oracle_round_bf16.argtypes = [_p, ctypes.c_int64, _p]
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def compress(X, Z, B, m: int, cu_tokens) -> np.ndarray:
+    """Group softmax-pool of every complete group (see oracle.c). X, Z: [T, d]; B: [m, d];
+    cu_tokens: [batch+1]. Returns the unrounded double rows [sum_b floor(N_b/m), d]."""
+    X, Z, B = _f32(X), _f32(Z), _f32(B)
+    cu = np.ascontiguousarray(cu_tokens, dtype=np.int64)
+    T, d = X.shape
+    assert Z.shape == (T, d) and B.shape == (m, d) and cu[-1] <= T and 1 <= m <= 1024
+    G = int(sum((cu[b + 1] - cu[b]) // m for b in range(len(cu) - 1)))
+    out = np.zeros((G, d), dtype=np.float64)
+    _load().oracle_compress(len(cu) - 1, d, m, _ptr(X), _ptr(Z), _ptr(B), _ptr(cu), _ptr(out))
+    return out
+
+
+def round_bf16(x) -> np.ndarray:
+    """Double -> nearest bfloat16 (ties to even), returned as fp32 values."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float32)
+    _load().oracle_round_bf16(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def store(x, bf16: bool) -> np.ndarray:
+    """The value a compressed entry holds once stored in the input precision."""
+    return round_bf16(x) if bf16 else np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def index_scores(q, w, K) -> np.ndarray:
+    """s_j = sum_h w_h ReLU(q_h . K_j) in double. q: [nh, dim]; w: [nh]; K: [n, dim]."""
+    q, w, K = _f32(q), _f32(w), _f32(K)
+    nh, dim = q.shape
+    n = K.shape[0]
+    assert w.shape == (nh,) and (n == 0 or K.shape[1] == dim)
+    s = np.zeros(n, dtype=np.float64)
+    _load().oracle_index_scores(nh, dim, _ptr(q), _ptr(w), n, _ptr(K.reshape(max(n, 0), dim)), _ptr(s))
+    return s
+
+
+def topk(scores, k: int) -> np.ndarray:
+    """The k largest scores (ties to the lower index), ascending, padded with -1."""
+    s = _f32(scores)
+    out = np.empty(k, dtype=np.int32)
+    cnt = _load().oracle_topk(_ptr(s), s.size, k, _ptr(out))
+    if cnt < 0:
+        raise ValueError("NaN score: outside the top-k contract")
+    return out
+
+
+def attend(q, keys, scale: float):
+    """One softmax over `keys` (which are also the values) for every query row.
+    q: [H, d]; keys: [n, d]. Returns (out [H, d] double, lse [H] double)."""
+    q, keys = _f32(q), _f32(keys)
+    H, d = q.shape
+    n = keys.shape[0]
+    out = np.zeros((H, d), dtype=np.float64)
+    lse = np.zeros(H, dtype=np.float64)
+    _load().oracle_attend(H, d, _ptr(q), n, _ptr(keys.reshape(max(n, 0), d)), scale, _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def step_keys(window_rows, comp_rows, sel=None) -> np.ndarray:
+    """Key set of one decode step: the window rows (the last min(N_b, W) raw tokens, current
+    token included) followed by the compressed entries comp_rows[j] for every j in `sel` with
+    0 <= j < len(comp_rows) (entries outside that range, -1 padding included, are skipped), or
+    all compressed entries when sel is None (dense C128 layer). A multiset: no deduplication."""
+    window_rows = _f32(window_rows)
+    comp_rows = _f32(comp_rows)
+    G = comp_rows.shape[0]
+    if sel is None:
+        extra = comp_rows
+    else:
+        idx = [int(j) for j in np.asarray(sel).ravel() if 0 <= int(j) < G]
+        extra = comp_rows[idx] if idx else np.zeros((0, window_rows.shape[1]), np.float32)
+    return np.concatenate([window_rows, extra.reshape(-1, window_rows.shape[1])], axis=0)
+
+
+def window_rows(X_seq, window: int) -> np.ndarray:
+    """The last min(N, W) rows of one sequence's token vectors."""
+    n = X_seq.shape[0]
+    return X_seq[max(0, n - window):n]
+
+
+def decode_step(q, X_seq, window: int, comp_rows, sel, scale: float):
+    """Attention of one sequence's decode step (see step_keys and attend)."""
+    return attend(q, step_keys(window_rows(X_seq, window), comp_rows, sel), scale)

@@ -1,0 +1,401 @@
+"""Pins for the CPU oracle, against facts that do not come from the oracle itself:
+closed forms, invariants, special cases that reduce to a library routine, brute force on tiny
+inputs, and the structural counts the pages print. Each pin is chosen so that a plausible
+mistake (a dropped term, a wrong sign or index, a transposed operand) fails it."""
+import itertools
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit, logsumexp, softmax
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_structure.txt")
+
+
+def _golden():
+    vals = {}
+    with open(GOLDEN, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split()
+                vals[k] = float(v)
+    return vals
+
+
+# ------------------------------------------------------------------ compressor
+def _groups(X, m):
+    n = (X.shape[0] // m) * m
+    return X[:n].astype(np.float64).reshape(-1, m, X.shape[1])
+
+
+@pytest.mark.parametrize("m", [2, 4, 5, 128])
+def test_compress_constant_gate_and_flat_bias_is_mean_pooling(rng, m):
+    X = rng.standard_normal((m * 6 + 3, 24)).astype(np.float32)
+    Z = np.full_like(X, 0.7)
+    B = np.full((m, 24), -1.25, np.float32)   # slot-constant bias: no preference between slots
+    C = oracle.compress(X, Z, B, m, [0, X.shape[0]])
+    np.testing.assert_allclose(C, _groups(X, m).mean(axis=1), rtol=0, atol=1e-12)
+
+
+def test_compress_m1_is_identity(rng):
+    X = rng.standard_normal((37, 16)).astype(np.float32)
+    Z = rng.standard_normal((37, 16)).astype(np.float32) * 3
+    B = rng.standard_normal((1, 16)).astype(np.float32)
+    C = oracle.compress(X, Z, B, 1, [0, 37])
+    assert np.array_equal(C.astype(np.float32), X)
+
+
+@pytest.mark.parametrize("m", [3, 4, 128])
+def test_compress_weights_sum_to_one(rng, m):
+    # With every token vector equal to 1, the output is the sum of the weights.
+    T = m * 5
+    X = np.ones((T, 8), np.float32)
+    Z = (rng.standard_normal((T, 8)) * 5).astype(np.float32)
+    B = rng.standard_normal((m, 8)).astype(np.float32)
+    C = oracle.compress(X, Z, B, m, [0, T])
+    assert np.abs(C - 1.0).max() <= 1e-12
+
+
+def test_compress_shift_invariance(rng):
+    m, T, d = 4, 40, 12
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    # Gates on a 1/64 grid, so adding an integer shift is exact in fp32.
+    Z = (np.round(rng.standard_normal((T, d)) * 64) / 64).astype(np.float32)
+    B = (rng.standard_normal((m, d)) * 0.1).astype(np.float32)
+    shift = np.repeat(rng.integers(-8, 8, (T // m, d)), m, axis=0).astype(np.float32)
+    C1 = oracle.compress(X, Z, B, m, [0, T])
+    C2 = oracle.compress(X, Z + shift, B, m, [0, T])
+    np.testing.assert_allclose(C1, C2, rtol=0, atol=1e-12)
+
+
+def test_compress_dominant_slot_selects_that_token(rng):
+    m, T, d = 4, 32, 10
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    Z = rng.standard_normal((T, d)).astype(np.float32)
+    B = np.zeros((m, d), np.float32)
+    slot = rng.integers(0, m, (T // m, d))
+    for g in range(T // m):
+        for c in range(d):
+            Z[g * m + slot[g, c], c] += 200.0
+    C = oracle.compress(X, Z, B, m, [0, T])
+    want = np.array([[X[g * m + slot[g, c], c] for c in range(d)] for g in range(T // m)])
+    np.testing.assert_allclose(C, want, rtol=0, atol=1e-12)
+
+
+def test_compress_m2_logistic_closed_form(rng):
+    # For two slots the softmax weight of slot 0 is the logistic function of a0 - a1.
+    T, d = 20, 9
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    Z = (rng.standard_normal((T, d)) * 2).astype(np.float32)
+    B = (rng.standard_normal((2, d)) * 0.5).astype(np.float32)
+    C = oracle.compress(X, Z, B, 2, [0, T])
+    a0 = Z[0::2].astype(np.float64) + B[0]
+    a1 = Z[1::2].astype(np.float64) + B[1]
+    want = expit(a0 - a1) * X[0::2] + expit(a1 - a0) * X[1::2]
+    np.testing.assert_allclose(C, want, rtol=1e-12, atol=1e-14)
+
+
+def test_compress_bias_is_per_slot_per_channel(rng):
+    # Constant gates leave only the bias: weights are softmax over slots of B[:, c].
+    m, d = 3, 7   # m != d, so a transposed bias would not even line up
+    T = m * 4
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    Z = np.zeros((T, d), np.float32)
+    B = rng.standard_normal((m, d)).astype(np.float32)
+    C = oracle.compress(X, Z, B, m, [0, T])
+    W = softmax(B.astype(np.float64), axis=0)          # [m, d]
+    want = np.einsum("gic,ic->gc", _groups(X, m), W)
+    np.testing.assert_allclose(C, want, rtol=1e-12, atol=1e-14)
+
+
+def test_compress_slot_permutation_invariance(rng):
+    m, T, d = 4, 24, 6
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    Z = rng.standard_normal((T, d)).astype(np.float32)
+    B = rng.standard_normal((m, d)).astype(np.float32)
+    perm = np.array([2, 0, 3, 1])
+    rows = (np.arange(T // m)[:, None] * m + perm[None, :]).ravel()
+    C1 = oracle.compress(X, Z, B, m, [0, T])
+    C2 = oracle.compress(X[rows], Z[rows], B[perm], m, [0, T])
+    np.testing.assert_allclose(C1, C2, rtol=1e-13, atol=1e-14)
+
+
+def test_compress_varlen_packing_and_tails(rng):
+    m, d = 4, 5
+    lens = [10, 7, 3, 12, 0, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = cu[-1]
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    Z = rng.standard_normal((T, d)).astype(np.float32)
+    B = rng.standard_normal((m, d)).astype(np.float32)
+    C = oracle.compress(X, Z, B, m, cu)
+    assert C.shape[0] == sum(n // m for n in lens) == 7
+    parts = [oracle.compress(X[cu[b]:cu[b + 1]], Z[cu[b]:cu[b + 1]], B, m, [0, lens[b]])
+             for b in range(len(lens))]
+    np.testing.assert_array_equal(C, np.concatenate(parts, axis=0))
+    # Tail tokens (the last N_b mod m of each sequence) do not enter any group.
+    X2, Z2 = X.copy(), Z.copy()
+    for b, n in enumerate(lens):
+        tail = range(cu[b] + (n // m) * m, cu[b + 1])
+        X2[list(tail)] = 99.0
+        Z2[list(tail)] = 50.0
+    np.testing.assert_array_equal(C, oracle.compress(X2, Z2, B, m, cu))
+
+
+def test_compress_group_count_matches_pages():
+    g = _golden()
+    n, m = int(g["context_tokens"]), int(g["c4_ratio"])
+    X = np.zeros((n, 1), np.float32)
+    C = oracle.compress(X, X, np.zeros((m, 1), np.float32), m, [0, n])
+    assert C.shape[0] == int(g["c4_candidates"])
+    C128 = oracle.compress(X, X, np.zeros((int(g["c128_ratio"]), 1), np.float32), int(g["c128_ratio"]), [0, n])
+    assert C128.shape[0] == n // int(g["c128_ratio"]) == 8192
+
+
+# ------------------------------------------------------------------ indexer scores
+def test_index_scores_one_hot_weight_is_relu_dot(rng):
+    q = rng.standard_normal((3, 16)).astype(np.float32)
+    K = rng.standard_normal((50, 16)).astype(np.float32)
+    for h in range(3):
+        w = np.zeros(3, np.float32)
+        w[h] = 1.0
+        s = oracle.index_scores(q, w, K)
+        np.testing.assert_allclose(s, np.maximum(K.astype(np.float64) @ q[h].astype(np.float64), 0.0),
+                                   rtol=1e-13, atol=1e-12)
+
+
+def test_index_scores_linear_in_weights(rng):
+    q = rng.standard_normal((4, 8)).astype(np.float32)
+    K = rng.standard_normal((30, 8)).astype(np.float32)
+    w1, w2 = rng.random(4).astype(np.float32), rng.random(4).astype(np.float32)
+    s12 = oracle.index_scores(q, (w1 + w2).astype(np.float32), K)
+    s1, s2 = oracle.index_scores(q, w1, K), oracle.index_scores(q, w2, K)
+    # w1 + w2 is rounded to fp32 before the call; compare against that same sum.
+    np.testing.assert_allclose(s12, s1 + s2, rtol=1e-6, atol=1e-9)
+
+
+def test_index_scores_odd_part_identity(rng):
+    # ReLU(x) - ReLU(-x) = x, so s(q) - s(-q) = sum_h w_h (q_h . k_j): catches a dropped ReLU,
+    # a sign error or transposed keys.
+    q = rng.standard_normal((4, 12)).astype(np.float32)
+    w = rng.random(4).astype(np.float32)
+    K = rng.standard_normal((40, 12)).astype(np.float32)
+    lhs = oracle.index_scores(q, w, K) - oracle.index_scores(-q, w, K)
+    rhs = (K.astype(np.float64) @ q.astype(np.float64).T) @ w.astype(np.float64)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_index_scores_negative_dots_give_zero(rng):
+    q = rng.standard_normal((1, 10)).astype(np.float32)
+    K = -np.abs(rng.standard_normal((20, 1))).astype(np.float32) * q
+    assert np.all(oracle.index_scores(q, np.ones(1, np.float32), K) == 0.0)
+
+
+def test_index_scores_positive_homogeneity(rng):
+    q = rng.standard_normal((2, 6)).astype(np.float32)
+    w = rng.random(2).astype(np.float32)
+    K = rng.standard_normal((25, 6)).astype(np.float32)
+    np.testing.assert_allclose(oracle.index_scores(4.0 * q, w, K), 4.0 * oracle.index_scores(q, w, K),
+                               rtol=1e-14, atol=0)
+
+
+# ------------------------------------------------------------------ top-k
+def _is_topk_set(s, S):
+    """Brute-force characterisation: every chosen element beats every unchosen one, by value
+    or, on equal values, by lower index."""
+    out = set(range(len(s))) - set(S)
+    return all(s[i] > s[j] or (s[i] == s[j] and i < j) for i in S for j in out)
+
+
+def test_topk_exhaustive_tiny(rng):
+    values = np.array([-1.0, -0.0, 0.0, 2.0, 3.5], np.float32)
+    for n in range(1, 7):
+        for _ in range(40):
+            s = rng.choice(values, n).astype(np.float32)
+            for k in range(1, n + 3):
+                got = oracle.topk(s, k)
+                c = min(k, n)
+                cands = [S for S in itertools.combinations(range(n), c) if _is_topk_set(s, S)]
+                assert len(cands) == 1, (s, k)      # the set is unique
+                assert list(got[:c]) == list(cands[0]) and all(got[c:] == -1)
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (100, 7), (4096, 512), (3000, 2048), (777, 777)])
+def test_topk_matches_lexsort(rng, n, k):
+    s = rng.integers(-20, 20, n).astype(np.float32) * 0.5    # many ties
+    order = np.lexsort((np.arange(n), -s.astype(np.float64)))
+    want = np.sort(order[:min(k, n)])
+    got = oracle.topk(s, k)
+    assert np.array_equal(got[:len(want)], want) and np.all(got[len(want):] == -1)
+
+
+def test_topk_k1_is_first_argmax(rng):
+    s = rng.integers(0, 5, 300).astype(np.float32)
+    assert oracle.topk(s, 1)[0] == np.argmax(s)
+
+
+def test_topk_all_equal_and_k_ge_n():
+    assert list(oracle.topk(np.full(10, 2.5, np.float32), 4)) == [0, 1, 2, 3]
+    assert list(oracle.topk(np.array([3, 1, 2], np.float32), 5)) == [0, 1, 2, -1, -1]
+    assert list(oracle.topk(np.zeros(0, np.float32), 3)) == [-1, -1, -1]
+
+
+def test_topk_signed_zero_ties():
+    assert list(oracle.topk(np.array([-0.0, 0.0, -0.0, -1.0], np.float32), 2)) == [0, 1]
+
+
+def test_topk_invariant_under_increasing_map(rng):
+    s = rng.standard_normal(2000).astype(np.float32)
+    t = np.exp(s.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(oracle.topk(s, 100), oracle.topk(t, 100))
+
+
+def test_topk_permutation_equivariance(rng):
+    s = rng.permutation(5000).astype(np.float32)
+    p = rng.permutation(5000)
+    a = oracle.topk(s, 300)
+    b = oracle.topk(s[p], 300)
+    assert np.array_equal(np.sort(p[b]), a)
+
+
+def test_topk_rejects_nan():
+    with pytest.raises(ValueError):
+        oracle.topk(np.array([1.0, np.nan], np.float32), 1)
+
+
+def test_topk_fraction_matches_pages():
+    g = _golden()
+    n, k = int(g["c4_candidates"]), int(g["c4_topk"])
+    sel = oracle.topk(np.arange(n, dtype=np.float32), k)
+    assert np.array_equal(sel, np.arange(n - k, n))
+    assert round(100.0 * k / n, 1) == g["c4_touched_percent"]
+
+
+# ------------------------------------------------------------------ attention
+def test_attend_single_key(rng):
+    q = rng.standard_normal((3, 8)).astype(np.float32)
+    k = rng.standard_normal((1, 8)).astype(np.float32)
+    o, lse = oracle.attend(q, k, 0.3)
+    np.testing.assert_allclose(o, np.repeat(k.astype(np.float64), 3, 0), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.3 * (q.astype(np.float64) @ k[0].astype(np.float64)), rtol=1e-13)
+
+
+def test_attend_identical_keys(rng):
+    q = rng.standard_normal((2, 6)).astype(np.float32)
+    k = rng.standard_normal((1, 6)).astype(np.float32)
+    o, lse = oracle.attend(q, np.repeat(k, 9, 0), 0.5)
+    np.testing.assert_allclose(o, np.repeat(k.astype(np.float64), 2, 0), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.5 * (q.astype(np.float64) @ k[0]) + np.log(9.0), rtol=1e-13)
+
+
+def test_attend_zero_query_is_mean(rng):
+    keys = rng.standard_normal((13, 5)).astype(np.float32)
+    o, lse = oracle.attend(np.zeros((2, 5), np.float32), keys, 1.0)
+    np.testing.assert_allclose(o, np.repeat(keys.astype(np.float64).mean(0, keepdims=True), 2, 0),
+                               rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, np.log(13.0), rtol=1e-14)
+
+
+def test_attend_two_keys_logistic(rng):
+    q = rng.standard_normal((4, 7)).astype(np.float32)
+    keys = rng.standard_normal((2, 7)).astype(np.float32)
+    sc = 1 / np.sqrt(7)
+    o, lse = oracle.attend(q, keys, sc)
+    l = sc * (q.astype(np.float64) @ keys.astype(np.float64).T)
+    p0 = expit(l[:, 0] - l[:, 1])
+    want = p0[:, None] * keys[0] + (1 - p0)[:, None] * keys[1]
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, logsumexp(l, axis=1), rtol=1e-13)
+
+
+def test_attend_lse_merge_identity(rng):
+    # Attention over A u B equals the LSE-weighted merge of attention over A and over B.
+    q = rng.standard_normal((5, 16)).astype(np.float32)
+    keys = rng.standard_normal((40, 16)).astype(np.float32)
+    o, lse = oracle.attend(q, keys, 0.25)
+    oa, la = oracle.attend(q, keys[:17], 0.25)
+    ob, lb = oracle.attend(q, keys[17:], 0.25)
+    L = np.logaddexp(la, lb)
+    np.testing.assert_allclose(lse, L, rtol=1e-13)
+    np.testing.assert_allclose(o, np.exp(la - L)[:, None] * oa + np.exp(lb - L)[:, None] * ob,
+                               rtol=1e-11, atol=1e-13)
+
+
+def test_attend_key_order_invariance(rng):
+    q = rng.standard_normal((3, 8)).astype(np.float32)
+    keys = rng.standard_normal((30, 8)).astype(np.float32)
+    o1, l1 = oracle.attend(q, keys, 0.35)
+    o2, l2 = oracle.attend(q, keys[rng.permutation(30)], 0.35)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13)
+
+
+def test_attend_large_logits_pick_argmax(rng):
+    q = rng.standard_normal((2, 8)).astype(np.float32) * 1000
+    keys = rng.standard_normal((6, 8)).astype(np.float32)
+    o, lse = oracle.attend(q, keys, 1.0)
+    l = q.astype(np.float64) @ keys.astype(np.float64).T
+    np.testing.assert_allclose(o, keys[np.argmax(l, 1)].astype(np.float64), rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_attend_no_keys():
+    o, lse = oracle.attend(np.ones((2, 4), np.float32), np.zeros((0, 4), np.float32), 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# ------------------------------------------------------------------ the decode step's key set
+def test_step_full_selection_equals_dense(rng):
+    # k >= number of candidates: the sparse step over all indices equals the dense step.
+    X = rng.standard_normal((300, 8)).astype(np.float32)
+    comp = rng.standard_normal((75, 8)).astype(np.float32)
+    q = rng.standard_normal((4, 8)).astype(np.float32)
+    sel = oracle.topk(rng.standard_normal(75).astype(np.float32), 100)   # all 75, padded with -1
+    o1, l1 = oracle.decode_step(q, X, 128, comp, sel, 0.3)
+    o2, l2 = oracle.decode_step(q, X, 128, comp, None, 0.3)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13)
+
+
+def test_step_window_is_last_w_tokens(rng):
+    X = rng.standard_normal((200, 4)).astype(np.float32)
+    keys = oracle.step_keys(oracle.window_rows(X, 128), np.zeros((0, 4), np.float32), None)
+    assert np.array_equal(keys, X[72:])
+    short = X[:50]
+    assert np.array_equal(oracle.window_rows(short, 128), short)     # N < W: every token
+
+
+def test_step_skips_invalid_indices_and_keeps_duplicates(rng):
+    win = rng.standard_normal((3, 4)).astype(np.float32)
+    comp = rng.standard_normal((5, 4)).astype(np.float32)
+    keys = oracle.step_keys(win, comp, np.array([4, -1, 7, 1, 1, 5]))
+    assert np.array_equal(keys, np.concatenate([win, comp[[4, 1, 1]]]))
+    assert oracle.step_keys(win, np.zeros((0, 4), np.float32), np.array([-1, -1])).shape == (3, 4)
+
+
+def test_step_c128_reads_every_entry_at_1m():
+    g = _golden()
+    n, m, W = int(g["context_tokens"]), int(g["c128_ratio"]), int(g["window_tokens"])
+    comp = np.zeros((n // m, 2), np.float32)
+    keys = oracle.step_keys(np.zeros((W, 2), np.float32), comp, None)
+    assert keys.shape[0] == W + 8192
+
+
+# ------------------------------------------------------------------ storage rounding
+def test_round_bf16_matches_integer_rne_of_fp32_values(rng):
+    # For doubles that are exactly fp32 values, rounding to bf16 equals the integer RNE on the
+    # fp32 bit pattern (an independent construction of the same rounding).
+    x = (rng.standard_normal(20000) * 10).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16).astype(np.uint32).view(np.float32)
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), r)
+
+
+def test_round_bf16_ties_and_exact():
+    one = 1.0
+    ulp = 2.0 ** -7
+    got = oracle.round_bf16(np.array([one, one + ulp / 2, one + 1.5 * ulp, one + ulp / 2 + 1e-12, 3.0]))
+    assert list(got) == [1.0, 1.0, 1.0 + 2 * ulp, 1.0 + ulp, 3.0]
