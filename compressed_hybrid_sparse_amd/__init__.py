@@ -1,0 +1,211 @@
+"""Python binding of libchs.so: one decode step of one hybrid-sparse-attention layer on MI355X.
+
+Argument marshalling only. Every step of the path runs in the library's HIP kernels; torch
+supplies device memory (outputs and workspaces are torch tensors) and the current stream.
+There is no fallback: if libchs.so is missing or a call fails, an exception is raised.
+
+The functions mirror the C ABI in include/chs.h (chs_compress, chs_index_topk,
+chs_decode_attn); see that header for the definitions and the pages they follow.
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  (load torch's HIP runtime first; libchs binds to the same libamdhip64)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libchs.so")
+
+CHS_F32, CHS_BF16 = 0, 1
+_STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE",
+           4: "CHS_ERR_WORKSPACE", 5: "CHS_ERR_UNSUPPORTED", 6: "CHS_ERR_LAUNCH"}
+EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
+           "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
+           "chs_decode_attn")
+
+_lib = None
+_i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+
+class ChsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {_STATUS.get(status, status)}")
+
+
+def lib():
+    """The loaded libchs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with compressed_hybrid_sparse_amd/build.py "
+                              "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        L.chs_version.restype = _i32
+        L.chs_status_string.restype = ctypes.c_char_p
+        L.chs_status_string.argtypes = [ctypes.c_int]
+        L.chs_workspace_clear.argtypes = [_p, _sz, _p]
+        L.chs_compress.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p]
+        L.chs_index_topk_workspace_size.restype = _sz
+        L.chs_index_topk_workspace_size.argtypes = [_i32, _i64, _i32]
+        L.chs_index_topk.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p,
+                                     _sz, _p]
+        L.chs_decode_attn_workspace_size.restype = _sz
+        L.chs_decode_attn_workspace_size.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i64]
+        L.chs_decode_attn.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _p, _p,
+                                      _i64, _p, _p, _p, _sz, _p]
+        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return CHS_BF16
+    if t.dtype == torch.float32:
+        return CHS_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise ChsError(status, what)
+
+
+def _need(t, name, dtype=None, dim=None):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+
+
+def _host_max_diff(cu):
+    """max_b (cu[b+1] - cu[b]) of an int64 prefix array (a host round trip if cu is on the GPU)."""
+    d = cu[1:] - cu[:-1]
+    return int(d.max().item()) if d.numel() else 0
+
+
+def workspace_clear(ws):
+    _check(lib().chs_workspace_clear(_ptr(ws), ws.numel() * ws.element_size(), _stream()), "chs_workspace_clear")
+
+
+def version() -> int:
+    return int(lib().chs_version())
+
+
+# ---------------------------------------------------------------- chs_compress
+def compress(x, gate, bias, m: int, cu_tokens, cu_groups=None, max_groups=None, out=None):
+    """Group softmax-pool of every complete group of m tokens (chs_compress).
+    x, gate: [T, d] (bf16 or fp32); bias: [m, d] fp32; cu_tokens: [B+1] int64 (CUDA).
+    cu_groups: [B+1] int64 output offsets (default: packed, prefix sums of floor(N_b/m)).
+    Returns out [cu_groups[-1], d] in x's dtype."""
+    _need(x, "x", dim=2)
+    _need(gate, "gate", x.dtype, 2)
+    _need(bias, "bias", torch.float32, 2)
+    _need(cu_tokens, "cu_tokens", torch.int64, 1)
+    if cu_groups is None:
+        lens = cu_tokens[1:] - cu_tokens[:-1]
+        cu_groups = torch.zeros_like(cu_tokens)
+        cu_groups[1:] = torch.cumsum(torch.div(lens, m, rounding_mode="floor"), 0)
+    _need(cu_groups, "cu_groups", torch.int64, 1)
+    if max_groups is None:
+        max_groups = _host_max_diff(cu_groups)
+    if out is None:
+        out = torch.empty(int(cu_groups[-1].item()), x.shape[1], dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, 2)
+    _check(lib().chs_compress(_dtype_code(x), cu_tokens.numel() - 1, x.shape[1], m, _ptr(x), _ptr(gate),
+                              _ptr(bias), _ptr(cu_tokens), _ptr(cu_groups), int(max_groups), _ptr(out),
+                              _stream()), "chs_compress")
+    return out
+
+
+# ---------------------------------------------------------------- chs_index_topk
+def index_topk_workspace(batch: int, max_cand: int, k: int, device="cuda"):
+    n = lib().chs_index_topk_workspace_size(batch, max_cand, k)
+    return torch.zeros(max(n, 4), dtype=torch.uint8, device=device)
+
+
+def index_topk(q_idx, w, k_idx, cu_cand, k: int, max_cand=None, scores=None, workspace=None, out=None):
+    """Indexer scores and exact top-k (chs_index_topk).
+    q_idx: [B, Hi, dim]; w: [B, Hi] fp32; k_idx: [G, dim]; cu_cand: [B+1] int64.
+    If q_idx is None, `scores` ([G] fp32) is the input and w, k_idx are ignored.
+    Returns (topk [B, k] int32, scores or None)."""
+    _need(cu_cand, "cu_cand", torch.int64, 1)
+    batch = cu_cand.numel() - 1
+    if max_cand is None:
+        max_cand = _host_max_diff(cu_cand)
+    if workspace is None:
+        workspace = index_topk_workspace(batch, max_cand, k, cu_cand.device)
+    if out is None:
+        out = torch.empty(batch, k, dtype=torch.int32, device=cu_cand.device)
+    _need(out, "topk", torch.int32, 2)
+    if q_idx is not None:
+        _need(q_idx, "q_idx", dim=3)
+        _need(w, "w", torch.float32, 2)
+        _need(k_idx, "k_idx", q_idx.dtype, 2)
+        dt, nh, dim = _dtype_code(q_idx), q_idx.shape[1], q_idx.shape[2]
+        if scores is not None:
+            _need(scores, "scores", torch.float32, 1)
+    else:
+        _need(scores, "scores", torch.float32, 1)
+        dt, nh, dim = CHS_F32, 0, 0
+    _check(lib().chs_index_topk(dt, batch, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(cu_cand),
+                                int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
+                                workspace.numel(), _stream()), "chs_index_topk")
+    return out, scores
+
+
+def topk_from_scores(scores, cu_cand, k: int, max_cand=None, workspace=None, out=None):
+    """Standalone exact top-k over given fp32 scores (chs_index_topk with q_idx = NULL)."""
+    return index_topk(None, None, None, cu_cand, k, max_cand, scores, workspace, out)[0]
+
+
+# ---------------------------------------------------------------- chs_decode_attn
+def decode_attn_workspace(dtype, batch, n_heads, d, window, k, max_comp, device="cuda"):
+    code = CHS_BF16 if dtype == torch.bfloat16 else CHS_F32
+    n = lib().chs_decode_attn_workspace_size(code, batch, n_heads, d, window, k, max_comp)
+    return torch.zeros(max(n, 4), dtype=torch.uint8, device=device)
+
+
+def decode_attn(q, swa_kv, swa_len, comp_kv, cu_comp, topk=None, scale=None, max_comp=None,
+                workspace=None, out=None, lse=None):
+    """One softmax over the window rows and the selected (topk) or all (topk=None) compressed
+    entries, keys doubling as values (chs_decode_attn).
+    q: [B, H, d]; swa_kv: [B, W, d]; swa_len: [B] int32; comp_kv: [G, d]; cu_comp: [B+1] int64;
+    topk: [B, k] int32 or None. Returns (out [B, H, d] fp32, lse [B, H] fp32)."""
+    _need(q, "q", dim=3)
+    _need(swa_kv, "swa_kv", q.dtype, 3)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_kv, "comp_kv", q.dtype, 2)
+    _need(cu_comp, "cu_comp", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_kv.shape[1]
+    k = 0
+    if topk is not None:
+        _need(topk, "topk", torch.int32, 2)
+        k = topk.shape[1]
+    if max_comp is None:
+        max_comp = _host_max_diff(cu_comp)
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = decode_attn_workspace(q.dtype, B, H, d, W, k, max_comp, q.device)
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _check(lib().chs_decode_attn(_dtype_code(q), B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_kv),
+                                 _ptr(swa_len), _ptr(comp_kv), _ptr(cu_comp), _ptr(topk), int(max_comp),
+                                 _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()),
+           "chs_decode_attn")
+    return out, lse

@@ -1,0 +1,433 @@
+// chs_decode_attn: one softmax over the sliding window plus the selected (C4) or all (C128)
+// compressed entries, keys doubling as values.
+//
+// Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", Kernel 層一堆狠活 (FlashMLA's new interface
+// runs the window attention and the extra C4/C128 attention in one call) and V4 到底改了啥
+// (window of 128; C4 top-512; C128 dense). "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速",
+// 3.2 (MLA decode is memory-bound; FlashMLA wants the head count padded to 64 or 128) and
+// 创新 3 (C128 reads every entry each step).
+//
+// gfx950 design (bf16). All query heads of a sequence share one latent KV row, so the heads
+// form the M dimension of the MFMA contraction and every KV row is fetched from HBM once per
+// step for all heads. The key list (window rows, then the selected or all compressed rows) is
+// split across workgroups (split-KV); a workgroup of 4 waves covers 64 heads (wave w: heads
+// 16w..16w+15, unused heads masked in-kernel, so callers never pad) and walks its slice of the
+// key list 32 rows at a time:
+//   1. the 32 rows are gathered from HBM with coalesced 16-byte loads (one wave per 1 KiB row
+//      at d = 512) and written to LDS twice: row-major (operand of Q.K^T, where d is the
+//      reduction) and transposed (operand of P.V, where the keys are the reduction);
+//   2. S = Q K^T with v_mfma_f32_16x16x32_bf16, Q held in registers for the whole walk;
+//   3. online softmax in fp32 (base-2 logits, running max and sum per head, DPP row reductions);
+//   4. P (rounded to bf16, and the running sum is taken over the rounded values so the weights
+//      sum to one exactly) goes through LDS into the A-operand layout, and O += P V with MFMA.
+// Each workgroup writes its unnormalised O with its running max and sum; a combine kernel
+// merges the splits with the log-sum-exp identity and writes out and lse. fp32 storage takes a
+// plain VALU kernel with the same split and merge (it has to meet an fp32 tolerance that bf16
+// MFMA operands cannot).
+#include "common.h"
+
+namespace chs {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kKeysPerChunk = 32;
+
+struct AttnArgs {
+  const void* q;            // [batch][H][D]
+  const void* swa;          // [batch][W][D]
+  const int32_t* swa_len;   // [batch]
+  const void* comp;         // [*][D]
+  const int64_t* cu_comp;   // [batch+1]
+  const int32_t* topk;      // [batch][k] or NULL
+  int32_t H, D, W, k;
+  int64_t max_comp;
+  float scale_log2;         // scale * log2(e)
+  int32_t n_splits, kps;    // key slots per split
+  float* part_o;            // [batch][n_splits][H][D]
+  float* part_ml;           // [batch][n_splits][H][2]: running max (base 2), running sum
+};
+
+// Key slots of sequence b: [0, swa_len) window rows, then k (C4) or G_b (C128) entries.
+struct SlotMap {
+  int64_t comp0, G;
+  int32_t nswa, nextra;
+  __device__ SlotMap(const AttnArgs& a, int b) {
+    int32_t L = a.swa_len[b];
+    nswa = L < 0 ? 0 : (L > a.W ? a.W : L);
+    comp0 = a.cu_comp[b];
+    G = a.cu_comp[b + 1] - comp0;
+    if (G < 0) G = 0;
+    if (a.topk) {
+      nextra = a.k;
+    } else {
+      int64_t g = G < a.max_comp ? G : a.max_comp;
+      nextra = (int32_t)g;
+    }
+  }
+  __device__ int32_t nslots() const { return nswa + nextra; }
+  // Element offset of slot s's row within its buffer; -1 if the slot holds no key.
+  // *is_swa tells which buffer.
+  __device__ int64_t row(const AttnArgs& a, int b, int32_t s, bool* is_swa) const {
+    if (s < nswa) { *is_swa = true; return ((int64_t)b * a.W + s) * a.D; }
+    *is_swa = false;
+    int64_t j = s - nswa;
+    if (a.topk) {
+      j = a.topk[(int64_t)b * a.k + j];
+      if (j < 0 || j >= G) return -1;
+    }
+    return (comp0 + j) * a.D;
+  }
+};
+
+// Max / sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane gets the result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// ---------------------------------------------------------------- bf16 MFMA split kernel
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int KC = kKeysPerChunk;
+  constexpr int KN_PITCH = D + 8;          // bf16 elements per row-major LDS row
+  constexpr int KT_PITCH = KC + 8;         // bf16 elements per transposed LDS row
+  constexpr int P_PITCH = KC + 8;
+  constexpr int VPR = D / 8;               // 16-byte vectors per row
+  constexpr int LOADS = KC * VPR / kThreads;
+  static_assert(KC * VPR % kThreads == 0, "tile");
+  __shared__ __attribute__((aligned(16))) uint16_t kn[KC * KN_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t kt[D * KT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t pb[4][16 * P_PITCH];
+  __shared__ int64_t rowoff[KC];
+  __shared__ int32_t rowswa[KC];
+
+  const int b = blockIdx.y, split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int h_base = blockIdx.z * 64 + wave * 16;
+  const SlotMap sm(a, b);
+  const int32_t s_begin = split * a.kps;
+  const int32_t s_end = min(s_begin + a.kps, sm.nslots());
+
+  // Q fragment (A operand): row c of this wave's 16 heads, d = 32t + 8g .. +8.
+  bf16x8 qf[D / 32];
+  {
+    const int h = h_base + c;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + h) * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      u32x4 v = (h < a.H) ? *reinterpret_cast<const u32x4*>(qp + 32 * t + 8 * g) : u32x4{0, 0, 0, 0};
+      qf[t] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) o[j] = f32x4{0, 0, 0, 0};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
+
+  const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
+  const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
+
+  for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) {
+    __syncthreads();   // previous chunk's LDS reads are done
+    if (tid < KC) {
+      const int32_t s = s0 + tid;
+      bool is_swa = false;
+      int64_t off = (s < s_end) ? sm.row(a, b, s, &is_swa) : -1;
+      rowoff[tid] = off;
+      rowswa[tid] = is_swa ? 1 : 0;
+    }
+    __syncthreads();
+    // 1. gather 32 rows, store row-major and transposed.
+    u32x4 v[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = tid + i * kThreads;
+      const int r = e / VPR, cv = e % VPR;
+      const int64_t off = rowoff[r];
+      const uint16_t* src = rowswa[r] ? swa : comp;
+      v[i] = off >= 0 ? *reinterpret_cast<const u32x4*>(src + off + 8 * cv) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = tid + i * kThreads;
+      const int r = e / VPR, cv = e % VPR;
+      *reinterpret_cast<u32x4*>(&kn[r * KN_PITCH + 8 * cv]) = v[i];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        kt[(8 * cv + 2 * x) * KT_PITCH + r] = (uint16_t)(v[i][x] & 0xFFFF);
+        kt[(8 * cv + 2 * x + 1) * KT_PITCH + r] = (uint16_t)(v[i][x] >> 16);
+      }
+    }
+    __syncthreads();
+    // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      sacc[n] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        u32x4 kb = *reinterpret_cast<const u32x4*>(&kn[(16 * n + c) * KN_PITCH + 32 * t + 8 * g]);
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t], __builtin_bit_cast(bf16x8, kb), sacc[n], 0, 0, 0);
+      }
+    }
+    // 3. online softmax (base-2), per head row 4g + r.
+    const bool valid0 = rowoff[c] >= 0, valid1 = rowoff[16 + c] >= 0;
+    float p[2][4], alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = valid0 ? sacc[0][r] * a.scale_log2 : -INFINITY;
+      const float x1 = valid1 ? sacc[1][r] * a.scale_log2 : -INFINITY;
+      const float cm = row16_max(fmaxf(x0, x1));
+      const float mn = fmaxf(m_run[r], cm);
+      const bool none = (mn == -INFINITY);
+      alpha[r] = none ? 1.f : fast_exp2(m_run[r] - mn);
+      // Round P to bf16 here so the running sum matches what the MFMA multiplies.
+      p[0][r] = none ? 0.f : bf16_to_f32((uint16_t)f32_to_bf16(fast_exp2(x0 - mn)));
+      p[1][r] = none ? 0.f : bf16_to_f32((uint16_t)f32_to_bf16(fast_exp2(x1 - mn)));
+      l_run[r] = l_run[r] * alpha[r] + row16_sum(p[0][r] + p[1][r]);
+      m_run[r] = mn;
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[j][r] *= alpha[r];
+    }
+    // 4. P to LDS as [head][key], read back as the A operand (row c, keys 8g .. 8g+7).
+    uint16_t* pw = pb[wave];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        pw[(4 * g + r) * P_PITCH + 16 * n + c] = (uint16_t)(__float_as_uint(p[n][r]) >> 16);
+    __syncthreads();
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pw[c * P_PITCH + 8 * g]));
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      u32x4 vb = *reinterpret_cast<const u32x4*>(&kt[(16 * j + c) * KT_PITCH + 8 * g]);
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8, vb), o[j], 0, 0, 0);
+    }
+  }
+  // Partial result of this split: unnormalised O, running max (base 2) and sum.
+  const int64_t pbase = ((int64_t)b * a.n_splits + split) * a.H;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = h_base + 4 * g + r;
+    if (h < a.H) {
+      float* po = a.part_o + (pbase + h) * D;
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) po[16 * j + c] = o[j][r];
+      if (c == 0) {
+        a.part_ml[(pbase + h) * 2] = m_run[r];
+        a.part_ml[(pbase + h) * 2 + 1] = l_run[r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 VALU split kernel
+// One workgroup per (split, sequence, head). Chunks of 256 key slots: one thread per key for
+// the logits, then one thread per channel for the weighted sum.
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
+  __shared__ float qs[1024];
+  __shared__ float ps[kThreads];
+  __shared__ int64_t offs[kThreads];
+  __shared__ int32_t isw[kThreads];
+  __shared__ float red[kThreads / 64];
+  const int b = blockIdx.y, split = blockIdx.x, h = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = a.D;
+  const SlotMap sm(a, b);
+  const int32_t s_begin = split * a.kps, s_end = min(s_begin + a.kps, sm.nslots());
+  const float* qp = static_cast<const float*>(a.q) + ((int64_t)b * a.H + h) * D;
+  for (int i = tid; i < D; i += kThreads) qs[i] = qp[i];
+  const float* swa = static_cast<const float*>(a.swa);
+  const float* comp = static_cast<const float*>(a.comp);
+  float acc[4] = {0, 0, 0, 0};
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int32_t s0 = s_begin; s0 < s_end; s0 += kThreads) {
+    __syncthreads();
+    const int32_t s = s0 + tid;
+    bool is_swa = false;
+    const int64_t off = (s < s_end) ? sm.row(a, b, s, &is_swa) : -1;
+    offs[tid] = off;
+    isw[tid] = is_swa;
+    __syncthreads();
+    float x = -INFINITY;
+    if (off >= 0) {
+      const float* kr = (is_swa ? swa : comp) + off;
+      float dot = 0.f;
+      for (int i = 0; i < D; ++i) dot = fmaf(qs[i], kr[i], dot);
+      x = dot * a.scale_log2;
+    }
+    float cm = x;
+    for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+    if (lane == 0) red[wave] = cm;
+    __syncthreads();
+    cm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float mn = fmaxf(m_run, cm);
+    const bool none = (mn == -INFINITY);
+    const float alpha = none ? 1.f : exp2f(m_run - mn);
+    const float p = (none || off < 0) ? 0.f : exp2f(x - mn);
+    ps[tid] = p;
+    float sum = p;
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    __syncthreads();
+    if (lane == 0) red[wave] = sum;
+    __syncthreads();
+    sum = red[0] + red[1] + red[2] + red[3];
+    l_run = l_run * alpha + sum;
+    m_run = mn;
+    const int nk = min(kThreads, s_end - s0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] *= alpha;
+    for (int i = 0; i < nk; ++i) {
+      const int64_t ro = offs[i];
+      if (ro < 0) continue;
+      const float* kr = (isw[i] ? swa : comp) + ro;
+      const float pi = ps[i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cc = tid + q * kThreads;
+        if (cc < D) acc[q] = fmaf(pi, kr[cc], acc[q]);
+      }
+    }
+  }
+  const int64_t pbase = (((int64_t)b * a.n_splits + split) * a.H + h);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int cc = tid + q * kThreads;
+    if (cc < D) a.part_o[pbase * D + cc] = acc[q];
+  }
+  if (tid == 0) { a.part_ml[pbase * 2] = m_run; a.part_ml[pbase * 2 + 1] = l_run; }
+}
+
+// ---------------------------------------------------------------- merge of the splits
+// One workgroup per (sequence, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// lse = (M + log2 L) * ln 2.
+__global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a, float* out, float* lse) {
+  const int b = blockIdx.y, h = blockIdx.x, D = a.D;
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s)
+    M = fmaxf(M, a.part_ml[(((int64_t)b * a.n_splits + s) * a.H + h) * 2]);
+  float L = 0.f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float* ml = a.part_ml + (((int64_t)b * a.n_splits + s) * a.H + h) * 2;
+    if (ml[0] != -INFINITY) L += exp2f(ml[0] - M) * ml[1];
+  }
+  const bool empty = !(L > 0.f);
+  const float invL = empty ? 0.f : 1.f / L;
+  for (int cc = threadIdx.x; cc < D; cc += kThreads) {
+    float acc = 0.f;
+    for (int s = 0; s < a.n_splits; ++s) {
+      const int64_t base = ((int64_t)b * a.n_splits + s) * a.H + h;
+      const float ms = a.part_ml[base * 2];
+      if (ms != -INFINITY) acc = fmaf(exp2f(ms - M), a.part_o[base * D + cc], acc);
+    }
+    out[((int64_t)b * a.H + h) * D + cc] = acc * invL;
+  }
+  if (lse && threadIdx.x == 0)
+    lse[(int64_t)b * a.H + h] = empty ? -INFINITY : (M + log2f(L)) * 0.69314718055994531f;
+}
+
+struct SplitPlan {
+  int32_t n_splits, kps;
+};
+
+SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, int32_t k, int64_t max_comp) {
+  const int64_t max_slots = (int64_t)window + (k > 0 ? k : max_comp);
+  const int gran = dt == CHS_BF16 ? kKeysPerChunk : kThreads;
+  const int64_t blocks_per_split = (int64_t)batch * (dt == CHS_BF16 ? (H + 63) / 64 : H);
+  int64_t want = (512 + blocks_per_split - 1) / blocks_per_split;
+  const int64_t most = (max_slots + gran - 1) / gran;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  int64_t kps = (max_slots + want - 1) / want;
+  kps = (kps + gran - 1) / gran * gran;
+  if (kps < gran) kps = gran;
+  SplitPlan p;
+  p.kps = (int32_t)kps;
+  p.n_splits = (int32_t)((max_slots + kps - 1) / kps);
+  if (p.n_splits < 1) p.n_splits = 1;
+  return p;
+}
+
+size_t ws_bytes(int32_t batch, int32_t H, int32_t D, const SplitPlan& p, float** po, float** pml, char* base) {
+  const size_t nparts = (size_t)batch * p.n_splits * H;
+  size_t o_po = 0, o_ml = align_up(nparts * D * 4, 256);
+  size_t total = align_up(o_ml + nparts * 2 * 4, 256);
+  if (po) *po = reinterpret_cast<float*>(base + o_po);
+  if (pml) *pml = reinterpret_cast<float*>(base + o_ml);
+  return total;
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" size_t chs_decode_attn_workspace_size(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
+                                                 int32_t window, int32_t k, int64_t max_comp) {
+  using namespace chs;
+  if (batch < 1 || n_heads < 1 || d < 1 || window < 0 || k < 0 || max_comp < 0) return 0;
+  SplitPlan p = plan_splits(dtype, batch, n_heads, window, k, max_comp);
+  return ws_bytes(batch, n_heads, d, p, nullptr, nullptr, nullptr);
+}
+
+extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
+                                      int32_t window, int32_t k, float scale, const void* q,
+                                      const void* swa_kv, const int32_t* swa_len, const void* comp_kv,
+                                      const int64_t* cu_comp, const int32_t* topk, int64_t max_comp,
+                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  using namespace chs;
+  if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
+  if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 128 || window < 0 || window > 4096 ||
+      k < 0 || k > 2048 || max_comp < 0 || max_comp >= (1LL << 31) || !(scale > 0.f) || !(scale < INFINITY))
+    return CHS_ERR_SHAPE;
+  if (dtype == CHS_BF16) {
+    if (d != 64 && d != 128 && d != 256 && d != 512) return CHS_ERR_SHAPE;
+  } else if (d < 1 || d > 1024 || d % 4 != 0) {
+    return CHS_ERR_SHAPE;
+  }
+  if (!q || !swa_len || !cu_comp || !out || !workspace) return CHS_ERR_NULL;
+  if (window > 0 && !swa_kv) return CHS_ERR_NULL;
+  if (!comp_kv && (topk ? k > 0 : max_comp > 0)) return CHS_ERR_NULL;
+  const int kk = topk ? k : 0;
+  SplitPlan p = plan_splits(dtype, batch, n_heads, window, kk, max_comp);
+  AttnArgs a;
+  a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
+  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
+  a.scale_log2 = scale * kLog2e;
+  a.n_splits = p.n_splits; a.kps = p.kps;
+  const size_t need = ws_bytes(batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == CHS_BF16) {
+    dim3 grid(p.n_splits, batch, (n_heads + 63) / 64);
+    switch (d) {
+      case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kThreads), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kThreads), 0, s, a); break;
+      case 256: hipLaunchKernelGGL(attn_bf16_kernel<256>, grid, dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL(attn_bf16_kernel<512>, grid, dim3(kThreads), 0, s, a); break;
+    }
+  } else {
+    dim3 grid(p.n_splits, batch, n_heads);
+    hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(kThreads), 0, s, a);
+  }
+  if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  hipLaunchKernelGGL(combine_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
+  return launch_status();
+}

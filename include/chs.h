@@ -1,0 +1,162 @@
+/* chs.h - C ABI of libchs.so: one decode step of one hybrid-sparse-attention layer on MI355X
+ * (gfx950), as hand-written HIP kernels.
+ *
+ * The method (web pages, cited by title and section):
+ *  - "DeepSeek-V4 本地部署，SGLang 把活做絕了", section V4 到底改了啥: every attention layer
+ *    combines a 128-token sliding window (SWA) with one of two compressions: C4 pools groups
+ *    of 4 tokens and attends to the top-512 of them; C128 pools groups of 128 tokens and
+ *    attends to all of them.
+ *  - same page, section Kernel 層一堆狠活: the window and the compressed ("extra") entries
+ *    are attended in one kernel call (FlashMLA's new interface); the compressor is one fused
+ *    pass (Flash Compressor); top-512 of 256K candidates is chosen by a radix select rather
+ *    than a global sort (Lightning TopK).
+ *  - "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", section 创新 2: the compressor's stages
+ *    (load tokens, score, softmax, weighted sum, store) fused into one on-chip pass; the top-k
+ *    threshold is found from per-block radix histograms, and the compressor's output feeds the
+ *    top-k with no copy. Section 创新 3: each C4 step touches about 0.2% of the entries, each
+ *    C128 step reads all of them.
+ * The pages print no formulas. This library computes the following readings of them:
+ *  - compressor: for every complete group of m tokens and every channel c, a softmax over the
+ *    group's gate logits plus a learned per-slot, per-channel bias B[i, c], then the weighted
+ *    sum of the group's token vectors; a trailing partial group is left to the window;
+ *  - indexer score: s_j = sum_h w_h * ReLU(q_h . k_j);
+ *  - top-k: the k largest scores, ties to the lower index, returned as an ascending index set;
+ *  - attention: one softmax over the window rows and the selected (C4) or all (C128) compressed
+ *    entries; keys double as values (a shared latent), logits scaled by `scale` (1/sqrt(d)).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers owned by the caller, except where marked (host).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are asynchronous
+ *    on it; they never synchronize, allocate, free or retain memory. Buffers must stay alive
+ *    until the stream has drained the call.
+ *  - Arguments passed by value are validated on the host before anything is launched; on
+ *    failure the call returns the error and launches nothing. Device-side arrays (cu_*, swa_len,
+ *    topk) are preconditions the host cannot see; out-of-range values there are clamped or
+ *    skipped as each call documents, never used to address memory outside the stated buffers.
+ *  - A failed launch returns CHS_ERR_LAUNCH. Faults inside a kernel surface, as usual for HIP,
+ *    at the caller's next synchronization.
+ *  - Workspaces must be zero-filled before their first use (chs_workspace_clear does that on a
+ *    stream); every call that completes leaves its workspace zero-filled again. Calls that run
+ *    concurrently must use distinct workspaces. No global mutable state exists.
+ *  - dtype CHS_BF16 means bfloat16 storage with fp32 arithmetic; CHS_F32 means fp32 throughout.
+ */
+#ifndef CHS_H
+#define CHS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CHS_OK = 0,
+  CHS_ERR_NULL = 1,         /* a required pointer is NULL */
+  CHS_ERR_SHAPE = 2,        /* a size argument is outside its documented range */
+  CHS_ERR_DTYPE = 3,        /* unknown dtype code */
+  CHS_ERR_WORKSPACE = 4,    /* workspace smaller than the size query returned */
+  CHS_ERR_UNSUPPORTED = 5,  /* valid arguments this build has no kernel for */
+  CHS_ERR_LAUNCH = 6        /* a kernel launch failed */
+} chs_status;
+
+typedef enum { CHS_F32 = 0, CHS_BF16 = 1 } chs_dtype;
+
+/* Library version: major*10000 + minor*100 + patch. */
+int32_t chs_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* chs_status_string(chs_status s);
+
+/* Zero-fill `bytes` bytes of a workspace on `stream` with a kernel (no hipMemsetAsync, so it
+ * can be captured in a HIP graph). bytes must be a multiple of 4. */
+chs_status chs_workspace_clear(void* workspace, size_t bytes, void* stream);
+
+/* ---- chs_compress: the fused group softmax-pool (Flash Compressor's role) ----------------
+ * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 2 (five stages fused into one
+ * pass); "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (C4: m = 4, C128: m = 128).
+ * For sequence b (tokens cu_tokens[b] .. cu_tokens[b+1]-1, N_b of them), every group
+ * g < G_b = floor(N_b / m) and channel c < d:
+ *   a_i = gate[t, c] + bias[i, c],  t = cu_tokens[b] + g*m + i  (i < m)
+ *   out[cu_groups[b] + g, c] = sum_i softmax_i(a)[i] * x[t, c]
+ * x, gate : [T, d] of `dtype`, row-major (T = cu_tokens[batch]).
+ * bias    : [m, d] fp32.
+ * cu_tokens, cu_groups : [batch + 1] int64, non-decreasing, element 0 = 0. cu_groups gives the
+ *   first output row of each sequence; at most cu_groups[b+1] - cu_groups[b] rows are written
+ *   for sequence b (so a packed layout is cu_groups = prefix sums of floor(N_b / m)).
+ * max_groups (host): an upper bound on max_b G_b; it sizes the grid, and groups at or beyond
+ *   it are not computed. 0 launches nothing.
+ * out     : [cu_groups[batch], d] of `dtype` (fp32 arithmetic, rounded to nearest-even once).
+ * Ranges: 1 <= batch <= 65535; 1 <= m <= 1024; 1 <= d <= 4096 with d*elem_size % 16 == 0. */
+chs_status chs_compress(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, const void* x,
+                        const void* gate, const float* bias, const int64_t* cu_tokens,
+                        const int64_t* cu_groups, int64_t max_groups, void* out, void* stream);
+
+/* ---- chs_index_topk: indexer scores, then exact top-k by radix select ------------------
+ * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 2 (Lightning TopK: per-block
+ * radix histograms, a threshold, then each block scatters its entries above it; no global
+ * sort) and 创新 5 (the indexer scores the candidates, then the top-k selects).
+ * Sequence b's candidates are rows cu_cand[b] .. cu_cand[b+1]-1 (G_b of them). Scores:
+ *   scores[cu_cand[b] + j] = sum_h w[b, h] * max(0, sum_t q_idx[b, h, t] * k_idx[cu_cand[b] + j, t])
+ * computed in fp32, then topk[b, :] = the min(k, G_b) largest scores of the sequence (ties to
+ * the lower index; -0.0 equals +0.0), as sequence-local indices in ascending order, padded
+ * with -1 to length k. The selection is exact: given the same score array it is bit-identical
+ * to a full sort.
+ * q_idx   : [batch, n_heads, head_dim] of `dtype`, or NULL: then `scores` is an INPUT holding
+ *           the scores (fp32) and w, k_idx are ignored (standalone top-k). NaN scores are
+ *           outside the contract (the output is then some valid index set, unspecified).
+ * w       : [batch, n_heads] fp32.
+ * k_idx   : [cu_cand[batch], head_dim] of `dtype`.
+ * cu_cand : [batch + 1] int64, non-decreasing, element 0 = 0.
+ * max_cand (host): an upper bound on max_b G_b (sizes the grid; candidates beyond it are
+ *           ignored).
+ * scores  : [cu_cand[batch]] fp32. OUTPUT when q_idx != NULL (may then be NULL: the workspace
+ *           holds them), INPUT when q_idx == NULL.
+ * topk    : [batch, k] int32 output.
+ * workspace: chs_index_topk_workspace_size(batch, max_cand, k) bytes (zero-filled, see above).
+ * Ranges: 1 <= batch <= 65535; 1 <= k <= 2048; 0 <= max_cand < 2^31; with q_idx:
+ *   1 <= n_heads <= 16, 8 <= head_dim <= 512, head_dim*elem_size % 16 == 0. */
+size_t chs_index_topk_workspace_size(int32_t batch, int64_t max_cand, int32_t k);
+chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
+                          int32_t k, const void* q_idx, const float* w, const void* k_idx,
+                          const int64_t* cu_cand, int64_t max_cand, float* scores, int32_t* topk,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- chs_decode_attn: one softmax over the window and the compressed entries ------------
+ * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", Kernel 層一堆狠活 (window and extra
+ * C4/C128 attention in one call) and V4 到底改了啥 (SWA = 128; C4 top-512; C128 dense);
+ * "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 3.2 (MLA decode over a shared latent is
+ * memory-bound; heads need no caller padding here: unused MFMA rows are masked in-kernel).
+ * For sequence b and head h, over the key multiset
+ *   K_b = { swa_kv[b, t] : t < swa_len[b] }  (+)  { comp_kv[cu_comp[b] + j] : j in S_b }
+ * where S_b = { topk[b, i] : i < k, 0 <= topk[b, i] < G_b } (C4; out-of-range entries, -1
+ * included, are skipped; repeats count twice) or S_b = { 0 .. G_b - 1 } when topk == NULL
+ * (C128), G_b = cu_comp[b+1] - cu_comp[b]:
+ *   l_i = scale * (q[b, h] . k_i),   lse[b, h] = log sum_i exp(l_i),
+ *   out[b, h, :] = sum_i exp(l_i - lse[b, h]) * k_i          (keys are also the values)
+ * An empty key set gives out = 0 and lse = -inf.
+ * q       : [batch, n_heads, d] of `dtype`.
+ * swa_kv  : [batch, window, d] of `dtype`: the window's rows (the last min(N_b, window) tokens,
+ *           current token included), any order. swa_len: [batch] int32, clamped to [0, window].
+ * comp_kv : [cu_comp[batch], d] of `dtype`; cu_comp: [batch + 1] int64 (element 0 = 0).
+ * topk    : [batch, k] int32 (as chs_index_topk writes it) or NULL for the dense form.
+ * max_comp (host): an upper bound on max_b G_b (sizes the grid for the dense form).
+ * out     : [batch, n_heads, d] fp32;  lse: [batch, n_heads] fp32, or NULL.
+ * workspace: chs_decode_attn_workspace_size(...) bytes with the same window, k (0 for dense),
+ *           max_comp, batch, n_heads and d (zero-filled, see above).
+ * Ranges: 1 <= batch <= 65535; 1 <= n_heads <= 128; 0 <= window <= 4096; 0 <= k <= 2048;
+ *   scale finite and > 0; bf16: d in {64, 128, 256, 512}; f32: 1 <= d <= 1024, d % 4 == 0. */
+size_t chs_decode_attn_workspace_size(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
+                                      int32_t window, int32_t k, int64_t max_comp);
+chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
+                           int32_t window, int32_t k, float scale, const void* q,
+                           const void* swa_kv, const int32_t* swa_len, const void* comp_kv,
+                           const int64_t* cu_comp, const int32_t* topk, int64_t max_comp,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHS_H */

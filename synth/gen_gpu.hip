@@ -9,36 +9,41 @@
 
 namespace {
 
+// The grid of a launch holds fewer than 2^32 work-items, so every kernel strides over its range.
+#define SYN_FOR_EACH(j, n) \
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < (n); j += (int64_t)gridDim.x * blockDim.x)
+
 __global__ void fill_normal_kernel(uint64_t stream, uint64_t start, int64_t count, double mean,
                                    double stdv, int bf16, void* out) {
-  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= count) return;
-  float v = syn_normal_f32(stream, start + (uint64_t)j, mean, stdv);
-  if (bf16) static_cast<uint16_t*>(out)[j] = syn_f32_to_bf16(v);
-  else static_cast<float*>(out)[j] = v;
+  SYN_FOR_EACH(j, count) {
+    float v = syn_normal_f32(stream, start + (uint64_t)j, mean, stdv);
+    if (bf16) static_cast<uint16_t*>(out)[j] = syn_f32_to_bf16(v);
+    else static_cast<float*>(out)[j] = v;
+  }
 }
 
 __global__ void fill_uniform_kernel(uint64_t stream, uint64_t start, int64_t count, double lo,
                                     double hi, float* out) {
-  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= count) return;
-  out[j] = syn_uniform_f32(stream, start + (uint64_t)j, lo, hi);
+  SYN_FOR_EACH(j, count) out[j] = syn_uniform_f32(stream, start + (uint64_t)j, lo, hi);
 }
 
 __global__ void fill_index_keys_kernel(uint64_t s_noise, uint64_t s_load, int64_t row_start,
                                        int64_t nrows, int32_t dim, int32_t nspike,
                                        const double* U, double alpha, int bf16, void* out) {
-  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= nrows * dim) return;
-  int64_t r = j / dim;
-  int32_t t = (int32_t)(j - r * dim);
-  float v = syn_index_key(s_noise, s_load, (uint64_t)(row_start + r), (uint32_t)t,
-                          (uint32_t)dim, (uint32_t)nspike, U, alpha);
-  if (bf16) static_cast<uint16_t*>(out)[j] = syn_f32_to_bf16(v);
-  else static_cast<float*>(out)[j] = v;
+  SYN_FOR_EACH(j, nrows * dim) {
+    int64_t r = j / dim;
+    int32_t t = (int32_t)(j - r * dim);
+    float v = syn_index_key(s_noise, s_load, (uint64_t)(row_start + r), (uint32_t)t,
+                            (uint32_t)dim, (uint32_t)nspike, U, alpha);
+    if (bf16) static_cast<uint16_t*>(out)[j] = syn_f32_to_bf16(v);
+    else static_cast<float*>(out)[j] = v;
+  }
 }
 
-unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+unsigned grid_for(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  return (unsigned)(b < 65536 * 8 ? b : 65536 * 8);
+}
 
 }  // namespace
 

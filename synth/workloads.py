@@ -120,6 +120,7 @@ def small_workload(dtype: str, lengths, m: int, k: Optional[int], window=128, he
 def host_tokens(wl: Workload, layer: Layer, which: int, b: int, t0: int, t1: int) -> np.ndarray:
     """Rows [t0, t1) of sequence b of X (which=T_X) or Z (which=T_Z), as fp32 [t1-t0, d]."""
     cu = wl.cu_tokens()
+    t0, t1 = int(t0), int(t1)      # Python ints: no fixed-width overflow in the offsets
     std = 1.0 if which == T_X else wl.gate_std
     start = (int(cu[b]) + t0) * wl.d
     return normal(wl.seed, layer.tensor_base + which, start, (t1 - t0) * wl.d, 0.0, std,
@@ -158,6 +159,7 @@ def host_basis(wl: Workload, layer: Layer) -> np.ndarray:
 
 def host_index_keys(wl: Workload, layer: Layer, b: int, j0: int, j1: int) -> np.ndarray:
     """Rows [j0, j1) of sequence b's index keys, fp32 [j1-j0, idx_dim]."""
+    j0, j1 = int(j0), int(j1)
     row0 = int(wl.cu_groups(layer)[b]) + j0
     if wl.spike_alpha == 0.0:
         return normal(wl.seed, layer.tensor_base + T_KN, row0 * wl.idx_dim, (j1 - j0) * wl.idx_dim,

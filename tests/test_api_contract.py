@@ -1,0 +1,105 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the header declares,
+and rejects invalid arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_hybrid_sparse_amd as chs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "chs.h")
+OK, NULL, SHAPE, DTYPE, WS, UNSUP = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails validation first
+
+
+def declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(chs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_python_exports():
+    assert declared() == sorted(chs.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = chs.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+    assert chs.version() >= 100
+    assert b"WORKSPACE" in L.chs_status_string(WS)
+
+
+def compress(dt=1, batch=1, d=512, m=4, x=FAKE, z=FAKE, b=FAKE, cut=FAKE, cug=FAKE, maxg=10, out=FAKE):
+    return chs.lib().chs_compress(dt, batch, d, m, x, z, b, cut, cug, maxg, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), DTYPE), (dict(batch=0), SHAPE), (dict(m=0), SHAPE), (dict(m=1025), SHAPE),
+    (dict(d=0), SHAPE), (dict(d=12), SHAPE), (dict(dt=0, d=6), SHAPE), (dict(maxg=-1), SHAPE),
+    (dict(x=None), NULL), (dict(z=None), NULL), (dict(b=None), NULL), (dict(cut=None), NULL),
+    (dict(cug=None), NULL), (dict(out=None), NULL), (dict(maxg=0), OK), (dict(batch=70000), SHAPE),
+])
+def test_compress_validation(kw, code):
+    assert compress(**kw) == code
+
+
+def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
+         ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_index_topk_workspace_size(batch, maxc, k)
+    return L.chs_index_topk(dt, batch, nh, dim, k, q, w, kk, cu, maxc, s, out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), DTYPE), (dict(k=0), SHAPE), (dict(k=2049), SHAPE), (dict(batch=0), SHAPE),
+    (dict(maxc=-1), SHAPE), (dict(maxc=1 << 31), SHAPE), (dict(nh=0), SHAPE), (dict(nh=17), SHAPE),
+    (dict(dim=4), SHAPE), (dict(dim=12), SHAPE), (dict(dim=1024), SHAPE), (dict(w=None), NULL),
+    (dict(kk=None), NULL), (dict(q=None, s=None), NULL), (dict(cu=None), NULL), (dict(out=None), NULL),
+    (dict(ws=None), NULL), (dict(wsb=16), WS),
+])
+def test_index_topk_validation(kw, code):
+    assert topk(**kw) == code
+
+
+def attn(dt=1, batch=1, H=64, d=512, W=128, k=512, scale=0.04, q=FAKE, swa=FAKE, sl=FAKE, comp=FAKE, cu=FAKE,
+         tk=FAKE, maxc=1000, out=FAKE, lse=FAKE, ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_decode_attn_workspace_size(dt, batch, H, d, W, k if tk else 0, maxc)
+    return L.chs_decode_attn(dt, batch, H, d, W, k, ctypes.c_float(scale), q, swa, sl, comp, cu, tk, maxc,
+                             out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), DTYPE), (dict(batch=0), SHAPE), (dict(H=0), SHAPE), (dict(H=129), SHAPE),
+    (dict(d=96), SHAPE), (dict(dt=0, d=1028), SHAPE), (dict(dt=0, d=6), SHAPE), (dict(W=-1), SHAPE),
+    (dict(k=2049), SHAPE), (dict(scale=0.0), SHAPE), (dict(scale=float("inf")), SHAPE),
+    (dict(scale=float("nan")), SHAPE), (dict(maxc=-2), SHAPE), (dict(q=None), NULL), (dict(sl=None), NULL),
+    (dict(cu=None), NULL), (dict(out=None), NULL), (dict(ws=None), NULL), (dict(swa=None), NULL),
+    (dict(comp=None), NULL), (dict(wsb=8), WS),
+])
+def test_decode_attn_validation(kw, code):
+    assert attn(**kw) == code
+
+
+def test_workspace_sizes_are_monotone():
+    L = chs.lib()
+    a = [L.chs_index_topk_workspace_size(b, n, 512) for b, n in [(1, 1000), (1, 262144), (4, 262144)]]
+    assert 0 < a[0] < a[1] < a[2]
+    s = [L.chs_decode_attn_workspace_size(1, 1, 64, 512, 128, 512, 262144),
+         L.chs_decode_attn_workspace_size(1, 4, 64, 512, 128, 0, 8192),
+         L.chs_decode_attn_workspace_size(1, 64, 64, 512, 128, 512, 50000)]
+    assert all(x > 0 for x in s)
+    assert L.chs_index_topk_workspace_size(0, 10, 5) == 0
+
+
+def test_workspace_clear_validation():
+    L = chs.lib()
+    assert L.chs_workspace_clear(None, 0, None) == OK
+    assert L.chs_workspace_clear(None, 16, None) == NULL
+    assert L.chs_workspace_clear(FAKE, 6, None) == SHAPE
