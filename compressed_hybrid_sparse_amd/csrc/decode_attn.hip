@@ -14,8 +14,9 @@
 // 16w..16w+15, unused heads masked in-kernel, so callers never pad) and walks its slice of the
 // key list 32 rows at a time:
 //   1. the 32 rows are gathered from HBM with coalesced 16-byte loads (one wave per 1 KiB row
-//      at d = 512) and written to LDS twice: row-major (operand of Q.K^T, where d is the
-//      reduction) and transposed (operand of P.V, where the keys are the reduction);
+//      at d = 512) into one row-major LDS tile; Q.K^T reads it with 16-byte loads (d is the
+//      reduction), P.V reads the same tile column-wise with 16-bit loads (keys are the
+//      reduction), so K = V is staged once;
 //   2. S = Q K^T with v_mfma_f32_16x16x32_bf16, Q held in registers for the whole walk;
 //   3. online softmax in fp32 (base-2 logits, running max and sum per head, DPP row reductions);
 //   4. P (rounded to bf16, and the running sum is taken over the rounded values so the weights
@@ -45,9 +46,16 @@ struct AttnArgs {
   int64_t max_comp;
   float scale_log2;         // scale * log2(e)
   int32_t n_splits, kps;    // key slots per split
-  float* part_o;            // [batch][n_splits][H][D]
+  int32_t head_tiles;       // ceil(H / 64) for bf16, H for fp32
+  float* part_o;            // per (sequence, split): see the layout note below
   float* part_ml;           // [batch][n_splits][H][2]: running max (base 2), running sum
 };
+
+constexpr int kCombineSplits = 512;   // most splits one call may use
+
+// Partial O of a split. bf16 (MFMA layout): per (sequence, split, 64-head tile, wave) the
+// wave's accumulators as they sit in registers, [16-column tile j][lane][4]: lane 16g + c,
+// element r hold head 16 * wave + 4g + r, channel 16j + c. fp32: [H][D].
 
 // Key slots of sequence b: [0, swa_len) window rows, then k (C4) or G_b (C128) entries.
 struct SlotMap {
@@ -102,13 +110,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KC = kKeysPerChunk;
   constexpr int KN_PITCH = D + 8;          // bf16 elements per row-major LDS row
-  constexpr int KT_PITCH = KC + 8;         // bf16 elements per transposed LDS row
   constexpr int P_PITCH = KC + 8;
   constexpr int VPR = D / 8;               // 16-byte vectors per row
   constexpr int LOADS = KC * VPR / kThreads;
   static_assert(KC * VPR % kThreads == 0, "tile");
   __shared__ __attribute__((aligned(16))) uint16_t kn[KC * KN_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t kt[D * KT_PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t pb[4][16 * P_PITCH];
   __shared__ int64_t rowoff[KC];
   __shared__ int32_t rowswa[KC];
@@ -167,11 +173,6 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       const int e = tid + i * kThreads;
       const int r = e / VPR, cv = e % VPR;
       *reinterpret_cast<u32x4*>(&kn[r * KN_PITCH + 8 * cv]) = v[i];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        kt[(8 * cv + 2 * x) * KT_PITCH + r] = (uint16_t)(v[i][x] & 0xFFFF);
-        kt[(8 * cv + 2 * x + 1) * KT_PITCH + r] = (uint16_t)(v[i][x] >> 16);
-      }
     }
     __syncthreads();
     // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
@@ -216,24 +217,33 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         pw[(4 * g + r) * P_PITCH + 16 * n + c] = (uint16_t)(__float_as_uint(p[n][r]) >> 16);
     __syncthreads();
     const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pw[c * P_PITCH + 8 * g]));
+    // B operand of P.V: column 16j + c of the tile, keys 8g .. 8g+7.
+    const uint16_t* vcol = &kn[(8 * g) * KN_PITCH + c];
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
-      u32x4 vb = *reinterpret_cast<const u32x4*>(&kt[(16 * j + c) * KT_PITCH + 8 * g]);
+      u32x4 vb;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t lo = vcol[(2 * x) * KN_PITCH + 16 * j];
+        const uint32_t hi = vcol[(2 * x + 1) * KN_PITCH + 16 * j];
+        vb[x] = lo | (hi << 16);
+      }
       o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8, vb), o[j], 0, 0, 0);
     }
   }
-  // Partial result of this split: unnormalised O, running max (base 2) and sum.
-  const int64_t pbase = ((int64_t)b * a.n_splits + split) * a.H;
+  // Partial result of this split: unnormalised O in the MFMA accumulator layout (one 16-byte
+  // store per tile and lane, coalesced), running max (base 2) and sum per head.
+  const int64_t pslot = (int64_t)b * a.n_splits + split;
+  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + ((pslot * a.head_tiles + blockIdx.z) * 4 + wave) * (D / 16) * 64;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = h_base + 4 * g + r;
-    if (h < a.H) {
-      float* po = a.part_o + (pbase + h) * D;
+  for (int j = 0; j < D / 16; ++j) po[j * 64 + lane] = o[j];
+  if (c == 0) {
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) po[16 * j + c] = o[j][r];
-      if (c == 0) {
-        a.part_ml[(pbase + h) * 2] = m_run[r];
-        a.part_ml[(pbase + h) * 2 + 1] = l_run[r];
+    for (int r = 0; r < 4; ++r) {
+      const int h = h_base + 4 * g + r;
+      if (h < a.H) {
+        a.part_ml[(pslot * a.H + h) * 2] = m_run[r];
+        a.part_ml[(pslot * a.H + h) * 2 + 1] = l_run[r];
       }
     }
   }
@@ -307,40 +317,115 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
       }
     }
   }
-  const int64_t pbase = (((int64_t)b * a.n_splits + split) * a.H + h);
+  const int64_t pslot = (int64_t)b * a.n_splits + split;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int cc = tid + q * kThreads;
-    if (cc < D) a.part_o[pbase * D + cc] = acc[q];
+    if (cc < D) a.part_o[(pslot * a.H + h) * D + cc] = acc[q];
   }
-  if (tid == 0) { a.part_ml[pbase * 2] = m_run; a.part_ml[pbase * 2 + 1] = l_run; }
+  if (tid == 0) { a.part_ml[(pslot * a.H + h) * 2] = m_run; a.part_ml[(pslot * a.H + h) * 2 + 1] = l_run; }
 }
 
 // ---------------------------------------------------------------- merge of the splits
-// One workgroup per (sequence, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// lse = (M + log2 L) * ln 2.
-__global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a, float* out, float* lse) {
-  const int b = blockIdx.y, h = blockIdx.x, D = a.D;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s)
-    M = fmaxf(M, a.part_ml[(((int64_t)b * a.n_splits + s) * a.H + h) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float* ml = a.part_ml + (((int64_t)b * a.n_splits + s) * a.H + h) * 2;
-    if (ml[0] != -INFINITY) L += exp2f(ml[0] - M) * ml[1];
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and lse = (M + log2 L) * ln 2, per head.
+// bf16 partials (MFMA layout): one workgroup per (group of 16 heads, 1024 accumulator words
+// of their tile, sequence); each thread reads one 16-byte accumulator (4 heads x 1 channel)
+// per split, so every load is a whole, coalesced vector. Split weights are computed once per
+// head in LDS.
+__global__ __launch_bounds__(kThreads) void combine_mfma_kernel(AttnArgs a, float* out, float* lse) {
+  __shared__ float wts[16][kCombineSplits];
+  __shared__ float lpart[16][kCombineSplits];
+  __shared__ float lsum[16];
+  const int b = blockIdx.z, hg = blockIdx.y;          // heads 16 hg .. 16 hg + 15
+  const int tid = threadIdx.x, D = a.D;
+  const int ns = a.n_splits;
+  // Weights: thread (h, s) pairs.
+  for (int e = tid; e < 16 * ns; e += kThreads) {
+    const int hl = e / ns, sp = e - hl * ns;
+    const int h = 16 * hg + hl;
+    float ms = -INFINITY, ls = 0.f;
+    if (h < a.H) {
+      ms = a.part_ml[(((int64_t)b * ns + sp) * a.H + h) * 2];
+      ls = a.part_ml[(((int64_t)b * ns + sp) * a.H + h) * 2 + 1];
+    }
+    wts[hl][sp] = ms;
+    lpart[hl][sp] = ls;
   }
+  __syncthreads();
+  if (tid < 16) {
+    const int h = 16 * hg + tid;
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, wts[tid][sp]);
+    float L = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float ms = wts[tid][sp];
+      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      wts[tid][sp] = wgt;
+      L += wgt * lpart[tid][sp];
+    }
+    lsum[tid] = L;
+    if (lse && h < a.H) lse[(int64_t)b * a.H + h] = (L > 0.f) ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  }
+  __syncthreads();
+  // Accumulator word index within the wave tile: (j, lane); this thread's 4 heads 4g + r.
+  const int wpos = blockIdx.x * kThreads + tid;       // (j * 64 + lane)
+  if (wpos >= (D / 16) * 64) return;
+  const int j = wpos >> 6, lane = wpos & 63, g = lane >> 4, c = lane & 15;
+  const int tile = hg >> 2, wave = hg & 3;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o);
+  const int64_t stride = (int64_t)a.head_tiles * 4 * (D / 16) * 64;   // one split, in f32x4
+  const int64_t base = (((int64_t)b * ns * a.head_tiles + tile) * 4 + wave) * (D / 16) * 64 + wpos;
+#pragma unroll 4
+  for (int sp = 0; sp < ns; ++sp) {
+    const f32x4 v = po[base + sp * stride];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(wts[4 * g + r][sp], v[r], acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hl = 4 * g + r, h = 16 * hg + hl;
+    if (h < a.H) {
+      const float L = lsum[hl];
+      out[((int64_t)b * a.H + h) * D + 16 * j + c] = (L > 0.f) ? acc[r] / L : 0.f;
+    }
+  }
+}
+
+// fp32 partials ([H][D] per split): one workgroup per (sequence, head).
+__global__ __launch_bounds__(kThreads) void combine_rows_kernel(AttnArgs a, float* out, float* lse) {
+  __shared__ float wts[kCombineSplits];
+  __shared__ float red[2][kThreads / 64];
+  const int b = blockIdx.y, h = blockIdx.x, D = a.D;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = a.n_splits;
+  const float* ml = a.part_ml + ((int64_t)b * ns * a.H + h) * 2;
+  float mloc = -INFINITY;
+  for (int s = tid; s < ns; s += kThreads) mloc = fmaxf(mloc, ml[(int64_t)s * a.H * 2]);
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+  if (lane == 0) red[0][wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  float lloc = 0.f;
+  for (int s = tid; s < ns; s += kThreads) {
+    const float ms = ml[(int64_t)s * a.H * 2];
+    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    wts[s] = wgt;
+    lloc += wgt * ml[(int64_t)s * a.H * 2 + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o, 64);
+  if (lane == 0) red[1][wave] = lloc;
+  __syncthreads();
+  const float L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
   const bool empty = !(L > 0.f);
   const float invL = empty ? 0.f : 1.f / L;
-  for (int cc = threadIdx.x; cc < D; cc += kThreads) {
+  for (int cc = tid; cc < D; cc += kThreads) {
     float acc = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-      const int64_t base = ((int64_t)b * a.n_splits + s) * a.H + h;
-      const float ms = a.part_ml[base * 2];
-      if (ms != -INFINITY) acc = fmaf(exp2f(ms - M), a.part_o[base * D + cc], acc);
-    }
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) acc = fmaf(wts[s], a.part_o[(((int64_t)b * ns + s) * a.H + h) * D + cc], acc);
     out[((int64_t)b * a.H + h) * D + cc] = acc * invL;
   }
-  if (lse && threadIdx.x == 0)
+  if (lse && tid == 0)
     lse[(int64_t)b * a.H + h] = empty ? -INFINITY : (M + log2f(L)) * 0.69314718055994531f;
 }
 
@@ -355,6 +440,7 @@ SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, in
   int64_t want = (512 + blocks_per_split - 1) / blocks_per_split;
   const int64_t most = (max_slots + gran - 1) / gran;
   if (want > most) want = most;
+  if (want > kCombineSplits) want = kCombineSplits;
   if (want < 1) want = 1;
   int64_t kps = (max_slots + want - 1) / want;
   kps = (kps + gran - 1) / gran * gran;
@@ -366,9 +452,11 @@ SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, in
   return p;
 }
 
-size_t ws_bytes(int32_t batch, int32_t H, int32_t D, const SplitPlan& p, float** po, float** pml, char* base) {
+size_t ws_bytes(chs_dtype dt, int32_t batch, int32_t H, int32_t D, const SplitPlan& p, float** po, float** pml,
+                char* base) {
   const size_t nparts = (size_t)batch * p.n_splits * H;
-  size_t o_po = 0, o_ml = align_up(nparts * D * 4, 256);
+  const size_t hpad = dt == CHS_BF16 ? (size_t)(H + 63) / 64 * 64 : (size_t)H;
+  size_t o_po = 0, o_ml = align_up((size_t)batch * p.n_splits * hpad * D * 4, 256);
   size_t total = align_up(o_ml + nparts * 2 * 4, 256);
   if (po) *po = reinterpret_cast<float*>(base + o_po);
   if (pml) *pml = reinterpret_cast<float*>(base + o_ml);
@@ -383,7 +471,7 @@ extern "C" size_t chs_decode_attn_workspace_size(chs_dtype dtype, int32_t batch,
   using namespace chs;
   if (batch < 1 || n_heads < 1 || d < 1 || window < 0 || k < 0 || max_comp < 0) return 0;
   SplitPlan p = plan_splits(dtype, batch, n_heads, window, k, max_comp);
-  return ws_bytes(batch, n_heads, d, p, nullptr, nullptr, nullptr);
+  return ws_bytes(dtype, batch, n_heads, d, p, nullptr, nullptr, nullptr);
 }
 
 extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
@@ -412,7 +500,8 @@ extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_
   a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
   a.n_splits = p.n_splits; a.kps = p.kps;
-  const size_t need = ws_bytes(batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
+  a.head_tiles = dtype == CHS_BF16 ? (n_heads + 63) / 64 : n_heads;
+  const size_t need = ws_bytes(dtype, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == CHS_BF16) {
@@ -428,6 +517,12 @@ extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(kThreads), 0, s, a);
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-  hipLaunchKernelGGL(combine_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
+  if (dtype == CHS_BF16) {
+    const dim3 cgrid((unsigned)((d / 16 * 64 + kThreads - 1) / kThreads), (unsigned)((n_heads + 15) / 16),
+                     (unsigned)batch);
+    hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(kThreads), 0, s, a, out, lse);
+  } else {
+    hipLaunchKernelGGL(combine_rows_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
+  }
   return launch_status();
 }

@@ -1,65 +1,84 @@
-// chs_index_topk: indexer scores, then the exact top-k by an LDS-histogram radix select.
+// chs_index_topk: indexer scores, then the exact top-k by radix selection, with no global sort.
 //
 // Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 2 (Lightning TopK): a global
-// sort of 256K candidates costs over 100 us at batch 1; instead each block builds a local
-// radix histogram, the histograms are reduced, a threshold is found, and each block writes out
-// its own entries above it. "DeepSeek-V4 本地部署，SGLang 把活做絕了", Kernel 層一堆狠活: top-512
-// of 256K candidates at 1M context. The same first page, 创新 5: the indexer scores every
-// candidate before the top-k selects.
+// sort of 256K candidates costs over 100 us at batch 1; instead, blocks build radix histograms
+// of their scores, a threshold is found, and each block writes out only its own entries above
+// it. Same page, 创新 5: the indexer scores every compressed candidate before the top-k.
+// "DeepSeek-V4 本地部署，SGLang 把活做絕了", Kernel 層一堆狠活: top-512 of 256K at 1M context.
 //
-// The pages' design uses clusters of 8 CTAs with distributed shared memory, which gfx950 does
-// not have. Here the cross-workgroup steps use the "last workgroup done" pattern instead: every
-// workgroup flushes its partial result with device-scope atomics, bumps a per-sequence counter,
-// and the workgroup that brings the counter to its final value does the sequential step. No
-// workgroup ever waits on another, so the kernels need no co-residency and cannot deadlock.
+// The pages' design reduces per-CTA histograms inside a thread-block cluster through
+// distributed shared memory, which gfx950 does not have; on MI355X a device-scope fence costs
+// tens of nanoseconds per workgroup, serialised, and same-address atomics about ten. So no
+// kernel here synchronises workgroups with each other: every cross-workgroup step is a kernel
+// boundary, and the data crossing it is written with plain stores.
 //
-// Kernel A (score_hist): one workgroup per chunk of CH candidates of one sequence. It streams
-//   the chunk's index keys once (non-temporal 16-byte loads), computes the scores with
-//   v_dot2_f32_bf16 (or fp32 FMAs), writes them, and counts them in an LDS histogram over the
-//   top 11 bits of an order-preserving 32-bit key. The last workgroup of a sequence reduces
-//   the global histogram and finds the bin that holds the k-th largest key.
-// Kernel B (select): each workgroup re-reads its chunk's scores (1 MiB for 256K candidates,
-//   from cache) and appends every candidate in or above the threshold bin to a per-sequence
-//   list. The last workgroup refines the threshold exactly with more radix passes over that
-//   short list (in LDS when it fits), breaks ties at the threshold by lower index, and writes
-//   the ascending index set.
-// The composite order (key descending, index ascending) is a total order, so the selected set
-// is unique and the result is bit-identical to a full sort of the same scores.
+//   K1 score_kernel (one workgroup per 128 candidates, many resident per CU): streams the
+//      index keys once (non-temporal 16-byte loads, v_dot2_f32_bf16 or fp32 FMAs, DPP lane
+//      reductions), writes the fp32 scores, and writes the maximum order-preserving key of
+//      every sub-chunk of SC consecutive candidates. max_kernel does only the maxima, for
+//      caller-provided scores.
+//   K2 bound_kernel (one workgroup per sequence): L = the k-th largest sub-chunk maximum
+//      (radix select in LDS over at most 16384 maxima, rounded down to 22 key bits). L never
+//      exceeds the k-th largest score: k disjoint sub-chunks each hold a score >= L. So every
+//      top-k candidate, and every tie at the threshold, has key >= L. Also the largest key.
+//   K3 select_kernel (one workgroup per 1024 candidates): writes the chunk's candidates with
+//      key >= L, in index order, to the chunk's own region, and their count.
+//   K4 final_kernel (one workgroup per sequence): gathers the regions in chunk order (so in
+//      index order), finds the exact k-th largest key tau by 8-bit radix passes over the bits
+//      below the prefix that L and the largest key share, takes every key above tau and the
+//      first ties at tau in index order, and writes the selection ascending by a prefix count:
+//      no sort is needed. If the superset exceeds the LDS capacity (heavy ties, adversarial
+//      inputs), the same passes stream from a global copy instead.
+// The composite order (key descending, then index ascending) is total, so the selected set is
+// unique and bit-identical to a full sort of the same scores.
 #include "common.h"
 
 namespace chs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBins1 = 2048;     // first pass: key bits [31:21]
-constexpr int kChunk = 512;      // candidates per workgroup
-constexpr int kListLds = 4096;   // final selection runs from LDS up to this many list entries
+constexpr int kThreads = 256;        // K1, K3
+constexpr int kBoundThreads = 1024;  // K2
+constexpr int kFinalThreads = 512;   // K4
+constexpr int kScoreChunk = 128;     // candidates per K1 workgroup
+constexpr int kMaxChunk = 2048;      // scores per max_kernel workgroup (256 threads x 8)
+constexpr int kSelChunk = 1024;      // candidates per K3 workgroup (256 threads x 4)
+constexpr int kMaxMaxima = 16384;    // sub-chunk maxima K2 ranks (LDS)
+constexpr int kLdsCand = 8192;       // superset size K4 keeps in LDS
+constexpr int kMaxSelChunks = 4096;  // K3 chunks per sequence (max_cand <= 4M)
 constexpr int kMaxK = 2048;
-constexpr int kCtrlWords = 8;    // per sequence: see Ctrl
-
-// Per-sequence control words in the workspace. All of them return to zero when a call ends.
-enum Ctrl { kDoneA = 0, kBin1 = 1, kAbove = 2, kListCount = 3, kDoneB = 4 };
+constexpr int64_t kMaxCand = (int64_t)kMaxSelChunks * kSelChunk;
 
 struct Workspace {
-  uint32_t* hist;   // [batch][kBins1]
-  uint32_t* ctrl;   // [batch][kCtrlWords]
-  uint32_t* list;   // [batch][max_cand][2]: (key, index)
-  float* scores;    // [batch][max_cand] (used when the caller passes no score array)
+  uint32_t* maxima;   // [batch][rc]: sub-chunk maximum keys, sub-chunk j at index j
+  uint32_t* bound;    // [batch][2]: L, largest key
+  uint32_t* counts;   // [batch][rc / kSelChunk]
+  uint32_t* region;   // [batch][rc][2]: per K3 chunk, (key, index) in index order
+  uint32_t* gather;   // [batch][rc][2]: K4's global superset copy (large supersets only)
+  float* scores;      // [batch][rc] when the caller passes no score array
 };
 
+// Candidate capacity per sequence, rounded up to whole K3 chunks.
+__host__ __device__ inline int64_t round_cand(int64_t max_cand) {
+  return (max_cand + kSelChunk - 1) / kSelChunk * kSelChunk;
+}
+
 size_t ws_layout(int32_t batch, int64_t max_cand, Workspace* w, char* base) {
-  size_t off = 0;
   const size_t nb = (size_t)batch;
-  const size_t mc = (size_t)(max_cand > 0 ? max_cand : 0);
-  size_t o_hist = off; off = align_up(off + nb * kBins1 * 4, 256);
-  size_t o_ctrl = off; off = align_up(off + nb * kCtrlWords * 4, 256);
-  size_t o_list = off; off = align_up(off + nb * mc * 8, 256);
-  size_t o_scores = off; off = align_up(off + nb * mc * 4, 256);
+  const size_t rc = (size_t)round_cand(max_cand > 0 ? max_cand : 0);
+  size_t off = 0;
+  const size_t o_max = off; off = align_up(off + nb * rc * 4, 256);
+  const size_t o_bnd = off; off = align_up(off + nb * 2 * 4, 256);
+  const size_t o_cnt = off; off = align_up(off + nb * (rc / kSelChunk + 1) * 4, 256);
+  const size_t o_reg = off; off = align_up(off + nb * rc * 8, 256);
+  const size_t o_gat = off; off = align_up(off + nb * rc * 8, 256);
+  const size_t o_sc = off; off = align_up(off + nb * rc * 4, 256);
   if (w) {
-    w->hist = reinterpret_cast<uint32_t*>(base + o_hist);
-    w->ctrl = reinterpret_cast<uint32_t*>(base + o_ctrl);
-    w->list = reinterpret_cast<uint32_t*>(base + o_list);
-    w->scores = reinterpret_cast<float*>(base + o_scores);
+    w->maxima = reinterpret_cast<uint32_t*>(base + o_max);
+    w->bound = reinterpret_cast<uint32_t*>(base + o_bnd);
+    w->counts = reinterpret_cast<uint32_t*>(base + o_cnt);
+    w->region = reinterpret_cast<uint32_t*>(base + o_reg);
+    w->gather = reinterpret_cast<uint32_t*>(base + o_gat);
+    w->scores = reinterpret_cast<float*>(base + o_sc);
   }
   return off;
 }
@@ -71,29 +90,54 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+struct Args {
+  const void* q;        // [batch][nh][dim] (NULL: scores are input)
+  const float* w;       // [batch][nh]
+  const void* keys;     // [cu[batch]][dim]
+  const int64_t* cu;    // [batch+1]
+  int64_t max_cand;
+  int32_t nh, nvec, lpc;
+  int32_t sc;           // sub-chunk size (power of two, at most kScoreChunk)
+  int32_t k;
+  float* scores;        // caller's packed array, or NULL -> workspace
+  Workspace ws;
+};
+
+__device__ __forceinline__ int64_t cand_count(const Args& a, int b, int64_t* base) {
+  const int64_t c0 = a.cu[b];
+  int64_t n = a.cu[b + 1] - c0;
+  if (n > a.max_cand) n = a.max_cand;
+  if (n < 0) n = 0;
+  *base = c0;
+  return n;
 }
-__device__ __forceinline__ void atomic_store_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float* score_ptr(const Args& a, int b, int64_t c0) {
+  return a.scores ? a.scores + c0 : a.ws.scores + (int64_t)b * round_cand(a.max_cand);
+}
+__device__ __forceinline__ uint32_t* maxima_ptr(const Args& a, int b) {
+  return a.ws.maxima + (size_t)b * round_cand(a.max_cand);
+}
+__device__ __forceinline__ size_t sel_chunk_base(const Args& a, int b) {
+  return (size_t)b * (size_t)(round_cand(a.max_cand) / kSelChunk);
 }
 
-// Block-wide exclusive prefix sum over kThreads threads; returns the block total in *total.
-__device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* scratch /*[kThreads/64 + 1]*/) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// ---------------------------------------------------------------- block scans
+// Exclusive prefix sum over blockDim.x (a multiple of 64, at most 1024) threads.
+// scratch: at least blockDim.x / 64 words. Returns the exclusive prefix; *total gets the sum.
+__device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   uint32_t inc = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(inc, o, 64);
+    const uint32_t t = __shfl_up(inc, o, 64);
     if (lane >= o) inc += t;
   }
   if (lane == 63) scratch[wave] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    uint32_t t = scratch[w];
-    if (w < wave) before += t;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t t = scratch[w];
+    before += (w < wave) ? t : 0u;
     all += t;
   }
   __syncthreads();
@@ -101,35 +145,46 @@ __device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* s
   return before + inc - v;
 }
 
-// In a histogram of `nbins` counts (nbins % kThreads == 0), find for rank r >= 1 counted from
-// the top (descending=true) or from the bottom: the bin holding the r-th element, and the
-// number of elements strictly before that bin in the scan order. Result in out[0..1].
-__device__ void find_rank_bin(const uint32_t* hist, int nbins, uint32_t r, bool descending,
-                              uint32_t* scratch, uint32_t* out) {
-  const int per = nbins / kThreads;
-  // Thread t owns scan positions [t*per, (t+1)*per); position p maps to bin p (ascending) or
-  // nbins-1-p (descending).
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) {
-    int p = threadIdx.x * per + i;
-    local += hist[descending ? nbins - 1 - p : p];
-  }
-  uint32_t total;
-  uint32_t before = block_exclusive_sum(local, &total, scratch);
-  if (before < r && before + local >= r) {
-    uint32_t run = before;
-    for (int i = 0; i < per; ++i) {
-      int p = threadIdx.x * per + i;
-      int bin = descending ? nbins - 1 - p : p;
-      uint32_t c = hist[bin];
-      if (run + c >= r) { out[0] = (uint32_t)bin; out[1] = run; break; }
-      run += c;
-    }
-  }
+// Block-wide maximum (blockDim.x a multiple of 64); scratch as above.
+__device__ uint32_t block_max(uint32_t v, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  if (lane == 0) scratch[wave] = v;
   __syncthreads();
+  uint32_t all = 0;
+  for (int w = 0; w < nw; ++w) all = max(all, scratch[w]);
+  __syncthreads();
+  return all;
 }
 
-// ---------------------------------------------------------------- kernel A: score + histogram
+// Given a 256-bin histogram and a rank r >= 1 counted from the top, wave 0 finds the bin that
+// holds the r-th largest element and the count strictly above it; results in out[0], out[1].
+__device__ void top_rank_bin256(const uint32_t* hist, uint32_t r, uint32_t* out) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // Lane l owns bins 255-4l .. 252-4l (descending scan order).
+    uint32_t c[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; local += c[i]; }
+    uint32_t inc = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    uint32_t run = inc - local;
+    if (run < r && inc >= r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (run + c[i] >= r) { out[0] = 255 - 4 * lane - i; out[1] = run; break; }
+        run += c[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- K1: scores + sub-chunk maxima
 template <typename ET>
 struct Dot16;
 
@@ -153,13 +208,16 @@ template <>
 struct Dot16<float> {      // 4 fp32 per 16 bytes
   __device__ static float dot(const u32x4& a, const u32x4& b, float acc) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = fmaf(__uint_as_float(a[j]), __uint_as_float(b[j]), acc);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = a[j], y = b[j];
+      acc = fmaf(__uint_as_float(x), __uint_as_float(y), acc);
+    }
     return acc;
   }
 };
 
-// Sum a float over groups of `lpc` adjacent lanes (lpc a power of two <= 64); every lane of a
-// group ends with the group total. Within rows of 16 lanes this uses DPP lane swizzles.
+// Sum over groups of `lpc` adjacent lanes (lpc a power of two <= 64); every lane of a group
+// ends with the group total. Within a row of 16 lanes this uses DPP lane swizzles.
 __device__ __forceinline__ float group_sum(float v, int lpc) {
   if (lpc >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // xor 1
   if (lpc >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // xor 2
@@ -170,85 +228,46 @@ __device__ __forceinline__ float group_sum(float v, int lpc) {
   return v;
 }
 
-struct ScoreArgs {
-  const void* q;        // [batch][nh][dim] (NULL: scores are input)
-  const float* w;       // [batch][nh]
-  const void* keys;     // [cu_cand[batch]][dim]
-  const int64_t* cu;    // [batch+1]
-  int64_t max_cand;
-  int32_t nh, dim;
-  int32_t nvec;         // 16-byte vectors per key row
-  int32_t lpc;          // lanes per candidate
-  float* scores;        // caller's packed array, or NULL -> workspace [b][max_cand]
-  Workspace ws;
-  int32_t k;
-};
-
-__device__ __forceinline__ int64_t cand_count(const ScoreArgs& a, int b, int64_t* base) {
-  const int64_t c0 = a.cu[b];
-  int64_t n = a.cu[b + 1] - c0;
-  if (n > a.max_cand) n = a.max_cand;
-  if (n < 0) n = 0;
-  *base = c0;
-  return n;
-}
-
-__device__ __forceinline__ float* score_ptr(const ScoreArgs& a, int b, int64_t c0) {
-  return a.scores ? a.scores + c0 : a.ws.scores + (int64_t)b * a.max_cand;
-}
-
-// Tail of kernel A, run by every workgroup: flush the LDS histogram, count the workgroup done,
-// and in the sequence's last workgroup locate the threshold bin.
-__device__ void flush_and_find_bin1(const ScoreArgs& a, int b, int64_t n, uint32_t* lhist,
-                                    uint32_t* scratch) {
-  __syncthreads();
-  uint32_t* gh = a.ws.hist + (size_t)b * kBins1;
-  for (int i = threadIdx.x; i < kBins1; i += kThreads) {
-    uint32_t c = lhist[i];
-    if (c) atomicAdd(gh + i, c);
-  }
-  __threadfence();
-  __syncthreads();
-  const int nchunks = n > 0 ? (int)((n + kChunk - 1) / kChunk) : 1;
-  uint32_t* ctrl = a.ws.ctrl + (size_t)b * kCtrlWords;
-  if (threadIdx.x == 0) scratch[8] = atomicAdd(ctrl + kDoneA, 1u);
-  __syncthreads();
-  if (scratch[8] != (uint32_t)(nchunks - 1)) return;
-  // Last workgroup of sequence b.
-  __threadfence();
-  for (int i = threadIdx.x; i < kBins1; i += kThreads) lhist[i] = atomicExch(gh + i, 0u);
-  __syncthreads();
-  const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
-  if (keff > 0) {
-    find_rank_bin(lhist, kBins1, keff, true, scratch, scratch + 12);
-    if (threadIdx.x == 0) {
-      atomic_store_agent(ctrl + kBin1, scratch[12]);
-      atomic_store_agent(ctrl + kAbove, scratch[13]);
-    }
-  }
-  if (threadIdx.x == 0) atomic_store_agent(ctrl + kDoneA, 0u);
+// Write the maxima of the sub-chunks that [j0, j1) covers (j0 a multiple of sc; LDS holds them
+// from index 0).
+__device__ __forceinline__ void store_maxima(const Args& a, int b, int64_t j0, int64_t j1, const uint32_t* smax) {
+  const int cnt = (int)((j1 - j0 + a.sc - 1) / a.sc);
+  uint32_t* g = maxima_ptr(a, b) + j0 / a.sc;
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) g[i] = smax[i];
 }
 
 template <typename ET, int NH, int MAXV>
-__global__ __launch_bounds__(kThreads) void score_hist_kernel(ScoreArgs a) {
-  __shared__ uint32_t lhist[kBins1];
-  __shared__ uint32_t scratch[16];
+__global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
+  __shared__ uint32_t smax[kScoreChunk];
   const int b = blockIdx.y;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
-  const int64_t chunk0 = (int64_t)blockIdx.x * kChunk;
-  const int nchunks = n > 0 ? (int)((n + kChunk - 1) / kChunk) : 1;
-  if ((int)blockIdx.x >= nchunks) return;
-  for (int i = threadIdx.x; i < kBins1; i += kThreads) lhist[i] = 0;
-  __syncthreads();
+  const int64_t chunk0 = (int64_t)blockIdx.x * kScoreChunk;
+  if (chunk0 >= n) return;
+  const int64_t chunk_end = min<int64_t>(chunk0 + kScoreChunk, n);
+  if (threadIdx.x < kScoreChunk) smax[threadIdx.x] = 0u;   // 0: below every key
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lpc = a.lpc;
   const int sub = lane & (lpc - 1);
   const int slot = (wave * 64 + lane) / lpc;          // candidate slot within a pass
   const int per_pass = kThreads / lpc;
-  // This lane's slice of every indexer query: vectors sub, sub + lpc, ...
-  u32x4 qv[NH][MAXV];
+  const u32x4* kb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.keys) + (size_t)c0 * a.nvec * 16);
+  // Issue the chunk's key loads first (U passes of per_pass candidates), then the query slices.
+  constexpr int U = 4;
+  u32x4 kv[U][MAXV];
+  int64_t j[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    j[u] = chunk0 + u * per_pass + slot;
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      const int vi = sub + v * lpc;
+      kv[u][v] = (j[u] < chunk_end && vi < a.nvec) ? __builtin_nontemporal_load(kb + j[u] * a.nvec + vi)
+                                                   : u32x4{0, 0, 0, 0};
+    }
+  }
+  u32x4 qv[NH][MAXV];                                 // this lane's slice of every query
   float wv[NH];
   const u32x4* qb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
                                                    (size_t)b * a.nh * a.nvec * 16);
@@ -261,21 +280,20 @@ __global__ __launch_bounds__(kThreads) void score_hist_kernel(ScoreArgs a) {
       qv[h][v] = (h < a.nh && vi < a.nvec) ? qb[h * a.nvec + vi] : u32x4{0, 0, 0, 0};
     }
   }
-  const u32x4* kb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.keys) + (size_t)c0 * a.nvec * 16);
+  __syncthreads();
   float* sp = score_ptr(a, b, c0);
-  const int64_t chunk_end = min<int64_t>(chunk0 + kChunk, n);
-  constexpr int U = 4;   // passes in flight per lane: U * MAXV 16-byte loads
+  // per_pass * U >= kScoreChunk whenever lpc <= 8; wider rows take more rounds.
   for (int64_t base = chunk0; base < chunk_end; base += per_pass * U) {
-    u32x4 kv[U][MAXV];
-    int64_t j[U];
+    if (base != chunk0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      j[u] = base + u * per_pass + slot;
+      for (int u = 0; u < U; ++u) {
+        j[u] = base + u * per_pass + slot;
 #pragma unroll
-      for (int v = 0; v < MAXV; ++v) {
-        const int vi = sub + v * lpc;
-        kv[u][v] = (j[u] < chunk_end && vi < a.nvec) ? __builtin_nontemporal_load(kb + j[u] * a.nvec + vi)
-                                                     : u32x4{0, 0, 0, 0};
+        for (int v = 0; v < MAXV; ++v) {
+          const int vi = sub + v * lpc;
+          kv[u][v] = (j[u] < chunk_end && vi < a.nvec) ? __builtin_nontemporal_load(kb + j[u] * a.nvec + vi)
+                                                       : u32x4{0, 0, 0, 0};
+        }
       }
     }
 #pragma unroll
@@ -291,222 +309,290 @@ __global__ __launch_bounds__(kThreads) void score_hist_kernel(ScoreArgs a) {
       }
       if (sub == 0 && j[u] < chunk_end) {
         sp[j[u]] = s;
-        atomicAdd(&lhist[score_key(s) >> 21], 1u);
+        atomicMax(&smax[(int)(j[u] - chunk0) / a.sc], score_key(s));
       }
     }
   }
-  flush_and_find_bin1(a, b, n, lhist, scratch);
+  __syncthreads();
+  store_maxima(a, b, chunk0, chunk_end, smax);
 }
 
-// Kernel A for caller-provided scores: histogram only.
-__global__ __launch_bounds__(kThreads) void hist_kernel(ScoreArgs a) {
-  __shared__ uint32_t lhist[kBins1];
-  __shared__ uint32_t scratch[16];
+// K1 for caller-provided scores: sub-chunk maxima only (8 scores per thread, 16-byte loads
+// when the row is 16-byte aligned).
+__global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
+  __shared__ uint32_t smax[kMaxChunk];
   const int b = blockIdx.y;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
-  const int nchunks = n > 0 ? (int)((n + kChunk - 1) / kChunk) : 1;
-  if ((int)blockIdx.x >= nchunks) return;
-  for (int i = threadIdx.x; i < kBins1; i += kThreads) lhist[i] = 0;
-  __syncthreads();
+  const int64_t chunk0 = (int64_t)blockIdx.x * kMaxChunk;
+  if (chunk0 >= n) return;
+  const int64_t chunk_end = min<int64_t>(chunk0 + kMaxChunk, n);
+  for (int i = threadIdx.x; i < kMaxChunk; i += kThreads) smax[i] = 0u;
   const float* sp = score_ptr(a, b, c0);
-  const int64_t chunk0 = (int64_t)blockIdx.x * kChunk, chunk_end = min<int64_t>(chunk0 + kChunk, n);
-  for (int64_t j = chunk0 + threadIdx.x; j < chunk_end; j += kThreads)
-    atomicAdd(&lhist[score_key(sp[j]) >> 21], 1u);
-  flush_and_find_bin1(a, b, n, lhist, scratch);
+  float v[8];
+  const int64_t j = chunk0 + 4 * threadIdx.x;   // this thread: j..j+3 and j+1024..j+1027
+  const bool vec = ((reinterpret_cast<uintptr_t>(sp) & 15) == 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t jj = j + h * 1024;
+    if (vec && jj + 3 < chunk_end) {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + jj));
+      v[4 * h] = x[0]; v[4 * h + 1] = x[1]; v[4 * h + 2] = x[2]; v[4 * h + 3] = x[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * h + e] = (jj + e < chunk_end) ? sp[jj + e] : 0.f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t jj = j + h * 1024 + e;
+      if (jj < chunk_end) atomicMax(&smax[(int)(jj - chunk0) / a.sc], score_key(v[4 * h + e]));
+    }
+  __syncthreads();
+  store_maxima(a, b, chunk0, chunk_end, smax);
 }
 
-// ---------------------------------------------------------------- kernel B: select
-struct SelectShared {
-  uint32_t key[kListLds];
-  uint32_t idx[kListLds];
-  uint32_t hist[kBins1];
-  uint32_t sorted[kMaxK];
-  uint32_t scratch[16];
+// ---------------------------------------------------------------- K2: the bound L
+// L = the k-th largest of the sequence's sub-chunk maxima (the first kMaxMaxima of them when
+// there are more: any k disjoint sub-chunks give a valid bound), rounded down to its top 22
+// bits; 0 (no pruning) when there are fewer than k maxima. Also the largest maximum, which is
+// the largest key of the sequence.
+__global__ __launch_bounds__(kBoundThreads) void bound_kernel(Args a) {
+  __shared__ uint32_t vals[kMaxMaxima];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scratch[40];
+  const int b = blockIdx.x;
+  int64_t c0;
+  const int64_t n = cand_count(a, b, &c0);
+  const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
+  const int64_t m_all = (n + a.sc - 1) / a.sc;
+  const int m = (int)min<int64_t>(m_all, kMaxMaxima);
+  const uint32_t* g = maxima_ptr(a, b);
+  uint32_t vmax = 0;
+  for (int i = threadIdx.x; i < m; i += kBoundThreads) { vals[i] = g[i]; vmax = max(vmax, vals[i]); }
+  vmax = block_max(vmax, scratch);   // (the maxima beyond kMaxMaxima only matter for pruning)
+  if (m_all > m) {
+    for (int64_t i = m + threadIdx.x; i < m_all; i += kBoundThreads) vmax = max(vmax, g[i]);
+    vmax = block_max(vmax, scratch);
+  }
+  uint32_t L = 0;
+  if (n > (int64_t)keff && m_all >= (int64_t)keff && keff > 0) {
+    uint32_t prefix = 0, r = keff;
+    for (int p = 0; p < 2; ++p) {
+      const int shift = p == 0 ? 21 : 10;
+      for (int i = threadIdx.x; i < 2048; i += kBoundThreads) hist[i] = 0u;
+      __syncthreads();
+      for (int i = threadIdx.x; i < m; i += kBoundThreads) {
+        const uint32_t v = vals[i];
+        if (p == 0 || (v >> 21) == prefix) atomicAdd(&hist[(v >> shift) & 2047u], 1u);
+      }
+      __syncthreads();
+      // The bin of the r-th largest: each thread owns 2 bins in descending order.
+      const uint32_t c1 = hist[2047 - 2 * threadIdx.x], c2 = hist[2046 - 2 * threadIdx.x];
+      uint32_t total;
+      const uint32_t run = block_exclusive_sum(c1 + c2, &total, scratch);
+      if (run < r && run + c1 >= r) { scratch[32] = 2047 - 2 * threadIdx.x; scratch[33] = run; }
+      else if (run + c1 < r && run + c1 + c2 >= r) { scratch[32] = 2046 - 2 * threadIdx.x; scratch[33] = run + c1; }
+      __syncthreads();
+      const uint32_t bin = scratch[32];
+      r -= scratch[33];
+      prefix = (p == 0) ? bin : ((prefix << 11) | bin);
+      __syncthreads();
+    }
+    L = prefix << 10;
+  }
+  if (threadIdx.x == 0) { a.ws.bound[2 * b] = L; a.ws.bound[2 * b + 1] = vmax; }
+}
+
+// ---------------------------------------------------------------- K3: the superset
+__global__ __launch_bounds__(kThreads) void select_kernel(Args a) {
+  __shared__ uint32_t scratch[8];
+  const int b = blockIdx.y;
+  int64_t c0;
+  const int64_t n = cand_count(a, b, &c0);
+  const int64_t chunk0 = (int64_t)blockIdx.x * kSelChunk;
+  if (chunk0 >= n) return;
+  const int64_t chunk_end = min<int64_t>(chunk0 + kSelChunk, n);
+  const uint32_t L = a.ws.bound[2 * b];
+  const float* sp = score_ptr(a, b, c0);
+  // Thread t owns candidates chunk0 + 4t .. 4t+3 (consecutive, so index order is kept).
+  const int64_t j = chunk0 + 4 * threadIdx.x;
+  float v[4];
+  if (((reinterpret_cast<uintptr_t>(sp) & 15) == 0) && j + 3 < chunk_end) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(sp + j);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (j + e < chunk_end) ? sp[j + e] : 0.f;
+  }
+  uint32_t key[4], cnt = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    key[e] = score_key(v[e]);
+    cnt += (j + e < chunk_end && key[e] >= L) ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t pos = block_exclusive_sum(cnt, &total, scratch);
+  const size_t cidx = sel_chunk_base(a, b) + blockIdx.x;
+  uint32_t* reg = a.ws.region + cidx * kSelChunk * 2;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (j + e < chunk_end && key[e] >= L) {
+      reg[2 * pos] = key[e];
+      reg[2 * pos + 1] = (uint32_t)(j + e);
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) a.ws.counts[cidx] = total;
+}
+
+// ---------------------------------------------------------------- K4: exact selection
+struct FinalShared {
+  uint32_t key[kLdsCand];
+  uint32_t idx[kLdsCand];
+  uint32_t off[kMaxSelChunks + 1];
+  uint32_t hist[256];
+  uint32_t scratch[40];
 };
 
-// Threshold refinement and output, run by the last workgroup of sequence b. The list holds
-// every candidate whose key is in the threshold bin b1 or above: `above` of them above b1.
-template <bool IN_LDS>
-__device__ void final_select(SelectShared& sh, const uint32_t* glist, uint32_t nlist, uint32_t keff,
-                             uint32_t b1, uint32_t above, int32_t* out, int32_t k) {
-  auto KEY = [&](uint32_t i) { return IN_LDS ? sh.key[i] : glist[2 * (size_t)i]; };
-  auto IDX = [&](uint32_t i) { return IN_LDS ? sh.idx[i] : glist[2 * (size_t)i + 1]; };
-  uint32_t tau = 0, idx_thr = 0xFFFFFFFFu;
-  if (nlist > keff) {
-    // Rank of the k-th largest inside bin b1 (1-based, descending).
-    uint32_t r = keff - above;
-    uint32_t prefix = b1;   // known high bits of the threshold key
-    // Passes over key bits [20:10] and [9:0] among candidates sharing the known prefix.
-    const int shifts[2] = {10, 0};
-    const int widths[2] = {11, 10};
-    int known = 11;
-    for (int p = 0; p < 2; ++p) {
-      const int nb = 1 << widths[p];
-      for (int i = threadIdx.x; i < nb; i += kThreads) sh.hist[i] = 0;
+// Superset accessors: LDS (small supersets) or the workspace's global copy.
+struct LdsSet {
+  FinalShared* sh;
+  __device__ uint32_t key(uint32_t i) const { return sh->key[i]; }
+  __device__ uint32_t idx(uint32_t i) const { return sh->idx[i]; }
+};
+struct GlobalSet {
+  const uint32_t* g;
+  __device__ uint32_t key(uint32_t i) const { return g[2 * (size_t)i]; }
+  __device__ uint32_t idx(uint32_t i) const { return g[2 * (size_t)i + 1]; }
+};
+
+// Exact selection of the keff largest (key desc, then position asc) of T candidates held in
+// index order, all with keys in [lo, hi]; writes their indices ascending to out[0..keff) and
+// -1 to out[keff..k).
+template <typename S>
+__device__ void select_exact(const S& set, uint32_t T, uint32_t keff, uint32_t lo, uint32_t hi, int32_t* out,
+                             int32_t k, FinalShared& sh) {
+  uint32_t tau = 0, ties_take = 0xFFFFFFFFu;
+  if (T > keff) {
+    // Bits above `start` are shared by every key in [lo, hi]: skip those radix passes.
+    const int diff_bits = (lo == hi) ? 0 : 32 - __clz(lo ^ hi);
+    const int npass = (diff_bits + 7) / 8;
+    uint32_t r = keff;
+    uint32_t prefix = (npass >= 4) ? 0u : (hi >> (8 * npass));   // the shared high bits
+    for (int p = npass - 1; p >= 0; --p) {
+      const int shift = 8 * p;
+      for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0u;
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < nlist; i += kThreads) {
-        uint32_t kk = KEY(i);
-        if ((kk >> (32 - known)) == prefix) atomicAdd(&sh.hist[(kk >> shifts[p]) & (nb - 1)], 1u);
+      for (uint32_t i = threadIdx.x; i < T; i += blockDim.x) {
+        const uint32_t kk = set.key(i);
+        const bool match = (p == 3) || ((kk >> (shift + 8)) == prefix);
+        if (match) atomicAdd(&sh.hist[(kk >> shift) & 255u], 1u);
       }
       __syncthreads();
-      find_rank_bin(sh.hist, nb, r, true, sh.scratch, sh.scratch + 12);
-      const uint32_t bin = sh.scratch[12], before = sh.scratch[13];
+      top_rank_bin256(sh.hist, r, sh.scratch + 32);
       __syncthreads();
-      r -= before;
-      prefix = (prefix << widths[p]) | bin;
-      known += widths[p];
+      r -= sh.scratch[33];
+      prefix = (prefix << 8) | sh.scratch[32];
+      __syncthreads();
     }
     tau = prefix;
-    // r is now the number of candidates with key == tau to take (1..ties), lowest index first.
-    for (int i = threadIdx.x; i < kBins1; i += kThreads) sh.hist[i] = 0;
-    if (threadIdx.x == 0) sh.scratch[14] = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nlist; i += kThreads)
-      if (KEY(i) == tau) atomicAdd(&sh.scratch[14], 1u);
-    __syncthreads();
-    const uint32_t ties = sh.scratch[14];
-    if (r < ties) {
-      // r-th smallest index among the ties: radix passes over index bits [30:20], [19:10], [9:0].
-      const int ish[3] = {20, 10, 0};
-      const int iw[3] = {11, 10, 10};
-      uint32_t ipre = 0;
-      int iknown = 1;   // bit 31 of an index is always 0
-      for (int p = 0; p < 3; ++p) {
-        const int nb = 1 << iw[p];
-        for (int i = threadIdx.x; i < kBins1; i += kThreads) sh.hist[i] = 0;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < nlist; i += kThreads) {
-          if (KEY(i) != tau) continue;
-          uint32_t ix = IDX(i);
-          if ((ix >> (32 - iknown)) == ipre) atomicAdd(&sh.hist[(ix >> ish[p]) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        find_rank_bin(sh.hist, nb, r, false, sh.scratch, sh.scratch + 12);
-        const uint32_t bin = sh.scratch[12], before = sh.scratch[13];
-        __syncthreads();
-        r -= before;
-        ipre = (ipre << iw[p]) | bin;
-        iknown += iw[p];
-      }
-      idx_thr = ipre;
-    }
+    ties_take = r;   // the first r candidates (in index order) with key == tau are taken
   }
-  // Gather the selection (exactly keff entries), sort ascending, write with -1 padding.
-  if (threadIdx.x == 0) sh.scratch[15] = 0;
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < nlist; i += kThreads) {
-    const uint32_t kk = KEY(i), ix = IDX(i);
-    const bool take = (nlist <= keff) || kk > tau || (kk == tau && ix <= idx_thr);
-    if (take) {
-      uint32_t pos = atomicAdd(&sh.scratch[15], 1u);
-      if (pos < (uint32_t)kMaxK) sh.sorted[pos] = ix;
-    }
+  // Ordered pass: tiles of blockDim.x consecutive candidates, one per thread, with carries.
+  uint32_t ties_before = 0, sel_before = 0;
+  for (uint32_t t0 = 0; t0 < T; t0 += blockDim.x) {
+    const uint32_t i = t0 + threadIdx.x;
+    uint32_t kk = 0, ix = 0;
+    if (i < T) { kk = set.key(i); ix = set.idx(i); }
+    const bool is_tie = i < T && T > keff && kk == tau;
+    uint32_t tie_total;
+    const uint32_t tie_rank = ties_before + block_exclusive_sum(is_tie ? 1u : 0u, &tie_total, sh.scratch);
+    const bool sel = i < T && (T <= keff || kk > tau || (is_tie && tie_rank < ties_take));
+    uint32_t sel_total;
+    const uint32_t pos = sel_before + block_exclusive_sum(sel ? 1u : 0u, &sel_total, sh.scratch);
+    if (sel && pos < keff) out[pos] = (int32_t)ix;
+    ties_before += tie_total;
+    sel_before += sel_total;
   }
-  __syncthreads();
-  const uint32_t cnt = min(sh.scratch[15], (uint32_t)kMaxK);
-  uint32_t P = 1;
-  while (P < cnt) P <<= 1;
-  for (uint32_t i = cnt + threadIdx.x; i < P; i += kThreads) sh.sorted[i] = 0xFFFFFFFFu;
-  __syncthreads();
-  // Bitonic sort of P entries, ascending.
-  for (uint32_t size = 2; size <= P; size <<= 1) {
-    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-      for (uint32_t t = threadIdx.x; t < P / 2; t += kThreads) {
-        const uint32_t i = 2 * t - (t & (stride - 1));
-        const uint32_t jx = i + stride;
-        const bool up = ((i & size) == 0);
-        const uint32_t x = sh.sorted[i], y = sh.sorted[jx];
-        if ((x > y) == up) { sh.sorted[i] = y; sh.sorted[jx] = x; }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = threadIdx.x; i < k; i += kThreads) out[i] = (uint32_t)i < cnt ? (int32_t)sh.sorted[i] : -1;
+  for (int i = (int)keff + threadIdx.x; i < k; i += blockDim.x) out[i] = -1;
 }
 
-__global__ __launch_bounds__(kThreads) void select_kernel(ScoreArgs a, int32_t* topk) {
-  __shared__ SelectShared sh;
-  const int b = blockIdx.y;
+__global__ __launch_bounds__(kFinalThreads) void final_kernel(Args a, int32_t* topk) {
+  __shared__ FinalShared sh;
+  const int b = blockIdx.x;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
-  const int nchunks = n > 0 ? (int)((n + kChunk - 1) / kChunk) : 1;
-  if ((int)blockIdx.x >= nchunks) return;
-  uint32_t* ctrl = a.ws.ctrl + (size_t)b * kCtrlWords;
-  uint32_t* glist = a.ws.list + (size_t)b * a.max_cand * 2;
-  const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
-  const uint32_t b1 = atomic_load_agent(ctrl + kBin1);
-  // Append this chunk's candidates in or above bin b1 to the sequence's list.
-  const float* sp = score_ptr(a, b, c0);
-  const int64_t chunk0 = (int64_t)blockIdx.x * kChunk, chunk_end = min<int64_t>(chunk0 + kChunk, n);
-  for (int64_t j0 = chunk0; j0 < chunk_end; j0 += kThreads) {
-    const int64_t j = j0 + threadIdx.x;
-    uint32_t kk = 0;
-    bool take = false;
-    if (j < chunk_end && keff > 0) {
-      kk = score_key(sp[j]);
-      take = (kk >> 21) >= b1;
-    }
-    uint32_t total;
-    const uint32_t off = block_exclusive_sum(take ? 1u : 0u, &total, sh.scratch);
-    if (total) {
-      if (threadIdx.x == 0) sh.scratch[8] = atomicAdd(ctrl + kListCount, total);
-      __syncthreads();
-      const uint32_t pos = sh.scratch[8] + off;
-      // pos < n <= max_cand whenever the workspace started zeroed; the bound keeps even a
-      // dirty workspace from addressing memory outside the list.
-      if (take && pos < (uint64_t)a.max_cand) {
-        glist[2 * (size_t)pos] = kk;
-        glist[2 * (size_t)pos + 1] = (uint32_t)j;
-      }
-      __syncthreads();
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) sh.scratch[9] = atomicAdd(ctrl + kDoneB, 1u);
-  __syncthreads();
-  if (sh.scratch[9] != (uint32_t)(nchunks - 1)) return;
-  // Last workgroup of sequence b.
-  __threadfence();
-  const uint32_t nlist = (uint32_t)min<int64_t>(atomic_load_agent(ctrl + kListCount), n);
-  const uint32_t above = atomic_load_agent(ctrl + kAbove);
   int32_t* out = topk + (size_t)b * a.k;
-  if (nlist <= (uint32_t)kListLds) {
-    for (uint32_t i = threadIdx.x; i < nlist; i += kThreads) {
-      sh.key[i] = __hip_atomic_load(glist + 2 * (size_t)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sh.idx[i] = __hip_atomic_load(glist + 2 * (size_t)i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
+  if (keff == 0) {
+    for (int i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
+    return;
+  }
+  const int nch = (int)((n + kSelChunk - 1) / kSelChunk);
+  const size_t cb = sel_chunk_base(a, b);
+  // Offsets of the chunk regions in the ordered superset.
+  uint32_t carry = 0;
+  for (int first = 0; first < nch; first += blockDim.x) {
+    const int c = first + threadIdx.x;
+    const uint32_t v = c < nch ? min(a.ws.counts[cb + c], (uint32_t)kSelChunk) : 0u;
+    uint32_t total;
+    const uint32_t ex = block_exclusive_sum(v, &total, sh.scratch);
+    if (c < nch) sh.off[c] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) sh.off[nch] = carry;
+  __syncthreads();
+  const uint32_t T = carry;
+  const uint32_t* reg = a.ws.region + cb * kSelChunk * 2;
+  // Gather: entry e lives in the chunk c with off[c] <= e < off[c+1] (binary search).
+  const bool in_lds = T <= (uint32_t)kLdsCand;
+  uint32_t* gdst = a.ws.gather + (size_t)b * round_cand(a.max_cand) * 2;
+  for (uint32_t e = threadIdx.x; e < T; e += blockDim.x) {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh.off[mid] <= e) lo = mid; else hi = mid - 1;
     }
-    __syncthreads();
-    final_select<true>(sh, glist, nlist, keff, b1, above, out, a.k);
-  } else {
-    final_select<false>(sh, glist, nlist, keff, b1, above, out, a.k);
+    const size_t src = ((size_t)lo * kSelChunk + (e - sh.off[lo])) * 2;
+    const uint32_t kk = reg[src], ix = reg[src + 1];
+    if (in_lds) { sh.key[e] = kk; sh.idx[e] = ix; }
+    else { gdst[2 * (size_t)e] = kk; gdst[2 * (size_t)e + 1] = ix; }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    atomic_store_agent(ctrl + kListCount, 0u);
-    atomic_store_agent(ctrl + kDoneB, 0u);
-    atomic_store_agent(ctrl + kBin1, 0u);
-    atomic_store_agent(ctrl + kAbove, 0u);
-  }
+  const uint32_t lo_key = a.ws.bound[2 * b], hi_key = a.ws.bound[2 * b + 1];
+  if (in_lds) select_exact(LdsSet{&sh}, T, keff, lo_key, hi_key, out, a.k, sh);
+  else select_exact(GlobalSet{gdst}, T, keff, lo_key, hi_key, out, a.k, sh);
 }
 
 template <typename ET, int NH>
-void launch_scores_nh(dim3 grid, hipStream_t s, const ScoreArgs& a, int maxv) {
+void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a, int maxv) {
   switch (maxv) {
-    case 1: hipLaunchKernelGGL((score_hist_kernel<ET, NH, 1>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((score_hist_kernel<ET, NH, 2>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((score_hist_kernel<ET, NH, 4>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((score_kernel<ET, NH, 1>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((score_kernel<ET, NH, 2>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((score_kernel<ET, NH, 4>), grid, dim3(kThreads), 0, s, a); break;
   }
 }
 
 template <typename ET>
-void launch_scores(dim3 grid, hipStream_t s, const ScoreArgs& a, int maxv) {
+void launch_scores(dim3 grid, hipStream_t s, const Args& a, int maxv) {
   if (a.nh <= 1) launch_scores_nh<ET, 1>(grid, s, a, maxv);
   else if (a.nh <= 2) launch_scores_nh<ET, 2>(grid, s, a, maxv);
   else if (a.nh <= 4) launch_scores_nh<ET, 4>(grid, s, a, maxv);
   else if (a.nh <= 8) launch_scores_nh<ET, 8>(grid, s, a, maxv);
   else launch_scores_nh<ET, 16>(grid, s, a, maxv);
+}
+
+// Sub-chunk size: up to 64 candidates, smaller when the longest sequence would otherwise give
+// fewer than 2k maxima, larger (up to a score chunk) when it would give more than kMaxMaxima.
+int pick_subchunk(int64_t max_cand, int32_t k) {
+  int sc = 64;
+  while (sc > 1 && max_cand / sc < 2LL * k) sc >>= 1;
+  while (sc < kScoreChunk && max_cand / sc > kMaxMaxima) sc <<= 1;
+  return sc;
 }
 
 }  // namespace
@@ -527,6 +613,7 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
   if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
   if (batch < 1 || batch > 65535 || k < 1 || k > kMaxK || max_cand < 0 || max_cand >= (1LL << 31))
     return CHS_ERR_SHAPE;
+  if (max_cand > kMaxCand) return CHS_ERR_UNSUPPORTED;
   const size_t es = elem_size(dtype);
   int nvec = 0, lpc = 1, maxv = 1;
   if (q_idx) {
@@ -547,19 +634,27 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
   Workspace ws;
   const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
-  ScoreArgs a;
+  Args a;
   a.q = q_idx; a.w = w; a.keys = k_idx; a.cu = cu_cand; a.max_cand = max_cand;
-  a.nh = n_heads; a.dim = head_dim; a.nvec = nvec; a.lpc = lpc; a.scores = scores; a.ws = ws; a.k = k;
-  const int64_t chunks = max_cand > 0 ? (max_cand + kChunk - 1) / kChunk : 1;
-  dim3 grid((unsigned)chunks, (unsigned)batch);
+  a.nh = n_heads; a.nvec = nvec; a.lpc = lpc; a.k = k; a.scores = scores; a.ws = ws;
+  a.sc = pick_subchunk(max_cand, k);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_idx) {
-    if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, a, maxv);
-    else launch_scores<float>(grid, s, a, maxv);
-  } else {
-    hipLaunchKernelGGL(hist_kernel, grid, dim3(kThreads), 0, s, a);
+  if (max_cand > 0) {
+    if (q_idx) {
+      const dim3 grid((unsigned)((max_cand + kScoreChunk - 1) / kScoreChunk), (unsigned)batch);
+      if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, a, maxv);
+      else launch_scores<float>(grid, s, a, maxv);
+    } else {
+      const dim3 grid((unsigned)((max_cand + kMaxChunk - 1) / kMaxChunk), (unsigned)batch);
+      hipLaunchKernelGGL(max_kernel, grid, dim3(kThreads), 0, s, a);
+    }
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+    hipLaunchKernelGGL(bound_kernel, dim3((unsigned)batch), dim3(kBoundThreads), 0, s, a);
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+    const dim3 sgrid((unsigned)((max_cand + kSelChunk - 1) / kSelChunk), (unsigned)batch);
+    hipLaunchKernelGGL(select_kernel, sgrid, dim3(kThreads), 0, s, a);
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   }
-  if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), 0, s, a, topk);
+  hipLaunchKernelGGL(final_kernel, dim3((unsigned)batch), dim3(kFinalThreads), 0, s, a, topk);
   return launch_status();
 }

@@ -35,8 +35,8 @@
  *    skipped as each call documents, never used to address memory outside the stated buffers.
  *  - A failed launch returns CHS_ERR_LAUNCH. Faults inside a kernel surface, as usual for HIP,
  *    at the caller's next synchronization.
- *  - Workspaces must be zero-filled before their first use (chs_workspace_clear does that on a
- *    stream); every call that completes leaves its workspace zero-filled again. Calls that run
+ *  - Workspaces are scratch memory the caller owns, sized by the matching *_workspace_size
+ *    query. They need no initialisation and hold nothing between calls; calls that run
  *    concurrently must use distinct workspaces. No global mutable state exists.
  *  - dtype CHS_BF16 means bfloat16 storage with fp32 arithmetic; CHS_F32 means fp32 throughout.
  */
@@ -68,8 +68,9 @@ int32_t chs_version(void);
 /* Human-readable name of a status code (static storage). */
 const char* chs_status_string(chs_status s);
 
-/* Zero-fill `bytes` bytes of a workspace on `stream` with a kernel (no hipMemsetAsync, so it
- * can be captured in a HIP graph). bytes must be a multiple of 4. */
+/* Zero-fill `bytes` bytes of device memory on `stream` with a kernel (no hipMemsetAsync, so it
+ * can be captured in a HIP graph). bytes must be a multiple of 4. Not needed by the calls below;
+ * a convenience for callers that want deterministic scratch contents. */
 chs_status chs_workspace_clear(void* workspace, size_t bytes, void* stream);
 
 /* ---- chs_compress: the fused group softmax-pool (Flash Compressor's role) ----------------
@@ -113,8 +114,9 @@ chs_status chs_compress(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, co
  * scores  : [cu_cand[batch]] fp32. OUTPUT when q_idx != NULL (may then be NULL: the workspace
  *           holds them), INPUT when q_idx == NULL.
  * topk    : [batch, k] int32 output.
- * workspace: chs_index_topk_workspace_size(batch, max_cand, k) bytes (zero-filled, see above).
- * Ranges: 1 <= batch <= 65535; 1 <= k <= 2048; 0 <= max_cand < 2^31; with q_idx:
+ * workspace: chs_index_topk_workspace_size(batch, max_cand, k) bytes.
+ * Ranges: 1 <= batch <= 65535; 1 <= k <= 2048; 0 <= max_cand <= 4194304 (CHS_ERR_UNSUPPORTED
+ *   above); with q_idx:
  *   1 <= n_heads <= 16, 8 <= head_dim <= 512, head_dim*elem_size % 16 == 0. */
 size_t chs_index_topk_workspace_size(int32_t batch, int64_t max_cand, int32_t k);
 chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
@@ -143,7 +145,7 @@ chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads, int32
  * max_comp (host): an upper bound on max_b G_b (sizes the grid for the dense form).
  * out     : [batch, n_heads, d] fp32;  lse: [batch, n_heads] fp32, or NULL.
  * workspace: chs_decode_attn_workspace_size(...) bytes with the same window, k (0 for dense),
- *           max_comp, batch, n_heads and d (zero-filled, see above).
+ *           max_comp, batch, n_heads and d.
  * Ranges: 1 <= batch <= 65535; 1 <= n_heads <= 128; 0 <= window <= 4096; 0 <= k <= 2048;
  *   scale finite and > 0; bf16: d in {64, 128, 256, 512}; f32: 1 <= d <= 1024, d % 4 == 0. */
 size_t chs_decode_attn_workspace_size(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
