@@ -9,47 +9,45 @@
 // The pages' design reduces per-CTA histograms inside a thread-block cluster through
 // distributed shared memory, which gfx950 does not have; on MI355X a device-scope fence costs
 // tens of nanoseconds per workgroup, serialised, and same-address atomics about ten. So no
-// kernel here synchronises workgroups with each other: every cross-workgroup step is a kernel
-// boundary, and the data crossing it is written with plain stores.
-//
-//   K1 score_kernel (one workgroup per 128 candidates, many resident per CU): streams the
-//      index keys once (non-temporal 16-byte loads, v_dot2_f32_bf16 or fp32 FMAs, DPP lane
-//      reductions), writes the fp32 scores, and writes the maximum order-preserving key of
-//      every sub-chunk of SC consecutive candidates. max_kernel does only the maxima, for
-//      caller-provided scores.
-//   K2 bound_kernel (one workgroup per sequence): L = the k-th largest sub-chunk maximum
-//      (radix select in LDS over at most 16384 maxima, rounded down to 22 key bits). L never
-//      exceeds the k-th largest score: k disjoint sub-chunks each hold a score >= L. So every
-//      top-k candidate, and every tie at the threshold, has key >= L. Also the largest key.
-//   K3 select_kernel (one workgroup per 1024 candidates): writes the chunk's candidates with
-//      key >= L, in index order, to the chunk's own region, and their count.
-//   K4 final_kernel (one workgroup per sequence): gathers the regions in chunk order (so in
-//      index order), finds the exact k-th largest key tau by 8-bit radix passes over the bits
-//      below the prefix that L and the largest key share, takes every key above tau and the
-//      first ties at tau in index order, and writes the selection ascending by a prefix count:
-//      no sort is needed. If the superset exceeds the LDS capacity (heavy ties, adversarial
-//      inputs), the same passes stream from a global copy instead.
+// kernel here synchronises workgroups with each other; kernel boundaries order the phases:
+//   K1 score_kernel (persistent grid, query slices in registers, next chunk's loads issued
+//      before the current chunk is scored) streams the index keys once and writes the fp32
+//      scores plus a maximum order-preserving key per group of candidates; max_kernel does
+//      the same for caller-provided scores.
+//   K2 bound_kernel (one workgroup per sequence): L = k-th largest group maximum, a lower
+//      bound on the k-th largest score (k disjoint groups each hold a score >= L).
+//   K3 select_kernel: every chunk of 1024 candidates keeps the ones with key >= L in index
+//      order and writes them, with their count, to its own region.
+//   K4 final_kernel (one workgroup per sequence): gathers the regions and selects exactly,
+//      by one-at-a-time removal when the superset exceeds k by at most 64, else by radix
+//      steps to the k-th largest key tau and an ordered pass (keys above tau, then the first
+//      ties at tau), written ascending by a prefix count.
 // The composite order (key descending, then index ascending) is total, so the selected set is
 // unique and bit-identical to a full sort of the same scores.
+#include <algorithm>
+
 #include "common.h"
 
 namespace chs {
 namespace {
 
-constexpr int kThreads = 256;        // K1, K3
-constexpr int kBoundThreads = 1024;  // K2
-constexpr int kFinalThreads = 512;   // K4
-constexpr int kScoreChunk = 128;     // candidates per K1 workgroup
-constexpr int kMaxChunk = 2048;      // scores per max_kernel workgroup (256 threads x 8)
+constexpr int kThreads = 256;        // every kernel here
+constexpr int kPasses = 8;           // K1 passes per chunk (one 16-byte load each per lane)
+constexpr int kScoreGrid = 1024;     // K1 workgroups per launch (all sequences together)
+constexpr int kMaxChunk = 2048;      // scores per max_kernel chunk (256 threads x 8)
 constexpr int kSelChunk = 1024;      // candidates per K3 workgroup (256 threads x 4)
-constexpr int kMaxMaxima = 16384;    // sub-chunk maxima K2 ranks (LDS)
+constexpr int kMaxMaxima = 8192;     // group maxima K2 ranks (the first ones if more)
 constexpr int kLdsCand = 8192;       // superset size K4 keeps in LDS
 constexpr int kMaxSelChunks = 4096;  // K3 chunks per sequence (max_cand <= 4M)
+constexpr int kPeekChunks = 512;     // K4 fetches region heads with the counts up to this many chunks
+constexpr int kPeek = 8;             // entries per region head
+constexpr int kRemoveMax = 64;       // K4 removes one by one when T - k <= this
 constexpr int kMaxK = 2048;
+constexpr int kRegMax = (kMaxK + kRemoveMax + 63) / 64;   // superset entries per lane (removal path)
 constexpr int64_t kMaxCand = (int64_t)kMaxSelChunks * kSelChunk;
 
 struct Workspace {
-  uint32_t* maxima;   // [batch][rc]: sub-chunk maximum keys, sub-chunk j at index j
+  uint32_t* maxima;   // [batch][rc]: group maximum keys
   uint32_t* bound;    // [batch][2]: L, largest key
   uint32_t* counts;   // [batch][rc / kSelChunk]
   uint32_t* region;   // [batch][rc][2]: per K3 chunk, (key, index) in index order
@@ -97,7 +95,8 @@ struct Args {
   const int64_t* cu;    // [batch+1]
   int64_t max_cand;
   int32_t nh, nvec, lpc;
-  int32_t sc;           // sub-chunk size (power of two, at most kScoreChunk)
+  int32_t chunk;        // K1 candidates per chunk
+  int32_t gpc;          // group maxima per K1 chunk: score 1, 4 or 32; max 1, 4 or 16
   int32_t k;
   float* scores;        // caller's packed array, or NULL -> workspace
   Workspace ws;
@@ -121,9 +120,9 @@ __device__ __forceinline__ size_t sel_chunk_base(const Args& a, int b) {
   return (size_t)b * (size_t)(round_cand(a.max_cand) / kSelChunk);
 }
 
-// ---------------------------------------------------------------- block scans
-// Exclusive prefix sum over blockDim.x (a multiple of 64, at most 1024) threads.
-// scratch: at least blockDim.x / 64 words. Returns the exclusive prefix; *total gets the sum.
+// ---------------------------------------------------------------- reductions and scans
+// Exclusive prefix sum over blockDim.x (a multiple of 64) threads; scratch: blockDim.x / 64
+// words. Returns the exclusive prefix; *total gets the sum.
 __device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   uint32_t inc = v;
@@ -145,12 +144,16 @@ __device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* s
   return before + inc - v;
 }
 
-// Block-wide maximum (blockDim.x a multiple of 64); scratch as above.
-__device__ uint32_t block_max(uint32_t v, uint32_t* scratch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  if (lane == 0) scratch[wave] = v;
+  for (int o = 1; o < 64; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+__device__ uint32_t block_max(uint32_t v, uint32_t* scratch) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) scratch[wave] = v;
   __syncthreads();
   uint32_t all = 0;
   for (int w = 0; w < nw; ++w) all = max(all, scratch[w]);
@@ -158,33 +161,79 @@ __device__ uint32_t block_max(uint32_t v, uint32_t* scratch) {
   return all;
 }
 
-// Given a 256-bin histogram and a rank r >= 1 counted from the top, wave 0 finds the bin that
-// holds the r-th largest element and the count strictly above it; results in out[0], out[1].
-__device__ void top_rank_bin256(const uint32_t* hist, uint32_t r, uint32_t* out) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    // Lane l owns bins 255-4l .. 252-4l (descending scan order).
-    uint32_t c[4], local = 0;
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; local += c[i]; }
-    uint32_t inc = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += t;
-    }
-    uint32_t run = inc - local;
-    if (run < r && inc >= r) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (run + c[i] >= r) { out[0] = 255 - 4 * lane - i; out[1] = run; break; }
-        run += c[i];
-      }
-    }
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
   }
+  return v;
 }
 
-// ---------------------------------------------------------------- K1: scores + sub-chunk maxima
+// Radix digits below the bits shared by every key in [lo, hi]: the first digit covers the
+// top `width` differing bits. Returns the number of differing bits.
+__device__ __forceinline__ int differing_bits(uint32_t lo, uint32_t hi) {
+  return lo == hi ? 0 : 32 - __clz(lo ^ hi);
+}
+
+// One radix step over `m` keys (from `get`) that all share their bits above `shift + width`:
+// histogram (nb >= 2^width bins, nb = 8 * blockDim.x... see callers) of the `width`-bit digit
+// at `shift` over keys whose bits from `shift + width` up equal `prefix`, then the digit
+// holding the r-th largest. Returns the digit; *above gets the count with larger digits.
+template <typename Get>
+__device__ uint32_t radix_step(Get get, uint32_t m, int shift, int width, uint32_t prefix, uint32_t r,
+                               uint32_t* hist, uint32_t* scratch, uint32_t* above) {
+  const int nb = 1 << width;                       // width <= 11: at most 2048 bins
+  for (int i = threadIdx.x; i < 2048; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < m; i += blockDim.x) {
+    const uint32_t v = get(i);
+    if ((uint32_t)((uint64_t)v >> (shift + width)) == prefix) atomicAdd(&hist[(v >> shift) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  // Thread t owns digits 2047-8t .. 2040-8t (descending).
+  uint32_t c[8], local = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { c[i] = hist[2047 - 8 * threadIdx.x - i]; local += c[i]; }
+  uint32_t total;
+  uint32_t run = block_exclusive_sum(local, &total, scratch);
+  if (run < r && run + local >= r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (run + c[i] >= r) { scratch[32] = 2047 - 8 * threadIdx.x - i; scratch[33] = run; break; }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t digit = scratch[32];
+  *above = scratch[33];
+  __syncthreads();
+  return digit;
+}
+
+// The r-th largest of m keys in [lo, hi] (1 <= r <= m), by 11-bit radix steps below the bits
+// lo and hi share; `steps` caps the number of steps (lower bits are then returned as 0, so the
+// result is rounded down). *rank_left gets r minus the number of keys above the result's
+// last-resolved digit (the rank among keys equal to the result when all bits are resolved).
+template <typename Get>
+__device__ uint32_t radix_select_desc(Get get, uint32_t m, uint32_t r, uint32_t lo, uint32_t hi, int steps,
+                                      uint32_t* hist, uint32_t* scratch, uint32_t* rank_left) {
+  int rem = differing_bits(lo, hi);
+  uint32_t prefix = rem == 32 ? 0u : (uint32_t)((uint64_t)hi >> rem);
+  for (int s = 0; s < steps && rem > 0; ++s) {
+    const int width = rem < 11 ? rem : 11;
+    rem -= width;
+    uint32_t above;
+    const uint32_t d = radix_step(get, m, rem, width, prefix, r, hist, scratch, &above);
+    r -= above;
+    prefix = (prefix << width) | d;
+  }
+  *rank_left = r;
+  return (uint32_t)((uint64_t)prefix << rem);
+}
+
+// ---------------------------------------------------------------- K1: scores + group maxima
 template <typename ET>
 struct Dot16;
 
@@ -194,7 +243,8 @@ struct Dot16<uint16_t> {   // 8 bf16 per 16 bytes: four v_dot2_f32_bf16
   // Element j is copied to a scalar before the bit cast: clang lowers a bit cast applied
   // directly to an ext-vector element access as a cast of element 0.
   __device__ static bf16x2 pair(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
-  __device__ static float dot(const u32x4& a, const u32x4& b, float acc) {
+  __device__ static float dot(const u32x4& a, const u32x4& b) {
+    float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t x = a[j], y = b[j];
@@ -206,7 +256,8 @@ struct Dot16<uint16_t> {   // 8 bf16 per 16 bytes: four v_dot2_f32_bf16
 
 template <>
 struct Dot16<float> {      // 4 fp32 per 16 bytes
-  __device__ static float dot(const u32x4& a, const u32x4& b, float acc) {
+  __device__ static float dot(const u32x4& a, const u32x4& b) {
+    float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t x = a[j], y = b[j];
@@ -216,193 +267,192 @@ struct Dot16<float> {      // 4 fp32 per 16 bytes
   }
 };
 
-// Sum over groups of `lpc` adjacent lanes (lpc a power of two <= 64); every lane of a group
-// ends with the group total. Within a row of 16 lanes this uses DPP lane swizzles.
-__device__ __forceinline__ float group_sum(float v, int lpc) {
-  if (lpc >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // xor 1
-  if (lpc >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // xor 2
-  if (lpc >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // half-row mirror
-  if (lpc >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)); // row mirror
-  if (lpc >= 32) v += __shfl_xor(v, 16, 64);
-  if (lpc >= 64) v += __shfl_xor(v, 32, 64);
+// Sum over groups of LPC adjacent lanes (a power of two <= 64); every lane of a group ends
+// with the group total. Within a row of 16 lanes this uses DPP lane swizzles.
+template <int LPC>
+__device__ __forceinline__ float group_sum(float v) {
+  if (LPC >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // xor 1
+  if (LPC >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // xor 2
+  if (LPC >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // half-row mirror
+  if (LPC >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)); // row mirror
+  if (LPC >= 32) v += __shfl_xor(v, 16, 64);
+  if (LPC >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
 
-// Write the maxima of the sub-chunks that [j0, j1) covers (j0 a multiple of sc; LDS holds them
-// from index 0).
-__device__ __forceinline__ void store_maxima(const Args& a, int b, int64_t j0, int64_t j1, const uint32_t* smax) {
-  const int cnt = (int)((j1 - j0 + a.sc - 1) / a.sc);
-  uint32_t* g = maxima_ptr(a, b) + j0 / a.sc;
-  for (int i = threadIdx.x; i < cnt; i += blockDim.x) g[i] = smax[i];
+template <int LPC>
+__device__ __forceinline__ void load_chunk(const u32x4* kb, int nvec, int64_t chunk0, int64_t n, int slot, int sub,
+                                           u32x4 (&kv)[kPasses]) {
+  constexpr int PER = kThreads / LPC;
+#pragma unroll
+  for (int u = 0; u < kPasses; ++u) {
+    const int64_t j = chunk0 + u * PER + slot;
+    kv[u] = (j < n && sub < nvec) ? __builtin_nontemporal_load(kb + j * nvec + sub) : u32x4{0, 0, 0, 0};
+  }
 }
 
-template <typename ET, int NH, int MAXV>
+// Score one chunk from registers; write scores and the chunk's group maxima.
+template <typename ET, int NH, int LPC>
+__device__ __forceinline__ void score_chunk(const Args& a, int64_t chunk, int64_t n, int slot, int sub,
+                                            const u32x4 (&qv)[NH], const float (&wv)[NH], const u32x4 (&kv)[kPasses],
+                                            float* sp, uint32_t* gmax, uint32_t* smax) {
+  constexpr int PER = kThreads / LPC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t mx = 0;
+#pragma unroll
+  for (int u = 0; u < kPasses; ++u) {
+    const int64_t j = chunk * a.chunk + u * PER + slot;
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s = fmaf(wv[h], fmaxf(group_sum<LPC>(Dot16<ET>::dot(qv[h], kv[u])), 0.f), s);
+    const bool valid = j < n;
+    if (sub == 0 && valid) sp[j] = s;
+    const uint32_t key = valid ? score_key(s) : 0u;   // 0: below every key
+    if (a.gpc == 32) {                                 // group = this wave's candidates of pass u
+      const uint32_t m = wave_max(key);
+      if (lane == 0) gmax[(chunk * 4 + wave) * kPasses + u] = m;
+    }
+    mx = max(mx, key);
+  }
+  if (a.gpc == 4) {                                    // group = this wave's candidates of the chunk
+    const uint32_t m = wave_max(mx);
+    if (lane == 0) gmax[chunk * 4 + wave] = m;
+  } else if (a.gpc == 1) {                             // group = the chunk
+    const uint32_t m = wave_max(mx);
+    if (lane == 0) smax[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) gmax[chunk] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
+    __syncthreads();
+  }
+}
+
+template <typename ET, int NH, int LPC>
 __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
-  __shared__ uint32_t smax[kScoreChunk];
+  constexpr int PER = kThreads / LPC;
+  __shared__ uint32_t smax[4];
   const int b = blockIdx.y;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
-  const int64_t chunk0 = (int64_t)blockIdx.x * kScoreChunk;
-  if (chunk0 >= n) return;
-  const int64_t chunk_end = min<int64_t>(chunk0 + kScoreChunk, n);
-  if (threadIdx.x < kScoreChunk) smax[threadIdx.x] = 0u;   // 0: below every key
-
+  const int64_t nch = (n + a.chunk - 1) / a.chunk;
+  int64_t chunk = blockIdx.x;
+  if (chunk >= nch) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lpc = a.lpc;
-  const int sub = lane & (lpc - 1);
-  const int slot = (wave * 64 + lane) / lpc;          // candidate slot within a pass
-  const int per_pass = kThreads / lpc;
+  const int sub = lane & (LPC - 1);
+  const int slot = (wave * 64 + lane) / LPC;          // candidate slot within a pass
   const u32x4* kb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.keys) + (size_t)c0 * a.nvec * 16);
-  // Issue the chunk's key loads first (U passes of per_pass candidates), then the query slices.
-  constexpr int U = 4;
-  u32x4 kv[U][MAXV];
-  int64_t j[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    j[u] = chunk0 + u * per_pass + slot;
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v) {
-      const int vi = sub + v * lpc;
-      kv[u][v] = (j[u] < chunk_end && vi < a.nvec) ? __builtin_nontemporal_load(kb + j[u] * a.nvec + vi)
-                                                   : u32x4{0, 0, 0, 0};
-    }
-  }
-  u32x4 qv[NH][MAXV];                                 // this lane's slice of every query
+  u32x4 ka[kPasses], kc[kPasses];
+  load_chunk<LPC>(kb, a.nvec, chunk * a.chunk, n, slot, sub, ka);
+  u32x4 qv[NH];                                       // this lane's 16 bytes of every query
   float wv[NH];
-  const u32x4* qb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
-                                                   (size_t)b * a.nh * a.nvec * 16);
+  const u32x4* qb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + (size_t)b * a.nh * a.nvec * 16);
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     wv[h] = h < a.nh ? a.w[(size_t)b * a.nh + h] : 0.f;
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v) {
-      const int vi = sub + v * lpc;
-      qv[h][v] = (h < a.nh && vi < a.nvec) ? qb[h * a.nvec + vi] : u32x4{0, 0, 0, 0};
-    }
+    qv[h] = (h < a.nh && sub < a.nvec) ? qb[h * a.nvec + sub] : u32x4{0, 0, 0, 0};
   }
-  __syncthreads();
   float* sp = score_ptr(a, b, c0);
-  // per_pass * U >= kScoreChunk whenever lpc <= 8; wider rows take more rounds.
-  for (int64_t base = chunk0; base < chunk_end; base += per_pass * U) {
-    if (base != chunk0) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        j[u] = base + u * per_pass + slot;
-#pragma unroll
-        for (int v = 0; v < MAXV; ++v) {
-          const int vi = sub + v * lpc;
-          kv[u][v] = (j[u] < chunk_end && vi < a.nvec) ? __builtin_nontemporal_load(kb + j[u] * a.nvec + vi)
-                                                       : u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float s = 0.f;
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        float dot = 0.f;
-#pragma unroll
-        for (int v = 0; v < MAXV; ++v) dot = Dot16<ET>::dot(qv[h][v], kv[u][v], dot);
-        dot = group_sum(dot, lpc);
-        s = fmaf(wv[h], fmaxf(dot, 0.f), s);
-      }
-      if (sub == 0 && j[u] < chunk_end) {
-        sp[j[u]] = s;
-        atomicMax(&smax[(int)(j[u] - chunk0) / a.sc], score_key(s));
-      }
-    }
+  uint32_t* gmax = maxima_ptr(a, b);
+  (void)PER;
+  // Two register buffers: the next chunk's loads are in flight while the current one is scored.
+  for (;;) {
+    const int64_t next = chunk + gridDim.x;
+    if (next < nch) load_chunk<LPC>(kb, a.nvec, next * a.chunk, n, slot, sub, kc);
+    score_chunk<ET, NH, LPC>(a, chunk, n, slot, sub, qv, wv, ka, sp, gmax, smax);
+    if (next >= nch) break;
+    chunk = next;
+    const int64_t next2 = chunk + gridDim.x;
+    if (next2 < nch) load_chunk<LPC>(kb, a.nvec, next2 * a.chunk, n, slot, sub, ka);
+    score_chunk<ET, NH, LPC>(a, chunk, n, slot, sub, qv, wv, kc, sp, gmax, smax);
+    if (next2 >= nch) break;
+    chunk = next2;
   }
-  __syncthreads();
-  store_maxima(a, b, chunk0, chunk_end, smax);
 }
 
-// K1 for caller-provided scores: sub-chunk maxima only (8 scores per thread, 16-byte loads
-// when the row is 16-byte aligned).
+// K1 for caller-provided scores: group maxima only. Chunks of 2048 scores (8 per thread, two
+// 16-byte loads); a group is a chunk, a wave's 512 scores, or a 16-lane row's 128 scores.
 __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
-  __shared__ uint32_t smax[kMaxChunk];
+  __shared__ uint32_t smax[4];
   const int b = blockIdx.y;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
-  const int64_t chunk0 = (int64_t)blockIdx.x * kMaxChunk;
-  if (chunk0 >= n) return;
-  const int64_t chunk_end = min<int64_t>(chunk0 + kMaxChunk, n);
-  for (int i = threadIdx.x; i < kMaxChunk; i += kThreads) smax[i] = 0u;
+  const int64_t nch = (n + kMaxChunk - 1) / kMaxChunk;
   const float* sp = score_ptr(a, b, c0);
-  float v[8];
-  const int64_t j = chunk0 + 4 * threadIdx.x;   // this thread: j..j+3 and j+1024..j+1027
+  uint32_t* gmax = maxima_ptr(a, b);
   const bool vec = ((reinterpret_cast<uintptr_t>(sp) & 15) == 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t chunk = blockIdx.x; chunk < nch; chunk += gridDim.x) {
+    const int64_t chunk0 = chunk * kMaxChunk;
+    uint32_t m = 0;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t jj = j + h * 1024;
-    if (vec && jj + 3 < chunk_end) {
-      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + jj));
-      v[4 * h] = x[0]; v[4 * h + 1] = x[1]; v[4 * h + 2] = x[2]; v[4 * h + 3] = x[3];
+    for (int h = 0; h < 2; ++h) {
+      const int64_t j = chunk0 + h * 1024 + 4 * threadIdx.x;
+      float v[4];
+      if (vec && j + 3 < n) {
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + j));
+        v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (j + e < n) ? sp[j + e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = max(m, (j + e < n) ? score_key(v[e]) : 0u);
+    }
+    if (a.gpc == 16) {
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));
+      if ((lane & 15) == 0) gmax[chunk * 16 + wave * 4 + (lane >> 4)] = m;
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * h + e] = (jj + e < chunk_end) ? sp[jj + e] : 0.f;
+      m = wave_max(m);
+      if (a.gpc == 4) {
+        if (lane == 0) gmax[chunk * 4 + wave] = m;
+      } else {
+        if (lane == 0) smax[wave] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) gmax[chunk] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
+        __syncthreads();
+      }
     }
   }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t jj = j + h * 1024 + e;
-      if (jj < chunk_end) atomicMax(&smax[(int)(jj - chunk0) / a.sc], score_key(v[4 * h + e]));
-    }
-  __syncthreads();
-  store_maxima(a, b, chunk0, chunk_end, smax);
 }
 
 // ---------------------------------------------------------------- K2: the bound L
-// L = the k-th largest of the sequence's sub-chunk maxima (the first kMaxMaxima of them when
-// there are more: any k disjoint sub-chunks give a valid bound), rounded down to its top 22
-// bits; 0 (no pruning) when there are fewer than k maxima. Also the largest maximum, which is
-// the largest key of the sequence.
-__global__ __launch_bounds__(kBoundThreads) void bound_kernel(Args a) {
-  __shared__ uint32_t vals[kMaxMaxima];
+__global__ __launch_bounds__(kThreads) void bound_kernel(Args a) {
+  constexpr int PER = kMaxMaxima / kThreads;   // 32 maxima per thread, in registers
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scratch[40];
   const int b = blockIdx.x;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
   const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
-  const int64_t m_all = (n + a.sc - 1) / a.sc;
-  const int m = (int)min<int64_t>(m_all, kMaxMaxima);
+  const int64_t m_all = (n + a.chunk - 1) / a.chunk * a.gpc;
+  const int m = (int)min<int64_t>(m_all, kMaxMaxima);   // any k disjoint groups give a bound
   const uint32_t* g = maxima_ptr(a, b);
-  uint32_t vmax = 0;
-  for (int i = threadIdx.x; i < m; i += kBoundThreads) { vals[i] = g[i]; vmax = max(vmax, vals[i]); }
-  vmax = block_max(vmax, scratch);   // (the maxima beyond kMaxMaxima only matter for pruning)
-  if (m_all > m) {
-    for (int64_t i = m + threadIdx.x; i < m_all; i += kBoundThreads) vmax = max(vmax, g[i]);
-    vmax = block_max(vmax, scratch);
+  uint32_t v[PER];
+  uint32_t vmax = 0, vmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = i * kThreads + threadIdx.x;
+    v[i] = e < m ? g[e] : 0u;
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (i * kThreads + (int)threadIdx.x < m) { vmax = max(vmax, v[i]); vmin = min(vmin, v[i]); }
+  }
+  for (int64_t e = kMaxMaxima + threadIdx.x; e < m_all; e += kThreads) vmax = max(vmax, g[e]);
+  vmax = block_max(vmax, scratch);
+  vmin = ~block_max(~vmin, scratch);
   uint32_t L = 0;
-  if (n > (int64_t)keff && m_all >= (int64_t)keff && keff > 0) {
-    uint32_t prefix = 0, r = keff;
-    for (int p = 0; p < 2; ++p) {
-      const int shift = p == 0 ? 21 : 10;
-      for (int i = threadIdx.x; i < 2048; i += kBoundThreads) hist[i] = 0u;
-      __syncthreads();
-      for (int i = threadIdx.x; i < m; i += kBoundThreads) {
-        const uint32_t v = vals[i];
-        if (p == 0 || (v >> 21) == prefix) atomicAdd(&hist[(v >> shift) & 2047u], 1u);
-      }
-      __syncthreads();
-      // The bin of the r-th largest: each thread owns 2 bins in descending order.
-      const uint32_t c1 = hist[2047 - 2 * threadIdx.x], c2 = hist[2046 - 2 * threadIdx.x];
-      uint32_t total;
-      const uint32_t run = block_exclusive_sum(c1 + c2, &total, scratch);
-      if (run < r && run + c1 >= r) { scratch[32] = 2047 - 2 * threadIdx.x; scratch[33] = run; }
-      else if (run + c1 < r && run + c1 + c2 >= r) { scratch[32] = 2046 - 2 * threadIdx.x; scratch[33] = run + c1; }
-      __syncthreads();
-      const uint32_t bin = scratch[32];
-      r -= scratch[33];
-      prefix = (p == 0) ? bin : ((prefix << 11) | bin);
-      __syncthreads();
-    }
-    L = prefix << 10;
+  if (n > (int64_t)keff && m >= (int)keff && keff > 0) {
+    // The maxima go through LDS once for the two radix steps.
+    __shared__ uint32_t vals[kMaxMaxima];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) vals[i * kThreads + threadIdx.x] = v[i];
+    __syncthreads();
+    uint32_t rank_left;
+    L = radix_select_desc([&](uint32_t i) { return vals[i]; }, (uint32_t)m, keff, vmin, vmax, 2, hist, scratch,
+                          &rank_left);
   }
   if (threadIdx.x == 0) { a.ws.bound[2 * b] = L; a.ws.bound[2 * b + 1] = vmax; }
 }
@@ -454,91 +504,105 @@ struct FinalShared {
   uint32_t key[kLdsCand];
   uint32_t idx[kLdsCand];
   uint32_t off[kMaxSelChunks + 1];
-  uint32_t hist[256];
+  uint32_t hist[2048];
   uint32_t scratch[40];
 };
 
-// Superset accessors: LDS (small supersets) or the workspace's global copy.
-struct LdsSet {
-  FinalShared* sh;
-  __device__ uint32_t key(uint32_t i) const { return sh->key[i]; }
-  __device__ uint32_t idx(uint32_t i) const { return sh->idx[i]; }
-};
-struct GlobalSet {
-  const uint32_t* g;
-  __device__ uint32_t key(uint32_t i) const { return g[2 * (size_t)i]; }
-  __device__ uint32_t idx(uint32_t i) const { return g[2 * (size_t)i + 1]; }
-};
-
-// Exact selection of the keff largest (key desc, then position asc) of T candidates held in
-// index order, all with keys in [lo, hi]; writes their indices ascending to out[0..keff) and
-// -1 to out[keff..k).
-template <typename S>
-__device__ void select_exact(const S& set, uint32_t T, uint32_t keff, uint32_t lo, uint32_t hi, int32_t* out,
-                             int32_t k, FinalShared& sh) {
-  uint32_t tau = 0, ties_take = 0xFFFFFFFFu;
-  if (T > keff) {
-    // Bits above `start` are shared by every key in [lo, hi]: skip those radix passes.
-    const int diff_bits = (lo == hi) ? 0 : 32 - __clz(lo ^ hi);
-    const int npass = (diff_bits + 7) / 8;
-    uint32_t r = keff;
-    uint32_t prefix = (npass >= 4) ? 0u : (hi >> (8 * npass));   // the shared high bits
-    for (int p = npass - 1; p >= 0; --p) {
-      const int shift = 8 * p;
-      for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0u;
-      __syncthreads();
-      for (uint32_t i = threadIdx.x; i < T; i += blockDim.x) {
-        const uint32_t kk = set.key(i);
-        const bool match = (p == 3) || ((kk >> (shift + 8)) == prefix);
-        if (match) atomicAdd(&sh.hist[(kk >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      top_rank_bin256(sh.hist, r, sh.scratch + 32);
-      __syncthreads();
-      r -= sh.scratch[33];
-      prefix = (prefix << 8) | sh.scratch[32];
-      __syncthreads();
-    }
-    tau = prefix;
-    ties_take = r;   // the first r candidates (in index order) with key == tau are taken
+// Keep the first `keff` of T candidates (index order) in the composite order (key desc, then
+// position asc); write their indices ascending. Case T - keff <= kRemoveMax, by wave 0 alone:
+// remove the smallest candidate T - keff times.
+__device__ void select_by_removal(const FinalShared& sh, uint32_t T, uint32_t keff, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t E = (T + 63) / 64;   // <= kRegMax
+  const uint32_t i0 = min(T, lane * E);
+  uint64_t comp[kRegMax];             // (key, position from the end): the minimum goes first
+#pragma unroll
+  for (int i = 0; i < kRegMax; ++i) {
+    const uint32_t e = i0 + i;
+    comp[i] = (i < (int)E && e < T) ? (((uint64_t)sh.key[e] << 32) | (uint64_t)(0xFFFFFFFFu - e)) : ~0ull;
   }
-  // Ordered pass: tiles of blockDim.x consecutive candidates, one per thread, with carries.
+  for (uint32_t rnd = keff; rnd < T; ++rnd) {
+    uint64_t mn = ~0ull;
+    int at = -1;
+#pragma unroll
+    for (int i = 0; i < kRegMax; ++i) if (comp[i] < mn) { mn = comp[i]; at = i; }
+    uint64_t w = mn;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t t = ((uint64_t)(uint32_t)__shfl_xor((int)(w >> 32), o, 64) << 32) |
+                         (uint32_t)__shfl_xor((int)(uint32_t)w, o, 64);
+      w = t < w ? t : w;
+    }
+    if (mn == w && at >= 0) {
+#pragma unroll
+      for (int i = 0; i < kRegMax; ++i) if (i == at) comp[i] = ~0ull;
+    }
+  }
+  uint32_t kept = 0;
+#pragma unroll
+  for (int i = 0; i < kRegMax; ++i) kept += comp[i] != ~0ull ? 1u : 0u;
+  uint32_t pos = wave_inclusive_sum(kept) - kept;
+#pragma unroll
+  for (int i = 0; i < kRegMax; ++i) {
+    if (comp[i] != ~0ull) {
+      if (pos < keff) out[pos] = (int32_t)sh.idx[i0 + i];
+      ++pos;
+    }
+  }
+}
+
+// General case: exact k-th largest key tau by radix steps, then an ordered pass that keeps
+// keys above tau and the first ties at tau. The whole workgroup; candidates from `get_key`,
+// `get_idx` (LDS or the workspace's global copy).
+template <typename GK, typename GI>
+__device__ void select_by_radix(GK get_key, GI get_idx, uint32_t T, uint32_t keff, uint32_t lo, uint32_t hi,
+                                int32_t* out, FinalShared& sh) {
+  uint32_t ties_take;
+  const uint32_t tau = radix_select_desc(get_key, T, keff, lo, hi, 3, sh.hist, sh.scratch, &ties_take);
   uint32_t ties_before = 0, sel_before = 0;
   for (uint32_t t0 = 0; t0 < T; t0 += blockDim.x) {
     const uint32_t i = t0 + threadIdx.x;
     uint32_t kk = 0, ix = 0;
-    if (i < T) { kk = set.key(i); ix = set.idx(i); }
-    const bool is_tie = i < T && T > keff && kk == tau;
+    if (i < T) { kk = get_key(i); ix = get_idx(i); }
+    const bool is_tie = i < T && kk == tau;
     uint32_t tie_total;
     const uint32_t tie_rank = ties_before + block_exclusive_sum(is_tie ? 1u : 0u, &tie_total, sh.scratch);
-    const bool sel = i < T && (T <= keff || kk > tau || (is_tie && tie_rank < ties_take));
+    const bool sel = i < T && (kk > tau || (is_tie && tie_rank < ties_take));
     uint32_t sel_total;
     const uint32_t pos = sel_before + block_exclusive_sum(sel ? 1u : 0u, &sel_total, sh.scratch);
     if (sel && pos < keff) out[pos] = (int32_t)ix;
     ties_before += tie_total;
     sel_before += sel_total;
   }
-  for (int i = (int)keff + threadIdx.x; i < k; i += blockDim.x) out[i] = -1;
 }
 
-__global__ __launch_bounds__(kFinalThreads) void final_kernel(Args a, int32_t* topk) {
+__global__ __launch_bounds__(kThreads) void final_kernel(Args a, int32_t* topk) {
   __shared__ FinalShared sh;
   const int b = blockIdx.x;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
   int32_t* out = topk + (size_t)b * a.k;
   const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
-  if (keff == 0) {
-    for (int i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
-    return;
-  }
+  for (int i = (int)keff + threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
+  if (keff == 0) return;
   const int nch = (int)((n + kSelChunk - 1) / kSelChunk);
   const size_t cb = sel_chunk_base(a, b);
-  // Offsets of the chunk regions in the ordered superset.
+  const uint32_t* reg = a.ws.region + cb * kSelChunk * 2;
+  const bool peek = nch <= kPeekChunks;
+  // Round trip 1: every region's count and (small sequences) its first kPeek entries.
+  u32x4 head[kPeek / 2 * ((kPeekChunks + kThreads - 1) / kThreads)];
   uint32_t carry = 0;
-  for (int first = 0; first < nch; first += blockDim.x) {
+  for (int first = 0, it = 0; first < nch; first += kThreads, ++it) {
     const int c = first + threadIdx.x;
-    const uint32_t v = c < nch ? min(a.ws.counts[cb + c], (uint32_t)kSelChunk) : 0u;
+    uint32_t v = 0;
+    if (c < nch) {
+      v = min(a.ws.counts[cb + c], (uint32_t)kSelChunk);
+      if (peek) {
+        const u32x4* hp = reinterpret_cast<const u32x4*>(reg + (size_t)c * kSelChunk * 2);
+#pragma unroll
+        for (int q = 0; q < kPeek / 2; ++q) head[it * (kPeek / 2) + q] = hp[q];
+      }
+    }
     uint32_t total;
     const uint32_t ex = block_exclusive_sum(v, &total, sh.scratch);
     if (c < nch) sh.off[c] = carry + ex;
@@ -547,52 +611,87 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(Args a, int32_t* t
   if (threadIdx.x == 0) sh.off[nch] = carry;
   __syncthreads();
   const uint32_t T = carry;
-  const uint32_t* reg = a.ws.region + cb * kSelChunk * 2;
-  // Gather: entry e lives in the chunk c with off[c] <= e < off[c+1] (binary search).
   const bool in_lds = T <= (uint32_t)kLdsCand;
   uint32_t* gdst = a.ws.gather + (size_t)b * round_cand(a.max_cand) * 2;
-  for (uint32_t e = threadIdx.x; e < T; e += blockDim.x) {
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sh.off[mid] <= e) lo = mid; else hi = mid - 1;
+  if (peek && in_lds) {
+    // Place the region heads, then fetch whatever did not fit in a head.
+    for (int first = 0, it = 0; first < nch; first += kThreads, ++it) {
+      const int c = first + threadIdx.x;
+      if (c < nch) {
+        const uint32_t o = sh.off[c], cnt = sh.off[c + 1] - o;
+#pragma unroll
+        for (int q = 0; q < kPeek / 2; ++q) {
+          const u32x4 hv = head[it * (kPeek / 2) + q];
+          if (2 * q < (int)cnt) { sh.key[o + 2 * q] = hv[0]; sh.idx[o + 2 * q] = hv[1]; }
+          if (2 * q + 1 < (int)cnt) { sh.key[o + 2 * q + 1] = hv[2]; sh.idx[o + 2 * q + 1] = hv[3]; }
+        }
+        for (uint32_t e = kPeek; e < cnt; ++e) {
+          sh.key[o + e] = reg[((size_t)c * kSelChunk + e) * 2];
+          sh.idx[o + e] = reg[((size_t)c * kSelChunk + e) * 2 + 1];
+        }
+      }
     }
-    const size_t src = ((size_t)lo * kSelChunk + (e - sh.off[lo])) * 2;
-    const uint32_t kk = reg[src], ix = reg[src + 1];
-    if (in_lds) { sh.key[e] = kk; sh.idx[e] = ix; }
-    else { gdst[2 * (size_t)e] = kk; gdst[2 * (size_t)e + 1] = ix; }
+  } else {
+    // Entry e lives in the chunk c with off[c] <= e < off[c+1] (binary search).
+    for (uint32_t e = threadIdx.x; e < T; e += blockDim.x) {
+      int lo = 0, hi = nch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh.off[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      const size_t src = ((size_t)lo * kSelChunk + (e - sh.off[lo])) * 2;
+      const uint32_t kk = reg[src], ix = reg[src + 1];
+      if (in_lds) { sh.key[e] = kk; sh.idx[e] = ix; }
+      else { gdst[2 * (size_t)e] = kk; gdst[2 * (size_t)e + 1] = ix; }
+    }
   }
   __syncthreads();
+  if (T <= keff) {                         // every candidate is selected, in index order
+    for (uint32_t e = threadIdx.x; e < T; e += blockDim.x)
+      out[e] = (int32_t)(in_lds ? sh.idx[e] : gdst[2 * (size_t)e + 1]);
+    return;
+  }
   const uint32_t lo_key = a.ws.bound[2 * b], hi_key = a.ws.bound[2 * b + 1];
-  if (in_lds) select_exact(LdsSet{&sh}, T, keff, lo_key, hi_key, out, a.k, sh);
-  else select_exact(GlobalSet{gdst}, T, keff, lo_key, hi_key, out, a.k, sh);
+  if (in_lds && T - keff <= (uint32_t)kRemoveMax) {
+    if (threadIdx.x < 64) select_by_removal(sh, T, keff, out);
+  } else if (in_lds) {
+    select_by_radix([&](uint32_t i) { return sh.key[i]; }, [&](uint32_t i) { return sh.idx[i]; }, T, keff, lo_key,
+                    hi_key, out, sh);
+  } else {
+    select_by_radix([&](uint32_t i) { return gdst[2 * (size_t)i]; },
+                    [&](uint32_t i) { return gdst[2 * (size_t)i + 1]; }, T, keff, lo_key, hi_key, out, sh);
+  }
 }
 
 template <typename ET, int NH>
-void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a, int maxv) {
-  switch (maxv) {
+void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a) {
+  switch (a.lpc) {
     case 1: hipLaunchKernelGGL((score_kernel<ET, NH, 1>), grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((score_kernel<ET, NH, 2>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((score_kernel<ET, NH, 4>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((score_kernel<ET, NH, 4>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((score_kernel<ET, NH, 8>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((score_kernel<ET, NH, 16>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((score_kernel<ET, NH, 32>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((score_kernel<ET, NH, 64>), grid, dim3(kThreads), 0, s, a); break;
   }
 }
 
 template <typename ET>
-void launch_scores(dim3 grid, hipStream_t s, const Args& a, int maxv) {
-  if (a.nh <= 1) launch_scores_nh<ET, 1>(grid, s, a, maxv);
-  else if (a.nh <= 2) launch_scores_nh<ET, 2>(grid, s, a, maxv);
-  else if (a.nh <= 4) launch_scores_nh<ET, 4>(grid, s, a, maxv);
-  else if (a.nh <= 8) launch_scores_nh<ET, 8>(grid, s, a, maxv);
-  else launch_scores_nh<ET, 16>(grid, s, a, maxv);
+void launch_scores(dim3 grid, hipStream_t s, const Args& a) {
+  if (a.nh <= 1) launch_scores_nh<ET, 1>(grid, s, a);
+  else if (a.nh <= 2) launch_scores_nh<ET, 2>(grid, s, a);
+  else if (a.nh <= 4) launch_scores_nh<ET, 4>(grid, s, a);
+  else if (a.nh <= 8) launch_scores_nh<ET, 8>(grid, s, a);
+  else launch_scores_nh<ET, 16>(grid, s, a);
 }
 
-// Sub-chunk size: up to 64 candidates, smaller when the longest sequence would otherwise give
-// fewer than 2k maxima, larger (up to a score chunk) when it would give more than kMaxMaxima.
-int pick_subchunk(int64_t max_cand, int32_t k) {
-  int sc = 64;
-  while (sc > 1 && max_cand / sc < 2LL * k) sc >>= 1;
-  while (sc < kScoreChunk && max_cand / sc > kMaxMaxima) sc <<= 1;
-  return sc;
+// Groups per K1 chunk: the coarsest choice that still gives the longest sequence at least 2k
+// group maxima (finer groups give a weaker bound, coarser ones too few groups).
+int pick_groups(int64_t max_cand, int32_t chunk, int32_t k, const int* choices, int nchoices) {
+  const int64_t nch = (max_cand + chunk - 1) / chunk;
+  for (int i = 0; i < nchoices; ++i)
+    if (nch * choices[i] >= 2LL * k) return choices[i];
+  return choices[nchoices - 1];
 }
 
 }  // namespace
@@ -615,18 +714,13 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
     return CHS_ERR_SHAPE;
   if (max_cand > kMaxCand) return CHS_ERR_UNSUPPORTED;
   const size_t es = elem_size(dtype);
-  int nvec = 0, lpc = 1, maxv = 1;
+  int nvec = 0, lpc = 1;
   if (q_idx) {
     if (n_heads < 1 || n_heads > 16 || head_dim < 8 || head_dim > 512 || (head_dim * es) % 16 != 0)
       return CHS_ERR_SHAPE;
     if (!w || !k_idx) return CHS_ERR_NULL;
-    nvec = (int)(head_dim * es / 16);
-    // Lanes per candidate: the largest power of two <= nvec/2 (at most 64); each lane then
-    // covers at most 4 of the row's 16-byte vectors.
-    while (lpc * 2 <= nvec / 2 && lpc < 64) lpc *= 2;
-    maxv = (nvec + lpc - 1) / lpc;
-    if (maxv > 4) return CHS_ERR_UNSUPPORTED;
-    maxv = maxv == 3 ? 4 : maxv;
+    nvec = (int)(head_dim * es / 16);   // 16-byte vectors per key row (<= 64)
+    while (lpc < nvec) lpc *= 2;        // one vector per lane
   } else if (!scores) {
     return CHS_ERR_NULL;
   }
@@ -637,24 +731,34 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
   Args a;
   a.q = q_idx; a.w = w; a.keys = k_idx; a.cu = cu_cand; a.max_cand = max_cand;
   a.nh = n_heads; a.nvec = nvec; a.lpc = lpc; a.k = k; a.scores = scores; a.ws = ws;
-  a.sc = pick_subchunk(max_cand, k);
+  if (q_idx) {
+    static const int score_groups[3] = {1, 4, 32};
+    a.chunk = (kThreads / lpc) * kPasses;
+    a.gpc = pick_groups(max_cand, a.chunk, k, score_groups, 3);
+  } else {
+    static const int max_groups[3] = {1, 4, 16};
+    a.chunk = kMaxChunk;
+    a.gpc = pick_groups(max_cand, a.chunk, k, max_groups, 3);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_cand > 0) {
+    // Persistent grid: about kScoreGrid workgroups over all sequences.
+    const int64_t chunks = (max_cand + a.chunk - 1) / a.chunk;
+    const int64_t per_seq = std::max<int64_t>(1, kScoreGrid / batch);
+    const dim3 grid((unsigned)std::min<int64_t>(chunks, per_seq), (unsigned)batch);
     if (q_idx) {
-      const dim3 grid((unsigned)((max_cand + kScoreChunk - 1) / kScoreChunk), (unsigned)batch);
-      if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, a, maxv);
-      else launch_scores<float>(grid, s, a, maxv);
+      if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, a);
+      else launch_scores<float>(grid, s, a);
     } else {
-      const dim3 grid((unsigned)((max_cand + kMaxChunk - 1) / kMaxChunk), (unsigned)batch);
       hipLaunchKernelGGL(max_kernel, grid, dim3(kThreads), 0, s, a);
     }
     if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-    hipLaunchKernelGGL(bound_kernel, dim3((unsigned)batch), dim3(kBoundThreads), 0, s, a);
+    hipLaunchKernelGGL(bound_kernel, dim3((unsigned)batch), dim3(kThreads), 0, s, a);
     if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
     const dim3 sgrid((unsigned)((max_cand + kSelChunk - 1) / kSelChunk), (unsigned)batch);
     hipLaunchKernelGGL(select_kernel, sgrid, dim3(kThreads), 0, s, a);
     if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL(final_kernel, dim3((unsigned)batch), dim3(kFinalThreads), 0, s, a, topk);
+  hipLaunchKernelGGL(final_kernel, dim3((unsigned)batch), dim3(kThreads), 0, s, a, topk);
   return launch_status();
 }
