@@ -9,19 +9,34 @@
 // The pages' design reduces per-CTA histograms inside a thread-block cluster through
 // distributed shared memory, which gfx950 does not have; on MI355X a device-scope fence costs
 // tens of nanoseconds per workgroup, serialised, and same-address atomics about ten. So no
-// kernel here synchronises workgroups with each other; kernel boundaries order the phases:
-//   K1 score_kernel (persistent grid, query slices in registers, next chunk's loads issued
-//      before the current chunk is scored) streams the index keys once and writes the fp32
-//      scores plus a maximum order-preserving key per group of candidates; max_kernel does
-//      the same for caller-provided scores.
-//   K2 bound_kernel (one workgroup per sequence): L = k-th largest group maximum, a lower
-//      bound on the k-th largest score (k disjoint groups each hold a score >= L).
-//   K3 select_kernel: every chunk of 1024 candidates keeps the ones with key >= L in index
-//      order and writes them, with their count, to its own region.
-//   K4 final_kernel (one workgroup per sequence): gathers the regions and selects exactly,
-//      by one-at-a-time removal when the superset exceeds k by at most 64, else by radix
-//      steps to the k-th largest key tau and an ordered pass (keys above tau, then the first
-//      ties at tau), written ascending by a prefix count.
+// kernel here synchronises workgroups with each other, and a call is two kernels:
+//
+//   K1 score_kernel streams the index keys once. LPC lanes (16 for 128 bf16 channels) share a
+//      key row, one 16-byte non-temporal load each, so every wave load instruction reads one
+//      contiguous 1 KiB; v_dot2_f32_bf16 (or fp32 FMAs) and DPP sums form the head dots. Each
+//      wave owns a run of consecutive rows and issues all of its loads before the first use
+//      (the loads are unconditional, with clamped addresses, so the compiler can count them),
+//      then writes the fp32 scores plus the maximum order-preserving key of every group of GS
+//      consecutive candidates (GS = 32; 16 or 8 for very wide keys). max_kernel does the same
+//      for caller-provided scores.
+//   K2 collect_kernel, one 1024-thread workgroup per sequence:
+//      (A) loads the group maxima and bins them by key into 2048 monotone bins spanning their
+//          range; L = the smallest maximum in the bin that holds the k-th largest maximum.
+//          L never exceeds the k-th largest score, because k disjoint groups each hold a score
+//          >= L; so every top-k candidate, and every tie at the threshold, has key >= L and
+//          sits in a group whose maximum is >= L;
+//      (B) lists those groups in index order (each thread owns eight consecutive maxima; one
+//          block scan of the per-thread counts places them);
+//      (C) loads only the listed groups' scores (about k groups of 128 bytes at 1M context),
+//          keeps the candidates with key >= L in index order in LDS, and bins their keys into
+//          2048 monotone bins over [L, largest maximum];
+//      (D) the bin holding the k-th largest kept key gives tau after comparing only the few
+//          keys inside it (a crowded bin, from heavy ties, falls back to radix steps); an
+//          ordered pass then writes the keys above tau and the first ties at tau, ascending
+//          by index (no sort).
+//      Inputs that defeat the bound (a superset too large for LDS: heavy ties, many equal
+//      zeros) are selected by the whole workgroup straight from the score array instead.
+//      Gathers go through buffer loads (32-bit offsets, reads beyond the array return 0).
 // The composite order (key descending, then index ascending) is total, so the selected set is
 // unique and bit-identical to a full sort of the same scores.
 #include <algorithm>
@@ -31,51 +46,41 @@
 namespace chs {
 namespace {
 
-constexpr int kThreads = 256;        // every kernel here
-constexpr int kPasses = 8;           // K1 passes per chunk (one 16-byte load each per lane)
-constexpr int kScoreGrid = 1024;     // K1 workgroups per launch (all sequences together)
-constexpr int kMaxChunk = 2048;      // scores per max_kernel chunk (256 threads x 8)
-constexpr int kSelChunk = 1024;      // candidates per K3 workgroup (256 threads x 4)
-constexpr int kMaxMaxima = 8192;     // group maxima K2 ranks (the first ones if more)
-constexpr int kLdsCand = 8192;       // superset size K4 keeps in LDS
-constexpr int kMaxSelChunks = 4096;  // K3 chunks per sequence (max_cand <= 4M)
-constexpr int kPeekChunks = 512;     // K4 fetches region heads with the counts up to this many chunks
-constexpr int kPeek = 8;             // entries per region head
-constexpr int kRemoveMax = 64;       // K4 removes one by one when T - k <= this
+constexpr int kThreads = 256;          // K1 workgroup
+constexpr int kPasses = 8;             // K1 loads per lane (16 bytes each)
+constexpr int kGroup = 32;             // candidates per group (K1 uses 16 or 8 for keys > 512 B)
+constexpr int kMinGroup = 8;
+constexpr int kCThreads = 1024;        // K2 workgroup: sixteen waves, four per SIMD
+constexpr int kCWaves = kCThreads / 64;
+constexpr int kMaxPerThread = 8;       // group maxima per K2 thread per tile (contiguous)
+constexpr int kTile = kCThreads * kMaxPerThread;   // 8192: the bound ranks the first tile
+constexpr int kBins = 2048;            // bound and superset histograms; global radix bins
+constexpr int kListCap = 8192;         // groups the LDS list holds
+constexpr int kLdsCand = 8192;         // superset entries LDS holds
+constexpr int kItemRounds = 8;         // superset items (4 candidates each) per K2 thread per batch
+constexpr int kBinCap = 64;            // threshold-bin entries resolved directly
+constexpr int kGlobalRounds = 16;      // global path: scores per thread per batch
+constexpr int kScanRounds = 16;        // the most rounds one ordered scan covers
 constexpr int kMaxK = 2048;
-constexpr int kRegMax = (kMaxK + kRemoveMax + 63) / 64;   // superset entries per lane (removal path)
-constexpr int64_t kMaxCand = (int64_t)kMaxSelChunks * kSelChunk;
+constexpr int64_t kMaxCand = 1 << 22;
 
 struct Workspace {
-  uint32_t* maxima;   // [batch][rc]: group maximum keys
-  uint32_t* bound;    // [batch][2]: L, largest key
-  uint32_t* counts;   // [batch][rc / kSelChunk]
-  uint32_t* region;   // [batch][rc][2]: per K3 chunk, (key, index) in index order
-  uint32_t* gather;   // [batch][rc][2]: K4's global superset copy (large supersets only)
+  uint32_t* maxima;   // [batch][mcap]: group maximum keys
   float* scores;      // [batch][rc] when the caller passes no score array
 };
 
-// Candidate capacity per sequence, rounded up to whole K3 chunks.
-__host__ __device__ inline int64_t round_cand(int64_t max_cand) {
-  return (max_cand + kSelChunk - 1) / kSelChunk * kSelChunk;
-}
+// Candidate capacity per sequence, rounded up to 1024; group maxima capacity per sequence.
+__host__ __device__ inline int64_t round_cand(int64_t max_cand) { return (max_cand + 1023) / 1024 * 1024; }
+__host__ __device__ inline int64_t maxima_cap(int64_t max_cand) { return round_cand(max_cand) / kMinGroup; }
 
 size_t ws_layout(int32_t batch, int64_t max_cand, Workspace* w, char* base) {
   const size_t nb = (size_t)batch;
-  const size_t rc = (size_t)round_cand(max_cand > 0 ? max_cand : 0);
+  const int64_t mc = max_cand > 0 ? max_cand : 0;
   size_t off = 0;
-  const size_t o_max = off; off = align_up(off + nb * rc * 4, 256);
-  const size_t o_bnd = off; off = align_up(off + nb * 2 * 4, 256);
-  const size_t o_cnt = off; off = align_up(off + nb * (rc / kSelChunk + 1) * 4, 256);
-  const size_t o_reg = off; off = align_up(off + nb * rc * 8, 256);
-  const size_t o_gat = off; off = align_up(off + nb * rc * 8, 256);
-  const size_t o_sc = off; off = align_up(off + nb * rc * 4, 256);
+  const size_t o_max = off; off = align_up(off + nb * (size_t)maxima_cap(mc) * 4, 256);
+  const size_t o_sc = off;  off = align_up(off + nb * (size_t)round_cand(mc) * 4, 256);
   if (w) {
     w->maxima = reinterpret_cast<uint32_t*>(base + o_max);
-    w->bound = reinterpret_cast<uint32_t*>(base + o_bnd);
-    w->counts = reinterpret_cast<uint32_t*>(base + o_cnt);
-    w->region = reinterpret_cast<uint32_t*>(base + o_reg);
-    w->gather = reinterpret_cast<uint32_t*>(base + o_gat);
     w->scores = reinterpret_cast<float*>(base + o_sc);
   }
   return off;
@@ -88,15 +93,26 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// A raw buffer resource over `bytes` bytes at p: loads through it take a 32-bit byte offset
+// (one VGPR per address instead of two) and return 0 beyond the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buffer_u32(__amdgpu_buffer_rsrc_t r, uint32_t index) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, index * 4u, 0, 0);
+}
+__device__ __forceinline__ u32x4 buffer_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t index) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, index * 4u, 0, 0);
+}
+
 struct Args {
   const void* q;        // [batch][nh][dim] (NULL: scores are input)
   const float* w;       // [batch][nh]
   const void* keys;     // [cu[batch]][dim]
   const int64_t* cu;    // [batch+1]
   int64_t max_cand;
-  int32_t nh, nvec, lpc;
-  int32_t chunk;        // K1 candidates per chunk
-  int32_t gpc;          // group maxima per K1 chunk: score 1, 4 or 32; max 1, 4 or 16
+  int32_t nh, nvec;     // heads; 16-byte vectors per key row
+  int32_t gs;           // group size (a power of two)
   int32_t k;
   float* scores;        // caller's packed array, or NULL -> workspace
   Workspace ws;
@@ -114,23 +130,51 @@ __device__ __forceinline__ float* score_ptr(const Args& a, int b, int64_t c0) {
   return a.scores ? a.scores + c0 : a.ws.scores + (int64_t)b * round_cand(a.max_cand);
 }
 __device__ __forceinline__ uint32_t* maxima_ptr(const Args& a, int b) {
-  return a.ws.maxima + (size_t)b * round_cand(a.max_cand);
-}
-__device__ __forceinline__ size_t sel_chunk_base(const Args& a, int b) {
-  return (size_t)b * (size_t)(round_cand(a.max_cand) / kSelChunk);
+  return a.ws.maxima + (size_t)b * maxima_cap(a.max_cand);
 }
 
-// ---------------------------------------------------------------- reductions and scans
-// Exclusive prefix sum over blockDim.x (a multiple of 64) threads; scratch: blockDim.x / 64
-// words. Returns the exclusive prefix; *total gets the sum.
+// ---------------------------------------------------------------- wave and block helpers
+// DPP move with zero fill: lanes whose source is outside the row (or whose row is not in
+// ROW_MASK) read 0, the identity of the sums and unsigned maxima below.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the wave: shifts by 1, 2, 4, 8 within each row of 16 lanes, then
+// row_bcast:15 (rows 1 and 3 add the last lane of the row before) and row_bcast:31 (rows 2
+// and 3 add lane 31).
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  v += dpp0<0x111>(v);
+  v += dpp0<0x112>(v);
+  v += dpp0<0x114>(v);
+  v += dpp0<0x118>(v);
+  v += dpp0<0x142, 0xA>(v);
+  v += dpp0<0x143, 0xC>(v);
+  return v;
+}
+
+// Maximum over the wave, returned wave-uniform (the same DPP pattern leaves it in lane 63).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, dpp0<0x111>(v));
+  v = max(v, dpp0<0x112>(v));
+  v = max(v, dpp0<0x114>(v));
+  v = max(v, dpp0<0x118>(v));
+  v = max(v, dpp0<0x142, 0xA>(v));
+  v = max(v, dpp0<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Number of set bits of a wave mask in the lanes below this one.
+__device__ __forceinline__ uint32_t mask_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exclusive prefix sum over the block (blockDim.x a multiple of 64); scratch: blockDim.x / 64
+// words. *total gets the sum.
 __device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += t;
-  }
+  const uint32_t inc = wave_inclusive_sum(v);
   if (lane == 63) scratch[wave] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -144,93 +188,21 @@ __device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* s
   return before + inc - v;
 }
 
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
-}
-
-__device__ uint32_t block_max(uint32_t v, uint32_t* scratch) {
+// Block-wide (min, max) of unsigned values; scratch: 2 * blockDim.x / 64 words.
+__device__ void block_minmax(uint32_t* vmin, uint32_t* vmax, uint32_t* scratch) {
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+  const uint32_t lo = ~wave_max(~*vmin), hi = wave_max(*vmax);
+  if ((threadIdx.x & 63) == 0) { scratch[2 * wave] = lo; scratch[2 * wave + 1] = hi; }
   __syncthreads();
-  uint32_t all = 0;
-  for (int w = 0; w < nw; ++w) all = max(all, scratch[w]);
+  uint32_t l = 0xFFFFFFFFu, h = 0;
+  for (int w = 0; w < nw; ++w) { l = min(l, scratch[2 * w]); h = max(h, scratch[2 * w + 1]); }
   __syncthreads();
-  return all;
+  *vmin = l; *vmax = h;
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// Radix digits below the bits shared by every key in [lo, hi]: the first digit covers the
-// top `width` differing bits. Returns the number of differing bits.
+// Radix digits below the bits shared by every key in [lo, hi]: returns how many bits differ.
 __device__ __forceinline__ int differing_bits(uint32_t lo, uint32_t hi) {
   return lo == hi ? 0 : 32 - __clz(lo ^ hi);
-}
-
-// One radix step over `m` keys (from `get`) that all share their bits above `shift + width`:
-// histogram (nb >= 2^width bins, nb = 8 * blockDim.x... see callers) of the `width`-bit digit
-// at `shift` over keys whose bits from `shift + width` up equal `prefix`, then the digit
-// holding the r-th largest. Returns the digit; *above gets the count with larger digits.
-template <typename Get>
-__device__ uint32_t radix_step(Get get, uint32_t m, int shift, int width, uint32_t prefix, uint32_t r,
-                               uint32_t* hist, uint32_t* scratch, uint32_t* above) {
-  const int nb = 1 << width;                       // width <= 11: at most 2048 bins
-  for (int i = threadIdx.x; i < 2048; i += blockDim.x) hist[i] = 0u;
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < m; i += blockDim.x) {
-    const uint32_t v = get(i);
-    if ((uint32_t)((uint64_t)v >> (shift + width)) == prefix) atomicAdd(&hist[(v >> shift) & (nb - 1)], 1u);
-  }
-  __syncthreads();
-  // Thread t owns digits 2047-8t .. 2040-8t (descending).
-  uint32_t c[8], local = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { c[i] = hist[2047 - 8 * threadIdx.x - i]; local += c[i]; }
-  uint32_t total;
-  uint32_t run = block_exclusive_sum(local, &total, scratch);
-  if (run < r && run + local >= r) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (run + c[i] >= r) { scratch[32] = 2047 - 8 * threadIdx.x - i; scratch[33] = run; break; }
-      run += c[i];
-    }
-  }
-  __syncthreads();
-  const uint32_t digit = scratch[32];
-  *above = scratch[33];
-  __syncthreads();
-  return digit;
-}
-
-// The r-th largest of m keys in [lo, hi] (1 <= r <= m), by 11-bit radix steps below the bits
-// lo and hi share; `steps` caps the number of steps (lower bits are then returned as 0, so the
-// result is rounded down). *rank_left gets r minus the number of keys above the result's
-// last-resolved digit (the rank among keys equal to the result when all bits are resolved).
-template <typename Get>
-__device__ uint32_t radix_select_desc(Get get, uint32_t m, uint32_t r, uint32_t lo, uint32_t hi, int steps,
-                                      uint32_t* hist, uint32_t* scratch, uint32_t* rank_left) {
-  int rem = differing_bits(lo, hi);
-  uint32_t prefix = rem == 32 ? 0u : (uint32_t)((uint64_t)hi >> rem);
-  for (int s = 0; s < steps && rem > 0; ++s) {
-    const int width = rem < 11 ? rem : 11;
-    rem -= width;
-    uint32_t above;
-    const uint32_t d = radix_step(get, m, rem, width, prefix, r, hist, scratch, &above);
-    r -= above;
-    prefix = (prefix << width) | d;
-  }
-  *rank_left = r;
-  return (uint32_t)((uint64_t)prefix << rem);
 }
 
 // ---------------------------------------------------------------- K1: scores + group maxima
@@ -280,393 +252,476 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Row geometry of K1 for LPC lanes per key row.
 template <int LPC>
-__device__ __forceinline__ void load_chunk(const u32x4* kb, int nvec, int64_t chunk0, int64_t n, int slot, int sub,
-                                           u32x4 (&kv)[kPasses]) {
-  constexpr int PER = kThreads / LPC;
-#pragma unroll
-  for (int u = 0; u < kPasses; ++u) {
-    const int64_t j = chunk0 + u * PER + slot;
-    kv[u] = (j < n && sub < nvec) ? __builtin_nontemporal_load(kb + j * nvec + sub) : u32x4{0, 0, 0, 0};
-  }
-}
+struct ScoreGeom {
+  static constexpr int RP = 64 / LPC;                  // rows per wave per pass
+  static constexpr int RW = kPasses * RP;              // rows per wave
+  static constexpr int GS = RW < kGroup ? RW : kGroup; // group size
+  static constexpr int NG = RW / GS;                   // groups per wave
+  static constexpr int PG = kPasses / NG;              // passes per group
+};
 
-// Score one chunk from registers; write scores and the chunk's group maxima.
-template <typename ET, int NH, int LPC>
-__device__ __forceinline__ void score_chunk(const Args& a, int64_t chunk, int64_t n, int slot, int sub,
-                                            const u32x4 (&qv)[NH], const float (&wv)[NH], const u32x4 (&kv)[kPasses],
-                                            float* sp, uint32_t* gmax, uint32_t* smax) {
-  constexpr int PER = kThreads / LPC;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t mx = 0;
-#pragma unroll
-  for (int u = 0; u < kPasses; ++u) {
-    const int64_t j = chunk * a.chunk + u * PER + slot;
-    float s = 0.f;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) s = fmaf(wv[h], fmaxf(group_sum<LPC>(Dot16<ET>::dot(qv[h], kv[u])), 0.f), s);
-    const bool valid = j < n;
-    if (sub == 0 && valid) sp[j] = s;
-    const uint32_t key = valid ? score_key(s) : 0u;   // 0: below every key
-    if (a.gpc == 32) {                                 // group = this wave's candidates of pass u
-      const uint32_t m = wave_max(key);
-      if (lane == 0) gmax[(chunk * 4 + wave) * kPasses + u] = m;
-    }
-    mx = max(mx, key);
-  }
-  if (a.gpc == 4) {                                    // group = this wave's candidates of the chunk
-    const uint32_t m = wave_max(mx);
-    if (lane == 0) gmax[chunk * 4 + wave] = m;
-  } else if (a.gpc == 1) {                             // group = the chunk
-    const uint32_t m = wave_max(mx);
-    if (lane == 0) smax[wave] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) gmax[chunk] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
-    __syncthreads();
-  }
-}
-
+// Grid (x: runs of 4 * RW rows, y: sequence). Wave w of block x scores rows
+// [(4x + w) * RW, +RW); pass u covers rows u * RP .. u * RP + RP - 1 of that run.
 template <typename ET, int NH, int LPC>
 __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
-  constexpr int PER = kThreads / LPC;
-  __shared__ uint32_t smax[4];
+  using G = ScoreGeom<LPC>;
   const int b = blockIdx.y;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
-  const int64_t nch = (n + a.chunk - 1) / a.chunk;
-  int64_t chunk = blockIdx.x;
-  if (chunk >= nch) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane & (LPC - 1);
-  const int slot = (wave * 64 + lane) / LPC;          // candidate slot within a pass
-  const u32x4* kb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.keys) + (size_t)c0 * a.nvec * 16);
-  u32x4 ka[kPasses], kc[kPasses];
-  load_chunk<LPC>(kb, a.nvec, chunk * a.chunk, n, slot, sub, ka);
-  u32x4 qv[NH];                                       // this lane's 16 bytes of every query
+  const int64_t row0 = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * G::RW;
+  if (row0 >= n) return;                               // no barriers follow
+  const int sub = lane & (LPC - 1), slot = lane / LPC;
+  const int nvec = a.nvec;
+  const int subc = sub < nvec ? sub : nvec - 1;
+  // Queries and weights first (their loads complete first), then every key load.
+  const u32x4* qb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + (size_t)b * a.nh * nvec * 16);
+  u32x4 qv[NH];
   float wv[NH];
-  const u32x4* qb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + (size_t)b * a.nh * a.nvec * 16);
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    wv[h] = h < a.nh ? a.w[(size_t)b * a.nh + h] : 0.f;
-    qv[h] = (h < a.nh && sub < a.nvec) ? qb[h * a.nvec + sub] : u32x4{0, 0, 0, 0};
+    const int hc = h < a.nh ? h : a.nh - 1;
+    qv[h] = qb[hc * nvec + subc];
+    wv[h] = a.w[(size_t)b * a.nh + hc];
+  }
+  const u32x4* kb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.keys) + (size_t)c0 * nvec * 16);
+  u32x4 kv[kPasses];
+#pragma unroll
+  for (int u = 0; u < kPasses; ++u) {
+    int64_t row = row0 + u * G::RP + slot;
+    if (row > n - 1) row = n - 1;
+    kv[u] = __builtin_nontemporal_load(kb + row * nvec + subc);
+  }
+  const bool sub_on = sub < nvec;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const bool on = sub_on && h < a.nh;
+    qv[h] = on ? qv[h] : u32x4{0, 0, 0, 0};
+    wv[h] = h < a.nh ? wv[h] : 0.f;
   }
   float* sp = score_ptr(a, b, c0);
   uint32_t* gmax = maxima_ptr(a, b);
-  (void)PER;
-  // Two register buffers: the next chunk's loads are in flight while the current one is scored.
-  for (;;) {
-    const int64_t next = chunk + gridDim.x;
-    if (next < nch) load_chunk<LPC>(kb, a.nvec, next * a.chunk, n, slot, sub, kc);
-    score_chunk<ET, NH, LPC>(a, chunk, n, slot, sub, qv, wv, ka, sp, gmax, smax);
-    if (next >= nch) break;
-    chunk = next;
-    const int64_t next2 = chunk + gridDim.x;
-    if (next2 < nch) load_chunk<LPC>(kb, a.nvec, next2 * a.chunk, n, slot, sub, ka);
-    score_chunk<ET, NH, LPC>(a, chunk, n, slot, sub, qv, wv, kc, sp, gmax, smax);
-    if (next2 >= nch) break;
-    chunk = next2;
+  uint32_t gm[G::NG];
+#pragma unroll
+  for (int g = 0; g < G::NG; ++g) gm[g] = 0u;
+#pragma unroll
+  for (int u = 0; u < kPasses; ++u) {
+    const int64_t row = row0 + u * G::RP + slot;
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s = fmaf(wv[h], fmaxf(group_sum<LPC>(Dot16<ET>::dot(qv[h], kv[u])), 0.f), s);
+    const bool valid = row < n;
+    if (sub == 0 && valid) sp[row] = s;
+    const uint32_t key = valid ? score_key(s) : 0u;   // 0: below every key
+    gm[u / G::PG] = max(gm[u / G::PG], key);
+  }
+#pragma unroll
+  for (int g = 0; g < G::NG; ++g) {
+    const uint32_t m = wave_max(gm[g]);
+    if (lane == 0) gmax[(row0 + g * G::GS) / G::GS] = m;
   }
 }
 
-// K1 for caller-provided scores: group maxima only. Chunks of 2048 scores (8 per thread, two
-// 16-byte loads); a group is a chunk, a wave's 512 scores, or a 16-lane row's 128 scores.
+// K1 for caller-provided scores: group maxima only. Wave w of block x covers 256 * P
+// consecutive scores starting at (4x + w) * 256 * P: P 16-byte loads per lane when the
+// sequence's scores are 16-byte aligned (a group of 32 is then 8 lanes of one load), else
+// 4P 4-byte loads (a group is half a wave of one load).
+template <int P>
 __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
-  __shared__ uint32_t smax[4];
   const int b = blockIdx.y;
   int64_t c0;
   const int64_t n = cand_count(a, b, &c0);
-  const int64_t nch = (n + kMaxChunk - 1) / kMaxChunk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * 256 * P;
+  if (base >= n) return;
   const float* sp = score_ptr(a, b, c0);
   uint32_t* gmax = maxima_ptr(a, b);
-  const bool vec = ((reinterpret_cast<uintptr_t>(sp) & 15) == 0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t chunk = blockIdx.x; chunk < nch; chunk += gridDim.x) {
-    const int64_t chunk0 = chunk * kMaxChunk;
-    uint32_t m = 0;
+  const int64_t nfull = n / 4;                         // whole 16-byte vectors in the sequence
+  if ((reinterpret_cast<uintptr_t>(sp) & 15) == 0 && nfull > 0) {
+    f32x4 v[P];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t j = chunk0 + h * 1024 + 4 * threadIdx.x;
-      float v[4];
-      if (vec && j + 3 < n) {
-        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + j));
-        v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (j + e < n) ? sp[j + e] : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) m = max(m, (j + e < n) ? score_key(v[e]) : 0u);
+    for (int u = 0; u < P; ++u) {
+      int64_t j = base / 4 + u * 64 + lane;
+      if (j > nfull - 1) j = nfull - 1;
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp) + j);
     }
-    if (a.gpc == 16) {
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));
-      if ((lane & 15) == 0) gmax[chunk * 16 + wave * 4 + (lane >> 4)] = m;
-    } else {
-      m = wave_max(m);
-      if (a.gpc == 4) {
-        if (lane == 0) gmax[chunk * 4 + wave] = m;
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int64_t j0 = base + (u * 64 + lane) * 4;
+      uint32_t m = 0;
+      if (j0 < 4 * nfull) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, score_key(v[u][e]));
       } else {
-        if (lane == 0) smax[wave] = m;
-        __syncthreads();
-        if (threadIdx.x == 0) gmax[chunk] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
-        __syncthreads();
+        for (int e = 0; e < 4; ++e) if (j0 + e < n) m = max(m, score_key(sp[j0 + e]));   // the tail
       }
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // xor 1
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // xor 2
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));  // half-row mirror
+      if ((lane & 7) == 0) gmax[j0 / kGroup] = m;
     }
-  }
-}
-
-// ---------------------------------------------------------------- K2: the bound L
-__global__ __launch_bounds__(kThreads) void bound_kernel(Args a) {
-  constexpr int PER = kMaxMaxima / kThreads;   // 32 maxima per thread, in registers
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t scratch[40];
-  const int b = blockIdx.x;
-  int64_t c0;
-  const int64_t n = cand_count(a, b, &c0);
-  const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
-  const int64_t m_all = (n + a.chunk - 1) / a.chunk * a.gpc;
-  const int m = (int)min<int64_t>(m_all, kMaxMaxima);   // any k disjoint groups give a bound
-  const uint32_t* g = maxima_ptr(a, b);
-  uint32_t v[PER];
-  uint32_t vmax = 0, vmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = i * kThreads + threadIdx.x;
-    v[i] = e < m ? g[e] : 0u;
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (i * kThreads + (int)threadIdx.x < m) { vmax = max(vmax, v[i]); vmin = min(vmin, v[i]); }
-  }
-  for (int64_t e = kMaxMaxima + threadIdx.x; e < m_all; e += kThreads) vmax = max(vmax, g[e]);
-  vmax = block_max(vmax, scratch);
-  vmin = ~block_max(~vmin, scratch);
-  uint32_t L = 0;
-  if (n > (int64_t)keff && m >= (int)keff && keff > 0) {
-    // The maxima go through LDS once for the two radix steps.
-    __shared__ uint32_t vals[kMaxMaxima];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) vals[i * kThreads + threadIdx.x] = v[i];
-    __syncthreads();
-    uint32_t rank_left;
-    L = radix_select_desc([&](uint32_t i) { return vals[i]; }, (uint32_t)m, keff, vmin, vmax, 2, hist, scratch,
-                          &rank_left);
-  }
-  if (threadIdx.x == 0) { a.ws.bound[2 * b] = L; a.ws.bound[2 * b + 1] = vmax; }
-}
-
-// ---------------------------------------------------------------- K3: the superset
-__global__ __launch_bounds__(kThreads) void select_kernel(Args a) {
-  __shared__ uint32_t scratch[8];
-  const int b = blockIdx.y;
-  int64_t c0;
-  const int64_t n = cand_count(a, b, &c0);
-  const int64_t chunk0 = (int64_t)blockIdx.x * kSelChunk;
-  if (chunk0 >= n) return;
-  const int64_t chunk_end = min<int64_t>(chunk0 + kSelChunk, n);
-  const uint32_t L = a.ws.bound[2 * b];
-  const float* sp = score_ptr(a, b, c0);
-  // Thread t owns candidates chunk0 + 4t .. 4t+3 (consecutive, so index order is kept).
-  const int64_t j = chunk0 + 4 * threadIdx.x;
-  float v[4];
-  if (((reinterpret_cast<uintptr_t>(sp) & 15) == 0) && j + 3 < chunk_end) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(sp + j);
-    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
   } else {
+    float v[4 * P];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (j + e < chunk_end) ? sp[j + e] : 0.f;
-  }
-  uint32_t key[4], cnt = 0;
+    for (int u = 0; u < 4 * P; ++u) {
+      int64_t j = base + u * 64 + lane;
+      if (j > n - 1) j = n - 1;
+      v[u] = sp[j];
+    }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    key[e] = score_key(v[e]);
-    cnt += (j + e < chunk_end && key[e] >= L) ? 1u : 0u;
-  }
-  uint32_t total;
-  uint32_t pos = block_exclusive_sum(cnt, &total, scratch);
-  const size_t cidx = sel_chunk_base(a, b) + blockIdx.x;
-  uint32_t* reg = a.ws.region + cidx * kSelChunk * 2;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (j + e < chunk_end && key[e] >= L) {
-      reg[2 * pos] = key[e];
-      reg[2 * pos + 1] = (uint32_t)(j + e);
-      ++pos;
+    for (int u = 0; u < 4 * P; ++u) {
+      const int64_t j = base + u * 64 + lane;
+      uint32_t m = j < n ? score_key(v[u]) : 0u;
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // xor 1
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // xor 2
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));  // half-row mirror
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));  // row mirror
+      m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));                                 // rows 0+1, 2+3
+      const int64_t g = (base + u * 64) / kGroup;
+      if (lane == 0) gmax[g] = m;
+      if (lane == 32) gmax[g + 1] = m;
     }
   }
-  if (threadIdx.x == 0) a.ws.counts[cidx] = total;
 }
 
-// ---------------------------------------------------------------- K4: exact selection
-struct FinalShared {
-  uint32_t key[kLdsCand];
-  uint32_t idx[kLdsCand];
-  uint32_t off[kMaxSelChunks + 1];
-  uint32_t hist[2048];
-  uint32_t scratch[40];
+// ---------------------------------------------------------------- K2: collect and select
+struct CollectShared {
+  uint32_t key[kLdsCand];       // superset keys, index order
+  uint32_t idx[kLdsCand];       // superset candidate indices
+  uint32_t list[kListCap];      // groups whose maximum is >= L, ascending
+  uint32_t hist[kBins];         // maxima bins (A), then superset bins (C, D)
+  uint32_t tot[kScanRounds * kCWaves + 1];
+  uint32_t red[2 * kCWaves];
+  uint32_t binv[kBinCap];       // keys in the bin that holds the k-th largest
+  uint32_t misc[8];
 };
 
-// Keep the first `keff` of T candidates (index order) in the composite order (key desc, then
-// position asc); write their indices ascending. Case T - keff <= kRemoveMax, by wave 0 alone:
-// remove the smallest candidate T - keff times.
-__device__ void select_by_removal(const FinalShared& sh, uint32_t T, uint32_t keff, int32_t* out) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t E = (T + 63) / 64;   // <= kRegMax
-  const uint32_t i0 = min(T, lane * E);
-  uint64_t comp[kRegMax];             // (key, position from the end): the minimum goes first
+// Ordered scan over items (round r, thread t), taken in that order, for the K2 block: given
+// this thread's count for each round, returns the total and sets off[r] to the sum of the
+// counts before item (r, t). Wave sums use DPP; wave 0 scans the per-(round, wave) totals.
+// Ends with a barrier, so LDS written before the call is visible after it.
+template <int R>
+__device__ uint32_t ordered_scan(const uint32_t (&cnt)[R], uint32_t (&off)[R], CollectShared& sh) {
+  static_assert(R <= kScanRounds, "too many rounds");
+  constexpr int N = R * kCWaves;
+  constexpr int PL = (N + 63) / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < kRegMax; ++i) {
-    const uint32_t e = i0 + i;
-    comp[i] = (i < (int)E && e < T) ? (((uint64_t)sh.key[e] << 32) | (uint64_t)(0xFFFFFFFFu - e)) : ~0ull;
+  for (int r = 0; r < R; ++r) {
+    const uint32_t inc = wave_inclusive_sum(cnt[r]);
+    off[r] = inc - cnt[r];
+    if (lane == 63) sh.tot[wave * R + r] = inc;
   }
-  for (uint32_t rnd = keff; rnd < T; ++rnd) {
-    uint64_t mn = ~0ull;
-    int at = -1;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    uint32_t v[PL], sum = 0;
 #pragma unroll
-    for (int i = 0; i < kRegMax; ++i) if (comp[i] < mn) { mn = comp[i]; at = i; }
-    uint64_t w = mn;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t t = ((uint64_t)(uint32_t)__shfl_xor((int)(w >> 32), o, 64) << 32) |
-                         (uint32_t)__shfl_xor((int)(uint32_t)w, o, 64);
-      w = t < w ? t : w;
+    for (int p = 0; p < PL; ++p) {
+      const int i = lane * PL + p;      // position in (round, wave) order
+      v[p] = i < N ? sh.tot[(i % kCWaves) * R + i / kCWaves] : 0u;
+      sum += v[p];
     }
-    if (mn == w && at >= 0) {
+    const uint32_t inc = wave_inclusive_sum(sum);
+    uint32_t run = inc - sum;
 #pragma unroll
-      for (int i = 0; i < kRegMax; ++i) if (i == at) comp[i] = ~0ull;
+    for (int p = 0; p < PL; ++p) {
+      const int i = lane * PL + p;
+      if (i < N) sh.tot[(i % kCWaves) * R + i / kCWaves] = run;
+      run += v[p];
     }
+    if (lane == 63) sh.tot[N] = inc;
   }
-  uint32_t kept = 0;
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kRegMax; ++i) kept += comp[i] != ~0ull ? 1u : 0u;
-  uint32_t pos = wave_inclusive_sum(kept) - kept;
-#pragma unroll
-  for (int i = 0; i < kRegMax; ++i) {
-    if (comp[i] != ~0ull) {
-      if (pos < keff) out[pos] = (int32_t)sh.idx[i0 + i];
-      ++pos;
-    }
-  }
+  for (int r = 0; r < R; ++r) off[r] += sh.tot[wave * R + r];
+  const uint32_t total = sh.tot[N];
+  __syncthreads();
+  return total;
 }
 
-// General case: exact k-th largest key tau by radix steps, then an ordered pass that keeps
-// keys above tau and the first ties at tau. The whole workgroup; candidates from `get_key`,
-// `get_idx` (LDS or the workspace's global copy).
+// The r-th largest (1 <= r <= m) of m keys from `get`, all in [lo, hi], by 11-bit radix
+// steps below the bits lo and hi share (2048 bins, two per thread); *ties_take gets how many
+// keys equal to the result rank within the top r.
+template <typename Get>
+__device__ uint32_t block_radix_select(Get get, uint32_t m, uint32_t r, uint32_t lo, uint32_t hi,
+                                       CollectShared& sh, uint32_t* ties_take) {
+  int rem = differing_bits(lo, hi);
+  uint32_t prefix = rem == 32 ? 0u : (uint32_t)((uint64_t)hi >> rem);
+  while (rem > 0) {
+    const int width = rem < 11 ? rem : 11;
+    rem -= width;
+    const uint32_t nb = 1u << width;
+    for (int i = threadIdx.x; i < kBins; i += kCThreads) sh.hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t x0 = 0; x0 < m; x0 += kGlobalRounds * kCThreads) {
+      uint32_t kk[kGlobalRounds];
+#pragma unroll
+      for (int q = 0; q < kGlobalRounds; ++q) kk[q] = get(min(x0 + q * kCThreads + threadIdx.x, m - 1));
+#pragma unroll
+      for (int q = 0; q < kGlobalRounds; ++q) {
+        const uint32_t v = kk[q];
+        if (x0 + q * kCThreads + threadIdx.x < m && (uint32_t)((uint64_t)v >> (rem + width)) == prefix)
+          atomicAdd(&sh.hist[(v >> rem) & (nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    const uint32_t t = threadIdx.x;
+    const uint32_t c0 = sh.hist[kBins - 1 - 2 * t], c1 = sh.hist[kBins - 2 - 2 * t];
+    uint32_t total;
+    const uint32_t run = block_exclusive_sum(c0 + c1, &total, sh.red);
+    if (run < r && run + c0 + c1 >= r) {
+      if (run + c0 >= r) { sh.misc[0] = kBins - 1 - 2 * t; sh.misc[1] = run; }
+      else { sh.misc[0] = kBins - 2 - 2 * t; sh.misc[1] = run + c0; }
+    }
+    __syncthreads();
+    r -= sh.misc[1];
+    prefix = (prefix << width) | sh.misc[0];
+    __syncthreads();
+  }
+  *ties_take = r;
+  return prefix;
+}
+
+// Writes, ascending, the indices of the m candidates (key from `key`, index from `idx`, in
+// index order) that are above tau or among the first ties_take equal to it.
 template <typename GK, typename GI>
-__device__ void select_by_radix(GK get_key, GI get_idx, uint32_t T, uint32_t keff, uint32_t lo, uint32_t hi,
-                                int32_t* out, FinalShared& sh) {
-  uint32_t ties_take;
-  const uint32_t tau = radix_select_desc(get_key, T, keff, lo, hi, 3, sh.hist, sh.scratch, &ties_take);
+__device__ void ordered_select(GK key, GI idx, uint32_t m, uint32_t tau, uint32_t ties_take, uint32_t keff,
+                               int32_t* out, CollectShared& sh) {
   uint32_t ties_before = 0, sel_before = 0;
-  for (uint32_t t0 = 0; t0 < T; t0 += blockDim.x) {
-    const uint32_t i = t0 + threadIdx.x;
-    uint32_t kk = 0, ix = 0;
-    if (i < T) { kk = get_key(i); ix = get_idx(i); }
-    const bool is_tie = i < T && kk == tau;
-    uint32_t tie_total;
-    const uint32_t tie_rank = ties_before + block_exclusive_sum(is_tie ? 1u : 0u, &tie_total, sh.scratch);
-    const bool sel = i < T && (kk > tau || (is_tie && tie_rank < ties_take));
-    uint32_t sel_total;
-    const uint32_t pos = sel_before + block_exclusive_sum(sel ? 1u : 0u, &sel_total, sh.scratch);
-    if (sel && pos < keff) out[pos] = (int32_t)ix;
+  for (uint32_t x0 = 0; x0 < m; x0 += kGlobalRounds * kCThreads) {
+    uint32_t kk[kGlobalRounds], c[kGlobalRounds], off[kGlobalRounds];
+#pragma unroll
+    for (int q = 0; q < kGlobalRounds; ++q) kk[q] = key(min(x0 + q * kCThreads + threadIdx.x, m - 1));
+#pragma unroll
+    for (int q = 0; q < kGlobalRounds; ++q)
+      c[q] = (x0 + q * kCThreads + threadIdx.x < m && kk[q] == tau) ? 1u : 0u;
+    const uint32_t tie_total = ordered_scan(c, off, sh);
+    uint32_t take = 0;
+#pragma unroll
+    for (int q = 0; q < kGlobalRounds; ++q) {
+      const bool in = x0 + q * kCThreads + threadIdx.x < m;
+      const bool t = in && (kk[q] > tau || (kk[q] == tau && ties_before + off[q] < ties_take));
+      take |= (t ? 1u : 0u) << q;
+      c[q] = t ? 1u : 0u;
+    }
+    const uint32_t sel_total = ordered_scan(c, off, sh);
+#pragma unroll
+    for (int q = 0; q < kGlobalRounds; ++q) {
+      const uint32_t pos = sel_before + off[q];
+      if (((take >> q) & 1u) && pos < keff) out[pos] = (int32_t)idx(x0 + q * kCThreads + threadIdx.x);
+    }
     ties_before += tie_total;
     sel_before += sel_total;
   }
 }
 
-__global__ __launch_bounds__(kThreads) void final_kernel(Args a, int32_t* topk) {
-  __shared__ FinalShared sh;
+__global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* topk) {
+  __shared__ CollectShared sh;
   const int b = blockIdx.x;
+  const uint32_t t = threadIdx.x;
   int64_t c0;
-  const int64_t n = cand_count(a, b, &c0);
+  const uint32_t n = (uint32_t)cand_count(a, b, &c0);   // <= 2^22: 32-bit index math below
   int32_t* out = topk + (size_t)b * a.k;
-  const uint32_t keff = (uint32_t)min<int64_t>(a.k, n);
-  for (int i = (int)keff + threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
+  const uint32_t keff = min((uint32_t)a.k, n);
+  for (uint32_t i = keff + t; i < (uint32_t)a.k; i += kCThreads) out[i] = -1;
   if (keff == 0) return;
-  const int nch = (int)((n + kSelChunk - 1) / kSelChunk);
-  const size_t cb = sel_chunk_base(a, b);
-  const uint32_t* reg = a.ws.region + cb * kSelChunk * 2;
-  const bool peek = nch <= kPeekChunks;
-  // Round trip 1: every region's count and (small sequences) its first kPeek entries.
-  u32x4 head[kPeek / 2 * ((kPeekChunks + kThreads - 1) / kThreads)];
-  uint32_t carry = 0;
-  for (int first = 0, it = 0; first < nch; first += kThreads, ++it) {
-    const int c = first + threadIdx.x;
-    uint32_t v = 0;
-    if (c < nch) {
-      v = min(a.ws.counts[cb + c], (uint32_t)kSelChunk);
-      if (peek) {
-        const u32x4* hp = reinterpret_cast<const u32x4*>(reg + (size_t)c * kSelChunk * 2);
-#pragma unroll
-        for (int q = 0; q < kPeek / 2; ++q) head[it * (kPeek / 2) + q] = hp[q];
-      }
-    }
-    uint32_t total;
-    const uint32_t ex = block_exclusive_sum(v, &total, sh.scratch);
-    if (c < nch) sh.off[c] = carry + ex;
-    carry += total;
-  }
-  if (threadIdx.x == 0) sh.off[nch] = carry;
-  __syncthreads();
-  const uint32_t T = carry;
-  const bool in_lds = T <= (uint32_t)kLdsCand;
-  uint32_t* gdst = a.ws.gather + (size_t)b * round_cand(a.max_cand) * 2;
-  if (peek && in_lds) {
-    // Place the region heads, then fetch whatever did not fit in a head.
-    for (int first = 0, it = 0; first < nch; first += kThreads, ++it) {
-      const int c = first + threadIdx.x;
-      if (c < nch) {
-        const uint32_t o = sh.off[c], cnt = sh.off[c + 1] - o;
-#pragma unroll
-        for (int q = 0; q < kPeek / 2; ++q) {
-          const u32x4 hv = head[it * (kPeek / 2) + q];
-          if (2 * q < (int)cnt) { sh.key[o + 2 * q] = hv[0]; sh.idx[o + 2 * q] = hv[1]; }
-          if (2 * q + 1 < (int)cnt) { sh.key[o + 2 * q + 1] = hv[2]; sh.idx[o + 2 * q + 1] = hv[3]; }
-        }
-        for (uint32_t e = kPeek; e < cnt; ++e) {
-          sh.key[o + e] = reg[((size_t)c * kSelChunk + e) * 2];
-          sh.idx[o + e] = reg[((size_t)c * kSelChunk + e) * 2 + 1];
-        }
-      }
-    }
-  } else {
-    // Entry e lives in the chunk c with off[c] <= e < off[c+1] (binary search).
-    for (uint32_t e = threadIdx.x; e < T; e += blockDim.x) {
-      int lo = 0, hi = nch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sh.off[mid] <= e) lo = mid; else hi = mid - 1;
-      }
-      const size_t src = ((size_t)lo * kSelChunk + (e - sh.off[lo])) * 2;
-      const uint32_t kk = reg[src], ix = reg[src + 1];
-      if (in_lds) { sh.key[e] = kk; sh.idx[e] = ix; }
-      else { gdst[2 * (size_t)e] = kk; gdst[2 * (size_t)e + 1] = ix; }
-    }
-  }
-  __syncthreads();
-  if (T <= keff) {                         // every candidate is selected, in index order
-    for (uint32_t e = threadIdx.x; e < T; e += blockDim.x)
-      out[e] = (int32_t)(in_lds ? sh.idx[e] : gdst[2 * (size_t)e + 1]);
+  if (n <= keff) {                                      // every candidate is selected
+    for (uint32_t i = t; i < n; i += kCThreads) out[i] = (int32_t)i;
     return;
   }
-  const uint32_t lo_key = a.ws.bound[2 * b], hi_key = a.ws.bound[2 * b + 1];
-  if (in_lds && T - keff <= (uint32_t)kRemoveMax) {
-    if (threadIdx.x < 64) select_by_removal(sh, T, keff, out);
-  } else if (in_lds) {
-    select_by_radix([&](uint32_t i) { return sh.key[i]; }, [&](uint32_t i) { return sh.idx[i]; }, T, keff, lo_key,
-                    hi_key, out, sh);
-  } else {
-    select_by_radix([&](uint32_t i) { return gdst[2 * (size_t)i]; },
-                    [&](uint32_t i) { return gdst[2 * (size_t)i + 1]; }, T, keff, lo_key, hi_key, out, sh);
+  const float* sp = score_ptr(a, b, c0);
+  const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(sp, n * 4u);
+  const int gs = a.gs;
+  const int gshift = __ffs(gs) - 1;
+  const uint32_t ng = (n + gs - 1) >> gshift;
+  const uint32_t nt = min(ng, (uint32_t)kTile);
+  const __amdgpu_buffer_rsrc_t mrs = buffer_rsrc(maxima_ptr(a, b), ng * 4u);
+  auto load_tile = [&](uint32_t t0, uint32_t (&mv)[kMaxPerThread]) {
+    const uint32_t e0 = t0 + kMaxPerThread * t;
+    const u32x4 lo4 = buffer_u32x4(mrs, e0), hi4 = buffer_u32x4(mrs, e0 + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { mv[j] = lo4[j]; mv[4 + j] = hi4[j]; }
+  };
+
+  // (A) The bound L from the first tile of group maxima (thread t holds maxima 8t .. 8t+7).
+  uint32_t mv[kMaxPerThread];
+  load_tile(0, mv);
+  for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;
+  if (t == 0) sh.misc[2] = 0;
+  uint32_t vmin = 0xFFFFFFFFu, vmax = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j)
+    if (kMaxPerThread * t + j < nt) { vmin = min(vmin, mv[j]); vmax = max(vmax, mv[j]); }
+  block_minmax(&vmin, &vmax, sh.red);                   // its barriers also order the clears
+  uint32_t L = 0;                                       // with fewer than k groups: every candidate
+  if (nt >= keff) {
+    const uint32_t span = vmax - vmin;
+    const float scale = span ? (float)(kBins - 1) / (float)span : 0.f;
+    // Monotone bins: a larger key never lands in a lower bin.
+    auto bin = [&](uint32_t v) { return min((uint32_t)(kBins - 1), (uint32_t)((float)(v - vmin) * scale)); };
+#pragma unroll
+    for (int j = 0; j < kMaxPerThread; ++j)
+      if (kMaxPerThread * t + j < nt) atomicAdd(&sh.hist[bin(mv[j])], 1u);
+    __syncthreads();
+    const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
+    uint32_t total;
+    const uint32_t run = block_exclusive_sum(h0 + h1, &total, sh.red);
+    if (run < keff && run + h0 + h1 >= keff) sh.misc[0] = run + h0 >= keff ? kBins - 1 - 2 * t : kBins - 2 - 2 * t;
+    __syncthreads();
+    const uint32_t bstar = sh.misc[0];
+    uint32_t lmin = 0xFFFFFFFFu, unused = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerThread; ++j)
+      if (kMaxPerThread * t + j < nt && bin(mv[j]) >= bstar) lmin = min(lmin, mv[j]);
+    block_minmax(&lmin, &unused, sh.red);
+    L = lmin;
   }
+  for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;   // reused for the superset
+
+  // (B) The groups whose maximum is >= L, ascending: one block scan per tile.
+  uint32_t G = 0;
+  for (uint32_t t0 = 0; t0 < ng; t0 += kTile) {
+    if (t0 > 0) load_tile(t0, mv);
+    uint32_t f = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerThread; ++j)
+      f |= ((t0 + kMaxPerThread * t + j < ng && mv[j] >= L) ? 1u : 0u) << j;
+    const uint32_t cnt[1] = {(uint32_t)__popc(f)};
+    uint32_t off[1];
+    const uint32_t total = ordered_scan(cnt, off, sh);
+    uint32_t pos = G + off[0];
+#pragma unroll
+    for (int j = 0; j < kMaxPerThread; ++j) {
+      if ((f >> j) & 1u) {
+        if (pos < (uint32_t)kListCap) sh.list[pos] = t0 + kMaxPerThread * t + j;
+        ++pos;
+      }
+    }
+    G += total;
+  }
+  __syncthreads();
+  bool fits = G <= (uint32_t)kListCap;
+
+  // (C) The superset: candidates of the listed groups with key >= L, in index order, binned
+  // by key over [L, vmax] (monotone, clamped) as they are kept.
+  uint32_t T = 0;
+  const uint32_t top = max(vmax, L);
+  const float scale2 = top > L ? (float)(kBins - 1) / (float)(top - L) : 0.f;
+  auto bin2 = [&](uint32_t v) { return min((uint32_t)(kBins - 1), (uint32_t)((float)(v - L) * scale2)); };
+  if (fits) {
+    const uint32_t E = G << gshift;                     // candidate slots of the listed groups
+    const uint32_t NI = (E + 3) / 4;                    // items of four (a group holds >= 8)
+    for (uint32_t i0 = 0; i0 < NI; i0 += kItemRounds * kCThreads) {
+      uint32_t kk[kItemRounds][4], cb[kItemRounds], cnt[kItemRounds], off[kItemRounds], f = 0;
+#pragma unroll
+      for (int r = 0; r < kItemRounds; ++r) {
+        const uint32_t x = 4 * min(i0 + r * kCThreads + t, NI - 1);
+        cb[r] = (sh.list[x >> gshift] << gshift) + (x & (gs - 1));
+      }
+#pragma unroll
+      for (int r = 0; r < kItemRounds; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[r][e] = buffer_u32(srs, cb[r] + e);
+      __builtin_amdgcn_sched_barrier(0);                // every load is in flight before any use
+#pragma unroll
+      for (int r = 0; r < kItemRounds; ++r) {
+        const uint32_t x = 4 * (i0 + r * kCThreads + t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kk[r][e] = score_key(__uint_as_float(kk[r][e]));
+          const bool keep = x + e < E && cb[r] + e < n && kk[r][e] >= L;
+          f |= (keep ? 1u : 0u) << (4 * r + e);
+        }
+        cnt[r] = (uint32_t)__popc((f >> (4 * r)) & 0xFu);
+      }
+      const uint32_t total = ordered_scan(cnt, off, sh);
+      if (T + total <= (uint32_t)kLdsCand) {
+#pragma unroll
+        for (int r = 0; r < kItemRounds; ++r) {
+          uint32_t pos = T + off[r];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if ((f >> (4 * r + e)) & 1u) {
+              sh.key[pos] = kk[r][e];
+              sh.idx[pos] = cb[r] + e;
+              atomicAdd(&sh.hist[bin2(kk[r][e])], 1u);
+              ++pos;
+            }
+          }
+        }
+      }
+      T += total;
+      if (T > (uint32_t)kLdsCand) { fits = false; break; }
+    }
+  }
+  __syncthreads();
+
+  // (D) Exact selection.
+  if (!fits) {                                          // global path
+    uint32_t ties_take;
+    const uint32_t tau = block_radix_select([&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); },
+                                            n, keff, 0u, 0xFFFFFFFFu, sh, &ties_take);
+    ordered_select([&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); },
+                   [&](uint32_t i) { return i; }, n, tau, ties_take, keff, out, sh);
+    return;
+  }
+  if (T <= keff) {                                      // (only when the bound is not binding)
+    for (uint32_t i = t; i < keff; i += kCThreads) out[i] = i < T ? (int32_t)sh.idx[i] : -1;
+    return;
+  }
+  // The bin holding the keff-th largest superset key, and the rank still to place inside it.
+  {
+    const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
+    uint32_t total;
+    const uint32_t run = block_exclusive_sum(h0 + h1, &total, sh.red);
+    if (run < keff && run + h0 + h1 >= keff) {
+      if (run + h0 >= keff) { sh.misc[0] = kBins - 1 - 2 * t; sh.misc[1] = run; }
+      else { sh.misc[0] = kBins - 2 - 2 * t; sh.misc[1] = run + h0; }
+    }
+    __syncthreads();
+  }
+  const uint32_t bstar2 = sh.misc[0], rank = keff - sh.misc[1];
+  for (uint32_t i = t; i < T; i += kCThreads) {
+    const uint32_t v = sh.key[i];
+    if (bin2(v) == bstar2) {
+      const uint32_t slot = atomicAdd(&sh.misc[2], 1u);
+      if (slot < (uint32_t)kBinCap) sh.binv[slot] = v;
+    }
+  }
+  __syncthreads();
+  const uint32_t nbin = sh.misc[2];
+  uint32_t tau, ties_take;
+  if (nbin <= (uint32_t)kBinCap) {
+    // tau is the key kappa of the bin with #{> kappa} < rank <= #{>= kappa}.
+    if (t < nbin) {
+      const uint32_t kappa = sh.binv[t];
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t j = 0; j < nbin; ++j) {
+        const uint32_t v = sh.binv[j];
+        gt += v > kappa ? 1u : 0u;
+        ge += v >= kappa ? 1u : 0u;
+      }
+      if (gt < rank && rank <= ge) { sh.misc[3] = kappa; sh.misc[4] = rank - gt; }
+    }
+    __syncthreads();
+    tau = sh.misc[3];
+    ties_take = sh.misc[4];
+  } else {                                              // a crowded bin (heavy ties): radix select
+    uint32_t hi = 0;
+    for (uint32_t i = t; i < T; i += kCThreads) hi = max(hi, sh.key[i]);
+    uint32_t unused = 0xFFFFFFFFu;
+    block_minmax(&unused, &hi, sh.red);
+    tau = block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, &ties_take);
+  }
+  ordered_select([&](uint32_t i) { return sh.key[i]; }, [&](uint32_t i) { return sh.idx[i]; }, T, tau, ties_take,
+                 keff, out, sh);
 }
 
 template <typename ET, int NH>
-void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a) {
-  switch (a.lpc) {
-    case 1: hipLaunchKernelGGL((score_kernel<ET, NH, 1>), grid, dim3(kThreads), 0, s, a); break;
+void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a, int lpc) {
+  switch (lpc) {
     case 2: hipLaunchKernelGGL((score_kernel<ET, NH, 2>), grid, dim3(kThreads), 0, s, a); break;
     case 4: hipLaunchKernelGGL((score_kernel<ET, NH, 4>), grid, dim3(kThreads), 0, s, a); break;
     case 8: hipLaunchKernelGGL((score_kernel<ET, NH, 8>), grid, dim3(kThreads), 0, s, a); break;
@@ -677,21 +732,12 @@ void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a) {
 }
 
 template <typename ET>
-void launch_scores(dim3 grid, hipStream_t s, const Args& a) {
-  if (a.nh <= 1) launch_scores_nh<ET, 1>(grid, s, a);
-  else if (a.nh <= 2) launch_scores_nh<ET, 2>(grid, s, a);
-  else if (a.nh <= 4) launch_scores_nh<ET, 4>(grid, s, a);
-  else if (a.nh <= 8) launch_scores_nh<ET, 8>(grid, s, a);
-  else launch_scores_nh<ET, 16>(grid, s, a);
-}
-
-// Groups per K1 chunk: the coarsest choice that still gives the longest sequence at least 2k
-// group maxima (finer groups give a weaker bound, coarser ones too few groups).
-int pick_groups(int64_t max_cand, int32_t chunk, int32_t k, const int* choices, int nchoices) {
-  const int64_t nch = (max_cand + chunk - 1) / chunk;
-  for (int i = 0; i < nchoices; ++i)
-    if (nch * choices[i] >= 2LL * k) return choices[i];
-  return choices[nchoices - 1];
+void launch_scores(dim3 grid, hipStream_t s, const Args& a, int lpc) {
+  if (a.nh <= 1) launch_scores_nh<ET, 1>(grid, s, a, lpc);
+  else if (a.nh <= 2) launch_scores_nh<ET, 2>(grid, s, a, lpc);
+  else if (a.nh <= 4) launch_scores_nh<ET, 4>(grid, s, a, lpc);
+  else if (a.nh <= 8) launch_scores_nh<ET, 8>(grid, s, a, lpc);
+  else launch_scores_nh<ET, 16>(grid, s, a, lpc);
 }
 
 }  // namespace
@@ -714,13 +760,13 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
     return CHS_ERR_SHAPE;
   if (max_cand > kMaxCand) return CHS_ERR_UNSUPPORTED;
   const size_t es = elem_size(dtype);
-  int nvec = 0, lpc = 1;
+  int nvec = 0, lpc = 2;
   if (q_idx) {
-    if (n_heads < 1 || n_heads > 16 || head_dim < 8 || head_dim > 512 || (head_dim * es) % 16 != 0)
+    if (n_heads < 1 || n_heads > 16 || head_dim < 8 || head_dim * es > 1024 || (head_dim * es) % 16 != 0)
       return CHS_ERR_SHAPE;
     if (!w || !k_idx) return CHS_ERR_NULL;
     nvec = (int)(head_dim * es / 16);   // 16-byte vectors per key row (<= 64)
-    while (lpc < nvec) lpc *= 2;        // one vector per lane
+    while (lpc < nvec) lpc *= 2;        // one vector per lane, at least two lanes per row
   } else if (!scores) {
     return CHS_ERR_NULL;
   }
@@ -730,35 +776,31 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
   Args a;
   a.q = q_idx; a.w = w; a.keys = k_idx; a.cu = cu_cand; a.max_cand = max_cand;
-  a.nh = n_heads; a.nvec = nvec; a.lpc = lpc; a.k = k; a.scores = scores; a.ws = ws;
-  if (q_idx) {
-    static const int score_groups[3] = {1, 4, 32};
-    a.chunk = (kThreads / lpc) * kPasses;
-    a.gpc = pick_groups(max_cand, a.chunk, k, score_groups, 3);
-  } else {
-    static const int max_groups[3] = {1, 4, 16};
-    a.chunk = kMaxChunk;
-    a.gpc = pick_groups(max_cand, a.chunk, k, max_groups, 3);
-  }
+  a.nh = n_heads; a.nvec = nvec; a.k = k; a.scores = scores; a.ws = ws;
+  a.gs = kGroup;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_cand > 0) {
-    // Persistent grid: about kScoreGrid workgroups over all sequences.
-    const int64_t chunks = (max_cand + a.chunk - 1) / a.chunk;
-    const int64_t per_seq = std::max<int64_t>(1, kScoreGrid / batch);
-    const dim3 grid((unsigned)std::min<int64_t>(chunks, per_seq), (unsigned)batch);
     if (q_idx) {
-      if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, a);
-      else launch_scores<float>(grid, s, a);
+      const int rw = kPasses * (64 / lpc);              // rows per wave
+      a.gs = std::min(rw, kGroup);
+      const dim3 grid((unsigned)((max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
+      if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, a, lpc);
+      else launch_scores<float>(grid, s, a, lpc);
     } else {
-      hipLaunchKernelGGL(max_kernel, grid, dim3(kThreads), 0, s, a);
+      // Loads per lane: the most (up to kPasses) that still give about 1024 workgroups
+      // (a workgroup covers 1024 * p scores).
+      int p = kPasses;
+      while (p > 1 && (int64_t)batch * ((max_cand + 1024 * p - 1) / (1024 * p)) < 1024) p /= 2;
+      const dim3 grid((unsigned)((max_cand + 1024 * p - 1) / (1024 * p)), (unsigned)batch);
+      switch (p) {
+        case 1: hipLaunchKernelGGL(max_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(max_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(max_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL(max_kernel<kPasses>, grid, dim3(kThreads), 0, s, a); break;
+      }
     }
     if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-    hipLaunchKernelGGL(bound_kernel, dim3((unsigned)batch), dim3(kThreads), 0, s, a);
-    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-    const dim3 sgrid((unsigned)((max_cand + kSelChunk - 1) / kSelChunk), (unsigned)batch);
-    hipLaunchKernelGGL(select_kernel, sgrid, dim3(kThreads), 0, s, a);
-    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL(final_kernel, dim3((unsigned)batch), dim3(kThreads), 0, s, a, topk);
+  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
   return launch_status();
 }

@@ -117,7 +117,8 @@ chs_status chs_compress(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, co
  * workspace: chs_index_topk_workspace_size(batch, max_cand, k) bytes.
  * Ranges: 1 <= batch <= 65535; 1 <= k <= 2048; 0 <= max_cand <= 4194304 (CHS_ERR_UNSUPPORTED
  *   above); with q_idx:
- *   1 <= n_heads <= 16, 8 <= head_dim <= 512, head_dim*elem_size % 16 == 0. */
+ *   1 <= n_heads <= 16, head_dim >= 8, head_dim*elem_size % 16 == 0 and <= 1024 bytes
+ *   (bf16 up to 512, fp32 up to 256). */
 size_t chs_index_topk_workspace_size(int32_t batch, int64_t max_cand, int32_t k);
 chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
                           int32_t k, const void* q_idx, const float* w, const void* k_idx,

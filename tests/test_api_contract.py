@@ -58,7 +58,7 @@ def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, 
 @pytest.mark.parametrize("kw,code", [
     (dict(dt=2), DTYPE), (dict(k=0), SHAPE), (dict(k=2049), SHAPE), (dict(batch=0), SHAPE),
     (dict(maxc=-1), SHAPE), (dict(maxc=1 << 31), SHAPE), (dict(nh=0), SHAPE), (dict(nh=17), SHAPE),
-    (dict(dim=4), SHAPE), (dict(dim=12), SHAPE), (dict(dim=1024), SHAPE), (dict(w=None), NULL),
+    (dict(dim=4), SHAPE), (dict(dim=12), SHAPE), (dict(dim=1024), SHAPE), (dict(dt=0, dim=512), SHAPE), (dict(w=None), NULL),
     (dict(kk=None), NULL), (dict(q=None, s=None), NULL), (dict(cu=None), NULL), (dict(out=None), NULL),
     (dict(ws=None), NULL), (dict(wsb=16), WS),
 ])
