@@ -57,7 +57,7 @@ constexpr int kTile = kCThreads * kMaxPerThread;   // 8192: the bound ranks the 
 constexpr int kBins = 2048;            // bound and superset histograms; global radix bins
 constexpr int kListCap = 8192;         // groups the LDS list holds
 constexpr int kLdsCand = 8192;         // superset entries LDS holds
-constexpr int kItemRounds = 8;         // superset items (4 candidates each) per K2 thread per batch
+constexpr int kItemRounds = 6;         // superset items (4 candidates each) per K2 thread per batch
 constexpr int kBinCap = 64;            // threshold-bin entries resolved directly
 constexpr int kGlobalRounds = 16;      // global path: scores per thread per batch
 constexpr int kScanRounds = 16;        // the most rounds one ordered scan covers
@@ -170,32 +170,41 @@ __device__ __forceinline__ uint32_t mask_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Exclusive prefix sum over the block (blockDim.x a multiple of 64); scratch: blockDim.x / 64
-// words. *total gets the sum.
-__device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* total, uint32_t* scratch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+// Block-wide helpers for the K2 block (kCWaves waves, declared below). The wave partials go
+// through LDS and every thread reads all of them with 16-byte loads, so no dependent chain of
+// LDS reads forms. `scratch` is 16-byte aligned; each call ends with a barrier.
+template <int NW>
+__device__ uint32_t block_exclusive_sum_t(uint32_t v, uint32_t* total, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_inclusive_sum(v);
   if (lane == 63) scratch[wave] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
-  for (int w = 0; w < nw; ++w) {
-    const uint32_t t = scratch[w];
-    before += (w < wave) ? t : 0u;
-    all += t;
+#pragma unroll
+  for (int w = 0; w < NW; w += 4) {
+    const u32x4 p = *reinterpret_cast<const u32x4*>(&scratch[w]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { before += (w + j < wave) ? p[j] : 0u; all += p[j]; }
   }
   __syncthreads();
   *total = all;
   return before + inc - v;
 }
 
-// Block-wide (min, max) of unsigned values; scratch: 2 * blockDim.x / 64 words.
-__device__ void block_minmax(uint32_t* vmin, uint32_t* vmax, uint32_t* scratch) {
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+template <int NW>
+__device__ void block_minmax_t(uint32_t* vmin, uint32_t* vmax, uint32_t* scratch) {
+  const int wave = threadIdx.x >> 6;
   const uint32_t lo = ~wave_max(~*vmin), hi = wave_max(*vmax);
-  if ((threadIdx.x & 63) == 0) { scratch[2 * wave] = lo; scratch[2 * wave + 1] = hi; }
+  if ((threadIdx.x & 63) == 0) { scratch[wave] = lo; scratch[NW + wave] = hi; }
   __syncthreads();
   uint32_t l = 0xFFFFFFFFu, h = 0;
-  for (int w = 0; w < nw; ++w) { l = min(l, scratch[2 * w]); h = max(h, scratch[2 * w + 1]); }
+#pragma unroll
+  for (int w = 0; w < NW; w += 4) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(&scratch[w]);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(&scratch[NW + w]);
+    l = min(min(l, min(x[0], x[1])), min(x[2], x[3]));
+    h = max(max(h, max(y[0], y[1])), max(y[2], y[3]));
+  }
   __syncthreads();
   *vmin = l; *vmax = h;
 }
@@ -387,13 +396,13 @@ __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------- K2: collect and select
-struct CollectShared {
+struct alignas(16) CollectShared {
   uint32_t key[kLdsCand];       // superset keys, index order
   uint32_t idx[kLdsCand];       // superset candidate indices
   uint32_t list[kListCap];      // groups whose maximum is >= L, ascending
   uint32_t hist[kBins];         // maxima bins (A), then superset bins (C, D)
-  uint32_t tot[kScanRounds * kCWaves + 1];
   uint32_t red[2 * kCWaves];
+  uint32_t tot[kScanRounds * kCWaves + 4];
   uint32_t binv[kBinCap];       // keys in the bin that holds the k-th largest
   uint32_t misc[8];
 };
@@ -408,11 +417,16 @@ __device__ uint32_t ordered_scan(const uint32_t (&cnt)[R], uint32_t (&off)[R], C
   constexpr int N = R * kCWaves;
   constexpr int PL = (N + 63) / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t wtot[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t inc = wave_inclusive_sum(cnt[r]);
     off[r] = inc - cnt[r];
-    if (lane == 63) sh.tot[wave * R + r] = inc;
+    wtot[r] = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sh.tot[wave * R + r] = wtot[r];
   }
   __syncthreads();
   if (threadIdx.x < 64) {
@@ -470,7 +484,7 @@ __device__ uint32_t block_radix_select(Get get, uint32_t m, uint32_t r, uint32_t
     const uint32_t t = threadIdx.x;
     const uint32_t c0 = sh.hist[kBins - 1 - 2 * t], c1 = sh.hist[kBins - 2 - 2 * t];
     uint32_t total;
-    const uint32_t run = block_exclusive_sum(c0 + c1, &total, sh.red);
+    const uint32_t run = block_exclusive_sum_t<kCWaves>(c0 + c1, &total, sh.red);
     if (run < r && run + c0 + c1 >= r) {
       if (run + c0 >= r) { sh.misc[0] = kBins - 1 - 2 * t; sh.misc[1] = run; }
       else { sh.misc[0] = kBins - 2 - 2 * t; sh.misc[1] = run + c0; }
@@ -485,22 +499,22 @@ __device__ uint32_t block_radix_select(Get get, uint32_t m, uint32_t r, uint32_t
 }
 
 // Writes, ascending, the indices of the m candidates (key from `key`, index from `idx`, in
-// index order) that are above tau or among the first ties_take equal to it.
-template <typename GK, typename GI>
+// index order) that are above tau or among the first ties_take equal to it. R rounds of the
+// block per batch (R * 1024 candidates).
+template <int R, typename GK, typename GI>
 __device__ void ordered_select(GK key, GI idx, uint32_t m, uint32_t tau, uint32_t ties_take, uint32_t keff,
                                int32_t* out, CollectShared& sh) {
   uint32_t ties_before = 0, sel_before = 0;
-  for (uint32_t x0 = 0; x0 < m; x0 += kGlobalRounds * kCThreads) {
-    uint32_t kk[kGlobalRounds], c[kGlobalRounds], off[kGlobalRounds];
+  for (uint32_t x0 = 0; x0 < m; x0 += R * kCThreads) {
+    uint32_t kk[R], c[R], off[R];
 #pragma unroll
-    for (int q = 0; q < kGlobalRounds; ++q) kk[q] = key(min(x0 + q * kCThreads + threadIdx.x, m - 1));
+    for (int q = 0; q < R; ++q) kk[q] = key(min(x0 + q * kCThreads + threadIdx.x, m - 1));
 #pragma unroll
-    for (int q = 0; q < kGlobalRounds; ++q)
-      c[q] = (x0 + q * kCThreads + threadIdx.x < m && kk[q] == tau) ? 1u : 0u;
+    for (int q = 0; q < R; ++q) c[q] = (x0 + q * kCThreads + threadIdx.x < m && kk[q] == tau) ? 1u : 0u;
     const uint32_t tie_total = ordered_scan(c, off, sh);
     uint32_t take = 0;
 #pragma unroll
-    for (int q = 0; q < kGlobalRounds; ++q) {
+    for (int q = 0; q < R; ++q) {
       const bool in = x0 + q * kCThreads + threadIdx.x < m;
       const bool t = in && (kk[q] > tau || (kk[q] == tau && ties_before + off[q] < ties_take));
       take |= (t ? 1u : 0u) << q;
@@ -508,7 +522,7 @@ __device__ void ordered_select(GK key, GI idx, uint32_t m, uint32_t tau, uint32_
     }
     const uint32_t sel_total = ordered_scan(c, off, sh);
 #pragma unroll
-    for (int q = 0; q < kGlobalRounds; ++q) {
+    for (int q = 0; q < R; ++q) {
       const uint32_t pos = sel_before + off[q];
       if (((take >> q) & 1u) && pos < keff) out[pos] = (int32_t)idx(x0 + q * kCThreads + threadIdx.x);
     }
@@ -554,7 +568,7 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
 #pragma unroll
   for (int j = 0; j < kMaxPerThread; ++j)
     if (kMaxPerThread * t + j < nt) { vmin = min(vmin, mv[j]); vmax = max(vmax, mv[j]); }
-  block_minmax(&vmin, &vmax, sh.red);                   // its barriers also order the clears
+  block_minmax_t<kCWaves>(&vmin, &vmax, sh.red);                   // its barriers also order the clears
   uint32_t L = 0;                                       // with fewer than k groups: every candidate
   if (nt >= keff) {
     const uint32_t span = vmax - vmin;
@@ -567,7 +581,7 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
     __syncthreads();
     const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
     uint32_t total;
-    const uint32_t run = block_exclusive_sum(h0 + h1, &total, sh.red);
+    const uint32_t run = block_exclusive_sum_t<kCWaves>(h0 + h1, &total, sh.red);
     if (run < keff && run + h0 + h1 >= keff) sh.misc[0] = run + h0 >= keff ? kBins - 1 - 2 * t : kBins - 2 - 2 * t;
     __syncthreads();
     const uint32_t bstar = sh.misc[0];
@@ -575,7 +589,7 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j)
       if (kMaxPerThread * t + j < nt && bin(mv[j]) >= bstar) lmin = min(lmin, mv[j]);
-    block_minmax(&lmin, &unused, sh.red);
+    block_minmax_t<kCWaves>(&lmin, &unused, sh.red);
     L = lmin;
   }
   for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;   // reused for the superset
@@ -613,6 +627,7 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
   if (fits) {
     const uint32_t E = G << gshift;                     // candidate slots of the listed groups
     const uint32_t NI = (E + 3) / 4;                    // items of four (a group holds >= 8)
+    const bool vec = (reinterpret_cast<uintptr_t>(sp) & 15) == 0;   // then items are 16-byte aligned
     for (uint32_t i0 = 0; i0 < NI; i0 += kItemRounds * kCThreads) {
       uint32_t kk[kItemRounds][4], cb[kItemRounds], cnt[kItemRounds], off[kItemRounds], f = 0;
 #pragma unroll
@@ -620,11 +635,26 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
         const uint32_t x = 4 * min(i0 + r * kCThreads + t, NI - 1);
         cb[r] = (sh.list[x >> gshift] << gshift) + (x & (gs - 1));
       }
+      if (vec) {                                        // one aligned 16-byte load per item
 #pragma unroll
-      for (int r = 0; r < kItemRounds; ++r)
+        for (int r = 0; r < kItemRounds; ++r) {
+          const u32x4 v = buffer_u32x4(srs, cb[r]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kk[r][e] = buffer_u32(srs, cb[r] + e);
+          for (int e = 0; e < 4; ++e) kk[r][e] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < kItemRounds; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[r][e] = buffer_u32(srs, cb[r] + e);
+      }
       __builtin_amdgcn_sched_barrier(0);                // every load is in flight before any use
+      if (vec) {                                        // the item that straddles the end, if any
+#pragma unroll
+        for (int r = 0; r < kItemRounds; ++r)
+          if (cb[r] < n && cb[r] + 4 > n)
+            for (int e = 0; e < 4; ++e) kk[r][e] = buffer_u32(srs, cb[r] + e);
+      }
 #pragma unroll
       for (int r = 0; r < kItemRounds; ++r) {
         const uint32_t x = 4 * (i0 + r * kCThreads + t);
@@ -663,7 +693,7 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
     uint32_t ties_take;
     const uint32_t tau = block_radix_select([&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); },
                                             n, keff, 0u, 0xFFFFFFFFu, sh, &ties_take);
-    ordered_select([&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); },
+    ordered_select<kGlobalRounds>([&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); },
                    [&](uint32_t i) { return i; }, n, tau, ties_take, keff, out, sh);
     return;
   }
@@ -675,7 +705,7 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
   {
     const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
     uint32_t total;
-    const uint32_t run = block_exclusive_sum(h0 + h1, &total, sh.red);
+    const uint32_t run = block_exclusive_sum_t<kCWaves>(h0 + h1, &total, sh.red);
     if (run < keff && run + h0 + h1 >= keff) {
       if (run + h0 >= keff) { sh.misc[0] = kBins - 1 - 2 * t; sh.misc[1] = run; }
       else { sh.misc[0] = kBins - 2 - 2 * t; sh.misc[1] = run + h0; }
@@ -712,11 +742,14 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
     uint32_t hi = 0;
     for (uint32_t i = t; i < T; i += kCThreads) hi = max(hi, sh.key[i]);
     uint32_t unused = 0xFFFFFFFFu;
-    block_minmax(&unused, &hi, sh.red);
+    block_minmax_t<kCWaves>(&unused, &hi, sh.red);
     tau = block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, &ties_take);
   }
-  ordered_select([&](uint32_t i) { return sh.key[i]; }, [&](uint32_t i) { return sh.idx[i]; }, T, tau, ties_take,
-                 keff, out, sh);
+  auto lk = [&](uint32_t i) { return sh.key[i]; };
+  auto li = [&](uint32_t i) { return sh.idx[i]; };
+  if (T <= kCThreads) ordered_select<1>(lk, li, T, tau, ties_take, keff, out, sh);
+  else if (T <= 2 * kCThreads) ordered_select<2>(lk, li, T, tau, ties_take, keff, out, sh);
+  else ordered_select<8>(lk, li, T, tau, ties_take, keff, out, sh);
 }
 
 template <typename ET, int NH>
