@@ -261,6 +261,32 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Four heads over a 16-lane row: s = sum_h w_h * ReLU(sum over the row of p[h]), in every
+// lane of the row. Reduce-scatter: two exchanges leave lane l with head 2*(l&1) + ((l>>1)&1)
+// summed over its quad, row rotations by 4 and 8 finish that head's sum over the row, and a
+// quad sum adds the weighted heads; wl is this lane's head weight.
+__device__ __forceinline__ float head4_row_score(const float (&p)[4], float wl, int lane) {
+  const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+  auto dpp = [](float v, int ctrl) {
+    switch (ctrl) {
+      case 0xB1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+      case 0x124: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+    }
+  };
+  const float s0 = b0 ? p[0] : p[2], s1 = b0 ? p[1] : p[3];        // sent to lane ^ 1
+  const float a0 = (b0 ? p[2] : p[0]) + dpp(s0, 0xB1);             // heads (0,1) or (2,3)
+  const float a1 = (b0 ? p[3] : p[1]) + dpp(s1, 0xB1);
+  float h = (b1 ? a1 : a0) + dpp(b1 ? a0 : a1, 0x4E);              // one head per lane
+  h += dpp(h, 0x124);                                              // row_ror:4
+  h += dpp(h, 0x128);                                              // row_ror:8
+  float r = fmaxf(h, 0.f) * wl;
+  r += dpp(r, 0xB1);
+  r += dpp(r, 0x4E);
+  return r;
+}
+
 // Row geometry of K1 for LPC lanes per key row.
 template <int LPC>
 struct ScoreGeom {
@@ -312,19 +338,43 @@ __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
   }
   float* sp = score_ptr(a, b, c0);
   uint32_t* gmax = maxima_ptr(a, b);
+  // The four-head row reduction applies when a row is exactly one 16-lane DPP row.
+  constexpr bool kHead4 = (NH == 4 && LPC == 16);
+  float wl = 0.f;
+  if (kHead4) {
+    const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+    wl = b0 ? (b1 ? wv[3] : wv[2]) : (b1 ? wv[1] : wv[0]);
+  }
   uint32_t gm[G::NG];
 #pragma unroll
   for (int g = 0; g < G::NG; ++g) gm[g] = 0u;
+  // With LPC >= 8, lane (slot * LPC + u) keeps pass u's score, so one store per wave writes the
+  // wave's RW consecutive scores.
+  constexpr bool kGather = LPC >= kPasses;
+  float mine = 0.f;
 #pragma unroll
   for (int u = 0; u < kPasses; ++u) {
     const int64_t row = row0 + u * G::RP + slot;
-    float s = 0.f;
+    float s;
+    if (kHead4) {
+      float pd[4];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) s = fmaf(wv[h], fmaxf(group_sum<LPC>(Dot16<ET>::dot(qv[h], kv[u])), 0.f), s);
+      for (int h = 0; h < 4; ++h) pd[h] = Dot16<ET>::dot(qv[h], kv[u]);
+      s = head4_row_score(pd, wl, lane);
+    } else {
+      s = 0.f;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) s = fmaf(wv[h], fmaxf(group_sum<LPC>(Dot16<ET>::dot(qv[h], kv[u])), 0.f), s);
+    }
     const bool valid = row < n;
-    if (sub == 0 && valid) sp[row] = s;
+    if (kGather) mine = (sub == u) ? s : mine;
+    else if (sub == 0 && valid) sp[row] = s;
     const uint32_t key = valid ? score_key(s) : 0u;   // 0: below every key
     gm[u / G::PG] = max(gm[u / G::PG], key);
+  }
+  if (kGather) {
+    const int64_t row = row0 + sub * G::RP + slot;
+    if (sub < kPasses && row < n) sp[row] = mine;
   }
 #pragma unroll
   for (int g = 0; g < G::NG; ++g) {
