@@ -31,6 +31,13 @@ namespace chs {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// An LDS address as the transposing load builtin takes it.
+__device__ __forceinline__ __attribute__((address_space(3))) v4i16* lds_v4i16(const uint16_t* p) {
+  return (__attribute__((address_space(3))) v4i16*)(p);
+}
 
 constexpr int kThreads = 256;
 constexpr int kKeysPerChunk = 32;
@@ -128,15 +135,17 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   const int32_t s_end = min(s_begin + a.kps, sm.nslots());
 
   // Q fragment (A operand): row c of this wave's 16 heads, d = 32t + 8g .. +8.
+  // Loaded unconditionally (head index clamped, then zeroed) so the loads stay in flight
+  // behind the first chunk's index and row gathers; they are first used by the S MFMA.
   bf16x8 qf[D / 32];
   {
     const int h = h_base + c;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + h) * D;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + min(h, a.H - 1)) * D;
+    u32x4 qv[D / 32];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      u32x4 v = (h < a.H) ? *reinterpret_cast<const u32x4*>(qp + 32 * t + 8 * g) : u32x4{0, 0, 0, 0};
-      qf[t] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int t = 0; t < D / 32; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qp + 32 * t + 8 * g);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, h < a.H ? qv[t] : u32x4{0, 0, 0, 0});
   }
   f32x4 o[D / 16];
 #pragma unroll
@@ -217,17 +226,16 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         pw[(4 * g + r) * P_PITCH + 16 * n + c] = (uint16_t)(__float_as_uint(p[n][r]) >> 16);
     __syncthreads();
     const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pw[c * P_PITCH + 8 * g]));
-    // B operand of P.V: column 16j + c of the tile, keys 8g .. 8g+7.
-    const uint16_t* vcol = &kn[(8 * g) * KN_PITCH + c];
+    // B operand of P.V: column 16j + c of the tile, keys 8g .. 8g+7. ds_read_b64_tr_b16 gives
+    // lane i of a 16-lane group element e of the group's 8-byte chunks read with stride 16,
+    // so lane c addressing channels 16j + 4(c&3) .. +3 of key row 8g + (c>>2) (+4 for the
+    // upper half) receives keys 8g .. 8g+3 (8g+4 .. 8g+7) of channel 16j + c.
+    const uint16_t* vrow = &kn[(8 * g + (c >> 2)) * KN_PITCH + 4 * (c & 3)];
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
-      u32x4 vb;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const uint32_t lo = vcol[(2 * x) * KN_PITCH + 16 * j];
-        const uint32_t hi = vcol[(2 * x + 1) * KN_PITCH + 16 * j];
-        vb[x] = lo | (hi << 16);
-      }
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 16 * j));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 4 * KN_PITCH + 16 * j));
+      const v8i16 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8, vb), o[j], 0, 0, 0);
     }
   }
@@ -332,6 +340,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 // of their tile, sequence); each thread reads one 16-byte accumulator (4 heads x 1 channel)
 // per split, so every load is a whole, coalesced vector. Split weights are computed once per
 // head in LDS.
+// Four lanes of a quad share one accumulator word, each summing a strided quarter of the
+// splits, so a launch has four times as many workgroups as words / 256.
+constexpr int kCombineLanes = 4;
+
 __global__ __launch_bounds__(kThreads) void combine_mfma_kernel(AttnArgs a, float* out, float* lse) {
   __shared__ float wts[16][kCombineSplits];
   __shared__ float lpart[16][kCombineSplits];
@@ -339,49 +351,76 @@ __global__ __launch_bounds__(kThreads) void combine_mfma_kernel(AttnArgs a, floa
   const int b = blockIdx.z, hg = blockIdx.y;          // heads 16 hg .. 16 hg + 15
   const int tid = threadIdx.x, D = a.D;
   const int ns = a.n_splits;
-  // Weights: thread (h, s) pairs.
-  for (int e = tid; e < 16 * ns; e += kThreads) {
-    const int hl = e / ns, sp = e - hl * ns;
-    const int h = 16 * hg + hl;
-    float ms = -INFINITY, ls = 0.f;
-    if (h < a.H) {
-      ms = a.part_ml[(((int64_t)b * ns + sp) * a.H + h) * 2];
-      ls = a.part_ml[(((int64_t)b * ns + sp) * a.H + h) * 2 + 1];
-    }
-    wts[hl][sp] = ms;
-    lpart[hl][sp] = ls;
-  }
-  __syncthreads();
-  if (tid < 16) {
-    const int h = 16 * hg + tid;
-    float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, wts[tid][sp]);
-    float L = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float ms = wts[tid][sp];
-      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      wts[tid][sp] = wgt;
-      L += wgt * lpart[tid][sp];
-    }
-    lsum[tid] = L;
-    if (lse && h < a.H) lse[(int64_t)b * a.H + h] = (L > 0.f) ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
-  }
-  __syncthreads();
+  const int sq = tid & (kCombineLanes - 1);           // this lane's quarter of the splits
   // Accumulator word index within the wave tile: (j, lane); this thread's 4 heads 4g + r.
-  const int wpos = blockIdx.x * kThreads + tid;       // (j * 64 + lane)
-  if (wpos >= (D / 16) * 64) return;
+  const int wraw = blockIdx.x * (kThreads / kCombineLanes) + tid / kCombineLanes;
+  const int wpos = min(wraw, (D / 16) * 64 - 1);
   const int j = wpos >> 6, lane = wpos & 63, g = lane >> 4, c = lane & 15;
   const int tile = hg >> 2, wave = hg & 3;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o);
   const int64_t stride = (int64_t)a.head_tiles * 4 * (D / 16) * 64;   // one split, in f32x4
   const int64_t base = (((int64_t)b * ns * a.head_tiles + tile) * 4 + wave) * (D / 16) * 64 + wpos;
-#pragma unroll 4
-  for (int sp = 0; sp < ns; ++sp) {
-    const f32x4 v = po[base + sp * stride];
+  // This lane's first splits (sq, sq + 4, ...) are requested before anything else, so they
+  // arrive while the split weights are computed.
+  constexpr int kBatch = 8;
+  f32x4 v[kBatch];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = fmaf(wts[4 * g + r][sp], v[r], acc[r]);
+  for (int q = 0; q < kBatch; ++q) v[q] = po[base + (int64_t)min(sq + kCombineLanes * q, ns - 1) * stride];
+  // The 16 heads' (max, sum) pairs of every split come through LDS in one coalesced pass; then
+  // head hl = tid / 16 is handled by the 16 lanes of one DPP row, each lane a strided subset of
+  // the splits, and the head's maximum and weighted sum are row reductions.
+  const int nh = min(16, a.H - 16 * hg);
+  for (int e = tid; e < ns * nh; e += kThreads) {
+    const int sp = e / nh, hl = e - sp * nh;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * ns + sp) * a.H + 16 * hg + hl) * 2);
+    wts[hl][sp] = ml.x;
+    lpart[hl][sp] = ml.y;
   }
+  __syncthreads();
+  {
+    const int hl = tid >> 4, sl = tid & 15;
+    const int h = 16 * hg + hl;
+    float M = -INFINITY;
+    if (hl < nh)
+      for (int sp = sl; sp < ns; sp += 16) M = fmaxf(M, wts[hl][sp]);
+    M = row16_max(M);
+    float L = 0.f;
+    for (int sp = sl; sp < ns; sp += 16) {
+      const float ms = hl < nh ? wts[hl][sp] : -INFINITY;
+      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      L += wgt * (hl < nh ? lpart[hl][sp] : 0.f);
+      wts[hl][sp] = wgt;
+    }
+    L = row16_sum(L);
+    if (sl == 0) {
+      lsum[hl] = L;
+      if (lse && hl < nh && blockIdx.x == 0) lse[(int64_t)b * a.H + h] = (L > 0.f) ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = 0; sp0 < ns; sp0 += kCombineLanes * kBatch) {
+    if (sp0 > 0) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        v[q] = po[base + (int64_t)min(sp0 + sq + kCombineLanes * q, ns - 1) * stride];
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int sp = sp0 + sq + kCombineLanes * q;
+      if (sp < ns) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(wts[4 * g + r][sp], v[q][r], acc[r]);
+      }
+    }
+  }
+  // Quad sum: the four lanes of a word hold disjoint split subsets.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    acc[r] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc[r]), 0xB1, 0xF, 0xF, false));
+    acc[r] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc[r]), 0x4E, 0xF, 0xF, false));
+  }
+  if (sq != 0 || wraw >= (D / 16) * 64) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int hl = 4 * g + r, h = 16 * hg + hl;
@@ -518,7 +557,8 @@ extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   if (dtype == CHS_BF16) {
-    const dim3 cgrid((unsigned)((d / 16 * 64 + kThreads - 1) / kThreads), (unsigned)((n_heads + 15) / 16),
+    const int words_per_block = kThreads / kCombineLanes;
+    const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
                      (unsigned)batch);
     hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(kThreads), 0, s, a, out, lse);
   } else {
