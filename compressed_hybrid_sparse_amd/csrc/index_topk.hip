@@ -15,27 +15,28 @@
 //      key row, one 16-byte non-temporal load each, so every wave load instruction reads one
 //      contiguous 1 KiB; v_dot2_f32_bf16 (or fp32 FMAs) and DPP sums form the head dots. Each
 //      wave owns a run of consecutive rows and issues all of its loads before the first use
-//      (the loads are unconditional, with clamped addresses, so the compiler can count them),
-//      then writes the fp32 scores plus the maximum order-preserving key of every group of GS
-//      consecutive candidates (GS = 32; 16 or 8 for very wide keys). max_kernel does the same
-//      for caller-provided scores.
-//   K2 collect_kernel, one 1024-thread workgroup per sequence:
-//      (A) loads the group maxima and bins them by key into 2048 monotone bins spanning their
-//          range; L = the smallest maximum in the bin that holds the k-th largest maximum.
-//          L never exceeds the k-th largest score, because k disjoint groups each hold a score
-//          >= L; so every top-k candidate, and every tie at the threshold, has key >= L and
-//          sits in a group whose maximum is >= L;
-//      (B) lists those groups in index order (each thread owns eight consecutive maxima; one
-//          block scan of the per-thread counts places them);
-//      (C) loads only the listed groups' scores (about k groups of 128 bytes at 1M context),
-//          keeps the candidates with key >= L in index order in LDS, and bins their keys into
-//          2048 monotone bins over [L, largest maximum];
+//      (the loads are unconditional, with clamped addresses, so the compiler can count them).
+//      It writes the fp32 scores and, for every group of GS consecutive candidates (GS = 32; 16
+//      or 8 for very wide keys), the group's largest key, the position of that maximum and
+//      its second-largest key. max_kernel does the same for caller-provided scores.
+//   K2 collect_kernel, one 1024-thread workgroup per sequence (one CU, so the work it does per
+//      candidate is what costs: it touches group statistics, not scores, wherever it can):
+//      (A) loads the group maxima and bins them, (key - smallest) >> shift, into 2048 monotone
+//          bins; L = the smallest maximum in the bin holding the k-th largest maximum. L never
+//          exceeds the k-th largest score, because k disjoint groups each hold a score >= L;
+//          so every top-k candidate, and every tie at the threshold, has key >= L and sits in
+//          a group whose maximum is >= L;
+//      (B) lists those groups in index order (one block scan of per-thread counts); a listed
+//          group whose second key is below L holds exactly one candidate >= L, its maximum,
+//          known from the statistics; the others ("full", typically a few percent) are read;
+//      (C) reads the full groups whole, two per wave, and builds the superset of keys >= L in
+//          index order in LDS, binning its keys into 2048 monotone bins over [L, max];
 //      (D) the bin holding the k-th largest kept key gives tau after comparing only the few
 //          keys inside it (a crowded bin, from heavy ties, falls back to radix steps); an
 //          ordered pass then writes the keys above tau and the first ties at tau, ascending
 //          by index (no sort).
-//      Inputs that defeat the bound (a superset too large for LDS: heavy ties, many equal
-//      zeros) are selected by the whole workgroup straight from the score array instead.
+//      Inputs that defeat the bound (a superset or list too large for LDS: heavy ties, many
+//      equal zeros) are selected by the whole workgroup straight from the score array instead.
 //      Gathers go through buffer loads (32-bit offsets, reads beyond the array return 0).
 // The composite order (key descending, then index ascending) is total, so the selected set is
 // unique and bit-identical to a full sort of the same scores.
@@ -55,8 +56,9 @@ constexpr int kCWaves = kCThreads / 64;
 constexpr int kMaxPerThread = 8;       // group maxima per K2 thread per tile (contiguous)
 constexpr int kTile = kCThreads * kMaxPerThread;   // 8192: the bound ranks the first tile
 constexpr int kBins = 2048;            // bound and superset histograms; global radix bins
-constexpr int kListCap = 8192;         // groups the LDS list holds
-constexpr int kLdsCand = 8192;         // superset entries LDS holds
+constexpr int kListCap = 4096;         // groups the LDS list holds
+constexpr int kLdsCand = 4096;         // superset entries LDS holds
+constexpr int kFullCap = 256;          // listed groups whose second key reaches L (scanned whole)
 constexpr int kItemRounds = 6;         // superset items (4 candidates each) per K2 thread per batch
 constexpr int kBinCap = 64;            // threshold-bin entries resolved directly
 constexpr int kGlobalRounds = 16;      // global path: scores per thread per batch
@@ -66,6 +68,7 @@ constexpr int64_t kMaxCand = 1 << 22;
 
 struct Workspace {
   uint32_t* maxima;   // [batch][mcap]: group maximum keys
+  uint32_t* second;   // [batch][mcap]: group statistics words (see pack_second)
   float* scores;      // [batch][rc] when the caller passes no score array
 };
 
@@ -78,9 +81,11 @@ size_t ws_layout(int32_t batch, int64_t max_cand, Workspace* w, char* base) {
   const int64_t mc = max_cand > 0 ? max_cand : 0;
   size_t off = 0;
   const size_t o_max = off; off = align_up(off + nb * (size_t)maxima_cap(mc) * 4, 256);
+  const size_t o_sec = off; off = align_up(off + nb * (size_t)maxima_cap(mc) * 4, 256);
   const size_t o_sc = off;  off = align_up(off + nb * (size_t)round_cand(mc) * 4, 256);
   if (w) {
     w->maxima = reinterpret_cast<uint32_t*>(base + o_max);
+    w->second = reinterpret_cast<uint32_t*>(base + o_sec);
     w->scores = reinterpret_cast<float*>(base + o_sc);
   }
   return off;
@@ -131,6 +136,35 @@ __device__ __forceinline__ float* score_ptr(const Args& a, int b, int64_t c0) {
 }
 __device__ __forceinline__ uint32_t* maxima_ptr(const Args& a, int b) {
   return a.ws.maxima + (size_t)b * maxima_cap(a.max_cand);
+}
+__device__ __forceinline__ uint32_t* second_ptr(const Args& a, int b) {
+  return a.ws.second + (size_t)b * maxima_cap(a.max_cand);
+}
+
+// Group statistics: the maximum key, the lowest position (< 32) holding it, and the largest
+// key at any other position. Stored as the maximum plus one word, (second & ~31) | position:
+// (word | 31) is never below the second key, so a test against it can only be conservative.
+struct Top2 {
+  uint32_t m1, p1, m2;
+};
+__device__ __forceinline__ uint32_t pack_second(const Top2& s) { return (s.m2 & ~31u) | s.p1; }
+// Adds key k at position p; a lane's positions grow from call to call, so ties keep the first.
+__device__ __forceinline__ void top2_add(Top2& s, uint32_t k, uint32_t p) {
+  const bool gt = k > s.m1;
+  s.m2 = gt ? s.m1 : max(s.m2, k);
+  s.p1 = gt ? p : s.p1;
+  s.m1 = gt ? k : s.m1;
+}
+__device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
+  Top2 r;
+  r.m1 = max(a.m1, b.m1);
+  r.p1 = a.m1 > b.m1 ? a.p1 : (b.m1 > a.m1 ? b.p1 : min(a.p1, b.p1));
+  r.m2 = max(max(a.m2, b.m2), min(a.m1, b.m1));
+  return r;
+}
+__device__ __forceinline__ Top2 top2_xor(const Top2& s, int o) {
+  return Top2{(uint32_t)__shfl_xor((int)s.m1, o, 64), (uint32_t)__shfl_xor((int)s.p1, o, 64),
+              (uint32_t)__shfl_xor((int)s.m2, o, 64)};
 }
 
 // ---------------------------------------------------------------- wave and block helpers
@@ -321,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
     qv[h] = qb[hc * nvec + subc];
     wv[h] = a.w[(size_t)b * a.nh + hc];
   }
+  __builtin_amdgcn_sched_barrier(0);                   // query loads go out (and return) first
   const u32x4* kb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.keys) + (size_t)c0 * nvec * 16);
   u32x4 kv[kPasses];
 #pragma unroll
@@ -329,6 +364,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
     if (row > n - 1) row = n - 1;
     kv[u] = __builtin_nontemporal_load(kb + row * nvec + subc);
   }
+  __builtin_amdgcn_sched_barrier(0);
   const bool sub_on = sub < nvec;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -345,9 +381,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
     const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
     wl = b0 ? (b1 ? wv[3] : wv[2]) : (b1 ? wv[1] : wv[0]);
   }
-  uint32_t gm[G::NG];
+  uint32_t* gsec = second_ptr(a, b);
+  Top2 st[G::NG];
 #pragma unroll
-  for (int g = 0; g < G::NG; ++g) gm[g] = 0u;
+  for (int g = 0; g < G::NG; ++g) st[g] = Top2{0u, 255u, 0u};
   // With LPC >= 8, lane (slot * LPC + u) keeps pass u's score, so one store per wave writes the
   // wave's RW consecutive scores.
   constexpr bool kGather = LPC >= kPasses;
@@ -370,20 +407,40 @@ __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
     if (kGather) mine = (sub == u) ? s : mine;
     else if (sub == 0 && valid) sp[row] = s;
     const uint32_t key = valid ? score_key(s) : 0u;   // 0: below every key
-    gm[u / G::PG] = max(gm[u / G::PG], key);
+    // Position of this row within its group: (u mod PG) * RP + slot.
+    top2_add(st[u / G::PG], key, (uint32_t)((u % G::PG) * G::RP + slot));
   }
   if (kGather) {
     const int64_t row = row0 + sub * G::RP + slot;
     if (sub < kPasses && row < n) sp[row] = mine;
   }
+  // The lanes of one key row agree; merge the statistics of the wave's rows.
 #pragma unroll
   for (int g = 0; g < G::NG; ++g) {
-    const uint32_t m = wave_max(gm[g]);
-    if (lane == 0) gmax[(row0 + g * G::GS) / G::GS] = m;
+#pragma unroll
+    for (int o = LPC; o < 64; o <<= 1) st[g] = top2_merge(st[g], top2_xor(st[g], o));
+    if (lane == 0) {
+      const int64_t gi = (row0 + g * G::GS) / G::GS;
+      gmax[gi] = st[g].m1;
+      gsec[gi] = pack_second(st[g]);
+    }
   }
 }
 
-// K1 for caller-provided scores: group maxima only. Wave w of block x covers 256 * P
+template <int CTRL>
+__device__ __forceinline__ Top2 top2_dpp(const Top2& s) {
+  return Top2{(uint32_t)__builtin_amdgcn_mov_dpp((int)s.m1, CTRL, 0xF, 0xF, false),
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)s.p1, CTRL, 0xF, 0xF, false),
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)s.m2, CTRL, 0xF, 0xF, false)};
+}
+// Merged over each group of 8 lanes (xor 1, xor 2, half-row mirror), every lane of the 8 gets it.
+__device__ __forceinline__ Top2 top2_merge8(Top2 s) {
+  s = top2_merge(s, top2_dpp<0xB1>(s));
+  s = top2_merge(s, top2_dpp<0x4E>(s));
+  return top2_merge(s, top2_dpp<0x141>(s));
+}
+
+// K1 for caller-provided scores: group statistics only. Wave w of block x covers 256 * P
 // consecutive scores starting at (4x + w) * 256 * P: P 16-byte loads per lane when the
 // sequence's scores are 16-byte aligned (a group of 32 is then 8 lanes of one load), else
 // 4P 4-byte loads (a group is half a wave of one load).
@@ -397,6 +454,7 @@ __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
   if (base >= n) return;
   const float* sp = score_ptr(a, b, c0);
   uint32_t* gmax = maxima_ptr(a, b);
+  uint32_t* gsec = second_ptr(a, b);
   const int64_t nfull = n / 4;                         // whole 16-byte vectors in the sequence
   if ((reinterpret_cast<uintptr_t>(sp) & 15) == 0 && nfull > 0) {
     f32x4 v[P];
@@ -409,17 +467,16 @@ __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       const int64_t j0 = base + (u * 64 + lane) * 4;
-      uint32_t m = 0;
+      Top2 st{0u, 255u, 0u};
       if (j0 < 4 * nfull) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) m = max(m, score_key(v[u][e]));
+        for (int e = 0; e < 4; ++e) top2_add(st, score_key(v[u][e]), (uint32_t)((lane & 7) * 4 + e));
       } else {
-        for (int e = 0; e < 4; ++e) if (j0 + e < n) m = max(m, score_key(sp[j0 + e]));   // the tail
+        for (int e = 0; e < 4; ++e)                    // the tail
+          top2_add(st, j0 + e < n ? score_key(sp[j0 + e]) : 0u, (uint32_t)((lane & 7) * 4 + e));
       }
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // xor 1
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // xor 2
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));  // half-row mirror
-      if ((lane & 7) == 0) gmax[j0 / kGroup] = m;
+      st = top2_merge8(st);
+      if ((lane & 7) == 0) { gmax[j0 / kGroup] = st.m1; gsec[j0 / kGroup] = pack_second(st); }
     }
   } else {
     float v[4 * P];
@@ -432,15 +489,13 @@ __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
 #pragma unroll
     for (int u = 0; u < 4 * P; ++u) {
       const int64_t j = base + u * 64 + lane;
-      uint32_t m = j < n ? score_key(v[u]) : 0u;
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // xor 1
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // xor 2
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));  // half-row mirror
-      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));  // row mirror
-      m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));                                 // rows 0+1, 2+3
+      Top2 st{j < n ? score_key(v[u]) : 0u, (uint32_t)(lane & 31), 0u};
+      st = top2_merge8(st);
+      st = top2_merge(st, top2_dpp<0x140>(st));        // row mirror: the 16 lanes of a row
+      st = top2_merge(st, top2_xor(st, 16));           // rows 0+1, 2+3: a half-wave
       const int64_t g = (base + u * 64) / kGroup;
-      if (lane == 0) gmax[g] = m;
-      if (lane == 32) gmax[g + 1] = m;
+      if (lane == 0) { gmax[g] = st.m1; gsec[g] = pack_second(st); }
+      if (lane == 32) { gmax[g + 1] = st.m1; gsec[g + 1] = pack_second(st); }
     }
   }
 }
@@ -450,12 +505,18 @@ struct alignas(16) CollectShared {
   uint32_t key[kLdsCand];       // superset keys, index order
   uint32_t idx[kLdsCand];       // superset candidate indices
   uint32_t list[kListCap];      // groups whose maximum is >= L, ascending
+  uint32_t lmax[kListCap];      // their maximum keys
+  uint32_t lpos[kListCap];      // position of the maximum, or kFullFlag | slot among full groups
+  uint32_t fkey[kFullCap][kGroup];   // keys of the full groups
+  uint32_t flist[kFullCap];     // list position of each full group
+  uint32_t fmask[kFullCap];     // its candidates with key >= L
   uint32_t hist[kBins];         // maxima bins (A), then superset bins (C, D)
   uint32_t red[2 * kCWaves];
   uint32_t tot[kScanRounds * kCWaves + 4];
   uint32_t binv[kBinCap];       // keys in the bin that holds the k-th largest
   uint32_t misc[8];
 };
+constexpr uint32_t kFullFlag = 0x80000000u;
 
 // Ordered scan over items (round r, thread t), taken in that order, for the K2 block: given
 // this thread's count for each round, returns the total and sets off[r] to the sum of the
@@ -581,6 +642,29 @@ __device__ void ordered_select(GK key, GI idx, uint32_t m, uint32_t tau, uint32_
   }
 }
 
+// The rare paths live out of line so the common path's code stays compact: a single
+// workgroup runs it once, so its size, not its instruction count, sets how long instruction
+// fetch takes.
+// Global path: exact selection over all n candidates, read from the score array.
+__device__ __attribute__((noinline)) void select_global(__amdgpu_buffer_rsrc_t srs, uint32_t n, uint32_t keff,
+                                                        int32_t* out, CollectShared& sh) {
+  uint32_t ties_take;
+  auto key = [&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); };
+  const uint32_t tau = block_radix_select(key, n, keff, 0u, 0xFFFFFFFFu, sh, &ties_take);
+  ordered_select<kGlobalRounds>(key, [&](uint32_t i) { return i; }, n, tau, ties_take, keff, out, sh);
+}
+
+// A crowded threshold bin (heavy ties): tau and the ties to take by radix steps over the LDS
+// superset, keys in [L, their maximum].
+__device__ __attribute__((noinline)) uint32_t tau_by_radix(CollectShared& sh, uint32_t T, uint32_t keff, uint32_t L,
+                                                           uint32_t* ties_take) {
+  uint32_t hi = 0;
+  for (uint32_t i = threadIdx.x; i < T; i += kCThreads) hi = max(hi, sh.key[i]);
+  uint32_t unused = 0xFFFFFFFFu;
+  block_minmax_t<kCWaves>(&unused, &hi, sh.red);
+  return block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, ties_take);
+}
+
 __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* topk) {
   __shared__ CollectShared sh;
   const int b = blockIdx.x;
@@ -602,133 +686,132 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
   const uint32_t ng = (n + gs - 1) >> gshift;
   const uint32_t nt = min(ng, (uint32_t)kTile);
   const __amdgpu_buffer_rsrc_t mrs = buffer_rsrc(maxima_ptr(a, b), ng * 4u);
-  auto load_tile = [&](uint32_t t0, uint32_t (&mv)[kMaxPerThread]) {
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(second_ptr(a, b), ng * 4u);
+  uint32_t mv[kMaxPerThread], sv[kMaxPerThread];        // thread t: groups t0 + 8t .. 8t+7
+  auto load_tile = [&](uint32_t t0) {
     const uint32_t e0 = t0 + kMaxPerThread * t;
-    const u32x4 lo4 = buffer_u32x4(mrs, e0), hi4 = buffer_u32x4(mrs, e0 + 4);
+    const u32x4 m0 = buffer_u32x4(mrs, e0), m1 = buffer_u32x4(mrs, e0 + 4);
+    const u32x4 s0 = buffer_u32x4(qrs, e0), s1 = buffer_u32x4(qrs, e0 + 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { mv[j] = lo4[j]; mv[4 + j] = hi4[j]; }
+    for (int j = 0; j < 4; ++j) { mv[j] = m0[j]; mv[4 + j] = m1[j]; sv[j] = s0[j]; sv[4 + j] = s1[j]; }
   };
 
-  // (A) The bound L from the first tile of group maxima (thread t holds maxima 8t .. 8t+7).
-  uint32_t mv[kMaxPerThread];
-  load_tile(0, mv);
+  // (A) The bound L from the first tile of group maxima: 2048 bins of (key - vmin) >> shift.
+  load_tile(0);
   for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;
   if (t == 0) sh.misc[2] = 0;
   uint32_t vmin = 0xFFFFFFFFu, vmax = 0;
 #pragma unroll
   for (int j = 0; j < kMaxPerThread; ++j)
     if (kMaxPerThread * t + j < nt) { vmin = min(vmin, mv[j]); vmax = max(vmax, mv[j]); }
-  block_minmax_t<kCWaves>(&vmin, &vmax, sh.red);                   // its barriers also order the clears
+  block_minmax_t<kCWaves>(&vmin, &vmax, sh.red);        // its barriers also order the clears
   uint32_t L = 0;                                       // with fewer than k groups: every candidate
   if (nt >= keff) {
-    const uint32_t span = vmax - vmin;
-    const float scale = span ? (float)(kBins - 1) / (float)span : 0.f;
-    // Monotone bins: a larger key never lands in a lower bin.
-    auto bin = [&](uint32_t v) { return min((uint32_t)(kBins - 1), (uint32_t)((float)(v - vmin) * scale)); };
+    const int span_bits = differing_bits(0u, vmax - vmin);
+    const int shift = span_bits > 11 ? span_bits - 11 : 0;   // monotone bins below 2048
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j)
-      if (kMaxPerThread * t + j < nt) atomicAdd(&sh.hist[bin(mv[j])], 1u);
+      if (kMaxPerThread * t + j < nt) atomicAdd(&sh.hist[(mv[j] - vmin) >> shift], 1u);
     __syncthreads();
     const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
     uint32_t total;
     const uint32_t run = block_exclusive_sum_t<kCWaves>(h0 + h1, &total, sh.red);
     if (run < keff && run + h0 + h1 >= keff) sh.misc[0] = run + h0 >= keff ? kBins - 1 - 2 * t : kBins - 2 - 2 * t;
     __syncthreads();
-    const uint32_t bstar = sh.misc[0];
+    const uint32_t floor_key = vmin + (sh.misc[0] << shift);   // every maximum in the bin or above
     uint32_t lmin = 0xFFFFFFFFu, unused = 0;
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j)
-      if (kMaxPerThread * t + j < nt && bin(mv[j]) >= bstar) lmin = min(lmin, mv[j]);
+      if (kMaxPerThread * t + j < nt && mv[j] >= floor_key) lmin = min(lmin, mv[j]);
     block_minmax_t<kCWaves>(&lmin, &unused, sh.red);
     L = lmin;
   }
   for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;   // reused for the superset
 
-  // (B) The groups whose maximum is >= L, ascending: one block scan per tile.
-  uint32_t G = 0;
+  // (B) The groups whose maximum is >= L, ascending; among them the "full" ones, whose second
+  // key may reach L too. One scan places both (counts packed in 16-bit halves).
+  uint32_t G = 0, F = 0;
   for (uint32_t t0 = 0; t0 < ng; t0 += kTile) {
-    if (t0 > 0) load_tile(t0, mv);
-    uint32_t f = 0;
+    if (t0 > 0) load_tile(t0);
+    uint32_t f = 0, ff = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerThread; ++j)
-      f |= ((t0 + kMaxPerThread * t + j < ng && mv[j] >= L) ? 1u : 0u) << j;
-    const uint32_t cnt[1] = {(uint32_t)__popc(f)};
+    for (int j = 0; j < kMaxPerThread; ++j) {
+      const bool listed = t0 + kMaxPerThread * t + j < ng && mv[j] >= L;
+      f |= (listed ? 1u : 0u) << j;
+      ff |= ((listed && (sv[j] | 31u) >= L) ? 1u : 0u) << j;
+    }
+    const uint32_t cnt[1] = {(uint32_t)__popc(f) | ((uint32_t)__popc(ff) << 16)};
     uint32_t off[1];
     const uint32_t total = ordered_scan(cnt, off, sh);
-    uint32_t pos = G + off[0];
+    uint32_t pos = G + (off[0] & 0xFFFFu), fpos = F + (off[0] >> 16);
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j) {
       if ((f >> j) & 1u) {
-        if (pos < (uint32_t)kListCap) sh.list[pos] = t0 + kMaxPerThread * t + j;
+        const bool full = (ff >> j) & 1u;
+        if (pos < (uint32_t)kListCap) {
+          sh.list[pos] = t0 + kMaxPerThread * t + j;
+          sh.lmax[pos] = mv[j];
+          sh.lpos[pos] = full ? (kFullFlag | fpos) : (sv[j] & 31u);
+          if (full && fpos < (uint32_t)kFullCap) sh.flist[fpos] = pos;
+        }
         ++pos;
+        fpos += full ? 1u : 0u;
       }
     }
-    G += total;
+    G += total & 0xFFFFu;
+    F += total >> 16;
   }
   __syncthreads();
-  bool fits = G <= (uint32_t)kListCap;
+  bool fits = G <= (uint32_t)kListCap && F <= (uint32_t)kFullCap;
 
   // (C) The superset: candidates of the listed groups with key >= L, in index order, binned
-  // by key over [L, vmax] (monotone, clamped) as they are kept.
+  // by key over [L, vmax] (monotone, clamped) as they are kept. A listed group contributes
+  // its maximum (known) unless it is full; full groups are read whole, two per wave, and
+  // their kept keys staged in LDS.
   uint32_t T = 0;
   const uint32_t top = max(vmax, L);
   const float scale2 = top > L ? (float)(kBins - 1) / (float)(top - L) : 0.f;
   auto bin2 = [&](uint32_t v) { return min((uint32_t)(kBins - 1), (uint32_t)((float)(v - L) * scale2)); };
   if (fits) {
-    const uint32_t E = G << gshift;                     // candidate slots of the listed groups
-    const uint32_t NI = (E + 3) / 4;                    // items of four (a group holds >= 8)
-    const bool vec = (reinterpret_cast<uintptr_t>(sp) & 15) == 0;   // then items are 16-byte aligned
-    for (uint32_t i0 = 0; i0 < NI; i0 += kItemRounds * kCThreads) {
-      uint32_t kk[kItemRounds][4], cb[kItemRounds], cnt[kItemRounds], off[kItemRounds], f = 0;
-#pragma unroll
-      for (int r = 0; r < kItemRounds; ++r) {
-        const uint32_t x = 4 * min(i0 + r * kCThreads + t, NI - 1);
-        cb[r] = (sh.list[x >> gshift] << gshift) + (x & (gs - 1));
+    const int lane = t & 63, half = lane >> 5, li = lane & 31;
+    for (uint32_t j0 = 2 * (t >> 6); j0 < F; j0 += 2 * kCWaves) {
+      const uint32_t j = j0 + half;
+      const bool on = j < F;
+      const uint32_t c = on ? (sh.list[sh.flist[j]] << gshift) + li : 0u;
+      const uint32_t v = score_key(__uint_as_float(buffer_u32(srs, c)));
+      const bool keep = on && li < gs && c < n && v >= L;
+      const uint32_t m = (uint32_t)(__ballot(keep) >> (32 * half));
+      if (on) {
+        sh.fkey[j][li] = v;
+        if (li == 0) sh.fmask[j] = m;
       }
-      if (vec) {                                        // one aligned 16-byte load per item
-#pragma unroll
-        for (int r = 0; r < kItemRounds; ++r) {
-          const u32x4 v = buffer_u32x4(srs, cb[r]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kk[r][e] = v[e];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < kItemRounds; ++r)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kk[r][e] = buffer_u32(srs, cb[r] + e);
+    }
+    __syncthreads();
+    for (uint32_t e0 = 0; e0 < G; e0 += kCThreads) {
+      const uint32_t e = e0 + t;
+      uint32_t lp = 0, c[1] = {0}, off[1];
+      if (e < G) {
+        lp = sh.lpos[e];
+        c[0] = (lp & kFullFlag) ? (uint32_t)__popc(sh.fmask[lp & ~kFullFlag]) : 1u;
       }
-      __builtin_amdgcn_sched_barrier(0);                // every load is in flight before any use
-      if (vec) {                                        // the item that straddles the end, if any
-#pragma unroll
-        for (int r = 0; r < kItemRounds; ++r)
-          if (cb[r] < n && cb[r] + 4 > n)
-            for (int e = 0; e < 4; ++e) kk[r][e] = buffer_u32(srs, cb[r] + e);
-      }
-#pragma unroll
-      for (int r = 0; r < kItemRounds; ++r) {
-        const uint32_t x = 4 * (i0 + r * kCThreads + t);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kk[r][e] = score_key(__uint_as_float(kk[r][e]));
-          const bool keep = x + e < E && cb[r] + e < n && kk[r][e] >= L;
-          f |= (keep ? 1u : 0u) << (4 * r + e);
-        }
-        cnt[r] = (uint32_t)__popc((f >> (4 * r)) & 0xFu);
-      }
-      const uint32_t total = ordered_scan(cnt, off, sh);
-      if (T + total <= (uint32_t)kLdsCand) {
-#pragma unroll
-        for (int r = 0; r < kItemRounds; ++r) {
-          uint32_t pos = T + off[r];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if ((f >> (4 * r + e)) & 1u) {
-              sh.key[pos] = kk[r][e];
-              sh.idx[pos] = cb[r] + e;
-              atomicAdd(&sh.hist[bin2(kk[r][e])], 1u);
-              ++pos;
-            }
+      const uint32_t total = ordered_scan(c, off, sh);
+      if (T + total <= (uint32_t)kLdsCand && e < G) {
+        const uint32_t gbase = sh.list[e] << gshift;
+        uint32_t pos = T + off[0];
+        if (!(lp & kFullFlag)) {
+          const uint32_t v = sh.lmax[e];
+          sh.key[pos] = v;
+          sh.idx[pos] = gbase + lp;
+          atomicAdd(&sh.hist[bin2(v)], 1u);
+        } else {
+          const uint32_t j = lp & ~kFullFlag;
+          for (uint32_t m = sh.fmask[j]; m; m &= m - 1) {
+            const uint32_t i = (uint32_t)__ffs(m) - 1;
+            const uint32_t v = sh.fkey[j][i];
+            sh.key[pos] = v;
+            sh.idx[pos] = gbase + i;
+            atomicAdd(&sh.hist[bin2(v)], 1u);
+            ++pos;
           }
         }
       }
@@ -740,11 +823,7 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
 
   // (D) Exact selection.
   if (!fits) {                                          // global path
-    uint32_t ties_take;
-    const uint32_t tau = block_radix_select([&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); },
-                                            n, keff, 0u, 0xFFFFFFFFu, sh, &ties_take);
-    ordered_select<kGlobalRounds>([&](uint32_t i) { return score_key(__uint_as_float(buffer_u32(srs, i))); },
-                   [&](uint32_t i) { return i; }, n, tau, ties_take, keff, out, sh);
+    select_global(srs, n, keff, out, sh);
     return;
   }
   if (T <= keff) {                                      // (only when the bound is not binding)
@@ -788,18 +867,12 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
     __syncthreads();
     tau = sh.misc[3];
     ties_take = sh.misc[4];
-  } else {                                              // a crowded bin (heavy ties): radix select
-    uint32_t hi = 0;
-    for (uint32_t i = t; i < T; i += kCThreads) hi = max(hi, sh.key[i]);
-    uint32_t unused = 0xFFFFFFFFu;
-    block_minmax_t<kCWaves>(&unused, &hi, sh.red);
-    tau = block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, &ties_take);
+  } else {                                              // a crowded bin (heavy ties)
+    tau = tau_by_radix(sh, T, keff, L, &ties_take);
   }
   auto lk = [&](uint32_t i) { return sh.key[i]; };
   auto li = [&](uint32_t i) { return sh.idx[i]; };
-  if (T <= kCThreads) ordered_select<1>(lk, li, T, tau, ties_take, keff, out, sh);
-  else if (T <= 2 * kCThreads) ordered_select<2>(lk, li, T, tau, ties_take, keff, out, sh);
-  else ordered_select<8>(lk, li, T, tau, ties_take, keff, out, sh);
+  ordered_select<1>(lk, li, T, tau, ties_take, keff, out, sh);
 }
 
 template <typename ET, int NH>
