@@ -440,6 +440,54 @@ __device__ __forceinline__ Top2 top2_merge8(Top2 s) {
   return top2_merge(s, top2_dpp<0x141>(s));
 }
 
+// One level of the composite reduction: merges (maximum, top composite, second composite)
+// with the lane that DPP control CTRL names (all lanes of a row are valid sources).
+template <int CTRL>
+__device__ __forceinline__ void top2c_step(uint32_t& m, uint32_t& c1, uint32_t& c2) {
+  // A zero `old` lets the compiler fold the moves of m and c1 into DPP forms of max and min.
+  const uint32_t om = dpp0<CTRL>(m);
+  const uint32_t o1 = dpp0<CTRL>(c1);
+  const uint32_t o2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)c2, CTRL, 0xF, 0xF, false);
+  m = max(m, om);
+  c2 = max(max(c2, o2), min(c1, o1));
+  c1 = max(c1, o1);
+}
+
+// Statistics of the groups of 32 held by a wave as 8 lanes x 4 consecutive scores. Beside
+// the exact maximum it ranks composite words (key & ~31) | position: their largest gives a
+// position of the maximum and their second largest the second key with its low five bits
+// cleared. When two keys share the maximum's upper 27 bits the position may be either of
+// them, but the word then satisfies (word | 31) >= maximum, so a group is only ever read
+// through its position when its maximum is the one key that large. Keys are taken raw here
+// (-0 one below +0) and mended on the results: the maximum maps key(-0) to key(+0), and a
+// second word in the 32 keys below key(+0) is raised to key(+0), which can only mark more
+// groups full. Lanes with lane % 8 == 0 store the group's two words; scores whose bit in
+// `valid` is clear count as key 0, below every score.
+__device__ __forceinline__ void group_stats4(const f32x4& x, const uint32_t (&pos)[4], int lane,
+                                             uint32_t* gm, uint32_t* gs, uint32_t valid = 0xFu) {
+  uint32_t k[4], c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t u = __float_as_uint(x[e]);
+    k[e] = (valid >> e) & 1u ? u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u) : 0u;
+    c[e] = (k[e] & ~31u) | pos[e];
+  }
+  uint32_t m = max(max(k[0], k[1]), max(k[2], k[3]));
+  const uint32_t hi01 = max(c[0], c[1]), lo01 = min(c[0], c[1]);
+  const uint32_t hi23 = max(c[2], c[3]), lo23 = min(c[2], c[3]);
+  uint32_t c1 = max(hi01, hi23);
+  uint32_t c2 = max(max(lo01, lo23), min(hi01, hi23));
+  top2c_step<0xB1>(m, c1, c2);     // xor 1
+  top2c_step<0x4E>(m, c1, c2);     // xor 2
+  top2c_step<0x141>(m, c1, c2);    // half-row mirror: lanes 0-3 with 4-7
+  if ((lane & 7) == 0) {
+    uint32_t s2 = c2 & ~31u;
+    s2 = s2 == 0x7FFFFFE0u ? 0x80000000u : s2;
+    *gm = m == 0x7FFFFFFFu ? 0x80000000u : m;
+    *gs = s2 | (c1 & 31u);
+  }
+}
+
 // K1 for caller-provided scores: group statistics only. Wave w of block x covers 256 * P
 // consecutive scores starting at (4x + w) * 256 * P: P 16-byte loads per lane when the
 // sequence's scores are 16-byte aligned (a group of 32 is then 8 lanes of one load), else
@@ -464,19 +512,30 @@ __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
       if (j > nfull - 1) j = nfull - 1;
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp) + j);
     }
+    uint32_t pos[4];
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int64_t j0 = base + (u * 64 + lane) * 4;
-      Top2 st{0u, 255u, 0u};
-      if (j0 < 4 * nfull) {
+    for (int e = 0; e < 4; ++e) pos[e] = (uint32_t)(lane & 7) * 4 + e;
+    // Only the wave that reaches the end of the sequence masks (and reads the last n % 4
+    // scores, which no whole vector holds); every other wave takes the unmasked path.
+    if (base + 256 * P <= 4 * nfull) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) top2_add(st, score_key(v[u][e]), (uint32_t)((lane & 7) * 4 + e));
-      } else {
-        for (int e = 0; e < 4; ++e)                    // the tail
-          top2_add(st, j0 + e < n ? score_key(sp[j0 + e]) : 0u, (uint32_t)((lane & 7) * 4 + e));
+      for (int u = 0; u < P; ++u) {
+        const int64_t j0 = base + (u * 64 + lane) * 4;
+        group_stats4(v[u], pos, lane, gmax + j0 / kGroup, gsec + j0 / kGroup);
       }
-      st = top2_merge8(st);
-      if ((lane & 7) == 0) { gmax[j0 / kGroup] = st.m1; gsec[j0 / kGroup] = pack_second(st); }
+    } else {
+      f32x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = sp[min(4 * nfull + e, n - 1)];
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const int64_t j0 = base + (u * 64 + lane) * 4;
+        f32x4 x = j0 < 4 * nfull ? v[u] : t;
+        uint32_t valid = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) valid |= (j0 + e < n ? 1u : 0u) << e;
+        group_stats4(x, pos, lane, gmax + j0 / kGroup, gsec + j0 / kGroup, valid);
+      }
     }
   } else {
     float v[4 * P];

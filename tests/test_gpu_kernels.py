@@ -164,6 +164,20 @@ def test_topk_ties_and_special_values(rng):
     _run_topk(rows, 64)
 
 
+def test_topk_signed_zero_and_denormal_threshold(rng):
+    # The k-th value is 0: +0 and -0 tie (lower index first) and the tiniest negative values
+    # sit just below them, so every group holding a zero must be read whole.
+    print("case: top-k threshold at signed zero", flush=True)
+    n = 40000
+    s = -(1.0 + np.abs(rng.standard_normal(n))).astype(np.float32)
+    z = rng.choice(n, 400, replace=False)
+    s[z[:300]] = np.where(rng.random(300) < 0.5, -0.0, 0.0)
+    s[z[300:350]] = -1e-45
+    s[z[350:]] = -3e-45
+    for k in (1, 150, 300, 320, 360):
+        _run_topk([s], k)
+
+
 def test_topk_large_threshold_bin_global_path(rng):
     # 30000 equal values straddle the threshold, so the final selection runs from global memory.
     print("case: top-k global-memory path", flush=True)
