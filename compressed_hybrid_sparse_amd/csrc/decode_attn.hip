@@ -8,19 +8,20 @@
 // 创新 3 (C128 reads every entry each step).
 //
 // gfx950 design (bf16). All query heads of a sequence share one latent KV row, so the heads
-// form the M dimension of the MFMA contraction and every KV row is fetched from HBM once per
-// step for all heads. The key list (window rows, then the selected or all compressed rows) is
-// split across workgroups (split-KV); a workgroup of 4 waves covers 64 heads (wave w: heads
-// 16w..16w+15, unused heads masked in-kernel, so callers never pad) and walks its slice of the
-// key list 32 rows at a time:
-//   1. the 32 rows are gathered from HBM with coalesced 16-byte loads (one wave per 1 KiB row
-//      at d = 512) into one row-major LDS tile; Q.K^T reads it with 16-byte loads (d is the
-//      reduction), P.V reads the same tile column-wise with 16-bit loads (keys are the
-//      reduction), so K = V is staged once;
-//   2. S = Q K^T with v_mfma_f32_16x16x32_bf16, Q held in registers for the whole walk;
-//   3. online softmax in fp32 (base-2 logits, running max and sum per head, DPP row reductions);
+// form the M dimension of the MFMA contraction (16 per tile, unused heads masked in-kernel, so
+// callers never pad). The key list (window rows, then the selected or all compressed rows) is
+// split across workgroups (split-KV); a workgroup of 4 waves covers one 16-head tile and walks
+// its slice of the key list 32 rows at a time:
+//   1. the chunk's top-k entries are read first (scalar loads, ahead of the Q loads), then the
+//      32 rows are gathered with coalesced 16-byte loads, 8 rows per wave, into one row-major
+//      LDS tile, so K = V is staged once;
+//   2. S = Q K^T with v_mfma_f32_16x16x32_bf16, each wave contracting a quarter of the
+//      channels; the four partial tiles are summed through LDS in a fixed order;
+//   3. online softmax in fp32 (base-2 logits, running max and sum per head, DPP row
+//      reductions), the same in every wave;
 //   4. P (rounded to bf16, and the running sum is taken over the rounded values so the weights
-//      sum to one exactly) goes through LDS into the A-operand layout, and O += P V with MFMA.
+//      sum to one exactly) goes through LDS into the A-operand layout, and each wave computes
+//      O += P V for its quarter of the channels, the B operand read with transposing LDS loads.
 // Each workgroup writes its unnormalised O with its running max and sum; a combine kernel
 // merges the splits with the log-sum-exp identity and writes out and lse. fp32 storage takes a
 // plain VALU kernel with the same split and merge (it has to meet an fp32 tolerance that bf16
@@ -112,77 +113,107 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Source rows of a 32-slot chunk starting at slot s0 for a wave whose load i covers slot
+// s0 + (4i + wave) * RPI + lr (null: no key there). Branch-free: the top-k entry is read at a
+// clamped position whether or not the slot needs it, so the reads issue back to back. At
+// d = 512 (RPI = 1) every operand is the same for the whole wave.
+template <int D, int LOADS, int RPI>
+__device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm, int b, int32_t s0, int32_t s_end,
+                                           int wave, int lr, const uint16_t* (&rp)[LOADS]) {
+  const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
+  const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
+  int32_t idx[LOADS];
+  if (a.topk != nullptr && a.k > 0) {
+    const int32_t* tk = a.topk + (int64_t)b * a.k;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) idx[i] = tk[min(max(s0 + (4 * i + wave) * RPI + lr - sm.nswa, 0), a.k - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) idx[i] = s0 + (4 * i + wave) * RPI + lr - sm.nswa;
+  }
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int32_t s = s0 + (4 * i + wave) * RPI + lr;
+    const bool in_swa = s < sm.nswa;
+    const bool ok = s < s_end && (in_swa || (idx[i] >= 0 && idx[i] < sm.G));
+    const uint16_t* p = in_swa ? swa + ((int64_t)b * a.W + s) * D : comp + (sm.comp0 + idx[i]) * D;
+    rp[i] = ok ? p : nullptr;
+  }
+}
+
 // ---------------------------------------------------------------- bf16 MFMA split kernel
+// One workgroup of 4 waves per (split, sequence, 16-head tile). The 16 heads are the MFMA
+// rows. Each wave gathers a quarter of a chunk's 32 rows and contracts Q K^T over a quarter of
+// the channels (d >= 128; all of them at d = 64). The four partial logit tiles are summed
+// through LDS in a fixed order, so every wave holds bit-identical logits and runs the same
+// softmax. Each wave then computes P.V for its quarter of the channels. A wave thus issues a
+// handful of loads and 8 KiB of partial stores (d = 512).
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KC = kKeysPerChunk;
   constexpr int KN_PITCH = D + 8;          // bf16 elements per row-major LDS row
   constexpr int P_PITCH = KC + 8;
   constexpr int VPR = D / 8;               // 16-byte vectors per row
-  constexpr int LOADS = KC * VPR / kThreads;
-  static_assert(KC * VPR % kThreads == 0, "tile");
+  constexpr int RPI = 64 / VPR;            // rows one wave-wide load covers (1 at d = 512)
+  constexpr int LOADS = KC / (4 * RPI);    // loads per wave per chunk
+  constexpr int TPW = D / 64;              // 16-channel output tiles per wave
+  constexpr bool SPLIT_S = D >= 128;       // logits contracted over a quarter of d per wave
+  constexpr int QD = SPLIT_S ? D / 4 : D;  // channels of Q (and of the logit contraction) per wave
+  static_assert(QD % 32 == 0, "k step");
+  static_assert(VPR <= 64 && 64 % VPR == 0 && KC % (4 * RPI) == 0 && TPW >= 1, "tile");
   __shared__ __attribute__((aligned(16))) uint16_t kn[KC * KN_PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t pb[4][16 * P_PITCH];
-  __shared__ int64_t rowoff[KC];
-  __shared__ int32_t rowswa[KC];
+  __shared__ int32_t rowok[KC];
+  __shared__ __attribute__((aligned(16))) f32x4 spart[SPLIT_S ? 4 : 1][2][64];
 
   const int b = blockIdx.y, split = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int h_base = blockIdx.z * 64 + wave * 16;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = RPI > 1 ? lane / VPR : 0, cv = lane % VPR;
+  const int h_base = blockIdx.z * 16;
   const SlotMap sm(a, b);
   const int32_t s_begin = split * a.kps;
   const int32_t s_end = min(s_begin + a.kps, sm.nslots());
 
-  // Q fragment (A operand): row c of this wave's 16 heads, d = 32t + 8g .. +8.
-  // Loaded unconditionally (head index clamped, then zeroed) so the loads stay in flight
-  // behind the first chunk's index and row gathers; they are first used by the S MFMA.
-  bf16x8 qf[D / 32];
+  // Source row of load i of the first chunk (null: no key). These index reads go out before
+  // the Q loads, so waiting for them does not wait for Q as well.
+  const uint16_t* rp[LOADS];
+  chunk_rows<D, LOADS, RPI>(a, sm, b, s_begin, s_end, wave, lr, rp);
+
+  // Q fragment (A operand): row c of the 16 heads, d = d0 + 32t + 8g .. +8 (d0 = this wave's
+  // quarter); head index clamped, then zeroed, so the loads are unconditional.
+  const int d0 = SPLIT_S ? QD * wave : 0;
+  bf16x8 qf[QD / 32];
   {
     const int h = h_base + c;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + min(h, a.H - 1)) * D;
-    u32x4 qv[D / 32];
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + min(h, a.H - 1)) * D + d0;
+    u32x4 qv[QD / 32];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qp + 32 * t + 8 * g);
+    for (int t = 0; t < QD / 32; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qp + 32 * t + 8 * g);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, h < a.H ? qv[t] : u32x4{0, 0, 0, 0});
+    for (int t = 0; t < QD / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, h < a.H ? qv[t] : u32x4{0, 0, 0, 0});
   }
-  f32x4 o[D / 16];
+  f32x4 o[TPW];
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) o[j] = f32x4{0, 0, 0, 0};
+  for (int j = 0; j < TPW; ++j) o[j] = f32x4{0, 0, 0, 0};
   float m_run[4], l_run[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
 
-  const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
-  const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
-
   for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) {
-    __syncthreads();   // previous chunk's LDS reads are done
-    if (tid < KC) {
-      const int32_t s = s0 + tid;
-      bool is_swa = false;
-      int64_t off = (s < s_end) ? sm.row(a, b, s, &is_swa) : -1;
-      rowoff[tid] = off;
-      rowswa[tid] = is_swa ? 1 : 0;
-    }
-    __syncthreads();
-    // 1. gather 32 rows, store row-major and transposed.
+    // 1. gather the chunk's rows (coalesced 16-byte loads) into a row-major LDS tile.
     u32x4 v[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int e = tid + i * kThreads;
-      const int r = e / VPR, cv = e % VPR;
-      const int64_t off = rowoff[r];
-      const uint16_t* src = rowswa[r] ? swa : comp;
-      v[i] = off >= 0 ? *reinterpret_cast<const u32x4*>(src + off + 8 * cv) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < LOADS; ++i)
+      v[i] = rp[i] ? *reinterpret_cast<const u32x4*>(rp[i] + 8 * cv) : u32x4{0, 0, 0, 0};
+    __syncthreads();   // the previous chunk's LDS reads are done
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int e = tid + i * kThreads;
-      const int r = e / VPR, cv = e % VPR;
+      const int r = (4 * i + wave) * RPI + lr;
       *reinterpret_cast<u32x4*>(&kn[r * KN_PITCH + 8 * cv]) = v[i];
+      if (cv == 0) rowok[r] = rp[i] != nullptr;
     }
+    if (s0 + KC < s_end) chunk_rows<D, LOADS, RPI>(a, sm, b, s0 + KC, s_end, wave, lr, rp);
     __syncthreads();
     // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
     f32x4 sacc[2];
@@ -190,13 +221,30 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     for (int n = 0; n < 2; ++n) {
       sacc[n] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        u32x4 kb = *reinterpret_cast<const u32x4*>(&kn[(16 * n + c) * KN_PITCH + 32 * t + 8 * g]);
+      for (int t = 0; t < QD / 32; ++t) {
+        u32x4 kb = *reinterpret_cast<const u32x4*>(&kn[(16 * n + c) * KN_PITCH + d0 + 32 * t + 8 * g]);
         sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t], __builtin_bit_cast(bf16x8, kb), sacc[n], 0, 0, 0);
       }
     }
+    if constexpr (SPLIT_S) {
+      // Sum the four channel quarters in wave order, the same order in every wave.
+      spart[wave][0][lane] = sacc[0];
+      spart[wave][1][lane] = sacc[1];
+      __syncthreads();
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        f32x4 t = spart[0][n][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          const f32x4 u = spart[w][n][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[r] += u[r];
+        }
+        sacc[n] = t;
+      }
+    }
     // 3. online softmax (base-2), per head row 4g + r.
-    const bool valid0 = rowoff[c] >= 0, valid1 = rowoff[16 + c] >= 0;
+    const bool valid0 = rowok[c] != 0, valid1 = rowok[16 + c] != 0;
     float p[2][4], alpha[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -213,11 +261,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       m_run[r] = mn;
     }
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
+    for (int j = 0; j < TPW; ++j) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[j][r] *= alpha[r];
     }
-    // 4. P to LDS as [head][key], read back as the A operand (row c, keys 8g .. 8g+7).
+    // 4. P to this wave's LDS slice as [head][key], read back as the A operand (row c, keys
+    // 8g .. 8g+7).
     uint16_t* pw = pb[wave];
 #pragma unroll
     for (int n = 0; n < 2; ++n)
@@ -230,9 +279,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     // lane i of a 16-lane group element e of the group's 8-byte chunks read with stride 16,
     // so lane c addressing channels 16j + 4(c&3) .. +3 of key row 8g + (c>>2) (+4 for the
     // upper half) receives keys 8g .. 8g+3 (8g+4 .. 8g+7) of channel 16j + c.
-    const uint16_t* vrow = &kn[(8 * g + (c >> 2)) * KN_PITCH + 4 * (c & 3)];
+    const uint16_t* vrow = &kn[(8 * g + (c >> 2)) * KN_PITCH + 4 * (c & 3) + 16 * TPW * wave];
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
+    for (int j = 0; j < TPW; ++j) {
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 16 * j));
       const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 4 * KN_PITCH + 16 * j));
       const v8i16 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -240,12 +289,13 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     }
   }
   // Partial result of this split: unnormalised O in the MFMA accumulator layout (one 16-byte
-  // store per tile and lane, coalesced), running max (base 2) and sum per head.
+  // store per tile and lane, coalesced; wave w holds tiles TPW w ..), running max (base 2) and
+  // sum per head. The slot of 16-head tile z is (64-head tile z / 4, quarter z % 4).
   const int64_t pslot = (int64_t)b * a.n_splits + split;
-  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + ((pslot * a.head_tiles + blockIdx.z) * 4 + wave) * (D / 16) * 64;
+  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (pslot * a.head_tiles * 4 + blockIdx.z) * (D / 16) * 64;
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) po[j * 64 + lane] = o[j];
-  if (c == 0) {
+  for (int j = 0; j < TPW; ++j) po[(TPW * wave + j) * 64 + lane] = o[j];
+  if (wave == 0 && c == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = h_base + 4 * g + r;
@@ -475,7 +525,8 @@ struct SplitPlan {
 SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, int32_t k, int64_t max_comp) {
   const int64_t max_slots = (int64_t)window + (k > 0 ? k : max_comp);
   const int gran = dt == CHS_BF16 ? kKeysPerChunk : kThreads;
-  const int64_t blocks_per_split = (int64_t)batch * (dt == CHS_BF16 ? (H + 63) / 64 : H);
+  // Aim at about 512 workgroups: bf16 runs one per 16-head tile, fp32 one per head.
+  const int64_t blocks_per_split = (int64_t)batch * (dt == CHS_BF16 ? (H + 15) / 16 : H);
   int64_t want = (512 + blocks_per_split - 1) / blocks_per_split;
   const int64_t most = (max_slots + gran - 1) / gran;
   if (want > most) want = most;
@@ -544,7 +595,7 @@ extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == CHS_BF16) {
-    dim3 grid(p.n_splits, batch, (n_heads + 63) / 64);
+    dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
     switch (d) {
       case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kThreads), 0, s, a); break;
       case 128: hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kThreads), 0, s, a); break;
