@@ -1,0 +1,468 @@
+// Attention device code shared by the decode-attention kernels and the fused decode step:
+// the key-slot map, the split body (gather, Q K^T, online softmax, P V) over one or several
+// 16-head tiles, the log-sum-exp combine body, and the split plan. The design is described
+// in decode_attn.hip.
+#pragma once
+
+#include "common.h"
+
+namespace chs {
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// An LDS address as the transposing load builtin takes it.
+__device__ __forceinline__ __attribute__((address_space(3))) v4i16* lds_v4i16(const uint16_t* p) {
+  return (__attribute__((address_space(3))) v4i16*)(p);
+}
+
+constexpr int kAttnThreads = 256;       // threads of the standalone split and combine blocks
+constexpr int kKeysPerChunk = 32;
+
+struct AttnArgs {
+  const void* q;            // [batch][H][D]
+  const void* swa;          // [batch][W][D]
+  const int32_t* swa_len;   // [batch]
+  const void* comp;         // [*][D]
+  const int64_t* cu_comp;   // [batch+1]
+  const int32_t* topk;      // [batch][k] or NULL
+  int32_t H, D, W, k;
+  int64_t max_comp;
+  float scale_log2;         // scale * log2(e)
+  int32_t n_splits, kps;    // key slots per split
+  int32_t head_tiles;       // ceil(H / 64) for bf16, H for fp32
+  float* part_o;            // per (sequence, split): see the layout note below
+  float* part_ml;           // [batch][n_splits][H][2]: running max (base 2), running sum
+};
+
+constexpr int kCombineSplits = 512;   // most splits one call may use
+constexpr int kCombineLanes = 4;      // lanes per output word in the combine
+
+// Partial O of a split. bf16 (MFMA layout): per (sequence, split, 64-head tile, 16-head
+// quarter z % 4) the 16-head tile's accumulators as they sit in registers, [16-column tile
+// j][lane][4]: lane 16g + c, element r hold head 16z + 4g + r, channel 16j + c. fp32: [H][D].
+
+// Key slots of sequence b: [0, swa_len) window rows, then k (C4) or G_b (C128) entries.
+struct SlotMap {
+  int64_t comp0, G;
+  int32_t nswa, nextra;
+  __device__ SlotMap(const AttnArgs& a, int b) {
+    int32_t L = a.swa_len[b];
+    nswa = L < 0 ? 0 : (L > a.W ? a.W : L);
+    comp0 = a.cu_comp[b];
+    G = a.cu_comp[b + 1] - comp0;
+    if (G < 0) G = 0;
+    if (a.topk) {
+      nextra = a.k;
+    } else {
+      int64_t g = G < a.max_comp ? G : a.max_comp;
+      nextra = (int32_t)g;
+    }
+  }
+  __device__ int32_t nslots() const { return nswa + nextra; }
+  // Element offset of slot s's row within its buffer; -1 if the slot holds no key.
+  // *is_swa tells which buffer.
+  __device__ int64_t row(const AttnArgs& a, int b, int32_t s, bool* is_swa) const {
+    if (s < nswa) { *is_swa = true; return ((int64_t)b * a.W + s) * a.D; }
+    *is_swa = false;
+    int64_t j = s - nswa;
+    if (a.topk) {
+      j = a.topk[(int64_t)b * a.k + j];
+      if (j < 0 || j >= G) return -1;
+    }
+    return (comp0 + j) * a.D;
+  }
+};
+
+// Max / sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane gets the result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Source rows of a 32-slot chunk starting at slot s0 for a workgroup of NW waves: load i of
+// wave w is wave-wide load li = i * NW + w of the chunk (none if li >= 32 / RPI), covering slot
+// s0 + li * RPI + lr (null: no key there). Branch-free: the top-k entry is read at a clamped
+// position whether or not the slot needs it, so the reads issue back to back. At d = 512
+// (RPI = 1) every operand is the same for the whole wave.
+template <int D, int LOADS, int RPI, int NW>
+__device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm, int b, int32_t s0, int32_t s_end,
+                                           int wave, int lr, const uint16_t* (&rp)[LOADS]) {
+  constexpr int NLOADS = kKeysPerChunk / RPI;
+  const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
+  const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
+  int32_t idx[LOADS];
+  if (a.topk != nullptr && a.k > 0) {
+    const int32_t* tk = a.topk + (int64_t)b * a.k;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) idx[i] = tk[min(max(s0 + (i * NW + wave) * RPI + lr - sm.nswa, 0), a.k - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) idx[i] = s0 + (i * NW + wave) * RPI + lr - sm.nswa;
+  }
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int32_t s = s0 + (i * NW + wave) * RPI + lr;
+    const bool in_swa = s < sm.nswa;
+    const bool ok = i * NW + wave < NLOADS && s < s_end && (in_swa || (idx[i] >= 0 && idx[i] < sm.G));
+    const uint16_t* p = in_swa ? swa + ((int64_t)b * a.W + s) * D : comp + (sm.comp0 + idx[i]) * D;
+    rp[i] = ok ? p : nullptr;
+  }
+}
+
+// LDS of one split body over TILES 16-head tiles: the chunk's row-major K (= V) tile, each
+// wave's P, the partial logit tiles of the four channel quarters, and the rows' validity.
+template <int D, int TILES>
+struct alignas(16) AttnShared {
+  uint16_t kn[kKeysPerChunk * (D + 8)];
+  uint16_t pb[4 * TILES][16 * (kKeysPerChunk + 8)];
+  f32x4 spart[D >= 128 ? TILES : 1][4][2][64];
+  int32_t rowok[kKeysPerChunk];
+};
+
+struct NoHook {
+  __device__ __forceinline__ void operator()(int32_t) {}
+};
+
+// Split `split` of sequence b for the 16-head tiles z0 .. z0 + TILES - 1, run by 4 * TILES
+// waves: wave w serves tile w / 4 and channel quarter w % 4. Every wave gathers a share of a
+// chunk's 32 rows into one row-major LDS tile; contracts Q K^T over its quarter of the channels
+// (d >= 128; all of them at d = 64), the four partial logit tiles of a head tile being summed
+// through LDS in a fixed order, so all four waves hold bit-identical logits and run the same
+// softmax; and computes P.V for its quarter. before_rows(s0) runs, uniformly over the
+// workgroup, before the rows of the chunk at slot s0 are looked up.
+template <int D, int TILES, typename Hook>
+__device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, int z0, int tid,
+                                           AttnShared<D, TILES>& sh, Hook& before_rows) {
+  constexpr int KC = kKeysPerChunk;
+  constexpr int KN_PITCH = D + 8;          // bf16 elements per row-major LDS row
+  constexpr int P_PITCH = KC + 8;
+  constexpr int NW = 4 * TILES;            // waves
+  constexpr int VPR = D / 8;               // 16-byte vectors per row
+  constexpr int RPI = 64 / VPR;            // rows one wave-wide load covers (1 at d = 512)
+  constexpr int NLOADS = KC / RPI;         // wave-wide loads per chunk
+  constexpr int LOADS = (NLOADS + NW - 1) / NW;   // per wave
+  constexpr int TPW = D / 64;              // 16-channel output tiles per wave
+  constexpr bool SPLIT_S = D >= 128;       // logits contracted over a quarter of d per wave
+  constexpr int QD = SPLIT_S ? D / 4 : D;  // channels of Q (and of the logit contraction) per wave
+  static_assert(VPR <= 64 && 64 % VPR == 0 && KC % RPI == 0 && TPW >= 1 && QD % 32 == 0, "tile");
+
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = wave >> 2, quarter = wave & 3;
+  const int z = z0 + tile;
+  const int lr = RPI > 1 ? lane / VPR : 0, cv = lane % VPR;
+  const int h_base = z * 16;
+  const SlotMap sm(a, b);
+  const int32_t s_begin = split * a.kps;
+  const int32_t s_end = min(s_begin + a.kps, sm.nslots());
+
+  // Source row of load i of the first chunk (null: no key). These index reads go out before
+  // the Q loads, so waiting for them does not wait for Q as well.
+  const uint16_t* rp[LOADS];
+  before_rows(s_begin);
+  chunk_rows<D, LOADS, RPI, NW>(a, sm, b, s_begin, s_end, wave, lr, rp);
+
+  // Q fragment (A operand): row c of the tile's 16 heads, d = d0 + 32t + 8g .. +8 (d0 = this
+  // wave's quarter); head index clamped, then zeroed, so the loads are unconditional.
+  const int d0 = SPLIT_S ? QD * quarter : 0;
+  bf16x8 qf[QD / 32];
+  {
+    const int h = h_base + c;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + min(h, a.H - 1)) * D + d0;
+    u32x4 qv[QD / 32];
+#pragma unroll
+    for (int t = 0; t < QD / 32; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qp + 32 * t + 8 * g);
+#pragma unroll
+    for (int t = 0; t < QD / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, h < a.H ? qv[t] : u32x4{0, 0, 0, 0});
+  }
+  f32x4 o[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) o[j] = f32x4{0, 0, 0, 0};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
+
+  for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) {
+    // 1. gather the chunk's rows (coalesced 16-byte loads) into a row-major LDS tile.
+    u32x4 v[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      v[i] = rp[i] ? *reinterpret_cast<const u32x4*>(rp[i] + 8 * cv) : u32x4{0, 0, 0, 0};
+    __syncthreads();   // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int li = i * NW + wave;
+      if (li < NLOADS) {
+        const int r = li * RPI + lr;
+        *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 8 * cv]) = v[i];
+        if (cv == 0) sh.rowok[r] = rp[i] != nullptr;
+      }
+    }
+    if (s0 + KC < s_end) {
+      before_rows(s0 + KC);
+      chunk_rows<D, LOADS, RPI, NW>(a, sm, b, s0 + KC, s_end, wave, lr, rp);
+    }
+    __syncthreads();
+    // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      sacc[n] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < QD / 32; ++t) {
+        u32x4 kb = *reinterpret_cast<const u32x4*>(&sh.kn[(16 * n + c) * KN_PITCH + d0 + 32 * t + 8 * g]);
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t], __builtin_bit_cast(bf16x8, kb), sacc[n], 0, 0, 0);
+      }
+    }
+    if constexpr (SPLIT_S) {
+      // Sum the four channel quarters in quarter order, the same order in every wave.
+      sh.spart[tile][quarter][0][lane] = sacc[0];
+      sh.spart[tile][quarter][1][lane] = sacc[1];
+      __syncthreads();
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        f32x4 t = sh.spart[tile][0][n][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          const f32x4 u = sh.spart[tile][w][n][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[r] += u[r];
+        }
+        sacc[n] = t;
+      }
+    }
+    // 3. online softmax (base-2), per head row 4g + r.
+    const bool valid0 = sh.rowok[c] != 0, valid1 = sh.rowok[16 + c] != 0;
+    float p[2][4], alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = valid0 ? sacc[0][r] * a.scale_log2 : -INFINITY;
+      const float x1 = valid1 ? sacc[1][r] * a.scale_log2 : -INFINITY;
+      const float cm = row16_max(fmaxf(x0, x1));
+      const float mn = fmaxf(m_run[r], cm);
+      const bool none = (mn == -INFINITY);
+      alpha[r] = none ? 1.f : fast_exp2(m_run[r] - mn);
+      // Round P to bf16 here so the running sum matches what the MFMA multiplies.
+      p[0][r] = none ? 0.f : bf16_to_f32((uint16_t)f32_to_bf16(fast_exp2(x0 - mn)));
+      p[1][r] = none ? 0.f : bf16_to_f32((uint16_t)f32_to_bf16(fast_exp2(x1 - mn)));
+      l_run[r] = l_run[r] * alpha[r] + row16_sum(p[0][r] + p[1][r]);
+      m_run[r] = mn;
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[j][r] *= alpha[r];
+    }
+    // 4. P to this wave's LDS slice as [head][key], read back as the A operand (row c, keys
+    // 8g .. 8g+7).
+    uint16_t* pw = sh.pb[wave];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        pw[(4 * g + r) * P_PITCH + 16 * n + c] = (uint16_t)(__float_as_uint(p[n][r]) >> 16);
+    __syncthreads();
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pw[c * P_PITCH + 8 * g]));
+    // B operand of P.V: column 16j + c of the tile, keys 8g .. 8g+7. ds_read_b64_tr_b16 gives
+    // lane i of a 16-lane group element e of the group's 8-byte chunks read with stride 16,
+    // so lane c addressing channels 16j + 4(c&3) .. +3 of key row 8g + (c>>2) (+4 for the
+    // upper half) receives keys 8g .. 8g+3 (8g+4 .. 8g+7) of channel 16j + c.
+    const uint16_t* vrow = &sh.kn[(8 * g + (c >> 2)) * KN_PITCH + 4 * (c & 3) + 16 * TPW * quarter];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 16 * j));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 4 * KN_PITCH + 16 * j));
+      const v8i16 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8, vb), o[j], 0, 0, 0);
+    }
+  }
+  // Partial result of this split: unnormalised O in the MFMA accumulator layout (one 16-byte
+  // store per tile and lane, coalesced; quarter q holds tiles TPW q ..), running max (base 2)
+  // and sum per head.
+  const int64_t pslot = (int64_t)b * a.n_splits + split;
+  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (pslot * a.head_tiles * 4 + z) * (D / 16) * 64;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) po[(TPW * quarter + j) * 64 + lane] = o[j];
+  if (quarter == 0 && c == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = h_base + 4 * g + r;
+      if (h < a.H) {
+        a.part_ml[(pslot * a.H + h) * 2] = m_run[r];
+        a.part_ml[(pslot * a.H + h) * 2 + 1] = l_run[r];
+      }
+    }
+  }
+}
+
+// LDS of one combine block that merges at most MAXS splits.
+template <int MAXS>
+struct CombineShared {
+  float wts[16][MAXS];
+  float lpart[16][MAXS];
+  float lsum[16];
+};
+
+// Merges the splits of 16-head group hg of sequence b for output block bx (64 words of the
+// MFMA-layout tile) with kAttnThreads threads (tid < kAttnThreads), by the log-sum-exp
+// identity: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2.
+template <int MAXS>
+__device__ __forceinline__ void combine_tile(const AttnArgs& a, float* out, float* lse, int bx, int hg, int b, int tid,
+                                             CombineShared<MAXS>& sh) {
+  float (&wts)[16][MAXS] = sh.wts;
+  float (&lpart)[16][MAXS] = sh.lpart;
+  float (&lsum)[16] = sh.lsum;
+  const int D = a.D;
+  const int ns = a.n_splits;
+  const int sq = tid & (kCombineLanes - 1);           // this lane's quarter of the splits
+  // Accumulator word index within the wave tile: (j, lane); this thread's 4 heads 4g + r.
+  const int wraw = bx * (kAttnThreads / kCombineLanes) + tid / kCombineLanes;
+  const int wpos = min(wraw, (D / 16) * 64 - 1);
+  const int j = wpos >> 6, lane = wpos & 63, g = lane >> 4, c = lane & 15;
+  const int tile = hg >> 2, wave = hg & 3;
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o);
+  const int64_t stride = (int64_t)a.head_tiles * 4 * (D / 16) * 64;   // one split, in f32x4
+  const int64_t base = (((int64_t)b * ns * a.head_tiles + tile) * 4 + wave) * (D / 16) * 64 + wpos;
+  // This lane's first splits (sq, sq + 4, ...) are requested before anything else, so they
+  // arrive while the split weights are computed.
+  constexpr int kBatch = 8;
+  f32x4 v[kBatch];
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) v[q] = po[base + (int64_t)min(sq + kCombineLanes * q, ns - 1) * stride];
+  // The 16 heads' (max, sum) pairs of every split come through LDS in one coalesced pass; then
+  // head hl = tid / 16 is handled by the 16 lanes of one DPP row, each lane a strided subset of
+  // the splits, and the head's maximum and weighted sum are row reductions.
+  const int nh = min(16, a.H - 16 * hg);
+  for (int e = tid; e < ns * nh; e += kAttnThreads) {
+    const int sp = e / nh, hl = e - sp * nh;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * ns + sp) * a.H + 16 * hg + hl) * 2);
+    wts[hl][sp] = ml.x;
+    lpart[hl][sp] = ml.y;
+  }
+  __syncthreads();
+  {
+    const int hl = tid >> 4, sl = tid & 15;
+    const int h = 16 * hg + hl;
+    float M = -INFINITY;
+    if (hl < nh)
+      for (int sp = sl; sp < ns; sp += 16) M = fmaxf(M, wts[hl][sp]);
+    M = row16_max(M);
+    float L = 0.f;
+    for (int sp = sl; sp < ns; sp += 16) {
+      const float ms = hl < nh ? wts[hl][sp] : -INFINITY;
+      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      L += wgt * (hl < nh ? lpart[hl][sp] : 0.f);
+      wts[hl][sp] = wgt;
+    }
+    L = row16_sum(L);
+    if (sl == 0) {
+      lsum[hl] = L;
+      if (lse && hl < nh && bx == 0) lse[(int64_t)b * a.H + h] = (L > 0.f) ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = 0; sp0 < ns; sp0 += kCombineLanes * kBatch) {
+    if (sp0 > 0) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        v[q] = po[base + (int64_t)min(sp0 + sq + kCombineLanes * q, ns - 1) * stride];
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int sp = sp0 + sq + kCombineLanes * q;
+      if (sp < ns) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(wts[4 * g + r][sp], v[q][r], acc[r]);
+      }
+    }
+  }
+  // Quad sum: the four lanes of a word hold disjoint split subsets.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    acc[r] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc[r]), 0xB1, 0xF, 0xF, false));
+    acc[r] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc[r]), 0x4E, 0xF, 0xF, false));
+  }
+  if (sq != 0 || wraw >= (D / 16) * 64) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hl = 4 * g + r, h = 16 * hg + hl;
+    if (h < a.H) {
+      const float L = lsum[hl];
+      out[((int64_t)b * a.H + h) * D + 16 * j + c] = (L > 0.f) ? acc[r] / L : 0.f;
+    }
+  }
+}
+
+// Host checks of chs_decode_attn's arguments (all but the workspace).
+inline chs_status check_args(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                             float scale, const void* q, const void* swa_kv, const int32_t* swa_len,
+                             const void* comp_kv, const int64_t* cu_comp, const int32_t* topk, int64_t max_comp,
+                             const float* out) {
+  if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
+  if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 128 || window < 0 || window > 4096 ||
+      k < 0 || k > 2048 || max_comp < 0 || max_comp >= (1LL << 31) || !(scale > 0.f) || !(scale < INFINITY))
+    return CHS_ERR_SHAPE;
+  if (dtype == CHS_BF16) {
+    if (d != 64 && d != 128 && d != 256 && d != 512) return CHS_ERR_SHAPE;
+  } else if (d < 1 || d > 1024 || d % 4 != 0) {
+    return CHS_ERR_SHAPE;
+  }
+  if (!q || !swa_len || !cu_comp || !out) return CHS_ERR_NULL;
+  if (window > 0 && !swa_kv) return CHS_ERR_NULL;
+  if (!comp_kv && (topk ? k > 0 : max_comp > 0)) return CHS_ERR_NULL;
+  return CHS_OK;
+}
+
+struct SplitPlan {
+  int32_t n_splits, kps;
+};
+
+inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, int32_t k, int64_t max_comp) {
+  const int64_t max_slots = (int64_t)window + (k > 0 ? k : max_comp);
+  const int gran = dt == CHS_BF16 ? kKeysPerChunk : kAttnThreads;
+  // Aim at about 512 workgroups: bf16 runs one per 16-head tile, fp32 one per head.
+  const int64_t blocks_per_split = (int64_t)batch * (dt == CHS_BF16 ? (H + 15) / 16 : H);
+  int64_t want = (512 + blocks_per_split - 1) / blocks_per_split;
+  const int64_t most = (max_slots + gran - 1) / gran;
+  if (want > most) want = most;
+  if (want > kCombineSplits) want = kCombineSplits;
+  if (want < 1) want = 1;
+  int64_t kps = (max_slots + want - 1) / want;
+  kps = (kps + gran - 1) / gran * gran;
+  if (kps < gran) kps = gran;
+  SplitPlan p;
+  p.kps = (int32_t)kps;
+  p.n_splits = (int32_t)((max_slots + kps - 1) / kps);
+  if (p.n_splits < 1) p.n_splits = 1;
+  return p;
+}
+
+inline size_t ws_bytes(chs_dtype dt, int32_t batch, int32_t H, int32_t D, const SplitPlan& p, float** po, float** pml,
+                char* base) {
+  const size_t nparts = (size_t)batch * p.n_splits * H;
+  const size_t hpad = dt == CHS_BF16 ? (size_t)(H + 63) / 64 * 64 : (size_t)H;
+  size_t o_po = 0, o_ml = align_up((size_t)batch * p.n_splits * hpad * D * 4, 256);
+  size_t total = align_up(o_ml + nparts * 2 * 4, 256);
+  if (po) *po = reinterpret_cast<float*>(base + o_po);
+  if (pml) *pml = reinterpret_cast<float*>(base + o_ml);
+  return total;
+}
+
+}  // namespace
+}  // namespace attn
+}  // namespace chs

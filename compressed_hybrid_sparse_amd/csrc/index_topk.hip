@@ -724,9 +724,9 @@ __device__ __attribute__((noinline)) uint32_t tau_by_radix(CollectShared& sh, ui
   return block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, ties_take);
 }
 
-__global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* topk) {
-  __shared__ CollectShared sh;
-  const int b = blockIdx.x;
+// The exact top-k of sequence b, run by a whole workgroup of kCThreads threads (t = threadIdx.x)
+// on LDS `sh`. Every early return below is uniform over the workgroup.
+__device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* topk, CollectShared& sh) {
   const uint32_t t = threadIdx.x;
   int64_t c0;
   const uint32_t n = (uint32_t)cand_count(a, b, &c0);   // <= 2^22: 32-bit index math below
@@ -934,6 +934,11 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
   ordered_select<1>(lk, li, T, tau, ties_take, keff, out, sh);
 }
 
+__global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* topk) {
+  __shared__ CollectShared sh;
+  collect_seq(a, blockIdx.x, topk, sh);
+}
+
 template <typename ET, int NH>
 void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a, int lpc) {
   switch (lpc) {
@@ -964,24 +969,28 @@ extern "C" size_t chs_index_topk_workspace_size(int32_t batch, int64_t max_cand,
   return chs::ws_layout(batch, max_cand, nullptr, nullptr);
 }
 
-extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads,
-                                     int32_t head_dim, int32_t k, const void* q_idx,
-                                     const float* w, const void* k_idx, const int64_t* cu_cand,
-                                     int64_t max_cand, float* scores, int32_t* topk,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace chs;
+namespace chs {
+namespace {
+
+// Validates chs_index_topk's arguments, lays out its workspace and fills *a and *lpc (lanes per
+// key row of the score kernel).
+chs_status topk_setup(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                      const void* q_idx, const float* w, const void* k_idx, const int64_t* cu_cand,
+                      int64_t max_cand, float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                      Args* a, int* lpc) {
   if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
   if (batch < 1 || batch > 65535 || k < 1 || k > kMaxK || max_cand < 0 || max_cand >= (1LL << 31))
     return CHS_ERR_SHAPE;
   if (max_cand > kMaxCand) return CHS_ERR_UNSUPPORTED;
   const size_t es = elem_size(dtype);
-  int nvec = 0, lpc = 2;
+  int nvec = 0;
+  *lpc = 2;
   if (q_idx) {
     if (n_heads < 1 || n_heads > 16 || head_dim < 8 || head_dim * es > 1024 || (head_dim * es) % 16 != 0)
       return CHS_ERR_SHAPE;
     if (!w || !k_idx) return CHS_ERR_NULL;
     nvec = (int)(head_dim * es / 16);   // 16-byte vectors per key row (<= 64)
-    while (lpc < nvec) lpc *= 2;        // one vector per lane, at least two lanes per row
+    while (*lpc < nvec) *lpc *= 2;      // one vector per lane, at least two lanes per row
   } else if (!scores) {
     return CHS_ERR_NULL;
   }
@@ -989,33 +998,55 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
   Workspace ws;
   const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
-  Args a;
-  a.q = q_idx; a.w = w; a.keys = k_idx; a.cu = cu_cand; a.max_cand = max_cand;
-  a.nh = n_heads; a.nvec = nvec; a.k = k; a.scores = scores; a.ws = ws;
-  a.gs = kGroup;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (max_cand > 0) {
-    if (q_idx) {
-      const int rw = kPasses * (64 / lpc);              // rows per wave
-      a.gs = std::min(rw, kGroup);
-      const dim3 grid((unsigned)((max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
-      if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, a, lpc);
-      else launch_scores<float>(grid, s, a, lpc);
-    } else {
-      // Loads per lane: the most (up to kPasses) that still give about 1024 workgroups
-      // (a workgroup covers 1024 * p scores).
-      int p = kPasses;
-      while (p > 1 && (int64_t)batch * ((max_cand + 1024 * p - 1) / (1024 * p)) < 1024) p /= 2;
-      const dim3 grid((unsigned)((max_cand + 1024 * p - 1) / (1024 * p)), (unsigned)batch);
-      switch (p) {
-        case 1: hipLaunchKernelGGL(max_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(max_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(max_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL(max_kernel<kPasses>, grid, dim3(kThreads), 0, s, a); break;
-      }
+  a->q = q_idx; a->w = w; a->keys = k_idx; a->cu = cu_cand; a->max_cand = max_cand;
+  a->nh = n_heads; a->nvec = nvec; a->k = k; a->scores = scores; a->ws = ws;
+  a->gs = kGroup;
+  return CHS_OK;
+}
+
+// The first kernel of the selection: scores and group statistics (q_idx given), or group
+// statistics of the caller's scores. Sets a->gs. Launches nothing when max_cand is 0.
+chs_status topk_first(chs_dtype dtype, int32_t batch, Args* a, int lpc, hipStream_t s) {
+  const int64_t max_cand = a->max_cand;
+  if (max_cand == 0) return CHS_OK;
+  if (a->q) {
+    const int rw = kPasses * (64 / lpc);              // rows per wave
+    a->gs = std::min(rw, kGroup);
+    const dim3 grid((unsigned)((max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
+    if (dtype == CHS_BF16) launch_scores<uint16_t>(grid, s, *a, lpc);
+    else launch_scores<float>(grid, s, *a, lpc);
+  } else {
+    // Loads per lane: the most (up to kPasses) that still give about 1024 workgroups
+    // (a workgroup covers 1024 * p scores).
+    int p = kPasses;
+    while (p > 1 && (int64_t)batch * ((max_cand + 1024 * p - 1) / (1024 * p)) < 1024) p /= 2;
+    const dim3 grid((unsigned)((max_cand + 1024 * p - 1) / (1024 * p)), (unsigned)batch);
+    switch (p) {
+      case 1: hipLaunchKernelGGL(max_kernel<1>, grid, dim3(kThreads), 0, s, *a); break;
+      case 2: hipLaunchKernelGGL(max_kernel<2>, grid, dim3(kThreads), 0, s, *a); break;
+      case 4: hipLaunchKernelGGL(max_kernel<4>, grid, dim3(kThreads), 0, s, *a); break;
+      default: hipLaunchKernelGGL(max_kernel<kPasses>, grid, dim3(kThreads), 0, s, *a); break;
     }
-    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads,
+                                     int32_t head_dim, int32_t k, const void* q_idx,
+                                     const float* w, const void* k_idx, const int64_t* cu_cand,
+                                     int64_t max_cand, float* scores, int32_t* topk,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace chs;
+  Args a;
+  int lpc = 2;
+  chs_status st = topk_setup(dtype, batch, n_heads, head_dim, k, q_idx, w, k_idx, cu_cand, max_cand, scores, topk,
+                             workspace, workspace_bytes, &a, &lpc);
+  if (st != CHS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (topk_first(dtype, batch, &a, lpc, s) != CHS_OK) return CHS_ERR_LAUNCH;
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
   return launch_status();
 }
