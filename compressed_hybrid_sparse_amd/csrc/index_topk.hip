@@ -7,9 +7,11 @@
 // "DeepSeek-V4 本地部署，SGLang 把活做絕了", Kernel 層一堆狠活: top-512 of 256K at 1M context.
 //
 // The pages' design reduces per-CTA histograms inside a thread-block cluster through
-// distributed shared memory, which gfx950 does not have; on MI355X a device-scope fence costs
-// tens of nanoseconds per workgroup, serialised, and same-address atomics about ten. So no
-// kernel here synchronises workgroups with each other, and a call is two kernels:
+// distributed shared memory, which gfx950 does not have; on MI355X the L2s of the 8 XCDs are
+// not coherent, so a handoff between workgroups inside a kernel needs an agent-scope release
+// and acquire (an L2 write-back and invalidate, microseconds when data is in flight), while
+// back-to-back kernels in a graph hand off for free. So no kernel here synchronises
+// workgroups with each other, and a call is two kernels:
 //
 //   K1 score_kernel streams the index keys once. LPC lanes (16 for 128 bf16 channels) share a
 //      key row, one 16-byte non-temporal load each, so every wave load instruction reads one
@@ -19,24 +21,25 @@
 //      It writes the fp32 scores and, for every group of GS consecutive candidates (GS = 32; 16
 //      or 8 for very wide keys), the group's largest key, the position of that maximum and
 //      its second-largest key. max_kernel does the same for caller-provided scores.
-//   K2 collect_kernel, one 1024-thread workgroup per sequence (one CU, so the work it does per
-//      candidate is what costs: it touches group statistics, not scores, wherever it can):
-//      (A) loads the group maxima and bins them, (key - smallest) >> shift, into 2048 monotone
-//          bins; L = the smallest maximum in the bin holding the k-th largest maximum. L never
-//          exceeds the k-th largest score, because k disjoint groups each hold a score >= L;
-//          so every top-k candidate, and every tie at the threshold, has key >= L and sits in
-//          a group whose maximum is >= L;
-//      (B) lists those groups in index order (one block scan of per-thread counts); a listed
-//          group whose second key is below L holds exactly one candidate >= L, its maximum,
-//          known from the statistics; the others ("full", typically a few percent) are read;
-//      (C) reads the full groups whole, two per wave, and builds the superset of keys >= L in
-//          index order in LDS, binning its keys into 2048 monotone bins over [L, max];
-//      (D) the bin holding the k-th largest kept key gives tau after comparing only the few
+//   K2 collect_kernel, one 1024-thread workgroup per sequence (one CU, 4 waves per SIMD, so
+//      the instructions it issues per candidate are what costs: it touches group statistics,
+//      not scores, wherever it can):
+//      (A) bins the maxima of runs of 4 groups (or of single groups when there are few),
+//          (key - smallest) >> shift, into 2048 monotone bins; L = the smallest run maximum in
+//          the bin holding the k-th largest. L never exceeds the k-th largest score, because
+//          k disjoint runs each hold a score >= L; so every top-k candidate, and every tie at
+//          the threshold, has key >= L and sits in a group whose maximum is >= L;
+//      (B) builds the superset of keys >= L in index order in LDS with one block scan: a group
+//          whose maximum is >= L but whose second key is below L holds exactly one such key,
+//          its maximum, known from the statistics; the others ("full", typically a few
+//          percent) are read whole, two per wave; kept keys are binned into 2048 monotone
+//          bins over [L, max];
+//      (C) the bin holding the k-th largest kept key gives tau after comparing only the few
 //          keys inside it (a crowded bin, from heavy ties, falls back to radix steps); an
 //          ordered pass then writes the keys above tau and the first ties at tau, ascending
 //          by index (no sort).
-//      Inputs that defeat the bound (a superset or list too large for LDS: heavy ties, many
-//      equal zeros) are selected by the whole workgroup straight from the score array instead.
+//      Inputs that defeat the bound (a superset too large for LDS: heavy ties, many equal
+//      zeros) are selected by the whole workgroup straight from the score array instead.
 //      Gathers go through buffer loads (32-bit offsets, reads beyond the array return 0).
 // The composite order (key descending, then index ascending) is total, so the selected set is
 // unique and bit-identical to a full sort of the same scores.
@@ -56,10 +59,8 @@ constexpr int kCWaves = kCThreads / 64;
 constexpr int kMaxPerThread = 8;       // group maxima per K2 thread per tile (contiguous)
 constexpr int kTile = kCThreads * kMaxPerThread;   // 8192: the bound ranks the first tile
 constexpr int kBins = 2048;            // bound and superset histograms; global radix bins
-constexpr int kListCap = 4096;         // groups the LDS list holds
 constexpr int kLdsCand = 4096;         // superset entries LDS holds
-constexpr int kFullCap = 256;          // listed groups whose second key reaches L (scanned whole)
-constexpr int kItemRounds = 6;         // superset items (4 candidates each) per K2 thread per batch
+constexpr int kFullCap = 256;          // groups whose second key may reach L (read whole)
 constexpr int kBinCap = 64;            // threshold-bin entries resolved directly
 constexpr int kGlobalRounds = 16;      // global path: scores per thread per batch
 constexpr int kScanRounds = 16;        // the most rounds one ordered scan covers
@@ -563,19 +564,15 @@ __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
 struct alignas(16) CollectShared {
   uint32_t key[kLdsCand];       // superset keys, index order
   uint32_t idx[kLdsCand];       // superset candidate indices
-  uint32_t list[kListCap];      // groups whose maximum is >= L, ascending
-  uint32_t lmax[kListCap];      // their maximum keys
-  uint32_t lpos[kListCap];      // position of the maximum, or kFullFlag | slot among full groups
-  uint32_t fkey[kFullCap][kGroup];   // keys of the full groups
-  uint32_t flist[kFullCap];     // list position of each full group
-  uint32_t fmask[kFullCap];     // its candidates with key >= L
-  uint32_t hist[kBins];         // maxima bins (A), then superset bins (C, D)
+  uint32_t fkey[kFullCap][kGroup];   // kept keys of the full groups, by slot
+  uint32_t fmask[kFullCap];     // their candidates with key >= L
+  uint32_t fgroup[kFullCap];    // the group in each slot
+  uint32_t hist[kBins];         // bound bins (A), then superset bins (B, D)
   uint32_t red[2 * kCWaves];
   uint32_t tot[kScanRounds * kCWaves + 4];
   uint32_t binv[kBinCap];       // keys in the bin that holds the k-th largest
-  uint32_t misc[8];
+  uint32_t misc[8];             // 0, 1: bin and rank; 2: bin fill; 3, 4: tau, ties; 5: full slots
 };
-constexpr uint32_t kFullFlag = 0x80000000u;
 
 // Ordered scan over items (round r, thread t), taken in that order, for the K2 block: given
 // this thread's count for each round, returns the total and sets off[r] to the sum of the
@@ -724,6 +721,41 @@ __device__ __attribute__((noinline)) uint32_t tau_by_radix(CollectShared& sh, ui
   return block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, ties_take);
 }
 
+// The bound of the collect step: over the workgroup's nonzero values u (NU per thread, at
+// least keff of them), the smallest value in the bin holding the keff-th largest or above,
+// with 2048 monotone bins (u - umin) >> shift. Also returns the largest value in *umax.
+template <int NU>
+__device__ uint32_t block_bound(const uint32_t (&u)[NU], uint32_t keff, uint32_t* umax, CollectShared& sh) {
+  const uint32_t t = threadIdx.x;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    lo = min(lo, u[j] - 1u);                            // key 0 wraps to the top: ignored
+    hi = max(hi, u[j]);
+  }
+  block_minmax_t<kCWaves>(&lo, &hi, sh.red);            // its barriers also order the clears
+  const uint32_t vmin = lo + 1u;
+  *umax = hi;
+  const int span_bits = differing_bits(0u, hi - vmin);
+  const int shift = span_bits > 11 ? span_bits - 11 : 0;
+#pragma unroll
+  for (int j = 0; j < NU; ++j)
+    if (u[j] != 0u) atomicAdd(&sh.hist[(u[j] - vmin) >> shift], 1u);
+  __syncthreads();
+  const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
+  uint32_t total;
+  const uint32_t run = block_exclusive_sum_t<kCWaves>(h0 + h1, &total, sh.red);
+  if (run < keff && run + h0 + h1 >= keff) sh.misc[0] = run + h0 >= keff ? kBins - 1 - 2 * t : kBins - 2 - 2 * t;
+  __syncthreads();
+  const uint32_t floor_key = vmin + (sh.misc[0] << shift);
+  uint32_t lmin = 0xFFFFFFFFu, unused = 0;
+#pragma unroll
+  for (int j = 0; j < NU; ++j)
+    if (u[j] >= floor_key) lmin = min(lmin, u[j]);
+  block_minmax_t<kCWaves>(&lmin, &unused, sh.red);
+  return lmin;
+}
+
 // The exact top-k of sequence b, run by a whole workgroup of kCThreads threads (t = threadIdx.x)
 // on LDS `sh`. Every early return below is uniform over the workgroup.
 __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* topk, CollectShared& sh) {
@@ -755,118 +787,98 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* topk,
     for (int j = 0; j < 4; ++j) { mv[j] = m0[j]; mv[4 + j] = m1[j]; sv[j] = s0[j]; sv[4 + j] = s1[j]; }
   };
 
-  // (A) The bound L from the first tile of group maxima: 2048 bins of (key - vmin) >> shift.
+  // (A) The bound L: at least keff groups have a maximum >= L, so L never exceeds the k-th
+  // largest score. L is the smallest, in the bin holding the keff-th largest or above, of the
+  // first tile's run maxima: the maxima of runs of 4 consecutive groups when the tile has at
+  // least 4 keff groups (a run at or above L holds a group at or above L), else the group
+  // maxima. Bins: (u - umin) >> shift, 2048 of them, monotone. Groups past the sequence read
+  // as key 0, below every score, and take no part.
   load_tile(0);
   for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;
-  if (t == 0) sh.misc[2] = 0;
-  uint32_t vmin = 0xFFFFFFFFu, vmax = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxPerThread; ++j)
-    if (kMaxPerThread * t + j < nt) { vmin = min(vmin, mv[j]); vmax = max(vmax, mv[j]); }
-  block_minmax_t<kCWaves>(&vmin, &vmax, sh.red);        // its barriers also order the clears
-  uint32_t L = 0;                                       // with fewer than k groups: every candidate
-  if (nt >= keff) {
-    const int span_bits = differing_bits(0u, vmax - vmin);
-    const int shift = span_bits > 11 ? span_bits - 11 : 0;   // monotone bins below 2048
-#pragma unroll
-    for (int j = 0; j < kMaxPerThread; ++j)
-      if (kMaxPerThread * t + j < nt) atomicAdd(&sh.hist[(mv[j] - vmin) >> shift], 1u);
+  if (t == 0) { sh.misc[2] = 0; sh.misc[5] = 0; }
+  uint32_t L = 0, vmax = 0;
+  if (nt >= 4u * keff) {
+    const uint32_t u[2] = {max(max(mv[0], mv[1]), max(mv[2], mv[3])), max(max(mv[4], mv[5]), max(mv[6], mv[7]))};
+    L = block_bound<2>(u, keff, &vmax, sh);
+  } else if (nt >= keff) {
+    L = block_bound<kMaxPerThread>(mv, keff, &vmax, sh);
+  } else {                                              // fewer than k groups: every candidate
     __syncthreads();
-    const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
-    uint32_t total;
-    const uint32_t run = block_exclusive_sum_t<kCWaves>(h0 + h1, &total, sh.red);
-    if (run < keff && run + h0 + h1 >= keff) sh.misc[0] = run + h0 >= keff ? kBins - 1 - 2 * t : kBins - 2 - 2 * t;
-    __syncthreads();
-    const uint32_t floor_key = vmin + (sh.misc[0] << shift);   // every maximum in the bin or above
-    uint32_t lmin = 0xFFFFFFFFu, unused = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxPerThread; ++j)
-      if (kMaxPerThread * t + j < nt && mv[j] >= floor_key) lmin = min(lmin, mv[j]);
-    block_minmax_t<kCWaves>(&lmin, &unused, sh.red);
-    L = lmin;
   }
   for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;   // reused for the superset
 
-  // (B) The groups whose maximum is >= L, ascending; among them the "full" ones, whose second
-  // key may reach L too. One scan places both (counts packed in 16-bit halves).
-  uint32_t G = 0, F = 0;
-  for (uint32_t t0 = 0; t0 < ng; t0 += kTile) {
-    if (t0 > 0) load_tile(t0);
-    uint32_t f = 0, ff = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxPerThread; ++j) {
-      const bool listed = t0 + kMaxPerThread * t + j < ng && mv[j] >= L;
-      f |= (listed ? 1u : 0u) << j;
-      ff |= ((listed && (sv[j] | 31u) >= L) ? 1u : 0u) << j;
-    }
-    const uint32_t cnt[1] = {(uint32_t)__popc(f) | ((uint32_t)__popc(ff) << 16)};
-    uint32_t off[1];
-    const uint32_t total = ordered_scan(cnt, off, sh);
-    uint32_t pos = G + (off[0] & 0xFFFFu), fpos = F + (off[0] >> 16);
-#pragma unroll
-    for (int j = 0; j < kMaxPerThread; ++j) {
-      if ((f >> j) & 1u) {
-        const bool full = (ff >> j) & 1u;
-        if (pos < (uint32_t)kListCap) {
-          sh.list[pos] = t0 + kMaxPerThread * t + j;
-          sh.lmax[pos] = mv[j];
-          sh.lpos[pos] = full ? (kFullFlag | fpos) : (sv[j] & 31u);
-          if (full && fpos < (uint32_t)kFullCap) sh.flist[fpos] = pos;
-        }
-        ++pos;
-        fpos += full ? 1u : 0u;
-      }
-    }
-    G += total & 0xFFFFu;
-    F += total >> 16;
-  }
-  __syncthreads();
-  bool fits = G <= (uint32_t)kListCap && F <= (uint32_t)kFullCap;
-
-  // (C) The superset: candidates of the listed groups with key >= L, in index order, binned
-  // by key over [L, vmax] (monotone, clamped) as they are kept. A listed group contributes
-  // its maximum (known) unless it is full; full groups are read whole, two per wave, and
-  // their kept keys staged in LDS.
-  uint32_t T = 0;
+  // (B) The superset: every candidate with key >= L, in index order, binned by key over
+  // [L, max] as it is kept. A group whose maximum is below L holds none. A group whose
+  // statistics word shows no second key that could reach L ((word | 31) < L) holds exactly
+  // one, its maximum at the stored position. The others ("full", typically a few percent of
+  // the listed ones) are read whole by the thread that owns them, their kept keys staged in
+  // LDS. One ordered scan per tile places everything.
+  uint32_t T = 0, fdone = 0;                            // superset size; full slots read so far
+  bool fits = true;
   const uint32_t top = max(vmax, L);
   const float scale2 = top > L ? (float)(kBins - 1) / (float)(top - L) : 0.f;
   auto bin2 = [&](uint32_t v) { return min((uint32_t)(kBins - 1), (uint32_t)((float)(v - L) * scale2)); };
-  if (fits) {
-    const int lane = t & 63, half = lane >> 5, li = lane & 31;
-    for (uint32_t j0 = 2 * (t >> 6); j0 < F; j0 += 2 * kCWaves) {
-      const uint32_t j = j0 + half;
-      const bool on = j < F;
-      const uint32_t c = on ? (sh.list[sh.flist[j]] << gshift) + li : 0u;
-      const uint32_t v = score_key(__uint_as_float(buffer_u32(srs, c)));
-      const bool keep = on && li < gs && c < n && v >= L;
-      const uint32_t m = (uint32_t)(__ballot(keep) >> (32 * half));
-      if (on) {
-        sh.fkey[j][li] = v;
-        if (li == 0) sh.fmask[j] = m;
+  for (uint32_t t0 = 0; t0 < ng; t0 += kTile) {
+    if (t0 > 0) load_tile(t0);
+    const uint32_t g0 = t0 + kMaxPerThread * t;          // this thread's first group
+    uint32_t lm = 0, fm = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerThread; ++j) {
+      const bool listed = g0 + j < ng && mv[j] >= L;
+      lm |= (listed ? 1u : 0u) << j;
+      fm |= ((listed && (sv[j] | 31u) >= L) ? 1u : 0u) << j;
+    }
+    // Full groups get LDS slots (in no particular order) and are read whole, two per wave,
+    // one score per lane; then each thread counts what its groups keep.
+    uint32_t slot0 = 0;
+    if (fm) {
+      slot0 = atomicAdd(&sh.misc[5], (uint32_t)__popc(fm));
+      uint32_t slot = slot0;
+#pragma unroll
+      for (int j = 0; j < kMaxPerThread; ++j)
+        if ((fm >> j) & 1u) {
+          if (slot < (uint32_t)kFullCap) sh.fgroup[slot] = g0 + j;
+          ++slot;
+        }
+    }
+    __syncthreads();
+    const uint32_t nfull = min(sh.misc[5], (uint32_t)kFullCap);   // this tile's slots: fdone ..
+    {
+      const int lane = t & 63, half = lane >> 5, li = lane & 31;
+      for (uint32_t j0 = fdone + 2 * (t >> 6); j0 < nfull; j0 += 2 * kCWaves) {
+        const uint32_t j = j0 + half;
+        const bool on = j < nfull;
+        const uint32_t c = on ? (sh.fgroup[j] << gshift) + li : 0u;
+        const uint32_t v = score_key(__uint_as_float(buffer_u32(srs, c)));
+        const bool keep = on && li < gs && c < n && v >= L;
+        const uint32_t m = (uint32_t)(__ballot(keep) >> (32 * half));
+        if (on) {
+          sh.fkey[j][li] = v;
+          if (li == 0) sh.fmask[j] = m;
+        }
       }
     }
     __syncthreads();
-    for (uint32_t e0 = 0; e0 < G; e0 += kCThreads) {
-      const uint32_t e = e0 + t;
-      uint32_t lp = 0, c[1] = {0}, off[1];
-      if (e < G) {
-        lp = sh.lpos[e];
-        c[0] = (lp & kFullFlag) ? (uint32_t)__popc(sh.fmask[lp & ~kFullFlag]) : 1u;
-      }
-      const uint32_t total = ordered_scan(c, off, sh);
-      if (T + total <= (uint32_t)kLdsCand && e < G) {
-        const uint32_t gbase = sh.list[e] << gshift;
-        uint32_t pos = T + off[0];
-        if (!(lp & kFullFlag)) {
-          const uint32_t v = sh.lmax[e];
-          sh.key[pos] = v;
-          sh.idx[pos] = gbase + lp;
-          atomicAdd(&sh.hist[bin2(v)], 1u);
+    fdone = nfull;
+    uint32_t cnt[1] = {(uint32_t)__popc(lm & ~fm)}, off[1];
+    for (uint32_t i = 0, nf = (uint32_t)__popc(fm); i < nf; ++i)
+      if (slot0 + i < (uint32_t)kFullCap) cnt[0] += (uint32_t)__popc(sh.fmask[slot0 + i]);
+    const uint32_t total = ordered_scan(cnt, off, sh);
+    if (sh.misc[5] > (uint32_t)kFullCap || T + total > (uint32_t)kLdsCand) { fits = false; break; }
+    uint32_t pos = T + off[0];
+#pragma unroll
+    for (int j = 0; j < kMaxPerThread; ++j) {
+      if ((lm >> j) & 1u) {
+        const uint32_t gbase = (g0 + j) << gshift;
+        if (!((fm >> j) & 1u)) {
+          sh.key[pos] = mv[j];
+          sh.idx[pos] = gbase + (sv[j] & 31u);
+          atomicAdd(&sh.hist[bin2(mv[j])], 1u);
+          ++pos;
         } else {
-          const uint32_t j = lp & ~kFullFlag;
-          for (uint32_t m = sh.fmask[j]; m; m &= m - 1) {
-            const uint32_t i = (uint32_t)__ffs(m) - 1;
-            const uint32_t v = sh.fkey[j][i];
+          const uint32_t slot = slot0 + (uint32_t)__popc(fm & ((1u << j) - 1u));
+          for (uint32_t m = sh.fmask[slot]; m; m &= m - 1) {
+            const uint32_t i = (uint32_t)__ffs(m) - 1, v = sh.fkey[slot][i];
             sh.key[pos] = v;
             sh.idx[pos] = gbase + i;
             atomicAdd(&sh.hist[bin2(v)], 1u);
@@ -874,13 +886,12 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* topk,
           }
         }
       }
-      T += total;
-      if (T > (uint32_t)kLdsCand) { fits = false; break; }
     }
+    T += total;
   }
   __syncthreads();
 
-  // (D) Exact selection.
+  // (C) Exact selection.
   if (!fits) {                                          // global path
     select_global(srs, n, keff, out, sh);
     return;
