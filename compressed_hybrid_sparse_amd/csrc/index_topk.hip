@@ -567,7 +567,7 @@ struct alignas(16) CollectShared {
   uint32_t fkey[kFullCap][kGroup];   // kept keys of the full groups, by slot
   uint32_t fmask[kFullCap];     // their candidates with key >= L
   uint32_t fgroup[kFullCap];    // the group in each slot
-  uint32_t hist[kBins];         // bound bins (A), then superset bins (B, D)
+  uint32_t hist[kBins];         // bound bins (A), then superset bins (B, C)
   uint32_t red[2 * kCWaves];
   uint32_t tot[kScanRounds * kCWaves + 4];
   uint32_t binv[kBinCap];       // keys in the bin that holds the k-th largest
