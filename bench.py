@@ -15,8 +15,9 @@ The headline value is the decode attention-layer latency (index_topk + decode_at
 microseconds per step: decode steps run back to back, replayed from a HIP graph (the
 stream-launched figure is reported beside it), median over repetitions. The line also reports the compressor's
 bandwidth, the standalone top-512-of-262144 latency (one row) and the fraction of the HBM
-roofline on a 64-row batch, plus the roofline of the dominant kernel and the CPU oracle timed
-on this host (a reported baseline, not a target).
+roofline on a 64-row batch, the same decode step with FP8 (E4M3) index keys and per-row scales
+(chs_index_topk_fp8; a component, not the headline), plus the roofline of the dominant kernel
+and the CPU oracle timed on this host (a reported baseline, not a target).
 
 Cache defeat: the index keys (64 MiB) rotate over 8 device copies (512 MiB, above the 256 MB
 Infinity Cache); the standalone top-k rows rotate over 256 copies (bs=1) and 8 copies (64 rows).
@@ -215,17 +216,40 @@ def main():
     for i in range(nk):
         decode(i)
     dec_ms = loop_ms(lambda: [decode(i) for i in range(nk)], 20, nk)
-    graph_ms = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(nk):
-                decode(i)
-        g.replay()
-        torch.cuda.synchronize()
-        graph_ms = loop_ms(g.replay, 20, nk)
-    except Exception as exc:   # graph capture is an extra measurement; report why it is absent
-        print(f"graph replay unavailable: {exc}", file=sys.stderr)
+    def graph_loop_ms(fn, count):
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(count):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            return loop_ms(g.replay, 20, count)
+        except Exception as exc:   # graph capture is an extra measurement; report why it is absent
+            print(f"graph replay unavailable: {exc}", file=sys.stderr)
+            return None
+
+    graph_ms = graph_loop_ms(decode, nk)
+
+    # The same step with FP8 (E4M3) index keys and per-row scales (chs_index_topk_fp8), which
+    # halves the key read. The keys are quantised per row on the device (input preparation):
+    # scale = max|k| / 448, code = E4M3(k / scale); 16 copies (528 MiB) defeat the cache.
+    def quantise(kb):
+        kf = kb.float()
+        sc = (kf.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
+        return (kf / sc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc.contiguous()
+
+    fp8 = [quantise(keys[i % nk]) for i in range(2 * nk)]
+
+    def decode_fp8(i):
+        codes, sc = fp8[i % len(fp8)]
+        chs.index_topk_fp8(inp["q_idx"], inp["w"], codes, sc, inp["cu_groups"], k, G, scores, ws_topk, topk)
+        chs.decode_attn(inp["q"], inp["swa_kv"], inp["swa_len"], comp, inp["cu_groups"], topk, scale, G,
+                        ws_attn, out, lse)
+
+    for i in range(len(fp8)):
+        decode_fp8(i)
+    fp8_graph_ms = graph_loop_ms(decode_fp8, len(fp8))
     # Per-call breakdown (events around each call; each event adds a little to what it brackets).
     bd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -278,6 +302,7 @@ def main():
     comp_bytes = 2 * n * d * e + layer.m * d * 4 + G * d * e
     step_bytes = (G * wl.idx_dim * e + wl.idx_heads * wl.idx_dim * e + wl.idx_heads * 4 + k * 4
                   + (k + wl.window) * d * e + H * d * e + H * d * 4 + H * 4)
+    step_fp8_bytes = step_bytes - G * wl.idx_dim * e + G * wl.idx_dim + G * 4   # 1-byte keys + fp32 row scales
     topk_row_bytes = G * 4 + 512 * 4
     c_us = median(comp_ms) * 1e3
     dec_stream_us = median(dec_ms) * 1e3
@@ -314,6 +339,12 @@ def main():
                                "decode_attn_us": round(median(attn_ms) * 1e3, 2),
                                "algorithmic_bytes": step_bytes,
                                "hbm_frac": round(step_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4)},
+            "decode_step_fp8_keys_us": {
+                "value_source": "graph replay", "call": "chs_index_topk_fp8 + chs_decode_attn",
+                "graph_median": None if fp8_graph_ms is None else round(median(fp8_graph_ms) * 1e3, 2),
+                "algorithmic_bytes": step_fp8_bytes,
+                "hbm_frac": None if fp8_graph_ms is None else
+                round(step_fp8_bytes / (median(fp8_graph_ms) * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)},
             "topk_512_of_262144_us": {"bs1_median": round(t1_us, 2), "bs1_p90": round(pct(t1_ms, 0.9) * 1e3, 2),
                                       "rows64_median": round(t64_us, 2),
                                       "rows64_hbm_frac": round(64 * topk_row_bytes / (t64_us * 1e-6)

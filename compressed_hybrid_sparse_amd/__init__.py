@@ -20,7 +20,7 @@ _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE
            4: "CHS_ERR_WORKSPACE", 5: "CHS_ERR_UNSUPPORTED", 6: "CHS_ERR_LAUNCH"}
 EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
-           "chs_decode_attn")
+           "chs_decode_attn", "chs_index_topk_fp8")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -53,7 +53,8 @@ def lib():
         L.chs_decode_attn_workspace_size.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i64]
         L.chs_decode_attn.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _p, _p,
                                       _i64, _p, _p, _p, _sz, _p]
-        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn"):
+        L.chs_index_topk_fp8.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _p]
+        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -209,3 +210,31 @@ def decode_attn(q, swa_kv, swa_len, comp_kv, cu_comp, topk=None, scale=None, max
                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()),
            "chs_decode_attn")
     return out, lse
+
+
+def index_topk_fp8(q_idx, w, k_codes, k_scale, cu_cand, k: int, max_cand=None, scores=None, workspace=None,
+                   out=None):
+    """Indexer scores with FP8 E4M3 keys and per-row scales, then the exact top-k
+    (chs_index_topk_fp8). q_idx: [B, Hi, dim] bf16; w: [B, Hi] fp32; k_codes: [G, dim] uint8 or
+    torch.float8_e4m3fn; k_scale: [G] fp32; cu_cand: [B+1] int64. Returns (topk [B, k] int32,
+    scores or None)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 2)
+    if k_codes.dtype != torch.uint8:
+        k_codes = k_codes.view(torch.uint8)
+    _need(k_codes, "k_codes", torch.uint8, 2)
+    _need(k_scale, "k_scale", torch.float32, 1)
+    _need(cu_cand, "cu_cand", torch.int64, 1)
+    batch = cu_cand.numel() - 1
+    nh, dim = q_idx.shape[1], q_idx.shape[2]
+    if max_cand is None:
+        max_cand = _host_max_diff(cu_cand)
+    if workspace is None:
+        workspace = index_topk_workspace(batch, max_cand, k, cu_cand.device)
+    if out is None:
+        out = torch.empty(batch, k, dtype=torch.int32, device=cu_cand.device)
+    _check(lib().chs_index_topk_fp8(batch, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(k_codes), _ptr(k_scale),
+                                    _ptr(cu_cand), int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
+                                    workspace.numel(), _stream()),
+           "chs_index_topk_fp8")
+    return out, scores

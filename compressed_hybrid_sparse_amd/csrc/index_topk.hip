@@ -44,6 +44,7 @@
 // The composite order (key descending, then index ascending) is total, so the selected set is
 // unique and bit-identical to a full sort of the same scores.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -121,6 +122,7 @@ struct Args {
   int32_t gs;           // group size (a power of two)
   int32_t k;
   float* scores;        // caller's packed array, or NULL -> workspace
+  const float* kscale;  // [cu[batch]] per-row scales of FP8 keys (NULL otherwise)
   Workspace ws;
 };
 
@@ -253,18 +255,22 @@ __device__ __forceinline__ int differing_bits(uint32_t lo, uint32_t hi) {
 template <typename ET>
 struct Dot16;
 
+// Dot product of one lane's 16 bytes of a key row with the matching query elements, which
+// take QV 16-byte vectors.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Element j is copied to a scalar before the bit cast: clang lowers a bit cast applied
+// directly to an ext-vector element access as a cast of element 0.
+__device__ __forceinline__ bf16x2 bf16_pair(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
+
 template <>
 struct Dot16<uint16_t> {   // 8 bf16 per 16 bytes: four v_dot2_f32_bf16
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  // Element j is copied to a scalar before the bit cast: clang lowers a bit cast applied
-  // directly to an ext-vector element access as a cast of element 0.
-  __device__ static bf16x2 pair(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
-  __device__ static float dot(const u32x4& a, const u32x4& b) {
+  static constexpr int QV = 1;
+  __device__ static float dot(const u32x4* q, const u32x4& k) {
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t x = a[j], y = b[j];
-      acc = __builtin_amdgcn_fdot2_f32_bf16(pair(x), pair(y), acc, false);
+      const uint32_t x = q[0][j], y = k[j];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(x), bf16_pair(y), acc, false);
     }
     return acc;
   }
@@ -272,12 +278,33 @@ struct Dot16<uint16_t> {   // 8 bf16 per 16 bytes: four v_dot2_f32_bf16
 
 template <>
 struct Dot16<float> {      // 4 fp32 per 16 bytes
-  __device__ static float dot(const u32x4& a, const u32x4& b) {
+  static constexpr int QV = 1;
+  __device__ static float dot(const u32x4* q, const u32x4& k) {
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t x = a[j], y = b[j];
+      const uint32_t x = q[0][j], y = k[j];
       acc = fmaf(__uint_as_float(x), __uint_as_float(y), acc);
+    }
+    return acc;
+  }
+};
+
+template <>
+struct Dot16<uint8_t> {    // 16 FP8 E4M3 per 16 bytes against 16 bf16 query values (2 vectors)
+  static constexpr int QV = 2;
+  // Every E4M3 value is a bf16 value, so the conversion (scale 1) is exact and the products
+  // go through v_dot2_f32_bf16 like bf16 keys.
+  __device__ static float dot(const u32x4* q, const u32x4& k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = k[j];
+      const uint32_t q0 = q[j >> 1][2 * (j & 1)], q1 = q[j >> 1][2 * (j & 1) + 1];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(q0), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false),
+                                            acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(q1), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true),
+                                            acc, false);
     }
     return acc;
   }
@@ -347,30 +374,36 @@ __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
   const int nvec = a.nvec;
   const int subc = sub < nvec ? sub : nvec - 1;
   // Queries and weights first (their loads complete first), then every key load.
-  const u32x4* qb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + (size_t)b * a.nh * nvec * 16);
-  u32x4 qv[NH];
+  constexpr int QV = Dot16<ET>::QV;                     // query vectors per key vector
+  constexpr bool kScaled = std::is_same<ET, uint8_t>::value;
+  const u32x4* qb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + (size_t)b * a.nh * nvec * QV * 16);
+  u32x4 qv[NH][QV];
   float wv[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int hc = h < a.nh ? h : a.nh - 1;
-    qv[h] = qb[hc * nvec + subc];
+#pragma unroll
+    for (int i = 0; i < QV; ++i) qv[h][i] = qb[(hc * nvec + subc) * QV + i];
     wv[h] = a.w[(size_t)b * a.nh + hc];
   }
   __builtin_amdgcn_sched_barrier(0);                   // query loads go out (and return) first
   const u32x4* kb = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.keys) + (size_t)c0 * nvec * 16);
   u32x4 kv[kPasses];
+  float ks[kPasses];
 #pragma unroll
   for (int u = 0; u < kPasses; ++u) {
     int64_t row = row0 + u * G::RP + slot;
     if (row > n - 1) row = n - 1;
     kv[u] = __builtin_nontemporal_load(kb + row * nvec + subc);
+    if (kScaled) ks[u] = a.kscale[c0 + row];
   }
   __builtin_amdgcn_sched_barrier(0);
   const bool sub_on = sub < nvec;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const bool on = sub_on && h < a.nh;
-    qv[h] = on ? qv[h] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < QV; ++i) qv[h][i] = on ? qv[h][i] : u32x4{0, 0, 0, 0};
     wv[h] = h < a.nh ? wv[h] : 0.f;
   }
   float* sp = score_ptr(a, b, c0);
@@ -404,6 +437,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(Args a) {
 #pragma unroll
       for (int h = 0; h < NH; ++h) s = fmaf(wv[h], fmaxf(group_sum<LPC>(Dot16<ET>::dot(qv[h], kv[u])), 0.f), s);
     }
+    // A key row scale c >= 0 leaves the ReLUs alone: sum_h w_h ReLU(c x_h) = c sum_h w_h ReLU(x_h).
+    if (kScaled) s *= ks[u];
     const bool valid = row < n;
     if (kGather) mine = (sub == u) ? s : mine;
     else if (sub == 0 && valid) sp[row] = s;
@@ -452,6 +487,143 @@ __device__ __forceinline__ void top2c_step(uint32_t& m, uint32_t& c1, uint32_t& 
   m = max(m, om);
   c2 = max(max(c2, o2), min(c1, o1));
   c1 = max(c1, o1);
+}
+
+// Tiles of 16 keys per wave in score_mfma_kernel: 8 KiB of keys, and at least one group.
+constexpr int mfma_tiles(int d, int es) { return 8192 / (16 * d * es) > 2 ? 8192 / (16 * d * es) : 2; }
+
+// K1 as a matrix product, for head_dim D in {64, 128, 256} and up to 16 heads. A wave scores
+// tiles of 16 consecutive keys with v_mfma_f32_16x16x32_bf16: A = the queries (row = head),
+// B = the keys (column = key), one MFMA per 32 channels.
+//   Loads: as in score_kernel, every instruction reads 1 KiB of whole consecutive rows (16
+//   bytes per lane, non-temporal), all issued before the first use.
+//   Each tile then goes through the wave's own LDS tile (rows padded by 16 bytes, so the 16
+//   keys of a fragment read fall in distinct banks) into the B layout: lane (g, c) = (lane / 16,
+//   lane % 16) supplies key c's channels for k-slots 8g .. 8g + 7. The channel order inside
+//   the contraction is free as long as A and B agree:
+//     bf16: MFMA t takes channels 32t + 8g .. + 8;
+//     fp8:  a 16-byte fragment read holds channels 64i + 16g .. + 16, MFMA 2i + h its half h
+//           (converted to bf16, exactly).
+// The result leaves lane (g, c) with the dots of heads 4g .. 4g + 3 against key c; ReLU,
+// weights and (fp8) the row scale follow, summed over the 4 lane rows when there are more
+// than 4 heads. A wave covers TILES tiles (8 KiB of keys; 2 tiles = one group at least).
+template <typename ET, int D, int NH4>
+__global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  constexpr int ES = (int)sizeof(ET);                  // 2: bf16 keys, 1: E4M3 keys
+  constexpr int ROWB = D * ES;                         // bytes per key row
+  constexpr int PITCH = ROWB + 16;                     // LDS row pitch
+  constexpr int T = D / 32;                            // MFMAs per tile
+  constexpr int TILES = mfma_tiles(D, ES);
+  constexpr int LPR = ROWB / 16;                       // lanes per row in a load
+  constexpr int RPI = 64 / LPR;                        // rows per load instruction
+  constexpr int LOADS = TILES * 16 / RPI;              // load instructions per wave
+  constexpr int LPT = 16 / RPI;                        // of them per tile
+  constexpr bool kScaled = ES == 1;
+  static_assert(D % 64 == 0 && TILES % 2 == 0 && RPI >= 1 && 16 % RPI == 0, "shape");
+  __shared__ __attribute__((aligned(16))) unsigned char tile_lds[kThreads / 64][16 * PITCH];
+  const int b = blockIdx.y;
+  int64_t c0;
+  const int64_t n = cand_count(a, b, &c0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const int64_t key0 = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TILES * 16;
+  if (key0 >= n) return;                               // no barriers follow
+  // Queries (A): MFMA t, lane (g, c): head c, the 8 channels this lane supplies.
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.nh + min(c, a.nh - 1)) * D;
+  u32x4 qv[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int ch = ES == 2 ? 32 * t + 8 * g : 64 * (t >> 1) + 16 * g + 8 * (t & 1);
+    qv[t] = *reinterpret_cast<const u32x4*>(qp + ch);
+  }
+  float wv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g + r;
+    wv[r] = a.w[(size_t)b * a.nh + min(h, a.nh - 1)];
+  }
+  __builtin_amdgcn_sched_barrier(0);                   // query loads go out (and return) first
+  const char* kb = static_cast<const char*>(a.keys) + (size_t)c0 * ROWB;
+  const int rr = lane / LPR, sc = lane % LPR;          // this lane's row and 16-byte chunk in a load
+  u32x4 kv[LOADS];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    int64_t row = key0 + u * RPI + rr;
+    if (row > n - 1) row = n - 1;
+    kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + row * ROWB + 16 * sc));
+  }
+  float ks[TILES];
+  if (kScaled) {
+#pragma unroll
+    for (int j = 0; j < TILES; ++j) ks[j] = a.kscale[c0 + min(key0 + 16 * j + c, n - 1)];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const bool qon = c < a.nh;
+#pragma unroll
+  for (int t = 0; t < T; ++t) qv[t] = qon ? qv[t] : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) wv[r] = 4 * g + r < a.nh ? wv[r] : 0.f;
+
+  float* sp = score_ptr(a, b, c0);
+  uint32_t* gmax = maxima_ptr(a, b);
+  uint32_t* gsec = second_ptr(a, b);
+  unsigned char* lt = tile_lds[wave];
+  uint32_t kk[TILES];                                  // the score keys of key c of each tile
+#pragma unroll
+  for (int j = 0; j < TILES; ++j) {
+    // The tile's rows into LDS, then this lane's fragments back out (one wave: LDS operations
+    // stay in program order, so no barrier is needed between them).
+#pragma unroll
+    for (int v = 0; v < LPT; ++v)
+      *reinterpret_cast<u32x4*>(lt + (v * RPI + rr) * PITCH + 16 * sc) = kv[j * LPT + v];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      u32x4 kf;
+      if (ES == 2) {
+        kf = *reinterpret_cast<const u32x4*>(lt + c * PITCH + 64 * t + 16 * g);
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(lt + c * PITCH + 64 * (t >> 1) + 16 * g + 8 * (t & 1));
+        kf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false));
+        kf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true));
+        kf[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false));
+        kf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true));
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qv[t]), __builtin_bit_cast(bf16x8, kf),
+                                                    acc, 0, 0, 0);
+    }
+    float p = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p = fmaf(wv[r], fmaxf(acc[r], 0.f), p);
+    if (NH4 > 1) {                                     // heads 4g .. 4g + 3 live in lane row g
+      p += __shfl_xor(p, 16, 64);
+      p += __shfl_xor(p, 32, 64);
+    }
+    // A key row scale >= 0 leaves the ReLUs alone: sum_h w_h ReLU(c x_h) = c sum_h w_h ReLU(x_h).
+    if (kScaled) p *= ks[j];
+    const int64_t key = key0 + 16 * j + c;
+    const bool valid = key < n;
+    if (g == 0 && valid) sp[key] = p;
+    kk[j] = valid ? score_key(p) : 0u;                 // 0: below every key
+  }
+  // Group statistics: tiles 2q and 2q + 1 form the group; key c of tile 2q + e sits at
+  // position 16e + c. Composite words (key & ~31) | position rank the candidates as in
+  // group_stats4, over the 16 lanes of row 0.
+#pragma unroll
+  for (int q = 0; q < TILES / 2; ++q) {
+    const uint32_t k0 = kk[2 * q], k1 = kk[2 * q + 1];
+    const uint32_t w0 = (k0 & ~31u) | (uint32_t)c, w1 = (k1 & ~31u) | (uint32_t)(16 + c);
+    uint32_t m = max(k0, k1), c1 = max(w0, w1), c2 = min(w0, w1);
+    top2c_step<0xB1>(m, c1, c2);     // xor 1
+    top2c_step<0x4E>(m, c1, c2);     // xor 2
+    top2c_step<0x141>(m, c1, c2);    // half-row mirror
+    top2c_step<0x140>(m, c1, c2);    // row mirror: all 16 lanes of the row
+    if (lane == 0) {
+      const int64_t gi = (key0 + 32 * q) / kGroup;
+      gmax[gi] = m;
+      gsec[gi] = (c2 & ~31u) | (c1 & 31u);
+    }
+  }
 }
 
 // Statistics of the groups of 32 held by a wave as 8 lanes x 4 consecutive scores. Beside
@@ -950,6 +1122,27 @@ __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* top
   collect_seq(a, blockIdx.x, topk, sh);
 }
 
+// The MFMA form of K1 when it applies (up to 16 heads, head_dim 64, 128 or 256): sets a->gs
+// and launches; returns false otherwise.
+template <typename ET>
+bool launch_scores_mfma(int32_t batch, int32_t head_dim, Args* a, hipStream_t s) {
+  if (a->nh > 16 || (head_dim != 64 && head_dim != 128 && head_dim != 256)) return false;
+  const int64_t per_block = 4 * 16 * (int64_t)mfma_tiles(head_dim, (int)sizeof(ET));
+  const dim3 grid((unsigned)((a->max_cand + per_block - 1) / per_block), (unsigned)batch);
+  a->gs = kGroup;
+  const bool wide = a->nh > 4;
+#define CHS_MFMA(DD)                                                                              \
+  if (wide) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 4>), grid, dim3(kThreads), 0, s, *a);   \
+  else hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 1>), grid, dim3(kThreads), 0, s, *a);
+  switch (head_dim) {
+    case 64: CHS_MFMA(64) break;
+    case 128: CHS_MFMA(128) break;
+    default: CHS_MFMA(256) break;
+  }
+#undef CHS_MFMA
+  return true;
+}
+
 template <typename ET, int NH>
 void launch_scores_nh(dim3 grid, hipStream_t s, const Args& a, int lpc) {
   switch (lpc) {
@@ -1010,7 +1203,7 @@ chs_status topk_setup(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t h
   const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
   a->q = q_idx; a->w = w; a->keys = k_idx; a->cu = cu_cand; a->max_cand = max_cand;
-  a->nh = n_heads; a->nvec = nvec; a->k = k; a->scores = scores; a->ws = ws;
+  a->nh = n_heads; a->nvec = nvec; a->k = k; a->scores = scores; a->ws = ws; a->kscale = nullptr;
   a->gs = kGroup;
   return CHS_OK;
 }
@@ -1021,6 +1214,7 @@ chs_status topk_first(chs_dtype dtype, int32_t batch, Args* a, int lpc, hipStrea
   const int64_t max_cand = a->max_cand;
   if (max_cand == 0) return CHS_OK;
   if (a->q) {
+    if (dtype == CHS_BF16 && launch_scores_mfma<uint16_t>(batch, a->nvec * 8, a, s)) return launch_status();
     const int rw = kPasses * (64 / lpc);              // rows per wave
     a->gs = std::min(rw, kGroup);
     const dim3 grid((unsigned)((max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
@@ -1058,6 +1252,40 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
   if (st != CHS_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (topk_first(dtype, batch, &a, lpc, s) != CHS_OK) return CHS_ERR_LAUNCH;
+  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
+  return launch_status();
+}
+
+extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                                         const void* q_idx, const float* w, const void* k_idx,
+                                         const float* k_scale, const int64_t* cu_cand, int64_t max_cand,
+                                         float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  using namespace chs;
+  if (batch < 1 || batch > 65535 || k < 1 || k > kMaxK || max_cand < 0 || max_cand >= (1LL << 31) ||
+      n_heads < 1 || n_heads > 16 || head_dim < 16 || head_dim > 512 || head_dim % 16 != 0)
+    return CHS_ERR_SHAPE;
+  if (max_cand > kMaxCand) return CHS_ERR_UNSUPPORTED;
+  if (!q_idx || !w || !k_idx || !k_scale || !cu_cand || !topk || !workspace) return CHS_ERR_NULL;
+  Workspace ws;
+  const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  Args a;
+  a.q = q_idx; a.w = w; a.keys = k_idx; a.cu = cu_cand; a.max_cand = max_cand;
+  a.nh = n_heads; a.nvec = head_dim / 16; a.k = k; a.scores = scores; a.ws = ws; a.kscale = k_scale;
+  a.gs = kGroup;
+  int lpc = 2;
+  while (lpc < a.nvec) lpc *= 2;                        // one 16-byte key vector per lane
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_cand > 0) {
+    if (!launch_scores_mfma<uint8_t>(batch, head_dim, &a, s)) {
+      const int rw = kPasses * (64 / lpc);
+      a.gs = std::min(rw, kGroup);
+      const dim3 grid((unsigned)((max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
+      launch_scores<uint8_t>(grid, s, a, lpc);
+    }
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  }
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
   return launch_status();
 }

@@ -125,6 +125,29 @@ chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads, int32
                           const int64_t* cu_cand, int64_t max_cand, float* scores, int32_t* topk,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- chs_index_topk_fp8: chs_index_topk with FP8 index keys --------------------------------
+ * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (the checkpoints keep
+ * attention in FP8) and "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 4.3 部署配置建议 (an
+ * fp8 KV cache). The pages fix neither the FP8 variant nor a scale layout; this call takes the
+ * OCP 8-bit E4M3 format (bias 7, exponent 0 subnormal, S.1111.111 NaN, no infinities) with one
+ * fp32 scale per key row:
+ *   key row j = k_scale[j] * decode(k_idx[j, :]),
+ *   scores[cu_cand[b] + j] = sum_h w[b, h] * max(0, sum_t q_idx[b, h, t] * key[cu_cand[b] + j, t])
+ * computed in fp32 (the FP8 values enter the products exactly), then the top-k exactly as
+ * chs_index_topk selects it.
+ * q_idx   : [batch, n_heads, head_dim] bf16.
+ * k_idx   : [cu_cand[batch], head_dim] bytes, E4M3 codes.
+ * k_scale : [cu_cand[batch]] fp32, each >= 0 and finite.
+ * Other arguments as chs_index_topk (scores is an OUTPUT here, or NULL); the workspace is
+ * chs_index_topk_workspace_size(batch, max_cand, k) bytes.
+ * Ranges: 1 <= batch <= 65535; 1 <= k <= 2048; 0 <= max_cand <= 4194304; 1 <= n_heads <= 16;
+ *   16 <= head_dim <= 512, head_dim % 16 == 0. NaN codes are outside the contract. */
+chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                              const void* q_idx, const float* w, const void* k_idx,
+                              const float* k_scale, const int64_t* cu_cand, int64_t max_cand,
+                              float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* ---- chs_decode_attn: one softmax over the window and the compressed entries ------------
  * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", Kernel 層一堆狠活 (window and extra
  * C4/C128 attention in one call) and V4 到底改了啥 (SWA = 128; C4 top-512; C128 dense);

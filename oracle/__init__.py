@@ -33,6 +33,8 @@ def _load():
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_compress.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p, _p, _p, _p, _p]
         lib.oracle_index_scores.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, _p, ctypes.c_int64, _p, _p]
+        lib.oracle_decode_e4m3_n.argtypes = [ctypes.c_int64, _p, _p]
+        lib.oracle_index_scores_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, _p, ctypes.c_int64, _p, _p, _p]
         lib.oracle_topk.argtypes = [_p, ctypes.c_int64, ctypes.c_int32, _p]
         lib.oracle_topk.restype = ctypes.c_int32
         lib.oracle_attend.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, ctypes.c_int64, _p, ctypes.c_double,
@@ -88,6 +90,29 @@ def index_scores(q, w, K) -> np.ndarray:
     assert w.shape == (nh,) and (n == 0 or K.shape[1] == dim)
     s = np.zeros(n, dtype=np.float64)
     _load().oracle_index_scores(nh, dim, _ptr(q), _ptr(w), n, _ptr(K.reshape(max(n, 0), dim)), _ptr(s))
+    return s
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (uint8 array) as doubles; see oracle.c."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().oracle_decode_e4m3_n(c.size, _ptr(c), _ptr(out))
+    return out
+
+
+def index_scores_fp8(q, w, K8, scale) -> np.ndarray:
+    """s_j = sum_h w_h ReLU(q_h . (scale_j * decode(K8_j))) in double. K8: [n, dim] uint8 E4M3
+    codes; scale: [n] fp32."""
+    q, w = _f32(q), _f32(w)
+    K8 = np.ascontiguousarray(K8, dtype=np.uint8)
+    scale = _f32(scale)
+    nh, dim = q.shape
+    n = K8.shape[0]
+    assert w.shape == (nh,) and scale.shape == (n,) and (n == 0 or K8.shape[1] == dim)
+    s = np.zeros(n, dtype=np.float64)
+    _load().oracle_index_scores_fp8(nh, dim, _ptr(q), _ptr(w), n, _ptr(K8.reshape(max(n, 0), dim)), _ptr(scale),
+                                    _ptr(s))
     return s
 
 

@@ -90,6 +90,41 @@ void oracle_index_scores(int32_t nh, int32_t dim, const float* q, const float* w
   }
 }
 
+/* ---- FP8 index keys ([P2] V4 到底改了啥: the checkpoints keep attention in FP8; [P3] 4.3 部署
+ * 配置建议: an fp8 KV cache). The pages fix neither the FP8 variant nor a scale layout;
+ * the reading taken here is the OCP 8-bit E4M3 format with one fp32 scale per key row.
+ * E4M3 byte: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0. Exponent 0 encodes
+ * subnormals m * 2^-9; exponent 15 with mantissa 7 is NaN; there are no infinities. */
+double oracle_decode_e4m3(uint8_t b) {
+  const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+void oracle_decode_e4m3_n(int64_t n, const uint8_t* in, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_decode_e4m3(in[i]);
+}
+
+/* The indexer score with FP8 keys: key row j is scale[j] * decode(K8[j, :]), and
+ *   s_j = sum_h w_h * max(0, sum_t q[h, t] * (scale[j] * decode(K8[j, t]))). */
+void oracle_index_scores_fp8(int32_t nh, int32_t dim, const float* q, const float* w, int64_t n,
+                             const uint8_t* K8, const float* scale, double* s) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < n; ++j) {
+    double acc = 0.0;
+    for (int32_t h = 0; h < nh; ++h) {
+      double dot = 0.0;
+      for (int32_t t = 0; t < dim; ++t)
+        dot += (double)q[(int64_t)h * dim + t] * ((double)scale[j] * oracle_decode_e4m3(K8[j * dim + t]));
+      acc += (double)w[h] * (dot > 0.0 ? dot : 0.0);
+    }
+    s[j] = acc;
+  }
+}
+
 /* ---- Top-k ([P3] 创新 2, Lightning TopK; [P2] Kernel 層一堆狠活) ------------------------
  * The definition a radix select must reproduce, computed by a full sort: order the pairs
  * (s_j, j) by s descending (compared as floats, so -0.0 equals +0.0), then j ascending; keep

@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails va
 def declared():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(chs_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(chs_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_python_exports():
@@ -64,6 +64,25 @@ def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, 
 ])
 def test_index_topk_validation(kw, code):
     assert topk(**kw) == code
+
+
+def topk8(batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, sc=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
+          ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_index_topk_workspace_size(batch, maxc, k)
+    return L.chs_index_topk_fp8(batch, nh, dim, k, q, w, kk, sc, cu, maxc, s, out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), SHAPE), (dict(k=2049), SHAPE), (dict(batch=0), SHAPE), (dict(maxc=-1), SHAPE),
+    (dict(maxc=1 << 31), SHAPE), (dict(nh=0), SHAPE), (dict(nh=17), SHAPE), (dict(dim=8), SHAPE),
+    (dict(dim=24), SHAPE), (dict(dim=528), SHAPE), (dict(maxc=(1 << 22) + 1), UNSUP), (dict(q=None), NULL),
+    (dict(w=None), NULL), (dict(kk=None), NULL), (dict(sc=None), NULL), (dict(cu=None), NULL),
+    (dict(out=None), NULL), (dict(ws=None), NULL), (dict(wsb=16), WS),
+])
+def test_index_topk_fp8_validation(kw, code):
+    assert topk8(**kw) == code
 
 
 def attn(dt=1, batch=1, H=64, d=512, W=128, k=512, scale=0.04, q=FAKE, swa=FAKE, sl=FAKE, comp=FAKE, cu=FAKE,

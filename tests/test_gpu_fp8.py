@@ -1,0 +1,99 @@
+"""chs_index_topk_fp8 (FP8 E4M3 index keys with per-row scales) against the oracle.
+
+Keys are seeded normals (with the index-key spike of the workloads where noted), quantised per
+row on the device: scale = max|k| / 448, code = E4M3(k / scale). That is input preparation, like
+the generator; the oracle then decodes the same codes from the format's definition."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_hybrid_sparse_amd as chs
+import oracle
+from chs_testutil import check_swaps, dev
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+NONNAN = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+
+
+def _quantise(keys):
+    """Per-row E4M3 codes (uint8) and fp32 scales of fp32/bf16 device keys [n, dim]."""
+    k = keys.float()
+    scale = (k.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
+    codes = (k / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.contiguous()
+
+
+def _run(q, w, codes, scale, lens, k):
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64, device=dev())
+    scores = torch.empty(max(int(sum(lens)), 1), dtype=torch.float32, device=dev())[:int(sum(lens))]
+    topk, _ = chs.index_topk_fp8(q, w, codes, scale, cu, k, max(lens) if lens else 0, scores)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), topk.cpu().numpy(), cu.cpu().numpy()
+
+
+@pytest.mark.parametrize("dim", [16, 128, 512])
+def test_fp8_every_code_at_every_byte_is_exact(dim):
+    # Heads e_t and -e_t with weights 1 and 2 read element t alone: s = c d (d > 0) or 2 c |d|,
+    # one fp32 rounding of an exact product, so the GPU must match the oracle bit for bit.
+    print(f"case: fp8 codes, dim {dim}", flush=True)
+    rng = np.random.default_rng(dim)
+    n = 2 * len(NONNAN)
+    K8 = np.stack([np.roll(np.resize(NONNAN, n + dim), r)[:dim] for r in range(n)]).astype(np.uint8)
+    scale = rng.uniform(0.5, 2.0, n).astype(np.float32)
+    codes = torch.from_numpy(K8).to(dev())
+    sc = torch.from_numpy(scale).to(dev())
+    w = torch.tensor([[1.0, 2.0]], dtype=torch.float32, device=dev())
+    for t in sorted({0, 1, 2, 3, 4, 7, 8, 15, dim // 2, dim - 1}):
+        qh = np.zeros((2, dim), np.float32)
+        qh[0, t], qh[1, t] = 1.0, -1.0
+        q = torch.from_numpy(qh).to(dev()).bfloat16().reshape(1, 2, dim)
+        s, _, _ = _run(q, w, codes, sc, [n], 64)
+        want = oracle.index_scores_fp8(qh, np.array([1.0, 2.0], np.float32), K8, scale).astype(np.float32)
+        assert np.array_equal(s, want), f"t={t}: {np.flatnonzero(s != want)[:8]}"
+
+
+@pytest.mark.parametrize("nh,dim,lens,k", [
+    (4, 128, [5000], 512),
+    (4, 128, [1000, 0, 7000, 3], 512),
+    (1, 16, [3000], 64),
+    (16, 64, [2500], 100),
+    (2, 512, [1777], 300),
+    (8, 32, [900, 64], 1000),
+])
+def test_fp8_scores_and_topk_match_oracle(nh, dim, lens, k):
+    print(f"case: fp8 nh={nh} dim={dim} lens={lens} k={k}", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(nh * 1000 + dim)
+    G = int(sum(lens))
+    keys = torch.randn(max(G, 1), dim, generator=g, device=dev())[:G] * 3
+    codes, scale = _quantise(keys)
+    q = torch.randn(len(lens), nh, dim, generator=g, device=dev()).bfloat16()
+    w = torch.rand(len(lens), nh, generator=g, device=dev())
+    s, t, cu = _run(q, w, codes, scale, lens, k)
+    qf, wf, K8, sf = q.float().cpu().numpy(), w.cpu().numpy(), codes.cpu().numpy(), scale.cpu().numpy()
+    for b in range(len(lens)):
+        lo, hi = cu[b], cu[b + 1]
+        ref = oracle.index_scores_fp8(qf[b], wf[b], K8[lo:hi], sf[lo:hi])
+        got = s[lo:hi]
+        if hi > lo:
+            assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max()), f"scores seq {b}"
+        assert np.array_equal(t[b], oracle.topk(got, k)), f"top-k seq {b}"
+        check_swaps(t[b], oracle.topk(ref.astype(np.float32), k), ref, k)
+
+
+def test_fp8_workload4_size():
+    # The 1M-context candidate count with the workload's spiked index keys, quantised.
+    wl = W.workload(4)
+    layer = wl.layers[0]
+    print("case: fp8 keys, 262144 candidates", flush=True)
+    inp = W.device_inputs(wl, layer, dev(), with_tokens=False)
+    codes, scale = _quantise(inp["k_idx"])
+    G = codes.shape[0]
+    s, t, _ = _run(inp["q_idx"], inp["w"], codes, scale, [G], layer.k)
+    ref = oracle.index_scores_fp8(inp["q_idx"].float().cpu().numpy()[0], inp["w"].cpu().numpy()[0],
+                                  codes.cpu().numpy(), scale.cpu().numpy())
+    assert np.all(np.abs(s - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+    assert np.array_equal(t[0], oracle.topk(s, layer.k))
+    swaps = check_swaps(t[0], oracle.topk(ref.astype(np.float32), layer.k), ref, layer.k)
+    print(f"  {swaps} legitimate swaps at the threshold", flush=True)

@@ -210,6 +210,59 @@ def _is_topk_set(s, S):
     return all(s[i] > s[j] or (s[i] == s[j] and i < j) for i in S for j in out)
 
 
+# ---------------------------------------------------------------- FP8 (E4M3) index keys
+def test_decode_e4m3_matches_torch_float8_on_every_code():
+    # An independent decoder: torch's float8_e4m3fn (the same OCP format) on all 256 codes.
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.decode_e4m3(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert list(codes[nan]) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+def test_decode_e4m3_closed_forms():
+    d = oracle.decode_e4m3(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x7E, 0x80, 0x81, 0xB8, 0xFE], np.uint8))
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 448.0, -0.0, -(2.0 ** -9), -1.0, -448.0]
+    assert list(d) == want
+    assert np.signbit(d[7]) and not np.signbit(d[0])
+    # Monotone over the non-negative codes, and a code's negation is its sign bit.
+    pos = oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(oracle.decode_e4m3(np.arange(0x80, 0xFF, dtype=np.uint8)), -pos)
+
+
+def test_index_scores_fp8_one_hot_query_reads_one_code(rng):
+    # q = e_t picks element t of the row: s = w0 relu(c d) + w1 relu(-c d) = c d (d > 0) or 2 c |d|.
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes != 0x7F) & (codes != 0xFF)]
+    dim = 16
+    K8 = np.resize(codes, (len(codes) // dim + 1) * dim).reshape(-1, dim)
+    scale = rng.uniform(0.5, 2.0, K8.shape[0]).astype(np.float32)
+    for t in (0, 5, 15):
+        q = np.zeros((2, dim), np.float32)
+        q[0, t], q[1, t] = 1.0, -1.0
+        s = oracle.index_scores_fp8(q, np.array([1.0, 2.0], np.float32), K8, scale)
+        d = oracle.decode_e4m3(K8[:, t]) * scale.astype(np.float64)
+        assert np.array_equal(s, np.where(d > 0, d, -2.0 * d))
+
+
+def test_index_scores_fp8_equals_scores_of_the_decoded_keys(rng):
+    # With scale 1 (and power-of-two scales, exact in fp32) the FP8 keys are just fp32 keys.
+    import torch
+    q = rng.standard_normal((4, 32)).astype(np.float32)
+    w = rng.uniform(0, 1, 4).astype(np.float32)
+    K8 = rng.integers(0, 256, (300, 32)).astype(np.uint8)
+    K8[(K8 == 0x7F) | (K8 == 0xFF)] = 0x38
+    dec = torch.from_numpy(K8.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    for c in (1.0, 0.25, 8.0):
+        scale = np.full(300, c, np.float32)
+        assert np.allclose(oracle.index_scores_fp8(q, w, K8, scale), oracle.index_scores(q, w, dec * c),
+                           rtol=1e-12, atol=0)
+
+
 def test_topk_exhaustive_tiny(rng):
     values = np.array([-1.0, -0.0, 0.0, 2.0, 3.5], np.float32)
     for n in range(1, 7):
