@@ -13,14 +13,17 @@
 // back-to-back kernels in a graph hand off for free. So no kernel here synchronises
 // workgroups with each other, and a call is two kernels:
 //
-//   K1 score_kernel streams the index keys once. LPC lanes (16 for 128 bf16 channels) share a
-//      key row, one 16-byte non-temporal load each, so every wave load instruction reads one
-//      contiguous 1 KiB; v_dot2_f32_bf16 (or fp32 FMAs) and DPP sums form the head dots. Each
-//      wave owns a run of consecutive rows and issues all of its loads before the first use
-//      (the loads are unconditional, with clamped addresses, so the compiler can count them).
-//      It writes the fp32 scores and, for every group of GS consecutive candidates (GS = 32; 16
-//      or 8 for very wide keys), the group's largest key, the position of that maximum and
-//      its second-largest key. max_kernel does the same for caller-provided scores.
+//   K1 streams the index keys once, every load instruction reading 1 KiB of whole rows (16
+//      bytes per lane, non-temporal), all of a wave's loads issued before the first use
+//      (unconditional, with clamped addresses, so the compiler can count them). For up to 16
+//      heads and head_dim 64, 128 or 256 (bf16 keys, or FP8 E4M3 keys with per-row scales,
+//      converted to bf16 exactly) score_mfma_kernel computes the head dots as 16x16x32 bf16
+//      MFMAs over 16-key tiles, each tile passing through the wave's LDS tile into the MFMA
+//      layout; other shapes take score_kernel, where LPC lanes (16 for 128 bf16 channels)
+//      share a key row and v_dot2_f32_bf16 (or fp32 FMAs) and DPP sums form the dots. Both
+//      write the fp32 scores and, for every group of GS consecutive candidates (GS = 32; 16 or
+//      8 for very wide keys in score_kernel), the group's largest key, the position of that
+//      maximum and its second-largest key. max_kernel does the same for caller-provided scores.
 //   K2 collect_kernel, one 1024-thread workgroup per sequence (one CU, 4 waves per SIMD, so
 //      the instructions it issues per candidate are what costs: it touches group statistics,
 //      not scores, wherever it can):
