@@ -15,9 +15,10 @@ The headline value is the decode attention-layer latency (index_topk + decode_at
 microseconds per step: decode steps run back to back, replayed from a HIP graph (the
 stream-launched figure is reported beside it), median over repetitions. The line also reports the compressor's
 bandwidth, the standalone top-512-of-262144 latency (one row) and the fraction of the HBM
-roofline on a 64-row batch, the same decode step with FP8 (E4M3) index keys and per-row scales
-(chs_index_topk_fp8; a component, not the headline), plus the roofline of the dominant kernel
-and the CPU oracle timed on this host (a reported baseline, not a target).
+roofline on a 64-row batch, the same decode step over FP8 (E4M3) index keys and KV cache with
+per-row scales (chs_index_topk_fp8 + chs_decode_attn_fp8; a component, not the headline), plus
+the roofline of the dominant kernel and the CPU oracle timed on this host (a reported baseline,
+not a target).
 
 Cache defeat: the index keys (64 MiB) rotate over 8 device copies (512 MiB, above the 256 MB
 Infinity Cache); the standalone top-k rows rotate over 256 copies (bs=1) and 8 copies (64 rows).
@@ -231,21 +232,25 @@ def main():
 
     graph_ms = graph_loop_ms(decode, nk)
 
-    # The same step with FP8 (E4M3) index keys and per-row scales (chs_index_topk_fp8), which
-    # halves the key read. The keys are quantised per row on the device (input preparation):
-    # scale = max|k| / 448, code = E4M3(k / scale); 16 copies (528 MiB) defeat the cache.
+    # The same step over FP8 (E4M3) storage with per-row scales: index keys
+    # (chs_index_topk_fp8, which halves the key read) and the KV cache (chs_decode_attn_fp8).
+    # Rows are quantised per row on the device (input preparation): scale = max|x| / 448,
+    # code = E4M3(x / scale); 16 copies of the keys (528 MiB) defeat the cache.
     def quantise(kb):
         kf = kb.float()
         sc = (kf.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
         return (kf / sc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc.contiguous()
 
     fp8 = [quantise(keys[i % nk]) for i in range(2 * nk)]
+    comp8, comp8_s = quantise(comp)
+    swa8, swa8_s = quantise(inp["swa_kv"].reshape(-1, d))
+    swa8, swa8_s = swa8.reshape(1, -1, d), swa8_s.reshape(1, -1)
 
     def decode_fp8(i):
         codes, sc = fp8[i % len(fp8)]
         chs.index_topk_fp8(inp["q_idx"], inp["w"], codes, sc, inp["cu_groups"], k, G, scores, ws_topk, topk)
-        chs.decode_attn(inp["q"], inp["swa_kv"], inp["swa_len"], comp, inp["cu_groups"], topk, scale, G,
-                        ws_attn, out, lse)
+        chs.decode_attn_fp8(inp["q"], swa8, swa8_s, inp["swa_len"], comp8, comp8_s, inp["cu_groups"], topk, scale, G,
+                            ws_attn, out, lse)
 
     for i in range(len(fp8)):
         decode_fp8(i)
@@ -302,7 +307,9 @@ def main():
     comp_bytes = 2 * n * d * e + layer.m * d * 4 + G * d * e
     step_bytes = (G * wl.idx_dim * e + wl.idx_heads * wl.idx_dim * e + wl.idx_heads * 4 + k * 4
                   + (k + wl.window) * d * e + H * d * e + H * d * 4 + H * 4)
-    step_fp8_bytes = step_bytes - G * wl.idx_dim * e + G * wl.idx_dim + G * 4   # 1-byte keys + fp32 row scales
+    # FP8: 1-byte index keys and KV rows, each row with an fp32 scale.
+    step_fp8_bytes = (step_bytes - G * wl.idx_dim * e + G * wl.idx_dim + G * 4
+                      - (k + wl.window) * d * e + (k + wl.window) * (d + 4))
     topk_row_bytes = G * 4 + 512 * 4
     c_us = median(comp_ms) * 1e3
     dec_stream_us = median(dec_ms) * 1e3
@@ -339,8 +346,8 @@ def main():
                                "decode_attn_us": round(median(attn_ms) * 1e3, 2),
                                "algorithmic_bytes": step_bytes,
                                "hbm_frac": round(step_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4)},
-            "decode_step_fp8_keys_us": {
-                "value_source": "graph replay", "call": "chs_index_topk_fp8 + chs_decode_attn",
+            "decode_step_fp8_us": {
+                "value_source": "graph replay", "call": "chs_index_topk_fp8 + chs_decode_attn_fp8",
                 "graph_median": None if fp8_graph_ms is None else round(median(fp8_graph_ms) * 1e3, 2),
                 "algorithmic_bytes": step_fp8_bytes,
                 "hbm_frac": None if fp8_graph_ms is None else

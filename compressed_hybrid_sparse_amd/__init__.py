@@ -20,7 +20,7 @@ _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE
            4: "CHS_ERR_WORKSPACE", 5: "CHS_ERR_UNSUPPORTED", 6: "CHS_ERR_LAUNCH"}
 EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
-           "chs_decode_attn", "chs_index_topk_fp8")
+           "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -54,7 +54,10 @@ def lib():
         L.chs_decode_attn.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _p, _p,
                                       _i64, _p, _p, _p, _sz, _p]
         L.chs_index_topk_fp8.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _p]
-        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8"):
+        L.chs_decode_attn_fp8.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p,
+                                          _p, _p, _sz, _p]
+        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
+                   "chs_decode_attn_fp8"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -238,3 +241,42 @@ def index_topk_fp8(q_idx, w, k_codes, k_scale, cu_cand, k: int, max_cand=None, s
                                     workspace.numel(), _stream()),
            "chs_index_topk_fp8")
     return out, scores
+
+
+def decode_attn_fp8(q, swa_codes, swa_scale, swa_len, comp_codes, comp_scale, cu_comp, topk=None, scale=None,
+                    max_comp=None, workspace=None, out=None, lse=None):
+    """decode_attn over an FP8 E4M3 KV cache with per-row scales (chs_decode_attn_fp8).
+    q: [B, H, d] bf16; swa_codes: [B, W, d] uint8 (or float8_e4m3fn); swa_scale: [B, W] fp32;
+    swa_len: [B] int32; comp_codes: [G, d]; comp_scale: [G] fp32; cu_comp: [B+1] int64;
+    topk: [B, k] int32 or None. Returns (out [B, H, d] fp32, lse [B, H] fp32)."""
+    _need(q, "q", torch.bfloat16, 3)
+    swa_codes = swa_codes.view(torch.uint8) if swa_codes.dtype != torch.uint8 else swa_codes
+    comp_codes = comp_codes.view(torch.uint8) if comp_codes.dtype != torch.uint8 else comp_codes
+    _need(swa_codes, "swa_codes", torch.uint8, 3)
+    _need(swa_scale, "swa_scale", torch.float32, 2)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_codes, "comp_codes", torch.uint8, 2)
+    _need(comp_scale, "comp_scale", torch.float32, 1)
+    _need(cu_comp, "cu_comp", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_codes.shape[1]
+    k = 0
+    if topk is not None:
+        _need(topk, "topk", torch.int32, 2)
+        k = topk.shape[1]
+    if max_comp is None:
+        max_comp = _host_max_diff(cu_comp)
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = decode_attn_workspace(torch.bfloat16, B, H, d, W, k, max_comp, q.device)
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _check(lib().chs_decode_attn_fp8(B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_codes), _ptr(swa_scale),
+                                     _ptr(swa_len), _ptr(comp_codes), _ptr(comp_scale), _ptr(cu_comp), _ptr(topk),
+                                     int(max_comp), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                     _stream()),
+           "chs_decode_attn_fp8")
+    return out, lse

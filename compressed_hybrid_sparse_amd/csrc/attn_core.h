@@ -4,6 +4,8 @@
 // in decode_attn.hip.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace chs {
@@ -36,6 +38,8 @@ struct AttnArgs {
   int32_t head_tiles;       // ceil(H / 64) for bf16, H for fp32
   float* part_o;            // per (sequence, split): see the layout note below
   float* part_ml;           // [batch][n_splits][H][2]: running max (base 2), running sum
+  const float* swa_scale;   // FP8 storage: [batch][W] row scales of swa (else unused)
+  const float* comp_scale;  // FP8 storage: [*] row scales of comp (else unused)
 };
 
 constexpr int kCombineSplits = 512;   // most splits one call may use
@@ -95,15 +99,15 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 // Source rows of a 32-slot chunk starting at slot s0 for a workgroup of NW waves: load i of
 // wave w is wave-wide load li = i * NW + w of the chunk (none if li >= 32 / RPI), covering slot
-// s0 + li * RPI + lr (null: no key there). Branch-free: the top-k entry is read at a clamped
-// position whether or not the slot needs it, so the reads issue back to back. At d = 512
-// (RPI = 1) every operand is the same for the whole wave.
-template <int D, int LOADS, int RPI, int NW>
+// s0 + li * RPI + lr (null: no key there); with FP8 storage also the row's scale. Branch-free:
+// the top-k entry is read at a clamped position whether or not the slot needs it, so the reads
+// issue back to back. When a load is one whole row every operand is the same for the whole wave.
+template <int D, int LOADS, int RPI, int NW, typename ET>
 __device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm, int b, int32_t s0, int32_t s_end,
-                                           int wave, int lr, const uint16_t* (&rp)[LOADS]) {
+                                           int wave, int lr, const ET* (&rp)[LOADS], const float* (&rs)[LOADS]) {
   constexpr int NLOADS = kKeysPerChunk / RPI;
-  const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
-  const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
+  const ET* swa = static_cast<const ET*>(a.swa);
+  const ET* comp = static_cast<const ET*>(a.comp);
   int32_t idx[LOADS];
   if (a.topk != nullptr && a.k > 0) {
     const int32_t* tk = a.topk + (int64_t)b * a.k;
@@ -118,8 +122,10 @@ __device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm,
     const int32_t s = s0 + (i * NW + wave) * RPI + lr;
     const bool in_swa = s < sm.nswa;
     const bool ok = i * NW + wave < NLOADS && s < s_end && (in_swa || (idx[i] >= 0 && idx[i] < sm.G));
-    const uint16_t* p = in_swa ? swa + ((int64_t)b * a.W + s) * D : comp + (sm.comp0 + idx[i]) * D;
+    const int64_t row = in_swa ? (int64_t)b * a.W + s : sm.comp0 + idx[i];
+    const ET* p = (in_swa ? swa : comp) + row * D;
     rp[i] = ok ? p : nullptr;
+    if (sizeof(ET) == 1) rs[i] = ok ? (in_swa ? a.swa_scale : a.comp_scale) + row : nullptr;
   }
 }
 
@@ -131,6 +137,7 @@ struct alignas(16) AttnShared {
   uint16_t pb[4 * TILES][16 * (kKeysPerChunk + 8)];
   f32x4 spart[D >= 128 ? TILES : 1][4][2][64];
   int32_t rowok[kKeysPerChunk];
+  float rowsc[kKeysPerChunk];          // FP8 storage: the chunk's row scales
 };
 
 struct NoHook {
@@ -144,14 +151,16 @@ struct NoHook {
 // through LDS in a fixed order, so all four waves hold bit-identical logits and run the same
 // softmax; and computes P.V for its quarter. before_rows(s0) runs, uniformly over the
 // workgroup, before the rows of the chunk at slot s0 are looked up.
-template <int D, int TILES, typename Hook>
+template <int D, int TILES, typename Hook, bool FP8 = false>
 __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, int z0, int tid,
                                            AttnShared<D, TILES>& sh, Hook& before_rows) {
   constexpr int KC = kKeysPerChunk;
   constexpr int KN_PITCH = D + 8;          // bf16 elements per row-major LDS row
   constexpr int P_PITCH = KC + 8;
   constexpr int NW = 4 * TILES;            // waves
-  constexpr int VPR = D / 8;               // 16-byte vectors per row
+  typedef typename std::conditional<FP8, uint8_t, uint16_t>::type ET;   // storage element
+  constexpr int EPV = 16 / (int)sizeof(ET);    // elements per 16-byte vector
+  constexpr int VPR = D / EPV;             // 16-byte vectors per row
   constexpr int RPI = 64 / VPR;            // rows one wave-wide load covers (1 at d = 512)
   constexpr int NLOADS = KC / RPI;         // wave-wide loads per chunk
   constexpr int LOADS = (NLOADS + NW - 1) / NW;   // per wave
@@ -170,11 +179,12 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
   const int32_t s_begin = split * a.kps;
   const int32_t s_end = min(s_begin + a.kps, sm.nslots());
 
-  // Source row of load i of the first chunk (null: no key). These index reads go out before
-  // the Q loads, so waiting for them does not wait for Q as well.
-  const uint16_t* rp[LOADS];
+  // Source row (and FP8 row scale) of load i of the first chunk (null: no key). These index
+  // reads go out before the Q loads, so waiting for them does not wait for Q as well.
+  const ET* rp[LOADS];
+  const float* rs[LOADS];
   before_rows(s_begin);
-  chunk_rows<D, LOADS, RPI, NW>(a, sm, b, s_begin, s_end, wave, lr, rp);
+  chunk_rows<D, LOADS, RPI, NW, ET>(a, sm, b, s_begin, s_end, wave, lr, rp, rs);
 
   // Q fragment (A operand): row c of the tile's 16 heads, d = d0 + 32t + 8g .. +8 (d0 = this
   // wave's quarter); head index clamped, then zeroed, so the loads are unconditional.
@@ -199,22 +209,41 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
   for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) {
     // 1. gather the chunk's rows (coalesced 16-byte loads) into a row-major LDS tile.
     u32x4 v[LOADS];
+    float vs[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      v[i] = rp[i] ? *reinterpret_cast<const u32x4*>(rp[i] + 8 * cv) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < LOADS; ++i) {
+      v[i] = rp[i] ? *reinterpret_cast<const u32x4*>(rp[i] + EPV * cv) : u32x4{0, 0, 0, 0};
+      if (FP8) vs[i] = rp[i] ? *rs[i] : 0.f;
+    }
     __syncthreads();   // the previous chunk's LDS reads are done
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int li = i * NW + wave;
       if (li < NLOADS) {
         const int r = li * RPI + lr;
-        *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 8 * cv]) = v[i];
+        if (FP8) {
+          // 16 E4M3 codes become 16 bf16 values, exactly (scale 1); the row scale is applied
+          // to the logits and to P below.
+          u32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = v[i][e];
+            const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+            if (e < 2) { lo[2 * e] = p0; lo[2 * e + 1] = p1; } else { hi[2 * e - 4] = p0; hi[2 * e - 3] = p1; }
+          }
+          *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 16 * cv]) = lo;
+          *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 16 * cv + 8]) = hi;
+          if (cv == 0) sh.rowsc[r] = vs[i];
+        } else {
+          *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 8 * cv]) = v[i];
+        }
         if (cv == 0) sh.rowok[r] = rp[i] != nullptr;
       }
     }
     if (s0 + KC < s_end) {
       before_rows(s0 + KC);
-      chunk_rows<D, LOADS, RPI, NW>(a, sm, b, s0 + KC, s_end, wave, lr, rp);
+      chunk_rows<D, LOADS, RPI, NW, ET>(a, sm, b, s0 + KC, s_end, wave, lr, rp, rs);
     }
     __syncthreads();
     // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
@@ -245,8 +274,13 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
         sacc[n] = t;
       }
     }
-    // 3. online softmax (base-2), per head row 4g + r.
+    // 3. online softmax (base-2), per head row 4g + r; FP8 rows scale their logits.
     const bool valid0 = sh.rowok[c] != 0, valid1 = sh.rowok[16 + c] != 0;
+    const float rsc0 = FP8 ? sh.rowsc[c] : 1.f, rsc1 = FP8 ? sh.rowsc[16 + c] : 1.f;
+    if (FP8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { sacc[0][r] *= rsc0; sacc[1][r] *= rsc1; }
+    }
     float p[2][4], alpha[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -268,13 +302,15 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
       for (int r = 0; r < 4; ++r) o[j][r] *= alpha[r];
     }
     // 4. P to this wave's LDS slice as [head][key], read back as the A operand (row c, keys
-    // 8g .. 8g+7).
+    // 8g .. 8g+7). An FP8 row's scale multiplies its weight here (the values are its codes).
     uint16_t* pw = sh.pb[wave];
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        pw[(4 * g + r) * P_PITCH + 16 * n + c] = (uint16_t)(__float_as_uint(p[n][r]) >> 16);
+      for (int r = 0; r < 4; ++r) {
+        const float pv = FP8 ? p[n][r] * (n ? rsc1 : rsc0) : p[n][r];
+        pw[(4 * g + r) * P_PITCH + 16 * n + c] = FP8 ? (uint16_t)f32_to_bf16(pv) : (uint16_t)(__float_as_uint(pv) >> 16);
+      }
     __syncthreads();
     const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pw[c * P_PITCH + 8 * g]));
     // B operand of P.V: column 16j + c of the tile, keys 8g .. 8g+7. ds_read_b64_tr_b16 gives

@@ -43,6 +43,14 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   attn_split<D, 1>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
 }
 
+// The same with FP8 E4M3 storage and per-row scales.
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_fp8_kernel(AttnArgs a) {
+  __shared__ AttnShared<D, 1> sh;
+  NoHook none;
+  attn_split<D, 1, NoHook, true>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
+}
+
 // ---------------------------------------------------------------- fp32 VALU split kernel
 // One workgroup per (split, sequence, head). Chunks of 256 key slots: one thread per key for
 // the logits, then one thread per channel for the weighted sum.
@@ -197,6 +205,7 @@ extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_
   SplitPlan p = plan_splits(dtype, batch, n_heads, window, kk, max_comp);
   AttnArgs a;
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
+  a.swa_scale = nullptr; a.comp_scale = nullptr;
   a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
   a.n_splits = p.n_splits; a.kps = p.kps;
@@ -225,5 +234,45 @@ extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_
   } else {
     hipLaunchKernelGGL(combine_rows_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
   }
+  return launch_status();
+}
+
+extern "C" chs_status chs_decode_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                          float scale, const void* q, const void* swa_kv, const float* swa_scale,
+                                          const int32_t* swa_len, const void* comp_kv, const float* comp_scale,
+                                          const int64_t* cu_comp, const int32_t* topk, int64_t max_comp,
+                                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  using namespace chs;
+  const chs_status st = attn::check_args(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv,
+                                         cu_comp, topk, max_comp, out);
+  if (st != CHS_OK) return st;
+  if (!workspace) return CHS_ERR_NULL;
+  if (window > 0 && !swa_scale) return CHS_ERR_NULL;
+  if (!comp_scale && (topk ? k > 0 : max_comp > 0)) return CHS_ERR_NULL;
+  const int kk = topk ? k : 0;
+  SplitPlan p = plan_splits(CHS_BF16, batch, n_heads, window, kk, max_comp);
+  AttnArgs a;
+  a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
+  a.swa_scale = swa_scale; a.comp_scale = comp_scale;
+  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
+  a.scale_log2 = scale * kLog2e;
+  a.n_splits = p.n_splits; a.kps = p.kps;
+  a.head_tiles = (n_heads + 63) / 64;
+  const size_t need = ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
+  switch (d) {
+    case 64: hipLaunchKernelGGL(attn_fp8_kernel<64>, grid, dim3(kThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(attn_fp8_kernel<128>, grid, dim3(kThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(attn_fp8_kernel<256>, grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(attn_fp8_kernel<512>, grid, dim3(kThreads), 0, s, a); break;
+  }
+  if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  const int words_per_block = kThreads / kCombineLanes;
+  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
+                   (unsigned)batch);
+  hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(kThreads), 0, s, a, out, lse);
   return launch_status();
 }

@@ -181,6 +181,24 @@ chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int3
                            float* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- chs_decode_attn_fp8: chs_decode_attn over an FP8 KV cache ------------------------------
+ * Source: as chs_decode_attn, with "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 4.3 部署配置
+ * 建议 (an fp8 KV cache) and "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (attention
+ * kept in FP8). Reading taken (the pages fix no format): window rows and compressed entries are
+ * OCP E4M3 codes with one fp32 scale per row, row = scale * decode(codes); the query is bf16.
+ * Computes chs_decode_attn's outputs for those rows (keys doubling as values).
+ * q        : [batch, n_heads, d] bf16.
+ * swa_kv   : [batch, window, d] E4M3 codes; swa_scale: [batch, window] fp32 (>= 0, finite).
+ * comp_kv  : [cu_comp[batch], d] E4M3 codes; comp_scale: [cu_comp[batch]] fp32 (>= 0, finite).
+ * Other arguments, ranges and the workspace as chs_decode_attn with dtype CHS_BF16
+ * (chs_decode_attn_workspace_size(CHS_BF16, ...)). NaN codes are outside the contract. */
+chs_status chs_decode_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                               float scale, const void* q, const void* swa_kv, const float* swa_scale,
+                               const int32_t* swa_len, const void* comp_kv, const float* comp_scale,
+                               const int64_t* cu_comp, const int32_t* topk, int64_t max_comp,
+                               float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

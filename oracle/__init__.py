@@ -35,6 +35,8 @@ def _load():
         lib.oracle_index_scores.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, _p, ctypes.c_int64, _p, _p]
         lib.oracle_decode_e4m3_n.argtypes = [ctypes.c_int64, _p, _p]
         lib.oracle_index_scores_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, _p, ctypes.c_int64, _p, _p, _p]
+        lib.oracle_attend_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, ctypes.c_int64, _p, _p, ctypes.c_double,
+                                          _p, _p]
         lib.oracle_topk.argtypes = [_p, ctypes.c_int64, ctypes.c_int32, _p]
         lib.oracle_topk.restype = ctypes.c_int32
         lib.oracle_attend.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, ctypes.c_int64, _p, ctypes.c_double,
@@ -135,6 +137,21 @@ def attend(q, keys, scale: float):
     out = np.zeros((H, d), dtype=np.float64)
     lse = np.zeros(H, dtype=np.float64)
     _load().oracle_attend(H, d, _ptr(q), n, _ptr(keys.reshape(max(n, 0), d)), scale, _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def attend_fp8(q, codes, scales, scale: float):
+    """attend() over FP8 key rows: key row i is scales[i] * decode(codes[i]) (exact, in double).
+    q: [H, d]; codes: [n, d] uint8 E4M3; scales: [n] fp32."""
+    q = _f32(q)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = _f32(scales)
+    H, d = q.shape
+    n = codes.shape[0]
+    out = np.zeros((H, d), dtype=np.float64)
+    lse = np.zeros(H, dtype=np.float64)
+    _load().oracle_attend_fp8(H, d, _ptr(q), n, _ptr(codes.reshape(max(n, 0), d)), _ptr(scales), scale, _ptr(out),
+                              _ptr(lse))
     return out, lse
 
 

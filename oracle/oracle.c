@@ -166,15 +166,15 @@ int32_t oracle_topk(const float* s, int64_t n, int32_t k, int32_t* out) {
  *   lse_h = log sum_i exp(l_i)            (computed as max + log sum exp(l_i - max))
  *   out[h, c] = sum_i exp(l_i - lse_h) * keys[i, c]
  * With no keys, out = 0 and lse = -inf. */
-void oracle_attend(int32_t H, int32_t d, const float* q, int64_t nkeys, const float* keys,
-                   double scale, double* out, double* lse) {
+static void attend_keys(int32_t H, int32_t d, const float* q, int64_t nkeys, const double* keys, double scale,
+                        double* out, double* lse) {
 #pragma omp parallel for schedule(static)
   for (int32_t h = 0; h < H; ++h) {
     double* l = (double*)malloc(sizeof(double) * (size_t)(nkeys > 0 ? nkeys : 1));
     double mx = -INFINITY;
     for (int64_t i = 0; i < nkeys; ++i) {
       double dot = 0.0;
-      for (int32_t c = 0; c < d; ++c) dot += (double)q[(int64_t)h * d + c] * (double)keys[i * d + c];
+      for (int32_t c = 0; c < d; ++c) dot += (double)q[(int64_t)h * d + c] * keys[i * d + c];
       l[i] = scale * dot;
       if (l[i] > mx) mx = l[i];
     }
@@ -184,11 +184,30 @@ void oracle_attend(int32_t H, int32_t d, const float* q, int64_t nkeys, const fl
     lse[h] = ls;
     for (int32_t c = 0; c < d; ++c) {
       double acc = 0.0;
-      for (int64_t i = 0; i < nkeys; ++i) acc += exp(l[i] - ls) * (double)keys[i * d + c];
+      for (int64_t i = 0; i < nkeys; ++i) acc += exp(l[i] - ls) * keys[i * d + c];
       out[(int64_t)h * d + c] = acc;
     }
     free(l);
   }
+}
+
+void oracle_attend(int32_t H, int32_t d, const float* q, int64_t nkeys, const float* keys,
+                   double scale, double* out, double* lse) {
+  double* kd = (double*)malloc(sizeof(double) * (size_t)(nkeys > 0 ? nkeys * d : 1));
+  for (int64_t i = 0; i < nkeys * d; ++i) kd[i] = (double)keys[i];
+  attend_keys(H, d, q, nkeys, kd, scale, out, lse);
+  free(kd);
+}
+
+/* The same attention over FP8 key rows (see the FP8 index keys above): key row i is
+ * scales[i] * decode(codes[i, :]), taken exactly in double. */
+void oracle_attend_fp8(int32_t H, int32_t d, const float* q, int64_t nkeys, const uint8_t* codes,
+                       const float* scales, double scale, double* out, double* lse) {
+  double* kd = (double*)malloc(sizeof(double) * (size_t)(nkeys > 0 ? nkeys * d : 1));
+  for (int64_t i = 0; i < nkeys; ++i)
+    for (int32_t c = 0; c < d; ++c) kd[i * d + c] = (double)scales[i] * oracle_decode_e4m3(codes[i * d + c]);
+  attend_keys(H, d, q, nkeys, kd, scale, out, lse);
+  free(kd);
 }
 
 /* ---- Storage rounding ----------------------------------------------------------------

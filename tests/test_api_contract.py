@@ -106,6 +106,25 @@ def test_decode_attn_validation(kw, code):
     assert attn(**kw) == code
 
 
+def attn8(batch=1, H=64, d=512, W=128, k=512, scale=0.04, q=FAKE, swa=FAKE, ssc=FAKE, sl=FAKE, comp=FAKE, csc=FAKE,
+          cu=FAKE, tk=FAKE, maxc=1000, out=FAKE, lse=FAKE, ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_decode_attn_workspace_size(1, batch, H, d, W, k if tk else 0, maxc)
+    return L.chs_decode_attn_fp8(batch, H, d, W, k, ctypes.c_float(scale), q, swa, ssc, sl, comp, csc, cu, tk, maxc,
+                                 out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(H=129), SHAPE), (dict(d=96), SHAPE), (dict(W=-1), SHAPE), (dict(k=2049), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(q=None), NULL), (dict(swa=None), NULL), (dict(ssc=None), NULL),
+    (dict(sl=None), NULL), (dict(comp=None), NULL), (dict(csc=None), NULL), (dict(cu=None), NULL),
+    (dict(out=None), NULL), (dict(ws=None), NULL), (dict(wsb=8), WS), (dict(W=0, swa=None, ssc=None, wsb=8), WS),
+])
+def test_decode_attn_fp8_validation(kw, code):
+    assert attn8(**kw) == code
+
+
 def test_workspace_sizes_are_monotone():
     L = chs.lib()
     a = [L.chs_index_topk_workspace_size(b, n, 512) for b, n in [(1, 1000), (1, 262144), (4, 262144)]]

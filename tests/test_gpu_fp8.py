@@ -9,7 +9,7 @@ import torch
 
 import compressed_hybrid_sparse_amd as chs
 import oracle
-from chs_testutil import check_swaps, dev
+from chs_testutil import assert_bf16_path, assert_lse, check_swaps, dev
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -97,3 +97,58 @@ def test_fp8_workload4_size():
     assert np.array_equal(t[0], oracle.topk(s, layer.k))
     swaps = check_swaps(t[0], oracle.topk(ref.astype(np.float32), layer.k), ref, layer.k)
     print(f"  {swaps} legitimate swaps at the threshold", flush=True)
+
+
+# ---------------------------------------------------------------- FP8 KV cache (attention)
+def _codes_rows(rng, n, d, spread=1.0):
+    """Seeded rows quantised per row: E4M3 codes (uint8 [n, d]) and fp32 scales [n]. Values are
+    N(0, spread^2), the workloads' range: the bf16-path tolerance allows one bf16 rounding of P,
+    whose effect on the output grows with |V| (about 2^-9 |V| for a dominant key)."""
+    k = torch.from_numpy((rng.standard_normal((max(n, 1), d)) * spread).astype(np.float32))[:n]
+    scale = (k.abs().amax(dim=1) / 448.0).clamp_min(1e-30) if n else torch.zeros(0)
+    codes = (k / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8) if n else torch.zeros(0, d, dtype=torch.uint8)
+    return codes.numpy(), scale.numpy().astype(np.float32)
+
+
+@pytest.mark.parametrize("H,d,W,swa_lens,G_list,k,dense", [
+    (64, 512, 128, [128], [3000], 512, False),
+    (64, 512, 128, [128, 40, 0], [700, 0, 2500], 96, False),
+    (8, 128, 64, [64, 13], [900, 333], 64, False),
+    (100, 256, 128, [77], [1500], 200, False),
+    (16, 64, 32, [32, 32], [400, 1200], 0, True),
+    (64, 512, 128, [128, 128], [2048, 1000], 0, True),
+])
+def test_fp8_attention_matches_oracle(H, d, W, swa_lens, G_list, k, dense):
+    print(f"case: fp8 attention H={H} d={d} W={W} G={G_list} k={k} dense={dense}", flush=True)
+    rng = np.random.default_rng(H * 7 + d + W)
+    B = len(G_list)
+    q = (rng.standard_normal((B, H, d))).astype(np.float32)
+    qb = torch.from_numpy(q).bfloat16()
+    qf = qb.float().numpy()
+    swa_c, swa_s = _codes_rows(rng, B * W, d)
+    swa_c, swa_s = swa_c.reshape(B, W, d), swa_s.reshape(B, W)
+    comp_c, comp_s = _codes_rows(rng, sum(G_list), d)
+    cu = np.concatenate([[0], np.cumsum(G_list)]).astype(np.int64)
+    topk = None
+    if not dense:
+        topk = np.full((B, k), -1, np.int32)
+        for b, G in enumerate(G_list):
+            sel = rng.integers(0, max(G, 1), k) if G else np.full(k, -1)
+            bad = rng.choice(k, min(5, k), replace=False)
+            sel[bad] = rng.choice([-1, -7, G, G + 9], len(bad))
+            topk[b] = sel
+    t = lambda x, dt=None: torch.from_numpy(np.ascontiguousarray(x)).to(dev()) if dt is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev(), dt)
+    comp_dev = t(comp_c) if comp_c.size else torch.zeros(1, d, dtype=torch.uint8, device=dev())
+    comp_s_dev = t(comp_s) if comp_s.size else torch.zeros(1, dtype=torch.float32, device=dev())
+    out, lse = chs.decode_attn_fp8(qb.to(dev()), t(swa_c), t(swa_s), t(np.array(swa_lens, np.int32)), comp_dev,
+                                   comp_s_dev, t(cu), None if dense else t(topk), d ** -0.5, max(G_list))
+    og, lg = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        nswa = min(max(swa_lens[b], 0), W)
+        lo, hi = cu[b], cu[b + 1]
+        rows = list(range(lo, hi)) if dense else [lo + int(j) for j in topk[b] if 0 <= j < hi - lo]
+        codes = np.concatenate([swa_c[b, :nswa], comp_c[rows].reshape(-1, d)])
+        scales = np.concatenate([swa_s[b, :nswa], comp_s[rows]]).astype(np.float32)
+        o_ref, l_ref = oracle.attend_fp8(qf[b], codes, scales, d ** -0.5)
+        assert_bf16_path(og[b], o_ref, f"fp8 attn b={b}")
+        assert_lse(lg[b], l_ref, f"fp8 lse b={b}", 1e-3)

@@ -263,6 +263,28 @@ def test_index_scores_fp8_equals_scores_of_the_decoded_keys(rng):
                            rtol=1e-12, atol=0)
 
 
+def test_attend_fp8_single_key_returns_the_scaled_row(rng):
+    codes = rng.integers(0, 256, (1, 64)).astype(np.uint8)
+    codes[(codes == 0x7F) | (codes == 0xFF)] = 0x40
+    out, lse = oracle.attend_fp8(rng.standard_normal((3, 64)).astype(np.float32), codes, np.array([0.75], np.float32),
+                                 0.125)
+    row = 0.75 * oracle.decode_e4m3(codes[0])
+    assert np.array_equal(out, np.tile(row, (3, 1)))
+    assert np.all(np.isfinite(lse))
+
+
+def test_attend_fp8_equals_attend_of_decoded_keys(rng):
+    import torch
+    codes = rng.integers(0, 256, (40, 32)).astype(np.uint8)
+    codes[(codes == 0x7F) | (codes == 0xFF)] = 0x38
+    dec = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    scales = (2.0 ** rng.integers(-3, 4, 40)).astype(np.float32)
+    q = rng.standard_normal((4, 32)).astype(np.float32)
+    o1, l1 = oracle.attend_fp8(q, codes, scales, 0.2)
+    o2, l2 = oracle.attend(q, dec * scales[:, None], 0.2)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12) and np.allclose(l1, l2, rtol=1e-12, atol=0)
+
+
 def test_topk_exhaustive_tiny(rng):
     values = np.array([-1.0, -0.0, 0.0, 2.0, 3.5], np.float32)
     for n in range(1, 7):
