@@ -180,3 +180,43 @@ def window_rows(X_seq, window: int) -> np.ndarray:
 def decode_step(q, X_seq, window: int, comp_rows, sel, scale: float):
     """Attention of one sequence's decode step (see step_keys and attend)."""
     return attend(q, step_keys(window_rows(X_seq, window), comp_rows, sel), scale)
+
+
+# ---------------------------------------------------------------- per-step append (state ring)
+def ring_image(rows, ring_size: int):
+    """What a ring of `ring_size` row slots holds after the rows of a token history were written
+    to it one token at a time, in order, token t into slot t mod ring_size. Returns (image
+    [ring_size, d] float32, written [ring_size] bool); slots no token reached hold zeros.
+
+    Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", ShadowRadix (the compression state ring sits
+    inside the SWA page: slot address = page * ring size + position mod ring size). Writing tokens
+    before N - ring_size only puts rows that a later token of the same residue overwrites, so the
+    replay starts there."""
+    rows = _f32(rows)
+    N, d = rows.shape
+    img = np.zeros((ring_size, d), np.float32)
+    written = np.zeros(ring_size, bool)
+    for t in range(max(0, N - ring_size), N):
+        img[t % ring_size] = rows[t]
+        written[t % ring_size] = True
+    return img, written
+
+
+def append_state(X_seq, Z_seq, B, m: int, window: int, ring_size: int) -> dict:
+    """The state one sequence's decode-time appends must leave after its history of N tokens
+    (X_seq, Z_seq: [N, d], token rows and gate logits), whatever mix of prefill and one-token
+    appends produced it:
+      swa / swa_written:   the window ring, token t's row at slot t mod window;
+      gate / gate_written: the gate state ring, token t's gate at slot t mod ring_size;
+      comp:                the compressed entries of every complete group (unrounded doubles),
+                           i.e. compress() of the whole history;
+      n, swa_len, comp_count: N, min(N, window) and floor(N / m).
+    Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", ShadowRadix (state rings nested in the SWA
+    pages) and V4 到底改了啥 (window of 128; C4 and C128 groups)."""
+    X_seq, Z_seq = _f32(X_seq), _f32(Z_seq)
+    N = X_seq.shape[0]
+    swa, swa_w = ring_image(X_seq, window)
+    gate, gate_w = ring_image(Z_seq, ring_size)
+    comp = compress(X_seq, Z_seq, B, m, np.array([0, N], np.int64))
+    return dict(swa=swa, swa_written=swa_w, gate=gate, gate_written=gate_w, comp=comp, n=N,
+                swa_len=min(N, window), comp_count=N // m)

@@ -459,6 +459,75 @@ def test_step_c128_reads_every_entry_at_1m():
     assert keys.shape[0] == W + 8192
 
 
+# ------------------------------------------------------------------ per-step append (state ring)
+@pytest.mark.parametrize("R", [1, 3, 4, 8])
+def test_ring_image_closed_form(R):
+    # Token t writes t + 1 into slot t mod R. Slot s < N then holds the last such token:
+    # s + R * floor((N - 1 - s) / R), plus one; slots s >= N were never written.
+    for N in range(0, 3 * R + 3):
+        img, written = oracle.ring_image((np.arange(N, dtype=np.float32) + 1)[:, None], R)
+        for s in range(R):
+            if s < N:
+                assert written[s] and img[s, 0] == s + R * ((N - 1 - s) // R) + 1, (N, R, s)
+            else:
+                assert not written[s] and img[s, 0] == 0, (N, R, s)
+
+
+def test_ring_image_short_history_is_the_history(rng):
+    X = rng.standard_normal((5, 3)).astype(np.float32)
+    img, written = oracle.ring_image(X, 8)
+    assert np.array_equal(img[:5], X) and written.tolist() == [True] * 5 + [False] * 3
+
+
+@pytest.mark.parametrize("N", [0, 1, 50, 127, 128, 129, 300, 1000])
+def test_window_ring_holds_the_step_window(rng, N):
+    # The written slots of the window ring are, as a set of rows, the decode step's window (the
+    # last min(N, W) tokens): attention over a set does not depend on the slot order.
+    X = rng.standard_normal((N, 4)).astype(np.float32)
+    img, written = oracle.ring_image(X, 128)
+    got = img[written]
+    want = oracle.window_rows(X, 128)
+    assert got.shape == want.shape
+    assert np.array_equal(got[np.lexsort(got.T)], want[np.lexsort(want.T)])
+
+
+@pytest.mark.parametrize("m,W", [(4, 128), (128, 128), (3, 10), (8, 8)])
+def test_completed_group_lies_in_the_window_ring(rng, m, W):
+    # When a group completes (N a multiple of m) and m <= W, all of its token rows are still in
+    # the window ring: an append can read the group's rows there.
+    X = rng.standard_normal((5 * W, 2)).astype(np.float32)
+    for N in range(m, 5 * W + 1, m):
+        img, written = oracle.ring_image(X[:N], W)
+        for t in range(N - m, N):
+            assert written[t % W] and np.array_equal(img[t % W], X[t]), (N, t)
+
+
+def test_append_state_counts_and_prefix_stability(rng):
+    # One token more changes one window slot, one gate slot, and adds one compressed entry
+    # exactly when it completes a group; the entries already there do not change (compress is
+    # prefix-stable, the property an append relies on).
+    m, W, R, d = 4, 16, 8, 6
+    X = rng.standard_normal((70, d)).astype(np.float32)
+    Z = rng.standard_normal((70, d)).astype(np.float32) * 2
+    B = rng.standard_normal((m, d)).astype(np.float32) * 0.1
+    prev = oracle.append_state(X[:0], Z[:0], B, m, W, R)
+    assert prev["comp"].shape == (0, d) and prev["n"] == 0 and prev["swa_len"] == 0
+    for N in range(1, 71):
+        cur = oracle.append_state(X[:N], Z[:N], B, m, W, R)
+        assert cur["n"] == N and cur["swa_len"] == min(N, W) and cur["comp_count"] == N // m
+        assert cur["comp"].shape[0] == N // m
+        assert np.array_equal(cur["comp"][:prev["comp"].shape[0]], prev["comp"])
+        diff_w = np.flatnonzero(np.any(cur["swa"] != prev["swa"], axis=1) | (cur["swa_written"] != prev["swa_written"]))
+        diff_g = np.flatnonzero(np.any(cur["gate"] != prev["gate"], axis=1) | (cur["gate_written"] != prev["gate_written"]))
+        assert set(diff_w) <= {(N - 1) % W} and set(diff_g) <= {(N - 1) % R}
+        if N % m == 0:   # the new entry is the pool of the last m tokens alone
+            g = X[N - m:N].astype(np.float64)
+            a = Z[N - m:N].astype(np.float64) + B
+            w = softmax(a, axis=0)
+            np.testing.assert_allclose(cur["comp"][-1], (w * g).sum(0), rtol=1e-12, atol=1e-14)
+        prev = cur
+
+
 # ------------------------------------------------------------------ storage rounding
 def test_round_bf16_matches_integer_rne_of_fp32_values(rng):
     # For doubles that are exactly fp32 values, rounding to bf16 equals the integer RNE on the
