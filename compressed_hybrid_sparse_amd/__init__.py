@@ -4,8 +4,9 @@ Argument marshalling only. Every step of the path runs in the library's HIP kern
 supplies device memory (outputs and workspaces are torch tensors) and the current stream.
 There is no fallback: if libchs.so is missing or a call fails, an exception is raised.
 
-The functions mirror the C ABI in include/chs.h (chs_compress, chs_index_topk,
-chs_decode_attn); see that header for the definitions and the pages they follow.
+The functions mirror the C ABI in include/chs.h (chs_compress, chs_append, chs_index_topk,
+chs_decode_attn and their FP8 forms); see that header for the definitions and the pages they
+follow.
 """
 import ctypes
 import os
@@ -20,7 +21,7 @@ _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE
            4: "CHS_ERR_WORKSPACE", 5: "CHS_ERR_UNSUPPORTED", 6: "CHS_ERR_LAUNCH"}
 EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
-           "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8")
+           "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -56,8 +57,10 @@ def lib():
         L.chs_index_topk_fp8.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _p]
         L.chs_decode_attn_fp8.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p,
                                           _p, _p, _sz, _p]
+        L.chs_append.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p,
+                                 _p, _i64, _p, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
-                   "chs_decode_attn_fp8"):
+                   "chs_decode_attn_fp8", "chs_append"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -131,6 +134,42 @@ def compress(x, gate, bias, m: int, cu_tokens, cu_groups=None, max_groups=None, 
                               _ptr(bias), _ptr(cu_tokens), _ptr(cu_groups), int(max_groups), _ptr(out),
                               _stream()), "chs_compress")
     return out
+
+
+# ---------------------------------------------------------------- chs_append
+def append(x_new, z_new, bias, m: int, n_tokens, swa_kv, gate_ring, ring_page, comp_kv, comp_start,
+           ring_size=None, swa_len=None, comp_count=None):
+    """One decode-time token per sequence (chs_append): writes x_new into the window ring and z_new
+    into the gate state ring, pools a group the token completes into comp_kv, and advances the
+    counters in place.
+    x_new, z_new: [B, d]; bias: [m, d] fp32; n_tokens: [B] int64 (in/out); swa_kv: [B, W, d];
+    gate_ring: [pages * ring_size, d]; ring_page: [B] int32; comp_kv: [rows, d];
+    comp_start: [B] int64; swa_len: [B] int32 or None; comp_count: [B] int64 or None (outputs).
+    ring_size defaults to gate_ring.shape[0] // the number of pages when that is 1 page per
+    sequence; pass it explicitly otherwise."""
+    _need(x_new, "x_new", dim=2)
+    dt = x_new.dtype
+    _need(z_new, "z_new", dt, 2)
+    _need(bias, "bias", torch.float32, 2)
+    _need(n_tokens, "n_tokens", torch.int64, 1)
+    _need(swa_kv, "swa_kv", dt, 3)
+    _need(gate_ring, "gate_ring", dt, 2)
+    _need(ring_page, "ring_page", torch.int32, 1)
+    _need(comp_kv, "comp_kv", dt, 2)
+    _need(comp_start, "comp_start", torch.int64, 1)
+    if swa_len is not None:
+        _need(swa_len, "swa_len", torch.int32, 1)
+    if comp_count is not None:
+        if comp_count.dtype != torch.int64 or not comp_count.is_cuda:
+            raise TypeError("comp_count must be an int64 CUDA tensor")
+    B, d = x_new.shape
+    if ring_size is None:
+        ring_size = gate_ring.shape[0] // B
+    pages = gate_ring.shape[0] // ring_size
+    _check(lib().chs_append(_dtype_code(x_new), B, d, m, swa_kv.shape[1], int(ring_size), _ptr(x_new), _ptr(z_new),
+                            _ptr(bias), _ptr(n_tokens), _ptr(swa_kv), _ptr(swa_len), _ptr(gate_ring),
+                            _ptr(ring_page), pages, _ptr(comp_kv), _ptr(comp_start), comp_kv.shape[0],
+                            _ptr(comp_count), _stream()), "chs_append")
 
 
 # ---------------------------------------------------------------- chs_index_topk

@@ -15,125 +15,10 @@
 // (m <= 8) keep every row in registers and take the max, the exponentials and the weighted sum
 // in one shot; larger groups (C128) stream 8 rows at a time with a running maximum
 // (online softmax), so registers stay bounded for any m.
-#include "common.h"
+#include "pool.h"
 
 namespace chs {
 namespace {
-
-template <typename ET>
-struct Vec16;
-
-template <>
-struct Vec16<uint16_t> {  // 8 bf16 channels
-  static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* v) {
-    u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r[j]); v[2 * j + 1] = bf16_hi(r[j]); }
-  }
-  __device__ static void store(uint16_t* p, const float* v) {
-    u32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-    *reinterpret_cast<u32x4*>(p) = r;
-  }
-};
-
-template <>
-struct Vec16<float> {  // 4 fp32 channels
-  static constexpr int N = 4;
-  __device__ static void load(const float* p, float* v) {
-    f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = r[j];
-  }
-  __device__ static void store(float* p, const float* v) {
-    f32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = v[j];
-    *reinterpret_cast<f32x4*>(p) = r;
-  }
-};
-
-__device__ __forceinline__ void load_bias(const float* p, float* v, int n) {
-#pragma unroll
-  for (int j = 0; j < 8; j += 4) {
-    if (j < n) {
-      f32x4 r = *reinterpret_cast<const f32x4*>(p + j);
-      v[j] = r[0]; v[j + 1] = r[1]; v[j + 2] = r[2]; v[j + 3] = r[3];
-    }
-  }
-}
-
-// One (group, 16-byte channel chunk) item: M > 0 is a compile-time group size (<= 8); M == 0
-// takes any m, streamed in chunks of 8 rows with a running maximum.
-template <typename ET, int M>
-__device__ __forceinline__ void compress_item(int32_t d, int32_t m, const ET* __restrict__ xp,
-                                              const ET* __restrict__ zp, const float* __restrict__ bp,
-                                              ET* __restrict__ op) {
-  using V = Vec16<ET>;
-  constexpr int N = V::N;
-  constexpr int R = M > 0 ? M : 8;
-  float mx[N], sum[N], acc[N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) { mx[j] = -INFINITY; sum[j] = 0.f; acc[j] = 0.f; }
-
-  for (int r0 = 0; r0 < m; r0 += R) {
-    const int nr = (M > 0) ? R : min(R, m - r0);
-    float xv[R][N], av[R][N];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r < nr) {
-        V::load(xp + (int64_t)(r0 + r) * d, xv[r]);
-        V::load(zp + (int64_t)(r0 + r) * d, av[r]);
-      }
-    }
-    float cmax[N];
-#pragma unroll
-    for (int j = 0; j < N; ++j) cmax[j] = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r < nr) {
-        float bv[8];
-        load_bias(bp + (int64_t)(r0 + r) * d, bv, N);
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          av[r][j] = (av[r][j] + bv[j]) * kLog2e;   // logit in base-2 units
-          cmax[j] = fmaxf(cmax[j], av[r][j]);
-        }
-      }
-    }
-    if (M == 0) {
-      // Online softmax: rescale what was accumulated under the previous maximum.
-#pragma unroll
-      for (int j = 0; j < N; ++j) {
-        const float nm = fmaxf(mx[j], cmax[j]);
-        const float sc = fast_exp2(mx[j] - nm);
-        sum[j] *= sc;
-        acc[j] *= sc;
-        mx[j] = nm;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < N; ++j) mx[j] = cmax[j];
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r < nr) {
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const float e = fast_exp2(av[r][j] - mx[j]);
-          sum[j] += e;
-          acc[j] = fmaf(e, xv[r][j], acc[j]);
-        }
-      }
-    }
-  }
-  float o[N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) o[j] = acc[j] / sum[j];
-  V::store(op, o);
-}
 
 // Grid: (x: items of the longest sequence, y: sequence). A launch holds fewer than 2^32
 // work-items per grid dimension, so the x dimension strides over the sequence's items.
@@ -158,8 +43,12 @@ __global__ __launch_bounds__(256) void compress_kernel(int32_t d, int32_t m, con
     const int64_t g = item / cpr;
     const int64_t col = (item - g * cpr) * N;
     const int64_t row = t0 + g * m;
-    compress_item<ET, M>(d, m, x + row * d + col, gate + row * d + col, bias + col,
-                         out + (o0 + g) * d + col);
+    const ET* xp = x + row * d + col;
+    const ET* zp = gate + row * d + col;
+    const float* bp = bias + col;
+    pool_group<ET, M>(
+        m, [&](int r) { return xp + (int64_t)r * d; }, [&](int r) { return zp + (int64_t)r * d; },
+        [&](int r) { return bp + (int64_t)r * d; }, out + (o0 + g) * d + col);
   }
 }
 

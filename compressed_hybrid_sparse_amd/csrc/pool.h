@@ -1,0 +1,173 @@
+// The group softmax-pool of one 16-byte channel chunk, shared by chs_compress (a whole prefill)
+// and chs_append (the group that one decode-time token completes).
+//
+// Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 2 (Flash Compressor: load the
+// tokens and gates, score, softmax, weighted sum and store in one on-chip pass).
+//
+// A chunk is 8 bf16 or 4 fp32 channels. Rows are reached through accessors (row index -> chunk
+// pointer), so the rows of a group need not be contiguous: a prefill walks x + r*d, an append
+// reads a ring. Logits are carried in base-2 units (times log2 e) so the exponentials are
+// single v_exp_f32 instructions.
+#pragma once
+
+#include "common.h"
+
+namespace chs {
+namespace {
+
+template <typename ET>
+struct Vec16;
+
+template <>
+struct Vec16<uint16_t> {  // 8 bf16 channels
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t* p, float* v) {
+    u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r[j]); v[2 * j + 1] = bf16_hi(r[j]); }
+  }
+  __device__ static void store(uint16_t* p, const float* v) {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+    *reinterpret_cast<u32x4*>(p) = r;
+  }
+  __device__ static void copy(uint16_t* dst, const uint16_t* src) {
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  }
+};
+
+template <>
+struct Vec16<float> {  // 4 fp32 channels
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* v) {
+    f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = r[j];
+  }
+  __device__ static void store(float* p, const float* v) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = v[j];
+    *reinterpret_cast<f32x4*>(p) = r;
+  }
+  __device__ static void copy(float* dst, const float* src) {
+    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
+  }
+};
+
+__device__ __forceinline__ void load_bias(const float* p, float* v, int n) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 4) {
+    if (j < n) {
+      f32x4 r = *reinterpret_cast<const f32x4*>(p + j);
+      v[j] = r[0]; v[j + 1] = r[1]; v[j + 2] = r[2]; v[j + 3] = r[3];
+    }
+  }
+}
+
+// Running state of one chunk's softmax-pool: maximum logit (base 2), sum of exponentials and
+// the weighted sum of rows, all relative to the maximum.
+template <int N>
+struct PoolState {
+  float mx[N], sum[N], acc[N];
+  __device__ void init() {
+#pragma unroll
+    for (int j = 0; j < N; ++j) { mx[j] = -INFINITY; sum[j] = 0.f; acc[j] = 0.f; }
+  }
+  // Folds in another state (the same chunk over other rows).
+  __device__ void merge(const float* omx, const float* osum, const float* oacc) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float nm = fmaxf(mx[j], omx[j]);
+      const float a = fast_exp2(mx[j] - nm), b = fast_exp2(omx[j] - nm);
+      sum[j] = sum[j] * a + osum[j] * b;
+      acc[j] = acc[j] * a + oacc[j] * b;
+      mx[j] = nm;
+    }
+  }
+};
+
+// Folds rows r0 .. r0 + nr - 1 (nr <= R) into the state: the block's maximum first, then the
+// previous sums rescaled to it (skipped when FIRST: the state is fresh), then each row's
+// exponential and weighted contribution in row order. bias(r) is row r's bias chunk.
+template <typename ET, int R, bool FIRST, typename XRow, typename ZRow, typename BRow>
+__device__ __forceinline__ void pool_block(PoolState<Vec16<ET>::N>& st, int r0, int nr, XRow xrow, ZRow zrow,
+                                           BRow brow) {
+  using V = Vec16<ET>;
+  constexpr int N = V::N;
+  float xv[R][N], av[R][N];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < nr) {
+      V::load(xrow(r0 + r), xv[r]);
+      V::load(zrow(r0 + r), av[r]);
+    }
+  }
+  float cmax[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) cmax[j] = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < nr) {
+      float bv[8];
+      load_bias(brow(r0 + r), bv, N);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        av[r][j] = (av[r][j] + bv[j]) * kLog2e;   // logit in base-2 units
+        cmax[j] = fmaxf(cmax[j], av[r][j]);
+      }
+    }
+  }
+  if (FIRST) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) st.mx[j] = cmax[j];
+  } else {
+    // Online softmax: rescale what was accumulated under the previous maximum.
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float nm = fmaxf(st.mx[j], cmax[j]);
+      const float sc = fast_exp2(st.mx[j] - nm);
+      st.sum[j] *= sc;
+      st.acc[j] *= sc;
+      st.mx[j] = nm;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < nr) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float e = fast_exp2(av[r][j] - st.mx[j]);
+        st.sum[j] += e;
+        st.acc[j] = fmaf(e, xv[r][j], st.acc[j]);
+      }
+    }
+  }
+}
+
+template <typename ET>
+__device__ __forceinline__ void pool_store(const PoolState<Vec16<ET>::N>& st, ET* op) {
+  constexpr int N = Vec16<ET>::N;
+  float o[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) o[j] = st.acc[j] / st.sum[j];
+  Vec16<ET>::store(op, o);
+}
+
+// A whole group of m rows: M > 0 is a compile-time group size (<= 8, one block); M == 0 takes
+// any m, streamed in blocks of 8 rows with a running maximum, so registers stay bounded.
+template <typename ET, int M, typename XRow, typename ZRow, typename BRow>
+__device__ __forceinline__ void pool_group(int m, XRow xrow, ZRow zrow, BRow brow, ET* op) {
+  PoolState<Vec16<ET>::N> st;
+  st.init();
+  if (M > 0) {
+    pool_block<ET, (M > 0 ? M : 1), true>(st, 0, M, xrow, zrow, brow);
+  } else {
+    for (int r0 = 0; r0 < m; r0 += 8) pool_block<ET, 8, false>(st, r0, min(8, m - r0), xrow, zrow, brow);
+  }
+  pool_store<ET>(st, op);
+}
+
+}  // namespace
+}  // namespace chs

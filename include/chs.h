@@ -93,6 +93,44 @@ chs_status chs_compress(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, co
                         const void* gate, const float* bias, const int64_t* cu_tokens,
                         const int64_t* cu_groups, int64_t max_groups, void* out, void* stream);
 
+/* ---- chs_append: one decode-time token per sequence into the window and the state ring ----
+ * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", ShadowRadix (a compression state ring per
+ * layer, nested in the sequence's SWA page at page * ring_size + position mod ring_size; 8 slots
+ * for C4, 128 for C128, doubled for speculative decoding) and V4 到底改了啥 (128-token window;
+ * C4 and C128 groups). The pooling is chs_compress's.
+ * For every sequence b, with t = n_tokens[b] tokens before the call (a negative count reads as 0):
+ *   swa_kv[b, t mod window, :]                  = x_new[b, :]
+ *   gate_ring[ring_page[b]*ring_size + t mod ring_size, :] = z_new[b, :]
+ *   if (t + 1) mod m == 0, the group g = t / m (tokens t+1-m .. t) is pooled as chs_compress pools
+ *   it and written to comp_kv[comp_start[b] + g, :]; its earlier token rows are read from
+ *   swa_kv (slot position mod window) and its gates from gate_ring, which therefore must hold
+ *   what earlier appends (or the caller, after a prefill) wrote there;
+ *   n_tokens[b] = t + 1;  swa_len[b] = min(t + 1, window);  comp_count[b] = floor((t + 1) / m).
+ * The window is a ring: after the call its rows [0, swa_len[b]) are exactly the last
+ * min(t + 1, window) tokens, in slot order rather than token order, which chs_decode_attn accepts
+ * (one softmax over a set). For m <= 8 the new entry is bit-identical to chs_compress's.
+ * x_new, z_new : [batch, d] of `dtype`: the new token's row (its KV latent) and gate logits.
+ * bias         : [m, d] fp32, as for chs_compress.
+ * n_tokens     : [batch] int64, read and advanced in place.
+ * swa_kv       : [batch, window, d] of `dtype` (the layout chs_decode_attn reads).
+ * swa_len      : [batch] int32 output, or NULL.
+ * gate_ring    : [ring_pages * ring_size, d] of `dtype`; ring_page: [batch] int32. A page outside
+ *                [0, ring_pages) makes the call skip that sequence's gate write and group.
+ * comp_kv      : [comp_rows, d] of `dtype`; comp_start: [batch] int64, the row of each sequence's
+ *                group 0. A group whose row falls outside [0, comp_rows) is not written.
+ * comp_count   : [batch] int64 output, or NULL. For one sequence stored from row 0, pointing it
+ *                at cu_comp + 1 keeps the cu arrays of chs_index_topk / chs_decode_attn current.
+ * Row pointers must be 16-byte aligned. Sequences must be distinct entries (one token each);
+ * n_tokens must not alias swa_len or comp_count.
+ * Ranges: 1 <= batch <= 2^20; 1 <= m <= 1024; m <= window <= 2^20; m <= ring_size <= 2^20;
+ * ring_pages >= 1; comp_rows >= 0; 1 <= d <= 4096 with d*elem_size % 16 == 0. */
+chs_status chs_append(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
+                      int32_t ring_size, const void* x_new, const void* z_new, const float* bias,
+                      int64_t* n_tokens, void* swa_kv, int32_t* swa_len, void* gate_ring,
+                      const int32_t* ring_page, int64_t ring_pages, void* comp_kv,
+                      const int64_t* comp_start, int64_t comp_rows, int64_t* comp_count,
+                      void* stream);
+
 /* ---- chs_index_topk: indexer scores, then exact top-k by radix select ------------------
  * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 2 (Lightning TopK: per-block
  * radix histograms, a threshold, then each block scatters its entries above it; no global

@@ -47,6 +47,25 @@ def test_compress_validation(kw, code):
     assert compress(**kw) == code
 
 
+def append(dt=1, batch=1, d=512, m=4, W=128, R=8, x=FAKE, z=FAKE, b=FAKE, n=FAKE, swa=FAKE, sl=FAKE, ring=FAKE,
+           page=FAKE, pages=1, comp=FAKE, cs=FAKE, rows=100, cc=FAKE):
+    return chs.lib().chs_append(dt, batch, d, m, W, R, x, z, b, n, swa, sl, ring, page, pages, comp, cs, rows, cc,
+                                None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), DTYPE), (dict(batch=0), SHAPE), (dict(batch=(1 << 20) + 1), SHAPE), (dict(d=0), SHAPE),
+    (dict(d=12), SHAPE), (dict(dt=0, d=6), SHAPE), (dict(d=4104), SHAPE), (dict(m=0), SHAPE), (dict(m=1025), SHAPE),
+    (dict(W=3), SHAPE), (dict(R=3), SHAPE), (dict(m=128, W=127, R=128), SHAPE), (dict(pages=0), SHAPE),
+    (dict(rows=-1), SHAPE), (dict(x=None), NULL), (dict(z=None), NULL), (dict(b=None), NULL), (dict(n=None), NULL),
+    (dict(swa=None), NULL), (dict(ring=None), NULL), (dict(page=None), NULL), (dict(comp=None), NULL),
+    (dict(cs=None), NULL),
+])
+def test_append_validation(kw, code):
+    # swa_len and comp_count are optional outputs; everything else is required.
+    assert append(**kw) == code
+
+
 def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
          ws=FAKE, wsb=None):
     L = chs.lib()
