@@ -16,7 +16,10 @@ microseconds per step: decode steps run back to back, replayed from a HIP graph 
 stream-launched figure is reported beside it), median over repetitions. The line also reports the compressor's
 bandwidth, the standalone top-512-of-262144 latency (one row) and the fraction of the HBM
 roofline on a 64-row batch, the same decode step over FP8 (E4M3) index keys and KV cache with
-per-row scales (chs_index_topk_fp8 + chs_decode_attn_fp8; a component, not the headline), plus
+per-row scales (chs_index_topk_fp8 + chs_decode_attn_fp8; a component, not the headline), the
+full per-token step with chs_append of the new token's KV row and index key (window ring, gate
+state ring, a pooled entry every 4th token) ahead of the top-k and the attention, chs_append
+alone on a 64-sequence batch (C4 and C128), plus
 the roofline of the dominant kernel and the CPU oracle timed on this host (a reported baseline,
 not a target).
 
@@ -255,6 +258,77 @@ def main():
     for i in range(len(fp8)):
         decode_fp8(i)
     fp8_graph_ms = graph_loop_ms(decode_fp8, len(fp8))
+    # The full per-token step: chs_append of the new token's KV row (window ring, gate ring,
+    # pooling every 4th step) and of its index-key row (the indexer's own stream), then the top-k
+    # and the attention over the grown context. The counters advance in place and comp_count
+    # feeds cu (element 1) directly, so the graph replays step after step with no host work. All
+    # four calls are on one stream: putting the KV append on a second stream of the graph (the
+    # pages' multi-stream preparation) measured 53.8 us against 38.6, the cross-stream edges
+    # costing more than the 2-3 us they overlap. The context starts 256 tokens short of 1M
+    # (G0 = G - 64 entries), leaving room for the replays.
+    G0 = G - 64
+    cu_app = torch.tensor([0, G0], dtype=torch.int64, device=dev)
+    n_kv = torch.tensor([G0 * layer.m], dtype=torch.int64, device=dev)
+    n_ix = n_kv.clone()
+    swa_app = inp["swa_kv"].clone()
+    swa_len_app = torch.empty(1, dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev).manual_seed(5)
+    x_tok = torch.randn(1, d, generator=g, device=dev).bfloat16()
+    z_tok = torch.randn(1, d, generator=g, device=dev).bfloat16()
+    ring_kv = torch.randn(8, d, generator=g, device=dev).bfloat16()
+    xi_tok = torch.randn(1, wl.idx_dim, generator=g, device=dev).bfloat16()
+    zi_tok = torch.randn(1, wl.idx_dim, generator=g, device=dev).bfloat16()
+    bias_i = torch.zeros(layer.m, wl.idx_dim, dtype=torch.float32, device=dev)
+    swa_i = torch.randn(1, 8, wl.idx_dim, generator=g, device=dev).bfloat16()
+    ring_i = torch.randn(8, wl.idx_dim, generator=g, device=dev).bfloat16()
+    page0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    start0 = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def decode_append(i):
+        kb = keys[i % nk]
+        chs.append(x_tok, z_tok, inp["bias"], layer.m, n_kv, swa_app, ring_kv, page0, comp, start0, ring_size=8,
+                   swa_len=swa_len_app, comp_count=cu_app[1:])
+        chs.append(xi_tok, zi_tok, bias_i, layer.m, n_ix, swa_i, ring_i, page0, kb, start0, ring_size=8)
+        chs.index_topk(inp["q_idx"], inp["w"], kb, cu_app, k, G, scores, ws_topk, topk)
+        chs.decode_attn(inp["q"], swa_app, swa_len_app, comp, cu_app, topk, scale, G, ws_attn, out, lse)
+
+    app_step_ms = graph_loop_ms(decode_append, nk)
+    app_added = int(n_kv.item()) - G0 * layer.m
+
+    # chs_append alone on a 64-sequence batch (d = 512, bf16), replayed 8 tokens per graph: a C4
+    # layer (groups of 4, ring of 8; a quarter of the sequences complete a group per token) and a
+    # C128 layer (ring of 128; the sequences start at even offsets into a group, so one of them
+    # pools a 128-token group every other token).
+    def append_batch(mm, ring):
+        Bn = 64
+        cap = 4096 // mm + 64
+        st = dict(n=torch.tensor([4096 + (b * mm // Bn) % mm for b in range(Bn)], dtype=torch.int64, device=dev),
+                  swa=torch.randn(Bn, wl.window, d, generator=g, device=dev).bfloat16(),
+                  ring=torch.randn(Bn * ring, d, generator=g, device=dev).bfloat16(),
+                  page=torch.arange(Bn, dtype=torch.int32, device=dev),
+                  comp=torch.empty(Bn * cap, d, dtype=torch.bfloat16, device=dev),
+                  start=torch.arange(0, Bn * cap, cap, dtype=torch.int64, device=dev),
+                  x=torch.randn(Bn, d, generator=g, device=dev).bfloat16(),
+                  z=torch.randn(Bn, d, generator=g, device=dev).bfloat16(),
+                  bias=torch.randn(mm, d, generator=g, device=dev) * 0.1,
+                  sl=torch.empty(Bn, dtype=torch.int32, device=dev),
+                  cc=torch.empty(Bn, dtype=torch.int64, device=dev))
+
+        def one(i):
+            chs.append(st["x"], st["z"], st["bias"], mm, st["n"], st["swa"], st["ring"], st["page"], st["comp"],
+                       st["start"], ring_size=ring, swa_len=st["sl"], comp_count=st["cc"])
+
+        ms = graph_loop_ms(one, 8)
+        # Bytes per token (all 64 sequences): new row and gate read and written once each, and per
+        # completed group its m - 1 earlier rows and gates, the bias and the entry written.
+        per_group = (2 * (mm - 1) * d * e_sz + mm * d * 4 + d * e_sz)
+        completing = Bn / mm
+        return ms, Bn * 4 * d * e_sz + completing * per_group
+
+    e_sz = 2
+    app4_ms, app4_bytes = append_batch(4, 8)
+    app128_ms, app128_bytes = append_batch(128, 128)
+
     # Per-call breakdown (events around each call; each event adds a little to what it brackets).
     bd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -317,8 +391,8 @@ def main():
     dec_us = dec_graph_us if dec_graph_us is not None else dec_stream_us
     t1_us, t64_us = median(t1_ms) * 1e3, median(t64_ms) * 1e3
     comp_gbps = comp_bytes / (c_us * 1e-6) / 1e9
-    kernel_hash = source_hash(os.path.join(ROOT, "compressed_hybrid_sparse_amd", "csrc", "compress.hip"),
-                              os.path.join(ROOT, "compressed_hybrid_sparse_amd", "csrc", "common.h"))
+    kernel_hash = source_hash(*[os.path.join(ROOT, "compressed_hybrid_sparse_amd", "csrc", f)
+                                for f in ("compress.hip", "pool.h", "common.h")])
     result = {
         "metric": METRIC,
         "value": round(dec_us, 2),
@@ -352,6 +426,17 @@ def main():
                 "algorithmic_bytes": step_fp8_bytes,
                 "hbm_frac": None if fp8_graph_ms is None else
                 round(step_fp8_bytes / (median(fp8_graph_ms) * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)},
+            "decode_step_with_append_us": {
+                "value_source": "graph replay",
+                "call": "chs_append (KV) + chs_append (index key) + chs_index_topk + chs_decode_attn",
+                "graph_median": None if app_step_ms is None else round(median(app_step_ms) * 1e3, 2),
+                "tokens_appended": app_added},
+            "append_us": {
+                "value_source": "graph replay", "batch": 64, "d": d,
+                "c4_median": None if app4_ms is None else round(median(app4_ms) * 1e3, 2),
+                "c4_algorithmic_bytes": int(app4_bytes),
+                "c128_median": None if app128_ms is None else round(median(app128_ms) * 1e3, 2),
+                "c128_algorithmic_bytes": int(app128_bytes)},
             "topk_512_of_262144_us": {"bs1_median": round(t1_us, 2), "bs1_p90": round(pct(t1_ms, 0.9) * 1e3, 2),
                                       "rows64_median": round(t64_us, 2),
                                       "rows64_hbm_frac": round(64 * topk_row_bytes / (t64_us * 1e-6)

@@ -16,14 +16,18 @@
 // The group's token rows are read from the window ring: with m <= W a completed group still lies
 // there in full, so the state ring holds gates only, and a token's row is written once.
 //
-// gfx950 design. One workgroup per sequence, so the counters are read and advanced by one
-// thread with no cross-workgroup ordering. The work is a few KiB per sequence, so the launch
-// is latency-bound: the aim is one round of loads per group.
-//   m <= 8: one thread per 16-byte channel chunk pools the whole group in registers (the same
-//   function and order as chs_compress, so the entries are bit-identical to a prefill's).
-//   m > 8: a thread pools one block of 8 rows of one chunk; the blocks of a chunk (a power-of-two
-//   count, at most 128) are adjacent threads of one pass, and their states are merged through LDS
-//   in block order. A pass covers 512 / blocks chunks.
+// gfx950 design. The launch is latency-bound (a few KiB per sequence, plus one group's rows when
+// it completes), so the aim is one round of loads and little serial work per group.
+//   m in {1, 2, 4, 8}: one workgroup per sequence; one thread per 16-byte channel chunk pools the
+//   whole group in registers (the same function and order as chs_compress, so the entries are
+//   bit-identical to a prefill's). Thread 0 reads and advances the counters: no other workgroup
+//   reads them.
+//   other m (C128): a group of 128 rows x 512 channels is about 0.7 M lane operations and 65 K
+//   exponentials, several microseconds for one CU, so a sequence's chunks are spread over
+//   several workgroups. A thread pools 8 (16 for m > 512) rows of one chunk; the nb blocks of a
+//   chunk (a power of two, at most 64) are adjacent lanes of one wave, merged by a butterfly of
+//   cross-lane moves, with no LDS and no barrier. Since several workgroups read a sequence's
+//   count, a second, one-thread-per-sequence kernel advances the counters after them.
 // The new token's row and gate are read from the inputs, not from the rings being written in the
 // same launch, so no thread depends on another's store.
 #include "pool.h"
@@ -47,132 +51,210 @@ struct AppendArgs {
   int64_t* comp_count;
 };
 
-constexpr int kSplitThreads = 512;
+constexpr int kSplitThreads = 256;
 
-template <typename ET, int M, int THREADS>
-__global__ __launch_bounds__(THREADS) void append_kernel(AppendArgs a) {
+// The counters after a token: n + 1, min(n + 1, W), floor((n + 1) / m).
+__device__ __forceinline__ void advance_counters(const AppendArgs& a, int b, int64_t n) {
+  a.n_tokens[b] = n + 1;
+  if (a.swa_len) a.swa_len[b] = (int32_t)(n + 1 < a.window ? n + 1 : a.window);
+  if (a.comp_count) a.comp_count[b] = (n + 1) / a.m;
+}
+
+__device__ __forceinline__ int64_t read_count(const AppendArgs& a, int b) {
+  const int64_t n = a.n_tokens[b];
+  return n < 0 ? 0 : n;                                 // a negative count is taken as empty
+}
+
+// Where sequence b's rings live, and whether its ring page is valid (else the gate write and
+// the group are skipped).
+template <typename ET>
+struct SeqRings {
+  ET* swa;
+  ET* ring;
+  bool page_ok;
+  __device__ SeqRings(const AppendArgs& a, int b) {
+    swa = static_cast<ET*>(a.swa) + (int64_t)b * a.window * a.d;
+    const int64_t page = a.ring_page[b];
+    page_ok = page >= 0 && page < a.ring_pages;
+    ring = static_cast<ET*>(a.gate_ring) + (page_ok ? page : 0) * a.ring * a.d;
+  }
+};
+
+// m in {1, 2, 4, 8}: one workgroup per sequence (grid.x = batch).
+template <typename ET, int M>
+__global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   using V = Vec16<ET>;
   constexpr int N = V::N;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int d = a.d;
   const int cpr = d / N;
+  const ET* xn = static_cast<const ET*>(a.x_new) + (int64_t)b * d;
+  const ET* zn = static_cast<const ET*>(a.z_new) + (int64_t)b * d;
+  // The new token's first chunk per thread is loaded before the count is known, so its round
+  // trip overlaps the count's.
+  u32x4 x0 = {0, 0, 0, 0}, z0 = {0, 0, 0, 0};
+  if (tid < cpr) {
+    x0 = *reinterpret_cast<const u32x4*>(xn + tid * N);
+    z0 = *reinterpret_cast<const u32x4*>(zn + tid * N);
+  }
   __shared__ int64_t s_t;
   if (tid == 0) {
-    int64_t n = a.n_tokens[b];
-    if (n < 0) n = 0;                                   // a negative count is taken as empty
+    const int64_t n = read_count(a, b);
     s_t = n;
-    a.n_tokens[b] = n + 1;
-    if (a.swa_len) a.swa_len[b] = (int32_t)(n + 1 < a.window ? n + 1 : a.window);
-    if (a.comp_count) a.comp_count[b] = (n + 1) / a.m;
+    advance_counters(a, b, n);
   }
   __syncthreads();
   const int64_t t = s_t;
-  const ET* xn = static_cast<const ET*>(a.x_new) + (int64_t)b * d;
-  const ET* zn = static_cast<const ET*>(a.z_new) + (int64_t)b * d;
-  ET* swa_b = static_cast<ET*>(a.swa) + (int64_t)b * a.window * d;
-  const int64_t page = a.ring_page[b];
-  const bool page_ok = page >= 0 && page < a.ring_pages;  // an out-of-range page is skipped
-  ET* ring_b = static_cast<ET*>(a.gate_ring) + (page_ok ? page : 0) * a.ring * d;
-
-  // 1 + 2: the new token's row and gate.
+  const SeqRings<ET> sr(a, b);
   const int64_t wslot = t % a.window, rslot = t % a.ring;
-  for (int c = tid; c < cpr; c += THREADS) {
-    V::copy(swa_b + wslot * d + c * N, xn + c * N);
-    if (page_ok) V::copy(ring_b + rslot * d + c * N, zn + c * N);
+  if (tid < cpr) {
+    *reinterpret_cast<u32x4*>(sr.swa + wslot * d + tid * N) = x0;
+    if (sr.page_ok) *reinterpret_cast<u32x4*>(sr.ring + rslot * d + tid * N) = z0;
   }
-  const int m = a.m;
-  if ((t + 1) % m != 0 || !page_ok) return;
-
-  // 3: the completed group, tokens t0 .. t. Row r < m - 1 sits at window slot (t0 + r) mod W
-  // and ring slot (t0 + r) mod R; row m - 1 is the new token.
-  const int64_t t0 = t + 1 - m;
-  const int64_t row = a.comp_start[b] + t / m;
+  for (int c = tid + 256; c < cpr; c += 256) {
+    V::copy(sr.swa + wslot * d + c * N, xn + c * N);
+    if (sr.page_ok) V::copy(sr.ring + rslot * d + c * N, zn + c * N);
+  }
+  if ((t + 1) % M != 0 || !sr.page_ok) return;
+  // The completed group: tokens t + 1 - M .. t. Row r < M - 1 sits at window slot
+  // (t0 + r) mod W and ring slot (t0 + r) mod R; row M - 1 is the new token.
+  const int64_t row = a.comp_start[b] + t / M;
   if (row < 0 || row >= a.comp_rows) return;            // outside the caller's pool: skipped
   ET* out = static_cast<ET*>(a.comp) + row * d;
+  const int64_t t0 = t + 1 - M;
   const int w0 = (int)(t0 % a.window), q0 = (int)(t0 % a.ring);
   const int W = a.window, R = a.ring;
-  if (M > 0) {
-    for (int c = tid; c < cpr; c += THREADS) {
-      const int col = c * N;
-      pool_group<ET, M>(
-          m,
-          [&](int r) -> const ET* {
-            if (r == M - 1) return xn + col;
-            const int s = w0 + r;
-            return swa_b + (int64_t)(s < W ? s : s - W) * d + col;
-          },
-          [&](int r) -> const ET* {
-            if (r == M - 1) return zn + col;
-            const int s = q0 + r;
-            return ring_b + (int64_t)(s < R ? s : s - R) * d + col;
-          },
-          [&](int r) { return a.bias + (int64_t)r * d + col; }, out + col);
-    }
-  } else {
-    __shared__ float part[3][N][THREADS];
-    int nb = 1;
-    while (nb * 8 < m) nb *= 2;                          // blocks per chunk (power of two)
-    const int chunks_per_pass = THREADS / nb;
-    const int blk = tid & (nb - 1);
-    for (int c0 = 0; c0 < cpr; c0 += chunks_per_pass) {
-      const int c = c0 + tid / nb;
-      const int r0 = blk * 8;
-      PoolState<N> st;
-      st.init();
-      if (c < cpr && r0 < m) {
-        const int col = c * N;
-        pool_block<ET, 8, true>(
-            st, r0, min(8, m - r0),
-            [&](int r) -> const ET* {
-              if (r == m - 1) return xn + col;
-              const int s = w0 + r;
-              return swa_b + (int64_t)(s < W ? s : s - W) * d + col;
-            },
-            [&](int r) -> const ET* {
-              if (r == m - 1) return zn + col;
-              const int s = q0 + r;
-              return ring_b + (int64_t)(s < R ? s : s - R) * d + col;
-            },
-            [&](int r) { return a.bias + (int64_t)r * d + col; });
-      }
-#pragma unroll
-      for (int j = 0; j < N; ++j) {
-        part[0][j][tid] = st.mx[j];
-        part[1][j][tid] = st.sum[j];
-        part[2][j][tid] = st.acc[j];
-      }
-      __syncthreads();
-      if (blk == 0 && c < cpr) {
-        const int nblk = (m + 7) / 8;
-        for (int k = 1; k < nblk; ++k) {
-          float omx[N], osum[N], oacc[N];
-#pragma unroll
-          for (int j = 0; j < N; ++j) {
-            omx[j] = part[0][j][tid + k];
-            osum[j] = part[1][j][tid + k];
-            oacc[j] = part[2][j][tid + k];
-          }
-          st.merge(omx, osum, oacc);
-        }
-        pool_store<ET>(st, out + c * N);
-      }
-      __syncthreads();
-    }
+  for (int c = tid; c < cpr; c += 256) {
+    const int col = c * N;
+    pool_group<ET, M, true>(
+        M,
+        [&](int r) -> const ET* {
+          if (r == M - 1) return xn + col;
+          const int s = w0 + r;
+          return sr.swa + (int64_t)(s < W ? s : s - W) * d + col;
+        },
+        [&](int r) -> const ET* {
+          if (r == M - 1) return zn + col;
+          const int s = q0 + r;
+          return sr.ring + (int64_t)(s < R ? s : s - R) * d + col;
+        },
+        [&](int r) { return a.bias + (int64_t)r * d + col; }, out + col);
   }
+}
+
+// Blocks per chunk for any m: rows per thread 8 (16 when m > 512), nb a power of two <= 64.
+__host__ __device__ inline int split_rows_per_thread(int m) { return m > 512 ? 16 : 8; }
+__host__ __device__ inline int split_blocks(int m) {
+  const int rpt = split_rows_per_thread(m);
+  int nb = 1;
+  while (nb * rpt < m) nb *= 2;
+  return nb;
+}
+
+// Merges a float across lanes lane ^ (1 << level) within groups of 2^(level+1) lanes (DPP for
+// the first four levels, a cross-lane permute beyond). The mirrors pair disjoint halves, which
+// is all a symmetric merge needs.
+template <int LEVEL>
+__device__ __forceinline__ float partner(float v) {
+  if (LEVEL == 0) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if (LEVEL == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (LEVEL == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  if (LEVEL == 3) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return __shfl_xor(v, 1 << LEVEL, 64);
+}
+
+template <int LEVEL, int N>
+__device__ __forceinline__ void merge_level(PoolState<N>& st) {
+  float omx[N], osum[N], oacc[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    omx[j] = partner<LEVEL>(st.mx[j]);
+    osum[j] = partner<LEVEL>(st.sum[j]);
+    oacc[j] = partner<LEVEL>(st.acc[j]);
+  }
+  st.merge(omx, osum, oacc);
+}
+
+// Any m: grid (ceil(cpr * nb / 256), batch). Thread (chunk, block) with block = lane % nb.
+template <typename ET>
+__global__ __launch_bounds__(kSplitThreads) void append_split_kernel(AppendArgs a) {
+  using V = Vec16<ET>;
+  constexpr int N = V::N;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int d = a.d;
+  const int cpr = d / N;
+  const int m = a.m;
+  const int nb = split_blocks(m);
+  const int rpt = split_rows_per_thread(m);
+  const int blk = tid & (nb - 1);
+  const int c = (blockIdx.x * kSplitThreads + tid) / nb;
+  const int64_t t = read_count(a, b);
+  const ET* xn = static_cast<const ET*>(a.x_new) + (int64_t)b * d;
+  const ET* zn = static_cast<const ET*>(a.z_new) + (int64_t)b * d;
+  const SeqRings<ET> sr(a, b);
+  if (blk == 0 && c < cpr) {
+    V::copy(sr.swa + (t % a.window) * d + c * N, xn + c * N);
+    if (sr.page_ok) V::copy(sr.ring + (t % a.ring) * d + c * N, zn + c * N);
+  }
+  if ((t + 1) % m != 0 || !sr.page_ok) return;
+  const int64_t row = a.comp_start[b] + t / m;
+  if (row < 0 || row >= a.comp_rows) return;            // outside the caller's pool: skipped
+  const int64_t t0 = t + 1 - m;
+  const int w0 = (int)(t0 % a.window), q0 = (int)(t0 % a.ring);
+  const int W = a.window, R = a.ring;
+  const int col = (c < cpr ? c : cpr - 1) * N;          // lanes past the last chunk read a valid one
+  auto xrow = [&](int r) -> const ET* {
+    if (r == m - 1) return xn + col;
+    const int s = w0 + r;
+    return sr.swa + (int64_t)(s < W ? s : s - W) * d + col;
+  };
+  auto zrow = [&](int r) -> const ET* {
+    if (r == m - 1) return zn + col;
+    const int s = q0 + r;
+    return sr.ring + (int64_t)(s < R ? s : s - R) * d + col;
+  };
+  auto brow = [&](int r) { return a.bias + (int64_t)r * d + col; };
+  PoolState<N> st;
+  st.init();
+  const int r0 = blk * rpt;
+  if (r0 < m) {
+    pool_block<ET, 8, true, true>(st, r0, min(8, m - r0), xrow, zrow, brow);
+    if (rpt == 16 && r0 + 8 < m) pool_block<ET, 8, false, true>(st, r0 + 8, min(8, m - r0 - 8), xrow, zrow, brow);
+  }
+  // Butterfly over the nb lanes of the chunk (nb is uniform: every lane takes the same levels).
+  if (nb > 1) merge_level<0>(st);
+  if (nb > 2) merge_level<1>(st);
+  if (nb > 4) merge_level<2>(st);
+  if (nb > 8) merge_level<3>(st);
+  if (nb > 16) merge_level<4>(st);
+  if (nb > 32) merge_level<5>(st);
+  if (blk == 0 && c < cpr) pool_store<ET>(st, static_cast<ET*>(a.comp) + row * d + col);
+}
+
+__global__ __launch_bounds__(256) void append_advance_kernel(AppendArgs a, int32_t batch) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < batch) advance_counters(a, b, read_count(a, b));
 }
 
 template <typename ET>
 chs_status launch_append(const AppendArgs& a, int32_t batch, hipStream_t s) {
   dim3 grid((unsigned)batch);
   switch (a.m) {
-    case 1: hipLaunchKernelGGL((append_kernel<ET, 1, 256>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((append_kernel<ET, 2, 256>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_kernel<ET, 4, 256>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((append_kernel<ET, 8, 256>), grid, dim3(256), 0, s, a); break;
-    default:   // any other m (3, 5, 6, 7 are one block of rows), through the block-split path
-      hipLaunchKernelGGL((append_kernel<ET, 0, kSplitThreads>), grid, dim3(kSplitThreads), 0, s, a);
+    case 1: hipLaunchKernelGGL((append_small_kernel<ET, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_small_kernel<ET, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_small_kernel<ET, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((append_small_kernel<ET, 8>), grid, dim3(256), 0, s, a); break;
+    default: {
+      const int cpr = a.d / Vec16<ET>::N;
+      const int64_t threads = (int64_t)cpr * split_blocks(a.m);
+      dim3 g2((unsigned)((threads + kSplitThreads - 1) / kSplitThreads), (unsigned)batch);
+      hipLaunchKernelGGL(append_split_kernel<ET>, g2, dim3(kSplitThreads), 0, s, a);
+      if (hipGetLastError() != hipSuccess) return CHS_ERR_LAUNCH;
+      hipLaunchKernelGGL(append_advance_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, s, a, batch);
       break;
+    }
   }
   return launch_status();
 }
@@ -188,7 +270,7 @@ extern "C" chs_status chs_append(chs_dtype dtype, int32_t batch, int32_t d, int3
                                  void* stream) {
   using namespace chs;
   if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
-  if (batch < 1 || batch > (1 << 20) || d < 1 || d > 4096 || m < 1 || m > 1024 || window < m ||
+  if (batch < 1 || batch > 65535 || d < 1 || d > 4096 || m < 1 || m > 1024 || window < m ||
       window > (1 << 20) || ring_size < m || ring_size > (1 << 20) || ring_pages < 1 || comp_rows < 0)
     return CHS_ERR_SHAPE;
   if ((d * elem_size(dtype)) % 16 != 0) return CHS_ERR_SHAPE;

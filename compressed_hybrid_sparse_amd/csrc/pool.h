@@ -75,12 +75,14 @@ struct PoolState {
 #pragma unroll
     for (int j = 0; j < N; ++j) { mx[j] = -INFINITY; sum[j] = 0.f; acc[j] = 0.f; }
   }
-  // Folds in another state (the same chunk over other rows).
+  // Folds in another state (the same chunk over other rows). Symmetric: merging a into b and b
+  // into a give the same bits. Two empty states (maximum -inf) merge into an empty state.
   __device__ void merge(const float* omx, const float* osum, const float* oacc) {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const float nm = fmaxf(mx[j], omx[j]);
-      const float a = fast_exp2(mx[j] - nm), b = fast_exp2(omx[j] - nm);
+      const float a = mx[j] == nm ? 1.f : fast_exp2(mx[j] - nm);
+      const float b = omx[j] == nm ? 1.f : fast_exp2(omx[j] - nm);
       sum[j] = sum[j] * a + osum[j] * b;
       acc[j] = acc[j] * a + oacc[j] * b;
       mx[j] = nm;
@@ -88,35 +90,38 @@ struct PoolState {
   }
 };
 
-// Folds rows r0 .. r0 + nr - 1 (nr <= R) into the state: the block's maximum first, then the
-// previous sums rescaled to it (skipped when FIRST: the state is fresh), then each row's
+// Folds rows r0 .. r0 + nr - 1 (1 <= nr <= R) into the state: the block's maximum first, then
+// the previous sums rescaled to it (skipped when FIRST: the state is fresh), then each row's
 // exponential and weighted contribution in row order. bias(r) is row r's bias chunk.
-template <typename ET, int R, bool FIRST, typename XRow, typename ZRow, typename BRow>
+// All R loads are issued unconditionally, so they are in flight together: a load under a
+// runtime guard gets its own wait for completion. Slots r >= nr re-read the block's last row
+// and take the logit -inf, so they add exactly zero (a weight of 0 times a finite row).
+// ALL_LOADS_FIRST keeps the compiler from interleaving the loads with the arithmetic (which it
+// does to save registers, leaving a few loads in flight at a time): for a launch with one
+// group per workgroup, where the round trips are the whole cost.
+template <typename ET, int R, bool FIRST, bool ALL_LOADS_FIRST = false, typename XRow, typename ZRow, typename BRow>
 __device__ __forceinline__ void pool_block(PoolState<Vec16<ET>::N>& st, int r0, int nr, XRow xrow, ZRow zrow,
                                            BRow brow) {
   using V = Vec16<ET>;
   constexpr int N = V::N;
-  float xv[R][N], av[R][N];
+  float xv[R][N], av[R][N], bv[R][8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r < nr) {
-      V::load(xrow(r0 + r), xv[r]);
-      V::load(zrow(r0 + r), av[r]);
-    }
+    const int rr = r0 + (r < nr ? r : nr - 1);
+    V::load(xrow(rr), xv[r]);
+    V::load(zrow(rr), av[r]);
+    load_bias(brow(rr), bv[r], N);
   }
+  if (ALL_LOADS_FIRST) __builtin_amdgcn_sched_barrier(0);
   float cmax[N];
 #pragma unroll
   for (int j = 0; j < N; ++j) cmax[j] = -INFINITY;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r < nr) {
-      float bv[8];
-      load_bias(brow(r0 + r), bv, N);
 #pragma unroll
-      for (int j = 0; j < N; ++j) {
-        av[r][j] = (av[r][j] + bv[j]) * kLog2e;   // logit in base-2 units
-        cmax[j] = fmaxf(cmax[j], av[r][j]);
-      }
+    for (int j = 0; j < N; ++j) {
+      av[r][j] = r < nr ? (av[r][j] + bv[r][j]) * kLog2e : -INFINITY;   // logit in base-2 units
+      cmax[j] = fmaxf(cmax[j], av[r][j]);
     }
   }
   if (FIRST) {
@@ -135,7 +140,7 @@ __device__ __forceinline__ void pool_block(PoolState<Vec16<ET>::N>& st, int r0, 
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r < nr) {
+    if (r < nr) {   // a uniform branch (nr is the same for every lane); no loads inside
 #pragma unroll
       for (int j = 0; j < N; ++j) {
         const float e = fast_exp2(av[r][j] - st.mx[j]);
@@ -157,12 +162,12 @@ __device__ __forceinline__ void pool_store(const PoolState<Vec16<ET>::N>& st, ET
 
 // A whole group of m rows: M > 0 is a compile-time group size (<= 8, one block); M == 0 takes
 // any m, streamed in blocks of 8 rows with a running maximum, so registers stay bounded.
-template <typename ET, int M, typename XRow, typename ZRow, typename BRow>
+template <typename ET, int M, bool ALL_LOADS_FIRST = false, typename XRow, typename ZRow, typename BRow>
 __device__ __forceinline__ void pool_group(int m, XRow xrow, ZRow zrow, BRow brow, ET* op) {
   PoolState<Vec16<ET>::N> st;
   st.init();
   if (M > 0) {
-    pool_block<ET, (M > 0 ? M : 1), true>(st, 0, M, xrow, zrow, brow);
+    pool_block<ET, (M > 0 ? M : 1), true, ALL_LOADS_FIRST>(st, 0, M, xrow, zrow, brow);
   } else {
     for (int r0 = 0; r0 < m; r0 += 8) pool_block<ET, 8, false>(st, r0, min(8, m - r0), xrow, zrow, brow);
   }

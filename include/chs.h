@@ -122,7 +122,7 @@ chs_status chs_compress(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, co
  *                at cu_comp + 1 keeps the cu arrays of chs_index_topk / chs_decode_attn current.
  * Row pointers must be 16-byte aligned. Sequences must be distinct entries (one token each);
  * n_tokens must not alias swa_len or comp_count.
- * Ranges: 1 <= batch <= 2^20; 1 <= m <= 1024; m <= window <= 2^20; m <= ring_size <= 2^20;
+ * Ranges: 1 <= batch <= 65535; 1 <= m <= 1024; m <= window <= 2^20; m <= ring_size <= 2^20;
  * ring_pages >= 1; comp_rows >= 0; 1 <= d <= 4096 with d*elem_size % 16 == 0. */
 chs_status chs_append(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
                       int32_t ring_size, const void* x_new, const void* z_new, const float* bias,

@@ -54,7 +54,7 @@ def append(dt=1, batch=1, d=512, m=4, W=128, R=8, x=FAKE, z=FAKE, b=FAKE, n=FAKE
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=5), DTYPE), (dict(batch=0), SHAPE), (dict(batch=(1 << 20) + 1), SHAPE), (dict(d=0), SHAPE),
+    (dict(dt=5), DTYPE), (dict(batch=0), SHAPE), (dict(batch=65536), SHAPE), (dict(d=0), SHAPE),
     (dict(d=12), SHAPE), (dict(dt=0, d=6), SHAPE), (dict(d=4104), SHAPE), (dict(m=0), SHAPE), (dict(m=1025), SHAPE),
     (dict(W=3), SHAPE), (dict(R=3), SHAPE), (dict(m=128, W=127, R=128), SHAPE), (dict(pages=0), SHAPE),
     (dict(rows=-1), SHAPE), (dict(x=None), NULL), (dict(z=None), NULL), (dict(b=None), NULL), (dict(n=None), NULL),
