@@ -220,3 +220,17 @@ def append_state(X_seq, Z_seq, B, m: int, window: int, ring_size: int) -> dict:
     comp = compress(X_seq, Z_seq, B, m, np.array([0, N], np.int64))
     return dict(swa=swa, swa_written=swa_w, gate=gate, gate_written=gate_w, comp=comp, n=N,
                 swa_len=min(N, window), comp_count=N // m)
+
+
+# ---------------------------------------------------------------- paged pools
+def paged_rows(pool, page_table, page_size: int, n: int) -> np.ndarray:
+    """The first n logical rows of one sequence stored in a paged pool: logical row j lives at
+    pool row page_table[j // page_size] * page_size + j % page_size.
+    Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", ShadowRadix, and "SGLang 如何为 DeepSeek V4
+    打造「Day-0」推理加速", 创新 1 (the SWA, C4 and C128 pools are managed as physical pools that
+    a per-request index maps into; slot address = page * size + position mod size)."""
+    pool = np.asarray(pool)
+    out = np.empty((n,) + pool.shape[1:], dtype=pool.dtype)
+    for j in range(n):
+        out[j] = pool[int(page_table[j // page_size]) * page_size + j % page_size]
+    return out

@@ -528,6 +528,28 @@ def test_append_state_counts_and_prefix_stability(rng):
         prev = cur
 
 
+# ------------------------------------------------------------------ paged pools
+def test_paged_rows_page_size_one_is_a_gather(rng):
+    pool = rng.standard_normal((40, 3)).astype(np.float32)
+    pt = rng.permutation(40)[:25]
+    assert np.array_equal(oracle.paged_rows(pool, pt, 1, 25), np.take(pool, pt, axis=0))
+
+
+@pytest.mark.parametrize("P", [1, 4, 16, 64])
+def test_paged_rows_identity_table_is_the_pool_prefix(rng, P):
+    pool = rng.standard_normal((256, 2)).astype(np.float32)
+    n = 200
+    assert np.array_equal(oracle.paged_rows(pool, np.arange(256 // P), P, n), pool[:n])
+
+
+def test_paged_rows_swapped_half_pages_swap_the_halves(rng):
+    pool = rng.standard_normal((64, 5)).astype(np.float32)
+    got = oracle.paged_rows(pool, [1, 0], 32, 64)
+    assert np.array_equal(got, np.concatenate([pool[32:], pool[:32]]))
+    part = oracle.paged_rows(pool, [1, 0], 32, 40)          # a ragged tail reads into the second page
+    assert np.array_equal(part, np.concatenate([pool[32:], pool[:8]]))
+
+
 # ------------------------------------------------------------------ storage rounding
 def test_round_bf16_matches_integer_rne_of_fp32_values(rng):
     # For doubles that are exactly fp32 values, rounding to bf16 equals the integer RNE on the
