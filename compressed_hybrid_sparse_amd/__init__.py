@@ -21,7 +21,8 @@ _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE
            4: "CHS_ERR_WORKSPACE", 5: "CHS_ERR_UNSUPPORTED", 6: "CHS_ERR_LAUNCH"}
 EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
-           "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append")
+           "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
+           "chs_decode_attn_paged", "chs_append_paged")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -59,8 +60,12 @@ def lib():
                                           _p, _p, _sz, _p]
         L.chs_append.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p,
                                  _p, _i64, _p, _p]
+        L.chs_decode_attn_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _i64, _p, _p,
+                                            _i64, _i32, _p, _i32, _p, _p, _i64, _p, _p, _p, _sz, _p]
+        L.chs_append_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _i64, _p, _p,
+                                       _p, _i64, _i32, _p, _i32, _p, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
-                   "chs_decode_attn_fp8", "chs_append"):
+                   "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -319,3 +324,71 @@ def decode_attn_fp8(q, swa_codes, swa_scale, swa_len, comp_codes, comp_scale, cu
                                      _stream()),
            "chs_decode_attn_fp8")
     return out, lse
+
+
+# ---------------------------------------------------------------- paged pools
+def decode_attn_paged(q, swa_pool, swa_page, swa_len, comp_pool, page_size: int, page_table, comp_len, topk=None,
+                      scale=None, max_comp=None, workspace=None, out=None, lse=None):
+    """chs_decode_attn over paged pools (chs_decode_attn_paged).
+    q: [B, H, d]; swa_pool: [swa_pages, W, d]; swa_page: [B] int32; swa_len: [B] int32;
+    comp_pool: [pool_rows, d] (pool_rows a multiple of page_size); page_table: [B, pt_stride] int32;
+    comp_len: [B] int64; topk: [B, k] int32 or None. Returns (out [B, H, d] fp32, lse [B, H] fp32)."""
+    _need(q, "q", dim=3)
+    _need(swa_pool, "swa_pool", q.dtype, 3)
+    _need(swa_page, "swa_page", torch.int32, 1)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_pool, "comp_pool", q.dtype, 2)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(comp_len, "comp_len", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_pool.shape[1]
+    k = 0
+    if topk is not None:
+        _need(topk, "topk", torch.int32, 2)
+        k = topk.shape[1]
+    if max_comp is None:
+        max_comp = int(comp_len.max().item()) if comp_len.numel() else 0
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = decode_attn_workspace(q.dtype, B, H, d, W, k, max_comp, q.device)
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _check(lib().chs_decode_attn_paged(_dtype_code(q), B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_pool),
+                                       _ptr(swa_page), swa_pool.shape[0], _ptr(swa_len), _ptr(comp_pool),
+                                       comp_pool.shape[0] // page_size, page_size, _ptr(page_table),
+                                       page_table.shape[1], _ptr(comp_len), _ptr(topk), int(max_comp), _ptr(out),
+                                       _ptr(lse), _ptr(workspace), workspace.numel(), _stream()),
+           "chs_decode_attn_paged")
+    return out, lse
+
+
+def append_paged(x_new, z_new, bias, m: int, n_tokens, swa_pool, swa_page, gate_ring, comp_pool, page_size: int,
+                 page_table, swa_len=None, comp_count=None):
+    """chs_append over paged pools (chs_append_paged). swa_pool: [swa_pages, W, d]; gate_ring:
+    [swa_pages * ring_size, d] (the ring of page p is rows p * ring_size ..); comp_pool:
+    [pool_rows, d]; page_table: [B, pt_stride] int32."""
+    _need(x_new, "x_new", dim=2)
+    dt = x_new.dtype
+    _need(z_new, "z_new", dt, 2)
+    _need(bias, "bias", torch.float32, 2)
+    _need(n_tokens, "n_tokens", torch.int64, 1)
+    _need(swa_pool, "swa_pool", dt, 3)
+    _need(swa_page, "swa_page", torch.int32, 1)
+    _need(gate_ring, "gate_ring", dt, 2)
+    _need(comp_pool, "comp_pool", dt, 2)
+    _need(page_table, "page_table", torch.int32, 2)
+    if swa_len is not None:
+        _need(swa_len, "swa_len", torch.int32, 1)
+    if comp_count is not None and (comp_count.dtype != torch.int64 or not comp_count.is_cuda):
+        raise TypeError("comp_count must be an int64 CUDA tensor")
+    B, d = x_new.shape
+    pages = swa_pool.shape[0]
+    ring_size = gate_ring.shape[0] // pages
+    _check(lib().chs_append_paged(_dtype_code(x_new), B, d, m, swa_pool.shape[1], ring_size, _ptr(x_new), _ptr(z_new),
+                                  _ptr(bias), _ptr(n_tokens), _ptr(swa_pool), _ptr(swa_page), pages, _ptr(swa_len),
+                                  _ptr(gate_ring), _ptr(comp_pool), comp_pool.shape[0] // page_size, page_size,
+                                  _ptr(page_table), page_table.shape[1], _ptr(comp_count), _stream()),
+           "chs_append_paged")

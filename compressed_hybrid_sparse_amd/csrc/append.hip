@@ -49,6 +49,13 @@ struct AppendArgs {
   void* comp;
   const int64_t* comp_start;
   int64_t* comp_count;
+  // Paged pools (NULL: contiguous). The window is page swa_page[b] of the window pool and the gate
+  // ring sits at the same page (the ring nested in the SWA page); entry g goes to pool row
+  // pt[b * pt_stride + g / 2^shift] * 2^shift + g mod 2^shift.
+  const int32_t* swa_page;
+  int64_t swa_pages;
+  const int32_t* pt;
+  int32_t pt_stride, shift;
 };
 
 constexpr int kSplitThreads = 256;
@@ -71,14 +78,38 @@ template <typename ET>
 struct SeqRings {
   ET* swa;
   ET* ring;
-  bool page_ok;
+  bool page_ok;      // the gate ring's page is valid (else the gate write and the group are skipped)
+  bool swa_ok;       // the window's page is valid (else the window write is skipped too)
   __device__ SeqRings(const AppendArgs& a, int b) {
-    swa = static_cast<ET*>(a.swa) + (int64_t)b * a.window * a.d;
-    const int64_t page = a.ring_page[b];
-    page_ok = page >= 0 && page < a.ring_pages;
+    int64_t wpage = b;
+    swa_ok = true;
+    int64_t page;
+    if (a.swa_page) {
+      wpage = a.swa_page[b];
+      swa_ok = wpage >= 0 && wpage < a.swa_pages;
+      if (!swa_ok) wpage = 0;
+      page = a.swa_page[b];
+    } else {
+      page = a.ring_page[b];
+    }
+    swa = static_cast<ET*>(a.swa) + wpage * a.window * a.d;
+    page_ok = swa_ok && page >= 0 && page < a.ring_pages;
     ring = static_cast<ET*>(a.gate_ring) + (page_ok ? page : 0) * a.ring * a.d;
   }
 };
+
+// Pool row of entry g of sequence b, or -1 when it falls outside the caller's pool.
+__device__ __forceinline__ int64_t entry_row(const AppendArgs& a, int b, int64_t g) {
+  if (a.pt) {
+    const int64_t idx = g >> a.shift;
+    if (idx >= a.pt_stride) return -1;
+    const int64_t p = a.pt[(int64_t)b * a.pt_stride + idx];
+    const int64_t row = (p << a.shift) | (g & ((1 << a.shift) - 1));
+    return p < 0 || row >= a.comp_rows ? -1 : row;
+  }
+  const int64_t row = a.comp_start[b] + g;
+  return row < 0 || row >= a.comp_rows ? -1 : row;
+}
 
 // m in {1, 2, 4, 8}: one workgroup per sequence (grid.x = batch).
 template <typename ET, int M>
@@ -108,19 +139,19 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   const int64_t t = s_t;
   const SeqRings<ET> sr(a, b);
   const int64_t wslot = t % a.window, rslot = t % a.ring;
-  if (tid < cpr) {
+  if (tid < cpr && sr.swa_ok) {
     *reinterpret_cast<u32x4*>(sr.swa + wslot * d + tid * N) = x0;
     if (sr.page_ok) *reinterpret_cast<u32x4*>(sr.ring + rslot * d + tid * N) = z0;
   }
-  for (int c = tid + 256; c < cpr; c += 256) {
+  for (int c = tid + 256; c < cpr && sr.swa_ok; c += 256) {
     V::copy(sr.swa + wslot * d + c * N, xn + c * N);
     if (sr.page_ok) V::copy(sr.ring + rslot * d + c * N, zn + c * N);
   }
   if ((t + 1) % M != 0 || !sr.page_ok) return;
   // The completed group: tokens t + 1 - M .. t. Row r < M - 1 sits at window slot
   // (t0 + r) mod W and ring slot (t0 + r) mod R; row M - 1 is the new token.
-  const int64_t row = a.comp_start[b] + t / M;
-  if (row < 0 || row >= a.comp_rows) return;            // outside the caller's pool: skipped
+  const int64_t row = entry_row(a, b, t / M);
+  if (row < 0) return;                                  // outside the caller's pool: skipped
   ET* out = static_cast<ET*>(a.comp) + row * d;
   const int64_t t0 = t + 1 - M;
   const int w0 = (int)(t0 % a.window), q0 = (int)(t0 % a.ring);
@@ -194,13 +225,13 @@ __global__ __launch_bounds__(kSplitThreads) void append_split_kernel(AppendArgs 
   const ET* xn = static_cast<const ET*>(a.x_new) + (int64_t)b * d;
   const ET* zn = static_cast<const ET*>(a.z_new) + (int64_t)b * d;
   const SeqRings<ET> sr(a, b);
-  if (blk == 0 && c < cpr) {
+  if (blk == 0 && c < cpr && sr.swa_ok) {
     V::copy(sr.swa + (t % a.window) * d + c * N, xn + c * N);
     if (sr.page_ok) V::copy(sr.ring + (t % a.ring) * d + c * N, zn + c * N);
   }
   if ((t + 1) % m != 0 || !sr.page_ok) return;
-  const int64_t row = a.comp_start[b] + t / m;
-  if (row < 0 || row >= a.comp_rows) return;            // outside the caller's pool: skipped
+  const int64_t row = entry_row(a, b, t / m);
+  if (row < 0) return;                                  // outside the caller's pool: skipped
   const int64_t t0 = t + 1 - m;
   const int w0 = (int)(t0 % a.window), q0 = (int)(t0 % a.ring);
   const int W = a.window, R = a.ring;
@@ -262,6 +293,24 @@ chs_status launch_append(const AppendArgs& a, int32_t batch, hipStream_t s) {
 }  // namespace
 }  // namespace chs
 
+namespace chs {
+namespace {
+
+chs_status check_append(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window, int32_t ring_size,
+                        const void* x_new, const void* z_new, const float* bias, const int64_t* n_tokens,
+                        const void* swa_kv, const void* gate_ring, const void* comp_kv, int64_t comp_rows) {
+  if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
+  if (batch < 1 || batch > 65535 || d < 1 || d > 4096 || m < 1 || m > 1024 || window < m ||
+      window > (1 << 20) || ring_size < m || ring_size > (1 << 20) || comp_rows < 0)
+    return CHS_ERR_SHAPE;
+  if ((d * elem_size(dtype)) % 16 != 0) return CHS_ERR_SHAPE;
+  if (!x_new || !z_new || !bias || !n_tokens || !swa_kv || !gate_ring || !comp_kv) return CHS_ERR_NULL;
+  return CHS_OK;
+}
+
+}  // namespace
+}  // namespace chs
+
 extern "C" chs_status chs_append(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
                                  int32_t ring_size, const void* x_new, const void* z_new, const float* bias,
                                  int64_t* n_tokens, void* swa_kv, int32_t* swa_len, void* gate_ring,
@@ -269,15 +318,34 @@ extern "C" chs_status chs_append(chs_dtype dtype, int32_t batch, int32_t d, int3
                                  const int64_t* comp_start, int64_t comp_rows, int64_t* comp_count,
                                  void* stream) {
   using namespace chs;
-  if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
-  if (batch < 1 || batch > 65535 || d < 1 || d > 4096 || m < 1 || m > 1024 || window < m ||
-      window > (1 << 20) || ring_size < m || ring_size > (1 << 20) || ring_pages < 1 || comp_rows < 0)
-    return CHS_ERR_SHAPE;
-  if ((d * elem_size(dtype)) % 16 != 0) return CHS_ERR_SHAPE;
-  if (!x_new || !z_new || !bias || !n_tokens || !swa_kv || !gate_ring || !ring_page || !comp_kv || !comp_start)
-    return CHS_ERR_NULL;
+  const chs_status st = check_append(dtype, batch, d, m, window, ring_size, x_new, z_new, bias, n_tokens, swa_kv,
+                                     gate_ring, comp_kv, comp_rows);
+  if (st != CHS_OK) return st;
+  if (ring_pages < 1) return CHS_ERR_SHAPE;
+  if (!ring_page || !comp_start) return CHS_ERR_NULL;
   AppendArgs a{d, m, window, ring_size, ring_pages, comp_rows, x_new, z_new, bias, n_tokens, swa_kv, swa_len,
-               gate_ring, ring_page, comp_kv, comp_start, comp_count};
+               gate_ring, ring_page, comp_kv, comp_start, comp_count, nullptr, 0, nullptr, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == CHS_BF16 ? launch_append<uint16_t>(a, batch, s) : launch_append<float>(a, batch, s);
+}
+
+extern "C" chs_status chs_append_paged(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
+                                       int32_t ring_size, const void* x_new, const void* z_new, const float* bias,
+                                       int64_t* n_tokens, void* swa_pool, const int32_t* swa_page, int64_t swa_pages,
+                                       int32_t* swa_len, void* gate_ring, void* comp_pool, int64_t pool_pages,
+                                       int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                                       int64_t* comp_count, void* stream) {
+  using namespace chs;
+  if (pool_pages < 0 || pool_pages > ((int64_t)1 << 40) / (page_size > 0 ? page_size : 1)) return CHS_ERR_SHAPE;
+  const chs_status st = check_append(dtype, batch, d, m, window, ring_size, x_new, z_new, bias, n_tokens, swa_pool,
+                                     gate_ring, comp_pool, pool_pages * (int64_t)page_size);
+  if (st != CHS_OK) return st;
+  if (swa_pages < 1 || page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0 || pt_stride < 1)
+    return CHS_ERR_SHAPE;
+  if (!swa_page || !page_table) return CHS_ERR_NULL;
+  AppendArgs a{d, m, window, ring_size, swa_pages, pool_pages * (int64_t)page_size, x_new, z_new, bias, n_tokens,
+               swa_pool, swa_len, gate_ring, nullptr, comp_pool, nullptr, comp_count, swa_page, swa_pages,
+               page_table, pt_stride, __builtin_ctz((unsigned)page_size)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return dtype == CHS_BF16 ? launch_append<uint16_t>(a, batch, s) : launch_append<float>(a, batch, s);
 }

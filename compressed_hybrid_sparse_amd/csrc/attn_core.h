@@ -24,6 +24,20 @@ __device__ __forceinline__ __attribute__((address_space(3))) v4i16* lds_v4i16(co
 constexpr int kAttnThreads = 256;       // threads of the standalone split and combine blocks
 constexpr int kKeysPerChunk = 32;
 
+// Paged pools (all NULL / 0: contiguous storage). The window of sequence b is page swa_page[b]
+// of the window pool (rows page * W .. + W - 1) instead of slot b; compressed entry j of sequence
+// b is pool row pt[b * pt_stride + j / 2^shift] * 2^shift + j mod 2^shift, and comp_len[b]
+// entries exist. A window page outside [0, swa_pages) drops the window; an entry whose page is
+// outside [0, pool_pages) is skipped.
+struct Paging {
+  const int32_t* swa_page;  // [batch] or NULL
+  int64_t swa_pages;
+  const int32_t* pt;        // [batch][pt_stride] or NULL
+  const int64_t* comp_len;  // [batch] (with pt)
+  int32_t pt_stride, shift;
+  int64_t pool_pages;
+};
+
 struct AttnArgs {
   const void* q;            // [batch][H][D]
   const void* swa;          // [batch][W][D]
@@ -40,6 +54,7 @@ struct AttnArgs {
   float* part_ml;           // [batch][n_splits][H][2]: running max (base 2), running sum
   const float* swa_scale;   // FP8 storage: [batch][W] row scales of swa (else unused)
   const float* comp_scale;  // FP8 storage: [*] row scales of comp (else unused)
+  Paging pg;                // paged pools (zeroed: contiguous)
 };
 
 constexpr int kCombineSplits = 512;   // most splits one call may use
@@ -52,12 +67,26 @@ constexpr int kCombineLanes = 4;      // lanes per output word in the combine
 // Key slots of sequence b: [0, swa_len) window rows, then k (C4) or G_b (C128) entries.
 struct SlotMap {
   int64_t comp0, G;
+  int64_t swa_row0;         // first row of the sequence's window in the window buffer
   int32_t nswa, nextra;
   __device__ SlotMap(const AttnArgs& a, int b) {
     int32_t L = a.swa_len[b];
     nswa = L < 0 ? 0 : (L > a.W ? a.W : L);
-    comp0 = a.cu_comp[b];
-    G = a.cu_comp[b + 1] - comp0;
+    swa_row0 = (int64_t)b * a.W;
+    if (a.pg.swa_page) {
+      const int64_t p = a.pg.swa_page[b];
+      if (p < 0 || p >= a.pg.swa_pages) nswa = 0;
+      swa_row0 = (p < 0 || p >= a.pg.swa_pages ? 0 : p) * a.W;
+    }
+    if (a.pg.pt) {
+      comp0 = 0;
+      G = a.pg.comp_len[b];
+      const int64_t cap = (int64_t)a.pg.pt_stride << a.pg.shift;
+      if (G > cap) G = cap;
+    } else {
+      comp0 = a.cu_comp[b];
+      G = a.cu_comp[b + 1] - comp0;
+    }
     if (G < 0) G = 0;
     if (a.topk) {
       nextra = a.k;
@@ -70,12 +99,17 @@ struct SlotMap {
   // Element offset of slot s's row within its buffer; -1 if the slot holds no key.
   // *is_swa tells which buffer.
   __device__ int64_t row(const AttnArgs& a, int b, int32_t s, bool* is_swa) const {
-    if (s < nswa) { *is_swa = true; return ((int64_t)b * a.W + s) * a.D; }
+    if (s < nswa) { *is_swa = true; return (swa_row0 + s) * a.D; }
     *is_swa = false;
     int64_t j = s - nswa;
     if (a.topk) {
       j = a.topk[(int64_t)b * a.k + j];
       if (j < 0 || j >= G) return -1;
+    }
+    if (a.pg.pt) {
+      const int64_t p = a.pg.pt[(int64_t)b * a.pg.pt_stride + (j >> a.pg.shift)];
+      if (p < 0 || p >= a.pg.pool_pages) return -1;
+      return ((p << a.pg.shift) | (j & ((1 << a.pg.shift) - 1))) * a.D;
     }
     return (comp0 + j) * a.D;
   }
@@ -102,7 +136,9 @@ __device__ __forceinline__ float row16_sum(float v) {
 // s0 + li * RPI + lr (null: no key there); with FP8 storage also the row's scale. Branch-free:
 // the top-k entry is read at a clamped position whether or not the slot needs it, so the reads
 // issue back to back. When a load is one whole row every operand is the same for the whole wave.
-template <int D, int LOADS, int RPI, int NW, typename ET>
+// PAGED: entries go through the page table (one more dependent read per row, clamped the same
+// way), and the window through the sequence's window page.
+template <int D, int LOADS, int RPI, int NW, typename ET, bool PAGED = false>
 __device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm, int b, int32_t s0, int32_t s_end,
                                            int wave, int lr, const ET* (&rp)[LOADS], const float* (&rs)[LOADS]) {
   constexpr int NLOADS = kKeysPerChunk / RPI;
@@ -117,12 +153,27 @@ __device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm,
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) idx[i] = s0 + (i * NW + wave) * RPI + lr - sm.nswa;
   }
+  int64_t prow[LOADS];                                 // PAGED: pool row of the entry
+  bool pok[LOADS];
+  if (PAGED) {
+    const int32_t* ptb = a.pg.pt + (int64_t)b * a.pg.pt_stride;
+    const int32_t mask = (1 << a.pg.shift) - 1;
+    const int64_t last = sm.G > 0 ? sm.G - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int64_t j = idx[i] < 0 ? 0 : (idx[i] > last ? last : idx[i]);
+      const int64_t p = ptb[j >> a.pg.shift];
+      pok[i] = p >= 0 && p < a.pg.pool_pages;
+      prow[i] = ((pok[i] ? p : 0) << a.pg.shift) | (j & mask);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int32_t s = s0 + (i * NW + wave) * RPI + lr;
     const bool in_swa = s < sm.nswa;
-    const bool ok = i * NW + wave < NLOADS && s < s_end && (in_swa || (idx[i] >= 0 && idx[i] < sm.G));
-    const int64_t row = in_swa ? (int64_t)b * a.W + s : sm.comp0 + idx[i];
+    const bool ok = i * NW + wave < NLOADS && s < s_end &&
+                    (in_swa || (idx[i] >= 0 && idx[i] < sm.G && (!PAGED || pok[i])));
+    const int64_t row = in_swa ? sm.swa_row0 + s : (PAGED ? prow[i] : sm.comp0 + idx[i]);
     const ET* p = (in_swa ? swa : comp) + row * D;
     rp[i] = ok ? p : nullptr;
     if (sizeof(ET) == 1) rs[i] = ok ? (in_swa ? a.swa_scale : a.comp_scale) + row : nullptr;
@@ -151,7 +202,7 @@ struct NoHook {
 // through LDS in a fixed order, so all four waves hold bit-identical logits and run the same
 // softmax; and computes P.V for its quarter. before_rows(s0) runs, uniformly over the
 // workgroup, before the rows of the chunk at slot s0 are looked up.
-template <int D, int TILES, typename Hook, bool FP8 = false>
+template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false>
 __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, int z0, int tid,
                                            AttnShared<D, TILES>& sh, Hook& before_rows) {
   constexpr int KC = kKeysPerChunk;
@@ -184,7 +235,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
   const ET* rp[LOADS];
   const float* rs[LOADS];
   before_rows(s_begin);
-  chunk_rows<D, LOADS, RPI, NW, ET>(a, sm, b, s_begin, s_end, wave, lr, rp, rs);
+  chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s_begin, s_end, wave, lr, rp, rs);
 
   // Q fragment (A operand): row c of the tile's 16 heads, d = d0 + 32t + 8g .. +8 (d0 = this
   // wave's quarter); head index clamped, then zeroed, so the loads are unconditional.
@@ -243,7 +294,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
     }
     if (s0 + KC < s_end) {
       before_rows(s0 + KC);
-      chunk_rows<D, LOADS, RPI, NW, ET>(a, sm, b, s0 + KC, s_end, wave, lr, rp, rs);
+      chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s0 + KC, s_end, wave, lr, rp, rs);
     }
     __syncthreads();
     // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.

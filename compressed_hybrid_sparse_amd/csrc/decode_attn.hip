@@ -36,11 +36,12 @@ constexpr int kThreads = kAttnThreads;
 
 // ---------------------------------------------------------------- bf16 MFMA split kernel
 // One workgroup of 4 waves per (split, sequence, 16-head tile).
-template <int D>
+// PAGED: the window and the compressed entries come from paged pools (AttnArgs::pg).
+template <int D, bool PAGED = false>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   __shared__ AttnShared<D, 1> sh;
   NoHook none;
-  attn_split<D, 1>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
+  attn_split<D, 1, NoHook, false, PAGED>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
 }
 
 // The same with FP8 E4M3 storage and per-row scales.
@@ -190,36 +191,35 @@ extern "C" size_t chs_decode_attn_workspace_size(chs_dtype dtype, int32_t batch,
   return ws_bytes(dtype, batch, n_heads, d, p, nullptr, nullptr, nullptr);
 }
 
-extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
-                                      int32_t window, int32_t k, float scale, const void* q,
-                                      const void* swa_kv, const int32_t* swa_len, const void* comp_kv,
-                                      const int64_t* cu_comp, const int32_t* topk, int64_t max_comp,
-                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
-  using namespace chs;
-  const chs_status st = attn::check_args(dtype, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv,
-                                         cu_comp, topk, max_comp, out);
-  if (st != CHS_OK) return st;
-  if (!workspace) return CHS_ERR_NULL;
+namespace chs {
+namespace {
+
+// Split kernel + combine for bf16 / fp32 storage, contiguous or paged (pg zeroed: contiguous).
+chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                       float scale, const void* q, const void* swa_kv, const int32_t* swa_len, const void* comp_kv,
+                       const int64_t* cu_comp, const attn::Paging& pg, const int32_t* topk, int64_t max_comp,
+                       float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int kk = topk ? k : 0;
   SplitPlan p = plan_splits(dtype, batch, n_heads, window, kk, max_comp);
   AttnArgs a;
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = nullptr; a.comp_scale = nullptr;
+  a.pg = pg;
   a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
   a.n_splits = p.n_splits; a.kps = p.kps;
   a.head_tiles = dtype == CHS_BF16 ? (n_heads + 63) / 64 : n_heads;
   const size_t need = ws_bytes(dtype, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool paged = pg.pt != nullptr;
   if (dtype == CHS_BF16) {
     dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, a); };
     switch (d) {
-      case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kThreads), 0, s, a); break;
-      case 128: hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kThreads), 0, s, a); break;
-      case 256: hipLaunchKernelGGL(attn_bf16_kernel<256>, grid, dim3(kThreads), 0, s, a); break;
-      default: hipLaunchKernelGGL(attn_bf16_kernel<512>, grid, dim3(kThreads), 0, s, a); break;
+      case 64: paged ? go(attn_bf16_kernel<64, true>) : go(attn_bf16_kernel<64>); break;
+      case 128: paged ? go(attn_bf16_kernel<128, true>) : go(attn_bf16_kernel<128>); break;
+      case 256: paged ? go(attn_bf16_kernel<256, true>) : go(attn_bf16_kernel<256>); break;
+      default: paged ? go(attn_bf16_kernel<512, true>) : go(attn_bf16_kernel<512>); break;
     }
   } else {
     dim3 grid(p.n_splits, batch, n_heads);
@@ -235,6 +235,54 @@ extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_
     hipLaunchKernelGGL(combine_rows_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
+                                      int32_t window, int32_t k, float scale, const void* q,
+                                      const void* swa_kv, const int32_t* swa_len, const void* comp_kv,
+                                      const int64_t* cu_comp, const int32_t* topk, int64_t max_comp,
+                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  using namespace chs;
+  const chs_status st = attn::check_args(dtype, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv,
+                                         cu_comp, topk, max_comp, out);
+  if (st != CHS_OK) return st;
+  if (!workspace) return CHS_ERR_NULL;
+  const attn::Paging none{};
+  return launch_attn(dtype, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv, cu_comp, none, topk,
+                     max_comp, out, lse, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" chs_status chs_decode_attn_paged(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
+                                            int32_t window, int32_t k, float scale, const void* q,
+                                            const void* swa_pool, const int32_t* swa_page, int64_t swa_pages,
+                                            const int32_t* swa_len, const void* comp_pool, int64_t pool_pages,
+                                            int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                                            const int64_t* comp_len, const int32_t* topk, int64_t max_comp,
+                                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  using namespace chs;
+  // The shared checks null-test their cu argument; here the per-sequence counts take its place.
+  const chs_status st = attn::check_args(dtype, batch, n_heads, d, window, k, scale, q, swa_pool, swa_len, comp_pool,
+                                         comp_len, topk, max_comp, out);
+  if (st != CHS_OK) return st;
+  if (!workspace || !page_table || (window > 0 && !swa_page)) return CHS_ERR_NULL;
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0 || pt_stride < 1 ||
+      pool_pages < 1 || (window > 0 && swa_pages < 1))
+    return CHS_ERR_SHAPE;
+  attn::Paging pg{};
+  pg.swa_page = window > 0 ? swa_page : nullptr;
+  pg.swa_pages = swa_pages;
+  pg.pt = page_table;
+  pg.comp_len = comp_len;
+  pg.pt_stride = pt_stride;
+  pg.shift = __builtin_ctz((unsigned)page_size);
+  pg.pool_pages = pool_pages;
+  return launch_attn(dtype, batch, n_heads, d, window, k, scale, q, swa_pool, swa_len, comp_pool, nullptr, pg, topk,
+                     max_comp, out, lse, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" chs_status chs_decode_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
@@ -255,6 +303,7 @@ extern "C" chs_status chs_decode_attn_fp8(int32_t batch, int32_t n_heads, int32_
   AttnArgs a;
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = swa_scale; a.comp_scale = comp_scale;
+  a.pg = attn::Paging{};
   a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
   a.n_splits = p.n_splits; a.kps = p.kps;

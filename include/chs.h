@@ -219,6 +219,46 @@ chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int3
                            float* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- Paged pools: chs_decode_attn_paged, chs_append_paged ----------------------------------
+ * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 1 (ShadowRadix: a per-request index
+ * projected onto separate physical pools for the window, the C4 and the C128 entries, plus the
+ * state rings, whose address is swa_page * ring_size + pos; the window pool frees a sequence's page
+ * as it slides while its compressed entries stay shared) and "DeepSeek-V4 本地部署，SGLang 把活做絕
+ * 了", ShadowRadix (the ring nested in the SWA page index).
+ * The calls compute exactly what chs_decode_attn / chs_append compute; only the addressing differs:
+ *   window of sequence b    : rows swa_page[b] * window .. + window - 1 of swa_pool
+ *                             ([swa_pages * window, d]); its gate ring (chs_append_paged) is page
+ *                             swa_page[b] of gate_ring ([swa_pages * ring_size, d]);
+ *   compressed entry j of b : row page_table[b * pt_stride + j / page_size] * page_size
+ *                             + j mod page_size of the pool ([pool_pages * page_size, d]);
+ *   entries of b            : comp_len[b] (int64, capped at pt_stride * page_size), in place of the
+ *                             cu_comp ranges. Top-k indices stay sequence-local.
+ * page_size is a power of two, 1 .. 65536; page tables are [batch, pt_stride] int32. A window page
+ * outside [0, swa_pages) drops that sequence's window (attention) or skips its writes (append);
+ * an entry whose page is outside the pool is skipped (attention) or not written (append).
+ * chs_decode_attn_paged takes the workspace of chs_decode_attn_workspace_size with the same
+ * arguments; max_comp (host) must bound max_b comp_len[b] for a dense (C128) call. dtype CHS_BF16
+ * or CHS_F32, d as for chs_decode_attn. One page table can serve the KV pool and the index-key pool
+ * (chs_index_topk_paged): they hold the same entry numbering. */
+chs_status chs_decode_attn_paged(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d,
+                                 int32_t window, int32_t k, float scale, const void* q,
+                                 const void* swa_pool, const int32_t* swa_page, int64_t swa_pages,
+                                 const int32_t* swa_len, const void* comp_pool, int64_t pool_pages,
+                                 int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                                 const int64_t* comp_len, const int32_t* topk, int64_t max_comp,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* chs_append_paged: chs_append with the window, the gate ring and the compressed pool paged as
+ * above (n_tokens, swa_len, comp_count as in chs_append; comp_count counts entries, so it can feed
+ * comp_len of chs_decode_attn_paged directly). */
+chs_status chs_append_paged(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
+                            int32_t ring_size, const void* x_new, const void* z_new, const float* bias,
+                            int64_t* n_tokens, void* swa_pool, const int32_t* swa_page, int64_t swa_pages,
+                            int32_t* swa_len, void* gate_ring, void* comp_pool, int64_t pool_pages,
+                            int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                            int64_t* comp_count, void* stream);
+
 /* ---- chs_decode_attn_fp8: chs_decode_attn over an FP8 KV cache ------------------------------
  * Source: as chs_decode_attn, with "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 4.3 部署配置
  * 建议 (an fp8 KV cache) and "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (attention

@@ -66,6 +66,42 @@ def test_append_validation(kw, code):
     assert append(**kw) == code
 
 
+def attn_paged(dt=1, batch=1, H=64, d=512, W=128, k=512, scale=0.04, q=FAKE, swa=FAKE, sp=FAKE, nsp=4, sl=FAKE,
+               pool=FAKE, npool=100, P=64, pt=FAKE, stride=8, cl=FAKE, tk=FAKE, maxc=1000, out=FAKE, lse=FAKE, ws=FAKE,
+               wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_decode_attn_workspace_size(dt, batch, H, d, W, k if tk else 0, maxc)
+    return L.chs_decode_attn_paged(dt, batch, H, d, W, k, ctypes.c_float(scale), q, swa, sp, nsp, sl, pool, npool, P, pt,
+                                   stride, cl, tk, maxc, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=4), DTYPE), (dict(batch=0), SHAPE), (dict(d=96), SHAPE), (dict(scale=-1.0), SHAPE), (dict(P=0), SHAPE),
+    (dict(P=48), SHAPE), (dict(P=131072), SHAPE), (dict(stride=0), SHAPE), (dict(npool=0), SHAPE), (dict(nsp=0), SHAPE),
+    (dict(q=None), NULL), (dict(sl=None), NULL), (dict(cl=None), NULL), (dict(pt=None), NULL), (dict(sp=None), NULL),
+    (dict(out=None), NULL), (dict(ws=None), NULL), (dict(wsb=8), WS),
+])
+def test_decode_attn_paged_validation(kw, code):
+    assert attn_paged(**kw) == code
+
+
+def append_paged(dt=1, batch=1, d=512, m=4, W=128, R=8, x=FAKE, z=FAKE, b=FAKE, n=FAKE, swa=FAKE, sp=FAKE, nsp=4,
+                 sl=FAKE, ring=FAKE, pool=FAKE, npool=100, P=64, pt=FAKE, stride=8, cc=FAKE):
+    return chs.lib().chs_append_paged(dt, batch, d, m, W, R, x, z, b, n, swa, sp, nsp, sl, ring, pool, npool, P, pt,
+                                      stride, cc, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=4), DTYPE), (dict(batch=0), SHAPE), (dict(d=12), SHAPE), (dict(m=0), SHAPE), (dict(W=3), SHAPE),
+    (dict(R=2), SHAPE), (dict(P=0), SHAPE), (dict(P=24), SHAPE), (dict(stride=0), SHAPE), (dict(nsp=0), SHAPE),
+    (dict(npool=-1), SHAPE), (dict(x=None), NULL), (dict(n=None), NULL), (dict(swa=None), NULL), (dict(sp=None), NULL),
+    (dict(ring=None), NULL), (dict(pool=None), NULL), (dict(pt=None), NULL),
+])
+def test_append_paged_validation(kw, code):
+    assert append_paged(**kw) == code
+
+
 def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
          ws=FAKE, wsb=None):
     L = chs.lib()

@@ -1,0 +1,226 @@
+"""Paged pools: chs_decode_attn_paged and chs_append_paged against the oracle, which reads the
+pools through its own paged_rows definition, and against the contiguous calls on the same rows.
+
+Pools are filled by scattering seeded rows to random pages (input preparation); pages no
+sequence owns hold a sentinel."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_hybrid_sparse_amd as chs
+import oracle
+from chs_testutil import assert_bf16_path, assert_bf16_stored, assert_f32, assert_lse, dev
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 7.0
+
+
+def _t(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev(), dt)
+
+
+def _round(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).float().numpy()
+
+
+def _paged_pool(rng, rows_per_seq, P, d, dt, extra_pages=3):
+    """Scatter each sequence's logical rows to shuffled pages. Returns (pool rows fp32 as stored,
+    page table [B, stride] int32)."""
+    need = [(len(r) + P - 1) // P for r in rows_per_seq]
+    stride = max(1, max(need))
+    total = sum(need) + extra_pages
+    pages = rng.permutation(total)
+    pool = np.full((total * P, d), SENTINEL, np.float32)
+    pt = np.full((len(rows_per_seq), stride), -1, np.int32)
+    k = 0
+    for b, rows in enumerate(rows_per_seq):
+        for i in range(need[b]):
+            pt[b, i] = pages[k]
+            k += 1
+        for j in range(len(rows)):
+            pool[pt[b, j // P] * P + j % P] = rows[j]
+    return _round(pool, dt), pt
+
+
+@pytest.mark.parametrize("dt,H,d,W,P,G_list,k,dense", [
+    (torch.bfloat16, 64, 512, 128, 64, [3000, 0, 700], 512, False),
+    (torch.bfloat16, 64, 512, 128, 128, [2048, 1000], 0, True),
+    (torch.bfloat16, 16, 128, 32, 1, [300, 45], 40, False),        # page size 1: a gather per entry
+    (torch.bfloat16, 100, 256, 128, 256, [5000], 200, False),
+    (torch.float32, 8, 64, 128, 16, [256, 77], 64, False),
+    (torch.float32, 8, 64, 16, 32, [100, 40], 0, True),
+])
+def test_paged_attention_matches_oracle_and_contiguous(dt, H, d, W, P, G_list, k, dense):
+    print(f"case: paged attention {dt} H={H} d={d} W={W} P={P} G={G_list} k={k} dense={dense}", flush=True)
+    rng = np.random.default_rng(H + d + W + P)
+    B = len(G_list)
+    q = _round(rng.standard_normal((B, H, d)), dt)
+    logical = [_round(rng.standard_normal((G, d)), dt) for G in G_list]
+    pool, pt = _paged_pool(rng, logical, P, d, dt)
+    swa_pages = B + 2
+    swa_page = rng.permutation(swa_pages)[:B].astype(np.int32)
+    swa_pool = _round(rng.standard_normal((swa_pages, W, d)), dt)
+    swa_len = rng.integers(0, W + 1, B).astype(np.int32)
+    swa_len[0] = W
+    topk = None
+    if not dense:
+        topk = np.full((B, k), -1, np.int32)
+        for b, G in enumerate(G_list):
+            sel = rng.integers(0, max(G, 1), k) if G else np.full(k, -1)
+            bad = rng.choice(k, min(5, k), replace=False)
+            sel[bad] = rng.choice([-1, -7, G, G + 9], len(bad))
+            topk[b] = sel
+    comp_len = np.array(G_list, np.int64)
+    out, lse = chs.decode_attn_paged(_t(q, dt), _t(swa_pool, dt), torch.from_numpy(swa_page).to(dev()),
+                                     torch.from_numpy(swa_len).to(dev()), _t(pool, dt), P,
+                                     torch.from_numpy(pt).to(dev()), torch.from_numpy(comp_len).to(dev()),
+                                     None if dense else torch.from_numpy(topk).to(dev()), d ** -0.5, max(G_list))
+    # The same rows, contiguous.
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(G_list)]), dtype=torch.int64, device=dev())
+    comp_c = _t(np.concatenate(logical) if sum(G_list) else np.zeros((1, d)), dt)
+    swa_c = _t(np.stack([swa_pool[p] for p in swa_page]), dt)
+    out_c, lse_c = chs.decode_attn(_t(q, dt), swa_c, torch.from_numpy(swa_len).to(dev()), comp_c, cu,
+                                   None if dense else torch.from_numpy(topk).to(dev()), d ** -0.5, max(G_list))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_c) and torch.equal(lse, lse_c), "paged and contiguous calls differ"
+    og, lg = out.cpu().numpy(), lse.cpu().numpy()
+    for b, G in enumerate(G_list):
+        comp_rows = oracle.paged_rows(pool, pt[b], P, G)
+        win = swa_pool[swa_page[b]][:swa_len[b]]
+        o_ref, l_ref = oracle.attend(q[b], oracle.step_keys(win, comp_rows, None if dense else topk[b]), d ** -0.5)
+        if dt == torch.bfloat16:
+            assert_bf16_path(og[b], o_ref, f"paged attention b={b}")
+            assert_lse(lg[b], l_ref, f"paged lse b={b}", 1e-3)
+        else:
+            assert_f32(og[b], o_ref, f"paged attention b={b}")
+            assert_lse(lg[b], l_ref, f"paged lse b={b}", 1e-5)
+
+
+def test_paged_attention_skips_bad_pages_and_caps_lengths():
+    # An entry whose page is outside the pool is skipped; a window page outside the window pool
+    # drops the window; comp_len beyond the page table's reach is capped.
+    print("case: paged attention with bad pages", flush=True)
+    rng = np.random.default_rng(9)
+    dt, H, d, W, P = torch.bfloat16, 16, 128, 32, 16
+    logical = [_round(rng.standard_normal((64, d)), dt), _round(rng.standard_normal((48, d)), dt)]
+    pool, pt = _paged_pool(rng, logical, P, d, dt)
+    pool_pages = pool.shape[0] // P
+    pt[0, 1] = pool_pages + 3                 # entries 16..31 of sequence 0: skipped
+    q = _round(rng.standard_normal((2, H, d)), dt)
+    swa_pool = _round(rng.standard_normal((2, W, d)), dt)
+    swa_page = np.array([0, 5], np.int32)     # sequence 1's window page is outside [0, 2)
+    swa_len = np.array([W, W], np.int32)
+    comp_len = np.array([64, 1000], np.int64)  # sequence 1: capped at stride * P = 64; its 4th page is -1
+    out, lse = chs.decode_attn_paged(_t(q, dt), _t(swa_pool, dt), torch.from_numpy(swa_page).to(dev()),
+                                     torch.from_numpy(swa_len).to(dev()), _t(pool, dt), P,
+                                     torch.from_numpy(pt).to(dev()), torch.from_numpy(comp_len).to(dev()), None,
+                                     d ** -0.5, 1000)
+    torch.cuda.synchronize()
+    og, lg = out.cpu().numpy(), lse.cpu().numpy()
+    keys0 = np.concatenate([swa_pool[0], logical[0][:16], logical[0][32:]])
+    assert pt[1, 3] == -1                     # entries 48..63 of the capped length: skipped
+    rows1 = oracle.paged_rows(pool, pt[1], P, 48)
+    for b, keys in ((0, keys0), (1, rows1)):
+        o_ref, l_ref = oracle.attend(q[b], keys, d ** -0.5)
+        assert_bf16_path(og[b], o_ref, f"b={b}")
+        assert_lse(lg[b], l_ref, f"lse b={b}", 1e-3)
+
+
+@pytest.mark.parametrize("dt,d,m,W,R,P,n0,steps", [
+    (torch.bfloat16, 512, 4, 128, 8, 64, [0, 3, 130, 1001], 13),
+    (torch.bfloat16, 256, 128, 128, 128, 16, [0, 127, 300], 130),
+    (torch.float32, 64, 4, 16, 4, 1, [5, 6, 70], 9),
+])
+def test_paged_append_matches_oracle(dt, d, m, W, R, P, n0, steps):
+    print(f"case: paged append {dt} d={d} m={m} W={W} R={R} P={P} n0={n0}", flush=True)
+    rng = np.random.default_rng(d + m + P)
+    B = len(n0)
+    X = [_round(rng.standard_normal((n + steps, d)), dt) for n in n0]
+    Z = [_round(rng.standard_normal((n + steps, d)) * 2, dt) for n in n0]
+    bias = (rng.standard_normal((m, d)) * 0.1).astype(np.float32)
+    swa_pages = B + 2
+    swa_page = rng.permutation(swa_pages)[:B].astype(np.int32)
+    swa_pool = np.zeros((swa_pages, W, d), np.float32)
+    ring = np.full((swa_pages * R, d), SENTINEL, np.float32)
+    for b in range(B):
+        img, wr = oracle.ring_image(X[b][:n0[b]], W)
+        swa_pool[swa_page[b]][wr] = img[wr]
+        img, wr = oracle.ring_image(Z[b][:n0[b]], R)
+        ring[swa_page[b] * R:(swa_page[b] + 1) * R][wr] = img[wr]
+    caps = [(n + steps) // m + 1 for n in n0]
+    placeholder = [np.zeros((c, d), np.float32) for c in caps]
+    pool, pt = _paged_pool(rng, placeholder, P, d, dt)
+    pool[:] = SENTINEL
+    swa_t, ring_t, pool_t = _t(swa_pool, dt), _t(ring, dt), _t(pool, dt)
+    n_t = torch.tensor(n0, dtype=torch.int64, device=dev())
+    sl = torch.zeros(B, dtype=torch.int32, device=dev())
+    cc = torch.zeros(B, dtype=torch.int64, device=dev())
+    page_t, pt_t, bias_t = torch.from_numpy(swa_page).to(dev()), torch.from_numpy(pt).to(dev()), _t(bias, torch.float32)
+    for s in range(steps):
+        xs = np.stack([X[b][n0[b] + s] for b in range(B)])
+        zs = np.stack([Z[b][n0[b] + s] for b in range(B)])
+        chs.append_paged(_t(xs, dt), _t(zs, dt), bias_t, m, n_t, swa_t, page_t, ring_t, pool_t, P, pt_t, swa_len=sl,
+                         comp_count=cc)
+    torch.cuda.synchronize()
+    swa_g, ring_g, pool_g = swa_t.float().cpu().numpy(), ring_t.float().cpu().numpy(), pool_t.float().cpu().numpy()
+    for b in range(B):
+        N = n0[b] + steps
+        want = oracle.append_state(X[b][:N], Z[b][:N], bias, m, W, R)
+        assert n_t[b].item() == N and sl[b].item() == want["swa_len"] and cc[b].item() == want["comp_count"]
+        wr = want["swa_written"]
+        assert np.array_equal(swa_g[swa_page[b]][wr], want["swa"][wr]), f"window page of sequence {b}"
+        gw = want["gate_written"]
+        assert np.array_equal(ring_g[swa_page[b] * R:(swa_page[b] + 1) * R][gw], want["gate"][gw])
+        entries = oracle.paged_rows(pool_g, pt[b], P, N // m)
+        new = slice(n0[b] // m, N // m)
+        if new.stop > new.start:
+            if dt == torch.bfloat16:
+                assert_bf16_stored(entries[new], want["comp"][new], f"entries of sequence {b}")
+            else:
+                assert_f32(entries[new], want["comp"][new], f"entries of sequence {b}")
+        assert np.all(entries[:new.start] == SENTINEL)
+
+
+def test_paged_decode_loop_dense():
+    # A dense (C128-style) layer over paged pools: each step appends the token (its window page,
+    # its gate ring, an entry every m tokens through the page table) and attends over the window
+    # and every entry; comp_count feeds comp_len directly.
+    print("case: paged decode loop", flush=True)
+    rng = np.random.default_rng(31)
+    dt, m, W, R, P, d, H = torch.bfloat16, 8, 16, 16, 4, 128, 16
+    n0, steps = 37, 30
+    N1 = n0 + steps
+    X = _round(rng.standard_normal((N1, d)), dt)
+    Z = _round(rng.standard_normal((N1, d)) * 2, dt)
+    bias = (rng.standard_normal((m, d)) * 0.1).astype(np.float32)
+    cap = N1 // m + 1
+    pool, pt = _paged_pool(rng, [np.zeros((cap, d), np.float32)], P, d, dt)
+    pre = oracle.store(oracle.compress(X[:n0], Z[:n0], bias, m, np.array([0, n0])), True)
+    for j in range(n0 // m):
+        pool[pt[0, j // P] * P + j % P] = pre[j]
+    swa_pool = np.zeros((3, W, d), np.float32)
+    swa_page = np.array([2], np.int32)
+    img, wr = oracle.ring_image(X[:n0], W)
+    swa_pool[2][wr] = img[wr]
+    ring = np.zeros((3 * R, d), np.float32)
+    img, wr = oracle.ring_image(Z[:n0], R)
+    ring[2 * R:3 * R][wr] = img[wr]
+    swa_t, ring_t, pool_t = _t(swa_pool, dt), _t(ring, dt), _t(pool, dt)
+    n_t = torch.tensor([n0], dtype=torch.int64, device=dev())
+    sl = torch.zeros(1, dtype=torch.int32, device=dev())
+    clen = torch.tensor([n0 // m], dtype=torch.int64, device=dev())
+    page_t, pt_t, bias_t = torch.from_numpy(swa_page).to(dev()), torch.from_numpy(pt).to(dev()), _t(bias, torch.float32)
+    for s in range(steps):
+        t = n0 + s
+        N = t + 1
+        chs.append_paged(_t(X[t:t + 1], dt), _t(Z[t:t + 1], dt), bias_t, m, n_t, swa_t, page_t, ring_t, pool_t, P, pt_t,
+                         swa_len=sl, comp_count=clen)
+        q = _round(rng.standard_normal((1, H, d)), dt)
+        out, lse = chs.decode_attn_paged(_t(q, dt), swa_t, page_t, sl, pool_t, P, pt_t, clen, None, d ** -0.5, cap)
+        torch.cuda.synchronize()
+        assert clen.item() == N // m and sl.item() == min(N, W)
+        cref = oracle.store(oracle.compress(X[:N], Z[:N], bias, m, np.array([0, N])), True)
+        o_ref, l_ref = oracle.decode_step(q[0], X[:N], W, cref, None, d ** -0.5)
+        assert_bf16_path(out[0].cpu().numpy(), o_ref, f"step {s}")
+        assert_lse(lse[0].cpu().numpy(), l_ref, f"step {s} lse")
