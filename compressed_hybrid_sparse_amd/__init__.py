@@ -22,7 +22,7 @@ _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE
 EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
-           "chs_decode_attn_paged", "chs_append_paged")
+           "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -64,8 +64,11 @@ def lib():
                                             _i64, _i32, _p, _i32, _p, _p, _i64, _p, _p, _p, _sz, _p]
         L.chs_append_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _i64, _p, _p,
                                        _p, _i64, _i32, _p, _i32, _p, _p]
+        L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
+                                           _i64, _p, _p, _p, _sz, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
-                   "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged"):
+                   "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
+                   "chs_index_topk_paged"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -392,3 +395,28 @@ def append_paged(x_new, z_new, bias, m: int, n_tokens, swa_pool, swa_page, gate_
                                   _ptr(gate_ring), _ptr(comp_pool), comp_pool.shape[0] // page_size, page_size,
                                   _ptr(page_table), page_table.shape[1], _ptr(comp_count), _stream()),
            "chs_append_paged")
+
+
+def index_topk_paged(q_idx, w, key_pool, page_size: int, page_table, cand_len, k: int, max_cand: int, scores=None,
+                     workspace=None, out=None):
+    """chs_index_topk over a paged key pool (chs_index_topk_paged). q_idx: [B, Hi, dim] bf16;
+    w: [B, Hi] fp32; key_pool: [pool_rows, dim] bf16; page_table: [B, pt_stride] int32;
+    cand_len: [B] int64; scores: [B, max_cand] fp32 or None. Returns (topk [B, k] int32, scores)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(key_pool, "key_pool", torch.bfloat16, 2)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(cand_len, "cand_len", torch.int64, 1)
+    B, nh, dim = q_idx.shape
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 2)
+    if workspace is None:
+        workspace = index_topk_workspace(B, max_cand, k, q_idx.device)
+    if out is None:
+        out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+    _need(out, "topk", torch.int32, 2)
+    _check(lib().chs_index_topk_paged(CHS_BF16, B, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(key_pool),
+                                      key_pool.shape[0] // page_size, page_size, _ptr(page_table), page_table.shape[1],
+                                      _ptr(cand_len), int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
+                                      workspace.numel(), _stream()), "chs_index_topk_paged")
+    return out, scores

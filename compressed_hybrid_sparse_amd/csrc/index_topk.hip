@@ -127,9 +127,25 @@ struct Args {
   float* scores;        // caller's packed array, or NULL -> workspace
   const float* kscale;  // [cu[batch]] per-row scales of FP8 keys (NULL otherwise)
   Workspace ws;
+  // Paged key pool (NULL: keys packed by cu). Candidate j of sequence b is pool row
+  // pt[b * pt_stride + j / 2^shift] * 2^shift + j mod 2^shift; cand_len[b] candidates; scores at
+  // b * max_cand + j of the caller's array.
+  const int32_t* pt;
+  const int64_t* cand_len;
+  int32_t pt_stride, shift;
+  int64_t pool_pages;
 };
 
 __device__ __forceinline__ int64_t cand_count(const Args& a, int b, int64_t* base) {
+  if (a.cand_len) {
+    int64_t n = a.cand_len[b];
+    const int64_t cap = (int64_t)a.pt_stride << a.shift;
+    if (n > cap) n = cap;
+    if (n > a.max_cand) n = a.max_cand;
+    if (n < 0) n = 0;
+    *base = (int64_t)b * a.max_cand;
+    return n;
+  }
   const int64_t c0 = a.cu[b];
   int64_t n = a.cu[b + 1] - c0;
   if (n > a.max_cand) n = a.max_cand;
@@ -510,7 +526,9 @@ constexpr int mfma_tiles(int d, int es) { return 8192 / (16 * d * es) > 2 ? 8192
 // The result leaves lane (g, c) with the dots of heads 4g .. 4g + 3 against key c; ReLU,
 // weights and (fp8) the row scale follow, summed over the 4 lane rows when there are more
 // than 4 heads. A wave covers TILES tiles (8 KiB of keys; 2 tiles = one group at least).
-template <typename ET, int D, int NH4>
+// PAGED: the keys come from a paged pool; a wave's keys (at most 64) lie in one page (pages of at
+// least 64 rows), so one page-table read, issued with the query loads, places them.
+template <typename ET, int D, int NH4, bool PAGED = false>
 __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   constexpr int ES = (int)sizeof(ET);                  // 2: bf16 keys, 1: E4M3 keys
@@ -531,6 +549,13 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
   const int64_t key0 = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TILES * 16;
   if (key0 >= n) return;                               // no barriers follow
+  static_assert(!PAGED || (ES == 2 && TILES * 16 <= 64), "paged keys: bf16, at most 64 keys per wave");
+  int64_t krow0 = c0 + key0;                           // storage row of key0; rows follow it
+  if (PAGED) {
+    const int64_t p = a.pt[(int64_t)b * a.pt_stride + (key0 >> a.shift)];
+    const int64_t pc = p < 0 || p >= a.pool_pages ? 0 : p;   // out of the pool: page 0 is read
+    krow0 = (pc << a.shift) | (key0 & (((int64_t)1 << a.shift) - 1));
+  }
   // Queries (A): MFMA t, lane (g, c): head c, the 8 channels this lane supplies.
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.nh + min(c, a.nh - 1)) * D;
   u32x4 qv[T];
@@ -546,14 +571,14 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
     wv[r] = a.w[(size_t)b * a.nh + min(h, a.nh - 1)];
   }
   __builtin_amdgcn_sched_barrier(0);                   // query loads go out (and return) first
-  const char* kb = static_cast<const char*>(a.keys) + (size_t)c0 * ROWB;
+  const char* kb = static_cast<const char*>(a.keys) + (size_t)krow0 * ROWB;
   const int rr = lane / LPR, sc = lane % LPR;          // this lane's row and 16-byte chunk in a load
   u32x4 kv[LOADS];
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     int64_t row = key0 + u * RPI + rr;
     if (row > n - 1) row = n - 1;
-    kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + row * ROWB + 16 * sc));
+    kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (row - key0) * ROWB + 16 * sc));
   }
   float ks[TILES];
   if (kScaled) {
@@ -1134,8 +1159,12 @@ bool launch_scores_mfma(int32_t batch, int32_t head_dim, Args* a, hipStream_t s)
   const dim3 grid((unsigned)((a->max_cand + per_block - 1) / per_block), (unsigned)batch);
   a->gs = kGroup;
   const bool wide = a->nh > 4;
-#define CHS_MFMA(DD)                                                                              \
-  if (wide) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 4>), grid, dim3(kThreads), 0, s, *a);   \
+  constexpr bool kBf16 = sizeof(ET) == 2;
+  const bool paged = kBf16 && a->pt != nullptr;
+#define CHS_MFMA(DD)                                                                                    \
+  if (paged && wide) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 4, kBf16>), grid, dim3(kThreads), 0, s, *a); \
+  else if (paged) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 1, kBf16>), grid, dim3(kThreads), 0, s, *a);   \
+  else if (wide) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 4>), grid, dim3(kThreads), 0, s, *a);           \
   else hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 1>), grid, dim3(kThreads), 0, s, *a);
   switch (head_dim) {
     case 64: CHS_MFMA(64) break;
@@ -1208,6 +1237,7 @@ chs_status topk_setup(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t h
   a->q = q_idx; a->w = w; a->keys = k_idx; a->cu = cu_cand; a->max_cand = max_cand;
   a->nh = n_heads; a->nvec = nvec; a->k = k; a->scores = scores; a->ws = ws; a->kscale = nullptr;
   a->gs = kGroup;
+  a->pt = nullptr; a->cand_len = nullptr; a->pt_stride = 0; a->shift = 0; a->pool_pages = 0;
   return CHS_OK;
 }
 
@@ -1277,6 +1307,7 @@ extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t
   a.q = q_idx; a.w = w; a.keys = k_idx; a.cu = cu_cand; a.max_cand = max_cand;
   a.nh = n_heads; a.nvec = head_dim / 16; a.k = k; a.scores = scores; a.ws = ws; a.kscale = k_scale;
   a.gs = kGroup;
+  a.pt = nullptr; a.cand_len = nullptr; a.pt_stride = 0; a.shift = 0; a.pool_pages = 0;
   int lpc = 2;
   while (lpc < a.nvec) lpc *= 2;                        // one 16-byte key vector per lane
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1287,6 +1318,39 @@ extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t
       const dim3 grid((unsigned)((max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
       launch_scores<uint8_t>(grid, s, a, lpc);
     }
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
+  return launch_status();
+}
+
+extern "C" chs_status chs_index_topk_paged(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
+                                           int32_t k, const void* q_idx, const float* w, const void* key_pool,
+                                           int64_t pool_pages, int32_t page_size, const int32_t* page_table,
+                                           int32_t pt_stride, const int64_t* cand_len, int64_t max_cand,
+                                           float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  using namespace chs;
+  if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
+  if (batch < 1 || batch > 65535 || k < 1 || k > kMaxK || max_cand < 0 || max_cand >= (1LL << 31) ||
+      n_heads < 1 || n_heads > 16 || head_dim < 8 || head_dim > 512 || page_size < 64 || page_size > 65536 ||
+      (page_size & (page_size - 1)) != 0 || pt_stride < 1 || pool_pages < 1)
+    return CHS_ERR_SHAPE;
+  if (max_cand > kMaxCand) return CHS_ERR_UNSUPPORTED;
+  if (dtype != CHS_BF16 || (head_dim != 64 && head_dim != 128 && head_dim != 256)) return CHS_ERR_UNSUPPORTED;
+  if (!q_idx || !w || !key_pool || !page_table || !cand_len || !topk || !workspace) return CHS_ERR_NULL;
+  Workspace ws;
+  const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  Args a;
+  a.q = q_idx; a.w = w; a.keys = key_pool; a.cu = nullptr; a.max_cand = max_cand;
+  a.nh = n_heads; a.nvec = head_dim / 8; a.k = k; a.scores = scores; a.ws = ws; a.kscale = nullptr;
+  a.gs = kGroup;
+  a.pt = page_table; a.cand_len = cand_len; a.pt_stride = pt_stride; a.shift = __builtin_ctz((unsigned)page_size);
+  a.pool_pages = pool_pages;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_cand > 0) {
+    launch_scores_mfma<uint16_t>(batch, head_dim, &a, s);
     if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   }
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);

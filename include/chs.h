@@ -249,6 +249,20 @@ chs_status chs_decode_attn_paged(chs_dtype dtype, int32_t batch, int32_t n_heads
                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* chs_index_topk_paged: chs_index_topk with the index keys in a paged pool, addressed as above
+ * (candidate j of sequence b at pool row page_table[b * pt_stride + j / page_size] * page_size +
+ * j mod page_size; cand_len[b] candidates, capped at max_cand and pt_stride * page_size). scores, if
+ * not NULL, is [batch, max_cand] fp32 with sequence b's scores from b * max_cand. The workspace is
+ * chs_index_topk_workspace_size(batch, max_cand, k). Supported: CHS_BF16 keys, head_dim in
+ * {64, 128, 256}, 1..16 heads, page_size a power of two >= 64 (a wave's keys then lie in one page);
+ * other shapes return CHS_ERR_UNSUPPORTED. A page outside [0, pool_pages) reads page 0 (the scores of
+ * its candidates are then unspecified; nothing outside the pool is read). */
+chs_status chs_index_topk_paged(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                                const void* q_idx, const float* w, const void* key_pool, int64_t pool_pages,
+                                int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                                const int64_t* cand_len, int64_t max_cand, float* scores, int32_t* topk,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* chs_append_paged: chs_append with the window, the gate ring and the compressed pool paged as
  * above (n_tokens, swa_len, comp_count as in chs_append; comp_count counts entries, so it can feed
  * comp_len of chs_decode_attn_paged directly). */

@@ -102,6 +102,26 @@ def test_append_paged_validation(kw, code):
     assert append_paged(**kw) == code
 
 
+def topk_paged(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, pool=FAKE, npool=100, P=64, pt=FAKE, stride=8,
+               cl=FAKE, maxc=1000, s=FAKE, out=FAKE, ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_index_topk_workspace_size(batch, maxc, k)
+    return L.chs_index_topk_paged(dt, batch, nh, dim, k, q, w, pool, npool, P, pt, stride, cl, maxc, s, out, ws, wsb,
+                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), DTYPE), (dict(batch=0), SHAPE), (dict(k=0), SHAPE), (dict(nh=17), SHAPE), (dict(P=32), SHAPE),
+    (dict(P=96), SHAPE), (dict(stride=0), SHAPE), (dict(npool=0), SHAPE), (dict(maxc=-1), SHAPE),
+    (dict(dt=0), UNSUP), (dict(dim=96), UNSUP), (dict(dim=512), UNSUP), (dict(q=None), NULL), (dict(w=None), NULL),
+    (dict(pool=None), NULL), (dict(pt=None), NULL), (dict(cl=None), NULL), (dict(out=None), NULL),
+    (dict(ws=None), NULL), (dict(wsb=16), WS),
+])
+def test_index_topk_paged_validation(kw, code):
+    assert topk_paged(**kw) == code
+
+
 def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
          ws=FAKE, wsb=None):
     L = chs.lib()

@@ -224,3 +224,121 @@ def test_paged_decode_loop_dense():
         o_ref, l_ref = oracle.decode_step(q[0], X[:N], W, cref, None, d ** -0.5)
         assert_bf16_path(out[0].cpu().numpy(), o_ref, f"step {s}")
         assert_lse(lse[0].cpu().numpy(), l_ref, f"step {s} lse")
+
+
+@pytest.mark.parametrize("nh,dim,P,lens,k", [
+    (4, 128, 64, [5000], 512),
+    (4, 128, 128, [1000, 0, 7000, 3], 512),
+    (16, 64, 64, [2500, 640], 100),
+    (2, 256, 1024, [1777], 300),
+    (8, 128, 256, [900, 64], 1000),
+])
+def test_paged_index_topk_matches_oracle_and_contiguous(nh, dim, P, lens, k):
+    print(f"case: paged index top-k nh={nh} dim={dim} P={P} lens={lens} k={k}", flush=True)
+    rng = np.random.default_rng(nh * 100 + dim + P)
+    B = len(lens)
+    bf = torch.bfloat16
+    logical = [_round(rng.standard_normal((n, dim)) * 3, bf) for n in lens]
+    pool, pt = _paged_pool(rng, logical, P, dim, bf)
+    q = _round(rng.standard_normal((B, nh, dim)), bf)
+    w = rng.random((B, nh)).astype(np.float32)
+    max_cand = max(lens)
+    scores = torch.full((B, max_cand), -5.0, dtype=torch.float32, device=dev())
+    topk, _ = chs.index_topk_paged(_t(q, bf), _t(w, torch.float32), _t(pool, bf), P, torch.from_numpy(pt).to(dev()),
+                                   torch.tensor(lens, dtype=torch.int64, device=dev()), k, max_cand, scores)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64, device=dev())
+    keys_c = _t(np.concatenate(logical) if sum(lens) else np.zeros((1, dim)), bf)
+    sc_c = torch.empty(max(sum(lens), 1), dtype=torch.float32, device=dev())
+    topk_c, _ = chs.index_topk(_t(q, bf), _t(w, torch.float32), keys_c, cu, k, max_cand, sc_c)
+    torch.cuda.synchronize()
+    assert torch.equal(topk, topk_c), "paged and contiguous top-k differ"
+    sg, cuh = scores.cpu().numpy(), cu.cpu().numpy()
+    for b, n in enumerate(lens):
+        assert np.array_equal(sg[b, :n], sc_c[cuh[b]:cuh[b + 1]].cpu().numpy()), f"scores of sequence {b}"
+        assert np.all(sg[b, n:] == -5.0), "scores written past the sequence"
+        ref = oracle.index_scores(q[b], w[b], oracle.paged_rows(pool, pt[b], P, n))
+        if n:
+            assert np.all(np.abs(sg[b, :n] - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+        assert np.array_equal(topk[b].cpu().numpy(), oracle.topk(sg[b, :n], k))
+
+
+def test_paged_decode_loop_c4():
+    # The whole step over paged pools, batch 2: appends of the KV row and of the index key (one page
+    # table for both pools: they share the entry numbering), the paged top-k and the paged attention;
+    # comp_count feeds comp_len / cand_len.
+    print("case: paged C4 decode loop", flush=True)
+    rng = np.random.default_rng(41)
+    bf = torch.bfloat16
+    m, W, R, P, d, H, dI, nhI, k = 4, 32, 8, 64, 128, 16, 64, 2, 32
+    n0 = [300, 517]
+    steps = 9
+    B = len(n0)
+    N1 = [n + steps for n in n0]
+    X = [_round(rng.standard_normal((n, d)), bf) for n in N1]
+    Z = [_round(rng.standard_normal((n, d)) * 2, bf) for n in N1]
+    XI = [rng.integers(-8, 9, (n, dI)).astype(np.float32) for n in N1]   # equal-weight pooling: exact keys
+    Bkv = (rng.standard_normal((m, d)) * 0.1).astype(np.float32)
+    BI = np.zeros((m, dI), np.float32)
+    caps = [n // m + 2 for n in N1]
+    _, pt = _paged_pool(rng, [np.zeros((c, 1), np.float32) for c in caps], P, 1, torch.float32)
+    pool_rows = (pt.max() + 1 + 3) * P
+    kv_pool = np.zeros((pool_rows, d), np.float32)
+    key_pool = np.zeros((pool_rows, dI), np.float32)
+    for b in range(B):
+        pre = oracle.store(oracle.compress(X[b][:n0[b]], Z[b][:n0[b]], Bkv, m, np.array([0, n0[b]])), True)
+        prek = oracle.store(oracle.compress(XI[b][:n0[b]], np.zeros((n0[b], dI), np.float32), BI, m,
+                                            np.array([0, n0[b]])), True)
+        for j in range(n0[b] // m):
+            kv_pool[pt[b, j // P] * P + j % P] = pre[j]
+            key_pool[pt[b, j // P] * P + j % P] = prek[j]
+    swa_page = np.array([3, 1], np.int32)
+    swa_pool = np.zeros((4, W, d), np.float32)
+    swaI_pool = np.zeros((4, 8, dI), np.float32)
+    ring = np.zeros((4 * R, d), np.float32)
+    ringI = np.zeros((4 * R, dI), np.float32)
+    for b in range(B):
+        img, wr = oracle.ring_image(X[b][:n0[b]], W)
+        swa_pool[swa_page[b]][wr] = img[wr]
+        img, wr = oracle.ring_image(Z[b][:n0[b]], R)
+        ring[swa_page[b] * R:(swa_page[b] + 1) * R][wr] = img[wr]
+        img, wr = oracle.ring_image(XI[b][:n0[b]], 8)
+        swaI_pool[swa_page[b]][wr] = img[wr]
+    t = {name: _t(a, bf) for name, a in
+         dict(kv=kv_pool, key=key_pool, swa=swa_pool, swaI=swaI_pool, ring=ring, ringI=ringI).items()}
+    n_kv = torch.tensor(n0, dtype=torch.int64, device=dev())
+    n_ix = n_kv.clone()
+    sl = torch.zeros(B, dtype=torch.int32, device=dev())
+    clen = torch.tensor([n // m for n in n0], dtype=torch.int64, device=dev())
+    page_t, pt_t = torch.from_numpy(swa_page).to(dev()), torch.from_numpy(pt).to(dev())
+    bkv, bix = _t(Bkv, torch.float32), _t(BI, torch.float32)
+    max_cand = max(caps)
+    for s in range(steps):
+        xs = np.stack([X[b][n0[b] + s] for b in range(B)])
+        zs = np.stack([Z[b][n0[b] + s] for b in range(B)])
+        xis = np.stack([XI[b][n0[b] + s] for b in range(B)])
+        chs.append_paged(_t(xs, bf), _t(zs, bf), bkv, m, n_kv, t["swa"], page_t, t["ring"], t["kv"], P, pt_t,
+                         swa_len=sl, comp_count=clen)
+        chs.append_paged(_t(xis, bf), torch.zeros(B, dI, dtype=bf, device=dev()), bix, m, n_ix, t["swaI"], page_t,
+                         t["ringI"], t["key"], P, pt_t)
+        q = _round(rng.standard_normal((B, H, d)), bf)
+        qI = _round(rng.standard_normal((B, nhI, dI)), bf)
+        w = rng.random((B, nhI)).astype(np.float32)
+        scores = torch.zeros((B, max_cand), dtype=torch.float32, device=dev())
+        topk, _ = chs.index_topk_paged(_t(qI, bf), _t(w, torch.float32), t["key"], P, pt_t, clen, k, max_cand, scores)
+        out, lse = chs.decode_attn_paged(_t(q, bf), t["swa"], page_t, sl, t["kv"], P, pt_t, clen, topk, d ** -0.5,
+                                         max_cand)
+        torch.cuda.synchronize()
+        for b in range(B):
+            N = n0[b] + s + 1
+            G = N // m
+            assert clen[b].item() == G and sl[b].item() == min(N, W)
+            kref = oracle.store(oracle.compress(XI[b][:N], np.zeros((N, dI), np.float32), BI, m, np.array([0, N])), True)
+            sref = oracle.index_scores(qI[b], w[b], kref)
+            sg = scores[b, :G].cpu().numpy()
+            assert np.all(np.abs(sg - sref) <= 1e-5 * np.abs(sref) + 1e-6 * np.abs(sref).max()), f"step {s} b={b}"
+            sel = topk[b].cpu().numpy()
+            assert np.array_equal(sel, oracle.topk(sg, k)), f"step {s} b={b}: top-k"
+            cref = oracle.store(oracle.compress(X[b][:N], Z[b][:N], Bkv, m, np.array([0, N])), True)
+            o_ref, l_ref = oracle.decode_step(q[b], X[b][:N], W, cref, sel, d ** -0.5)
+            assert_bf16_path(out[b].cpu().numpy(), o_ref, f"step {s} b={b}: attention")
+            assert_lse(lse[b].cpu().numpy(), l_ref, f"step {s} b={b}: lse")
