@@ -19,7 +19,8 @@ roofline on a 64-row batch, the same decode step over FP8 (E4M3) index keys and 
 per-row scales (chs_index_topk_fp8 + chs_decode_attn_fp8; a component, not the headline), the
 full per-token step with chs_append of the new token's KV row and index key (window ring, gate
 state ring, a pooled entry every 4th token) ahead of the top-k and the attention, chs_append
-alone on a 64-sequence batch (C4 and C128), plus
+alone on a 64-sequence batch (C4 and C128), the step over paged pools (index keys and entries in
+64-row pages through a permuted page table), plus
 the roofline of the dominant kernel and the CPU oracle timed on this host (a reported baseline,
 not a target).
 
@@ -329,6 +330,26 @@ def main():
     app4_ms, app4_bytes = append_batch(4, 8)
     app128_ms, app128_bytes = append_batch(128, 128)
 
+    # The same step over paged pools: index keys and compressed entries in pages of 64 rows, the
+    # page table a seeded random permutation of the pages (scattered, as a pool allocator leaves
+    # them), the window page 0 of a one-page window pool. The key copies double as the pools.
+    PG = 64
+    perm = torch.randperm(G // PG, generator=torch.Generator().manual_seed(3)).to(torch.int32)
+    pt_paged = perm[None, :].contiguous().to(dev)
+    len_paged = torch.tensor([G], dtype=torch.int64, device=dev)
+    swa_page0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    scores2d = scores.view(1, G)
+
+    def decode_paged(i):
+        chs.index_topk_paged(inp["q_idx"], inp["w"], keys[i % nk], PG, pt_paged, len_paged, k, G, scores2d, ws_topk,
+                             topk)
+        chs.decode_attn_paged(inp["q"], inp["swa_kv"], swa_page0, inp["swa_len"], comp, PG, pt_paged, len_paged, topk,
+                              scale, G, ws_attn, out, lse)
+
+    for i in range(nk):
+        decode_paged(i)
+    paged_ms = graph_loop_ms(decode_paged, nk)
+
     # Per-call breakdown (events around each call; each event adds a little to what it brackets).
     bd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -431,6 +452,10 @@ def main():
                 "call": "chs_append (KV) + chs_append (index key) + chs_index_topk + chs_decode_attn",
                 "graph_median": None if app_step_ms is None else round(median(app_step_ms) * 1e3, 2),
                 "tokens_appended": app_added},
+            "decode_step_paged_us": {
+                "value_source": "graph replay", "call": "chs_index_topk_paged + chs_decode_attn_paged",
+                "page_rows": PG,
+                "graph_median": None if paged_ms is None else round(median(paged_ms) * 1e3, 2)},
             "append_us": {
                 "value_source": "graph replay", "batch": 64, "d": d,
                 "c4_median": None if app4_ms is None else round(median(app4_ms) * 1e3, 2),
