@@ -20,7 +20,8 @@ per-row scales (chs_index_topk_fp8 + chs_decode_attn_fp8; a component, not the h
 full per-token step with chs_append of the new token's KV row and index key (window ring, gate
 state ring, a pooled entry every 4th token) ahead of the top-k and the attention, chs_append
 alone on a 64-sequence batch (C4 and C128), the step over paged pools (index keys and entries in
-64-row pages through a permuted page table), plus
+64-row pages through a permuted page table), the working-set gather of the 512 selected entries from
+a mirror in HBM or in pinned host memory (chs_gather_selected), plus
 the roofline of the dominant kernel and the CPU oracle timed on this host (a reported baseline,
 not a target).
 
@@ -390,6 +391,18 @@ def main():
                        100)
     t64_ms = time_calls(lambda i: chs.topk_from_scores(rows64[(i % 8) * 64 * G:(i % 8 + 1) * 64 * G], cu64, 512, G,
                                                        ws64, tk64), 50)
+    # HiSparse-style working-set gather of the step's 512 selected entries (1 KiB rows) from a mirror
+    # of the 262,144 compressed entries held in HBM or in pinned host memory (read over PCIe).
+    work_rows = torch.empty(k, d, dtype=torch.bfloat16, device=dev)
+    work_tk = torch.empty(1, k, dtype=torch.int32, device=dev)
+    chs.index_topk(inp["q_idx"], inp["w"], keys[0], inp["cu_groups"], k, G, scores, ws_topk, topk)
+    host_mirror = torch.empty(G, d, dtype=torch.bfloat16, pin_memory=True)
+    host_mirror.copy_(comp)
+    cu_ws = torch.tensor([0, k], dtype=torch.int64, device=dev)
+    gdev_ms = graph_loop_ms(lambda i: chs.gather_selected(comp, inp["cu_groups"], topk, work=work_rows,
+                                                          work_topk=work_tk, cu_work=cu_ws), 8)
+    ghost_ms = graph_loop_ms(lambda i: chs.gather_selected(host_mirror, inp["cu_groups"], topk, work=work_rows,
+                                                           work_topk=work_tk, cu_work=cu_ws), 8)
     if args.calib_copy:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
         bcopy = torch.empty_like(a)
@@ -456,6 +469,11 @@ def main():
                 "value_source": "graph replay", "call": "chs_index_topk_paged + chs_decode_attn_paged",
                 "page_rows": PG,
                 "graph_median": None if paged_ms is None else round(median(paged_ms) * 1e3, 2)},
+            "gather_selected_us": {
+                "value_source": "graph replay", "rows": k, "row_bytes": d * 2,
+                "from_hbm_median": None if gdev_ms is None else round(median(gdev_ms) * 1e3, 2),
+                "from_pinned_host_median": None if ghost_ms is None else round(median(ghost_ms) * 1e3, 2),
+                "host_GBps": None if ghost_ms is None else round(k * d * 2 / (median(ghost_ms) * 1e-3) / 1e9, 2)},
             "append_us": {
                 "value_source": "graph replay", "batch": 64, "d": d,
                 "c4_median": None if app4_ms is None else round(median(app4_ms) * 1e3, 2),

@@ -22,7 +22,7 @@ _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE
 EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
-           "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged")
+           "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -64,11 +64,12 @@ def lib():
                                             _i64, _i32, _p, _i32, _p, _p, _i64, _p, _p, _p, _sz, _p]
         L.chs_append_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _i64, _p, _p,
                                        _p, _i64, _i32, _p, _i32, _p, _p]
+        L.chs_gather_selected.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
-                   "chs_index_topk_paged"):
+                   "chs_index_topk_paged", "chs_gather_selected"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -420,3 +421,34 @@ def index_topk_paged(q_idx, w, key_pool, page_size: int, page_table, cand_len, k
                                       _ptr(cand_len), int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
                                       workspace.numel(), _stream()), "chs_index_topk_paged")
     return out, scores
+
+
+# ---------------------------------------------------------------- working-set gather
+def gather_selected(mirror, cu_comp, topk, cache=None, resident=None, work=None, work_topk=None, cu_work=None):
+    """The selected entries of each sequence gathered into a dense device working set
+    (chs_gather_selected). mirror: [G, d] on the device, or a pinned host tensor (pin_memory=True);
+    cu_comp: [B+1] int64; topk: [B, k] int32; cache: [rows, d] and resident: [G] int32 (device), both or
+    neither. Returns (work [B*k, d], work_topk [B, k] int32, cu_work [B+1] int64 = {0, k, 2k, ..}; pass
+    cu_work to reuse one)."""
+    if mirror.dim() != 2 or not mirror.is_contiguous():
+        raise ValueError("mirror must be a contiguous 2-D tensor")
+    on_host = not mirror.is_cuda
+    if on_host and not mirror.is_pinned():
+        raise ValueError("a host mirror must be pinned (pin_memory=True)")
+    _need(cu_comp, "cu_comp", torch.int64, 1)
+    _need(topk, "topk", torch.int32, 2)
+    B, k = topk.shape
+    d = mirror.shape[1]
+    if cache is not None or resident is not None:
+        _need(cache, "cache", mirror.dtype, 2)
+        _need(resident, "resident", torch.int32, 1)
+    if work is None:
+        work = torch.empty(B * k, d, dtype=mirror.dtype, device=topk.device)
+    if work_topk is None:
+        work_topk = torch.empty(B, k, dtype=torch.int32, device=topk.device)
+    _check(lib().chs_gather_selected(_dtype_code(mirror), B, d, k, _ptr(mirror), int(on_host), _ptr(cu_comp), _ptr(topk),
+                                     _ptr(cache), _ptr(resident), 0 if cache is None else cache.shape[0], _ptr(work),
+                                     _ptr(work_topk), _stream()), "chs_gather_selected")
+    if cu_work is None:
+        cu_work = torch.arange(0, (B + 1) * k, k, dtype=torch.int64, device=topk.device)
+    return work, work_topk, cu_work

@@ -273,6 +273,30 @@ chs_status chs_append_paged(chs_dtype dtype, int32_t batch, int32_t d, int32_t m
                             int32_t page_size, const int32_t* page_table, int32_t pt_stride,
                             int64_t* comp_count, void* stream);
 
+/* ---- chs_gather_selected: a HiSparse-style working-set gather --------------------------------
+ * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 3 (HiSparse: each C4 step touches about
+ * 0.2% of the entries, so the full pool can be mirrored in pinned host memory while the GPU keeps a
+ * working set of what each step hits; misses come in from the mirror) and "DeepSeek-V4 本地部署，SGLang
+ * 把活做絕了", HiSparse 把不活躍 KV 甩到 CPU.
+ * For every sequence b and slot i with j = topk[b, i] in [0, G_b), G_b = cu_comp[b+1] - cu_comp[b]:
+ *   work[b*k + i, :] = cache[resident[cu_comp[b] + j], :]  if resident is not NULL and that value is in
+ *                                                           [0, cache_rows),
+ *                    = mirror[cu_comp[b] + j, :]            otherwise;
+ *   work_topk[b, i]  = i; other slots get work_topk = -1 and their work row is left untouched.
+ * chs_decode_attn over (work, cu = {0, k, 2k, ...}, work_topk) is then bit-identical to chs_decode_attn
+ * over (mirror, cu_comp, topk). The residency map and the cache are the caller's (its eviction policy
+ * decides them); the call only reads them.
+ * mirror       : [cu_comp[batch], d] of `dtype`; device memory, or, with mirror_on_host = 1, pinned host
+ *                memory allocated by the HIP runtime (hipHostMalloc; torch's pin_memory), read over PCIe.
+ *                Host memory the runtime cannot map returns CHS_ERR_UNSUPPORTED before any launch.
+ * cache        : [cache_rows, d] device rows, and resident: [cu_comp[batch]] int32, both or neither.
+ * work         : [batch * k, d] device; work_topk: [batch, k] int32.
+ * Ranges: 1 <= batch <= 65535; 1 <= k <= 2048; 1 <= d <= 4096 with d*elem_size % 16 == 0. */
+chs_status chs_gather_selected(chs_dtype dtype, int32_t batch, int32_t d, int32_t k, const void* mirror,
+                               int32_t mirror_on_host, const int64_t* cu_comp, const int32_t* topk,
+                               const void* cache, const int32_t* resident, int64_t cache_rows, void* work,
+                               int32_t* work_topk, void* stream);
+
 /* ---- chs_decode_attn_fp8: chs_decode_attn over an FP8 KV cache ------------------------------
  * Source: as chs_decode_attn, with "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 4.3 部署配置
  * 建议 (an fp8 KV cache) and "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (attention

@@ -122,6 +122,27 @@ def test_index_topk_paged_validation(kw, code):
     assert topk_paged(**kw) == code
 
 
+def gather(dt=1, batch=1, d=512, k=512, mirror=FAKE, host=0, cu=FAKE, tk=FAKE, cache=None, res=None, rows=0,
+           work=FAKE, wtk=FAKE):
+    return chs.lib().chs_gather_selected(dt, batch, d, k, mirror, host, cu, tk, cache, res, rows, work, wtk, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), DTYPE), (dict(batch=0), SHAPE), (dict(k=0), SHAPE), (dict(k=2049), SHAPE), (dict(d=0), SHAPE),
+    (dict(d=12), SHAPE), (dict(rows=-1), SHAPE), (dict(mirror=None), NULL), (dict(cu=None), NULL),
+    (dict(tk=None), NULL), (dict(work=None), NULL), (dict(wtk=None), NULL), (dict(res=FAKE), NULL),
+])
+def test_gather_selected_validation(kw, code):
+    assert gather(**kw) == code
+
+
+def test_gather_binding_refuses_unpinned_host_mirror():
+    # The binding checks a host mirror is pinned before anything reaches the library or the GPU.
+    import torch
+    with pytest.raises(ValueError, match="pinned"):
+        chs.gather_selected(torch.zeros(4, 8, dtype=torch.bfloat16), None, None)
+
+
 def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
          ws=FAKE, wsb=None):
     L = chs.lib()
