@@ -17,8 +17,9 @@ stream-launched figure is reported beside it), median over repetitions. The line
 bandwidth, the standalone top-512-of-262144 latency (one row) and the fraction of the HBM
 roofline on a 64-row batch, the same decode step over FP8 (E4M3) index keys and KV cache with
 per-row scales (chs_index_topk_fp8 + chs_decode_attn_fp8; a component, not the headline), the
-full per-token step with chs_append of the new token's KV row and index key (window ring, gate
-state ring, a pooled entry every 4th token) ahead of the top-k and the attention, chs_append
+full per-token step with the new token's KV row and index key appended in one chs_append_multi
+launch (window rings, gate state rings, a pooled entry every 4th token) ahead of the top-k and the
+attention, chs_append
 alone on a 64-sequence batch (C4 and C128), the step over paged pools (index keys and entries in
 64-row pages through a permuted page table), the working-set gather of the 512 selected entries from
 a mirror in HBM or in pinned host memory (chs_gather_selected), plus
@@ -286,11 +287,15 @@ def main():
     page0 = torch.zeros(1, dtype=torch.int32, device=dev)
     start0 = torch.zeros(1, dtype=torch.int64, device=dev)
 
+    kv_stream = chs.append_stream(x_tok, z_tok, inp["bias"], n_kv, swa_app, ring_kv, comp, ring_page=page0,
+                                  comp_start=start0, ring_size=8, swa_len=swa_len_app, comp_count=cu_app[1:])
+    ix_streams = [chs.append_stream(xi_tok, zi_tok, bias_i, n_ix, swa_i, ring_i, kb, ring_page=page0,
+                                    comp_start=start0, ring_size=8) for kb in keys]
+
     def decode_append(i):
+        # Both compressor streams (the KV row and the index key) in one chs_append_multi launch.
         kb = keys[i % nk]
-        chs.append(x_tok, z_tok, inp["bias"], layer.m, n_kv, swa_app, ring_kv, page0, comp, start0, ring_size=8,
-                   swa_len=swa_len_app, comp_count=cu_app[1:])
-        chs.append(xi_tok, zi_tok, bias_i, layer.m, n_ix, swa_i, ring_i, page0, kb, start0, ring_size=8)
+        chs.append_multi(layer.m, [kv_stream, ix_streams[i % nk]])
         chs.index_topk(inp["q_idx"], inp["w"], kb, cu_app, k, G, scores, ws_topk, topk)
         chs.decode_attn(inp["q"], swa_app, swa_len_app, comp, cu_app, topk, scale, G, ws_attn, out, lse)
 
@@ -462,7 +467,7 @@ def main():
                 round(step_fp8_bytes / (median(fp8_graph_ms) * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)},
             "decode_step_with_append_us": {
                 "value_source": "graph replay",
-                "call": "chs_append (KV) + chs_append (index key) + chs_index_topk + chs_decode_attn",
+                "call": "chs_append_multi (KV row + index key, one launch) + chs_index_topk + chs_decode_attn",
                 "graph_median": None if app_step_ms is None else round(median(app_step_ms) * 1e3, 2),
                 "tokens_appended": app_added},
             "decode_step_paged_us": {

@@ -22,10 +22,23 @@ _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE
 EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compress",
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
-           "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected")
+           "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
+           "chs_append_multi")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+
+class AppendStream(ctypes.Structure):
+    """chs_append_stream: one compressor stream of chs_append_multi (field for field as in chs.h)."""
+    _fields_ = [("d", ctypes.c_int32), ("window", ctypes.c_int32), ("ring_size", ctypes.c_int32),
+                ("x_new", ctypes.c_void_p), ("z_new", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("n_tokens", ctypes.c_void_p), ("swa_kv", ctypes.c_void_p), ("swa_len", ctypes.c_void_p),
+                ("gate_ring", ctypes.c_void_p), ("ring_page", ctypes.c_void_p), ("ring_pages", ctypes.c_int64),
+                ("comp_kv", ctypes.c_void_p), ("comp_start", ctypes.c_void_p), ("comp_rows", ctypes.c_int64),
+                ("comp_count", ctypes.c_void_p), ("swa_page", ctypes.c_void_p), ("swa_pages", ctypes.c_int64),
+                ("page_table", ctypes.c_void_p), ("pt_stride", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("pool_pages", ctypes.c_int64)]
 
 
 class ChsError(RuntimeError):
@@ -64,12 +77,13 @@ def lib():
                                             _i64, _i32, _p, _i32, _p, _p, _i64, _p, _p, _p, _sz, _p]
         L.chs_append_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _i64, _p, _p,
                                        _p, _i64, _i32, _p, _i32, _p, _p]
+        L.chs_append_multi.argtypes = [ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(AppendStream), _p]
         L.chs_gather_selected.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
-                   "chs_index_topk_paged", "chs_gather_selected"):
+                   "chs_index_topk_paged", "chs_gather_selected", "chs_append_multi"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -452,3 +466,50 @@ def gather_selected(mirror, cu_comp, topk, cache=None, resident=None, work=None,
     if cu_work is None:
         cu_work = torch.arange(0, (B + 1) * k, k, dtype=torch.int64, device=topk.device)
     return work, work_topk, cu_work
+
+
+# ---------------------------------------------------------------- several compressor streams
+def append_stream(x_new, z_new, bias, n_tokens, swa_kv, gate_ring, comp_kv, ring_page=None, comp_start=None,
+                  ring_size=None, swa_len=None, comp_count=None, swa_page=None, page_table=None, page_size=1):
+    """One stream for append_multi: contiguous (ring_page, comp_start; as chs.append) or paged
+    (swa_page, page_table, page_size; as chs.append_paged). Keeps the tensors alive with it."""
+    dt = x_new.dtype
+    _need(x_new, "x_new", dim=2)
+    _need(z_new, "z_new", dt, 2)
+    _need(bias, "bias", torch.float32, 2)
+    _need(n_tokens, "n_tokens", torch.int64, 1)
+    _need(gate_ring, "gate_ring", dt, 2)
+    _need(comp_kv, "comp_kv", dt, 2)
+    B, d = x_new.shape
+    st = AppendStream()
+    st.d = d
+    st.x_new, st.z_new, st.bias, st.n_tokens = (x_new.data_ptr(), z_new.data_ptr(), bias.data_ptr(),
+                                                n_tokens.data_ptr())
+    st.swa_kv, st.gate_ring, st.comp_kv = swa_kv.data_ptr(), gate_ring.data_ptr(), comp_kv.data_ptr()
+    st.swa_len = swa_len.data_ptr() if swa_len is not None else None
+    st.comp_count = comp_count.data_ptr() if comp_count is not None else None
+    if page_table is None:
+        _need(swa_kv, "swa_kv", dt, 3)
+        st.window = swa_kv.shape[1]
+        st.ring_size = int(ring_size if ring_size is not None else gate_ring.shape[0] // B)
+        st.ring_page, st.ring_pages = ring_page.data_ptr(), gate_ring.shape[0] // st.ring_size
+        st.comp_start, st.comp_rows = comp_start.data_ptr(), comp_kv.shape[0]
+    else:
+        _need(swa_kv, "swa_pool", dt, 3)
+        _need(page_table, "page_table", torch.int32, 2)
+        st.window = swa_kv.shape[1]
+        st.swa_page, st.swa_pages = swa_page.data_ptr(), swa_kv.shape[0]
+        st.ring_size = gate_ring.shape[0] // swa_kv.shape[0]
+        st.page_table, st.pt_stride, st.page_size = page_table.data_ptr(), page_table.shape[1], page_size
+        st.pool_pages = comp_kv.shape[0] // page_size
+    st._keep = (x_new, z_new, bias, n_tokens, swa_kv, gate_ring, comp_kv, ring_page, comp_start, swa_len, comp_count,
+                swa_page, page_table)
+    return st
+
+
+def append_multi(m: int, streams):
+    """chs_append_multi: the new token of every sequence appended to each stream (a list of
+    append_stream(...) descriptions) in one launch. Streams share dtype, batch and m."""
+    arr = (AppendStream * len(streams))(*streams)
+    x0 = streams[0]._keep[0]
+    _check(lib().chs_append_multi(_dtype_code(x0), x0.shape[0], m, len(streams), arr, _stream()), "chs_append_multi")

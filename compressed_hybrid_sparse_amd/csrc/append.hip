@@ -30,6 +30,8 @@
 //   count, a second, one-thread-per-sequence kernel advances the counters after them.
 // The new token's row and gate are read from the inputs, not from the rings being written in the
 // same launch, so no thread depends on another's store.
+#include <algorithm>
+
 #include "pool.h"
 
 namespace chs {
@@ -59,6 +61,13 @@ struct AppendArgs {
 };
 
 constexpr int kSplitThreads = 256;
+constexpr int kMaxStreams = 4;
+
+// The compressor streams of one launch (grid dimension y or z): streams share dtype, batch and m
+// and have their own rows, rings, pools and counters.
+struct AppendSet {
+  AppendArgs s[kMaxStreams];
+};
 
 // The counters after a token: n + 1, min(n + 1, W), floor((n + 1) / m).
 __device__ __forceinline__ void advance_counters(const AppendArgs& a, int b, int64_t n) {
@@ -111,9 +120,10 @@ __device__ __forceinline__ int64_t entry_row(const AppendArgs& a, int b, int64_t
   return row < 0 || row >= a.comp_rows ? -1 : row;
 }
 
-// m in {1, 2, 4, 8}: one workgroup per sequence (grid.x = batch).
+// m in {1, 2, 4, 8}: one workgroup per (sequence, stream) (grid.x = batch, grid.y = stream).
 template <typename ET, int M>
-__global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
+__global__ __launch_bounds__(256) void append_small_kernel(AppendSet set) {
+  const AppendArgs& a = set.s[blockIdx.y];
   using V = Vec16<ET>;
   constexpr int N = V::N;
   const int b = blockIdx.x;
@@ -207,9 +217,11 @@ __device__ __forceinline__ void merge_level(PoolState<N>& st) {
   st.merge(omx, osum, oacc);
 }
 
-// Any m: grid (ceil(cpr * nb / 256), batch). Thread (chunk, block) with block = lane % nb.
+// Any m: grid (ceil(max cpr * nb / 256), batch, stream). Thread (chunk, block) with block =
+// lane % nb. Workgroups past the stream's last chunk exit at once (streams differ in width).
 template <typename ET>
-__global__ __launch_bounds__(kSplitThreads) void append_split_kernel(AppendArgs a) {
+__global__ __launch_bounds__(kSplitThreads) void append_split_kernel(AppendSet set) {
+  const AppendArgs& a = set.s[blockIdx.z];
   using V = Vec16<ET>;
   constexpr int N = V::N;
   const int b = blockIdx.y;
@@ -219,6 +231,7 @@ __global__ __launch_bounds__(kSplitThreads) void append_split_kernel(AppendArgs 
   const int m = a.m;
   const int nb = split_blocks(m);
   const int rpt = split_rows_per_thread(m);
+  if ((int64_t)blockIdx.x * kSplitThreads / nb >= cpr) return;   // uniform: the whole workgroup
   const int blk = tid & (nb - 1);
   const int c = (blockIdx.x * kSplitThreads + tid) / nb;
   const int64_t t = read_count(a, b);
@@ -264,26 +277,30 @@ __global__ __launch_bounds__(kSplitThreads) void append_split_kernel(AppendArgs 
   if (blk == 0 && c < cpr) pool_store<ET>(st, static_cast<ET*>(a.comp) + row * d + col);
 }
 
-__global__ __launch_bounds__(256) void append_advance_kernel(AppendArgs a, int32_t batch) {
+__global__ __launch_bounds__(256) void append_advance_kernel(AppendSet set, int32_t batch) {
+  const AppendArgs& a = set.s[blockIdx.y];
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b < batch) advance_counters(a, b, read_count(a, b));
 }
 
+// One launch for all the streams (plus the counter kernel for the split path).
 template <typename ET>
-chs_status launch_append(const AppendArgs& a, int32_t batch, hipStream_t s) {
-  dim3 grid((unsigned)batch);
-  switch (a.m) {
-    case 1: hipLaunchKernelGGL((append_small_kernel<ET, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((append_small_kernel<ET, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_small_kernel<ET, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((append_small_kernel<ET, 8>), grid, dim3(256), 0, s, a); break;
+chs_status launch_append(const AppendSet& set, int n, int32_t batch, hipStream_t s) {
+  const int m = set.s[0].m;
+  dim3 grid((unsigned)batch, (unsigned)n);
+  switch (m) {
+    case 1: hipLaunchKernelGGL((append_small_kernel<ET, 1>), grid, dim3(256), 0, s, set); break;
+    case 2: hipLaunchKernelGGL((append_small_kernel<ET, 2>), grid, dim3(256), 0, s, set); break;
+    case 4: hipLaunchKernelGGL((append_small_kernel<ET, 4>), grid, dim3(256), 0, s, set); break;
+    case 8: hipLaunchKernelGGL((append_small_kernel<ET, 8>), grid, dim3(256), 0, s, set); break;
     default: {
-      const int cpr = a.d / Vec16<ET>::N;
-      const int64_t threads = (int64_t)cpr * split_blocks(a.m);
-      dim3 g2((unsigned)((threads + kSplitThreads - 1) / kSplitThreads), (unsigned)batch);
-      hipLaunchKernelGGL(append_split_kernel<ET>, g2, dim3(kSplitThreads), 0, s, a);
+      int64_t threads = 0;
+      for (int i = 0; i < n; ++i) threads = std::max<int64_t>(threads, (int64_t)(set.s[i].d / Vec16<ET>::N) * split_blocks(m));
+      dim3 g2((unsigned)((threads + kSplitThreads - 1) / kSplitThreads), (unsigned)batch, (unsigned)n);
+      hipLaunchKernelGGL(append_split_kernel<ET>, g2, dim3(kSplitThreads), 0, s, set);
       if (hipGetLastError() != hipSuccess) return CHS_ERR_LAUNCH;
-      hipLaunchKernelGGL(append_advance_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, s, a, batch);
+      hipLaunchKernelGGL(append_advance_kernel, dim3((unsigned)((batch + 255) / 256), (unsigned)n), dim3(256), 0, s,
+                         set, batch);
       break;
     }
   }
@@ -323,10 +340,11 @@ extern "C" chs_status chs_append(chs_dtype dtype, int32_t batch, int32_t d, int3
   if (st != CHS_OK) return st;
   if (ring_pages < 1) return CHS_ERR_SHAPE;
   if (!ring_page || !comp_start) return CHS_ERR_NULL;
-  AppendArgs a{d, m, window, ring_size, ring_pages, comp_rows, x_new, z_new, bias, n_tokens, swa_kv, swa_len,
-               gate_ring, ring_page, comp_kv, comp_start, comp_count, nullptr, 0, nullptr, 0, 0};
+  AppendSet set{};
+  set.s[0] = AppendArgs{d, m, window, ring_size, ring_pages, comp_rows, x_new, z_new, bias, n_tokens, swa_kv, swa_len,
+                        gate_ring, ring_page, comp_kv, comp_start, comp_count, nullptr, 0, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == CHS_BF16 ? launch_append<uint16_t>(a, batch, s) : launch_append<float>(a, batch, s);
+  return dtype == CHS_BF16 ? launch_append<uint16_t>(set, 1, batch, s) : launch_append<float>(set, 1, batch, s);
 }
 
 extern "C" chs_status chs_append_paged(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
@@ -343,9 +361,46 @@ extern "C" chs_status chs_append_paged(chs_dtype dtype, int32_t batch, int32_t d
   if (swa_pages < 1 || page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0 || pt_stride < 1)
     return CHS_ERR_SHAPE;
   if (!swa_page || !page_table) return CHS_ERR_NULL;
-  AppendArgs a{d, m, window, ring_size, swa_pages, pool_pages * (int64_t)page_size, x_new, z_new, bias, n_tokens,
-               swa_pool, swa_len, gate_ring, nullptr, comp_pool, nullptr, comp_count, swa_page, swa_pages,
-               page_table, pt_stride, __builtin_ctz((unsigned)page_size)};
+  AppendSet set{};
+  set.s[0] = AppendArgs{d, m, window, ring_size, swa_pages, pool_pages * (int64_t)page_size, x_new, z_new, bias,
+                        n_tokens, swa_pool, swa_len, gate_ring, nullptr, comp_pool, nullptr, comp_count, swa_page,
+                        swa_pages, page_table, pt_stride, __builtin_ctz((unsigned)page_size)};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == CHS_BF16 ? launch_append<uint16_t>(a, batch, s) : launch_append<float>(a, batch, s);
+  return dtype == CHS_BF16 ? launch_append<uint16_t>(set, 1, batch, s) : launch_append<float>(set, 1, batch, s);
+}
+
+extern "C" chs_status chs_append_multi(chs_dtype dtype, int32_t batch, int32_t m, int32_t n_streams,
+                                       const chs_append_stream* streams, void* stream) {
+  using namespace chs;
+  if (n_streams < 1 || n_streams > kMaxStreams) return CHS_ERR_SHAPE;
+  if (!streams) return CHS_ERR_NULL;
+  AppendSet set{};
+  for (int i = 0; i < n_streams; ++i) {
+    const chs_append_stream& t = streams[i];
+    const bool paged = t.page_table != nullptr;
+    const int64_t page_size = paged ? t.page_size : 1;
+    if (paged && (t.page_size < 1 || t.page_size > 65536 || (t.page_size & (t.page_size - 1)) != 0 ||
+                  t.pt_stride < 1 || t.pool_pages < 0 || t.pool_pages > ((int64_t)1 << 40) / page_size))
+      return CHS_ERR_SHAPE;
+    const int64_t rows = paged ? t.pool_pages * page_size : t.comp_rows;
+    const chs_status st = check_append(dtype, batch, t.d, m, t.window, t.ring_size, t.x_new, t.z_new, t.bias,
+                                       t.n_tokens, t.swa_kv, t.gate_ring, t.comp_kv, rows);
+    if (st != CHS_OK) return st;
+    if (paged) {
+      if (t.swa_pages < 1) return CHS_ERR_SHAPE;
+      if (!t.swa_page) return CHS_ERR_NULL;
+      set.s[i] = AppendArgs{t.d, m, t.window, t.ring_size, t.swa_pages, rows, t.x_new, t.z_new, t.bias, t.n_tokens,
+                            t.swa_kv, t.swa_len, t.gate_ring, nullptr, t.comp_kv, nullptr, t.comp_count, t.swa_page,
+                            t.swa_pages, t.page_table, t.pt_stride, __builtin_ctz((unsigned)t.page_size)};
+    } else {
+      if (t.ring_pages < 1) return CHS_ERR_SHAPE;
+      if (!t.ring_page || !t.comp_start) return CHS_ERR_NULL;
+      set.s[i] = AppendArgs{t.d, m, t.window, t.ring_size, t.ring_pages, rows, t.x_new, t.z_new, t.bias, t.n_tokens,
+                            t.swa_kv, t.swa_len, t.gate_ring, t.ring_page, t.comp_kv, t.comp_start, t.comp_count,
+                            nullptr, 0, nullptr, 0, 0};
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == CHS_BF16 ? launch_append<uint16_t>(set, n_streams, batch, s)
+                           : launch_append<float>(set, n_streams, batch, s);
 }

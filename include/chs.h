@@ -131,6 +131,39 @@ chs_status chs_append(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int3
                       const int64_t* comp_start, int64_t comp_rows, int64_t* comp_count,
                       void* stream);
 
+/* ---- chs_append_multi: chs_append for several compressor streams in one launch --------------
+ * The layer appends each new token to more than one compressed stream: the KV latent's and the
+ * indexer's own ("SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 5: the compressor and the
+ * indexer among the per-step preparation operators). Each stream is described by one
+ * chs_append_stream and gets exactly what chs_append (page_table == NULL) or chs_append_paged
+ * (page_table != NULL) would do for it; one launch covers them all. The streams share dtype, batch
+ * and m; each has its own rows, rings, pools and counters, which must not overlap between streams.
+ * 1 <= n_streams <= 4; `streams` is a host array, read during the call only. */
+typedef struct {
+  int32_t d, window, ring_size;
+  const void* x_new;            /* [batch, d] */
+  const void* z_new;            /* [batch, d] */
+  const float* bias;            /* [m, d] */
+  int64_t* n_tokens;            /* [batch], advanced in place */
+  void* swa_kv;                 /* contiguous: [batch, window, d]; paged: the window pool */
+  int32_t* swa_len;             /* [batch] or NULL */
+  void* gate_ring;              /* the gate rings (pages of ring_size rows) */
+  const int32_t* ring_page;     /* contiguous: [batch] */
+  int64_t ring_pages;           /* contiguous: pages in gate_ring */
+  void* comp_kv;                /* the compressed entries (pool) */
+  const int64_t* comp_start;    /* contiguous: [batch] */
+  int64_t comp_rows;            /* contiguous: rows of comp_kv */
+  int64_t* comp_count;          /* [batch] or NULL */
+  const int32_t* swa_page;      /* paged: [batch] window page (also the gate ring's page) */
+  int64_t swa_pages;            /* paged: pages of the window pool */
+  const int32_t* page_table;    /* paged: [batch, pt_stride]; NULL selects the contiguous form */
+  int32_t pt_stride, page_size; /* paged */
+  int64_t pool_pages;           /* paged: pages of comp_kv */
+} chs_append_stream;
+
+chs_status chs_append_multi(chs_dtype dtype, int32_t batch, int32_t m, int32_t n_streams,
+                            const chs_append_stream* streams, void* stream);
+
 /* ---- chs_index_topk: indexer scores, then exact top-k by radix select ------------------
  * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 2 (Lightning TopK: per-block
  * radix histograms, a threshold, then each block scatters its entries above it; no global

@@ -143,6 +143,39 @@ def test_gather_binding_refuses_unpinned_host_mirror():
         chs.gather_selected(torch.zeros(4, 8, dtype=torch.bfloat16), None, None)
 
 
+def test_append_stream_struct_layout():
+    # Field offsets of chs_append_stream under the C ABI (natural alignment, 8-byte pointers).
+    S = chs.AppendStream
+    assert S.d.offset == 0 and S.ring_size.offset == 8 and S.x_new.offset == 16
+    assert S.ring_pages.offset == 80 and S.comp_count.offset == 112 and S.page_table.offset == 136
+    assert S.pt_stride.offset == 144 and S.page_size.offset == 148 and S.pool_pages.offset == 152
+    assert ctypes.sizeof(S) == 160
+
+
+def test_append_multi_validation():
+    L = chs.lib()
+    arr = (chs.AppendStream * 2)()
+    assert L.chs_append_multi(1, 1, 4, 0, arr, None) == SHAPE
+    assert L.chs_append_multi(1, 1, 4, 5, arr, None) == SHAPE
+    assert L.chs_append_multi(1, 1, 4, 1, None, None) == NULL
+    assert L.chs_append_multi(1, 1, 4, 1, arr, None) == SHAPE            # d = 0
+    for st in arr:
+        st.d, st.window, st.ring_size = 512, 128, 8
+        st.x_new = st.z_new = st.bias = st.n_tokens = st.swa_kv = st.gate_ring = st.comp_kv = 0x1000
+        st.ring_page = st.comp_start = 0x1000
+        st.ring_pages, st.comp_rows = 4, 100
+    assert L.chs_append_multi(7, 1, 4, 2, arr, None) == DTYPE
+    arr[1].x_new = None
+    assert L.chs_append_multi(1, 1, 4, 2, arr, None) == NULL              # the second stream is checked too
+    arr[1].x_new = 0x1000
+    arr[1].page_table, arr[1].page_size, arr[1].pt_stride, arr[1].pool_pages = 0x1000, 48, 2, 10
+    assert L.chs_append_multi(1, 1, 4, 2, arr, None) == SHAPE             # page size not a power of two
+    arr[1].page_size = 64
+    assert L.chs_append_multi(1, 1, 4, 2, arr, None) == SHAPE             # paged without window pages
+    arr[1].swa_pages = 2
+    assert L.chs_append_multi(1, 1, 4, 2, arr, None) == NULL              # paged without swa_page
+
+
 def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
          ws=FAKE, wsb=None):
     L = chs.lib()

@@ -246,3 +246,72 @@ def test_decode_loop_with_append_matches_oracle():
         o_ref, l_ref = oracle.decode_step(q[0], X[:N], W, cref, sel, d ** -0.5)
         assert_bf16_path(out[0].cpu().numpy(), o_ref, f"step {s}: attention")
         assert_lse(lse[0].cpu().numpy(), l_ref, f"step {s}: lse")
+
+
+@pytest.mark.parametrize("m,streams", [
+    (4, [(torch.bfloat16, 512, 128, 8, False), (torch.bfloat16, 128, 8, 8, False)]),    # KV + index keys (C4)
+    (4, [(torch.bfloat16, 256, 32, 8, True), (torch.bfloat16, 64, 8, 4, False), (torch.bfloat16, 128, 16, 4, True)]),
+    (128, [(torch.bfloat16, 512, 128, 128, False), (torch.bfloat16, 128, 128, 128, True)]),  # split path
+])
+def test_append_multi_equals_single_streams(m, streams):
+    # chs_append_multi over several streams (contiguous and paged mixed) leaves every buffer
+    # bit-identical to one chs_append / chs_append_paged call per stream.
+    print(f"case: append multi m={m} streams={[(s[1], s[4]) for s in streams]}", flush=True)
+    rng = np.random.default_rng(m + len(streams))
+    B, steps = 3, (m + 3 if m > 8 else 2 * m + 1)
+    n0 = [0, m - 1, 5 * m + 2]
+
+    def build():
+        out = []
+        for dt, d, W, R, paged in streams:
+            g = np.random.default_rng(d * 7 + W + R + paged)
+            st = dict(dt=dt, d=d, paged=paged, R=R,
+                      x=[_t(g.standard_normal((B, d)), dt) for _ in range(steps)],
+                      z=[_t(g.standard_normal((B, d)) * 2, dt) for _ in range(steps)],
+                      bias=_t(g.standard_normal((m, d)) * 0.1, torch.float32),
+                      n=torch.tensor(n0, dtype=torch.int64, device=dev()),
+                      sl=torch.zeros(B, dtype=torch.int32, device=dev()),
+                      cc=torch.zeros(B, dtype=torch.int64, device=dev()))
+            pages = B + 1
+            st["swa"] = _t(g.standard_normal((pages if paged else B, W, d)), dt)
+            st["ring"] = _t(g.standard_normal(((pages if paged else B) * R, d)), dt)
+            cap = (n0[-1] + steps) // m + 2
+            if paged:
+                P = 4
+                st["P"] = P
+                st["pt"] = torch.from_numpy(g.permutation(B * ((cap + P - 1) // P)).reshape(B, -1).astype(np.int32)).to(dev())
+                st["comp"] = torch.zeros(B * ((cap + P - 1) // P) * P, d, dtype=dt, device=dev())
+                st["page"] = torch.from_numpy(g.permutation(pages)[:B].astype(np.int32)).to(dev())
+            else:
+                st["comp"] = torch.zeros(B * cap, d, dtype=dt, device=dev())
+                st["page"] = torch.arange(B, dtype=torch.int32, device=dev())
+                st["start"] = torch.arange(0, B * cap, cap, dtype=torch.int64, device=dev())
+            out.append(st)
+        return out
+
+    def single(st, s):
+        if st["paged"]:
+            chs.append_paged(st["x"][s], st["z"][s], st["bias"], m, st["n"], st["swa"], st["page"], st["ring"], st["comp"],
+                             st["P"], st["pt"], swa_len=st["sl"], comp_count=st["cc"])
+        else:
+            chs.append(st["x"][s], st["z"][s], st["bias"], m, st["n"], st["swa"], st["ring"], st["page"], st["comp"],
+                       st["start"], ring_size=st["R"], swa_len=st["sl"], comp_count=st["cc"])
+
+    def desc(st, s):
+        if st["paged"]:
+            return chs.append_stream(st["x"][s], st["z"][s], st["bias"], st["n"], st["swa"], st["ring"], st["comp"],
+                                     swa_len=st["sl"], comp_count=st["cc"], swa_page=st["page"], page_table=st["pt"],
+                                     page_size=st["P"])
+        return chs.append_stream(st["x"][s], st["z"][s], st["bias"], st["n"], st["swa"], st["ring"], st["comp"],
+                                 ring_page=st["page"], comp_start=st["start"], ring_size=st["R"], swa_len=st["sl"],
+                                 comp_count=st["cc"])
+
+    A, Bs = build(), build()
+    for s in range(steps):
+        for st in A:
+            single(st, s)
+        chs.append_multi(m, [desc(st, s) for st in Bs])
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(A, Bs)):
+        for key in ("n", "sl", "cc", "swa", "ring", "comp"):
+            assert torch.equal(a[key], b[key]), f"stream {i}: {key} differs"
