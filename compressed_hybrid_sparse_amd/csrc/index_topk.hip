@@ -693,14 +693,9 @@ __device__ __forceinline__ void group_stats4(const f32x4& x, const uint32_t (&po
 // consecutive scores starting at (4x + w) * 256 * P: P 16-byte loads per lane when the
 // sequence's scores are 16-byte aligned (a group of 32 is then 8 lanes of one load), else
 // 4P 4-byte loads (a group is half a wave of one load).
+// The statistics of one wave's 256 * P scores from `base` (the body of max_kernel).
 template <int P>
-__global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
-  const int b = blockIdx.y;
-  int64_t c0;
-  const int64_t n = cand_count(a, b, &c0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * 256 * P;
-  if (base >= n) return;
+__device__ __forceinline__ void max_wave(const Args& a, int b, int64_t n, int64_t c0, int64_t base, int lane) {
   const float* sp = score_ptr(a, b, c0);
   uint32_t* gmax = maxima_ptr(a, b);
   uint32_t* gsec = second_ptr(a, b);
@@ -758,6 +753,81 @@ __global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
       if (lane == 32) { gmax[g + 1] = st.m1; gsec[g + 1] = pack_second(st); }
     }
   }
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void max_kernel(Args a) {
+  const int b = blockIdx.y;
+  int64_t c0;
+  const int64_t n = cand_count(a, b, &c0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * 256 * P;
+  if (base >= n) return;
+  max_wave<P>(a, b, n, c0, base, lane);
+}
+
+// max_kernel for 8 loads per lane with one group per lane. A wave's 2048 scores are 64 groups:
+// they are loaded coalesced (1 KiB per instruction), transposed through the wave's LDS tile so that
+// lane L holds group L's 32 scores in order, and each lane then walks its own group: the maximum
+// by max3, the top two composite words by max3 / med3 (c1' = max3(c1, x, y), c2' = max(c2,
+// med3(c1, x, y)) keeps the two largest of c1 >= c2, x, y). About a third of the VALU work of the
+// cross-lane reduction, and no cross-lane steps. The results are the same words group_stats4
+// writes. Waves that are not whole and aligned take max_wave<8>.
+constexpr int kLaneThreads = 256;
+constexpr int kLaneTilePitch = 9;   // 16-byte vectors per lane in the tile: 8 plus one of padding
+
+// The median of three (v_med3_u32).
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+
+__global__ __launch_bounds__(kLaneThreads) void max_lane_kernel(Args a) {
+  __shared__ f32x4 tile[kLaneThreads / 64][64 * kLaneTilePitch];
+  const int b = blockIdx.y;
+  int64_t c0;
+  const int64_t n = cand_count(a, b, &c0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = ((int64_t)blockIdx.x * (kLaneThreads / 64) + wave) * 2048;
+  if (base >= n) return;
+  const float* sp = score_ptr(a, b, c0);
+  const int64_t nfull = n / 4;
+  if ((reinterpret_cast<uintptr_t>(sp) & 15) != 0 || base + 2048 > 4 * nfull) {
+    max_wave<8>(a, b, n, c0, base, lane);
+    return;
+  }
+  const f32x4* sp4 = reinterpret_cast<const f32x4*>(sp) + base / 4;
+  f32x4 v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(sp4 + u * 64 + lane);
+  // Vector u * 64 + lane belongs to lane (u * 64 + lane) / 8, at slot lane % 8 of its group.
+  f32x4* t = tile[wave];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) t[(u * 8 + lane / 8) * kLaneTilePitch + (lane & 7)] = v[u];
+  // The wave's LDS operations execute in order, so its own writes are visible to these reads.
+  __asm__ volatile("" ::: "memory");
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = t[lane * kLaneTilePitch + u];
+  uint32_t m = 0, c1 = 0, c2 = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const uint32_t ux = __float_as_uint(v[u][e]), uy = __float_as_uint(v[u][e + 1]);
+      const uint32_t kx = ux ^ ((uint32_t)((int32_t)ux >> 31) | 0x80000000u);
+      const uint32_t ky = uy ^ ((uint32_t)((int32_t)uy >> 31) | 0x80000000u);
+      const uint32_t cx = (kx & ~31u) | (uint32_t)(4 * u + e);
+      const uint32_t cy = (ky & ~31u) | (uint32_t)(4 * u + e + 1);
+      m = max(m, max(kx, ky));
+      c2 = max(c2, med3u(c1, cx, cy));
+      c1 = max(c1, max(cx, cy));
+    }
+  }
+  // Mend the raw keys as group_stats4 does: -0 counts as +0.
+  uint32_t s2 = c2 & ~31u;
+  s2 = s2 == 0x7FFFFFE0u ? 0x80000000u : s2;
+  const int64_t g = base / kGroup + lane;
+  maxima_ptr(a, b)[g] = m == 0x7FFFFFFFu ? 0x80000000u : m;
+  second_ptr(a, b)[g] = s2 | (c1 & 31u);
 }
 
 // ---------------------------------------------------------------- K2: collect and select
@@ -1263,7 +1333,13 @@ chs_status topk_first(chs_dtype dtype, int32_t batch, Args* a, int lpc, hipStrea
       case 1: hipLaunchKernelGGL(max_kernel<1>, grid, dim3(kThreads), 0, s, *a); break;
       case 2: hipLaunchKernelGGL(max_kernel<2>, grid, dim3(kThreads), 0, s, *a); break;
       case 4: hipLaunchKernelGGL(max_kernel<4>, grid, dim3(kThreads), 0, s, *a); break;
-      default: hipLaunchKernelGGL(max_kernel<kPasses>, grid, dim3(kThreads), 0, s, *a); break;
+      default: {
+        // 8 loads per lane: the lane-per-group kernel (workgroups of 2048 * 4 scores).
+        static_assert(kPasses == 8, "max_lane_kernel covers 8 vectors per lane");
+        const dim3 g8((unsigned)((max_cand + 4 * 2048 - 1) / (4 * 2048)), (unsigned)batch);
+        hipLaunchKernelGGL(max_lane_kernel, g8, dim3(kLaneThreads), 0, s, *a);
+        break;
+      }
     }
   }
   return launch_status();

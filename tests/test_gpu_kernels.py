@@ -191,6 +191,24 @@ def test_topk_batched_varlen(rng):
     _run_topk([rng.standard_normal(n).astype(np.float32) * 3 for n in lens], 512)
 
 
+def test_topk_wide_batch_ragged_unaligned(rng):
+    # 33 rows of about 200K-262K scores: enough work for the 8-loads-per-lane statistics kernel.
+    # Ragged lengths give masked tail waves and row starts that are not 16-byte aligned (the
+    # fallback path); heavy ties and signed zeros sit in a few rows.
+    print("case: top-k wide batch, ragged and unaligned", flush=True)
+    lens = [262144, 262143, 262141, 200000, 200001] + list(rng.integers(200000, 262145, 28))
+    rows = []
+    for i, n in enumerate(lens):
+        r = rng.standard_normal(int(n)).astype(np.float32)
+        if i % 7 == 3:
+            r = (rng.integers(-4, 4, int(n)) * 0.5).astype(np.float32)
+        if i % 11 == 5:
+            r[rng.choice(int(n), 2000, replace=False)] = np.where(rng.random(2000) < 0.5, -0.0, 0.0)
+            r = np.minimum(r, np.float32(0.0))
+        rows.append(r)
+    _run_topk(rows, 512, reps=1)
+
+
 # ------------------------------------------------------------------ index scores + top-k
 @pytest.mark.parametrize("dtype,nh,dim,lens,k", [
     ("bf16", 4, 128, [32768], 512),
