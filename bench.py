@@ -396,6 +396,12 @@ def main():
                        100)
     t64_ms = time_calls(lambda i: chs.topk_from_scores(rows64[(i % 8) * 64 * G:(i % 8 + 1) * 64 * G], cu64, 512, G,
                                                        ws64, tk64), 50)
+    # The same calls replayed from a HIP graph (as the decode step is timed): 16 rotated rows per
+    # graph at bs = 1, the 8 rotated 64-row batches.
+    t1_graph = graph_loop_ms(lambda i: chs.topk_from_scores(rows1[(i % 256) * G:(i % 256 + 1) * G], cu1, 512, G, ws1,
+                                                            tk1), 16)
+    t64_graph = graph_loop_ms(lambda i: chs.topk_from_scores(rows64[(i % 8) * 64 * G:(i % 8 + 1) * 64 * G], cu64, 512,
+                                                             G, ws64, tk64), 8)
     # HiSparse-style working-set gather of the step's 512 selected entries (1 KiB rows) from a mirror
     # of the 262,144 compressed entries held in HBM or in pinned host memory (read over PCIe).
     work_rows = torch.empty(k, d, dtype=torch.bfloat16, device=dev)
@@ -488,7 +494,13 @@ def main():
             "topk_512_of_262144_us": {"bs1_median": round(t1_us, 2), "bs1_p90": round(pct(t1_ms, 0.9) * 1e3, 2),
                                       "rows64_median": round(t64_us, 2),
                                       "rows64_hbm_frac": round(64 * topk_row_bytes / (t64_us * 1e-6)
-                                                               / (HBM_PEAK_GBPS * 1e9), 4)},
+                                                               / (HBM_PEAK_GBPS * 1e9), 4),
+                                      "value_source": "stream launch (events around each call); graph replay beside",
+                                      "bs1_graph_median": None if t1_graph is None else round(median(t1_graph) * 1e3, 2),
+                                      "rows64_graph_median": None if t64_graph is None else
+                                      round(median(t64_graph) * 1e3, 2),
+                                      "rows64_graph_hbm_frac": None if t64_graph is None else
+                                      round(64 * topk_row_bytes / (median(t64_graph) * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)},
             "compress": {"median_us": round(c_us, 2), "GBps": round(comp_gbps, 1),
                          "hbm_frac": round(comp_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": comp_bytes},
         },

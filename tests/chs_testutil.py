@@ -1,7 +1,9 @@
 """Shared helpers for the GPU parity tests: tolerance checks and small utilities.
 
 Tolerances (stated per output kind):
-  fp32 storage: elementwise |a - b| <= 1e-4 |b| + 1e-7 max|b|, and rel-L2 <= 1e-4.
+  fp32 storage: elementwise |a - b| <= 1e-4 |b| + 1e-6 max|b|, and rel-L2 <= 1e-4. The absolute
+    floor covers entries that nearly cancel: an fp32 attention logit is exact to about
+    d 2^-24 |q||k| scale, which moves an output element by about 1e-6 of the values' scale.
   bf16 storage of a compressed entry: compared with the oracle's unrounded double value b,
     |a - b| <= max(1e-2, ulp_bf16(b)) and rel-L2 <= 5e-3; in addition the kernel's own error
     bound (fp32 arithmetic, one rounding to bf16) is asserted:
@@ -33,7 +35,7 @@ def assert_f32(got, want, what="", rtol=1e-4):
         return
     scale = np.abs(want).max()
     err = np.abs(got - want)
-    bound = rtol * np.abs(want) + rtol * 1e-3 * scale
+    bound = rtol * np.abs(want) + rtol * 1e-2 * scale
     bad = np.flatnonzero(err > bound)
     assert bad.size == 0, f"{what}: {bad.size} elements beyond fp32 tolerance, worst " \
                           f"{err.ravel()[bad[:5]]} at {bad[:5]}"

@@ -13,7 +13,11 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: full-size workload (minutes of host work)")
 
 
-@pytest.fixture(scope="session")
-def rng():
+@pytest.fixture
+def rng(request):
+    """A generator seeded from the test's own id, so a test's inputs do not depend on which other
+    tests ran before it."""
+    import zlib
+
     import numpy as np
-    return np.random.default_rng(12345)
+    return np.random.default_rng(zlib.crc32(request.node.nodeid.encode()))
