@@ -23,7 +23,7 @@ EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compr
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
            "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
-           "chs_append_multi")
+           "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -77,13 +77,18 @@ def lib():
                                             _i64, _i32, _p, _i32, _p, _p, _i64, _p, _p, _p, _sz, _p]
         L.chs_append_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _i64, _p, _p,
                                        _p, _i64, _i32, _p, _i32, _p, _p]
+        L.chs_index_topk_fp8_paged.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64,
+                                               _p, _p, _p, _sz, _p]
+        L.chs_decode_attn_fp8_paged.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _i64, _p, _p, _p,
+                                                _i64, _i32, _p, _i32, _p, _p, _i64, _p, _p, _p, _sz, _p]
         L.chs_append_multi.argtypes = [ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(AppendStream), _p]
         L.chs_gather_selected.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
-                   "chs_index_topk_paged", "chs_gather_selected", "chs_append_multi"):
+                   "chs_index_topk_paged", "chs_gather_selected", "chs_append_multi", "chs_index_topk_fp8_paged",
+                   "chs_decode_attn_fp8_paged"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -513,3 +518,66 @@ def append_multi(m: int, streams):
     arr = (AppendStream * len(streams))(*streams)
     x0 = streams[0]._keep[0]
     _check(lib().chs_append_multi(_dtype_code(x0), x0.shape[0], m, len(streams), arr, _stream()), "chs_append_multi")
+
+
+def index_topk_fp8_paged(q_idx, w, code_pool, scale_pool, page_size: int, page_table, cand_len, k: int, max_cand: int,
+                         scores=None, workspace=None, out=None):
+    """chs_index_topk_fp8 over paged pools of E4M3 key codes ([rows, dim] uint8) and their fp32
+    row scales ([rows]) (chs_index_topk_fp8_paged). Returns (topk [B, k] int32, scores)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(code_pool, "code_pool", torch.uint8, 2)
+    _need(scale_pool, "scale_pool", torch.float32, 1)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(cand_len, "cand_len", torch.int64, 1)
+    B, nh, dim = q_idx.shape
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 2)
+    if workspace is None:
+        workspace = index_topk_workspace(B, max_cand, k, q_idx.device)
+    if out is None:
+        out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+    _check(lib().chs_index_topk_fp8_paged(B, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(code_pool), _ptr(scale_pool),
+                                          code_pool.shape[0] // page_size, page_size, _ptr(page_table),
+                                          page_table.shape[1], _ptr(cand_len), int(max_cand), _ptr(scores), _ptr(out),
+                                          _ptr(workspace), workspace.numel(), _stream()), "chs_index_topk_fp8_paged")
+    return out, scores
+
+
+def decode_attn_fp8_paged(q, swa_codes, swa_scales, swa_page, swa_len, comp_codes, comp_scales, page_size: int,
+                          page_table, comp_len, topk=None, scale=None, max_comp=None, workspace=None, out=None,
+                          lse=None):
+    """chs_decode_attn_fp8 over paged pools (chs_decode_attn_fp8_paged). swa_codes: [swa_pages, W, d]
+    uint8, swa_scales: [swa_pages, W] fp32; comp_codes: [rows, d] uint8, comp_scales: [rows] fp32."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(swa_codes, "swa_codes", torch.uint8, 3)
+    _need(swa_scales, "swa_scales", torch.float32, 2)
+    _need(swa_page, "swa_page", torch.int32, 1)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_codes, "comp_codes", torch.uint8, 2)
+    _need(comp_scales, "comp_scales", torch.float32, 1)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(comp_len, "comp_len", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_codes.shape[1]
+    k = 0
+    if topk is not None:
+        _need(topk, "topk", torch.int32, 2)
+        k = topk.shape[1]
+    if max_comp is None:
+        max_comp = int(comp_len.max().item()) if comp_len.numel() else 0
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = decode_attn_workspace(torch.bfloat16, B, H, d, W, k, max_comp, q.device)
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _check(lib().chs_decode_attn_fp8_paged(B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_codes), _ptr(swa_scales),
+                                           _ptr(swa_page), swa_codes.shape[0], _ptr(swa_len), _ptr(comp_codes),
+                                           _ptr(comp_scales), comp_codes.shape[0] // page_size, page_size,
+                                           _ptr(page_table), page_table.shape[1], _ptr(comp_len), _ptr(topk),
+                                           int(max_comp), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                           _stream()), "chs_decode_attn_fp8_paged")
+    return out, lse

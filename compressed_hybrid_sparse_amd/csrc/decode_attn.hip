@@ -44,12 +44,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   attn_split<D, 1, NoHook, false, PAGED>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
 }
 
-// The same with FP8 E4M3 storage and per-row scales.
-template <int D>
+// The same with FP8 E4M3 storage and per-row scales (PAGED: rows and scales from paged pools).
+template <int D, bool PAGED = false>
 __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(AttnArgs a) {
   __shared__ AttnShared<D, 1> sh;
   NoHook none;
-  attn_split<D, 1, NoHook, true>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
+  attn_split<D, 1, NoHook, true, PAGED>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
 }
 
 // ---------------------------------------------------------------- fp32 VALU split kernel
@@ -285,6 +285,46 @@ extern "C" chs_status chs_decode_attn_paged(chs_dtype dtype, int32_t batch, int3
                      max_comp, out, lse, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+namespace chs {
+namespace {
+
+chs_status launch_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, float scale,
+                           const void* q, const void* swa_kv, const float* swa_scale, const int32_t* swa_len,
+                           const void* comp_kv, const float* comp_scale, const int64_t* cu_comp,
+                           const attn::Paging& pg, const int32_t* topk, int64_t max_comp, float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t s) {
+  const int kk = topk ? k : 0;
+  SplitPlan p = plan_splits(CHS_BF16, batch, n_heads, window, kk, max_comp);
+  AttnArgs a;
+  a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
+  a.swa_scale = swa_scale; a.comp_scale = comp_scale;
+  a.pg = pg;
+  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
+  a.scale_log2 = scale * kLog2e;
+  a.n_splits = p.n_splits; a.kps = p.kps;
+  a.head_tiles = (n_heads + 63) / 64;
+  const size_t need = ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
+  const bool paged = pg.pt != nullptr;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, a); };
+  switch (d) {
+    case 64: paged ? go(attn_fp8_kernel<64, true>) : go(attn_fp8_kernel<64>); break;
+    case 128: paged ? go(attn_fp8_kernel<128, true>) : go(attn_fp8_kernel<128>); break;
+    case 256: paged ? go(attn_fp8_kernel<256, true>) : go(attn_fp8_kernel<256>); break;
+    default: paged ? go(attn_fp8_kernel<512, true>) : go(attn_fp8_kernel<512>); break;
+  }
+  if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  const int words_per_block = kThreads / kCombineLanes;
+  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
+                   (unsigned)batch);
+  hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(kThreads), 0, s, a, out, lse);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace chs
+
 extern "C" chs_status chs_decode_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
                                           float scale, const void* q, const void* swa_kv, const float* swa_scale,
                                           const int32_t* swa_len, const void* comp_kv, const float* comp_scale,
@@ -298,30 +338,39 @@ extern "C" chs_status chs_decode_attn_fp8(int32_t batch, int32_t n_heads, int32_
   if (!workspace) return CHS_ERR_NULL;
   if (window > 0 && !swa_scale) return CHS_ERR_NULL;
   if (!comp_scale && (topk ? k > 0 : max_comp > 0)) return CHS_ERR_NULL;
-  const int kk = topk ? k : 0;
-  SplitPlan p = plan_splits(CHS_BF16, batch, n_heads, window, kk, max_comp);
-  AttnArgs a;
-  a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
-  a.swa_scale = swa_scale; a.comp_scale = comp_scale;
-  a.pg = attn::Paging{};
-  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
-  a.scale_log2 = scale * kLog2e;
-  a.n_splits = p.n_splits; a.kps = p.kps;
-  a.head_tiles = (n_heads + 63) / 64;
-  const size_t need = ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
-  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
-  switch (d) {
-    case 64: hipLaunchKernelGGL(attn_fp8_kernel<64>, grid, dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_fp8_kernel<128>, grid, dim3(kThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(attn_fp8_kernel<256>, grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(attn_fp8_kernel<512>, grid, dim3(kThreads), 0, s, a); break;
-  }
-  if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-  const int words_per_block = kThreads / kCombineLanes;
-  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
-                   (unsigned)batch);
-  hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(kThreads), 0, s, a, out, lse);
-  return launch_status();
+  const attn::Paging none{};
+  return launch_attn_fp8(batch, n_heads, d, window, k, scale, q, swa_kv, swa_scale, swa_len, comp_kv, comp_scale,
+                         cu_comp, none, topk, max_comp, out, lse, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" chs_status chs_decode_attn_fp8_paged(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                                float scale, const void* q, const void* swa_pool,
+                                                const float* swa_scale_pool, const int32_t* swa_page,
+                                                int64_t swa_pages, const int32_t* swa_len, const void* comp_pool,
+                                                const float* comp_scale_pool, int64_t pool_pages, int32_t page_size,
+                                                const int32_t* page_table, int32_t pt_stride, const int64_t* comp_len,
+                                                const int32_t* topk, int64_t max_comp, float* out, float* lse,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace chs;
+  // The shared checks null-test their cu argument; here the per-sequence counts take its place.
+  const chs_status st = attn::check_args(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_pool, swa_len,
+                                         comp_pool, comp_len, topk, max_comp, out);
+  if (st != CHS_OK) return st;
+  if (!workspace || !page_table || (window > 0 && (!swa_page || !swa_scale_pool))) return CHS_ERR_NULL;
+  if (!comp_scale_pool && (topk ? k > 0 : max_comp > 0)) return CHS_ERR_NULL;
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0 || pt_stride < 1 ||
+      pool_pages < 1 || (window > 0 && swa_pages < 1))
+    return CHS_ERR_SHAPE;
+  attn::Paging pg{};
+  pg.swa_page = window > 0 ? swa_page : nullptr;
+  pg.swa_pages = swa_pages;
+  pg.pt = page_table;
+  pg.comp_len = comp_len;
+  pg.pt_stride = pt_stride;
+  pg.shift = __builtin_ctz((unsigned)page_size);
+  pg.pool_pages = pool_pages;
+  return launch_attn_fp8(batch, n_heads, d, window, k, scale, q, swa_pool, swa_scale_pool, swa_len, comp_pool,
+                         comp_scale_pool, nullptr, pg, topk, max_comp, out, lse, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
 }

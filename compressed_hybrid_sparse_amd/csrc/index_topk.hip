@@ -526,8 +526,9 @@ constexpr int mfma_tiles(int d, int es) { return 8192 / (16 * d * es) > 2 ? 8192
 // The result leaves lane (g, c) with the dots of heads 4g .. 4g + 3 against key c; ReLU,
 // weights and (fp8) the row scale follow, summed over the 4 lane rows when there are more
 // than 4 heads. A wave covers TILES tiles (8 KiB of keys; 2 tiles = one group at least).
-// PAGED: the keys come from a paged pool; a wave's keys (at most 64) lie in one page (pages of at
-// least 64 rows), so one page-table read, issued with the query loads, places them.
+// PAGED: the keys (and FP8 row scales) come from paged pools; a wave's keys lie in one page (pages
+// of at least as many rows as a wave scores), so one page-table read, issued with the query
+// loads, places them.
 template <typename ET, int D, int NH4, bool PAGED = false>
 __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
   const int64_t key0 = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TILES * 16;
   if (key0 >= n) return;                               // no barriers follow
-  static_assert(!PAGED || (ES == 2 && TILES * 16 <= 64), "paged keys: bf16, at most 64 keys per wave");
+  static_assert(TILES * 16 <= 128, "a wave scores at most 128 keys (the paged calls' smallest page)");
   int64_t krow0 = c0 + key0;                           // storage row of key0; rows follow it
   if (PAGED) {
     const int64_t p = a.pt[(int64_t)b * a.pt_stride + (key0 >> a.shift)];
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
   float ks[TILES];
   if (kScaled) {
 #pragma unroll
-    for (int j = 0; j < TILES; ++j) ks[j] = a.kscale[c0 + min(key0 + 16 * j + c, n - 1)];
+    for (int j = 0; j < TILES; ++j) ks[j] = a.kscale[krow0 + (min(key0 + 16 * j + c, n - 1) - key0)];
   }
   __builtin_amdgcn_sched_barrier(0);
   const bool qon = c < a.nh;
@@ -1229,11 +1230,10 @@ bool launch_scores_mfma(int32_t batch, int32_t head_dim, Args* a, hipStream_t s)
   const dim3 grid((unsigned)((a->max_cand + per_block - 1) / per_block), (unsigned)batch);
   a->gs = kGroup;
   const bool wide = a->nh > 4;
-  constexpr bool kBf16 = sizeof(ET) == 2;
-  const bool paged = kBf16 && a->pt != nullptr;
+  const bool paged = a->pt != nullptr;
 #define CHS_MFMA(DD)                                                                                    \
-  if (paged && wide) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 4, kBf16>), grid, dim3(kThreads), 0, s, *a); \
-  else if (paged) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 1, kBf16>), grid, dim3(kThreads), 0, s, *a);   \
+  if (paged && wide) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 4, true>), grid, dim3(kThreads), 0, s, *a);  \
+  else if (paged) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 1, true>), grid, dim3(kThreads), 0, s, *a);    \
   else if (wide) hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 4>), grid, dim3(kThreads), 0, s, *a);           \
   else hipLaunchKernelGGL((score_mfma_kernel<ET, DD, 1>), grid, dim3(kThreads), 0, s, *a);
   switch (head_dim) {
@@ -1427,6 +1427,40 @@ extern "C" chs_status chs_index_topk_paged(chs_dtype dtype, int32_t batch, int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_cand > 0) {
     launch_scores_mfma<uint16_t>(batch, head_dim, &a, s);
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
+  return launch_status();
+}
+
+extern "C" chs_status chs_index_topk_fp8_paged(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                                               const void* q_idx, const float* w, const void* key_pool,
+                                               const float* scale_pool, int64_t pool_pages, int32_t page_size,
+                                               const int32_t* page_table, int32_t pt_stride, const int64_t* cand_len,
+                                               int64_t max_cand, float* scores, int32_t* topk, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  using namespace chs;
+  if (batch < 1 || batch > 65535 || k < 1 || k > kMaxK || max_cand < 0 || max_cand >= (1LL << 31) ||
+      n_heads < 1 || n_heads > 16 || head_dim < 16 || head_dim > 512 || page_size < 1 || page_size > 65536 ||
+      (page_size & (page_size - 1)) != 0 || pt_stride < 1 || pool_pages < 1)
+    return CHS_ERR_SHAPE;
+  if (max_cand > kMaxCand) return CHS_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return CHS_ERR_UNSUPPORTED;
+  if (page_size < 16 * mfma_tiles(head_dim, 1)) return CHS_ERR_SHAPE;   // a wave's keys in one page
+  if (!q_idx || !w || !key_pool || !scale_pool || !page_table || !cand_len || !topk || !workspace)
+    return CHS_ERR_NULL;
+  Workspace ws;
+  const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  Args a;
+  a.q = q_idx; a.w = w; a.keys = key_pool; a.cu = nullptr; a.max_cand = max_cand;
+  a.nh = n_heads; a.nvec = head_dim / 16; a.k = k; a.scores = scores; a.ws = ws; a.kscale = scale_pool;
+  a.gs = kGroup;
+  a.pt = page_table; a.cand_len = cand_len; a.pt_stride = pt_stride; a.shift = __builtin_ctz((unsigned)page_size);
+  a.pool_pages = pool_pages;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_cand > 0) {
+    launch_scores_mfma<uint8_t>(batch, head_dim, &a, s);
     if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   }
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);

@@ -296,6 +296,28 @@ chs_status chs_index_topk_paged(chs_dtype dtype, int32_t batch, int32_t n_heads,
                                 const int64_t* cand_len, int64_t max_cand, float* scores, int32_t* topk,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* chs_index_topk_fp8_paged, chs_decode_attn_fp8_paged: the FP8 calls (chs_index_topk_fp8,
+ * chs_decode_attn_fp8) over paged pools, addressed as above; each row's fp32 scale sits at the same
+ * row index of a scale pool ([pool_pages * page_size] for keys and entries, [swa_pages * window] for
+ * the windows). The index call supports head_dim 64, 128, 256 with page_size at least the keys a
+ * wave scores (128, 64, 32 respectively; else CHS_ERR_SHAPE). Results are bit-identical to the
+ * contiguous FP8 calls on the same rows. */
+chs_status chs_index_topk_fp8_paged(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                                    const void* q_idx, const float* w, const void* key_pool,
+                                    const float* scale_pool, int64_t pool_pages, int32_t page_size,
+                                    const int32_t* page_table, int32_t pt_stride, const int64_t* cand_len,
+                                    int64_t max_cand, float* scores, int32_t* topk, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+chs_status chs_decode_attn_fp8_paged(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                     float scale, const void* q, const void* swa_pool,
+                                     const float* swa_scale_pool, const int32_t* swa_page, int64_t swa_pages,
+                                     const int32_t* swa_len, const void* comp_pool,
+                                     const float* comp_scale_pool, int64_t pool_pages, int32_t page_size,
+                                     const int32_t* page_table, int32_t pt_stride, const int64_t* comp_len,
+                                     const int32_t* topk, int64_t max_comp, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* chs_append_paged: chs_append with the window, the gate ring and the compressed pool paged as
  * above (n_tokens, swa_len, comp_count as in chs_append; comp_count counts entries, so it can feed
  * comp_len of chs_decode_attn_paged directly). */

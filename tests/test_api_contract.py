@@ -176,6 +176,45 @@ def test_append_multi_validation():
     assert L.chs_append_multi(1, 1, 4, 2, arr, None) == NULL              # paged without swa_page
 
 
+def topk8_paged(batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, pool=FAKE, sc=FAKE, npool=100, P=64, pt=FAKE,
+                stride=8, cl=FAKE, maxc=1000, s=FAKE, out=FAKE, ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_index_topk_workspace_size(batch, maxc, k)
+    return L.chs_index_topk_fp8_paged(batch, nh, dim, k, q, w, pool, sc, npool, P, pt, stride, cl, maxc, s, out, ws,
+                                      wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(k=0), SHAPE), (dict(nh=17), SHAPE), (dict(P=48), SHAPE), (dict(P=32), SHAPE),
+    (dict(dim=64, P=64), SHAPE), (dict(stride=0), SHAPE), (dict(npool=0), SHAPE), (dict(dim=96), UNSUP),
+    (dict(dim=512), UNSUP), (dict(q=None), NULL), (dict(sc=None), NULL), (dict(pool=None), NULL),
+    (dict(pt=None), NULL), (dict(cl=None), NULL), (dict(ws=None), NULL), (dict(wsb=16), WS),
+    (dict(dim=256, P=32, pt=None), NULL),   # 32-row pages suffice at 256 channels: only the NULL is caught
+])
+def test_index_topk_fp8_paged_validation(kw, code):
+    assert topk8_paged(**kw) == code
+
+
+def attn8_paged(batch=1, H=64, d=512, W=128, k=512, scale=0.04, q=FAKE, swa=FAKE, ssc=FAKE, sp=FAKE, nsp=4, sl=FAKE,
+                pool=FAKE, csc=FAKE, npool=100, P=64, pt=FAKE, stride=8, cl=FAKE, tk=FAKE, maxc=1000, out=FAKE,
+                lse=FAKE, ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_decode_attn_workspace_size(1, batch, H, d, W, k if tk else 0, maxc)
+    return L.chs_decode_attn_fp8_paged(batch, H, d, W, k, ctypes.c_float(scale), q, swa, ssc, sp, nsp, sl, pool, csc,
+                                       npool, P, pt, stride, cl, tk, maxc, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(d=96), SHAPE), (dict(P=0), SHAPE), (dict(P=24), SHAPE), (dict(stride=0), SHAPE),
+    (dict(npool=0), SHAPE), (dict(nsp=0), SHAPE), (dict(q=None), NULL), (dict(ssc=None), NULL), (dict(sp=None), NULL),
+    (dict(csc=None), NULL), (dict(pt=None), NULL), (dict(cl=None), NULL), (dict(ws=None), NULL), (dict(wsb=8), WS),
+])
+def test_decode_attn_fp8_paged_validation(kw, code):
+    assert attn8_paged(**kw) == code
+
+
 def topk(dt=1, batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, out=FAKE,
          ws=FAKE, wsb=None):
     L = chs.lib()

@@ -342,3 +342,104 @@ def test_paged_decode_loop_c4():
             o_ref, l_ref = oracle.decode_step(q[b], X[b][:N], W, cref, sel, d ** -0.5)
             assert_bf16_path(out[b].cpu().numpy(), o_ref, f"step {s} b={b}: attention")
             assert_lse(lse[b].cpu().numpy(), l_ref, f"step {s} b={b}: lse")
+
+
+def _quantise_rows(x):
+    """Per-row E4M3 codes (uint8) and fp32 scales of fp32 device rows (input preparation)."""
+    scale = (x.abs().amax(dim=-1) / 448.0).clamp_min(1e-30)
+    codes = (x / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.contiguous()
+
+
+def _scatter_pages(rows, pt, P, n_rows):
+    """Logical rows of each sequence (a list) into a pool of n_rows rows through the page table."""
+    pool = torch.zeros((n_rows,) + tuple(rows[0].shape[1:]), dtype=rows[0].dtype, device=dev())
+    for b, r in enumerate(rows):
+        j = torch.arange(r.shape[0], device=dev())
+        phys = pt[b][j // P].long() * P + j % P
+        pool[phys] = r
+    return pool
+
+
+@pytest.mark.parametrize("nh,dim,P,lens,k", [(4, 128, 64, [5000, 700], 512), (16, 64, 128, [3000], 100),
+                                             (2, 256, 32, [1500, 0, 333], 300)])
+def test_paged_fp8_index_equals_contiguous(nh, dim, P, lens, k):
+    print(f"case: paged fp8 index nh={nh} dim={dim} P={P} lens={lens}", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(dim + P)
+    rows = [torch.randn(n, dim, generator=g, device=dev()) * 3 for n in lens]
+    qc = [_quantise_rows(r) for r in rows]
+    need = [(n + P - 1) // P for n in lens]
+    stride = max(1, max(need))
+    total = sum(need) + 2
+    perm = torch.randperm(total, generator=torch.Generator().manual_seed(1)).to(torch.int32)
+    pt = torch.full((len(lens), stride), -1, dtype=torch.int32)
+    o = 0
+    for b, nb in enumerate(need):
+        pt[b, :nb] = perm[o:o + nb]
+        o += nb
+    pt = pt.to(dev())
+    codes_pool = _scatter_pages([c for c, _ in qc], pt, P, total * P)
+    scale_pool = _scatter_pages([s for _, s in qc], pt, P, total * P)
+    q = torch.randn(len(lens), nh, dim, generator=g, device=dev()).bfloat16()
+    w = torch.rand(len(lens), nh, generator=g, device=dev())
+    max_cand = max(lens)
+    sp = torch.full((len(lens), max_cand), -5.0, device=dev())
+    tp, _ = chs.index_topk_fp8_paged(q, w, codes_pool, scale_pool, P, pt, torch.tensor(lens, device=dev()), k,
+                                     max_cand, sp)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64, device=dev())
+    codes_c = torch.cat([c for c, _ in qc]) if sum(lens) else torch.zeros(1, dim, dtype=torch.uint8, device=dev())
+    scales_c = torch.cat([s for _, s in qc]) if sum(lens) else torch.zeros(1, device=dev())
+    sc = torch.empty(max(sum(lens), 1), device=dev())
+    tc, _ = chs.index_topk_fp8(q, w, codes_c, scales_c, cu, k, max_cand, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(tp, tc)
+    cuh = cu.cpu().numpy()
+    for b, n in enumerate(lens):
+        assert torch.equal(sp[b, :n], sc[cuh[b]:cuh[b + 1]]), f"scores of sequence {b}"
+
+
+@pytest.mark.parametrize("H,d,W,P,G_list,k,dense", [(64, 512, 128, 64, [3000, 700], 512, False),
+                                                    (16, 128, 32, 16, [400, 1200], 0, True)])
+def test_paged_fp8_attention_equals_contiguous_and_oracle(H, d, W, P, G_list, k, dense):
+    print(f"case: paged fp8 attention H={H} d={d} P={P} G={G_list} dense={dense}", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(H + d + P)
+    B = len(G_list)
+    rows = [torch.randn(G, d, generator=g, device=dev()) for G in G_list]
+    qc = [_quantise_rows(r) for r in rows]
+    need = [(G + P - 1) // P for G in G_list]
+    stride = max(need)
+    total = sum(need) + 1
+    perm = torch.randperm(total, generator=torch.Generator().manual_seed(2)).to(torch.int32)
+    pt = torch.full((B, stride), -1, dtype=torch.int32)
+    o = 0
+    for b, nb in enumerate(need):
+        pt[b, :nb] = perm[o:o + nb]
+        o += nb
+    pt = pt.to(dev())
+    cpool = _scatter_pages([c for c, _ in qc], pt, P, total * P)
+    spool = _scatter_pages([s for _, s in qc], pt, P, total * P)
+    swa_pages = B + 1
+    swa_codes, swa_scales = _quantise_rows(torch.randn(swa_pages, W, d, generator=g, device=dev()))
+    swa_page = torch.tensor([2, 0], dtype=torch.int32, device=dev())[:B]
+    swa_len = torch.tensor([W, W // 3], dtype=torch.int32, device=dev())[:B]
+    q = torch.randn(B, H, d, generator=g, device=dev()).bfloat16()
+    topk = None
+    if not dense:
+        topk = torch.stack([torch.randint(-2, G + 3, (k,), generator=g, device=dev()) for G in G_list]).int()
+    clen = torch.tensor(G_list, dtype=torch.int64, device=dev())
+    op, lp = chs.decode_attn_fp8_paged(q, swa_codes, swa_scales, swa_page, swa_len, cpool, spool, P, pt, clen, topk,
+                                       d ** -0.5, max(G_list))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(G_list)]), dtype=torch.int64, device=dev())
+    oc, lc = chs.decode_attn_fp8(q, swa_codes[swa_page.long()].contiguous(), swa_scales[swa_page.long()].contiguous(),
+                                 swa_len, torch.cat([c for c, _ in qc]), torch.cat([s for _, s in qc]), cu, topk,
+                                 d ** -0.5, max(G_list))
+    torch.cuda.synchronize()
+    assert torch.equal(op, oc) and torch.equal(lp, lc), "paged and contiguous FP8 calls differ"
+    b = 0
+    nsw = int(swa_len[b])
+    sel = [int(j) for j in (range(G_list[b]) if dense else topk[b].tolist()) if 0 <= j < G_list[b]]
+    codes = torch.cat([swa_codes[int(swa_page[b]), :nsw], qc[b][0][sel]]).cpu().numpy()
+    scales = torch.cat([swa_scales[int(swa_page[b]), :nsw], qc[b][1][sel]]).cpu().numpy()
+    o_ref, l_ref = oracle.attend_fp8(q[b].float().cpu().numpy(), codes, scales, d ** -0.5)
+    assert_bf16_path(op[b].cpu().numpy(), o_ref, "paged fp8 attention")
+    assert_lse(lp[b].cpu().numpy(), l_ref, "paged fp8 lse", 1e-3)
