@@ -238,6 +238,19 @@ def main():
 
     graph_ms = graph_loop_ms(decode, nk)
 
+    # The same step as one chs_decode_step call (the selection's second kernel runs inside the
+    # attention's split kernel): bit-identical outputs, three launches instead of four.
+    ws_step = chs.decode_step_workspace(1, H, d, wl.window, k, G, dev)
+
+    def decode_fused(i):
+        chs.decode_step(inp["q_idx"], inp["w"], keys[i % len(keys)], inp["q"], inp["swa_kv"], inp["swa_len"], comp,
+                        inp["cu_groups"], k, scale, G, scores, ws_step, topk, out, lse)
+
+    for i in range(nk):
+        decode_fused(i)
+    fused_ms = loop_ms(lambda: [decode_fused(i) for i in range(nk)], 20, nk)
+    fused_graph_ms = graph_loop_ms(decode_fused, nk)
+
     # The same step over FP8 (E4M3) storage with per-row scales: index keys
     # (chs_index_topk_fp8, which halves the key read) and the KV cache (chs_decode_attn_fp8).
     # Rows are quantised per row on the device (input preparation): scale = max|x| / 448,
@@ -465,6 +478,13 @@ def main():
                                "decode_attn_us": round(median(attn_ms) * 1e3, 2),
                                "algorithmic_bytes": step_bytes,
                                "hbm_frac": round(step_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4)},
+            "decode_step_fused_us": {
+                "value_source": "graph replay", "call": "chs_decode_step",
+                "graph_median": None if fused_graph_ms is None else round(median(fused_graph_ms) * 1e3, 2),
+                "stream_median": round(median(fused_ms) * 1e3, 2),
+                "algorithmic_bytes": step_bytes,
+                "hbm_frac": None if fused_graph_ms is None else
+                round(step_bytes / (median(fused_graph_ms) * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)},
             "decode_step_fp8_us": {
                 "value_source": "graph replay", "call": "chs_index_topk_fp8 + chs_decode_attn_fp8",
                 "graph_median": None if fp8_graph_ms is None else round(median(fp8_graph_ms) * 1e3, 2),

@@ -23,7 +23,8 @@ EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compr
            "chs_index_topk_workspace_size", "chs_index_topk", "chs_decode_attn_workspace_size",
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
            "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
-           "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged")
+           "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged",
+           "chs_decode_step_workspace_size", "chs_decode_step")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -81,6 +82,10 @@ def lib():
                                                _p, _p, _p, _sz, _p]
         L.chs_decode_attn_fp8_paged.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _i64, _p, _p, _p,
                                                 _i64, _i32, _p, _i32, _p, _p, _i64, _p, _p, _p, _sz, _p]
+        L.chs_decode_step_workspace_size.restype = _sz
+        L.chs_decode_step_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64]
+        L.chs_decode_step.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
+                                      _i64, _p, _p, _p, _p, _p, _sz, _p]
         L.chs_append_multi.argtypes = [ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(AppendStream), _p]
         L.chs_gather_selected.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
@@ -280,6 +285,51 @@ def decode_attn(q, swa_kv, swa_len, comp_kv, cu_comp, topk=None, scale=None, max
                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()),
            "chs_decode_attn")
     return out, lse
+
+
+# ---------------------------------------------------------------- chs_decode_step
+def decode_step_workspace(batch, n_heads, d, window, k, max_comp, device="cuda"):
+    n = lib().chs_decode_step_workspace_size(batch, n_heads, d, window, k, max_comp)
+    return torch.zeros(max(n, 4), dtype=torch.uint8, device=device)
+
+
+def decode_step(q_idx, w, k_idx, q, swa_kv, swa_len, comp_kv, cu_comp, k: int, scale=None, max_comp=None,
+                scores=None, workspace=None, topk=None, out=None, lse=None):
+    """The C4 decode step in one call (chs_decode_step, bf16): the indexer scores and exact top-k
+    of index_topk over the compressed entries, then decode_attn over the window and the selected
+    entries, with bit-identical results. q_idx: [B, Hi, dim]; w: [B, Hi] fp32; k_idx: [G, dim];
+    q: [B, H, d]; swa_kv: [B, W, d]; swa_len: [B] int32; comp_kv: [G, d]; cu_comp: [B+1] int64.
+    Returns (topk [B, k] int32, out [B, H, d] fp32, lse [B, H] fp32, scores or None)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(swa_kv, "swa_kv", torch.bfloat16, 3)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_kv, "comp_kv", torch.bfloat16, 2)
+    _need(cu_comp, "cu_comp", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_kv.shape[1]
+    if max_comp is None:
+        max_comp = _host_max_diff(cu_comp)
+    if scale is None:
+        scale = d ** -0.5
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 1)
+    if workspace is None:
+        workspace = decode_step_workspace(B, H, d, W, k, max_comp, q.device)
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _need(topk, "topk", torch.int32, 2)
+    _check(lib().chs_decode_step(B, H, d, W, k, float(scale), q_idx.shape[1], q_idx.shape[2], _ptr(q_idx), _ptr(w),
+                                 _ptr(k_idx), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(cu_comp),
+                                 int(max_comp), _ptr(scores), _ptr(topk), _ptr(out), _ptr(lse), _ptr(workspace),
+                                 workspace.numel(), _stream()), "chs_decode_step")
+    return topk, out, lse, scores
 
 
 def index_topk_fp8(q_idx, w, k_codes, k_scale, cu_cand, k: int, max_cand=None, scores=None, workspace=None,

@@ -44,7 +44,8 @@ struct AttnArgs {
   const int32_t* swa_len;   // [batch]
   const void* comp;         // [*][D]
   const int64_t* cu_comp;   // [batch+1]
-  const int32_t* topk;      // [batch][k] or NULL
+  const int32_t* topk;      // [batch][k] or NULL (row b at topk + b * topk_stride)
+  int32_t topk_stride;      // entries between sequences' rows: k, or 0 for one row of this sequence
   int32_t H, D, W, k;
   int64_t max_comp;
   float scale_log2;         // scale * log2(e)
@@ -103,7 +104,7 @@ struct SlotMap {
     *is_swa = false;
     int64_t j = s - nswa;
     if (a.topk) {
-      j = a.topk[(int64_t)b * a.k + j];
+      j = a.topk[(int64_t)b * a.topk_stride + j];
       if (j < 0 || j >= G) return -1;
     }
     if (a.pg.pt) {
@@ -146,7 +147,7 @@ __device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm,
   const ET* comp = static_cast<const ET*>(a.comp);
   int32_t idx[LOADS];
   if (a.topk != nullptr && a.k > 0) {
-    const int32_t* tk = a.topk + (int64_t)b * a.k;
+    const int32_t* tk = a.topk + (int64_t)b * a.topk_stride;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) idx[i] = tk[min(max(s0 + (i * NW + wave) * RPI + lr - sm.nswa, 0), a.k - 1)];
   } else {
@@ -383,7 +384,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
   const int64_t pslot = (int64_t)b * a.n_splits + split;
   f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (pslot * a.head_tiles * 4 + z) * (D / 16) * 64;
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) po[(TPW * quarter + j) * 64 + lane] = o[j];
+  for (int j = 0; j < TPW; ++j) __builtin_nontemporal_store(o[j], &po[(TPW * quarter + j) * 64 + lane]);
   if (quarter == 0 && c == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

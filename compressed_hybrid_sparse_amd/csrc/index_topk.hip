@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "attn_core.h"
 
 namespace chs {
 namespace {
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
     if (kScaled) p *= ks[j];
     const int64_t key = key0 + 16 * j + c;
     const bool valid = key < n;
-    if (g == 0 && valid) sp[key] = p;
+    if (g == 0 && valid) __builtin_nontemporal_store(p, &sp[key]);   // read again only for full groups
     kk[j] = valid ? score_key(p) : 0u;                 // 0: below every key
   }
   // Group statistics: tiles 2q and 2q + 1 form the group; key c of tile 2q + e sits at
@@ -838,6 +839,7 @@ struct alignas(16) CollectShared {
   uint32_t fkey[kFullCap][kGroup];   // kept keys of the full groups, by slot
   uint32_t fmask[kFullCap];     // their candidates with key >= L
   uint32_t fgroup[kFullCap];    // the group in each slot
+  uint32_t fbase[kFullCap];     // superset position of each slot's first kept key
   uint32_t hist[kBins];         // bound bins (A), then superset bins (B, C)
   uint32_t red[2 * kCWaves];
   uint32_t tot[kScanRounds * kCWaves + 4];
@@ -1027,13 +1029,13 @@ __device__ uint32_t block_bound(const uint32_t (&u)[NU], uint32_t keff, uint32_t
   return lmin;
 }
 
-// The exact top-k of sequence b, run by a whole workgroup of kCThreads threads (t = threadIdx.x)
+// The exact top-k of sequence b into out[0 .. k) (global or LDS), run by a whole workgroup of
+// kCThreads threads (t = threadIdx.x)
 // on LDS `sh`. Every early return below is uniform over the workgroup.
-__device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* topk, CollectShared& sh) {
+__device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, CollectShared& sh) {
   const uint32_t t = threadIdx.x;
   int64_t c0;
   const uint32_t n = (uint32_t)cand_count(a, b, &c0);   // <= 2^22: 32-bit index math below
-  int32_t* out = topk + (size_t)b * a.k;
   const uint32_t keff = min((uint32_t)a.k, n);
   for (uint32_t i = keff + t; i < (uint32_t)a.k; i += kCThreads) out[i] = -1;
   if (keff == 0) return;
@@ -1130,30 +1132,43 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* topk,
       }
     }
     __syncthreads();
+    const uint32_t fstart = fdone;
     fdone = nfull;
     uint32_t cnt[1] = {(uint32_t)__popc(lm & ~fm)}, off[1];
     for (uint32_t i = 0, nf = (uint32_t)__popc(fm); i < nf; ++i)
       if (slot0 + i < (uint32_t)kFullCap) cnt[0] += (uint32_t)__popc(sh.fmask[slot0 + i]);
     const uint32_t total = ordered_scan(cnt, off, sh);
     if (sh.misc[5] > (uint32_t)kFullCap || T + total > (uint32_t)kLdsCand) { fits = false; break; }
+    // A group with one key at or above L is placed by its owner; a full group's place is
+    // recorded and its kept keys are placed afterwards by the lanes that read them.
     uint32_t pos = T + off[0];
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j) {
       if ((lm >> j) & 1u) {
-        const uint32_t gbase = (g0 + j) << gshift;
         if (!((fm >> j) & 1u)) {
           sh.key[pos] = mv[j];
-          sh.idx[pos] = gbase + (sv[j] & 31u);
+          sh.idx[pos] = ((g0 + j) << gshift) + (sv[j] & 31u);
           atomicAdd(&sh.hist[bin2(mv[j])], 1u);
           ++pos;
         } else {
           const uint32_t slot = slot0 + (uint32_t)__popc(fm & ((1u << j) - 1u));
-          for (uint32_t m = sh.fmask[slot]; m; m &= m - 1) {
-            const uint32_t i = (uint32_t)__ffs(m) - 1, v = sh.fkey[slot][i];
-            sh.key[pos] = v;
-            sh.idx[pos] = gbase + i;
+          sh.fbase[slot] = pos;
+          pos += (uint32_t)__popc(sh.fmask[slot]);
+        }
+      }
+    }
+    if (nfull > fstart) {                               // uniform: this tile has full groups
+      __syncthreads();
+      const int lane = t & 63, half = lane >> 5, li = lane & 31;
+      for (uint32_t j0 = fstart + 2 * (t >> 6); j0 < nfull; j0 += 2 * kCWaves) {
+        const uint32_t j = j0 + half;
+        if (j < nfull) {
+          const uint32_t m = sh.fmask[j];
+          if ((m >> li) & 1u) {
+            const uint32_t p = sh.fbase[j] + (uint32_t)__popc(m & ((1u << li) - 1u)), v = sh.fkey[j][li];
+            sh.key[p] = v;
+            sh.idx[p] = (sh.fgroup[j] << gshift) + li;
             atomicAdd(&sh.hist[bin2(v)], 1u);
-            ++pos;
           }
         }
       }
@@ -1218,7 +1233,7 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* topk,
 
 __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* topk) {
   __shared__ CollectShared sh;
-  collect_seq(a, blockIdx.x, topk, sh);
+  collect_seq(a, blockIdx.x, topk + (size_t)blockIdx.x * a.k, sh);
 }
 
 // The MFMA form of K1 when it applies (up to 16 heads, head_dim 64, 128 or 256): sets a->gs
@@ -1464,5 +1479,113 @@ extern "C" chs_status chs_index_topk_fp8_paged(int32_t batch, int32_t n_heads, i
     if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   }
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- the C4 decode step, fused
+// chs_decode_step: the selection's second kernel and the attention's split kernel are one
+// launch. Every attention split whose key slots reach past the window runs the exact top-k of
+// its sequence itself (the same collect body, into LDS) and reads its entries from there, so
+// the selection is done redundantly by those workgroups and no workgroup waits for another;
+// window-only splits start attending at once. The split of the first selected slot (head tile
+// 0) also stores the top-k row. Waves 4 .. 15 end once the selection is done; the attention
+// body is the four-wave one of chs_decode_attn. Scores, top-k, out and lse are bit-identical
+// to chs_index_topk followed by chs_decode_attn.
+namespace chs {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::AttnArgs aa, int32_t* topk) {
+  union alignas(16) StepShared {
+    CollectShared c;
+    attn::AttnShared<D, 1> at;
+  };
+  __shared__ StepShared sh;
+  __shared__ int32_t sel[kMaxK];
+  const int b = blockIdx.y, split = blockIdx.x, z = blockIdx.z;
+  const attn::SlotMap sm(aa, b);
+  const int32_t s_begin = split * aa.kps, s_end = min(s_begin + aa.kps, sm.nslots());
+  if (s_begin < s_end && s_end > sm.nswa) {           // uniform over the workgroup
+    collect_seq(ia, b, sel, sh.c);
+    __syncthreads();
+    if (z == 0 && s_begin <= sm.nswa)
+      for (int i = threadIdx.x; i < aa.k; i += kCThreads) topk[(int64_t)b * aa.k + i] = sel[i];
+    __syncthreads();                                    // the LDS is the attention's from here
+  }
+  if (threadIdx.x >= attn::kAttnThreads) return;        // whole waves
+  attn::AttnArgs a = aa;
+  a.topk = sel;
+  a.topk_stride = 0;
+  attn::NoHook none;
+  attn::attn_split<D, 1, attn::NoHook, false, false>(a, b, split, z, threadIdx.x, sh.at, none);
+}
+
+__global__ __launch_bounds__(attn::kAttnThreads) void step_combine_kernel(attn::AttnArgs a, float* out, float* lse) {
+  __shared__ attn::CombineShared<attn::kCombineSplits> sh;
+  attn::combine_tile<attn::kCombineSplits>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
+}
+
+// Workspace of chs_decode_step: the selection's, then the attention's partials.
+size_t step_ws(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, int64_t max_comp,
+               size_t* attn_off) {
+  const size_t sel = align_up(ws_layout(batch, max_comp, nullptr, nullptr), 256);
+  const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, window, k, max_comp);
+  if (attn_off) *attn_off = sel;
+  return sel + attn::ws_bytes(CHS_BF16, batch, n_heads, d, p, nullptr, nullptr, nullptr);
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" size_t chs_decode_step_workspace_size(int32_t batch, int32_t n_heads, int32_t d, int32_t window,
+                                                 int32_t k, int64_t max_comp) {
+  if (batch < 1 || n_heads < 1 || d < 1 || window < 0 || k < 1 || max_comp < 0) return 0;
+  return chs::step_ws(batch, n_heads, d, window, k, max_comp, nullptr);
+}
+
+extern "C" chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                      float scale, int32_t idx_heads, int32_t idx_dim, const void* q_idx,
+                                      const float* w, const void* k_idx, const void* q, const void* swa_kv,
+                                      const int32_t* swa_len, const void* comp_kv, const int64_t* cu_comp,
+                                      int64_t max_comp, float* scores, int32_t* topk, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace chs;
+  chs_status st = attn::check_args(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv,
+                                   cu_comp, topk, max_comp, out);
+  if (st != CHS_OK) return st;
+  if (k < 1) return CHS_ERR_SHAPE;
+  if (!q_idx || !topk || !workspace) return CHS_ERR_NULL;
+  size_t attn_off = 0;
+  const size_t need = step_ws(batch, n_heads, d, window, k, max_comp, &attn_off);
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  Args ia;
+  int lpc = 2;
+  st = topk_setup(CHS_BF16, batch, idx_heads, idx_dim, k, q_idx, w, k_idx, cu_comp, max_comp, scores, topk,
+                  workspace, attn_off, &ia, &lpc);
+  if (st != CHS_OK) return st;
+  const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, window, k, max_comp);
+  attn::AttnArgs a;
+  a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
+  a.swa_scale = nullptr; a.comp_scale = nullptr;
+  a.pg = attn::Paging{nullptr, 0, nullptr, nullptr, 0, 0, 0};
+  a.H = n_heads; a.D = d; a.W = window; a.k = k; a.topk_stride = k; a.max_comp = max_comp;
+  a.scale_log2 = scale * kLog2e;
+  a.n_splits = p.n_splits; a.kps = p.kps;
+  a.head_tiles = (n_heads + 63) / 64;
+  attn::ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace) + attn_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (topk_first(CHS_BF16, batch, &ia, lpc, s) != CHS_OK) return CHS_ERR_LAUNCH;
+  const dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
+  switch (d) {
+    case 64: hipLaunchKernelGGL(collect_attn_kernel<64>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
+    case 128: hipLaunchKernelGGL(collect_attn_kernel<128>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
+    case 256: hipLaunchKernelGGL(collect_attn_kernel<256>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
+    default: hipLaunchKernelGGL(collect_attn_kernel<512>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
+  }
+  if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  const int words_per_block = attn::kAttnThreads / attn::kCombineLanes;
+  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
+                   (unsigned)batch);
+  hipLaunchKernelGGL(step_combine_kernel, cgrid, dim3(attn::kAttnThreads), 0, s, a, out, lse);
   return launch_status();
 }

@@ -252,6 +252,28 @@ chs_status chs_decode_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int3
                            float* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- chs_decode_step: the C4 decode step (index scores, top-k, attention) in one call --------
+ * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", Kernel 層一堆狠活 (the indexer's top-512
+ * feeds the attention over the window and the selected C4 entries) and "SGLang 如何为 DeepSeek
+ * V4 打造「Day-0」推理加速", 创新 2 (the selected set goes to the attention with no copy).
+ * Computes exactly chs_index_topk(CHS_BF16, batch, idx_heads, idx_dim, k, q_idx, w, k_idx,
+ * cu_comp, max_comp, scores, topk, ...) followed by chs_decode_attn(CHS_BF16, batch, n_heads, d,
+ * window, k, scale, q, swa_kv, swa_len, comp_kv, cu_comp, topk, max_comp, out, lse, ...): the
+ * candidates are the compressed entries (cu_comp), and scores, topk, out and lse are
+ * bit-identical to those two calls. The selection's second kernel runs inside the attention's
+ * split kernel, so the step takes three launches instead of four.
+ * Argument meanings, layouts and ranges are those of the two calls (bf16 storage only;
+ * q_idx must not be NULL; scores may be NULL); topk [batch, k] is an output.
+ * workspace: chs_decode_step_workspace_size(batch, n_heads, d, window, k, max_comp) bytes. */
+size_t chs_decode_step_workspace_size(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                      int64_t max_comp);
+chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, float scale,
+                           int32_t idx_heads, int32_t idx_dim, const void* q_idx, const float* w,
+                           const void* k_idx, const void* q, const void* swa_kv, const int32_t* swa_len,
+                           const void* comp_kv, const int64_t* cu_comp, int64_t max_comp, float* scores,
+                           int32_t* topk, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* ---- Paged pools: chs_decode_attn_paged, chs_append_paged ----------------------------------
  * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 1 (ShadowRadix: a per-request index
  * projected onto separate physical pools for the window, the C4 and the C128 entries, plus the

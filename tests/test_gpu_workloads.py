@@ -67,16 +67,24 @@ def _check_attn_c4(wl, layer, q, sel, out, lse, b):
     assert_lse(lse[b], l_ref, f"lse seq {b}", 1e-3 if wl.bf16 else 1e-5)
 
 
-def _run_c4(wl, layer, rng, score_seqs, attn_seqs, full=False):
-    print(f"case: workload {wl.index} ({wl.name}) C4 layer: generating inputs", flush=True)
+def _run_c4(wl, layer, rng, score_seqs, attn_seqs, full=False, fused=False):
+    """fused: the decode step as one chs_decode_step call instead of chs_index_topk followed by
+    chs_decode_attn."""
+    print(f"case: workload {wl.index} ({wl.name}) C4 layer{' (chs_decode_step)' if fused else ''}: "
+          "generating inputs", flush=True)
     inp = W.device_inputs(wl, layer, dev())
     cug = wl.cu_groups(layer)
     max_g = int((cug[1:] - cug[:-1]).max())
     comp = chs.compress(inp["X"], inp["Z"], inp["bias"], layer.m, inp["cu_tokens"], inp["cu_groups"], max_g)
     scores = torch.empty(max(int(cug[-1]), 1), dtype=torch.float32, device=dev())[:int(cug[-1])]
-    topk, _ = chs.index_topk(inp["q_idx"], inp["w"], inp["k_idx"], inp["cu_groups"], layer.k, max_g, scores)
-    out, lse = chs.decode_attn(inp["q"], inp["swa_kv"], inp["swa_len"], comp, inp["cu_groups"], topk,
-                               wl.d ** -0.5, max_g)
+    if fused:
+        topk, out, lse, _ = chs.decode_step(inp["q_idx"], inp["w"], inp["k_idx"], inp["q"], inp["swa_kv"],
+                                            inp["swa_len"], comp, inp["cu_groups"], layer.k, wl.d ** -0.5,
+                                            max_g, scores)
+    else:
+        topk, _ = chs.index_topk(inp["q_idx"], inp["w"], inp["k_idx"], inp["cu_groups"], layer.k, max_g, scores)
+        out, lse = chs.decode_attn(inp["q"], inp["swa_kv"], inp["swa_len"], comp, inp["cu_groups"], topk,
+                                   wl.d ** -0.5, max_g)
     torch.cuda.synchronize()
     print(f"case: workload {wl.index} C4 layer: checking", flush=True)
     del inp["X"], inp["Z"]
@@ -141,6 +149,11 @@ def test_workload2_c4_128k_bf16():
     _run_c4(wl, wl.layers[0], np.random.default_rng(2), [0], [0], full=True)
 
 
+def test_workload2_c4_128k_bf16_fused_step():
+    wl = W.workload(2)
+    _run_c4(wl, wl.layers[0], np.random.default_rng(2), [0], [0], full=True, fused=True)
+
+
 def test_workload3_c128_1m_bs4_bf16():
     wl = W.workload(3)
     _run_c128(wl, wl.layers[0], np.random.default_rng(3), [3])
@@ -149,6 +162,11 @@ def test_workload3_c128_1m_bs4_bf16():
 def test_workload4_c4_1m_bf16():
     wl = W.workload(4)
     _run_c4(wl, wl.layers[0], np.random.default_rng(4), [0], [0])
+
+
+def test_workload4_c4_1m_bf16_fused_step():
+    wl = W.workload(4)
+    _run_c4(wl, wl.layers[0], np.random.default_rng(4), [0], [0], fused=True)
 
 
 def test_workload4_standalone_topk():
@@ -175,5 +193,7 @@ def test_workload5_mixed_bs64():
     rng = np.random.default_rng(5)
     c4, c128 = wl.layers
     _run_c4(wl, c4, rng, [0, 17, 40, 63], [0, 33, 63])
+    torch.cuda.empty_cache()
+    _run_c4(wl, c4, rng, [9], [9, 50], fused=True)
     torch.cuda.empty_cache()
     _run_c128(wl, c128, rng, [5, 63])
