@@ -230,7 +230,9 @@ __device__ __forceinline__ uint32_t mask_below(uint64_t m) {
 // Block-wide helpers for the K2 block (kCWaves waves, declared below). The wave partials go
 // through LDS and every thread reads all of them with 16-byte loads, so no dependent chain of
 // LDS reads forms. `scratch` is 16-byte aligned; each call ends with a barrier.
-template <int NW>
+// TRAIL = false leaves out the closing barrier where the caller reaches another barrier before
+// `scratch` is written again.
+template <int NW, bool TRAIL = true>
 __device__ uint32_t block_exclusive_sum_t(uint32_t v, uint32_t* total, uint32_t* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_inclusive_sum(v);
@@ -243,12 +245,12 @@ __device__ uint32_t block_exclusive_sum_t(uint32_t v, uint32_t* total, uint32_t*
 #pragma unroll
     for (int j = 0; j < 4; ++j) { before += (w + j < wave) ? p[j] : 0u; all += p[j]; }
   }
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   *total = all;
   return before + inc - v;
 }
 
-template <int NW>
+template <int NW, bool TRAIL = true>
 __device__ void block_minmax_t(uint32_t* vmin, uint32_t* vmax, uint32_t* scratch) {
   const int wave = threadIdx.x >> 6;
   const uint32_t lo = ~wave_max(~*vmin), hi = wave_max(*vmax);
@@ -262,7 +264,7 @@ __device__ void block_minmax_t(uint32_t* vmin, uint32_t* vmax, uint32_t* scratch
     l = min(min(l, min(x[0], x[1])), min(x[2], x[3]));
     h = max(max(h, max(y[0], y[1])), max(y[2], y[3]));
   }
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   *vmin = l; *vmax = h;
 }
 
@@ -940,34 +942,35 @@ __device__ uint32_t block_radix_select(Get get, uint32_t m, uint32_t r, uint32_t
 
 // Writes, ascending, the indices of the m candidates (key from `key`, index from `idx`, in
 // index order) that are above tau or among the first ties_take equal to it. R rounds of the
-// block per batch (R * 1024 candidates).
+// block per batch (R * 1024 candidates). One ordered scan per batch counts, for every
+// candidate, the keys above tau (low 16 bits) and the ties (high 16 bits) before it: a
+// candidate is taken if it is above tau or is a tie with fewer than ties_take ties before it,
+// and its place is (keys above tau before it) + min(ties before it, ties_take).
 template <int R, typename GK, typename GI>
 __device__ void ordered_select(GK key, GI idx, uint32_t m, uint32_t tau, uint32_t ties_take, uint32_t keff,
                                int32_t* out, CollectShared& sh) {
-  uint32_t ties_before = 0, sel_before = 0;
+  static_assert(R * kCThreads < 65536, "per-batch counts must fit 16 bits");
+  uint32_t gt_before = 0, ties_before = 0;
   for (uint32_t x0 = 0; x0 < m; x0 += R * kCThreads) {
     uint32_t kk[R], c[R], off[R];
 #pragma unroll
     for (int q = 0; q < R; ++q) kk[q] = key(min(x0 + q * kCThreads + threadIdx.x, m - 1));
 #pragma unroll
-    for (int q = 0; q < R; ++q) c[q] = (x0 + q * kCThreads + threadIdx.x < m && kk[q] == tau) ? 1u : 0u;
-    const uint32_t tie_total = ordered_scan(c, off, sh);
-    uint32_t take = 0;
+    for (int q = 0; q < R; ++q) {
+      const bool in = x0 + q * kCThreads + threadIdx.x < m;
+      c[q] = !in ? 0u : kk[q] > tau ? 1u : kk[q] == tau ? 0x10000u : 0u;
+    }
+    const uint32_t total = ordered_scan(c, off, sh);
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       const bool in = x0 + q * kCThreads + threadIdx.x < m;
-      const bool t = in && (kk[q] > tau || (kk[q] == tau && ties_before + off[q] < ties_take));
-      take |= (t ? 1u : 0u) << q;
-      c[q] = t ? 1u : 0u;
+      const uint32_t gt = gt_before + (off[q] & 0xFFFFu), eq = ties_before + (off[q] >> 16);
+      const bool take = in && (kk[q] > tau || (kk[q] == tau && eq < ties_take));
+      const uint32_t pos = gt + min(eq, ties_take);
+      if (take && pos < keff) out[pos] = (int32_t)idx(x0 + q * kCThreads + threadIdx.x);
     }
-    const uint32_t sel_total = ordered_scan(c, off, sh);
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const uint32_t pos = sel_before + off[q];
-      if (((take >> q) & 1u) && pos < keff) out[pos] = (int32_t)idx(x0 + q * kCThreads + threadIdx.x);
-    }
-    ties_before += tie_total;
-    sel_before += sel_total;
+    gt_before += total & 0xFFFFu;
+    ties_before += total >> 16;
   }
 }
 
@@ -995,8 +998,9 @@ __device__ __attribute__((noinline)) uint32_t tau_by_radix(CollectShared& sh, ui
 }
 
 // The bound of the collect step: over the workgroup's nonzero values u (NU per thread, at
-// least keff of them), the smallest value in the bin holding the keff-th largest or above,
-// with 2048 monotone bins (u - umin) >> shift. Also returns the largest value in *umax.
+// least keff of them), the lower edge of the bin holding the keff-th largest, with 2048
+// monotone bins (u - umin) >> shift: every value in that bin or above is at least the edge,
+// and there are at least keff of them. Also returns the largest value in *umax.
 template <int NU>
 __device__ uint32_t block_bound(const uint32_t (&u)[NU], uint32_t keff, uint32_t* umax, CollectShared& sh) {
   const uint32_t t = threadIdx.x;
@@ -1006,7 +1010,7 @@ __device__ uint32_t block_bound(const uint32_t (&u)[NU], uint32_t keff, uint32_t
     lo = min(lo, u[j] - 1u);                            // key 0 wraps to the top: ignored
     hi = max(hi, u[j]);
   }
-  block_minmax_t<kCWaves>(&lo, &hi, sh.red);            // its barriers also order the clears
+  block_minmax_t<kCWaves, false>(&lo, &hi, sh.red);     // its barrier also orders the clears
   const uint32_t vmin = lo + 1u;
   *umax = hi;
   const int span_bits = differing_bits(0u, hi - vmin);
@@ -1017,16 +1021,10 @@ __device__ uint32_t block_bound(const uint32_t (&u)[NU], uint32_t keff, uint32_t
   __syncthreads();
   const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
   uint32_t total;
-  const uint32_t run = block_exclusive_sum_t<kCWaves>(h0 + h1, &total, sh.red);
+  const uint32_t run = block_exclusive_sum_t<kCWaves, false>(h0 + h1, &total, sh.red);
   if (run < keff && run + h0 + h1 >= keff) sh.misc[0] = run + h0 >= keff ? kBins - 1 - 2 * t : kBins - 2 - 2 * t;
   __syncthreads();
-  const uint32_t floor_key = vmin + (sh.misc[0] << shift);
-  uint32_t lmin = 0xFFFFFFFFu, unused = 0;
-#pragma unroll
-  for (int j = 0; j < NU; ++j)
-    if (u[j] >= floor_key) lmin = min(lmin, u[j]);
-  block_minmax_t<kCWaves>(&lmin, &unused, sh.red);
-  return lmin;
+  return vmin + (sh.misc[0] << shift);
 }
 
 // The exact top-k of sequence b into out[0 .. k) (global or LDS), run by a whole workgroup of
@@ -1190,7 +1188,7 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, 
   {
     const uint32_t h0 = sh.hist[kBins - 1 - 2 * t], h1 = sh.hist[kBins - 2 - 2 * t];
     uint32_t total;
-    const uint32_t run = block_exclusive_sum_t<kCWaves>(h0 + h1, &total, sh.red);
+    const uint32_t run = block_exclusive_sum_t<kCWaves, false>(h0 + h1, &total, sh.red);
     if (run < keff && run + h0 + h1 >= keff) {
       if (run + h0 >= keff) { sh.misc[0] = kBins - 1 - 2 * t; sh.misc[1] = run; }
       else { sh.misc[0] = kBins - 2 - 2 * t; sh.misc[1] = run + h0; }
