@@ -988,13 +988,19 @@ __device__ __attribute__((noinline)) void select_global(__amdgpu_buffer_rsrc_t s
 
 // A crowded threshold bin (heavy ties): tau and the ties to take by radix steps over the LDS
 // superset, keys in [L, their maximum].
-__device__ __attribute__((noinline)) uint32_t tau_by_radix(CollectShared& sh, uint32_t T, uint32_t keff, uint32_t L,
-                                                           uint32_t* ties_take) {
+// Returned by value (in registers): an out-parameter would put the caller's variable in
+// scratch memory on the common path too.
+struct TauTies {
+  uint32_t tau, ties_take;
+};
+__device__ __attribute__((noinline)) TauTies tau_by_radix(CollectShared& sh, uint32_t T, uint32_t keff, uint32_t L) {
   uint32_t hi = 0;
   for (uint32_t i = threadIdx.x; i < T; i += kCThreads) hi = max(hi, sh.key[i]);
   uint32_t unused = 0xFFFFFFFFu;
   block_minmax_t<kCWaves>(&unused, &hi, sh.red);
-  return block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, ties_take);
+  TauTies r;
+  r.tau = block_radix_select([&](uint32_t i) { return sh.key[i]; }, T, keff, L, hi, sh, &r.ties_take);
+  return r;
 }
 
 // The bound of the collect step: over the workgroup's nonzero values u (NU per thread, at
@@ -1222,7 +1228,9 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, 
     tau = sh.misc[3];
     ties_take = sh.misc[4];
   } else {                                              // a crowded bin (heavy ties)
-    tau = tau_by_radix(sh, T, keff, L, &ties_take);
+    const TauTies r = tau_by_radix(sh, T, keff, L);
+    tau = r.tau;
+    ties_take = r.ties_take;
   }
   auto lk = [&](uint32_t i) { return sh.key[i]; };
   auto li = [&](uint32_t i) { return sh.idx[i]; };
