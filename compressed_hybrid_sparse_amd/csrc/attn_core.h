@@ -16,6 +16,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
+// Loads through pointers the compiler cannot place (a row pointer that may be null, a top-k row
+// that may live in LDS) would otherwise be flat loads, which also hold the LDS counter: these
+// name the address space.
+__device__ __forceinline__ u32x4 load_global_u32x4(const void* p) {
+  return *(const __attribute__((address_space(1))) u32x4*)(p);
+}
+__device__ __forceinline__ float load_global_f32(const float* p) {
+  return *(const __attribute__((address_space(1))) float*)(p);
+}
+__device__ __forceinline__ int32_t load_global_i32(const int32_t* p) {
+  return *(const __attribute__((address_space(1))) int32_t*)(p);
+}
+__device__ __forceinline__ int32_t load_lds_i32(const int32_t* p) {
+  return *(const __attribute__((address_space(3))) int32_t*)(p);
+}
+
 // An LDS address as the transposing load builtin takes it.
 __device__ __forceinline__ __attribute__((address_space(3))) v4i16* lds_v4i16(const uint16_t* p) {
   return (__attribute__((address_space(3))) v4i16*)(p);
@@ -139,17 +155,26 @@ __device__ __forceinline__ float row16_sum(float v) {
 // issue back to back. When a load is one whole row every operand is the same for the whole wave.
 // PAGED: entries go through the page table (one more dependent read per row, clamped the same
 // way), and the window through the sequence's window page.
+// sel: the sequence's top-k row in LDS, read instead of a.topk when given.
 template <int D, int LOADS, int RPI, int NW, typename ET, bool PAGED = false>
 __device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm, int b, int32_t s0, int32_t s_end,
-                                           int wave, int lr, const ET* (&rp)[LOADS], const float* (&rs)[LOADS]) {
+                                           int wave, int lr, const ET* (&rp)[LOADS], const float* (&rs)[LOADS],
+                                           const int32_t* sel = nullptr) {
   constexpr int NLOADS = kKeysPerChunk / RPI;
   const ET* swa = static_cast<const ET*>(a.swa);
   const ET* comp = static_cast<const ET*>(a.comp);
   int32_t idx[LOADS];
   if (a.topk != nullptr && a.k > 0) {
-    const int32_t* tk = a.topk + (int64_t)b * a.topk_stride;
+    if (sel) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) idx[i] = tk[min(max(s0 + (i * NW + wave) * RPI + lr - sm.nswa, 0), a.k - 1)];
+      for (int i = 0; i < LOADS; ++i)
+        idx[i] = load_lds_i32(sel + min(max(s0 + (i * NW + wave) * RPI + lr - sm.nswa, 0), a.k - 1));
+    } else {
+      const int32_t* tk = a.topk + (int64_t)b * a.topk_stride;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        idx[i] = load_global_i32(tk + min(max(s0 + (i * NW + wave) * RPI + lr - sm.nswa, 0), a.k - 1));
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) idx[i] = s0 + (i * NW + wave) * RPI + lr - sm.nswa;
@@ -203,9 +228,12 @@ struct NoHook {
 // through LDS in a fixed order, so all four waves hold bit-identical logits and run the same
 // softmax; and computes P.V for its quarter. before_rows(s0) runs, uniformly over the
 // workgroup, before the rows of the chunk at slot s0 are looked up.
+// sm is sequence b's slot map (SlotMap(a, b)), passed in by callers that already hold it; sel,
+// when given, is the sequence's top-k row in LDS (read instead of a.topk).
 template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false>
-__device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, int z0, int tid,
-                                           AttnShared<D, TILES>& sh, Hook& before_rows) {
+__device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& sm, int b, int split, int z0, int tid,
+                                              AttnShared<D, TILES>& sh, Hook& before_rows,
+                                              const int32_t* sel = nullptr) {
   constexpr int KC = kKeysPerChunk;
   constexpr int KN_PITCH = D + 8;          // bf16 elements per row-major LDS row
   constexpr int P_PITCH = KC + 8;
@@ -227,7 +255,6 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
   const int z = z0 + tile;
   const int lr = RPI > 1 ? lane / VPR : 0, cv = lane % VPR;
   const int h_base = z * 16;
-  const SlotMap sm(a, b);
   const int32_t s_begin = split * a.kps;
   const int32_t s_end = min(s_begin + a.kps, sm.nslots());
 
@@ -236,20 +263,20 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
   const ET* rp[LOADS];
   const float* rs[LOADS];
   before_rows(s_begin);
-  chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s_begin, s_end, wave, lr, rp, rs);
+  chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s_begin, s_end, wave, lr, rp, rs, sel);
 
   // Q fragment (A operand): row c of the tile's 16 heads, d = d0 + 32t + 8g .. +8 (d0 = this
-  // wave's quarter); head index clamped, then zeroed, so the loads are unconditional.
+  // wave's quarter). A head past H reads head H - 1 (clamped, so the loads are unconditional);
+  // its rows of S, P and O are never stored or combined, and every other head's rows are
+  // computed independently of them. Nothing waits on Q before the first chunk's rows are
+  // requested.
   const int d0 = SPLIT_S ? QD * quarter : 0;
   bf16x8 qf[QD / 32];
   {
     const int h = h_base + c;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + min(h, a.H - 1)) * D + d0;
-    u32x4 qv[QD / 32];
 #pragma unroll
-    for (int t = 0; t < QD / 32; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qp + 32 * t + 8 * g);
-#pragma unroll
-    for (int t = 0; t < QD / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, h < a.H ? qv[t] : u32x4{0, 0, 0, 0});
+    for (int t = 0; t < QD / 32; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(qp + 32 * t + 8 * g);
   }
   f32x4 o[TPW];
 #pragma unroll
@@ -264,8 +291,8 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
     float vs[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      v[i] = rp[i] ? *reinterpret_cast<const u32x4*>(rp[i] + EPV * cv) : u32x4{0, 0, 0, 0};
-      if (FP8) vs[i] = rp[i] ? *rs[i] : 0.f;
+      v[i] = rp[i] ? load_global_u32x4(rp[i] + EPV * cv) : u32x4{0, 0, 0, 0};
+      if (FP8) vs[i] = rp[i] ? load_global_f32(rs[i]) : 0.f;
     }
     __syncthreads();   // the previous chunk's LDS reads are done
 #pragma unroll
@@ -295,7 +322,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
     }
     if (s0 + KC < s_end) {
       before_rows(s0 + KC);
-      chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s0 + KC, s_end, wave, lr, rp, rs);
+      chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s0 + KC, s_end, wave, lr, rp, rs, sel);
     }
     __syncthreads();
     // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
@@ -395,6 +422,13 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, 
       }
     }
   }
+}
+
+template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false>
+__device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, int z0, int tid,
+                                           AttnShared<D, TILES>& sh, Hook& before_rows) {
+  const SlotMap sm(a, b);
+  attn_split_sm<D, TILES, Hook, FP8, PAGED>(a, sm, b, split, z0, tid, sh, before_rows);
 }
 
 // LDS of one combine block that merges at most MAXS splits.

@@ -635,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(Args a) {
     if (kScaled) p *= ks[j];
     const int64_t key = key0 + 16 * j + c;
     const bool valid = key < n;
-    if (g == 0 && valid) __builtin_nontemporal_store(p, &sp[key]);   // read again only for full groups
+    if (g == 0 && valid) sp[key] = p;
     kk[j] = valid ? score_key(p) : 0u;                 // 0: below every key
   }
   // Group statistics: tiles 2q and 2q + 1 form the group; key c of tile 2q + e sits at
@@ -1494,8 +1494,8 @@ extern "C" chs_status chs_index_topk_fp8_paged(int32_t batch, int32_t n_heads, i
 // its sequence itself (the same collect body, into LDS) and reads its entries from there, so
 // the selection is done redundantly by those workgroups and no workgroup waits for another;
 // window-only splits start attending at once. The split of the first selected slot (head tile
-// 0) also stores the top-k row. Waves 4 .. 15 end once the selection is done; the attention
-// body is the four-wave one of chs_decode_attn. Scores, top-k, out and lse are bit-identical
+// 0) also stores the top-k row, from waves 4 .. 15, which then end; the attention body is the
+// four-wave one of chs_decode_attn, reading the selection from LDS. Scores, top-k, out and lse are bit-identical
 // to chs_index_topk followed by chs_decode_attn.
 namespace chs {
 namespace {
@@ -1511,19 +1511,21 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
   const int b = blockIdx.y, split = blockIdx.x, z = blockIdx.z;
   const attn::SlotMap sm(aa, b);
   const int32_t s_begin = split * aa.kps, s_end = min(s_begin + aa.kps, sm.nslots());
-  if (s_begin < s_end && s_end > sm.nswa) {           // uniform over the workgroup
+  const bool selects = s_begin < s_end && s_end > sm.nswa;   // uniform over the workgroup
+  if (selects) {
     collect_seq(ia, b, sel, sh.c);
-    __syncthreads();
-    if (z == 0 && s_begin <= sm.nswa)
-      for (int i = threadIdx.x; i < aa.k; i += kCThreads) topk[(int64_t)b * aa.k + i] = sel[i];
-    __syncthreads();                                    // the LDS is the attention's from here
+    __syncthreads();                                    // sel is complete; the LDS is the attention's
   }
-  if (threadIdx.x >= attn::kAttnThreads) return;        // whole waves
-  attn::AttnArgs a = aa;
-  a.topk = sel;
-  a.topk_stride = 0;
+  if (threadIdx.x >= attn::kAttnThreads) {              // whole waves
+    // The attention's waves issue no global store before their gathers; the top-k row is
+    // stored by these ones.
+    if (selects && z == 0 && s_begin <= sm.nswa)
+      for (int i = threadIdx.x - attn::kAttnThreads; i < aa.k; i += kCThreads - attn::kAttnThreads)
+        topk[(int64_t)b * aa.k + i] = sel[i];
+    return;
+  }
   attn::NoHook none;
-  attn::attn_split<D, 1, attn::NoHook, false, false>(a, b, split, z, threadIdx.x, sh.at, none);
+  attn::attn_split_sm<D, 1, attn::NoHook, false, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
 }
 
 __global__ __launch_bounds__(attn::kAttnThreads) void step_combine_kernel(attn::AttnArgs a, float* out, float* lse) {
