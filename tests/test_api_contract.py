@@ -293,6 +293,37 @@ def test_decode_attn_fp8_validation(kw, code):
     assert attn8(**kw) == code
 
 
+def step(batch=1, H=64, d=512, W=128, k=512, scale=0.04, nh=4, dI=128, qi=FAKE, w=FAKE, ki=FAKE, q=FAKE, swa=FAKE,
+         sl=FAKE, comp=FAKE, cu=FAKE, maxc=1000, sc=FAKE, tk=FAKE, out=FAKE, lse=FAKE, ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_decode_step_workspace_size(batch, H, d, W, k, maxc)
+    return L.chs_decode_step(batch, H, d, W, k, ctypes.c_float(scale), nh, dI, qi, w, ki, q, swa, sl, comp, cu, maxc,
+                             sc, tk, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(H=0), SHAPE), (dict(H=129), SHAPE), (dict(d=96), SHAPE), (dict(d=1024), SHAPE),
+    (dict(W=-1), SHAPE), (dict(k=0), SHAPE), (dict(k=2049), SHAPE), (dict(scale=0.0), SHAPE),
+    (dict(scale=float("nan")), SHAPE), (dict(maxc=-1), SHAPE), (dict(nh=0), SHAPE), (dict(nh=17), SHAPE),
+    (dict(dI=4), SHAPE), (dict(dI=1024), SHAPE), (dict(qi=None), NULL), (dict(w=None), NULL), (dict(ki=None), NULL),
+    (dict(q=None), NULL), (dict(swa=None), NULL), (dict(sl=None), NULL), (dict(comp=None), NULL),
+    (dict(cu=None), NULL), (dict(tk=None), NULL), (dict(out=None), NULL), (dict(ws=None), NULL), (dict(wsb=8), WS),
+])
+def test_decode_step_validation(kw, code):
+    assert step(**kw) == code
+
+
+def test_decode_step_workspace_covers_both_calls():
+    L = chs.lib()
+    for batch, H, d, W, k, G in [(1, 64, 512, 128, 512, 262144), (64, 64, 512, 128, 512, 50000), (2, 8, 64, 128, 64, 256)]:
+        need = L.chs_decode_step_workspace_size(batch, H, d, W, k, G)
+        assert need >= (L.chs_index_topk_workspace_size(batch, G, k)
+                        + L.chs_decode_attn_workspace_size(1, batch, H, d, W, k, G))
+    assert L.chs_decode_step_workspace_size(0, 64, 512, 128, 512, 10) == 0
+    assert L.chs_decode_step_workspace_size(1, 64, 512, 128, 0, 10) == 0
+
+
 def test_workspace_sizes_are_monotone():
     L = chs.lib()
     a = [L.chs_index_topk_workspace_size(b, n, 512) for b, n in [(1, 1000), (1, 262144), (4, 262144)]]
