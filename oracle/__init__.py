@@ -26,7 +26,9 @@ _p = ctypes.c_void_p
 def _load():
     global _lib
     if _lib is None:
-        path = os.path.join(HERE, "liboracle.so")
+        # CHS_ORACLE_LIB names another build of oracle.c: the mutation tests load copies with a
+        # planted mistake to show that the pins catch it.
+        path = os.environ.get("CHS_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run oracle/build.py")
         lib = ctypes.CDLL(path)
