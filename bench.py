@@ -371,6 +371,30 @@ def main():
         decode_paged(i)
     paged_ms = graph_loop_ms(decode_paged, nk)
 
+    # The C128 dense step at workload 3's shape: 4 sequences of 1,048,576 tokens, 8192 entries each
+    # (all attended) plus the 128-token window, 64 heads x 512, through chs_decode_attn with no top-k.
+    # The entries are seeded normals (the attention's cost does not depend on their values); 10
+    # rotated copies of the 32 MiB entry pool defeat the 256 MB Infinity Cache.
+    B3, G3 = 4, 8192
+    g3 = torch.Generator(device=dev).manual_seed(33)
+    pools3 = [torch.randn(B3 * G3, d, generator=g3, device=dev).bfloat16() for _ in range(10)]
+    cu3 = torch.arange(0, (B3 + 1) * G3, G3, dtype=torch.int64, device=dev)
+    swa3 = torch.randn(B3, wl.window, d, generator=g3, device=dev).bfloat16()
+    swa_len3 = torch.full((B3,), wl.window, dtype=torch.int32, device=dev)
+    q3 = torch.randn(B3, H, d, generator=g3, device=dev).bfloat16()
+    out3 = torch.empty(B3, H, d, dtype=torch.float32, device=dev)
+    lse3 = torch.empty(B3, H, dtype=torch.float32, device=dev)
+    ws3 = chs.decode_attn_workspace(torch.bfloat16, B3, H, d, wl.window, 0, G3, dev)
+
+    def c128(i):
+        chs.decode_attn(q3, swa3, swa_len3, pools3[i % len(pools3)], cu3, None, scale, G3, ws3, out3, lse3)
+
+    for i in range(len(pools3)):
+        c128(i)
+    c128_ms = graph_loop_ms(c128, len(pools3))
+    c128_bytes = B3 * (G3 + wl.window) * d * 2 + B3 * H * d * 2 + B3 * H * d * 4 + B3 * H * 4
+    del pools3
+
     # Per-call breakdown (events around each call; each event adds a little to what it brackets).
     bd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -495,6 +519,13 @@ def main():
                 "algorithmic_bytes": step_bytes,
                 "hbm_frac": None if fused_graph_ms is None else
                 round(step_bytes / (median(fused_graph_ms) * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)},
+            "decode_c128_us": {
+                "value_source": "graph replay", "call": "chs_decode_attn (no top-k: every entry)",
+                "workload": "c128_1m_bs4_bf16 (4 x 8192 entries + window 128, 64 heads x 512)",
+                "graph_median": None if c128_ms is None else round(median(c128_ms) * 1e3, 2),
+                "algorithmic_bytes": c128_bytes,
+                "hbm_frac": None if c128_ms is None else
+                round(c128_bytes / (median(c128_ms) * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)},
             "decode_step_fp8_us": {
                 "value_source": "graph replay", "call": "chs_index_topk_fp8 + chs_decode_attn_fp8",
                 "graph_median": None if fp8_graph_ms is None else round(median(fp8_graph_ms) * 1e3, 2),

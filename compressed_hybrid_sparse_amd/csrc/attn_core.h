@@ -229,8 +229,11 @@ struct NoHook {
 // softmax; and computes P.V for its quarter. before_rows(s0) runs, uniformly over the
 // workgroup, before the rows of the chunk at slot s0 are looked up.
 // sm is sequence b's slot map (SlotMap(a, b)), passed in by callers that already hold it; sel,
-// when given, is the sequence's top-k row in LDS (read instead of a.topk).
-template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false>
+// when given, is the sequence's top-k row in LDS (read instead of a.topk). PF: how many chunks
+// ahead the rows are requested (0: each chunk's rows when its turn comes; 1 or 2: a split of
+// several chunks keeps that many chunks of rows in flight, in as many register buffers, while
+// it computes).
+template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false, int PF = 0>
 __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& sm, int b, int split, int z0, int tid,
                                               AttnShared<D, TILES>& sh, Hook& before_rows,
                                               const int32_t* sel = nullptr) {
@@ -285,15 +288,34 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
 #pragma unroll
   for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
 
-  for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) {
-    // 1. gather the chunk's rows (coalesced 16-byte loads) into a row-major LDS tile.
-    u32x4 v[LOADS];
-    float vs[LOADS];
+  static_assert(PF >= 0 && PF <= 2, "prefetch depth");
+  constexpr int NB = PF == 2 ? 2 : 1;      // register buffers of chunk rows
+  u32x4 v[NB][LOADS];
+  float vs[NB][LOADS];
+  bool vok[NB][LOADS];
+  auto load_rows = [&](auto bc) {
+    constexpr int B = decltype(bc)::value;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      v[i] = rp[i] ? load_global_u32x4(rp[i] + EPV * cv) : u32x4{0, 0, 0, 0};
-      if (FP8) vs[i] = rp[i] ? load_global_f32(rs[i]) : 0.f;
+      v[B][i] = rp[i] ? load_global_u32x4(rp[i] + EPV * cv) : u32x4{0, 0, 0, 0};
+      if (FP8) vs[B][i] = rp[i] ? load_global_f32(rs[i]) : 0.f;
+      if (PF == 2) vok[B][i] = rp[i] != nullptr;
     }
+  };
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, NB - 1> B1;
+  if (PF >= 1) load_rows(B0{});
+  if (PF == 2 && s_begin + KC < s_end) {
+    before_rows(s_begin + KC);
+    chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s_begin + KC, s_end, wave, lr, rp, rs, sel);
+    load_rows(B1{});
+  }
+  // One chunk at slot s0 from register buffer B: rows into LDS, then the next rows requested.
+  auto stage = [&](auto bc, int32_t s0) {
+    constexpr int B = decltype(bc)::value;
+    // 1. gather the chunk's rows (coalesced 16-byte loads) into a row-major LDS tile (with PF
+    // they were requested PF chunks earlier).
+    if (PF == 0) load_rows(B0{});
     __syncthreads();   // the previous chunk's LDS reads are done
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -306,23 +328,27 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
           u32x4 lo, hi;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t x = v[i][e];
+            const uint32_t x = v[B][i][e];
             const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
             const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
             if (e < 2) { lo[2 * e] = p0; lo[2 * e + 1] = p1; } else { hi[2 * e - 4] = p0; hi[2 * e - 3] = p1; }
           }
           *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 16 * cv]) = lo;
           *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 16 * cv + 8]) = hi;
-          if (cv == 0) sh.rowsc[r] = vs[i];
+          if (cv == 0) sh.rowsc[r] = vs[B][i];
         } else {
-          *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 8 * cv]) = v[i];
+          *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 8 * cv]) = v[B][i];
         }
-        if (cv == 0) sh.rowok[r] = rp[i] != nullptr;
+        // With two buffers the row pointers already describe a later chunk; otherwise they are
+        // still this chunk's.
+        if (cv == 0) sh.rowok[r] = PF == 2 ? vok[B][i] : rp[i] != nullptr;
       }
     }
-    if (s0 + KC < s_end) {
-      before_rows(s0 + KC);
-      chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s0 + KC, s_end, wave, lr, rp, rs, sel);
+    const int32_t nxt = s0 + (PF == 2 ? 2 : 1) * KC;
+    if (nxt < s_end) {
+      before_rows(nxt);
+      chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, nxt, s_end, wave, lr, rp, rs, sel);
+      if (PF >= 1) load_rows(bc);
     }
     __syncthreads();
     // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
@@ -404,6 +430,14 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
       const v8i16 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8, vb), o[j], 0, 0, 0);
     }
+  };
+  if (PF == 2) {
+    for (int32_t s0 = s_begin; s0 < s_end; s0 += 2 * KC) {   // the two buffers in turn
+      stage(B0{}, s0);
+      if (s0 + KC < s_end) stage(B1{}, s0 + KC);
+    }
+  } else {
+    for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) stage(B0{}, s0);
   }
   // Partial result of this split: unnormalised O in the MFMA accumulator layout (one 16-byte
   // store per tile and lane, coalesced; quarter q holds tiles TPW q ..), running max (base 2)
@@ -424,11 +458,11 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
   }
 }
 
-template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false>
+template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false, int PF = 0>
 __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int split, int z0, int tid,
                                            AttnShared<D, TILES>& sh, Hook& before_rows) {
   const SlotMap sm(a, b);
-  attn_split_sm<D, TILES, Hook, FP8, PAGED>(a, sm, b, split, z0, tid, sh, before_rows);
+  attn_split_sm<D, TILES, Hook, FP8, PAGED, PF>(a, sm, b, split, z0, tid, sh, before_rows);
 }
 
 // LDS of one combine block that merges at most MAXS splits.
@@ -442,7 +476,9 @@ struct CombineShared {
 // Merges the splits of 16-head group hg of sequence b for output block bx (64 words of the
 // MFMA-layout tile) with kAttnThreads threads (tid < kAttnThreads), by the log-sum-exp
 // identity: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2.
-template <int MAXS>
+// KB: partial loads a lane requests at once (its splits sq, sq + 4, ...; 4 * KB splits per
+// round of loads).
+template <int MAXS, int KB = 8>
 __device__ __forceinline__ void combine_tile(const AttnArgs& a, float* out, float* lse, int bx, int hg, int b, int tid,
                                              CombineShared<MAXS>& sh) {
   float (&wts)[16][MAXS] = sh.wts;
@@ -461,7 +497,7 @@ __device__ __forceinline__ void combine_tile(const AttnArgs& a, float* out, floa
   const int64_t base = (((int64_t)b * ns * a.head_tiles + tile) * 4 + wave) * (D / 16) * 64 + wpos;
   // This lane's first splits (sq, sq + 4, ...) are requested before anything else, so they
   // arrive while the split weights are computed.
-  constexpr int kBatch = 8;
+  constexpr int kBatch = KB;
   f32x4 v[kBatch];
 #pragma unroll
   for (int q = 0; q < kBatch; ++q) v[q] = po[base + (int64_t)min(sq + kCombineLanes * q, ns - 1) * stride];
@@ -554,12 +590,28 @@ struct SplitPlan {
   int32_t n_splits, kps;
 };
 
+constexpr int kDenseThreads = 1024;   // dense split workgroup: 16 waves, four 16-head tiles
+constexpr int kDenseBlocks = 256;     // about one dense split workgroup per CU
+
+// Dense bf16 (or FP8) attention over many heads (every compressed entry, no top-k) uses one
+// workgroup per 64 heads, so each gathered row is read from HBM once, and streams the
+// split's chunks with rows requested ahead (PF). Selected (C4) attention keeps one workgroup per 16 heads and
+// one chunk per split: it is latency bound, and more workgroups start sooner.
+inline bool dense_split(chs_dtype dt, int32_t k, int32_t H) { return dt == CHS_BF16 && k == 0 && H > 48; }
+
+// Partial loads per combine lane: enough for every split in one round when there are more
+// than 32 splits (up to 64), else 8.
+inline int combine_batch(int32_t n_splits) { return n_splits > 4 * 8 ? 16 : 8; }
+
 inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, int32_t k, int64_t max_comp) {
   const int64_t max_slots = (int64_t)window + (k > 0 ? k : max_comp);
   const int gran = dt == CHS_BF16 ? kKeysPerChunk : kAttnThreads;
-  // Aim at about 512 workgroups: bf16 runs one per 16-head tile, fp32 one per head.
-  const int64_t blocks_per_split = (int64_t)batch * (dt == CHS_BF16 ? (H + 15) / 16 : H);
-  int64_t want = (512 + blocks_per_split - 1) / blocks_per_split;
+  // Aim at about 512 workgroups: bf16 runs one per 16-head tile, fp32 one per head; dense bf16
+  // aims at kDenseBlocks workgroups of 64 heads.
+  const bool dense = dense_split(dt, k, H);
+  const int64_t blocks_per_split = (int64_t)batch * (dense ? (H + 63) / 64 : dt == CHS_BF16 ? (H + 15) / 16 : H);
+  const int64_t target = dense ? kDenseBlocks : 512;
+  int64_t want = (target + blocks_per_split - 1) / blocks_per_split;
   const int64_t most = (max_slots + gran - 1) / gran;
   if (want > most) want = most;
   if (want > kCombineSplits) want = kCombineSplits;

@@ -52,6 +52,28 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(AttnArgs a) {
   attn_split<D, 1, NoHook, true, PAGED>(a, blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sh, none);
 }
 
+// The dense form (every compressed entry attended, more than 48 heads): one workgroup of 16
+// waves per (split, sequence, 64 heads), so each gathered row is read from HBM once for all
+// of them, and the split's chunks stream with the rows of the next chunks requested while the
+// current one is computed. FP8 / PAGED as above.
+template <int D, bool FP8, bool PAGED>
+__global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(AttnArgs a) {
+  __shared__ AttnShared<D, 4> sh;
+  NoHook none;
+  // One chunk of rows in flight ahead (a second register buffer spills at 1024 threads).
+  attn_split<D, 4, NoHook, FP8, PAGED, 1>(a, blockIdx.y, blockIdx.x, 4 * blockIdx.z, threadIdx.x, sh, none);
+}
+
+template <bool FP8, bool PAGED>
+void launch_dense(int d, dim3 grid, hipStream_t s, const AttnArgs& a) {
+  switch (d) {
+    case 64: hipLaunchKernelGGL((attn_dense_kernel<64, FP8, PAGED>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((attn_dense_kernel<128, FP8, PAGED>), grid, dim3(kDenseThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((attn_dense_kernel<256, FP8, PAGED>), grid, dim3(kDenseThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_dense_kernel<512, FP8, PAGED>), grid, dim3(kDenseThreads), 0, s, a); break;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 VALU split kernel
 // One workgroup per (split, sequence, head). Chunks of 256 key slots: one thread per key for
 // the logits, then one thread per channel for the weighted sum.
@@ -138,9 +160,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 // Four lanes of a quad share one accumulator word, each summing a strided quarter of the
 // splits, so a launch has four times as many workgroups as words / 256.
 // bf16 partials: one block per (64 output words of a 16-head tile, head group, sequence).
+template <int KB>
 __global__ __launch_bounds__(kThreads) void combine_mfma_kernel(AttnArgs a, float* out, float* lse) {
   __shared__ CombineShared<kCombineSplits> sh;
-  combine_tile<kCombineSplits>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
+  combine_tile<kCombineSplits, KB>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
 }
 
 // fp32 partials ([H][D] per split): one workgroup per (sequence, head).
@@ -212,7 +235,10 @@ chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t 
   const size_t need = ws_bytes(dtype, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
   const bool paged = pg.pt != nullptr;
-  if (dtype == CHS_BF16) {
+  if (dense_split(dtype, kk, n_heads)) {
+    const dim3 grid(p.n_splits, batch, (n_heads + 63) / 64);
+    paged ? launch_dense<false, true>(d, grid, s, a) : launch_dense<false, false>(d, grid, s, a);
+  } else if (dtype == CHS_BF16) {
     dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, a); };
     switch (d) {
@@ -230,7 +256,10 @@ chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t 
     const int words_per_block = kThreads / kCombineLanes;
     const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
                      (unsigned)batch);
-    hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(kThreads), 0, s, a, out, lse);
+    if (combine_batch(p.n_splits) == 16)
+      hipLaunchKernelGGL(combine_mfma_kernel<16>, cgrid, dim3(kThreads), 0, s, a, out, lse);
+    else
+      hipLaunchKernelGGL(combine_mfma_kernel<8>, cgrid, dim3(kThreads), 0, s, a, out, lse);
   } else {
     hipLaunchKernelGGL(combine_rows_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
   }
@@ -308,17 +337,25 @@ chs_status launch_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t wi
   dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
   const bool paged = pg.pt != nullptr;
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, a); };
-  switch (d) {
-    case 64: paged ? go(attn_fp8_kernel<64, true>) : go(attn_fp8_kernel<64>); break;
-    case 128: paged ? go(attn_fp8_kernel<128, true>) : go(attn_fp8_kernel<128>); break;
-    case 256: paged ? go(attn_fp8_kernel<256, true>) : go(attn_fp8_kernel<256>); break;
-    default: paged ? go(attn_fp8_kernel<512, true>) : go(attn_fp8_kernel<512>); break;
+  if (dense_split(CHS_BF16, kk, n_heads)) {
+    const dim3 dgrid(p.n_splits, batch, (n_heads + 63) / 64);
+    paged ? launch_dense<true, true>(d, dgrid, s, a) : launch_dense<true, false>(d, dgrid, s, a);
+  } else {
+    switch (d) {
+      case 64: paged ? go(attn_fp8_kernel<64, true>) : go(attn_fp8_kernel<64>); break;
+      case 128: paged ? go(attn_fp8_kernel<128, true>) : go(attn_fp8_kernel<128>); break;
+      case 256: paged ? go(attn_fp8_kernel<256, true>) : go(attn_fp8_kernel<256>); break;
+      default: paged ? go(attn_fp8_kernel<512, true>) : go(attn_fp8_kernel<512>); break;
+    }
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   const int words_per_block = kThreads / kCombineLanes;
   const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
                    (unsigned)batch);
-  hipLaunchKernelGGL(combine_mfma_kernel, cgrid, dim3(kThreads), 0, s, a, out, lse);
+  if (combine_batch(p.n_splits) == 16)
+    hipLaunchKernelGGL(combine_mfma_kernel<16>, cgrid, dim3(kThreads), 0, s, a, out, lse);
+  else
+    hipLaunchKernelGGL(combine_mfma_kernel<8>, cgrid, dim3(kThreads), 0, s, a, out, lse);
   return launch_status();
 }
 
