@@ -447,9 +447,12 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
 #pragma unroll
   for (int j = 0; j < TPW; ++j) __builtin_nontemporal_store(o[j], &po[(TPW * quarter + j) * 64 + lane]);
   if (quarter == 0 && c == 0) {
+    // The lane's head group, taken again from the lane id: keeping g live to here made the
+    // 1024-thread fused kernel spill it.
+    const int gl = (int)(__lane_id() >> 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int h = h_base + 4 * g + r;
+      const int h = h_base + 4 * gl + r;
       if (h < a.H) {
         a.part_ml[(pslot * a.H + h) * 2] = m_run[r];
         a.part_ml[(pslot * a.H + h) * 2 + 1] = l_run[r];
