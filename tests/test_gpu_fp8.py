@@ -117,6 +117,7 @@ def _codes_rows(rng, n, d, spread=1.0):
     (100, 256, 128, [77], [1500], 200, False),
     (16, 64, 32, [32, 32], [400, 1200], 0, True),
     (64, 512, 128, [128, 128], [2048, 1000], 0, True),
+    (100, 256, 128, [128, 9], [3000, 500], 0, True),
 ])
 def test_fp8_attention_matches_oracle(H, d, W, swa_lens, G_list, k, dense):
     print(f"case: fp8 attention H={H} d={d} W={W} G={G_list} k={k} dense={dense}", flush=True)

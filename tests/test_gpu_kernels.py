@@ -292,6 +292,14 @@ def test_attn_dense_bf16_dims(rng, d):
     _attn_case(rng, "bf16", 3, 64, d, 128, [128, 5, 0], [1000, 1, 2100], 0, True)
 
 
+@pytest.mark.parametrize("H,d", [(72, 512), (100, 128), (128, 256)])
+def test_attn_dense_bf16_many_heads(rng, H, d):
+    # More than 64 heads: a second 64-head workgroup whose last heads are masked; several chunks
+    # per split.
+    print(f"case: attn dense bf16 H={H} d={d}", flush=True)
+    _attn_case(rng, "bf16", 2, H, d, 128, [128, 50], [4000, 700], 0, True)
+
+
 def test_attn_f32(rng):
     print("case: attn f32", flush=True)
     _attn_case(rng, "f32", 2, 8, 64, 128, [128, 30], [256, 300], 64, False, n_bad=3)

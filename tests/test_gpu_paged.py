@@ -48,6 +48,7 @@ def _paged_pool(rng, rows_per_seq, P, d, dt, extra_pages=3):
     (torch.bfloat16, 64, 512, 128, 128, [2048, 1000], 0, True),
     (torch.bfloat16, 16, 128, 32, 1, [300, 45], 40, False),        # page size 1: a gather per entry
     (torch.bfloat16, 100, 256, 128, 256, [5000], 200, False),
+    (torch.bfloat16, 100, 256, 128, 64, [3000, 900], 0, True),
     (torch.float32, 8, 64, 128, 16, [256, 77], 64, False),
     (torch.float32, 8, 64, 16, 32, [100, 40], 0, True),
 ])
@@ -399,7 +400,8 @@ def test_paged_fp8_index_equals_contiguous(nh, dim, P, lens, k):
 
 
 @pytest.mark.parametrize("H,d,W,P,G_list,k,dense", [(64, 512, 128, 64, [3000, 700], 512, False),
-                                                    (16, 128, 32, 16, [400, 1200], 0, True)])
+                                                    (16, 128, 32, 16, [400, 1200], 0, True),
+                                                    (64, 512, 128, 64, [2500, 600], 0, True)])
 def test_paged_fp8_attention_equals_contiguous_and_oracle(H, d, W, P, G_list, k, dense):
     print(f"case: paged fp8 attention H={H} d={d} P={P} G={G_list} dense={dense}", flush=True)
     g = torch.Generator(device=dev()).manual_seed(H + d + P)
