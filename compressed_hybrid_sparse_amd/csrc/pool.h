@@ -30,7 +30,7 @@ struct Vec16<uint16_t> {  // 8 bf16 channels
     u32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-    *reinterpret_cast<u32x4*>(p) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));   // not re-read soon
   }
   __device__ static void copy(uint16_t* dst, const uint16_t* src) {
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
@@ -49,7 +49,7 @@ struct Vec16<float> {  // 4 fp32 channels
     f32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = v[j];
-    *reinterpret_cast<f32x4*>(p) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
   }
   __device__ static void copy(float* dst, const float* src) {
     *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
