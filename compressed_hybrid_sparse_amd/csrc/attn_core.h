@@ -60,8 +60,7 @@ struct AttnArgs {
   const int32_t* swa_len;   // [batch]
   const void* comp;         // [*][D]
   const int64_t* cu_comp;   // [batch+1]
-  const int32_t* topk;      // [batch][k] or NULL (row b at topk + b * topk_stride)
-  int32_t topk_stride;      // entries between sequences' rows: k, or 0 for one row of this sequence
+  const int32_t* topk;      // [batch][k] or NULL
   int32_t H, D, W, k;
   int64_t max_comp;
   float scale_log2;         // scale * log2(e)
@@ -120,7 +119,7 @@ struct SlotMap {
     *is_swa = false;
     int64_t j = s - nswa;
     if (a.topk) {
-      j = a.topk[(int64_t)b * a.topk_stride + j];
+      j = a.topk[(int64_t)b * a.k + j];
       if (j < 0 || j >= G) return -1;
     }
     if (a.pg.pt) {
@@ -170,7 +169,7 @@ __device__ __forceinline__ void chunk_rows(const AttnArgs& a, const SlotMap& sm,
       for (int i = 0; i < LOADS; ++i)
         idx[i] = load_lds_i32(sel + min(max(s0 + (i * NW + wave) * RPI + lr - sm.nswa, 0), a.k - 1));
     } else {
-      const int32_t* tk = a.topk + (int64_t)b * a.topk_stride;
+      const int32_t* tk = a.topk + (int64_t)b * a.k;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i)
         idx[i] = load_global_i32(tk + min(max(s0 + (i * NW + wave) * RPI + lr - sm.nswa, 0), a.k - 1));

@@ -228,7 +228,7 @@ chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t 
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = nullptr; a.comp_scale = nullptr;
   a.pg = pg;
-  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.topk_stride = kk; a.max_comp = max_comp;
+  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
   a.n_splits = p.n_splits; a.kps = p.kps;
   a.head_tiles = dtype == CHS_BF16 ? (n_heads + 63) / 64 : n_heads;
@@ -328,7 +328,7 @@ chs_status launch_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t wi
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = swa_scale; a.comp_scale = comp_scale;
   a.pg = pg;
-  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.topk_stride = kk; a.max_comp = max_comp;
+  a.H = n_heads; a.D = d; a.W = window; a.k = kk; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
   a.n_splits = p.n_splits; a.kps = p.kps;
   a.head_tiles = (n_heads + 63) / 64;

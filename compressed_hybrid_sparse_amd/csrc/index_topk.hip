@@ -1576,7 +1576,7 @@ extern "C" chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d,
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = nullptr; a.comp_scale = nullptr;
   a.pg = attn::Paging{nullptr, 0, nullptr, nullptr, 0, 0, 0};
-  a.H = n_heads; a.D = d; a.W = window; a.k = k; a.topk_stride = k; a.max_comp = max_comp;
+  a.H = n_heads; a.D = d; a.W = window; a.k = k; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
   a.n_splits = p.n_splits; a.kps = p.kps;
   a.head_tiles = (n_heads + 63) / 64;
