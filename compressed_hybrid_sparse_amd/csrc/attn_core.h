@@ -228,10 +228,10 @@ struct NoHook {
 // softmax; and computes P.V for its quarter. before_rows(s0) runs, uniformly over the
 // workgroup, before the rows of the chunk at slot s0 are looked up.
 // sm is sequence b's slot map (SlotMap(a, b)), passed in by callers that already hold it; sel,
-// when given, is the sequence's top-k row in LDS (read instead of a.topk). PF: how many chunks
-// ahead the rows are requested (0: each chunk's rows when its turn comes; 1 or 2: a split of
-// several chunks keeps that many chunks of rows in flight, in as many register buffers, while
-// it computes).
+// when given, is the sequence's top-k row in LDS (read instead of a.topk). PF = 1: a split of
+// several chunks requests the next chunk's rows as soon as the current one is in LDS, so they
+// arrive while it computes (PF = 0: each chunk's rows when its turn comes). A second register
+// buffer (two chunks ahead) spills at 1024 threads.
 template <int D, int TILES, typename Hook, bool FP8 = false, bool PAGED = false, int PF = 0>
 __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& sm, int b, int split, int z0, int tid,
                                               AttnShared<D, TILES>& sh, Hook& before_rows,
@@ -287,34 +287,22 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
 #pragma unroll
   for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
 
-  static_assert(PF >= 0 && PF <= 2, "prefetch depth");
-  constexpr int NB = PF == 2 ? 2 : 1;      // register buffers of chunk rows
-  u32x4 v[NB][LOADS];
-  float vs[NB][LOADS];
-  bool vok[NB][LOADS];
-  auto load_rows = [&](auto bc) {
-    constexpr int B = decltype(bc)::value;
+  static_assert(PF == 0 || PF == 1, "prefetch depth");
+  u32x4 v[LOADS];
+  float vs[LOADS];
+  auto load_rows = [&]() {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      v[B][i] = rp[i] ? load_global_u32x4(rp[i] + EPV * cv) : u32x4{0, 0, 0, 0};
-      if (FP8) vs[B][i] = rp[i] ? load_global_f32(rs[i]) : 0.f;
-      if (PF == 2) vok[B][i] = rp[i] != nullptr;
+      v[i] = rp[i] ? load_global_u32x4(rp[i] + EPV * cv) : u32x4{0, 0, 0, 0};
+      if (FP8) vs[i] = rp[i] ? load_global_f32(rs[i]) : 0.f;
     }
   };
-  typedef std::integral_constant<int, 0> B0;
-  typedef std::integral_constant<int, NB - 1> B1;
-  if (PF >= 1) load_rows(B0{});
-  if (PF == 2 && s_begin + KC < s_end) {
-    before_rows(s_begin + KC);
-    chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s_begin + KC, s_end, wave, lr, rp, rs, sel);
-    load_rows(B1{});
-  }
-  // One chunk at slot s0 from register buffer B: rows into LDS, then the next rows requested.
-  auto stage = [&](auto bc, int32_t s0) {
-    constexpr int B = decltype(bc)::value;
+  if (PF == 1) load_rows();
+  // One chunk at slot s0: rows into LDS, then the next chunk's rows looked up (and requested).
+  auto stage = [&](int32_t s0) {
     // 1. gather the chunk's rows (coalesced 16-byte loads) into a row-major LDS tile (with PF
-    // they were requested PF chunks earlier).
-    if (PF == 0) load_rows(B0{});
+    // they were requested during the previous chunk).
+    if (PF == 0) load_rows();
     __syncthreads();   // the previous chunk's LDS reads are done
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -327,27 +315,24 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
           u32x4 lo, hi;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t x = v[B][i][e];
+            const uint32_t x = v[i][e];
             const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
             const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
             if (e < 2) { lo[2 * e] = p0; lo[2 * e + 1] = p1; } else { hi[2 * e - 4] = p0; hi[2 * e - 3] = p1; }
           }
           *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 16 * cv]) = lo;
           *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 16 * cv + 8]) = hi;
-          if (cv == 0) sh.rowsc[r] = vs[B][i];
+          if (cv == 0) sh.rowsc[r] = vs[i];
         } else {
-          *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 8 * cv]) = v[B][i];
+          *reinterpret_cast<u32x4*>(&sh.kn[r * KN_PITCH + 8 * cv]) = v[i];
         }
-        // With two buffers the row pointers already describe a later chunk; otherwise they are
-        // still this chunk's.
-        if (cv == 0) sh.rowok[r] = PF == 2 ? vok[B][i] : rp[i] != nullptr;
+        if (cv == 0) sh.rowok[r] = rp[i] != nullptr;   // the row pointers are still this chunk's
       }
     }
-    const int32_t nxt = s0 + (PF == 2 ? 2 : 1) * KC;
-    if (nxt < s_end) {
-      before_rows(nxt);
-      chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, nxt, s_end, wave, lr, rp, rs, sel);
-      if (PF >= 1) load_rows(bc);
+    if (s0 + KC < s_end) {
+      before_rows(s0 + KC);
+      chunk_rows<D, LOADS, RPI, NW, ET, PAGED>(a, sm, b, s0 + KC, s_end, wave, lr, rp, rs, sel);
+      if (PF == 1) load_rows();
     }
     __syncthreads();
     // 2. S = Q K^T for keys 16n + c (n = 0, 1); lane holds heads 4g + r.
@@ -430,14 +415,7 @@ __device__ __forceinline__ void attn_split_sm(const AttnArgs& a, const SlotMap& 
       o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8, vb), o[j], 0, 0, 0);
     }
   };
-  if (PF == 2) {
-    for (int32_t s0 = s_begin; s0 < s_end; s0 += 2 * KC) {   // the two buffers in turn
-      stage(B0{}, s0);
-      if (s0 + KC < s_end) stage(B1{}, s0 + KC);
-    }
-  } else {
-    for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) stage(B0{}, s0);
-  }
+  for (int32_t s0 = s_begin; s0 < s_end; s0 += KC) stage(s0);
   // Partial result of this split: unnormalised O in the MFMA accumulator layout (one 16-byte
   // store per tile and lane, coalesced; quarter q holds tiles TPW q ..), running max (base 2)
   // and sum per head.

@@ -60,7 +60,6 @@ template <int D, bool FP8, bool PAGED>
 __global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(AttnArgs a) {
   __shared__ AttnShared<D, 4> sh;
   NoHook none;
-  // One chunk of rows in flight ahead (a second register buffer spills at 1024 threads).
   attn_split<D, 4, NoHook, FP8, PAGED, 1>(a, blockIdx.y, blockIdx.x, 4 * blockIdx.z, threadIdx.x, sh, none);
 }
 
