@@ -21,11 +21,15 @@ struct Vec16;
 template <>
 struct Vec16<uint16_t> {  // 8 bf16 channels
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* v) {
-    u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  // The 16 raw bytes, non-temporal (rows are read once), and their widening to fp32.
+  __device__ static u32x4 load_raw(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ static void unpack(const u32x4& r, float* v) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r[j]); v[2 * j + 1] = bf16_hi(r[j]); }
   }
+  __device__ static void load(const uint16_t* p, float* v) { unpack(load_raw(p), v); }
   __device__ static void store(uint16_t* p, const float* v) {
     u32x4 r;
 #pragma unroll
@@ -40,11 +44,14 @@ struct Vec16<uint16_t> {  // 8 bf16 channels
 template <>
 struct Vec16<float> {  // 4 fp32 channels
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* v) {
-    f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = r[j];
+  __device__ static u32x4 load_raw(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   }
+  __device__ static void unpack(const u32x4& r, float* v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(r[j]);
+  }
+  __device__ static void load(const float* p, float* v) { unpack(load_raw(p), v); }
   __device__ static void store(float* p, const float* v) {
     f32x4 r;
 #pragma unroll
@@ -160,8 +167,78 @@ __device__ __forceinline__ void pool_store(const PoolState<Vec16<ET>::N>& st, ET
   Vec16<ET>::store(op, o);
 }
 
+// Any m, in blocks of R rows with a running maximum (online softmax), so registers stay bounded.
+// The rows of the next block are requested before the current block is computed, so a wave
+// always has a block of HBM reads in flight while it does the arithmetic. The current block's
+// bias (a cache hit: one [m, d] table for every group) is requested before them, because a
+// wave's loads complete in issue order for its wait counter: waiting for the bias then leaves
+// the next block's reads outstanding. Slots past row m - 1 re-read the last row and are
+// masked as in pool_block.
+template <typename ET, int R, typename XRow, typename ZRow, typename BRow>
+__device__ __forceinline__ void pool_stream(PoolState<Vec16<ET>::N>& st, int m, XRow xrow, ZRow zrow,
+                                            BRow brow) {
+  using V = Vec16<ET>;
+  constexpr int N = V::N;
+  u32x4 xc[R], zc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rr = min(r, m - 1);
+    xc[r] = V::load_raw(xrow(rr));
+    zc[r] = V::load_raw(zrow(rr));
+  }
+  for (int r0 = 0; r0 < m; r0 += R) {
+    const int nr = min(R, m - r0);
+    float bv[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_bias(brow(r0 + (r < nr ? r : nr - 1)), bv[r], N);
+    __builtin_amdgcn_sched_barrier(0);   // keep the bias requests ahead of the next block's
+    u32x4 xn[R], zn[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int rr = min(r0 + R + r, m - 1);
+      xn[r] = V::load_raw(xrow(rr));
+      zn[r] = V::load_raw(zrow(rr));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float xv[R][N], av[R][N], cmax[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) cmax[j] = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      V::unpack(xc[r], xv[r]);
+      V::unpack(zc[r], av[r]);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        av[r][j] = r < nr ? (av[r][j] + bv[r][j]) * kLog2e : -INFINITY;   // logit in base-2 units
+        cmax[j] = fmaxf(cmax[j], av[r][j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {   // rescale to the new maximum (the first block: 0 * 0)
+      const float nm = fmaxf(st.mx[j], cmax[j]);
+      const float sc = fast_exp2(st.mx[j] - nm);
+      st.sum[j] *= sc;
+      st.acc[j] *= sc;
+      st.mx[j] = nm;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < nr) {   // uniform: nr is the same for every lane
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          const float e = fast_exp2(av[r][j] - st.mx[j]);
+          st.sum[j] += e;
+          st.acc[j] = fmaf(e, xv[r][j], st.acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) { xc[r] = xn[r]; zc[r] = zn[r]; }
+  }
+}
+
 // A whole group of m rows: M > 0 is a compile-time group size (<= 8, one block); M == 0 takes
-// any m, streamed in blocks of 8 rows with a running maximum, so registers stay bounded.
+// any m through pool_stream.
 template <typename ET, int M, bool ALL_LOADS_FIRST = false, typename XRow, typename ZRow, typename BRow>
 __device__ __forceinline__ void pool_group(int m, XRow xrow, ZRow zrow, BRow brow, ET* op) {
   PoolState<Vec16<ET>::N> st;
@@ -169,7 +246,7 @@ __device__ __forceinline__ void pool_group(int m, XRow xrow, ZRow zrow, BRow bro
   if (M > 0) {
     pool_block<ET, (M > 0 ? M : 1), true, ALL_LOADS_FIRST>(st, 0, M, xrow, zrow, brow);
   } else {
-    for (int r0 = 0; r0 < m; r0 += 8) pool_block<ET, 8, false>(st, r0, min(8, m - r0), xrow, zrow, brow);
+    pool_stream<ET, 4>(st, m, xrow, zrow, brow);
   }
   pool_store<ET>(st, op);
 }
