@@ -13,8 +13,9 @@
 // a wave is one contiguous, fully coalesced 1 KiB (d = 512, bf16). Tokens and gates are read
 // once with non-temporal loads (they are not reused); the bias rows stay in cache. Small groups
 // (m <= 8) keep every row in registers and take the max, the exponentials and the weighted sum
-// in one shot; larger groups (C128) stream 8 rows at a time with a running maximum
-// (online softmax), so registers stay bounded for any m.
+// in one shot; larger groups (C128) stream 4 rows at a time with a running maximum
+// (online softmax), so registers stay bounded for any m, with the next 4 rows in flight; up to
+// d = 512 a workgroup stages each block's bias rows once in LDS for all its groups.
 #include "pool.h"
 
 namespace chs {
@@ -52,6 +53,136 @@ __global__ __launch_bounds__(256) void compress_kernel(int32_t d, int32_t m, con
   }
 }
 
+
+// Groups of any m for d <= kStageMaxD: the same online softmax as pool_stream (blocks of 4 rows,
+// the next block's rows in flight during the arithmetic), but the bias rows of a block are
+// staged once per workgroup in LDS (two stages, the next block's bias requested with its rows)
+// instead of being read by every thread from the cache: a bias row is the same for every group.
+// The workgroup walks its items in lock step (every thread takes every barrier; a thread past
+// the last item computes a clamped item and stores nothing).
+constexpr int kStageRows = 4;
+constexpr int kStageMaxD = 512;
+constexpr int kStageVec = kStageRows * kStageMaxD / 4 / 256;   // bias f32x4 per thread and stage
+
+template <typename ET>
+__global__ __launch_bounds__(256) void compress_staged_kernel(int32_t d, int32_t m, const ET* __restrict__ x,
+                                                              const ET* __restrict__ gate,
+                                                              const float* __restrict__ bias,
+                                                              const int64_t* __restrict__ cu_tokens,
+                                                              const int64_t* __restrict__ cu_groups,
+                                                              int64_t max_groups, ET* __restrict__ out) {
+  using V = Vec16<ET>;
+  constexpr int N = V::N;
+  constexpr int R = kStageRows;
+  extern __shared__ f32x4 stage_lds[];   // [2][R * d / 4]
+  const int tid = threadIdx.x;
+  const int cpr = d / N;
+  const int q4 = d / 4;                  // f32x4 per bias row
+  const int nv = R * q4;                 // f32x4 per stage
+  const int b = blockIdx.y;
+  const int64_t t0 = cu_tokens[b];
+  int64_t n_groups = (cu_tokens[b + 1] - t0) / m;
+  const int64_t o0 = cu_groups[b];
+  const int64_t room = cu_groups[b + 1] - o0;
+  if (room < n_groups) n_groups = room;
+  if (n_groups > max_groups) n_groups = max_groups;
+  const int64_t total = n_groups * cpr;
+  const f32x4* bias4 = reinterpret_cast<const f32x4*>(bias);
+  // Stage slot i of block r0 holds bias row min(r0 + i / q4, m - 1), column quad i % q4.
+  auto bias_src = [&](int r0, int i) { return bias4 + (int64_t)min(r0 + i / q4, m - 1) * q4 + i % q4; };
+  for (int64_t base = (int64_t)blockIdx.x * 256; base < total; base += (int64_t)gridDim.x * 256) {
+    const bool live = base + tid < total;
+    const int64_t item = live ? base + tid : total - 1;
+    const int64_t g = item / cpr;
+    const int64_t col = (item - g * cpr) * N;
+    const ET* xp = x + (t0 + g * m) * d + col;
+    const ET* zp = gate + (t0 + g * m) * d + col;
+    __syncthreads();   // the previous item's readers are done with both stages
+#pragma unroll
+    for (int k = 0; k < kStageVec; ++k) {
+      const int i = tid + 256 * k;
+      if (i < nv) stage_lds[i] = *bias_src(0, i);
+    }
+    u32x4 xc[R], zc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int rr = min(r, m - 1);
+      xc[r] = V::load_raw(xp + (int64_t)rr * d);
+      zc[r] = V::load_raw(zp + (int64_t)rr * d);
+    }
+    PoolState<N> st;
+    st.init();
+    int cur = 0;
+    for (int r0 = 0; r0 < m; r0 += R) {
+      const int nr = min(R, m - r0);
+      u32x4 xn[R], zn[R];
+      f32x4 bn[kStageVec];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int rr = min(r0 + R + r, m - 1);
+        xn[r] = V::load_raw(xp + (int64_t)rr * d);
+        zn[r] = V::load_raw(zp + (int64_t)rr * d);
+      }
+#pragma unroll
+      for (int k = 0; k < kStageVec; ++k) {
+        const int i = min(tid + 256 * k, nv - 1);
+        bn[k] = *bias_src(r0 + R, i);
+      }
+      __syncthreads();   // stage cur is written
+      const float* bl = reinterpret_cast<const float*>(stage_lds + cur * nv);
+      float xv[R][N], av[R][N], cmax[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j) cmax[j] = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        V::unpack(xc[r], xv[r]);
+        V::unpack(zc[r], av[r]);
+        float bv[8];
+        const float* brow = bl + r * d + col;
+#pragma unroll
+        for (int j = 0; j < N; j += 4) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(brow + j);
+          bv[j] = t[0]; bv[j + 1] = t[1]; bv[j + 2] = t[2]; bv[j + 3] = t[3];
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          av[r][j] = r < nr ? (av[r][j] + bv[j]) * kLog2e : -INFINITY;
+          cmax[j] = fmaxf(cmax[j], av[r][j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float nm = fmaxf(st.mx[j], cmax[j]);
+        const float sc = fast_exp2(st.mx[j] - nm);
+        st.sum[j] *= sc;
+        st.acc[j] *= sc;
+        st.mx[j] = nm;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r < nr) {
+#pragma unroll
+          for (int j = 0; j < N; ++j) {
+            const float e = fast_exp2(av[r][j] - st.mx[j]);
+            st.sum[j] += e;
+            st.acc[j] = fmaf(e, xv[r][j], st.acc[j]);
+          }
+        }
+      }
+      // The other stage was last read before this block's barrier: safe to overwrite.
+#pragma unroll
+      for (int k = 0; k < kStageVec; ++k) {
+        const int i = tid + 256 * k;
+        if (i < nv) stage_lds[(cur ^ 1) * nv + i] = bn[k];
+      }
+      cur ^= 1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) { xc[r] = xn[r]; zc[r] = zn[r]; }
+    }
+    if (live) pool_store<ET>(st, out + (o0 + g) * d + col);
+  }
+}
+
 template <typename ET>
 chs_status launch(int32_t batch, int32_t d, int32_t m, const void* x, const void* gate,
                   const float* bias, const int64_t* cu_tokens, const int64_t* cu_groups,
@@ -71,7 +202,16 @@ chs_status launch(int32_t batch, int32_t d, int32_t m, const void* x, const void
     case 2: args(compress_kernel<ET, 2>); break;
     case 4: args(compress_kernel<ET, 4>); break;
     case 8: args(compress_kernel<ET, 8>); break;
-    default: args(compress_kernel<ET, 0>); break;
+    default:
+      if (d <= kStageMaxD) {
+        const size_t lds = 2 * (size_t)kStageRows * d * sizeof(float);
+        hipLaunchKernelGGL(compress_staged_kernel<ET>, grid, block, lds, stream, d, m, static_cast<const ET*>(x),
+                           static_cast<const ET*>(gate), bias, cu_tokens, cu_groups, max_groups,
+                           static_cast<ET*>(out));
+      } else {
+        args(compress_kernel<ET, 0>);
+      }
+      break;
   }
   return launch_status();
 }

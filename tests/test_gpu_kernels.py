@@ -55,6 +55,9 @@ COMPRESS_CASES = [
     ("bf16", 512, 8, [1601]),
     ("bf16", 128, 130, [1000, 520]),
     ("bf16", 64, 1024, [2100]),
+    # d above the LDS-staged bias path's limit: the per-thread bias reads
+    ("bf16", 1024, 16, [100, 37]),
+    ("f32", 640, 6, [50, 13]),
 ]
 
 
