@@ -58,6 +58,7 @@ COMPRESS_CASES = [
     # d above the LDS-staged bias path's limit: the per-thread bias reads
     ("bf16", 1024, 16, [100, 37]),
     ("f32", 640, 6, [50, 13]),
+    ("bf16", 1024, 8, [200, 17]),   # wide rows at a compile-time group size
 ]
 
 
