@@ -102,24 +102,35 @@ def test_compress_m1_identity_and_mean_pooling():
     assert_bf16_stored(c4, mean, "mean pooling")
 
 
-def test_compress_output_offsets_are_caller_controlled():
-    # cu_groups need not be packed: sequence 1 is written after a gap; rows outside stay put.
-    print("case: compress offsets", flush=True)
-    d, m = 64, 4
-    lens = [40, 24]
+@pytest.mark.parametrize("d,m", [(64, 4), (64, 6), (512, 128)])
+def test_compress_output_offsets_are_caller_controlled(d, m):
+    # cu_groups need not be packed: sequence 1 is written after a gap; sequence 2 has room for 3
+    # of its 5 groups, so only its first 3 are written; rows outside stay put. m = 4 runs the
+    # compile-time group size, m = 6 and 128 the LDS-staged bias path.
+    print(f"case: compress offsets d={d} m={m}", flush=True)
+    lens = [10 * m, 6 * m + 1, 5 * m]
     T = sum(lens)
     X = synth.normal(8, 1, 0, T * d, 0, 1, True).reshape(T, d)
     Z = synth.normal(8, 2, 0, T * d, 0, 1, True).reshape(T, d)
-    B = np.zeros((m, d), np.float32)
-    cug = np.array([0, 12, 18], np.int64)          # room 12 >= 10 groups, then 6 groups
-    out = torch.full((20, d), 3.0, dtype=torch.bfloat16, device=dev())
+    B = synth.normal(8, 3, 0, m * d, 0, 0.5).reshape(m, d)
+    cug = np.array([0, 12, 18, 21], np.int64)      # room 12 >= 10 groups, 6 for 6, 3 for 5
+    out = torch.full((24, d), 3.0, dtype=torch.bfloat16, device=dev())
     chs.compress(_to_dev(X, torch.bfloat16), _to_dev(Z, torch.bfloat16), _to_dev(B, torch.float32), m,
                  _to_dev(_cu(lens), torch.int64), _to_dev(cug, torch.int64), 10, out)
     got = out.float().cpu().numpy()
-    want = oracle.compress(X, Z, B, m, _cu(lens))
+    want = oracle.compress(X, Z, B, m, _cu(lens))   # packed: 10 + 6 + 5 rows
     assert_bf16_stored(got[0:10], want[0:10])
-    assert np.all(got[10:12] == 3.0) and np.all(got[18:] == 3.0)
+    assert np.all(got[10:12] == 3.0) and np.all(got[21:] == 3.0)
     assert_bf16_stored(got[12:18], want[10:16])
+    assert_bf16_stored(got[18:21], want[16:19])
+    # max_groups = 2: groups 2 and later of every sequence are not computed.
+    out2 = torch.full((24, d), 3.0, dtype=torch.bfloat16, device=dev())
+    chs.compress(_to_dev(X, torch.bfloat16), _to_dev(Z, torch.bfloat16), _to_dev(B, torch.float32), m,
+                 _to_dev(_cu(lens), torch.int64), _to_dev(cug, torch.int64), 2, out2)
+    got2 = out2.float().cpu().numpy()
+    for row0, src0, room in ((0, 0, 12), (12, 10, 6), (18, 16, 3)):
+        assert_bf16_stored(got2[row0:row0 + 2], want[src0:src0 + 2])
+        assert np.all(got2[row0 + 2:row0 + room] == 3.0)
 
 
 # ------------------------------------------------------------------ standalone top-k (exact)
