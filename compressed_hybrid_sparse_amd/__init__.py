@@ -24,7 +24,7 @@ EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compr
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
            "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
            "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged",
-           "chs_decode_step_workspace_size", "chs_decode_step")
+           "chs_decode_step_workspace_size", "chs_decode_step", "chs_index_scores")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -69,6 +69,7 @@ def lib():
         L.chs_decode_attn_workspace_size.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i64]
         L.chs_decode_attn.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _p, _p,
                                       _i64, _p, _p, _p, _sz, _p]
+        L.chs_index_scores.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _sz, _p]
         L.chs_index_topk_fp8.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _p]
         L.chs_decode_attn_fp8.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p,
                                           _p, _p, _sz, _p]
@@ -90,7 +91,7 @@ def lib():
         L.chs_gather_selected.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
-        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_decode_attn", "chs_index_topk_fp8",
+        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_index_scores", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
                    "chs_index_topk_paged", "chs_gather_selected", "chs_append_multi", "chs_index_topk_fp8_paged",
                    "chs_decode_attn_fp8_paged"):
@@ -135,6 +136,35 @@ def _host_max_diff(cu):
     return int(d.max().item()) if d.numel() else 0
 
 
+def _host_cu(cu):
+    """(max_b (cu[b+1] - cu[b]), cu[-1]) read on the host in one transfer."""
+    h = cu.cpu()
+    d = h[1:] - h[:-1]
+    return (int(d.max()) if d.numel() else 0), int(h[-1]) if h.numel() else 0
+
+
+def _shape(t, shape, name):
+    """t must have exactly `shape` (checked before any launch: an undersized buffer would be
+    read or written out of bounds on the device)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows(t, n, name):
+    """t must hold at least n rows (dimension 0)."""
+    if t.shape[0] < n:
+        raise ValueError(f"{name} has {t.shape[0]} rows, the call addresses {n}")
+
+
+def _cu_sizes(cu, max_given):
+    """The (max per-sequence count, total) of a cu prefix array. When the caller passes the
+    maximum, the array is not read (no device round trip, so the call can be captured in a graph)
+    and the total is None: buffers sized from cu[-1] are then the caller's responsibility."""
+    if max_given is None:
+        return _host_cu(cu)
+    return int(max_given), None
+
+
 def workspace_clear(ws):
     _check(lib().chs_workspace_clear(_ptr(ws), ws.numel() * ws.element_size(), _stream()), "chs_workspace_clear")
 
@@ -158,11 +188,21 @@ def compress(x, gate, bias, m: int, cu_tokens, cu_groups=None, max_groups=None, 
         cu_groups = torch.zeros_like(cu_tokens)
         cu_groups[1:] = torch.cumsum(torch.div(lens, m, rounding_mode="floor"), 0)
     _need(cu_groups, "cu_groups", torch.int64, 1)
-    if max_groups is None:
-        max_groups = _host_max_diff(cu_groups)
+    if cu_groups.numel() != cu_tokens.numel():
+        raise ValueError("cu_groups and cu_tokens must have the same length")
+    _shape(gate, x.shape, "gate")
+    _shape(bias, (m, x.shape[1]), "bias")
+    max_groups, n_out = _cu_sizes(cu_groups, max_groups)
+    if n_out is not None:
+        _rows(x, int(cu_tokens[-1].item()), "x")
     if out is None:
-        out = torch.empty(int(cu_groups[-1].item()), x.shape[1], dtype=x.dtype, device=x.device)
+        out = torch.empty(n_out if n_out is not None else int(cu_groups[-1].item()), x.shape[1], dtype=x.dtype,
+                          device=x.device)
     _need(out, "out", x.dtype, 2)
+    if out.shape[1] != x.shape[1]:
+        raise ValueError(f"out must have {x.shape[1]} columns")
+    if n_out is not None:
+        _rows(out, n_out, "out")
     _check(lib().chs_compress(_dtype_code(x), cu_tokens.numel() - 1, x.shape[1], m, _ptr(x), _ptr(gate),
                               _ptr(bias), _ptr(cu_tokens), _ptr(cu_groups), int(max_groups), _ptr(out),
                               _stream()), "chs_compress")
@@ -196,6 +236,18 @@ def append(x_new, z_new, bias, m: int, n_tokens, swa_kv, gate_ring, ring_page, c
         if comp_count.dtype != torch.int64 or not comp_count.is_cuda:
             raise TypeError("comp_count must be an int64 CUDA tensor")
     B, d = x_new.shape
+    _shape(z_new, (B, d), "z_new")
+    _shape(bias, (m, d), "bias")
+    _shape(n_tokens, (B,), "n_tokens")
+    if swa_kv.shape[0] != B or swa_kv.shape[2] != d:
+        raise ValueError(f"swa_kv must be [{B}, W, {d}], got {tuple(swa_kv.shape)}")
+    _shape(ring_page, (B,), "ring_page")
+    _shape(comp_start, (B,), "comp_start")
+    if gate_ring.shape[1] != d or comp_kv.shape[1] != d:
+        raise ValueError("gate_ring and comp_kv must have d columns")
+    for t, name in ((swa_len, "swa_len"), (comp_count, "comp_count")):
+        if t is not None and t.numel() < B:
+            raise ValueError(f"{name} must hold {B} entries")
     if ring_size is None:
         ring_size = gate_ring.shape[0] // B
     pages = gate_ring.shape[0] // ring_size
@@ -218,27 +270,67 @@ def index_topk(q_idx, w, k_idx, cu_cand, k: int, max_cand=None, scores=None, wor
     Returns (topk [B, k] int32, scores or None)."""
     _need(cu_cand, "cu_cand", torch.int64, 1)
     batch = cu_cand.numel() - 1
-    if max_cand is None:
-        max_cand = _host_max_diff(cu_cand)
+    max_cand, total = _cu_sizes(cu_cand, max_cand)
     if workspace is None:
         workspace = index_topk_workspace(batch, max_cand, k, cu_cand.device)
     if out is None:
         out = torch.empty(batch, k, dtype=torch.int32, device=cu_cand.device)
     _need(out, "topk", torch.int32, 2)
+    _shape(out, (batch, k), "topk")
     if q_idx is not None:
         _need(q_idx, "q_idx", dim=3)
         _need(w, "w", torch.float32, 2)
         _need(k_idx, "k_idx", q_idx.dtype, 2)
         dt, nh, dim = _dtype_code(q_idx), q_idx.shape[1], q_idx.shape[2]
+        if q_idx.shape[0] != batch:
+            raise ValueError(f"q_idx must have {batch} rows (one per sequence)")
+        _shape(w, (batch, nh), "w")
+        if k_idx.shape[1] != dim:
+            raise ValueError(f"k_idx must have {dim} columns")
         if scores is not None:
             _need(scores, "scores", torch.float32, 1)
+        if total is not None:
+            _rows(k_idx, total, "k_idx")
+            if scores is not None:
+                _rows(scores, total, "scores")
     else:
         _need(scores, "scores", torch.float32, 1)
         dt, nh, dim = CHS_F32, 0, 0
+        if total is not None:
+            _rows(scores, total, "scores")
     _check(lib().chs_index_topk(dt, batch, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(cu_cand),
                                 int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
                                 workspace.numel(), _stream()), "chs_index_topk")
     return out, scores
+
+
+def index_scores(q_idx, w, k_idx, cu_cand, max_cand=None, scores=None, workspace=None):
+    """The indexer scores alone (chs_index_scores): the values index_topk computes, no selection.
+    q_idx: [B, Hi, dim]; w: [B, Hi] fp32; k_idx: [G, dim]; cu_cand: [B+1] int64. Returns scores [G]
+    fp32."""
+    _need(cu_cand, "cu_cand", torch.int64, 1)
+    _need(q_idx, "q_idx", dim=3)
+    _need(w, "w", torch.float32, 2)
+    _need(k_idx, "k_idx", q_idx.dtype, 2)
+    batch = cu_cand.numel() - 1
+    nh, dim = q_idx.shape[1], q_idx.shape[2]
+    if q_idx.shape[0] != batch or k_idx.shape[1] != dim:
+        raise ValueError("q_idx must be [B, Hi, dim] and k_idx [G, dim]")
+    _shape(w, (batch, nh), "w")
+    max_cand, total = _cu_sizes(cu_cand, max_cand)
+    if scores is None:
+        scores = torch.empty(total if total is not None else k_idx.shape[0], dtype=torch.float32,
+                             device=q_idx.device)
+    _need(scores, "scores", torch.float32, 1)
+    if total is not None:
+        _rows(k_idx, total, "k_idx")
+        _rows(scores, total, "scores")
+    if workspace is None:
+        workspace = index_topk_workspace(batch, max_cand, 1, cu_cand.device)
+    _check(lib().chs_index_scores(_dtype_code(q_idx), batch, nh, dim, _ptr(q_idx), _ptr(w), _ptr(k_idx),
+                                  _ptr(cu_cand), int(max_cand), _ptr(scores), _ptr(workspace), workspace.numel(),
+                                  _stream()), "chs_index_scores")
+    return scores
 
 
 def topk_from_scores(scores, cu_cand, k: int, max_cand=None, workspace=None, out=None):
@@ -247,6 +339,31 @@ def topk_from_scores(scores, cu_cand, k: int, max_cand=None, workspace=None, out
 
 
 # ---------------------------------------------------------------- chs_decode_attn
+def _attn_shapes(q, swa_kv, swa_len, comp_kv, cu_comp):
+    """The shapes every attention call shares: q [B, H, d], swa_kv [B or pages, W, d] (d codes for
+    FP8), swa_len [B], comp_kv [*, d], cu_comp [B + 1] (or per-sequence counts [B])."""
+    B, H, d = q.shape
+    if swa_kv.shape[2] != d or comp_kv.shape[1] != d:
+        raise ValueError(f"swa_kv and comp_kv rows must have {d} elements")
+    _shape(swa_len, (B,), "swa_len")
+    if cu_comp is not None and cu_comp.numel() not in (B, B + 1):
+        raise ValueError(f"cu_comp / comp_len must have {B + 1} / {B} entries")
+
+
+def _attn_outputs(q, out, lse):
+    """out [B, H, d] fp32 and lse [B, H] fp32, allocated if not given, checked if given."""
+    B, H, d = q.shape
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _shape(out, (B, H, d), "out")
+    _shape(lse, (B, H), "lse")
+    return out, lse
+
+
 def decode_attn_workspace(dtype, batch, n_heads, d, window, k, max_comp, device="cuda"):
     code = CHS_BF16 if dtype == torch.bfloat16 else CHS_F32
     n = lib().chs_decode_attn_workspace_size(code, batch, n_heads, d, window, k, max_comp)
@@ -270,16 +387,18 @@ def decode_attn(q, swa_kv, swa_len, comp_kv, cu_comp, topk=None, scale=None, max
     if topk is not None:
         _need(topk, "topk", torch.int32, 2)
         k = topk.shape[1]
-    if max_comp is None:
-        max_comp = _host_max_diff(cu_comp)
+        _shape(topk, (B, k), "topk")
+    _attn_shapes(q, swa_kv, swa_len, comp_kv, cu_comp)
+    if swa_kv.shape[0] != B:
+        raise ValueError(f"swa_kv must have {B} windows")
+    max_comp, total = _cu_sizes(cu_comp, max_comp)
+    if total is not None:
+        _rows(comp_kv, total, "comp_kv")
     if scale is None:
         scale = d ** -0.5
     if workspace is None:
         workspace = decode_attn_workspace(q.dtype, B, H, d, W, k, max_comp, q.device)
-    if out is None:
-        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    out, lse = _attn_outputs(q, out, lse)
     _check(lib().chs_decode_attn(_dtype_code(q), B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_kv),
                                  _ptr(swa_len), _ptr(comp_kv), _ptr(cu_comp), _ptr(topk), int(max_comp),
                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()),
@@ -310,21 +429,29 @@ def decode_step(q_idx, w, k_idx, q, swa_kv, swa_len, comp_kv, cu_comp, k: int, s
     _need(cu_comp, "cu_comp", torch.int64, 1)
     B, H, d = q.shape
     W = swa_kv.shape[1]
-    if max_comp is None:
-        max_comp = _host_max_diff(cu_comp)
+    _attn_shapes(q, swa_kv, swa_len, comp_kv, cu_comp)
+    if swa_kv.shape[0] != B or cu_comp.numel() != B + 1:
+        raise ValueError(f"swa_kv must have {B} windows and cu_comp {B + 1} entries")
+    if q_idx.shape[0] != B or k_idx.shape[1] != q_idx.shape[2]:
+        raise ValueError("q_idx must be [B, Hi, dim] and k_idx [G, dim]")
+    _shape(w, q_idx.shape[:2], "w")
+    max_comp, total = _cu_sizes(cu_comp, max_comp)
     if scale is None:
         scale = d ** -0.5
     if scores is not None:
         _need(scores, "scores", torch.float32, 1)
+    if total is not None:
+        _rows(comp_kv, total, "comp_kv")
+        _rows(k_idx, total, "k_idx")
+        if scores is not None:
+            _rows(scores, total, "scores")
     if workspace is None:
         workspace = decode_step_workspace(B, H, d, W, k, max_comp, q.device)
     if topk is None:
         topk = torch.empty(B, k, dtype=torch.int32, device=q.device)
-    if out is None:
-        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    out, lse = _attn_outputs(q, out, lse)
     _need(topk, "topk", torch.int32, 2)
+    _shape(topk, (B, k), "topk")
     _check(lib().chs_decode_step(B, H, d, W, k, float(scale), q_idx.shape[1], q_idx.shape[2], _ptr(q_idx), _ptr(w),
                                  _ptr(k_idx), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(cu_comp),
                                  int(max_comp), _ptr(scores), _ptr(topk), _ptr(out), _ptr(lse), _ptr(workspace),
@@ -347,12 +474,24 @@ def index_topk_fp8(q_idx, w, k_codes, k_scale, cu_cand, k: int, max_cand=None, s
     _need(cu_cand, "cu_cand", torch.int64, 1)
     batch = cu_cand.numel() - 1
     nh, dim = q_idx.shape[1], q_idx.shape[2]
-    if max_cand is None:
-        max_cand = _host_max_diff(cu_cand)
+    if q_idx.shape[0] != batch or k_codes.shape[1] != dim:
+        raise ValueError("q_idx must be [B, Hi, dim] and k_codes [G, dim]")
+    _shape(w, (batch, nh), "w")
+    if k_scale.numel() != k_codes.shape[0]:
+        raise ValueError("k_scale must hold one scale per key row")
+    max_cand, total = _cu_sizes(cu_cand, max_cand)
+    if total is not None:
+        _rows(k_codes, total, "k_codes")
+        if scores is not None:
+            _rows(scores, total, "scores")
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 1)
     if workspace is None:
         workspace = index_topk_workspace(batch, max_cand, k, cu_cand.device)
     if out is None:
         out = torch.empty(batch, k, dtype=torch.int32, device=cu_cand.device)
+    _need(out, "topk", torch.int32, 2)
+    _shape(out, (batch, k), "topk")
     _check(lib().chs_index_topk_fp8(batch, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(k_codes), _ptr(k_scale),
                                     _ptr(cu_cand), int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
                                     workspace.numel(), _stream()),
@@ -381,16 +520,21 @@ def decode_attn_fp8(q, swa_codes, swa_scale, swa_len, comp_codes, comp_scale, cu
     if topk is not None:
         _need(topk, "topk", torch.int32, 2)
         k = topk.shape[1]
-    if max_comp is None:
-        max_comp = _host_max_diff(cu_comp)
+        _shape(topk, (B, k), "topk")
+    _attn_shapes(q, swa_codes, swa_len, comp_codes, cu_comp)
+    if swa_codes.shape[0] != B:
+        raise ValueError(f"swa_codes must have {B} windows")
+    _shape(swa_scale, (B, W), "swa_scale")
+    if comp_scale.numel() != comp_codes.shape[0]:
+        raise ValueError("comp_scale must hold one scale per entry row")
+    max_comp, total = _cu_sizes(cu_comp, max_comp)
+    if total is not None:
+        _rows(comp_codes, total, "comp_codes")
     if scale is None:
         scale = d ** -0.5
     if workspace is None:
         workspace = decode_attn_workspace(torch.bfloat16, B, H, d, W, k, max_comp, q.device)
-    if out is None:
-        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    out, lse = _attn_outputs(q, out, lse)
     _check(lib().chs_decode_attn_fp8(B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_codes), _ptr(swa_scale),
                                      _ptr(swa_len), _ptr(comp_codes), _ptr(comp_scale), _ptr(cu_comp), _ptr(topk),
                                      int(max_comp), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -419,16 +563,19 @@ def decode_attn_paged(q, swa_pool, swa_page, swa_len, comp_pool, page_size: int,
     if topk is not None:
         _need(topk, "topk", torch.int32, 2)
         k = topk.shape[1]
+        _shape(topk, (B, k), "topk")
+    _attn_shapes(q, swa_pool, swa_len, comp_pool, comp_len)
+    _shape(swa_page, (B,), "swa_page")
+    _shape(comp_len, (B,), "comp_len")
+    if page_table.shape[0] != B:
+        raise ValueError("page_table must have B rows")
     if max_comp is None:
         max_comp = int(comp_len.max().item()) if comp_len.numel() else 0
     if scale is None:
         scale = d ** -0.5
     if workspace is None:
         workspace = decode_attn_workspace(q.dtype, B, H, d, W, k, max_comp, q.device)
-    if out is None:
-        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    out, lse = _attn_outputs(q, out, lse)
     _check(lib().chs_decode_attn_paged(_dtype_code(q), B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_pool),
                                        _ptr(swa_page), swa_pool.shape[0], _ptr(swa_len), _ptr(comp_pool),
                                        comp_pool.shape[0] // page_size, page_size, _ptr(page_table),
@@ -478,13 +625,19 @@ def index_topk_paged(q_idx, w, key_pool, page_size: int, page_table, cand_len, k
     _need(page_table, "page_table", torch.int32, 2)
     _need(cand_len, "cand_len", torch.int64, 1)
     B, nh, dim = q_idx.shape
+    _shape(w, (B, nh), "w")
+    _shape(cand_len, (B,), "cand_len")
+    if key_pool.shape[1] != dim or page_table.shape[0] != B:
+        raise ValueError("key_pool must have dim columns and page_table B rows")
     if scores is not None:
         _need(scores, "scores", torch.float32, 2)
+        _shape(scores, (B, max_cand), "scores")
     if workspace is None:
         workspace = index_topk_workspace(B, max_cand, k, q_idx.device)
     if out is None:
         out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
     _need(out, "topk", torch.int32, 2)
+    _shape(out, (B, k), "topk")
     _check(lib().chs_index_topk_paged(CHS_BF16, B, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(key_pool),
                                       key_pool.shape[0] // page_size, page_size, _ptr(page_table), page_table.shape[1],
                                       _ptr(cand_len), int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
@@ -508,13 +661,21 @@ def gather_selected(mirror, cu_comp, topk, cache=None, resident=None, work=None,
     _need(topk, "topk", torch.int32, 2)
     B, k = topk.shape
     d = mirror.shape[1]
+    if cu_comp.numel() != B + 1:
+        raise ValueError(f"cu_comp must have {B + 1} entries")
     if cache is not None or resident is not None:
         _need(cache, "cache", mirror.dtype, 2)
         _need(resident, "resident", torch.int32, 1)
+        if cache.shape[1] != d:
+            raise ValueError(f"cache rows must have {d} elements")
     if work is None:
         work = torch.empty(B * k, d, dtype=mirror.dtype, device=topk.device)
     if work_topk is None:
         work_topk = torch.empty(B, k, dtype=torch.int32, device=topk.device)
+    _need(work, "work", mirror.dtype, 2)
+    _need(work_topk, "work_topk", torch.int32, 2)
+    _shape(work, (B * k, d), "work")
+    _shape(work_topk, (B, k), "work_topk")
     _check(lib().chs_gather_selected(_dtype_code(mirror), B, d, k, _ptr(mirror), int(on_host), _ptr(cu_comp), _ptr(topk),
                                      _ptr(cache), _ptr(resident), 0 if cache is None else cache.shape[0], _ptr(work),
                                      _ptr(work_topk), _stream()), "chs_gather_selected")
@@ -581,12 +742,21 @@ def index_topk_fp8_paged(q_idx, w, code_pool, scale_pool, page_size: int, page_t
     _need(page_table, "page_table", torch.int32, 2)
     _need(cand_len, "cand_len", torch.int64, 1)
     B, nh, dim = q_idx.shape
+    _shape(w, (B, nh), "w")
+    _shape(cand_len, (B,), "cand_len")
+    if code_pool.shape[1] != dim or page_table.shape[0] != B:
+        raise ValueError("code_pool must have dim columns and page_table B rows")
+    if scale_pool.numel() != code_pool.shape[0]:
+        raise ValueError("scale_pool must hold one scale per pool row")
     if scores is not None:
         _need(scores, "scores", torch.float32, 2)
+        _shape(scores, (B, max_cand), "scores")
     if workspace is None:
         workspace = index_topk_workspace(B, max_cand, k, q_idx.device)
     if out is None:
         out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+    _need(out, "topk", torch.int32, 2)
+    _shape(out, (B, k), "topk")
     _check(lib().chs_index_topk_fp8_paged(B, nh, dim, k, _ptr(q_idx), _ptr(w), _ptr(code_pool), _ptr(scale_pool),
                                           code_pool.shape[0] // page_size, page_size, _ptr(page_table),
                                           page_table.shape[1], _ptr(cand_len), int(max_cand), _ptr(scores), _ptr(out),
@@ -614,16 +784,22 @@ def decode_attn_fp8_paged(q, swa_codes, swa_scales, swa_page, swa_len, comp_code
     if topk is not None:
         _need(topk, "topk", torch.int32, 2)
         k = topk.shape[1]
+        _shape(topk, (B, k), "topk")
+    _attn_shapes(q, swa_codes, swa_len, comp_codes, comp_len)
+    _shape(swa_page, (B,), "swa_page")
+    _shape(comp_len, (B,), "comp_len")
+    _shape(swa_scales, swa_codes.shape[:2], "swa_scales")
+    if comp_scales.numel() != comp_codes.shape[0]:
+        raise ValueError("comp_scales must hold one scale per pool row")
+    if page_table.shape[0] != B:
+        raise ValueError("page_table must have B rows")
     if max_comp is None:
         max_comp = int(comp_len.max().item()) if comp_len.numel() else 0
     if scale is None:
         scale = d ** -0.5
     if workspace is None:
         workspace = decode_attn_workspace(torch.bfloat16, B, H, d, W, k, max_comp, q.device)
-    if out is None:
-        out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    out, lse = _attn_outputs(q, out, lse)
     _check(lib().chs_decode_attn_fp8_paged(B, H, d, W, k, float(scale), _ptr(q), _ptr(swa_codes), _ptr(swa_scales),
                                            _ptr(swa_page), swa_codes.shape[0], _ptr(swa_len), _ptr(comp_codes),
                                            _ptr(comp_scales), comp_codes.shape[0] // page_size, page_size,

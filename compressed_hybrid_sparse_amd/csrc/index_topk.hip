@@ -27,11 +27,12 @@
 //   K2 collect_kernel, one 1024-thread workgroup per sequence (one CU, 4 waves per SIMD, so
 //      the instructions it issues per candidate are what costs: it touches group statistics,
 //      not scores, wherever it can):
-//      (A) bins the maxima of runs of 4 groups (or of single groups when there are few),
-//          (key - smallest) >> shift, into 2048 monotone bins; L = the smallest run maximum in
-//          the bin holding the k-th largest. L never exceeds the k-th largest score, because
-//          k disjoint runs each hold a score >= L; so every top-k candidate, and every tie at
-//          the threshold, has key >= L and sits in a group whose maximum is >= L;
+//      (A) bins the maxima of runs of 4 groups (or of single groups when there are few; past
+//          8192 groups a "group" is the set of groups congruent modulo 8192), (key - smallest)
+//          >> shift, into 2048 monotone bins; L = the lower edge of the bin holding the k-th
+//          largest. L never exceeds the k-th largest score, because k disjoint runs each hold
+//          a score >= L; so every top-k candidate, and every tie at the threshold, has key >= L
+//          and sits in a group whose maximum is >= L;
 //      (B) builds the superset of keys >= L in index order in LDS with one block scan: a group
 //          whose maximum is >= L but whose second key is below L holds exactly one such key,
 //          its maximum, known from the statistics; the others ("full", typically a few
@@ -62,7 +63,7 @@ constexpr int kMinGroup = 8;
 constexpr int kCThreads = 1024;        // K2 workgroup: sixteen waves, four per SIMD
 constexpr int kCWaves = kCThreads / 64;
 constexpr int kMaxPerThread = 8;       // group maxima per K2 thread per tile (contiguous)
-constexpr int kTile = kCThreads * kMaxPerThread;   // 8192: the bound ranks the first tile
+constexpr int kTile = kCThreads * kMaxPerThread;   // 8192 groups: one pass of the K2 block
 constexpr int kBins = 2048;            // bound and superset histograms; global radix bins
 constexpr int kLdsCand = 4096;         // superset entries LDS holds
 constexpr int kFullCap = 256;          // groups whose second key may reach L (read whole)
@@ -1064,21 +1065,41 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, 
     for (int j = 0; j < 4; ++j) { mv[j] = m0[j]; mv[4 + j] = m1[j]; sv[j] = s0[j]; sv[4 + j] = s1[j]; }
   };
 
-  // (A) The bound L: at least keff groups have a maximum >= L, so L never exceeds the k-th
-  // largest score. L is the smallest, in the bin holding the keff-th largest or above, of the
-  // first tile's run maxima: the maxima of runs of 4 consecutive groups when the tile has at
-  // least 4 keff groups (a run at or above L holds a group at or above L), else the group
-  // maxima. Bins: (u - umin) >> shift, 2048 of them, monotone. Groups past the sequence read
-  // as key 0, below every score, and take no part.
+  // (A) The bound L: at least keff disjoint sets of groups have a maximum >= L, so L never
+  // exceeds the k-th largest score. The sets are the tile slots: slot e (< 8192) holds groups
+  // e, e + 8192, e + 2 * 8192, ... (one group when the sequence fits one tile), and its
+  // maximum is the largest over the tiles. L is the lower edge of the bin holding the
+  // keff-th largest of the maxima of runs of 4 consecutive slots when there are at least
+  // 4 keff slots (a run at or above L holds a slot at or above L), else of the slot maxima.
+  // Bins: (u - umin) >> shift, 2048 of them, monotone. Groups past the sequence read as key 0,
+  // below every score, and take no part. Every tile's maxima are ranked, so the bound and the
+  // largest key (the superset's bin range) cover the whole sequence.
   load_tile(0);
+  uint32_t rm[kMaxPerThread];                           // slot maxima over the tiles
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j) rm[j] = mv[j];
+  for (uint32_t t0 = kTile; t0 < ng; t0 += 4u * kTile) {
+    // Up to four further tiles per round: their loads are issued before any is used.
+    u32x4 x[4][2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t e0 = min(t0 + (uint32_t)r * kTile, ng) + kMaxPerThread * t;   // past ng: reads 0
+      x[r][0] = buffer_u32x4(mrs, e0);
+      x[r][1] = buffer_u32x4(mrs, e0 + 4);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { rm[j] = max(rm[j], x[r][0][j]); rm[4 + j] = max(rm[4 + j], x[r][1][j]); }
+  }
   for (uint32_t i = t; i < kBins; i += kCThreads) sh.hist[i] = 0u;
   if (t == 0) { sh.misc[2] = 0; sh.misc[5] = 0; }
   uint32_t L = 0, vmax = 0;
   if (nt >= 4u * keff) {
-    const uint32_t u[2] = {max(max(mv[0], mv[1]), max(mv[2], mv[3])), max(max(mv[4], mv[5]), max(mv[6], mv[7]))};
+    const uint32_t u[2] = {max(max(rm[0], rm[1]), max(rm[2], rm[3])), max(max(rm[4], rm[5]), max(rm[6], rm[7]))};
     L = block_bound<2>(u, keff, &vmax, sh);
   } else if (nt >= keff) {
-    L = block_bound<kMaxPerThread>(mv, keff, &vmax, sh);
+    L = block_bound<kMaxPerThread>(rm, keff, &vmax, sh);
   } else {                                              // fewer than k groups: every candidate
     __syncthreads();
   }
@@ -1384,6 +1405,21 @@ extern "C" chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_h
   if (topk_first(dtype, batch, &a, lpc, s) != CHS_OK) return CHS_ERR_LAUNCH;
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
   return launch_status();
+}
+
+extern "C" chs_status chs_index_scores(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
+                                       const void* q_idx, const float* w, const void* k_idx, const int64_t* cu_cand,
+                                       int64_t max_cand, float* scores, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  using namespace chs;
+  if (!q_idx || !scores) return CHS_ERR_NULL;
+  Args a;
+  int lpc = 2;
+  int32_t unused_topk = 0;                              // the selection's output is never written here
+  chs_status st = topk_setup(dtype, batch, n_heads, head_dim, 1, q_idx, w, k_idx, cu_cand, max_cand, scores,
+                             &unused_topk, workspace, workspace_bytes, &a, &lpc);
+  if (st != CHS_OK) return st;
+  return topk_first(dtype, batch, &a, lpc, static_cast<hipStream_t>(stream)) == CHS_OK ? CHS_OK : CHS_ERR_LAUNCH;
 }
 
 extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,

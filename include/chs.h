@@ -196,6 +196,20 @@ chs_status chs_index_topk(chs_dtype dtype, int32_t batch, int32_t n_heads, int32
                           const int64_t* cu_cand, int64_t max_cand, float* scores, int32_t* topk,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- chs_index_scores: the indexer scores alone ---------------------------------------------
+ * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 5 (the indexer scores every compressed
+ * candidate ahead of the top-k). Computes exactly the scores chs_index_topk computes (the same kernel,
+ * bit-identical values) and no selection:
+ *   scores[cu_cand[b] + j] = sum_h w[b, h] * max(0, sum_t q_idx[b, h, t] * k_idx[cu_cand[b] + j, t]).
+ * q_idx, w, k_idx, cu_cand, max_cand: as chs_index_topk (q_idx must not be NULL).
+ * scores  : [cu_cand[batch]] fp32 output (not NULL).
+ * workspace: chs_index_topk_workspace_size(batch, max_cand, 1) bytes (the kernel also leaves its
+ *   per-group statistics there). Ranges and errors as chs_index_topk with q_idx given. */
+chs_status chs_index_scores(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
+                            const void* q_idx, const float* w, const void* k_idx, const int64_t* cu_cand,
+                            int64_t max_cand, float* scores, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* ---- chs_index_topk_fp8: chs_index_topk with FP8 index keys --------------------------------
  * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (the checkpoints keep
  * attention in FP8) and "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 4.3 部署配置建议 (an

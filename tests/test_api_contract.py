@@ -242,6 +242,26 @@ def topk8(batch=1, nh=4, dim=128, k=512, q=FAKE, w=FAKE, kk=FAKE, sc=FAKE, cu=FA
     return L.chs_index_topk_fp8(batch, nh, dim, k, q, w, kk, sc, cu, maxc, s, out, ws, wsb, None)
 
 
+def index_scores(dt=1, batch=1, nh=4, dim=128, q=FAKE, w=FAKE, kk=FAKE, cu=FAKE, maxc=1000, s=FAKE, ws=FAKE,
+                 wsb=1 << 20):
+    return chs.lib().chs_index_scores(dt, batch, nh, dim, q, w, kk, cu, maxc, s, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), DTYPE), (dict(batch=0), SHAPE), (dict(nh=0), SHAPE), (dict(nh=17), SHAPE), (dict(dim=4), SHAPE),
+    (dict(dim=520), SHAPE), (dict(maxc=-1), SHAPE), (dict(maxc=(1 << 22) + 1), UNSUP), (dict(q=None), NULL),
+    (dict(w=None), NULL), (dict(kk=None), NULL), (dict(cu=None), NULL), (dict(s=None), NULL), (dict(ws=None), NULL),
+    (dict(wsb=16), WS), (dict(maxc=0), OK),
+])
+def test_index_scores_validation(kw, code):
+    assert index_scores(**kw) == code
+
+
+def test_index_scores_workspace_is_the_topk_workspace():
+    L = chs.lib()
+    assert L.chs_index_topk_workspace_size(3, 262144, 1) == L.chs_index_topk_workspace_size(3, 262144, 512)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(k=0), SHAPE), (dict(k=2049), SHAPE), (dict(batch=0), SHAPE), (dict(maxc=-1), SHAPE),
     (dict(maxc=1 << 31), SHAPE), (dict(nh=0), SHAPE), (dict(nh=17), SHAPE), (dict(dim=8), SHAPE),

@@ -249,6 +249,10 @@ def test_index_topk_matches_oracle(dtype, nh, dim, lens, k):
                              _to_dev(cu, torch.int64), k, scores=scores)
     sg = scores.cpu().numpy()
     tg = topk.cpu().numpy()
+    # chs_index_scores runs the same score kernel with no selection: bit-identical scores.
+    alone = chs.index_scores(_to_dev(q, TORCH_DT[dtype]), _to_dev(w, torch.float32), _to_dev(K, TORCH_DT[dtype]),
+                             _to_dev(cu, torch.int64)).cpu().numpy()
+    assert np.array_equal(alone.view(np.uint32), sg.view(np.uint32)), "index_scores differs from index_topk's scores"
     for b in range(B):
         s_ref = oracle.index_scores(q[b], w[b], K[cu[b]:cu[b + 1]])
         s_gpu = sg[cu[b]:cu[b + 1]]

@@ -57,6 +57,8 @@ CASES = [
     (4, [0, 4000, 1], 24, 128, 64, 100, 4, 64, [5, 64, 0]),
     (5, [20000], 72, 256, 128, 512, 8, 128, [0]),
     (6, [70000], 64, 512, 128, 2048, 4, 128, [128]),
+    # more than one selection tile (8192 groups of 32 candidates) in one sequence
+    (7, [300000, 2000], 16, 64, 64, 512, 4, 128, [64, 10]),
 ]
 
 
