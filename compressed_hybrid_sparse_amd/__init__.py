@@ -24,7 +24,7 @@ EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compr
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
            "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
            "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged",
-           "chs_decode_step_workspace_size", "chs_decode_step", "chs_index_scores")
+           "chs_decode_step_workspace_size", "chs_decode_step", "chs_index_scores", "chs_decode_step_noalloc")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -87,11 +87,14 @@ def lib():
         L.chs_decode_step_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64]
         L.chs_decode_step.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
                                       _i64, _p, _p, _p, _p, _p, _sz, _p]
+        L.chs_decode_step_noalloc.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
+                                              _p, _i64, _p, _p, _p, _p, _p]
         L.chs_append_multi.argtypes = [ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(AppendStream), _p]
         L.chs_gather_selected.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
-        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_index_scores", "chs_decode_attn", "chs_index_topk_fp8",
+        for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_index_scores", "chs_decode_step_noalloc",
+                   "chs_decode_step", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
                    "chs_index_topk_paged", "chs_gather_selected", "chs_append_multi", "chs_index_topk_fp8_paged",
                    "chs_decode_attn_fp8_paged"):
@@ -456,6 +459,50 @@ def decode_step(q_idx, w, k_idx, q, swa_kv, swa_len, comp_kv, cu_comp, k: int, s
                                  _ptr(k_idx), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(cu_comp),
                                  int(max_comp), _ptr(scores), _ptr(topk), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel(), _stream()), "chs_decode_step")
+    return topk, out, lse, scores
+
+
+def decode_step_noalloc(q_idx, w, k_idx, q, swa_kv, swa_len, comp_kv, cu_comp, k: int, scale=None, max_comp=None,
+                        scores=None, topk=None, out=None, lse=None):
+    """decode_step without a workspace (chs_decode_step_noalloc): the library's per-GPU scratch array
+    (CHS_NOALLOC_SCRATCH_BYTES) serves instead, so the C call allocates nothing. Calls that overlap on
+    one GPU race on that array. Arguments and results as decode_step; outputs not given are allocated
+    here by torch, before the call."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(swa_kv, "swa_kv", torch.bfloat16, 3)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_kv, "comp_kv", torch.bfloat16, 2)
+    _need(cu_comp, "cu_comp", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_kv.shape[1]
+    _attn_shapes(q, swa_kv, swa_len, comp_kv, cu_comp)
+    if swa_kv.shape[0] != B or cu_comp.numel() != B + 1:
+        raise ValueError(f"swa_kv must have {B} windows and cu_comp {B + 1} entries")
+    if q_idx.shape[0] != B or k_idx.shape[1] != q_idx.shape[2]:
+        raise ValueError("q_idx must be [B, Hi, dim] and k_idx [G, dim]")
+    _shape(w, q_idx.shape[:2], "w")
+    max_comp, total = _cu_sizes(cu_comp, max_comp)
+    if scale is None:
+        scale = d ** -0.5
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 1)
+    if total is not None:
+        _rows(comp_kv, total, "comp_kv")
+        _rows(k_idx, total, "k_idx")
+        if scores is not None:
+            _rows(scores, total, "scores")
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=q.device)
+    out, lse = _attn_outputs(q, out, lse)
+    _need(topk, "topk", torch.int32, 2)
+    _shape(topk, (B, k), "topk")
+    _check(lib().chs_decode_step_noalloc(B, H, d, W, k, float(scale), q_idx.shape[1], q_idx.shape[2], _ptr(q_idx),
+                                         _ptr(w), _ptr(k_idx), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv),
+                                         _ptr(cu_comp), int(max_comp), _ptr(scores), _ptr(topk), _ptr(out), _ptr(lse),
+                                         _stream()), "chs_decode_step_noalloc")
     return topk, out, lse, scores
 
 

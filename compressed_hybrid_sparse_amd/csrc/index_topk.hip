@@ -48,6 +48,7 @@
 // The composite order (key descending, then index ascending) is total, so the selected set is
 // unique and bit-identical to a full sort of the same scores.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1587,13 +1588,14 @@ extern "C" size_t chs_decode_step_workspace_size(int32_t batch, int32_t n_heads,
   return chs::step_ws(batch, n_heads, d, window, k, max_comp, nullptr);
 }
 
-extern "C" chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
-                                      float scale, int32_t idx_heads, int32_t idx_dim, const void* q_idx,
-                                      const float* w, const void* k_idx, const void* q, const void* swa_kv,
-                                      const int32_t* swa_len, const void* comp_kv, const int64_t* cu_comp,
-                                      int64_t max_comp, float* scores, int32_t* topk, float* out, float* lse,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace chs;
+namespace chs {
+namespace {
+
+chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, float scale,
+                            int32_t idx_heads, int32_t idx_dim, const void* q_idx, const float* w, const void* k_idx,
+                            const void* q, const void* swa_kv, const int32_t* swa_len, const void* comp_kv,
+                            const int64_t* cu_comp, int64_t max_comp, float* scores, int32_t* topk, float* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   chs_status st = attn::check_args(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv,
                                    cu_comp, topk, max_comp, out);
   if (st != CHS_OK) return st;
@@ -1632,4 +1634,60 @@ extern "C" chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d,
                    (unsigned)batch);
   hipLaunchKernelGGL(step_combine_kernel, cgrid, dim3(attn::kAttnThreads), 0, s, a, out, lse);
   return launch_status();
+}
+
+// Scratch of chs_decode_step_noalloc: one array per GPU, part of the code object, so the call itself
+// allocates nothing. Host code uses the device address hipGetSymbolAddress returns for the current
+// device (the array's name is not a device address on the host).
+constexpr size_t kNoAllocScratch = CHS_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch array's device address on the current device, looked up once per device.
+chs_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CHS_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CHS_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CHS_OK;
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                      float scale, int32_t idx_heads, int32_t idx_dim, const void* q_idx,
+                                      const float* w, const void* k_idx, const void* q, const void* swa_kv,
+                                      const int32_t* swa_len, const void* comp_kv, const int64_t* cu_comp,
+                                      int64_t max_comp, float* scores, int32_t* topk, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return chs::decode_step_impl(batch, n_heads, d, window, k, scale, idx_heads, idx_dim, q_idx, w, k_idx, q, swa_kv,
+                               swa_len, comp_kv, cu_comp, max_comp, scores, topk, out, lse, workspace,
+                               workspace_bytes, stream);
+}
+
+extern "C" chs_status chs_decode_step_noalloc(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                              float scale, int32_t idx_heads, int32_t idx_dim, const void* q_idx,
+                                              const float* w, const void* k_idx, const void* q, const void* swa_kv,
+                                              const int32_t* swa_len, const void* comp_kv, const int64_t* cu_comp,
+                                              int64_t max_comp, float* scores, int32_t* topk, float* out, float* lse,
+                                              void* stream) {
+  using namespace chs;
+  // The size check comes first, so an oversized call is refused before the device is touched.
+  const size_t need = chs_decode_step_workspace_size(batch, n_heads, d, window, k, max_comp);
+  if (need == 0) return CHS_ERR_SHAPE;
+  if (need > kNoAllocScratch) return CHS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const chs_status st = scratch_for_current_device(&ws);
+  if (st != CHS_OK) return st;
+  return decode_step_impl(batch, n_heads, d, window, k, scale, idx_heads, idx_dim, q_idx, w, k_idx, q, swa_kv,
+                          swa_len, comp_kv, cu_comp, max_comp, scores, topk, out, lse, ws, kNoAllocScratch, stream);
 }

@@ -288,6 +288,28 @@ chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d, int32_t wi
                            int32_t* topk, float* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- chs_decode_step_noalloc: chs_decode_step for callers that cannot allocate ------------------
+ * For callers that cannot call hipMalloc or pass a workspace: code under HIP graph capture that must
+ * not allocate, tight serving loops, harnesses that forbid allocation. Computes exactly what
+ * chs_decode_step computes (the same kernels; scores, topk, out and lse bit-identical), with the
+ * workspace taken from a scratch array inside the library instead of the caller: one array of
+ * CHS_NOALLOC_SCRATCH_BYTES per GPU, part of the library's device code, held by each GPU the call
+ * runs on until the process ends. The call allocates and frees nothing; its first call on a device
+ * looks the array's device address up once (hipGetSymbolAddress).
+ * Arguments: as chs_decode_step, without the workspace. A call whose chs_decode_step workspace would
+ * exceed CHS_NOALLOC_SCRATCH_BYTES returns CHS_ERR_WORKSPACE and launches nothing (at 1M tokens
+ * and batch 1 the step needs about 3.8 MiB; 64 sequences of 200K tokens about 33 MiB).
+ * Every call on a GPU shares that GPU's array, and the array keeps the last call's contents (the
+ * step needs no initialised scratch): calls that overlap on one GPU, on different streams or from
+ * different threads, race on it and must be serialised by the caller. */
+#define CHS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+chs_status chs_decode_step_noalloc(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                   float scale, int32_t idx_heads, int32_t idx_dim, const void* q_idx,
+                                   const float* w, const void* k_idx, const void* q, const void* swa_kv,
+                                   const int32_t* swa_len, const void* comp_kv, const int64_t* cu_comp,
+                                   int64_t max_comp, float* scores, int32_t* topk, float* out, float* lse,
+                                   void* stream);
+
 /* ---- Paged pools: chs_decode_attn_paged, chs_append_paged ----------------------------------
  * Source: "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 创新 1 (ShadowRadix: a per-request index
  * projected onto separate physical pools for the window, the C4 and the C128 entries, plus the

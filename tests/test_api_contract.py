@@ -360,3 +360,15 @@ def test_workspace_clear_validation():
     assert L.chs_workspace_clear(None, 0, None) == OK
     assert L.chs_workspace_clear(None, 16, None) == NULL
     assert L.chs_workspace_clear(FAKE, 6, None) == SHAPE
+
+
+def test_decode_step_noalloc_refuses_before_touching_the_device():
+    # Checked without a GPU: a workspace beyond the scratch array and invalid shapes are refused
+    # before the call looks up its device or launches anything.
+    L = chs.lib()
+    big = L.chs_decode_step_noalloc(64, 128, 512, 4096, 2048, ctypes.c_float(0.04), 4, 128, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, 1 << 22, None, FAKE, FAKE, FAKE, None)
+    assert big == WS
+    bad = L.chs_decode_step_noalloc(0, 64, 512, 128, 512, ctypes.c_float(0.04), 4, 128, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, 1000, None, FAKE, FAKE, FAKE, None)
+    assert bad == SHAPE
