@@ -44,6 +44,8 @@ def _load():
         lib.oracle_attend.argtypes = [ctypes.c_int32, ctypes.c_int32, _p, ctypes.c_int64, _p, ctypes.c_double,
                                       _p, _p]
         lib.oracle_round_bf16.argtypes = [_p, ctypes.c_int64, _p]
+        lib.oracle_encode_e4m3_n.argtypes = [ctypes.c_int64, _p, _p]
+        lib.oracle_quantize_e4m3_rows.argtypes = [ctypes.c_int64, ctypes.c_int32, _p, _p, _p]
         _lib = lib
     return _lib
 
@@ -103,6 +105,25 @@ def decode_e4m3(codes) -> np.ndarray:
     out = np.empty(c.shape, dtype=np.float64)
     _load().oracle_decode_e4m3_n(c.size, _ptr(c), _ptr(out))
     return out
+
+
+def encode_e4m3(y) -> np.ndarray:
+    """fp32 values -> E4M3 codes: nearest value, ties to the even code, saturating at +-448."""
+    y = _f32(y)
+    out = np.empty(y.shape, dtype=np.uint8)
+    _load().oracle_encode_e4m3_n(y.size, _ptr(y), _ptr(out))
+    return out
+
+
+def quantize_e4m3(rows):
+    """Per-row E4M3 quantisation of fp32 rows [n, d] (see oracle.c): returns (codes [n, d] uint8,
+    scales [n] fp32), row r = scales[r] * decode(codes[r])."""
+    x = _f32(rows)
+    n, d = x.shape
+    codes = np.empty((n, d), dtype=np.uint8)
+    scales = np.empty(n, dtype=np.float32)
+    _load().oracle_quantize_e4m3_rows(n, d, _ptr(x), _ptr(codes), _ptr(scales))
+    return codes, scales
 
 
 def index_scores_fp8(q, w, K8, scale) -> np.ndarray:

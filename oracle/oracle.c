@@ -223,3 +223,49 @@ void oracle_round_bf16(const double* x, int64_t n, float* out) {
     out[j] = (float)ldexp(r, e - 8);
   }
 }
+
+/* ---- FP8 E4M3 storage written by the library ([P2] V4 到底改了啥: attention kept in FP8; [P3]
+ * 4.3 部署配置建议: an fp8 KV cache). The pages fix no rounding or scale rule; the reading taken here:
+ * one fp32 scale per row, the row's largest magnitude mapped to the largest E4M3 value 448, every
+ * element rounded to the nearest E4M3 value.
+ *
+ * Encoding of one value y (fp32): the nearest of the 254 finite E4M3 values (decode above), ties to
+ * the even code (the code whose lowest mantissa bit is 0); magnitudes above 448 saturate to 448.
+ * Written as the plain search over the non-negative codes 0x00 .. 0x7E (0x7F is NaN), in double,
+ * where both y and every E4M3 value are exact. */
+uint8_t oracle_encode_e4m3(float y) {
+  const double a = fabs((double)y);
+  const uint8_t sign = signbit(y) ? 0x80 : 0x00;      /* the sign is kept, zeros included */
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    const double err = fabs(oracle_decode_e4m3((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) { best = c; best_err = err; }
+  }
+  if (a > 448.0) best = 0x7E;
+  return (uint8_t)(sign | best);
+}
+
+void oracle_encode_e4m3_n(int64_t n, const float* y, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_encode_e4m3(y[i]);
+}
+
+/* Per-row quantisation of rows [n, d] of fp32 values:
+ *   amax = max_c |x_c|,  scale = fp32(amax / 448),  code_c = encode(fp32(x_c / scale)),
+ * each division rounded once to fp32 (a double quotient of two fp32 operands rounds to the same
+ * fp32 value as a correctly rounded fp32 division). A row with amax = 0 has scale 0 and all codes 0.
+ * Row r decodes as scale_r * decode(code). */
+void oracle_quantize_e4m3_rows(int64_t n, int32_t d, const float* x, uint8_t* codes, float* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    float amax = 0.0f;
+    for (int32_t c = 0; c < d; ++c) {
+      const float v = fabsf(x[r * d + c]);
+      if (v > amax) amax = v;
+    }
+    const float s = (float)((double)amax / 448.0);
+    scales[r] = s;
+    for (int32_t c = 0; c < d; ++c)
+      codes[r * d + c] = s == 0.0f ? 0 : oracle_encode_e4m3((float)((double)x[r * d + c] / (double)s));
+  }
+}

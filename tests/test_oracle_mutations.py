@@ -47,6 +47,15 @@ MUTATIONS = [
     ("E4M3 decode: exponent bias off by one",
      "else v = ldexp(1.0 + m / 8.0, e - 7);",
      "else v = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("E4M3 encode: ties to the odd code",
+     "if (err < best_err || (err == best_err && (c & 1) == 0)) { best = c; best_err = err; }",
+     "if (err < best_err || (err == best_err && (c & 1) == 1)) { best = c; best_err = err; }"),
+    ("E4M3 encode: no saturation above 448",
+     "if (a > 448.0) best = 0x7E;",
+     "if (a > 464.0) best = 0x7F;"),
+    ("E4M3 quantisation: row maximum mapped to 240 instead of 448",
+     "const float s = (float)((double)amax / 448.0);",
+     "const float s = (float)((double)amax / 240.0);"),
 ]
 
 

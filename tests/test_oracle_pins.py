@@ -234,6 +234,92 @@ def test_decode_e4m3_closed_forms():
     assert np.array_equal(oracle.decode_e4m3(np.arange(0x80, 0xFF, dtype=np.uint8)), -pos)
 
 
+# ---------------------------------------------------------------- FP8 (E4M3) encoding and row quantisation
+def _torch_e4m3(y):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(y, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_grid():
+    """The 127 non-negative finite E4M3 values in code order, from torch's decoder."""
+    import torch
+    return torch.from_numpy(np.arange(0x7F, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_encode_e4m3_matches_torch_on_representable_values_midpoints_and_neighbours():
+    # An independent encoder: torch's float8_e4m3fn cast (round to nearest even). Inputs: every
+    # representable value, every midpoint between neighbours (the ties), and the fp32 neighbours
+    # of each midpoint (which must round away from the tie), in both signs, up to 448.
+    g = _e4m3_grid()
+    mids = (g[:-1] + g[1:]) / 2
+    pts = np.concatenate([g, mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                          np.nextafter(mids.astype(np.float32), np.float32(-np.inf))]).astype(np.float32)
+    pts = np.concatenate([pts, -pts, np.array([0.0, -0.0, 464.0, -464.0], np.float32)])
+    assert np.array_equal(oracle.encode_e4m3(pts), _torch_e4m3(pts))
+
+
+def test_encode_e4m3_matches_torch_on_random_fp32(rng):
+    # Wide exponent range, subnormal E4M3 results included (|y| < 2^-6), up to the tie at 464.
+    y = (rng.standard_normal(200000) * np.exp2(rng.uniform(-14, 9, 200000))).astype(np.float32)
+    y = y[np.abs(y) <= 464]
+    assert np.array_equal(oracle.encode_e4m3(y), _torch_e4m3(y))
+
+
+def test_encode_e4m3_closed_forms_and_saturation():
+    y = np.array([0.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -6, 1.0, 1.0625, 1.1875, 448.0, 460.0, 464.0,
+                  470.0, 1e6, np.float32(3.4e38), -448.0, -1e6, 2.0 ** -12, -2.0 ** -12], np.float32)
+    want = [0x00, 0x01, 0x00,         # 2^-10 ties between 0 and 2^-9: to the even code 0
+            0x02,                     # 3 * 2^-10 ties between codes 1 and 2: to 2
+            0x08, 0x38, 0x38,         # 1.0625 ties between 1 and 1.125: to 1.0 (0x38, even)
+            0x3A,                     # 1.1875 ties between 1.125 (0x39) and 1.25 (0x3A): to 0x3A
+            0x7E, 0x7E, 0x7E,         # 460 rounds to 448; 464 ties 448 / 480 and 480 does not exist: 448
+            0x7E, 0x7E, 0x7E,         # beyond 464 the magnitude saturates at 448 (no NaN is produced)
+            0xFE, 0xFE, 0x00, 0x80]   # tiny values round to a signed zero
+    assert oracle.encode_e4m3(y).tolist() == want
+
+
+def test_encode_e4m3_round_trip_and_monotone():
+    g = _e4m3_grid().astype(np.float32)
+    assert np.array_equal(oracle.encode_e4m3(g), np.arange(0x7F, dtype=np.uint8))
+    assert np.array_equal(oracle.encode_e4m3(-g[1:]), (np.arange(1, 0x7F) | 0x80).astype(np.uint8))
+    y = np.sort(np.random.default_rng(5).uniform(0, 500, 20000)).astype(np.float32)
+    c = oracle.encode_e4m3(y).astype(np.int64)
+    assert np.all(np.diff(c) >= 0)
+
+
+def test_quantize_rows_scale_and_error_bound(rng):
+    # The row's largest magnitude maps to 448 exactly; every element decodes within half a step of
+    # the E4M3 grid at its magnitude (relative 2^-4 for normals, absolute 2^-10 * scale below 2^-6).
+    x = (rng.standard_normal((300, 128)) * np.exp2(rng.uniform(-10, 10, (300, 1)))).astype(np.float32)
+    x[7] = 0.0
+    x[8, :] = 0.0
+    x[8, 3] = -2.5
+    codes, scales = oracle.quantize_e4m3(x)
+    assert scales[7] == 0.0 and np.all(codes[7] == 0)
+    amax = np.abs(x).max(axis=1)
+    assert np.array_equal(scales, (amax.astype(np.float64) / 448.0).astype(np.float32))
+    dec = oracle.decode_e4m3(codes)
+    j = np.abs(x).argmax(axis=1)
+    nz = amax > 0
+    assert np.all(np.abs(dec[np.arange(300), j][nz]) == 448.0)
+    y = x.astype(np.float64) / np.where(nz, scales, 1.0)[:, None]
+    step = np.where(np.abs(y) >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3),
+                    2.0 ** -9)
+    assert np.all(np.abs(dec - y)[nz] <= step[nz] / 2 * (1 + 1e-6))
+    assert dec[8, 3] == -448.0 and np.count_nonzero(dec[8]) == 1
+
+
+def test_quantize_rows_are_independent_and_scale_invariant(rng):
+    # Scaling a row by a power of two scales its scale and leaves its codes unchanged; rows do not
+    # interact.
+    x = rng.standard_normal((20, 64)).astype(np.float32)
+    c1, s1 = oracle.quantize_e4m3(x)
+    c2, s2 = oracle.quantize_e4m3(x * np.float32(8.0))
+    assert np.array_equal(c1, c2) and np.array_equal(s2, s1 * 8)
+    c3, s3 = oracle.quantize_e4m3(x[::-1].copy())
+    assert np.array_equal(c3, c1[::-1]) and np.array_equal(s3, s1[::-1])
+
+
 def test_index_scores_fp8_one_hot_query_reads_one_code(rng):
     # q = e_t picks element t of the row: s = w0 relu(c d) + w1 relu(-c d) = c d (d > 0) or 2 c |d|.
     codes = np.arange(256, dtype=np.uint8)
