@@ -328,6 +328,18 @@ def main():
                                         algorithmic_bytes=compress_bytes([G], 4, d),
                                         hbm_frac=frac(compress_bytes([G], 4, d), median(c4_us)),
                                         value_source="events around each call")
+    # The same prefill with E4M3 output (chs_compress_fp8): the FP8 step below reads these entries.
+    comp8 = torch.empty(G, d, dtype=torch.uint8, device=dev)
+    comp8_s = torch.empty(G, dtype=torch.float32, device=dev)
+
+    def compress4_fp8(_i):
+        chs.compress_fp8(inp["X"], inp["Z"], inp["bias"], layer.m, inp["cu_tokens"], inp["cu_groups"], G, comp8,
+                         comp8_s)
+
+    c8_us = per_call_us(compress4_fp8, 5, warm=2)
+    c8_bytes = compress_bytes([G], 4, d) - G * d * 2 + G * (d + 4)
+    comps["compress_fp8_c4_1m_bf16"] = dict(call="chs_compress_fp8", m=4, tokens=n, median_us=r2(median(c8_us)),
+                                            algorithmic_bytes=c8_bytes, hbm_frac=frac(c8_bytes, median(c8_us)))
     del inp["X"], inp["Z"]
     torch.cuda.empty_cache()
 
@@ -389,7 +401,7 @@ def main():
                                          algorithmic_bytes=step_bytes, hbm_frac=frac(step_bytes, step_us))
     if not args.headline_only:
         run_components(torch, chs, synth, W, dev, comps, per_call_us, graph_us, wl, layer, inp, sets, comp, scores,
-                       topk, out, lse, ws_step, step)
+                       topk, out, lse, ws_step, step, comp8, comp8_s)
     if args.calib_copy:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
         bcopy = torch.empty_like(a)
@@ -434,7 +446,7 @@ def main():
 
 
 def run_components(torch, chs, synth, W, dev, comps, per_call_us, graph_us, wl, layer, inp, sets, comp, scores, topk,
-                   out, lse, ws_step, step):
+                   out, lse, ws_step, step, comp8, comp8_s):
     import numpy as np
     n, d, H, k = wl.lengths[0], wl.d, wl.heads, layer.k
     G = n // layer.m
@@ -466,17 +478,16 @@ def run_components(torch, chs, synth, W, dev, comps, per_call_us, graph_us, wl, 
     comps["decode_step_hot_us"] = dict(call="chs_decode_step on one input set (keys and gathers cache-resident)",
                                        graph_median=r2(hot_us), hbm_frac_if_cold=frac(step_bytes, hot_us))
 
-    # ---- FP8 storage: index keys and KV cache quantised per row (input preparation, torch's cast)
+    # ---- FP8 storage written by the library: the entries by chs_compress_fp8 (in main), the index keys
+    # and the windows by chs_quantize_e4m3 (E4M3 codes, one fp32 scale per row)
     log("components: fp8 step")
-
-    def quantise(kb):
-        kf = kb.float()
-        sc = (kf.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
-        return (kf / sc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc.contiguous()
-
-    fp8 = [quantise(sets[i]["keys"]) for i in range(C)]
-    comp8, comp8_s = quantise(comp)
-    sw8 = [quantise(sets[i]["swa"].reshape(-1, d)) for i in range(C)]
+    fp8 = [chs.quantize_e4m3(sets[i]["keys"]) for i in range(C)]
+    sw8 = [chs.quantize_e4m3(sets[i]["swa"].reshape(-1, d)) for i in range(C)]
+    kq_us = per_call_us(lambda i: chs.quantize_e4m3(sets[i % C]["keys"], *fp8[i % C]), 2 * C)
+    kq_bytes = G * wl.idx_dim * 2 + G * wl.idx_dim + G * 4
+    comps["quantize_e4m3_keys_us"] = dict(call="chs_quantize_e4m3 (262,144 index keys of 128)",
+                                          median_us=r2(median(kq_us)), algorithmic_bytes=kq_bytes,
+                                          hbm_frac=frac(kq_bytes, median(kq_us)))
 
     def decode_fp8(i):
         codes, sc = fp8[i % C]
@@ -491,7 +502,7 @@ def run_components(torch, chs, synth, W, dev, comps, per_call_us, graph_us, wl, 
                  + (k + wl.window) * (d + 4))
     comps["decode_step_fp8_us"] = dict(call="chs_index_topk_fp8 + chs_decode_attn_fp8", graph_median=r2(fp8_us),
                                        algorithmic_bytes=fp8_bytes, hbm_frac=frac(fp8_bytes, fp8_us))
-    del fp8, comp8, comp8_s, sw8
+    del fp8, sw8
     torch.cuda.empty_cache()
 
     # ---- the per-token step: appends of the new token's KV row and index key (one launch), then the

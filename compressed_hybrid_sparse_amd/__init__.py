@@ -24,7 +24,8 @@ EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compr
            "chs_decode_attn", "chs_index_topk_fp8", "chs_decode_attn_fp8", "chs_append",
            "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
            "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged",
-           "chs_decode_step_workspace_size", "chs_decode_step", "chs_index_scores", "chs_decode_step_noalloc")
+           "chs_decode_step_workspace_size", "chs_decode_step", "chs_index_scores", "chs_decode_step_noalloc",
+           "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -89,11 +90,16 @@ def lib():
                                       _i64, _p, _p, _p, _p, _p, _sz, _p]
         L.chs_decode_step_noalloc.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                                               _p, _i64, _p, _p, _p, _p, _p]
+        L.chs_quantize_e4m3.argtypes = [ctypes.c_int, _i64, _i32, _p, _p, _p, _p]
+        L.chs_compress_fp8.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _p]
+        L.chs_append_fp8.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                     _p, _i64, _p, _p, _p, _i64, _p, _p]
         L.chs_append_multi.argtypes = [ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(AppendStream), _p]
         L.chs_gather_selected.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_index_scores", "chs_decode_step_noalloc",
+                   "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8",
                    "chs_decode_step", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
                    "chs_index_topk_paged", "chs_gather_selected", "chs_append_multi", "chs_index_topk_fp8_paged",
@@ -210,6 +216,104 @@ def compress(x, gate, bias, m: int, cu_tokens, cu_groups=None, max_groups=None, 
                               _ptr(bias), _ptr(cu_tokens), _ptr(cu_groups), int(max_groups), _ptr(out),
                               _stream()), "chs_compress")
     return out
+
+
+# ---------------------------------------------------------------- FP8 writers
+def quantize_e4m3(rows, codes=None, scales=None):
+    """Per-row E4M3 codes and fp32 scales of rows [n, d] (bf16 or fp32) (chs_quantize_e4m3).
+    Returns (codes [n, d] uint8, scales [n] fp32)."""
+    _need(rows, "rows", dim=2)
+    n, d = rows.shape
+    if codes is None:
+        codes = torch.empty(n, d, dtype=torch.uint8, device=rows.device)
+    if scales is None:
+        scales = torch.empty(n, dtype=torch.float32, device=rows.device)
+    _need(codes, "codes", torch.uint8, 2)
+    _need(scales, "scales", torch.float32, 1)
+    _shape(codes, (n, d), "codes")
+    _shape(scales, (n,), "scales")
+    _check(lib().chs_quantize_e4m3(_dtype_code(rows), n, d, _ptr(rows), _ptr(codes), _ptr(scales), _stream()),
+           "chs_quantize_e4m3")
+    return codes, scales
+
+
+def compress_fp8(x, gate, bias, m: int, cu_tokens, cu_groups=None, max_groups=None, codes=None, scales=None):
+    """chs_compress with E4M3 output (chs_compress_fp8): returns (codes [G, d] uint8, scales [G] fp32)."""
+    _need(x, "x", dim=2)
+    _need(gate, "gate", x.dtype, 2)
+    _need(bias, "bias", torch.float32, 2)
+    _need(cu_tokens, "cu_tokens", torch.int64, 1)
+    if cu_groups is None:
+        lens = cu_tokens[1:] - cu_tokens[:-1]
+        cu_groups = torch.zeros_like(cu_tokens)
+        cu_groups[1:] = torch.cumsum(torch.div(lens, m, rounding_mode="floor"), 0)
+    _need(cu_groups, "cu_groups", torch.int64, 1)
+    if cu_groups.numel() != cu_tokens.numel():
+        raise ValueError("cu_groups and cu_tokens must have the same length")
+    _shape(gate, x.shape, "gate")
+    _shape(bias, (m, x.shape[1]), "bias")
+    max_groups, n_out = _cu_sizes(cu_groups, max_groups)
+    if n_out is not None:
+        _rows(x, int(cu_tokens[-1].item()), "x")
+    rows = n_out if n_out is not None else int(cu_groups[-1].item())
+    if codes is None:
+        codes = torch.empty(rows, x.shape[1], dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8, 2)
+    _need(scales, "scales", torch.float32, 1)
+    if codes.shape[1] != x.shape[1] or scales.shape[0] < codes.shape[0]:
+        raise ValueError("codes must have d columns and scales one entry per code row")
+    if n_out is not None:
+        _rows(codes, n_out, "codes")
+    _check(lib().chs_compress_fp8(_dtype_code(x), cu_tokens.numel() - 1, x.shape[1], m, _ptr(x), _ptr(gate),
+                                  _ptr(bias), _ptr(cu_tokens), _ptr(cu_groups), int(max_groups), _ptr(codes),
+                                  _ptr(scales), _stream()), "chs_compress_fp8")
+    return codes, scales
+
+
+def append_fp8(x_new, z_new, bias, m: int, n_tokens, swa_codes, swa_scale, x_ring, gate_ring, ring_page, comp_codes,
+               comp_scale, comp_start, ring_size=None, swa_len=None, comp_count=None):
+    """chs_append over an FP8 cache (chs_append_fp8): the new token's row quantised into the window
+    (swa_codes [B, W, d] uint8, swa_scale [B, W] fp32), its row and gate into the state rings (x_ring,
+    gate_ring [pages * ring_size, d], the storage type), a completed group pooled from the rings and
+    quantised into comp_codes [rows, d] uint8 / comp_scale [rows] fp32; counters advanced in place."""
+    _need(x_new, "x_new", dim=2)
+    dt = x_new.dtype
+    B, d = x_new.shape
+    _need(z_new, "z_new", dt, 2)
+    _need(bias, "bias", torch.float32, 2)
+    _need(n_tokens, "n_tokens", torch.int64, 1)
+    _need(swa_codes, "swa_codes", torch.uint8, 3)
+    _need(swa_scale, "swa_scale", torch.float32, 2)
+    _need(x_ring, "x_ring", dt, 2)
+    _need(gate_ring, "gate_ring", dt, 2)
+    _need(ring_page, "ring_page", torch.int32, 1)
+    _need(comp_codes, "comp_codes", torch.uint8, 2)
+    _need(comp_scale, "comp_scale", torch.float32, 1)
+    _need(comp_start, "comp_start", torch.int64, 1)
+    _shape(z_new, (B, d), "z_new")
+    _shape(bias, (m, d), "bias")
+    _shape(n_tokens, (B,), "n_tokens")
+    if swa_codes.shape[0] != B or swa_codes.shape[2] != d:
+        raise ValueError(f"swa_codes must be [{B}, W, {d}]")
+    W = swa_codes.shape[1]
+    _shape(swa_scale, (B, W), "swa_scale")
+    _shape(gate_ring, x_ring.shape, "gate_ring")
+    _shape(ring_page, (B,), "ring_page")
+    _shape(comp_start, (B,), "comp_start")
+    if x_ring.shape[1] != d or comp_codes.shape[1] != d or comp_scale.numel() < comp_codes.shape[0]:
+        raise ValueError("rings and pool must have d columns, comp_scale one entry per pool row")
+    for t, name in ((swa_len, "swa_len"), (comp_count, "comp_count")):
+        if t is not None and t.numel() < B:
+            raise ValueError(f"{name} must hold {B} entries")
+    if ring_size is None:
+        ring_size = x_ring.shape[0] // B
+    pages = x_ring.shape[0] // ring_size
+    _check(lib().chs_append_fp8(_dtype_code(x_new), B, d, m, W, int(ring_size), _ptr(x_new), _ptr(z_new), _ptr(bias),
+                                _ptr(n_tokens), _ptr(swa_codes), _ptr(swa_scale), _ptr(swa_len), _ptr(x_ring),
+                                _ptr(gate_ring), _ptr(ring_page), pages, _ptr(comp_codes), _ptr(comp_scale),
+                                _ptr(comp_start), comp_codes.shape[0], _ptr(comp_count), _stream()), "chs_append_fp8")
 
 
 # ---------------------------------------------------------------- chs_append

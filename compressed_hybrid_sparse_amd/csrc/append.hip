@@ -30,8 +30,17 @@
 //   count, a second, one-thread-per-sequence kernel advances the counters after them.
 // The new token's row and gate are read from the inputs, not from the rings being written in the
 // same launch, so no thread depends on another's store.
+//
+// chs_append_fp8 keeps an FP8 cache (E4M3 codes plus one fp32 scale per row, the rule of fp8.h):
+// the window gets the quantised row, which is lossy, so the state ring keeps the group's token rows
+// beside its gates in the storage type (the pages' ring keeps both), and a completed group is pooled
+// from the ring and quantised. The row scale is a maximum over the whole row, so one workgroup of 512
+// threads serves a sequence: a chunk's rows are split over adjacent lanes (merged by the butterfly
+// below; for m in {1, 2, 4, 8} one lane pools the whole group, bit-identical to chs_compress_fp8), and the row
+// maxima of the new token and of the pooled entry meet in LDS.
 #include <algorithm>
 
+#include "fp8.h"
 #include "pool.h"
 
 namespace chs {
@@ -277,6 +286,140 @@ __global__ __launch_bounds__(kSplitThreads) void append_split_kernel(AppendSet s
   if (blk == 0 && c < cpr) pool_store<ET>(st, static_cast<ET*>(a.comp) + row * d + col);
 }
 
+// ---------------------------------------------------------------- FP8 cache
+struct AppendFp8Args {
+  int32_t d, m, window, ring;
+  int64_t ring_pages, comp_rows;
+  const void* x_new;
+  const void* z_new;
+  const float* bias;
+  int64_t* n_tokens;
+  uint8_t* swa_codes;         // [batch][window][d]
+  float* swa_scale;           // [batch][window]
+  int32_t* swa_len;
+  void* x_ring;               // [ring_pages * ring][d], storage type
+  void* gate_ring;            // [ring_pages * ring][d], storage type
+  const int32_t* ring_page;   // [batch]
+  uint8_t* comp_codes;        // [comp_rows][d]
+  float* comp_scale;          // [comp_rows]
+  const int64_t* comp_start;  // [batch]
+  int64_t* comp_count;
+};
+
+constexpr int kFp8Threads = 512;
+
+// One workgroup per sequence. Thread (chunk c, block blk) = (tid / nb, tid % nb): nb lanes per
+// chunk (a power of two, at most 64), so a chunk's lanes are adjacent in one wave. M in {1, 2, 4, 8}:
+// lane blk = 0 pools the whole group with the prefill's instantiation (so the bits match); M = 0: any
+// m, the rows split over the chunk's lanes.
+template <typename ET, int M>
+__global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(AppendFp8Args a) {
+  using V = Vec16<ET>;
+  constexpr int N = V::N;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int d = a.d, m = a.m, W = a.window, R = a.ring;
+  const int cpr = d / N;                                // a power of two <= 64 (checked on the host)
+  const int nb = min(kFp8Threads / cpr, 64);
+  const int c = tid / nb, blk = tid & (nb - 1);
+  const bool on = c < cpr;                              // whole groups of nb lanes
+  const int col = (on ? c : cpr - 1) * N;
+  const ET* xn = static_cast<const ET*>(a.x_new) + (int64_t)b * d;
+  const ET* zn = static_cast<const ET*>(a.z_new) + (int64_t)b * d;
+  u32x4 x0 = {0, 0, 0, 0}, z0 = {0, 0, 0, 0};
+  if (on && blk == 0) {                                 // requested before the count is known
+    x0 = *reinterpret_cast<const u32x4*>(xn + col);
+    z0 = *reinterpret_cast<const u32x4*>(zn + col);
+  }
+  __shared__ int64_t s_t;
+  __shared__ float s_am[2][64];
+  if (tid == 0) {
+    int64_t n = a.n_tokens[b];
+    n = n < 0 ? 0 : n;
+    s_t = n;
+    a.n_tokens[b] = n + 1;
+    if (a.swa_len) a.swa_len[b] = (int32_t)(n + 1 < W ? n + 1 : W);
+    if (a.comp_count) a.comp_count[b] = (n + 1) / m;
+  }
+  __syncthreads();
+  const int64_t t = s_t;
+  const int64_t page = a.ring_page[b];
+  const bool page_ok = page >= 0 && page < a.ring_pages;
+  ET* xr = static_cast<ET*>(a.x_ring) + (page_ok ? page : 0) * R * d;
+  ET* zr = static_cast<ET*>(a.gate_ring) + (page_ok ? page : 0) * R * d;
+  if (on && blk == 0 && page_ok) {
+    *reinterpret_cast<u32x4*>(xr + (t % R) * d + col) = x0;
+    *reinterpret_cast<u32x4*>(zr + (t % R) * d + col) = z0;
+  }
+  int64_t row = -1;
+  if (page_ok && (t + 1) % m == 0) {
+    row = a.comp_start[b] + t / m;
+    if (row < 0 || row >= a.comp_rows) row = -1;        // outside the caller's pool: skipped
+  }
+  float o[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) o[j] = 0.f;
+  if (row >= 0 && on) {                                 // uniform over each chunk's lanes
+    const int64_t t0 = t + 1 - m;
+    const int q0 = (int)(t0 % R);
+    auto xrow = [&](int r) -> const ET* {
+      if (r == m - 1) return xn + col;
+      const int sl = q0 + r;
+      return xr + (int64_t)(sl < R ? sl : sl - R) * d + col;
+    };
+    auto zrow = [&](int r) -> const ET* {
+      if (r == m - 1) return zn + col;
+      const int sl = q0 + r;
+      return zr + (int64_t)(sl < R ? sl : sl - R) * d + col;
+    };
+    auto brow = [&](int r) { return a.bias + (int64_t)r * d + col; };
+    PoolState<N> st;
+    st.init();
+    if (M > 0) {
+      if (blk == 0) pool_block<ET, (M > 0 ? M : 1), true>(st, 0, M, xrow, zrow, brow);
+    } else {
+      const int rpt = (m + nb - 1) / nb;
+      const int r0 = blk * rpt, r1 = min(r0 + rpt, m);
+      for (int rr = r0; rr < r1; rr += 4) {
+        if (rr == r0) pool_block<ET, 4, true, true>(st, rr, min(4, r1 - rr), xrow, zrow, brow);
+        else pool_block<ET, 4, false, true>(st, rr, min(4, r1 - rr), xrow, zrow, brow);
+      }
+      if (nb > 1) merge_level<0>(st);
+      if (nb > 2) merge_level<1>(st);
+      if (nb > 4) merge_level<2>(st);
+      if (nb > 8) merge_level<3>(st);
+      if (nb > 16) merge_level<4>(st);
+      if (nb > 32) merge_level<5>(st);
+    }
+    pool_values<N>(st, o);
+  }
+  // The row maxima of the new token's row and of the pooled entry, one chunk per lane blk == 0.
+  float xv[N];
+  V::unpack(x0, xv);
+  if (on && blk == 0) {
+    float ax = 0.f, ao = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) { ax = fmaxf(ax, fabsf(xv[j])); ao = fmaxf(ao, fabsf(o[j])); }
+    s_am[0][c] = ax;
+    s_am[1][c] = ao;
+  }
+  __syncthreads();
+  if (!(on && blk == 0)) return;
+  float ax = 0.f, ao = 0.f;
+  for (int i = 0; i < cpr; ++i) { ax = fmaxf(ax, s_am[0][i]); ao = fmaxf(ao, s_am[1][i]); }
+  uint32_t w[N / 4];
+  const int64_t wrow = (int64_t)b * W + t % W;
+  const float sx = e4m3_scale(ax);
+  e4m3_pack<N>(xv, ax, w);
+  e4m3_store<N>(a.swa_codes + wrow * d + col, w);
+  if (c == 0) a.swa_scale[wrow] = sx;
+  if (row >= 0) {
+    const float so = e4m3_scale(ao);
+    e4m3_pack<N>(o, ao, w);
+    e4m3_store<N>(a.comp_codes + row * d + col, w);
+    if (c == 0) a.comp_scale[row] = so;
+  }
+}
+
 __global__ __launch_bounds__(256) void append_advance_kernel(AppendSet set, int32_t batch) {
   const AppendArgs& a = set.s[blockIdx.y];
   const int b = blockIdx.x * 256 + threadIdx.x;
@@ -403,4 +546,33 @@ extern "C" chs_status chs_append_multi(chs_dtype dtype, int32_t batch, int32_t m
   hipStream_t s = static_cast<hipStream_t>(stream);
   return dtype == CHS_BF16 ? launch_append<uint16_t>(set, n_streams, batch, s)
                            : launch_append<float>(set, n_streams, batch, s);
+}
+
+extern "C" chs_status chs_append_fp8(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
+                                     int32_t ring_size, const void* x_new, const void* z_new, const float* bias,
+                                     int64_t* n_tokens, uint8_t* swa_codes, float* swa_scale, int32_t* swa_len,
+                                     void* x_ring, void* gate_ring, const int32_t* ring_page, int64_t ring_pages,
+                                     uint8_t* comp_codes, float* comp_scale, const int64_t* comp_start,
+                                     int64_t comp_rows, int64_t* comp_count, void* stream) {
+  using namespace chs;
+  const chs_status st = check_append(dtype, batch, d, m, window, ring_size, x_new, z_new, bias, n_tokens, swa_codes,
+                                     gate_ring, comp_codes, comp_rows);
+  if (st != CHS_OK) return st;
+  if (ring_pages < 1) return CHS_ERR_SHAPE;
+  const int cpr = (int)(d * elem_size(dtype) / 16);
+  if (cpr > 64 || (cpr & (cpr - 1)) != 0) return CHS_ERR_UNSUPPORTED;
+  if (!swa_scale || !x_ring || !ring_page || !comp_scale || !comp_start) return CHS_ERR_NULL;
+  AppendFp8Args a{d, m, window, ring_size, ring_pages, comp_rows, x_new, z_new, bias, n_tokens, swa_codes, swa_scale,
+                  swa_len, x_ring, gate_ring, ring_page, comp_codes, comp_scale, comp_start, comp_count};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3((unsigned)batch), dim3(kFp8Threads), 0, s, a); };
+  const bool bf = dtype == CHS_BF16;
+  switch (m) {
+    case 1: bf ? go(append_fp8_kernel<uint16_t, 1>) : go(append_fp8_kernel<float, 1>); break;
+    case 2: bf ? go(append_fp8_kernel<uint16_t, 2>) : go(append_fp8_kernel<float, 2>); break;
+    case 4: bf ? go(append_fp8_kernel<uint16_t, 4>) : go(append_fp8_kernel<float, 4>); break;
+    case 8: bf ? go(append_fp8_kernel<uint16_t, 8>) : go(append_fp8_kernel<float, 8>); break;
+    default: bf ? go(append_fp8_kernel<uint16_t, 0>) : go(append_fp8_kernel<float, 0>); break;
+  }
+  return launch_status();
 }

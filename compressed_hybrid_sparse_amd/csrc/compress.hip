@@ -16,20 +16,50 @@
 // in one shot; larger groups (C128) stream 4 rows at a time with a running maximum
 // (online softmax), so registers stay bounded for any m, with the next 4 rows in flight; up to
 // d = 512 a workgroup stages each block's bias rows once in LDS for all its groups.
+//
+// chs_compress_fp8 is the same pass with E4M3 output: the pooled fp32 values of a group's row are
+// quantised in registers (the row maximum over the row's chunks by cross-lane moves, the threads of
+// a row being adjacent lanes of one wave), and the row is stored as 1-byte codes plus one fp32
+// scale, so the pass still reads the tokens and gates once and writes each entry once.
+#include "fp8.h"
 #include "pool.h"
 
 namespace chs {
 namespace {
 
+// Output of one entry chunk: the storage type (FP8 false) or E4M3 codes plus the row's scale (FP8
+// true; the cpr threads of a row, cpr a power of two <= 64, are adjacent lanes and all call it).
+template <typename ET, bool FP8>
+__device__ __forceinline__ void store_entry(const float* o, int cpr, int64_t row, int64_t col, int32_t d, ET* out,
+                                            uint8_t* codes, float* scales, bool store) {
+  constexpr int N = Vec16<ET>::N;
+  if (FP8) {
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) am = fmaxf(am, fabsf(o[j]));
+    am = group_max(am, cpr);
+    const float sc = e4m3_scale(am);
+    uint32_t w[N / 4];
+    e4m3_pack<N>(o, am, w);
+    if (store) {
+      e4m3_store<N>(codes + row * d + col, w);
+      if (col == 0) scales[row] = sc;
+    }
+  } else if (store) {
+    Vec16<ET>::store(out + row * d + col, o);
+  }
+}
+
 // Grid: (x: items of the longest sequence, y: sequence). A launch holds fewer than 2^32
 // work-items per grid dimension, so the x dimension strides over the sequence's items.
-template <typename ET, int M>
+template <typename ET, int M, bool FP8>
 __global__ __launch_bounds__(256) void compress_kernel(int32_t d, int32_t m, const ET* __restrict__ x,
                                                        const ET* __restrict__ gate,
                                                        const float* __restrict__ bias,
                                                        const int64_t* __restrict__ cu_tokens,
                                                        const int64_t* __restrict__ cu_groups,
-                                                       int64_t max_groups, ET* __restrict__ out) {
+                                                       int64_t max_groups, ET* __restrict__ out,
+                                                       uint8_t* __restrict__ codes, float* __restrict__ scales) {
   constexpr int N = Vec16<ET>::N;
   const int cpr = d / N;
   const int b = blockIdx.y;
@@ -47,9 +77,11 @@ __global__ __launch_bounds__(256) void compress_kernel(int32_t d, int32_t m, con
     const ET* xp = x + row * d + col;
     const ET* zp = gate + row * d + col;
     const float* bp = bias + col;
-    pool_group<ET, M>(
+    float o[N];
+    pool_group_values<ET, M>(
         m, [&](int r) { return xp + (int64_t)r * d; }, [&](int r) { return zp + (int64_t)r * d; },
-        [&](int r) { return bp + (int64_t)r * d; }, out + (o0 + g) * d + col);
+        [&](int r) { return bp + (int64_t)r * d; }, o);
+    store_entry<ET, FP8>(o, cpr, o0 + g, col, d, out, codes, scales, true);
   }
 }
 
@@ -64,13 +96,14 @@ constexpr int kStageRows = 4;
 constexpr int kStageMaxD = 512;
 constexpr int kStageVec = kStageRows * kStageMaxD / 4 / 256;   // bias f32x4 per thread and stage
 
-template <typename ET>
+template <typename ET, bool FP8>
 __global__ __launch_bounds__(256) void compress_staged_kernel(int32_t d, int32_t m, const ET* __restrict__ x,
                                                               const ET* __restrict__ gate,
                                                               const float* __restrict__ bias,
                                                               const int64_t* __restrict__ cu_tokens,
                                                               const int64_t* __restrict__ cu_groups,
-                                                              int64_t max_groups, ET* __restrict__ out) {
+                                                              int64_t max_groups, ET* __restrict__ out,
+                                                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
   using V = Vec16<ET>;
   constexpr int N = V::N;
   constexpr int R = kStageRows;
@@ -179,14 +212,16 @@ __global__ __launch_bounds__(256) void compress_staged_kernel(int32_t d, int32_t
 #pragma unroll
       for (int r = 0; r < R; ++r) { xc[r] = xn[r]; zc[r] = zn[r]; }
     }
-    if (live) pool_store<ET>(st, out + (o0 + g) * d + col);
+    float o[N];
+    pool_values<N>(st, o);
+    store_entry<ET, FP8>(o, cpr, o0 + g, col, d, out, codes, scales, live);
   }
 }
 
-template <typename ET>
+template <typename ET, bool FP8>
 chs_status launch(int32_t batch, int32_t d, int32_t m, const void* x, const void* gate,
                   const float* bias, const int64_t* cu_tokens, const int64_t* cu_groups,
-                  int64_t max_groups, void* out, hipStream_t stream) {
+                  int64_t max_groups, void* out, uint8_t* codes, float* scales, hipStream_t stream) {
   const int cpr = d / Vec16<ET>::N;
   const int64_t items = max_groups * cpr;
   int64_t blocks = (items + 255) / 256;
@@ -195,21 +230,21 @@ chs_status launch(int32_t batch, int32_t d, int32_t m, const void* x, const void
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, stream, d, m, static_cast<const ET*>(x),
                        static_cast<const ET*>(gate), bias, cu_tokens, cu_groups, max_groups,
-                       static_cast<ET*>(out));
+                       static_cast<ET*>(out), codes, scales);
   };
   switch (m) {
-    case 1: args(compress_kernel<ET, 1>); break;
-    case 2: args(compress_kernel<ET, 2>); break;
-    case 4: args(compress_kernel<ET, 4>); break;
-    case 8: args(compress_kernel<ET, 8>); break;
+    case 1: args(compress_kernel<ET, 1, FP8>); break;
+    case 2: args(compress_kernel<ET, 2, FP8>); break;
+    case 4: args(compress_kernel<ET, 4, FP8>); break;
+    case 8: args(compress_kernel<ET, 8, FP8>); break;
     default:
       if (d <= kStageMaxD) {
         const size_t lds = 2 * (size_t)kStageRows * d * sizeof(float);
-        hipLaunchKernelGGL(compress_staged_kernel<ET>, grid, block, lds, stream, d, m, static_cast<const ET*>(x),
-                           static_cast<const ET*>(gate), bias, cu_tokens, cu_groups, max_groups,
-                           static_cast<ET*>(out));
+        hipLaunchKernelGGL((compress_staged_kernel<ET, FP8>), grid, block, lds, stream, d, m,
+                           static_cast<const ET*>(x), static_cast<const ET*>(gate), bias, cu_tokens, cu_groups,
+                           max_groups, static_cast<ET*>(out), codes, scales);
       } else {
-        args(compress_kernel<ET, 0>);
+        args(compress_kernel<ET, 0, FP8>);
       }
       break;
   }
@@ -232,6 +267,31 @@ extern "C" chs_status chs_compress(chs_dtype dtype, int32_t batch, int32_t d, in
   if (max_groups == 0) return CHS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return dtype == CHS_BF16
-             ? launch<uint16_t>(batch, d, m, x, gate, bias, cu_tokens, cu_groups, max_groups, out, s)
-             : launch<float>(batch, d, m, x, gate, bias, cu_tokens, cu_groups, max_groups, out, s);
+             ? launch<uint16_t, false>(batch, d, m, x, gate, bias, cu_tokens, cu_groups, max_groups, out, nullptr,
+                                       nullptr, s)
+             : launch<float, false>(batch, d, m, x, gate, bias, cu_tokens, cu_groups, max_groups, out, nullptr,
+                                    nullptr, s);
+}
+
+extern "C" chs_status chs_compress_fp8(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, const void* x,
+                                       const void* gate, const float* bias, const int64_t* cu_tokens,
+                                       const int64_t* cu_groups, int64_t max_groups, uint8_t* out_codes,
+                                       float* out_scales, void* stream) {
+  using namespace chs;
+  if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
+  if (batch < 1 || batch > 65535 || m < 1 || m > 1024 || d < 1 || d > 4096 || max_groups < 0)
+    return CHS_ERR_SHAPE;
+  if ((d * elem_size(dtype)) % 16 != 0) return CHS_ERR_SHAPE;
+  // A row's chunks must be adjacent lanes of one wave: d / (elements per 16 bytes) a power of two
+  // of at most 64 (bf16: d in {8, 16, ..., 512}; fp32: d in {4, ..., 256}).
+  const int cpr = (int)(d * elem_size(dtype) / 16);
+  if (cpr > 64 || (cpr & (cpr - 1)) != 0) return CHS_ERR_UNSUPPORTED;
+  if (!x || !gate || !bias || !cu_tokens || !cu_groups || !out_codes || !out_scales) return CHS_ERR_NULL;
+  if (max_groups == 0) return CHS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == CHS_BF16
+             ? launch<uint16_t, true>(batch, d, m, x, gate, bias, cu_tokens, cu_groups, max_groups, nullptr,
+                                      out_codes, out_scales, s)
+             : launch<float, true>(batch, d, m, x, gate, bias, cu_tokens, cu_groups, max_groups, nullptr, out_codes,
+                                   out_scales, s);
 }

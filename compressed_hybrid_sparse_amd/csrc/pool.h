@@ -158,12 +158,18 @@ __device__ __forceinline__ void pool_block(PoolState<Vec16<ET>::N>& st, int r0, 
   }
 }
 
+// The pooled fp32 values of the chunk.
+template <int N>
+__device__ __forceinline__ void pool_values(const PoolState<N>& st, float* o) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) o[j] = st.acc[j] / st.sum[j];
+}
+
 template <typename ET>
 __device__ __forceinline__ void pool_store(const PoolState<Vec16<ET>::N>& st, ET* op) {
   constexpr int N = Vec16<ET>::N;
   float o[N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) o[j] = st.acc[j] / st.sum[j];
+  pool_values<N>(st, o);
   Vec16<ET>::store(op, o);
 }
 
@@ -237,10 +243,10 @@ __device__ __forceinline__ void pool_stream(PoolState<Vec16<ET>::N>& st, int m, 
   }
 }
 
-// A whole group of m rows: M > 0 is a compile-time group size (<= 8, one block); M == 0 takes
-// any m through pool_stream.
+// A whole group of m rows into its pooled fp32 values o: M > 0 is a compile-time group size
+// (<= 8, one block); M == 0 takes any m through pool_stream.
 template <typename ET, int M, bool ALL_LOADS_FIRST = false, typename XRow, typename ZRow, typename BRow>
-__device__ __forceinline__ void pool_group(int m, XRow xrow, ZRow zrow, BRow brow, ET* op) {
+__device__ __forceinline__ void pool_group_values(int m, XRow xrow, ZRow zrow, BRow brow, float* o) {
   PoolState<Vec16<ET>::N> st;
   st.init();
   if (M > 0) {
@@ -248,7 +254,15 @@ __device__ __forceinline__ void pool_group(int m, XRow xrow, ZRow zrow, BRow bro
   } else {
     pool_stream<ET, 4>(st, m, xrow, zrow, brow);
   }
-  pool_store<ET>(st, op);
+  pool_values<Vec16<ET>::N>(st, o);
+}
+
+// The same, stored in the storage type at op.
+template <typename ET, int M, bool ALL_LOADS_FIRST = false, typename XRow, typename ZRow, typename BRow>
+__device__ __forceinline__ void pool_group(int m, XRow xrow, ZRow zrow, BRow brow, ET* op) {
+  float o[Vec16<ET>::N];
+  pool_group_values<ET, M, ALL_LOADS_FIRST>(m, xrow, zrow, brow, o);
+  Vec16<ET>::store(op, o);
 }
 
 }  // namespace

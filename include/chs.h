@@ -93,6 +93,61 @@ chs_status chs_compress(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, co
                         const void* gate, const float* bias, const int64_t* cu_tokens,
                         const int64_t* cu_groups, int64_t max_groups, void* out, void* stream);
 
+/* ---- FP8 (E4M3) writers: chs_quantize_e4m3, chs_compress_fp8, chs_append_fp8 ---------------------
+ * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (the checkpoints keep attention in
+ * FP8) and "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 4.3 部署配置建议 (an fp8 KV cache). The
+ * pages fix neither the FP8 variant, the rounding nor a scale layout. Reading taken (the same one the
+ * FP8 readers chs_index_topk_fp8 and chs_decode_attn_fp8 take): OCP 8-bit E4M3 codes with one fp32
+ * scale per row, written as
+ *   amax = max_c |v_c|,  scale = amax / 448,  inv = min(448 / amax, FLT_MAX),  code_c = E4M3(v_c * inv)
+ * with every operation rounded once to fp32, E4M3() the nearest E4M3 value with ties to the even
+ * code and magnitudes from 448 up saturating to 448 (no NaN is written); a row of zeros gets scale 0
+ * and codes 0x00. The row then decodes as scale * decode(code), its largest element to +-448 * scale.
+ *
+ * chs_quantize_e4m3: rows the caller holds (the window after a prefill, index keys made elsewhere).
+ * in: [n_rows, d] of `dtype` (16-byte aligned); codes: [n_rows, d] bytes (8-byte aligned); scales:
+ * [n_rows] fp32. 0 <= n_rows <= 2^40; 8 <= d <= 4096, d % 8 == 0. n_rows = 0 launches nothing. */
+chs_status chs_quantize_e4m3(chs_dtype dtype, int64_t n_rows, int32_t d, const void* in, uint8_t* codes,
+                             float* scales, void* stream);
+
+/* chs_compress_fp8: chs_compress with E4M3 output, in the same single pass: every pooled entry row
+ * (the fp32 values chs_compress would round to its storage type) is quantised as above and written as
+ * out_codes[cu_groups[b] + g, :] ([cu_groups[batch], d] bytes) and out_scales[cu_groups[b] + g]
+ * ([cu_groups[batch]] fp32). Other arguments and ranges as chs_compress; in addition the row must be
+ * at most 64 16-byte chunks, a power of two of them (bf16: d in {8, 16, ..., 512}; fp32: d in
+ * {4, ..., 256}), else CHS_ERR_UNSUPPORTED. */
+chs_status chs_compress_fp8(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, const void* x,
+                            const void* gate, const float* bias, const int64_t* cu_tokens,
+                            const int64_t* cu_groups, int64_t max_groups, uint8_t* out_codes,
+                            float* out_scales, void* stream);
+
+/* chs_append_fp8: chs_append over an FP8 cache. For every sequence b, with t = n_tokens[b] before the
+ * call (a negative count reads as 0) and page = ring_page[b]:
+ *   swa_codes[b, t mod window, :], swa_scale[b, t mod window] = the quantised x_new[b, :];
+ *   x_ring[page * ring_size + t mod ring_size, :] = x_new[b, :];  gate_ring[same row, :] = z_new[b, :];
+ *   if (t + 1) mod m == 0, the group g = t / m (tokens t+1-m .. t) is pooled as chs_compress pools it,
+ *   its token rows and gates read from x_ring and gate_ring (which must hold what earlier appends, or
+ *   the caller after a prefill, wrote there), then quantised into comp_codes[comp_start[b] + g, :] and
+ *   comp_scale[comp_start[b] + g];
+ *   n_tokens, swa_len, comp_count as chs_append.
+ * The window holds quantised rows, so the group's rows come from the state ring, which keeps them
+ * in the storage type beside the gates. For m in {1, 2, 4, 8} the entries (codes and scales) are
+ * bit-identical to chs_compress_fp8's over the same history; the window codes are bit-identical to
+ * chs_quantize_e4m3 of the token rows.
+ * x_new, z_new: [batch, d] of `dtype`; bias: [m, d] fp32; n_tokens: [batch] int64 (in/out);
+ * swa_codes: [batch, window, d] bytes; swa_scale: [batch, window] fp32; swa_len: [batch] int32 or NULL;
+ * x_ring, gate_ring: [ring_pages * ring_size, d] of `dtype`; ring_page: [batch] int32 (a page outside
+ * [0, ring_pages) skips that sequence's ring writes and group); comp_codes: [comp_rows, d] bytes;
+ * comp_scale: [comp_rows] fp32; comp_start: [batch] int64 (a group whose row falls outside
+ * [0, comp_rows) is not written); comp_count: [batch] int64 or NULL.
+ * Ranges as chs_append, plus the row limit of chs_compress_fp8 (else CHS_ERR_UNSUPPORTED). */
+chs_status chs_append_fp8(chs_dtype dtype, int32_t batch, int32_t d, int32_t m, int32_t window,
+                          int32_t ring_size, const void* x_new, const void* z_new, const float* bias,
+                          int64_t* n_tokens, uint8_t* swa_codes, float* swa_scale, int32_t* swa_len,
+                          void* x_ring, void* gate_ring, const int32_t* ring_page, int64_t ring_pages,
+                          uint8_t* comp_codes, float* comp_scale, const int64_t* comp_start,
+                          int64_t comp_rows, int64_t* comp_count, void* stream);
+
 /* ---- chs_append: one decode-time token per sequence into the window and the state ring ----
  * Source: "DeepSeek-V4 本地部署，SGLang 把活做絕了", ShadowRadix (a compression state ring per
  * layer, nested in the sequence's SWA page at page * ring_size + position mod ring_size; 8 slots

@@ -22,6 +22,7 @@
  * top-k = the k largest, ties to the lower index, returned ascending; attention is one softmax
  * over window plus selected entries with K = V and logits scaled by 1/sqrt(d).
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -251,10 +252,12 @@ void oracle_encode_e4m3_n(int64_t n, const float* y, uint8_t* out) {
 }
 
 /* Per-row quantisation of rows [n, d] of fp32 values:
- *   amax = max_c |x_c|,  scale = fp32(amax / 448),  code_c = encode(fp32(x_c / scale)),
- * each division rounded once to fp32 (a double quotient of two fp32 operands rounds to the same
- * fp32 value as a correctly rounded fp32 division). A row with amax = 0 has scale 0 and all codes 0.
- * Row r decodes as scale_r * decode(code). */
+ *   amax = max_c |x_c|,  scale = fp32(amax / 448),  inv = min(fp32(448 / amax), FLT_MAX),
+ *   code_c = encode(fp32(x_c * inv)),
+ * every operation rounded once to fp32 (a double quotient or product of two fp32 operands rounds to
+ * the same fp32 value as the correctly rounded fp32 operation). A row with amax = 0 has scale 0 and
+ * all codes 0. Row r decodes as scale_r * decode(code); inv and 1 / scale differ by at most a few
+ * fp32 ulps, far below the E4M3 step. */
 void oracle_quantize_e4m3_rows(int64_t n, int32_t d, const float* x, uint8_t* codes, float* scales) {
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < n; ++r) {
@@ -264,8 +267,10 @@ void oracle_quantize_e4m3_rows(int64_t n, int32_t d, const float* x, uint8_t* co
       if (v > amax) amax = v;
     }
     const float s = (float)((double)amax / 448.0);
+    float inv = (float)(448.0 / (double)amax);
+    if (!(inv <= FLT_MAX)) inv = FLT_MAX;
     scales[r] = s;
     for (int32_t c = 0; c < d; ++c)
-      codes[r * d + c] = s == 0.0f ? 0 : oracle_encode_e4m3((float)((double)x[r * d + c] / (double)s));
+      codes[r * d + c] = amax == 0.0f ? 0 : oracle_encode_e4m3((float)((double)x[r * d + c] * (double)inv));
   }
 }

@@ -372,3 +372,44 @@ def test_decode_step_noalloc_refuses_before_touching_the_device():
     bad = L.chs_decode_step_noalloc(0, 64, 512, 128, 512, ctypes.c_float(0.04), 4, 128, FAKE, FAKE, FAKE, FAKE,
                                     FAKE, FAKE, FAKE, FAKE, 1000, None, FAKE, FAKE, FAKE, None)
     assert bad == SHAPE
+
+
+def quantize(dt=1, n=10, d=128, x=FAKE, c=FAKE, s=FAKE):
+    return chs.lib().chs_quantize_e4m3(dt, n, d, x, c, s, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=4), DTYPE), (dict(n=-1), SHAPE), (dict(d=4), SHAPE), (dict(d=12), SHAPE), (dict(d=4104), SHAPE),
+    (dict(x=None), NULL), (dict(c=None), NULL), (dict(s=None), NULL), (dict(n=0, x=None), OK),
+])
+def test_quantize_e4m3_validation(kw, code):
+    assert quantize(**kw) == code
+
+
+def compress_fp8(dt=1, batch=1, d=512, m=4, x=FAKE, z=FAKE, b=FAKE, cut=FAKE, cug=FAKE, maxg=10, c=FAKE, s=FAKE):
+    return chs.lib().chs_compress_fp8(dt, batch, d, m, x, z, b, cut, cug, maxg, c, s, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), DTYPE), (dict(batch=0), SHAPE), (dict(m=0), SHAPE), (dict(d=12), SHAPE), (dict(maxg=-1), SHAPE),
+    (dict(d=1024), UNSUP), (dict(d=384), UNSUP), (dict(dt=0, d=512), UNSUP), (dict(x=None), NULL),
+    (dict(c=None), NULL), (dict(s=None), NULL), (dict(maxg=0), OK), (dict(dt=0, d=256, maxg=0), OK),
+])
+def test_compress_fp8_validation(kw, code):
+    assert compress_fp8(**kw) == code
+
+
+def append_fp8(dt=1, batch=1, d=512, m=4, W=128, R=8, x=FAKE, z=FAKE, b=FAKE, n=FAKE, sc=FAKE, ss=FAKE, sl=FAKE,
+               xr=FAKE, gr=FAKE, page=FAKE, pages=1, cc=FAKE, cs=FAKE, start=FAKE, rows=100, cnt=FAKE):
+    return chs.lib().chs_append_fp8(dt, batch, d, m, W, R, x, z, b, n, sc, ss, sl, xr, gr, page, pages, cc, cs, start,
+                                    rows, cnt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), DTYPE), (dict(batch=0), SHAPE), (dict(d=12), SHAPE), (dict(m=0), SHAPE), (dict(W=3), SHAPE),
+    (dict(R=3), SHAPE), (dict(pages=0), SHAPE), (dict(rows=-1), SHAPE), (dict(d=1024), UNSUP), (dict(d=520), UNSUP),
+    (dict(x=None), NULL), (dict(sc=None), NULL), (dict(ss=None), NULL), (dict(xr=None), NULL), (dict(gr=None), NULL),
+    (dict(page=None), NULL), (dict(cc=None), NULL), (dict(cs=None), NULL), (dict(start=None), NULL),
+])
+def test_append_fp8_validation(kw, code):
+    assert append_fp8(**kw) == code

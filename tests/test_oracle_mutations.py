@@ -53,9 +53,12 @@ MUTATIONS = [
     ("E4M3 encode: no saturation above 448",
      "if (a > 448.0) best = 0x7E;",
      "if (a > 464.0) best = 0x7F;"),
-    ("E4M3 quantisation: row maximum mapped to 240 instead of 448",
+    ("E4M3 quantisation: stored scale for a row maximum of 240 instead of 448",
      "const float s = (float)((double)amax / 448.0);",
      "const float s = (float)((double)amax / 240.0);"),
+    ("E4M3 quantisation: row maximum mapped to 240 instead of 448",
+     "float inv = (float)(448.0 / (double)amax);",
+     "float inv = (float)(240.0 / (double)amax);"),
 ]
 
 
