@@ -14,7 +14,9 @@ import os
 import torch  # noqa: F401  (load torch's HIP runtime first; libchs binds to the same libamdhip64)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libchs.so")
+# CHS_LIB names another build of the library (the CPU sanitizer test loads a host-only build with
+# AddressSanitizer and UndefinedBehaviorSanitizer).
+LIB_PATH = os.environ.get("CHS_LIB") or os.path.join(HERE, "libchs.so")
 
 CHS_F32, CHS_BF16 = 0, 1
 _STATUS = {0: "CHS_OK", 1: "CHS_ERR_NULL", 2: "CHS_ERR_SHAPE", 3: "CHS_ERR_DTYPE",

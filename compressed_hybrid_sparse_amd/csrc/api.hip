@@ -25,6 +25,7 @@ extern "C" const char* chs_status_string(chs_status s) {
     case CHS_ERR_WORKSPACE: return "CHS_ERR_WORKSPACE: workspace too small";
     case CHS_ERR_UNSUPPORTED: return "CHS_ERR_UNSUPPORTED: no kernel for these arguments";
     case CHS_ERR_LAUNCH: return "CHS_ERR_LAUNCH: kernel launch failed";
+    default: break;
   }
   return "unknown chs_status";
 }

@@ -57,10 +57,22 @@ typedef enum {
   CHS_ERR_DTYPE = 3,        /* unknown dtype code */
   CHS_ERR_WORKSPACE = 4,    /* workspace smaller than the size query returned */
   CHS_ERR_UNSUPPORTED = 5,  /* valid arguments this build has no kernel for */
-  CHS_ERR_LAUNCH = 6        /* a kernel launch failed */
+  CHS_ERR_LAUNCH = 6,       /* a kernel launch failed */
+  /* Range markers, never returned: with them every int32 value is a valid chs_status in C++ (whose
+     enums otherwise only hold the values their enumerators span), so chs_status_string may be
+     given any code. */
+  CHS_STATUS_MIN_ = -0x7fffffff - 1,
+  CHS_STATUS_MAX_ = 0x7fffffff
 } chs_status;
 
-typedef enum { CHS_F32 = 0, CHS_BF16 = 1 } chs_dtype;
+/* The storage type of a call's tensors. Unknown codes are rejected with CHS_ERR_DTYPE; the range
+   markers make every int32 value a valid chs_dtype in C++, so that check is defined behaviour. */
+typedef enum {
+  CHS_F32 = 0,
+  CHS_BF16 = 1,
+  CHS_DTYPE_MIN_ = -0x7fffffff - 1,
+  CHS_DTYPE_MAX_ = 0x7fffffff
+} chs_dtype;
 
 /* Library version: major*10000 + minor*100 + patch. */
 int32_t chs_version(void);
