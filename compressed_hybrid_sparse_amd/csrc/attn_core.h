@@ -571,7 +571,10 @@ struct SplitPlan {
 };
 
 constexpr int kDenseThreads = 1024;   // dense split workgroup: 16 waves, four 16-head tiles
-constexpr int kDenseBlocks = 256;     // about one dense split workgroup per CU
+#ifndef CHS_DENSE_BLOCKS
+#define CHS_DENSE_BLOCKS 256
+#endif
+constexpr int kDenseBlocks = CHS_DENSE_BLOCKS;   // dense split workgroups aimed at per call
 
 // Dense bf16 (or FP8) attention over many heads (every compressed entry, no top-k) uses one
 // workgroup per 64 heads, so each gathered row is read from HBM once, and streams the
@@ -579,16 +582,14 @@ constexpr int kDenseBlocks = 256;     // about one dense split workgroup per CU
 // one chunk per split: it is latency bound, and more workgroups start sooner.
 inline bool dense_split(chs_dtype dt, int32_t k, int32_t H) { return dt == CHS_BF16 && k == 0 && H > 48; }
 
-// Partial loads per combine lane: enough for every split in one round when there are more
-// than 32 splits (up to 64), else 8.
-inline int combine_batch(int32_t n_splits) { return n_splits > 4 * 8 ? 16 : 8; }
-
 inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, int32_t k, int64_t max_comp) {
   const int64_t max_slots = (int64_t)window + (k > 0 ? k : max_comp);
-  const int gran = dt == CHS_BF16 ? kKeysPerChunk : kAttnThreads;
+  const bool dense = dense_split(dt, k, H);
+  // Dense splits walk 64-key chunks (the d = 512 kernel's chunk; the 16-wave kernel takes any
+  // multiple of 32).
+  const int gran = dense ? 64 : dt == CHS_BF16 ? kKeysPerChunk : kAttnThreads;
   // Aim at about 512 workgroups: bf16 runs one per 16-head tile, fp32 one per head; dense bf16
   // aims at kDenseBlocks workgroups of 64 heads.
-  const bool dense = dense_split(dt, k, H);
   const int64_t blocks_per_split = (int64_t)batch * (dense ? (H + 63) / 64 : dt == CHS_BF16 ? (H + 15) / 16 : H);
   const int64_t target = dense ? kDenseBlocks : 512;
   int64_t want = (target + blocks_per_split - 1) / blocks_per_split;

@@ -63,8 +63,278 @@ __global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(AttnArgs a) {
   attn_split<D, 4, NoHook, FP8, PAGED, 1>(a, blockIdx.y, blockIdx.x, 4 * blockIdx.z, threadIdx.x, sh, none);
 }
 
+// ---------------------------------------------------------------- dense bf16, d = 512
+// Every compressed entry attended by many heads is a skinny GEMM pair per sequence (64 heads x
+// 512 channels against thousands of keys). What bounds it on gfx950 is how often each K element
+// has to reach the MFMA units from LDS, and how much of the LDS and MFMA latency the waves of a CU
+// can hide, not the HBM bytes. This kernel runs one workgroup of 8 waves (two per SIMD) per 64
+// heads and split:
+//   - Key rows go from HBM straight into LDS (global_load_lds_dwordx4: one 1 KB row per
+//     instruction, the LDS row pitch padded by 16 bytes), double-buffered, so the next chunk of 64
+//     keys is in flight during the current one without holding registers.
+//   - Q K^T is computed as S^T = K Q^T (v_mfma_f32_16x16x32_bf16): K (16 keys x 32 channels) is
+//     the A operand read from LDS, Q^T the B operand kept in registers for the whole split. Wave w
+//     takes heads 16 (w & 3) .. +15 and keys 32 (w >> 2) .. +31 of the chunk; the two key halves
+//     of a head tile agree on the chunk's maximum through LDS.
+//   - The S^T accumulator holds, in each lane, 4 consecutive keys of one head: P goes to LDS as
+//     [head][key] with 8-byte stores and comes back as the A operand of P V with 16-byte loads.
+//   - P V (v_mfma_f32_32x32x16_bf16) is split by channels: wave w owns O for all 64 heads and
+//     channels 64 w .. +63, so V is read from LDS once per chunk; its B operand comes from the
+//     transposing LDS load (4 keys of one channel per read).
+// Per 64-key chunk (64 KB of keys) the LDS sees 64 KB of row writes, 256 KB of K reads, 64 KB of V
+// reads and about 80 KB of P and softmax exchange, with three barriers; each wave runs 32 MFMAs
+// of each kind. The partial results use the layout of the 16-head-tile kernels, so the same combine
+// merges them.
+constexpr int kD512Threads = 512;             // 8 waves
+constexpr int kD512Chunk = 64;                // keys per chunk
+constexpr int kD512Pitch = 512 + 8;           // bf16 elements per LDS key row
+constexpr int kD512PPitch = kD512Chunk + 8;   // bf16 elements per LDS row of P
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One row by DMA into LDS: lane l's 16 bytes at src (its own address) land at dst + 16 l, dst the
+// same in every lane (it goes into M0). Written as an instruction of its own rather than through the
+// compiler builtin: the builtin lets the compiler track the LDS write, and it then waits for every
+// DMA in flight before LDS reads it cannot tell apart from the destination (the P V operand loads),
+// which would empty the prefetch each chunk. The instruction writes no register; the caller waits
+// for it (vmcnt) before reading the rows, and never reads or writes the destination rows meanwhile
+// (so the compiler may move other LDS accesses across it).
+__device__ __forceinline__ void lds_row_dma(const uint16_t* src, uint16_t* dst) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst;
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds));
+}
+
+// A workgroup barrier for LDS data only: this wave's LDS operations are complete, then every wave
+// meets. __syncthreads() would also wait for the row DMAs still in flight (they write LDS), which
+// must stay in flight across the chunk.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// PAGED: entries through the page table (an entry whose page is outside the pool is skipped) and
+// the window through the sequence's window page, as in the other split kernels.
+template <bool PAGED>
+__global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a) {
+  constexpr int D = 512, KC = kD512Chunk, KP = kD512Pitch, PP = kD512PPitch;
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[KC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[KC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t pb[64 * PP];
+  __shared__ float cmax[2][64];                              // [key half][head]: the chunk's maxima
+  __shared__ __attribute__((aligned(16))) float alph[64];   // the chunk's rescale factor per head
+  __shared__ float lpart[64];                                // key half 1's running sums at the end
+  __shared__ uint8_t rowok[2][KC];                           // PAGED: which rows of each buffer hold a key
+
+  const int b = blockIdx.y, split = blockIdx.x, zg = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ht = wave & 3, kh = wave >> 2;        // Q K^T: head tile, key half
+  const int l32 = lane & 31, lh = lane >> 5;      // 32 x 32 operand layout (P V)
+  const int c16 = lane & 15, g4 = lane >> 4;      // 16 x 16 operand layout (Q K^T)
+  const int hq = 16 * ht + c16;                   // this lane's head in Q K^T and the softmax
+  const SlotMap sm(a, b);
+  const int32_t s_begin = split * a.kps;
+  const int32_t s_end = min(s_begin + a.kps, sm.nslots());
+  const int nchunks = s_end > s_begin ? (s_end - s_begin + KC - 1) / KC : 0;
+  const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
+  const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
+
+  // Row 8 w + i of the chunk at slot s0 into buffer bi, by DMA (lane l brings bytes 16 l .. + 15).
+  // The source is chosen without branches (the row addresses formed, one kept by mask), so a run of
+  // these stays one basic block. Slots that hold no key read the query buffer instead.
+  const uint64_t swa_a = (uint64_t)(uintptr_t)(swa + sm.swa_row0 * D);
+  const uint64_t comp_a = (uint64_t)(uintptr_t)(comp + (sm.comp0 - sm.nswa) * D);
+  const uint64_t safe_a = (uint64_t)(uintptr_t)a.q;
+  auto issue_row = [&](uint16_t* buf, int bi, int32_t s0, int i) {
+    const int r = 8 * wave + i;
+    const int32_t s = s0 + r;
+    const uint64_t in_w = 0ull - (uint64_t)(s < sm.nswa);
+    bool ok = s < s_end;
+    uint64_t comp_row = comp_a + (uint64_t)(int64_t)s * (D * 2);
+    if (PAGED) {
+      // The entry's page (read at a clamped position, so also for window rows and past the end).
+      const int64_t j = min(max((int64_t)s - sm.nswa, (int64_t)0), sm.G > 0 ? sm.G - 1 : (int64_t)0);
+      const int64_t pg = a.pg.pt[(int64_t)b * a.pg.pt_stride + (j >> a.pg.shift)];
+      const bool pok = pg >= 0 && pg < a.pg.pool_pages;
+      ok = ok && (s < sm.nswa || pok);
+      comp_row = (uint64_t)(uintptr_t)(comp + (((pok ? pg : 0) << a.pg.shift) | (j & ((1 << a.pg.shift) - 1))) * D);
+      if (lane == 0) rowok[bi][r] = ok ? 1 : 0;
+    }
+    const uint64_t past = 0ull - (uint64_t)(!ok);
+    const uint64_t row = PAGED ? (((swa_a + (uint64_t)(int64_t)s * (D * 2)) & in_w) | (comp_row & ~in_w))
+                               : ((swa_a & in_w) | (comp_a & ~in_w)) + (uint64_t)(int64_t)s * (D * 2);
+    const uint64_t src = (safe_a & past) | (row & ~past);
+    lds_row_dma(reinterpret_cast<const uint16_t*>(src) + 8 * lane, buf + r * KP);
+  };
+  if (nchunks > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_row(kt0, 0, s_begin, i);
+  }
+
+  // The 64 query rows come in once per workgroup, by DMA into kt1 (free until chunk 1 is requested,
+  // after the first barrier of the loop). Q^T (B operand): lane (head hq, channel group g4) holds
+  // channels 32 t + 8 g4 .. +7 of k-step t. Heads past H read head H - 1; their rows are never
+  // combined.
+  bf16x8 qf[D / 32];
+  {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int h = min(64 * zg + 8 * wave + i, a.H - 1);
+      lds_row_dma(static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + h) * D + 8 * lane, kt1 + (8 * wave + i) * KP);
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint16_t* qrow = kt1 + hq * KP + 8 * g4;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * t));
+  }
+  f32x16 o[2][2];                        // [head tile 32 hp][channel tile 64 w + 32 ct]
+#pragma unroll
+  for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) o[hp][ct] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;  // head hq; l_run over this lane's keys
+
+  auto chunk = [&](const uint16_t* cur, uint16_t* nxt, int cb, int c) {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's rows of chunk c landed
+    __syncthreads();                                      // every wave's rows; chunk c - 1 is done
+    const int32_t s0 = s_begin + c * KC;
+    if (c + 1 < nchunks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) issue_row(nxt, cb ^ 1, s0 + KC, i);
+    }
+    // S^T for keys 32 kh .. +31 (two 16-key tiles) and heads 16 ht .. +15. The K fragments of
+    // step t + 1 are read while step t's MFMAs run.
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const uint16_t* krow = cur + (32 * kh + c16) * KP + 8 * g4;
+    bf16x8 kf[2][2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) kf[0][n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * n * KP));
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      if (t + 1 < D / 32) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          kf[(t + 1) & 1][n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * n * KP + 32 * (t + 1)));
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n) sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t & 1][n], qf[t], sacc[n], 0, 0, 0);
+    }
+    // Register r of tile n of lane (c16, g4) holds key 32 kh + 16 n + 4 g4 + r of head hq.
+    float x[8];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = 32 * kh + 16 * n + 4 * g4 + r;
+        const bool valid = PAGED ? rowok[cb][kr] != 0 : s0 + kr < s_end;
+        x[4 * n + r] = valid ? sacc[n][r] * a.scale_log2 : -INFINITY;
+        cm = fmaxf(cm, x[4 * n + r]);
+      }
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    if (g4 == 0) cmax[kh][hq] = cm;
+    lds_barrier();
+    const float mn = fmaxf(m_run, fmaxf(cm, cmax[kh ^ 1][hq]));
+    const bool none = (mn == -INFINITY);
+    const float alpha = none ? 1.f : fast_exp2(m_run - mn);
+    float psum = 0.f;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      uint32_t w2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        // Rounded to bf16 here so the running sum matches what the MFMA multiplies.
+        const uint32_t lo = none ? 0u : f32_to_bf16(fast_exp2(x[4 * n + 2 * e] - mn));
+        const uint32_t hi = none ? 0u : f32_to_bf16(fast_exp2(x[4 * n + 2 * e + 1] - mn));
+        psum += bf16_to_f32((uint16_t)lo) + bf16_to_f32((uint16_t)hi);
+        w2[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint2*>(&pb[hq * PP + 32 * kh + 16 * n + 4 * g4]) = make_uint2(w2[0], w2[1]);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = mn;
+    if (kh == 0 && g4 == 0) alph[hq] = alpha;
+    lds_barrier();
+    // O (all 64 heads, channels 64 w .. +63) rescaled, then O += P V over the chunk's 64 keys.
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+      float al[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&alph[32 * hp + 8 * q4 + 4 * lh]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) al[4 * q4 + e] = v[e];
+      }
+      // Skipped when none of the tile's heads raised its maximum this chunk (alpha exactly 1), the
+      // usual case once the running maxima settle.
+      bool moved = false;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) moved |= al[r] != 1.f;
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[hp][ct][r] *= al[r];
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC / 16; ++kk) {
+      bf16x8 pa[2];
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp)
+        pa[hp] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pb[(32 * hp + l32) * PP + 16 * kk + 8 * lh]));
+      // Lane (channel l32, key group lh): keys 16 kk + 8 lh .. +7 of its channel, as two
+      // transposing reads of 4 keys each.
+      const uint16_t* vrow = cur + (16 * kk + 8 * (g4 >> 1) + (c16 >> 2)) * KP + 64 * wave + 16 * (g4 & 1) + 4 * (c16 & 3);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 32 * ct));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 4 * KP + 32 * ct));
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) o[hp][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hp], vb, o[hp][ct], 0, 0, 0);
+      }
+    }
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    chunk(kt0, kt1, 0, c);
+    if (c + 1 < nchunks) chunk(kt1, kt0, 1, c + 1);
+  }
+
+  // Partial result: running max (base 2) and sum per head, O in the 16-head-tile layout of the
+  // combine ([16-channel tile][lane 16 g + c][4]: head 4 g + r of the tile, channel 16 j + c).
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (kh == 1 && g4 == 0) lpart[hq] = l_run;
+  __syncthreads();
+  const int64_t pslot = (int64_t)b * a.n_splits + split;
+  if (kh == 0 && g4 == 0) {
+    const int h = 64 * zg + hq;
+    if (h < a.H) {
+      a.part_ml[(pslot * a.H + h) * 2] = m_run;
+      a.part_ml[(pslot * a.H + h) * 2 + 1] = l_run + lpart[hq];
+    }
+  }
+  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (pslot * a.head_tiles * 4 + 4 * zg) * (D / 16) * 64;
+#pragma unroll
+  for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int h0 = 32 * hp + 8 * q4 + 4 * lh;           // local head of register 4 q4
+        const int ch = 64 * wave + 32 * ct + l32;
+        const int64_t idx = (int64_t)(h0 >> 4) * (D / 16) * 64 + (ch >> 4) * 64 + 16 * ((h0 & 15) >> 2) + (ch & 15);
+        const f32x4 v = {o[hp][ct][4 * q4], o[hp][ct][4 * q4 + 1], o[hp][ct][4 * q4 + 2], o[hp][ct][4 * q4 + 3]};
+        __builtin_nontemporal_store(v, &po[idx]);
+      }
+}
+
 template <bool FP8, bool PAGED>
 void launch_dense(int d, dim3 grid, hipStream_t s, const AttnArgs& a) {
+  if (!FP8 && d == 512) {
+    hipLaunchKernelGGL(attn_dense512_kernel<PAGED>, grid, dim3(kD512Threads), 0, s, a);
+    return;
+  }
   switch (d) {
     case 64: hipLaunchKernelGGL((attn_dense_kernel<64, FP8, PAGED>), grid, dim3(kDenseThreads), 0, s, a); break;
     case 128: hipLaunchKernelGGL((attn_dense_kernel<128, FP8, PAGED>), grid, dim3(kDenseThreads), 0, s, a); break;
@@ -158,11 +428,26 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 // head in LDS.
 // Four lanes of a quad share one accumulator word, each summing a strided quarter of the
 // splits, so a launch has four times as many workgroups as words / 256.
-// bf16 partials: one block per (64 output words of a 16-head tile, head group, sequence).
-template <int KB>
+// bf16 partials: one block per (64 output words of a 16-head tile, head group, sequence). The LDS
+// holds the weights of at most MAXS splits: sized to the call, it stays small enough for many
+// resident workgroups when there are many sequences.
+template <int KB, int MAXS>
 __global__ __launch_bounds__(kThreads) void combine_mfma_kernel(AttnArgs a, float* out, float* lse) {
-  __shared__ CombineShared<kCombineSplits> sh;
-  combine_tile<kCombineSplits, KB>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
+  __shared__ CombineShared<MAXS> sh;
+  combine_tile<MAXS, KB>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
+}
+
+void launch_combine_mfma(const AttnArgs& a, int32_t batch, int32_t n_heads, int32_t d, float* out, float* lse,
+                         hipStream_t s) {
+  const int words_per_block = kThreads / kCombineLanes;
+  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
+                   (unsigned)batch);
+  if (a.n_splits <= 4 * 8)
+    hipLaunchKernelGGL((combine_mfma_kernel<8, 64>), cgrid, dim3(kThreads), 0, s, a, out, lse);
+  else if (a.n_splits <= 64)
+    hipLaunchKernelGGL((combine_mfma_kernel<16, 64>), cgrid, dim3(kThreads), 0, s, a, out, lse);
+  else
+    hipLaunchKernelGGL((combine_mfma_kernel<16, kCombineSplits>), cgrid, dim3(kThreads), 0, s, a, out, lse);
 }
 
 // fp32 partials ([H][D] per split): one workgroup per (sequence, head).
@@ -252,13 +537,7 @@ chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t 
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   if (dtype == CHS_BF16) {
-    const int words_per_block = kThreads / kCombineLanes;
-    const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
-                     (unsigned)batch);
-    if (combine_batch(p.n_splits) == 16)
-      hipLaunchKernelGGL(combine_mfma_kernel<16>, cgrid, dim3(kThreads), 0, s, a, out, lse);
-    else
-      hipLaunchKernelGGL(combine_mfma_kernel<8>, cgrid, dim3(kThreads), 0, s, a, out, lse);
+    launch_combine_mfma(a, batch, n_heads, d, out, lse, s);
   } else {
     hipLaunchKernelGGL(combine_rows_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
   }
@@ -348,13 +627,7 @@ chs_status launch_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t wi
     }
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-  const int words_per_block = kThreads / kCombineLanes;
-  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
-                   (unsigned)batch);
-  if (combine_batch(p.n_splits) == 16)
-    hipLaunchKernelGGL(combine_mfma_kernel<16>, cgrid, dim3(kThreads), 0, s, a, out, lse);
-  else
-    hipLaunchKernelGGL(combine_mfma_kernel<8>, cgrid, dim3(kThreads), 0, s, a, out, lse);
+  launch_combine_mfma(a, batch, n_heads, d, out, lse, s);
   return launch_status();
 }
 

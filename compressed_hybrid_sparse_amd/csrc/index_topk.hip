@@ -1565,9 +1565,11 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
   attn::attn_split_sm<D, 1, attn::NoHook, false, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
 }
 
+// MAXS: the most splits the launch merges (the LDS holds their weights).
+template <int MAXS>
 __global__ __launch_bounds__(attn::kAttnThreads) void step_combine_kernel(attn::AttnArgs a, float* out, float* lse) {
-  __shared__ attn::CombineShared<attn::kCombineSplits> sh;
-  attn::combine_tile<attn::kCombineSplits>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
+  __shared__ attn::CombineShared<MAXS> sh;
+  attn::combine_tile<MAXS>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
 }
 
 // Workspace of chs_decode_step: the selection's, then the attention's partials.
@@ -1632,7 +1634,10 @@ chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t w
   const int words_per_block = attn::kAttnThreads / attn::kCombineLanes;
   const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
                    (unsigned)batch);
-  hipLaunchKernelGGL(step_combine_kernel, cgrid, dim3(attn::kAttnThreads), 0, s, a, out, lse);
+  if (p.n_splits <= 64)
+    hipLaunchKernelGGL(step_combine_kernel<64>, cgrid, dim3(attn::kAttnThreads), 0, s, a, out, lse);
+  else
+    hipLaunchKernelGGL(step_combine_kernel<attn::kCombineSplits>, cgrid, dim3(attn::kAttnThreads), 0, s, a, out, lse);
   return launch_status();
 }
 

@@ -340,6 +340,9 @@ def test_attn_degenerate(rng):
 
 
 def test_attn_sparse_with_every_index_equals_dense(rng):
+    # Selecting every entry reduces the sparse call to the dense one. The two calls run different
+    # kernels whose splits and chunks differ, so P is rounded to bf16 against different running
+    # maxima: both meet the bf16-path tolerance against the oracle, and each other within it.
     print("case: attn sparse == dense", flush=True)
     d, H, G = 512, 64, 300
     q = torch.from_numpy(synth.normal(3, 4, 0, H * d, 0, 1, True).reshape(1, H, d)).to(dev()).bfloat16()
@@ -351,7 +354,13 @@ def test_attn_sparse_with_every_index_equals_dense(rng):
     sel[0, :G] = torch.arange(G, dtype=torch.int32, device=dev())
     o1, l1 = chs.decode_attn(q, swa, sl, comp, cu, sel)
     o2, l2 = chs.decode_attn(q, swa, sl, comp, cu, None)
-    assert torch.allclose(o1, o2, rtol=1e-5, atol=1e-6) and torch.allclose(l1, l2, rtol=1e-6, atol=1e-6)
+    keys = np.concatenate([swa[0].float().cpu().numpy(), comp.float().cpu().numpy()])
+    o_ref, l_ref = oracle.attend(q[0].float().cpu().numpy(), keys, d ** -0.5)
+    for o, l, what in ((o1, l1, "sparse"), (o2, l2, "dense")):
+        assert_bf16_path(o[0].cpu().numpy(), o_ref, what)
+        assert_lse(l[0].cpu().numpy(), l_ref, what)
+    assert_bf16_path(o1.cpu().numpy(), o2.cpu().numpy(), "sparse vs dense")
+    assert_lse(l1.cpu().numpy(), l2.cpu().numpy(), "sparse vs dense lse")
 
 
 def test_attn_is_deterministic():
