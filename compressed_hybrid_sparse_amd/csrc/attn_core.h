@@ -546,6 +546,87 @@ __device__ __forceinline__ void combine_tile(const AttnArgs& a, float* out, floa
   }
 }
 
+// ---- merge kernels, shared by chs_decode_attn and the fused decode step (one dispatch rule, so the
+// two give the same bits)
+constexpr int kFewSplits = 8;
+
+// At most kFewSplits splits: one thread per accumulator word of a 16-head tile (4 heads x 1
+// channel) requests its partials at once; the tile's (max, sum) pairs come through LDS in one
+// coalesced load (one per thread), so a thread is one round trip plus one barrier. Grid: (words /
+// 256, 16-head tiles, sequences).
+__global__ __launch_bounds__(kAttnThreads) void combine_few_kernel(AttnArgs a, float* out, float* lse) {
+  __shared__ float2 sml[kFewSplits][16];
+  const int b = blockIdx.z, hg = blockIdx.y;
+  const int D = a.D, ns = a.n_splits, H = a.H;
+  const int words = (D / 16) * 64;
+  const int wpos = min((int)(blockIdx.x * kAttnThreads + threadIdx.x), words - 1);
+  const int j = wpos >> 6, lane = wpos & 63, g = lane >> 4, c = lane & 15;
+  const int tile = hg >> 2, quarter = hg & 3;
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o);
+  const int64_t stride = (int64_t)a.head_tiles * 4 * words;    // one split, in f32x4
+  const int64_t base = (((int64_t)b * ns * a.head_tiles + tile) * 4 + quarter) * words + wpos;
+  f32x4 v[kFewSplits];
+#pragma unroll
+  for (int sp = 0; sp < kFewSplits; ++sp)
+    if (sp < ns) v[sp] = po[base + sp * stride];
+  if ((int)threadIdx.x < ns * 16) {
+    const int sp = threadIdx.x >> 4, h = min(16 * hg + (int)(threadIdx.x & 15), H - 1);
+    sml[sp][threadIdx.x & 15] = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * ns + sp) * H + h) * 2);
+  }
+  __syncthreads();
+  if ((int)(blockIdx.x * kAttnThreads + threadIdx.x) >= words) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kFewSplits; ++sp)
+      if (sp < ns) M = fmaxf(M, sml[sp][4 * g + r].x);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kFewSplits; ++sp)
+      if (sp < ns) {
+        const float2 ml = sml[sp][4 * g + r];
+        const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+        L += wgt * ml.y;
+        acc = fmaf(wgt, v[sp][r], acc);
+      }
+    const int h = 16 * hg + 4 * g + r;
+    if (h < H) {
+      out[((int64_t)b * H + h) * D + 16 * j + c] = (L > 0.f) ? acc / L : 0.f;
+      if (lse && j == 0 && c == 0) lse[(int64_t)b * H + h] = (L > 0.f) ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+}
+
+// More splits: a workgroup per (64 output words, 16-head tile, sequence), split weights once per
+// head in LDS sized for at most MAXS splits (small LDS keeps many workgroups resident).
+template <int KB, int MAXS>
+__global__ __launch_bounds__(kAttnThreads) void combine_tile_kernel(AttnArgs a, float* out, float* lse) {
+  __shared__ CombineShared<MAXS> sh;
+  combine_tile<MAXS, KB>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
+}
+
+// The merge of a bf16 (MFMA-layout) split kernel's partials into out and lse.
+inline void launch_combine(const AttnArgs& a, int32_t batch, int32_t n_heads, int32_t d, float* out, float* lse,
+                           hipStream_t s) {
+  const int words = d / 16 * 64;
+  if (a.n_splits <= kFewSplits) {
+    const dim3 grid((unsigned)((words + kAttnThreads - 1) / kAttnThreads), (unsigned)((n_heads + 15) / 16),
+                    (unsigned)batch);
+    hipLaunchKernelGGL(combine_few_kernel, grid, dim3(kAttnThreads), 0, s, a, out, lse);
+    return;
+  }
+  const int words_per_block = kAttnThreads / kCombineLanes;
+  const dim3 grid((unsigned)((words + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
+                  (unsigned)batch);
+  if (a.n_splits <= 4 * 8)
+    hipLaunchKernelGGL((combine_tile_kernel<8, 64>), grid, dim3(kAttnThreads), 0, s, a, out, lse);
+  else if (a.n_splits <= 64)
+    hipLaunchKernelGGL((combine_tile_kernel<16, 64>), grid, dim3(kAttnThreads), 0, s, a, out, lse);
+  else
+    hipLaunchKernelGGL((combine_tile_kernel<16, kCombineSplits>), grid, dim3(kAttnThreads), 0, s, a, out, lse);
+}
+
 // Host checks of chs_decode_attn's arguments (all but the workspace).
 inline chs_status check_args(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
                              float scale, const void* q, const void* swa_kv, const int32_t* swa_len,

@@ -422,34 +422,11 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- merge of the splits
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and lse = (M + log2 L) * ln 2, per head.
-// bf16 partials (MFMA layout): one workgroup per (group of 16 heads, 1024 accumulator words
-// of their tile, sequence); each thread reads one 16-byte accumulator (4 heads x 1 channel)
-// per split, so every load is a whole, coalesced vector. Split weights are computed once per
-// head in LDS.
-// Four lanes of a quad share one accumulator word, each summing a strided quarter of the
-// splits, so a launch has four times as many workgroups as words / 256.
-// bf16 partials: one block per (64 output words of a 16-head tile, head group, sequence). The LDS
-// holds the weights of at most MAXS splits: sized to the call, it stays small enough for many
-// resident workgroups when there are many sequences.
-template <int KB, int MAXS>
-__global__ __launch_bounds__(kThreads) void combine_mfma_kernel(AttnArgs a, float* out, float* lse) {
-  __shared__ CombineShared<MAXS> sh;
-  combine_tile<MAXS, KB>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
-}
-
-void launch_combine_mfma(const AttnArgs& a, int32_t batch, int32_t n_heads, int32_t d, float* out, float* lse,
-                         hipStream_t s) {
-  const int words_per_block = kThreads / kCombineLanes;
-  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
-                   (unsigned)batch);
-  if (a.n_splits <= 4 * 8)
-    hipLaunchKernelGGL((combine_mfma_kernel<8, 64>), cgrid, dim3(kThreads), 0, s, a, out, lse);
-  else if (a.n_splits <= 64)
-    hipLaunchKernelGGL((combine_mfma_kernel<16, 64>), cgrid, dim3(kThreads), 0, s, a, out, lse);
-  else
-    hipLaunchKernelGGL((combine_mfma_kernel<16, kCombineSplits>), cgrid, dim3(kThreads), 0, s, a, out, lse);
-}
-
+// bf16 partials (MFMA layout): launch_combine (attn_core.h). Up to 8 splits, one thread per
+// 16-byte accumulator (4 heads x 1 channel) merges them with every load in flight at once; more
+// splits go to a workgroup per (group of 16 heads, 64 accumulator words, sequence) that computes
+// the split weights once per head in LDS, four lanes of a quad summing a strided quarter of the
+// splits each. Every load is a whole, coalesced 16-byte vector.
 // fp32 partials ([H][D] per split): one workgroup per (sequence, head).
 __global__ __launch_bounds__(kThreads) void combine_rows_kernel(AttnArgs a, float* out, float* lse) {
   __shared__ float wts[kCombineSplits];
@@ -537,7 +514,7 @@ chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t 
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   if (dtype == CHS_BF16) {
-    launch_combine_mfma(a, batch, n_heads, d, out, lse, s);
+    launch_combine(a, batch, n_heads, d, out, lse, s);
   } else {
     hipLaunchKernelGGL(combine_rows_kernel, dim3(n_heads, batch), dim3(kThreads), 0, s, a, out, lse);
   }
@@ -627,7 +604,7 @@ chs_status launch_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t wi
     }
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-  launch_combine_mfma(a, batch, n_heads, d, out, lse, s);
+  launch_combine(a, batch, n_heads, d, out, lse, s);
   return launch_status();
 }
 

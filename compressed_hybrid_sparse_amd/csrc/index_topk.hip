@@ -1565,13 +1565,6 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
   attn::attn_split_sm<D, 1, attn::NoHook, false, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
 }
 
-// MAXS: the most splits the launch merges (the LDS holds their weights).
-template <int MAXS>
-__global__ __launch_bounds__(attn::kAttnThreads) void step_combine_kernel(attn::AttnArgs a, float* out, float* lse) {
-  __shared__ attn::CombineShared<MAXS> sh;
-  attn::combine_tile<MAXS>(a, out, lse, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
-}
-
 // Workspace of chs_decode_step: the selection's, then the attention's partials.
 size_t step_ws(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, int64_t max_comp,
                size_t* attn_off) {
@@ -1631,13 +1624,7 @@ chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t w
     default: hipLaunchKernelGGL(collect_attn_kernel<512>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
-  const int words_per_block = attn::kAttnThreads / attn::kCombineLanes;
-  const dim3 cgrid((unsigned)((d / 16 * 64 + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
-                   (unsigned)batch);
-  if (p.n_splits <= 64)
-    hipLaunchKernelGGL(step_combine_kernel<64>, cgrid, dim3(attn::kAttnThreads), 0, s, a, out, lse);
-  else
-    hipLaunchKernelGGL(step_combine_kernel<attn::kCombineSplits>, cgrid, dim3(attn::kAttnThreads), 0, s, a, out, lse);
+  attn::launch_combine(a, batch, n_heads, d, out, lse, s);
   return launch_status();
 }
 
