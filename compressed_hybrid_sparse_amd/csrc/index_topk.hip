@@ -1036,10 +1036,32 @@ __device__ uint32_t block_bound(const uint32_t (&u)[NU], uint32_t keff, uint32_t
 }
 
 // The exact top-k of sequence b into out[0 .. k) (global or LDS), run by a whole workgroup of
-// kCThreads threads (t = threadIdx.x)
-// on LDS `sh`. Every early return below is uniform over the workgroup.
-__device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, CollectShared& sh) {
+// kCThreads threads (t = threadIdx.x) on LDS `sh`, from the first statistics tile ft that
+// collect_prefetch requested. Every early return below is uniform over the workgroup.
+// The first tile of sequence b's group statistics (thread t: groups 8t .. 8t+7), requested before
+// anything else is known: its address depends on the sequence only, and the buffer bound covers
+// the sequence's whole statistics area. collect_seq clears the entries past the sequence's groups
+// once the candidate count has arrived.
+struct FirstTile {
+  uint32_t mv[kMaxPerThread], sv[kMaxPerThread];
+};
+__device__ __forceinline__ void collect_prefetch(const Args& a, int b, FirstTile& ft) {
   const uint32_t t = threadIdx.x;
+  const uint32_t cap = (uint32_t)maxima_cap(a.max_cand);
+  const __amdgpu_buffer_rsrc_t mrs = buffer_rsrc(maxima_ptr(a, b), cap * 4u);
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(second_ptr(a, b), cap * 4u);
+  const u32x4 m0 = buffer_u32x4(mrs, kMaxPerThread * t), m1 = buffer_u32x4(mrs, kMaxPerThread * t + 4);
+  const u32x4 q0 = buffer_u32x4(qrs, kMaxPerThread * t), q1 = buffer_u32x4(qrs, kMaxPerThread * t + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ft.mv[j] = m0[j]; ft.mv[4 + j] = m1[j]; ft.sv[j] = q0[j]; ft.sv[4 + j] = q1[j];
+  }
+}
+
+__device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, CollectShared& sh, FirstTile& ft) {
+  const uint32_t t = threadIdx.x;
+  uint32_t (&mv)[kMaxPerThread] = ft.mv;                 // thread t: groups t0 + 8t .. 8t+7
+  uint32_t (&sv)[kMaxPerThread] = ft.sv;
   int64_t c0;
   const uint32_t n = (uint32_t)cand_count(a, b, &c0);   // <= 2^22: 32-bit index math below
   const uint32_t keff = min((uint32_t)a.k, n);
@@ -1057,7 +1079,9 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, 
   const uint32_t nt = min(ng, (uint32_t)kTile);
   const __amdgpu_buffer_rsrc_t mrs = buffer_rsrc(maxima_ptr(a, b), ng * 4u);
   const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(second_ptr(a, b), ng * 4u);
-  uint32_t mv[kMaxPerThread], sv[kMaxPerThread];        // thread t: groups t0 + 8t .. 8t+7
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j)
+    if (kMaxPerThread * t + j >= ng) { mv[j] = 0u; sv[j] = 0u; }
   auto load_tile = [&](uint32_t t0) {
     const uint32_t e0 = t0 + kMaxPerThread * t;
     const u32x4 m0 = buffer_u32x4(mrs, e0), m1 = buffer_u32x4(mrs, e0 + 4);
@@ -1075,8 +1099,7 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, 
   // Bins: (u - umin) >> shift, 2048 of them, monotone. Groups past the sequence read as key 0,
   // below every score, and take no part. Every tile's maxima are ranked, so the bound and the
   // largest key (the superset's bin range) cover the whole sequence.
-  load_tile(0);
-  uint32_t rm[kMaxPerThread];                           // slot maxima over the tiles
+  uint32_t rm[kMaxPerThread];                           // slot maxima over the tiles (tile 0 is in mv)
 #pragma unroll
   for (int j = 0; j < kMaxPerThread; ++j) rm[j] = mv[j];
   for (uint32_t t0 = kTile; t0 < ng; t0 += 4u * kTile) {
@@ -1261,7 +1284,9 @@ __device__ __forceinline__ void collect_seq(const Args& a, int b, int32_t* out, 
 
 __global__ __launch_bounds__(kCThreads) void collect_kernel(Args a, int32_t* topk) {
   __shared__ CollectShared sh;
-  collect_seq(a, blockIdx.x, topk + (size_t)blockIdx.x * a.k, sh);
+  FirstTile ft;
+  collect_prefetch(a, blockIdx.x, ft);
+  collect_seq(a, blockIdx.x, topk + (size_t)blockIdx.x * a.k, sh, ft);
 }
 
 // The MFMA form of K1 when it applies (up to 16 heads, head_dim 64, 128 or 256): sets a->gs
@@ -1546,11 +1571,13 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
   __shared__ StepShared sh;
   __shared__ int32_t sel[kMaxK];
   const int b = blockIdx.y, split = blockIdx.x, z = blockIdx.z;
+  FirstTile ft;                                         // before the slot map's reads are waited on
+  collect_prefetch(ia, b, ft);
   const attn::SlotMap sm(aa, b);
   const int32_t s_begin = split * aa.kps, s_end = min(s_begin + aa.kps, sm.nslots());
   const bool selects = s_begin < s_end && s_end > sm.nswa;   // uniform over the workgroup
   if (selects) {
-    collect_seq(ia, b, sel, sh.c);
+    collect_seq(ia, b, sel, sh.c, ft);
     __syncthreads();                                    // sel is complete; the LDS is the attention's
   }
   if (threadIdx.x >= attn::kAttnThreads) {              // whole waves
