@@ -18,29 +18,6 @@
 namespace chs {
 namespace {
 
-// E4M3 code of an fp32 value, from its bits: the sign is kept (zeros included); below 2^-6 the
-// result is subnormal, round(|y| * 2^9) (exact scaling, then round half to even); above, the
-// exponent is rebiased and the 23-bit mantissa rounded to 3 bits, half to even, a carry moving
-// into the exponent; from 464 (the tie between 448 and the missing 480) up the magnitude is 448.
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E80000u) {                              // |y| >= 464
-    code = 0x7Eu;
-  } else if (a < 0x3C800000u) {                        // |y| < 2^-6
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    const uint32_t e = (a >> 23) - 120u;               // E4M3 biased exponent: e32 - 127 + 7
-    const uint32_t mant = a & 0x7FFFFFu;
-    const uint32_t q = mant >> 20, rem = mant & 0xFFFFFu;
-    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
-    code = min((e << 3) + q + up, 0x7Eu);              // [448, 464) rounds to 448
-  }
-  return sign | code;
-}
-
 // Maximum over each group of G adjacent lanes (G a power of two, at most 64, the same in every
 // lane); every lane of a group gets it.
 __device__ __forceinline__ float group_max(float v, int G) {
@@ -53,16 +30,18 @@ __device__ __forceinline__ float e4m3_scale(float amax) { return amax / 448.0f; 
 __device__ __forceinline__ float e4m3_inv(float amax) { return fminf(448.0f / amax, 3.40282347e38f); }
 
 // N (4 or 8) values of a row with row maximum amax into N codes, packed little-endian into N / 4
-// words.
+// words. E4M3() is gfx950's conversion (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even, the sign
+// kept on zeros, two values per instruction). The scaled values never exceed 448 by more than the
+// rounding of one product, so no input reaches the overflow point (464) where the instruction's
+// result and the saturating rule would part.
 template <int N>
 __device__ __forceinline__ void e4m3_pack(const float* v, float amax, uint32_t* w) {
   const float inv = e4m3_inv(amax);
 #pragma unroll
   for (int k = 0; k < N / 4; ++k) {
-    uint32_t r = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r |= (amax == 0.f ? 0u : e4m3_encode(v[4 * k + j] * inv)) << (8 * j);
-    w[k] = r;
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k] * inv, v[4 * k + 1] * inv, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 2] * inv, v[4 * k + 3] * inv, r, true);
+    w[k] = amax == 0.f ? 0u : (uint32_t)r;
   }
 }
 
