@@ -100,7 +100,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // for it (vmcnt) before reading the rows, and never reads or writes the destination rows meanwhile
 // (so the compiler may move other LDS accesses across it).
 __device__ __forceinline__ void lds_row_dma(const uint16_t* src, uint16_t* dst) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst);
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds));
 }
 
