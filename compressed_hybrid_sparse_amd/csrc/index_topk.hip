@@ -1562,11 +1562,14 @@ extern "C" chs_status chs_index_topk_fp8_paged(int32_t batch, int32_t n_heads, i
 namespace chs {
 namespace {
 
-template <int D>
+// TILES 16-head tiles per workgroup: 1 (four waves attend, the others store the top-k row and end)
+// or 4 (all sixteen waves attend 64 heads, so a split's selection runs once, not once per head
+// tile). The split plan and the arithmetic are the same either way, so the results are too.
+template <int D, int TILES>
 __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::AttnArgs aa, int32_t* topk) {
   union alignas(16) StepShared {
     CollectShared c;
-    attn::AttnShared<D, 1> at;
+    attn::AttnShared<D, TILES> at;
   };
   __shared__ StepShared sh;
   __shared__ int32_t sel[kMaxK];
@@ -1580,16 +1583,25 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
     collect_seq(ia, b, sel, sh.c, ft);
     __syncthreads();                                    // sel is complete; the LDS is the attention's
   }
-  if (threadIdx.x >= attn::kAttnThreads) {              // whole waves
-    // The attention's waves issue no global store before their gathers; the top-k row is
-    // stored by these ones.
+  if constexpr (TILES == 4) {
+    // All 16 waves attend the split for 64 heads; the top-k row is stored afterwards (a store before
+    // the gathers would hold the wait counter they use).
+    attn::NoHook none;
+    attn::attn_split_sm<D, 4, attn::NoHook, false, false>(aa, sm, b, split, 4 * z, threadIdx.x, sh.at, none, sel);
     if (selects && z == 0 && s_begin <= sm.nswa)
-      for (int i = threadIdx.x - attn::kAttnThreads; i < aa.k; i += kCThreads - attn::kAttnThreads)
-        topk[(int64_t)b * aa.k + i] = sel[i];
-    return;
+      for (int i = threadIdx.x; i < aa.k; i += kCThreads) topk[(int64_t)b * aa.k + i] = sel[i];
+  } else {
+    if (threadIdx.x >= attn::kAttnThreads) {            // whole waves
+      // The attention's waves issue no global store before their gathers; the top-k row is
+      // stored by these ones.
+      if (selects && z == 0 && s_begin <= sm.nswa)
+        for (int i = threadIdx.x - attn::kAttnThreads; i < aa.k; i += kCThreads - attn::kAttnThreads)
+          topk[(int64_t)b * aa.k + i] = sel[i];
+      return;
+    }
+    attn::NoHook none;
+    attn::attn_split_sm<D, 1, attn::NoHook, false, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
   }
-  attn::NoHook none;
-  attn::attn_split_sm<D, 1, attn::NoHook, false, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
 }
 
 // Workspace of chs_decode_step: the selection's, then the attention's partials.
@@ -1643,12 +1655,17 @@ chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t w
   attn::ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace) + attn_off);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (topk_first(CHS_BF16, batch, &ia, lpc, s) != CHS_OK) return CHS_ERR_LAUNCH;
-  const dim3 grid(p.n_splits, batch, (n_heads + 15) / 16);
+  // One workgroup per 16-head tile while the selecting workgroups fit the GPU at once (each selection
+  // then runs on its own CU and the copies cost nothing); past that, one per 64 heads, so each split
+  // selects once: at 64 sequences the step took 196 us against 227 us.
+  const bool wide = (int64_t)p.n_splits * batch * ((n_heads + 15) / 16) > 256;
+  const dim3 grid(p.n_splits, batch, wide ? (n_heads + 63) / 64 : (n_heads + 15) / 16);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kCThreads), 0, s, ia, a, topk); };
   switch (d) {
-    case 64: hipLaunchKernelGGL(collect_attn_kernel<64>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
-    case 128: hipLaunchKernelGGL(collect_attn_kernel<128>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
-    case 256: hipLaunchKernelGGL(collect_attn_kernel<256>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
-    default: hipLaunchKernelGGL(collect_attn_kernel<512>, grid, dim3(kCThreads), 0, s, ia, a, topk); break;
+    case 64: wide ? go(collect_attn_kernel<64, 4>) : go(collect_attn_kernel<64, 1>); break;
+    case 128: wide ? go(collect_attn_kernel<128, 4>) : go(collect_attn_kernel<128, 1>); break;
+    case 256: wide ? go(collect_attn_kernel<256, 4>) : go(collect_attn_kernel<256, 1>); break;
+    default: wide ? go(collect_attn_kernel<512, 4>) : go(collect_attn_kernel<512, 1>); break;
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   attn::launch_combine(a, batch, n_heads, d, out, lse, s);

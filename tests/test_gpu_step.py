@@ -59,6 +59,8 @@ CASES = [
     (6, [70000], 64, 512, 128, 2048, 4, 128, [128]),
     # more than one selection tile (8192 groups of 32 candidates) in one sequence
     (7, [300000, 2000], 16, 64, 64, 512, 4, 128, [64, 10]),
+    # more selecting workgroups than CUs: one workgroup per 64 heads (the second one partly past H)
+    (8, [1000 + 97 * i for i in range(24)], 72, 128, 32, 128, 4, 64, [32, 7, 0, 32] * 6),
 ]
 
 
