@@ -652,6 +652,10 @@ struct SplitPlan {
 };
 
 constexpr int kDenseThreads = 1024;   // dense split workgroup: 16 waves, four 16-head tiles
+#ifndef CHS_SPARSE_BLOCKS
+#define CHS_SPARSE_BLOCKS 1024
+#endif
+constexpr int kSparseBlocks = CHS_SPARSE_BLOCKS;  // selected (C4) and fp32 split workgroups aimed at per call
 #ifndef CHS_DENSE_BLOCKS
 #define CHS_DENSE_BLOCKS 256
 #endif
@@ -669,10 +673,12 @@ inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t win
   // Dense splits walk 64-key chunks (the d = 512 kernel's chunk; the 16-wave kernel takes any
   // multiple of 32).
   const int gran = dense ? 64 : dt == CHS_BF16 ? kKeysPerChunk : kAttnThreads;
-  // Aim at about 512 workgroups: bf16 runs one per 16-head tile, fp32 one per head; dense bf16
-  // aims at kDenseBlocks workgroups of 64 heads.
+  // Aim at about kSparseBlocks workgroups: bf16 runs one per 16-head tile, fp32 one per head (at 64
+  // sequences of a C4 layer, 1024 gave the fused step 186 us against 196 us at 512 and 207 us at
+  // 2048; at batch 1 the chunk count caps the splits first); dense bf16 aims at kDenseBlocks
+  // workgroups of 64 heads.
   const int64_t blocks_per_split = (int64_t)batch * (dense ? (H + 63) / 64 : dt == CHS_BF16 ? (H + 15) / 16 : H);
-  const int64_t target = dense ? kDenseBlocks : 512;
+  const int64_t target = dense ? kDenseBlocks : kSparseBlocks;
   int64_t want = (target + blocks_per_split - 1) / blocks_per_split;
   const int64_t most = (max_slots + gran - 1) / gran;
   if (want > most) want = most;
