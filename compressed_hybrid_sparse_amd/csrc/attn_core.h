@@ -649,6 +649,7 @@ inline chs_status check_args(chs_dtype dtype, int32_t batch, int32_t n_heads, in
 
 struct SplitPlan {
   int32_t n_splits, kps;
+  bool wide;
 };
 
 constexpr int kDenseThreads = 1024;   // dense split workgroup: 16 waves, four 16-head tiles
@@ -660,6 +661,8 @@ constexpr int kSparseBlocks = CHS_SPARSE_BLOCKS;  // selected (C4) and fp32 spli
 #define CHS_DENSE_BLOCKS 256
 #endif
 constexpr int kDenseBlocks = CHS_DENSE_BLOCKS;   // dense split workgroups aimed at per call
+constexpr int kWideSparseBlocks = 256;        // selected attention goes wide past this many 16-head workgroups
+constexpr int kWideMaxSelected = 2048;        // most selected entries one wide split stages in LDS
 
 // Dense bf16 (or FP8) attention over many heads (every compressed entry, no top-k) uses one
 // workgroup per 64 heads, so each gathered row is read from HBM once, and streams the
@@ -667,18 +670,9 @@ constexpr int kDenseBlocks = CHS_DENSE_BLOCKS;   // dense split workgroups aimed
 // one chunk per split: it is latency bound, and more workgroups start sooner.
 inline bool dense_split(chs_dtype dt, int32_t k, int32_t H) { return dt == CHS_BF16 && k == 0 && H > 48; }
 
-inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t window, int32_t k, int64_t max_comp) {
-  const int64_t max_slots = (int64_t)window + (k > 0 ? k : max_comp);
-  const bool dense = dense_split(dt, k, H);
-  // Dense splits walk 64-key chunks (the d = 512 kernel's chunk; the 16-wave kernel takes any
-  // multiple of 32).
-  const int gran = dense ? 64 : dt == CHS_BF16 ? kKeysPerChunk : kAttnThreads;
-  // Aim at about kSparseBlocks workgroups: bf16 runs one per 16-head tile, fp32 one per head (at 64
-  // sequences of a C4 layer, 1024 gave the fused step 186 us against 196 us at 512 and 207 us at
-  // 2048; at batch 1 the chunk count caps the splits first); dense bf16 aims at kDenseBlocks
-  // workgroups of 64 heads.
-  const int64_t blocks_per_split = (int64_t)batch * (dense ? (H + 63) / 64 : dt == CHS_BF16 ? (H + 15) / 16 : H);
-  const int64_t target = dense ? kDenseBlocks : kSparseBlocks;
+// kps (a multiple of gran) and the split count for about `target` workgroups of blocks_per_split
+// each, at most kCombineSplits splits.
+inline SplitPlan plan_for(int64_t max_slots, int64_t blocks_per_split, int64_t target, int gran) {
   int64_t want = (target + blocks_per_split - 1) / blocks_per_split;
   const int64_t most = (max_slots + gran - 1) / gran;
   if (want > most) want = most;
@@ -691,7 +685,39 @@ inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t win
   p.kps = (int32_t)kps;
   p.n_splits = (int32_t)((max_slots + kps - 1) / kps);
   if (p.n_splits < 1) p.n_splits = 1;
+  p.wide = false;
   return p;
+}
+
+// The split plan of one call, shared by the workspace queries and the launches (the same plan gives
+// the same bits). wide: the 64-head d = 512 kernel (attn_dense512_kernel) runs the splits:
+//   - dense bf16 with more than 48 heads at d = 512 always; its 64-key chunks set the granularity,
+//     and it aims at kDenseBlocks workgroups;
+//   - selected (C4) bf16 attention with more than 48 heads at d = 512 once its 16-head workgroups
+//     would outnumber the CUs (many sequences): each split's rows are then read once for 64 heads
+//     instead of once per 16-head tile.
+// Otherwise bf16 runs one workgroup per 16-head tile over 32-key chunks, aiming at kSparseBlocks (at
+// 64 sequences of a C4 layer 1024 measured better than 512 and 2048; at batch 1 the chunk count caps
+// the splits first), and fp32 one per head over 256-key chunks. FP8 calls take the bf16 plan.
+inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t d, int32_t window, int32_t k,
+                             int64_t max_comp) {
+  const int64_t max_slots = (int64_t)window + (k > 0 ? k : max_comp);
+  const int64_t tiles16 = (H + 15) / 16, tiles64 = (H + 63) / 64;
+  if (dense_split(dt, k, H)) {
+    SplitPlan p = plan_for(max_slots, (int64_t)batch * tiles64, kDenseBlocks, 64);
+    p.wide = d == 512;
+    return p;
+  }
+  if (dt != CHS_BF16) return plan_for(max_slots, (int64_t)batch * H, kSparseBlocks, kAttnThreads);
+  const SplitPlan narrow = plan_for(max_slots, (int64_t)batch * tiles16, kSparseBlocks, kKeysPerChunk);
+  if (d == 512 && H > 48 && (int64_t)narrow.n_splits * batch * tiles16 > kWideSparseBlocks) {
+    SplitPlan p = plan_for(max_slots, (int64_t)batch * tiles64, kDenseBlocks, 64);
+    if (p.kps <= kWideMaxSelected) {
+      p.wide = true;
+      return p;
+    }
+  }
+  return narrow;
 }
 
 inline size_t ws_bytes(chs_dtype dt, int32_t batch, int32_t H, int32_t D, const SplitPlan& p, float** po, float** pml,

@@ -111,7 +111,10 @@ __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkm
 
 // PAGED: entries through the page table (an entry whose page is outside the pool is skipped) and
 // the window through the sequence's window page, as in the other split kernels.
-template <bool PAGED>
+// TOPK: the split's slots past the window are the selected entries a.topk lists (C4 at many
+// sequences); the split's slice of the list is staged in LDS first, and an entry outside [0, G) is
+// skipped.
+template <bool PAGED, bool TOPK>
 __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a) {
   constexpr int D = 512, KC = kD512Chunk, KP = kD512Pitch, PP = kD512PPitch;
   __shared__ __attribute__((aligned(16))) uint16_t kt0[KC * KP];
@@ -120,7 +123,8 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   __shared__ float cmax[2][64];                              // [key half][head]: the chunk's maxima
   __shared__ __attribute__((aligned(16))) float alph[64];   // the chunk's rescale factor per head
   __shared__ float lpart[64];                                // key half 1's running sums at the end
-  __shared__ uint8_t rowok[2][KC];                           // PAGED: which rows of each buffer hold a key
+  __shared__ uint8_t rowok[2][KC];                           // PAGED, TOPK: which rows of each buffer hold a key
+  __shared__ int32_t selrow[TOPK ? kWideMaxSelected : 1];    // TOPK: the split's selected entries
 
   const int b = blockIdx.y, split = blockIdx.x, zg = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -142,24 +146,43 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   const uint64_t swa_a = (uint64_t)(uintptr_t)(swa + sm.swa_row0 * D);
   const uint64_t comp_a = (uint64_t)(uintptr_t)(comp + (sm.comp0 - sm.nswa) * D);
   const uint64_t safe_a = (uint64_t)(uintptr_t)a.q;
+  // TOPK: selected positions j0 .. j0 + nsel - 1 belong to this split.
+  const int32_t j0 = max(s_begin - sm.nswa, 0);
+  const int32_t nsel = TOPK ? max(s_end - sm.nswa - j0, 0) : 0;
+  if (TOPK) {
+    const int32_t* tk = a.topk + (int64_t)b * a.k;
+    for (int i = threadIdx.x; i < nsel; i += kD512Threads) selrow[i] = tk[j0 + i];
+    __syncthreads();
+  }
   auto issue_row = [&](uint16_t* buf, int bi, int32_t s0, int i) {
     const int r = 8 * wave + i;
     const int32_t s = s0 + r;
     const uint64_t in_w = 0ull - (uint64_t)(s < sm.nswa);
     bool ok = s < s_end;
     uint64_t comp_row = comp_a + (uint64_t)(int64_t)s * (D * 2);
-    if (PAGED) {
-      // The entry's page (read at a clamped position, so also for window rows and past the end).
-      const int64_t j = min(max((int64_t)s - sm.nswa, (int64_t)0), sm.G > 0 ? sm.G - 1 : (int64_t)0);
-      const int64_t pg = a.pg.pt[(int64_t)b * a.pg.pt_stride + (j >> a.pg.shift)];
-      const bool pok = pg >= 0 && pg < a.pg.pool_pages;
-      ok = ok && (s < sm.nswa || pok);
-      comp_row = (uint64_t)(uintptr_t)(comp + (((pok ? pg : 0) << a.pg.shift) | (j & ((1 << a.pg.shift) - 1))) * D);
+    if (PAGED || TOPK) {
+      // The entry (read at a clamped position, so also for window rows and past the end), then,
+      // paged, its page.
+      int64_t j = (int64_t)s - sm.nswa;
+      if (TOPK) {
+        const int32_t e = selrow[min(max((int32_t)j - j0, 0), max(nsel - 1, 0))];
+        ok = ok && (s < sm.nswa || (e >= 0 && e < sm.G));
+        j = e;
+      }
+      j = min(max(j, (int64_t)0), sm.G > 0 ? sm.G - 1 : (int64_t)0);
+      if (PAGED) {
+        const int64_t pg = a.pg.pt[(int64_t)b * a.pg.pt_stride + (j >> a.pg.shift)];
+        const bool pok = pg >= 0 && pg < a.pg.pool_pages;
+        ok = ok && (s < sm.nswa || pok);
+        comp_row = (uint64_t)(uintptr_t)(comp + (((pok ? pg : 0) << a.pg.shift) | (j & ((1 << a.pg.shift) - 1))) * D);
+      } else {
+        comp_row = (uint64_t)(uintptr_t)(comp + (sm.comp0 + j) * D);
+      }
       if (lane == 0) rowok[bi][r] = ok ? 1 : 0;
     }
     const uint64_t past = 0ull - (uint64_t)(!ok);
-    const uint64_t row = PAGED ? (((swa_a + (uint64_t)(int64_t)s * (D * 2)) & in_w) | (comp_row & ~in_w))
-                               : ((swa_a & in_w) | (comp_a & ~in_w)) + (uint64_t)(int64_t)s * (D * 2);
+    const uint64_t row = (PAGED || TOPK) ? (((swa_a + (uint64_t)(int64_t)s * (D * 2)) & in_w) | (comp_row & ~in_w))
+                                         : ((swa_a & in_w) | (comp_a & ~in_w)) + (uint64_t)(int64_t)s * (D * 2);
     const uint64_t src = (safe_a & past) | (row & ~past);
     lds_row_dma(reinterpret_cast<const uint16_t*>(src) + 8 * lane, buf + r * KP);
   };
@@ -225,7 +248,7 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kr = 32 * kh + 16 * n + 4 * g4 + r;
-        const bool valid = PAGED ? rowok[cb][kr] != 0 : s0 + kr < s_end;
+        const bool valid = (PAGED || TOPK) ? rowok[cb][kr] != 0 : s0 + kr < s_end;
         x[4 * n + r] = valid ? sacc[n][r] * a.scale_log2 : -INFINITY;
         cm = fmaxf(cm, x[4 * n + r]);
       }
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
 template <bool FP8, bool PAGED>
 void launch_dense(int d, dim3 grid, hipStream_t s, const AttnArgs& a) {
   if (!FP8 && d == 512) {
-    hipLaunchKernelGGL(attn_dense512_kernel<PAGED>, grid, dim3(kD512Threads), 0, s, a);
+    hipLaunchKernelGGL((attn_dense512_kernel<PAGED, false>), grid, dim3(kD512Threads), 0, s, a);
     return;
   }
   switch (d) {
@@ -471,7 +494,7 @@ extern "C" size_t chs_decode_attn_workspace_size(chs_dtype dtype, int32_t batch,
                                                  int32_t window, int32_t k, int64_t max_comp) {
   using namespace chs;
   if (batch < 1 || n_heads < 1 || d < 1 || window < 0 || k < 0 || max_comp < 0) return 0;
-  SplitPlan p = plan_splits(dtype, batch, n_heads, window, k, max_comp);
+  SplitPlan p = plan_splits(dtype, batch, n_heads, d, window, k, max_comp);
   return ws_bytes(dtype, batch, n_heads, d, p, nullptr, nullptr, nullptr);
 }
 
@@ -484,7 +507,7 @@ chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t 
                        const int64_t* cu_comp, const attn::Paging& pg, const int32_t* topk, int64_t max_comp,
                        float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int kk = topk ? k : 0;
-  SplitPlan p = plan_splits(dtype, batch, n_heads, window, kk, max_comp);
+  SplitPlan p = plan_splits(dtype, batch, n_heads, d, window, kk, max_comp);
   AttnArgs a;
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = nullptr; a.comp_scale = nullptr;
@@ -496,7 +519,14 @@ chs_status launch_attn(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t 
   const size_t need = ws_bytes(dtype, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
   const bool paged = pg.pt != nullptr;
-  if (dense_split(dtype, kk, n_heads)) {
+  if (p.wide && kk > 0) {
+    // Selected entries at many sequences: the 64-head kernel, its slots' entries from the top-k list.
+    const dim3 grid(p.n_splits, batch, (n_heads + 63) / 64);
+    if (paged)
+      hipLaunchKernelGGL((attn_dense512_kernel<true, true>), grid, dim3(kD512Threads), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_dense512_kernel<false, true>), grid, dim3(kD512Threads), 0, s, a);
+  } else if (dense_split(dtype, kk, n_heads)) {
     const dim3 grid(p.n_splits, batch, (n_heads + 63) / 64);
     paged ? launch_dense<false, true>(d, grid, s, a) : launch_dense<false, false>(d, grid, s, a);
   } else if (dtype == CHS_BF16) {
@@ -578,7 +608,7 @@ chs_status launch_attn_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t wi
                            const attn::Paging& pg, const int32_t* topk, int64_t max_comp, float* out, float* lse,
                            void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int kk = topk ? k : 0;
-  SplitPlan p = plan_splits(CHS_BF16, batch, n_heads, window, kk, max_comp);
+  SplitPlan p = plan_splits(CHS_BF16, batch, n_heads, d, window, kk, max_comp);
   AttnArgs a;
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = swa_scale; a.comp_scale = comp_scale;

@@ -1608,7 +1608,7 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
 size_t step_ws(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, int64_t max_comp,
                size_t* attn_off) {
   const size_t sel = align_up(ws_layout(batch, max_comp, nullptr, nullptr), 256);
-  const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, window, k, max_comp);
+  const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, d, window, k, max_comp);
   if (attn_off) *attn_off = sel;
   return sel + attn::ws_bytes(CHS_BF16, batch, n_heads, d, p, nullptr, nullptr, nullptr);
 }
@@ -1643,7 +1643,7 @@ chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t w
   st = topk_setup(CHS_BF16, batch, idx_heads, idx_dim, k, q_idx, w, k_idx, cu_comp, max_comp, scores, topk,
                   workspace, attn_off, &ia, &lpc);
   if (st != CHS_OK) return st;
-  const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, window, k, max_comp);
+  const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, d, window, k, max_comp);
   attn::AttnArgs a;
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
   a.swa_scale = nullptr; a.comp_scale = nullptr;
@@ -1655,6 +1655,16 @@ chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t w
   attn::ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace) + attn_off);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (topk_first(CHS_BF16, batch, &ia, lpc, s) != CHS_OK) return CHS_ERR_LAUNCH;
+  if (p.wide) {
+    // Many sequences at d = 512: the attention's splits run in the 64-head kernel, which stages each
+    // split's entries from the top-k list, so the selection runs once per sequence into that list
+    // and the attention is chs_decode_attn's own launch (the results are the two calls', trivially).
+    hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, ia, topk);
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+    return chs_decode_attn(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv, cu_comp, topk,
+                           max_comp, out, lse, static_cast<char*>(workspace) + attn_off, workspace_bytes - attn_off,
+                           stream);
+  }
   // One workgroup per 16-head tile while the selecting workgroups fit the GPU at once (each selection
   // then runs on its own CU and the copies cost nothing); past that, one per 64 heads, so each split
   // selects once: at 64 sequences the step took 196 us against 227 us.

@@ -305,6 +305,15 @@ def test_attn_c4_bf16_heads(rng, H):
     _attn_case(rng, "bf16", 2, H, 512, 128, [128, 77], [3000, 40], 512, False, n_bad=9)
 
 
+def test_attn_c4_bf16_many_sequences(rng):
+    # Enough sequences that the 16-head workgroups would outnumber the CUs: the selected entries go
+    # through the 64-head d = 512 kernel (its second head group partly past H), with invalid and
+    # duplicate indices, ragged and empty windows, and an empty sequence.
+    print("case: attn c4 bf16 many sequences", flush=True)
+    G = [500 + 41 * i for i in range(23)] + [0]
+    _attn_case(rng, "bf16", 24, 72, 512, 128, [128, 77, 0, 5] * 6, G, 64, False, n_bad=9)
+
+
 @pytest.mark.parametrize("d", [64, 128, 256, 512])
 def test_attn_dense_bf16_dims(rng, d):
     print(f"case: attn dense bf16 d={d}", flush=True)

@@ -45,6 +45,8 @@ def _paged_pool(rng, rows_per_seq, P, d, dt, extra_pages=3):
 
 @pytest.mark.parametrize("dt,H,d,W,P,G_list,k,dense", [
     (torch.bfloat16, 64, 512, 128, 64, [3000, 0, 700], 512, False),
+    # many sequences: the selected entries go through the 64-head d = 512 kernel
+    (torch.bfloat16, 72, 512, 128, 64, [400 + 37 * i for i in range(24)], 64, False),
     (torch.bfloat16, 64, 512, 128, 128, [2048, 1000], 0, True),
     (torch.bfloat16, 16, 128, 32, 1, [300, 45], 40, False),        # page size 1: a gather per entry
     (torch.bfloat16, 100, 256, 128, 256, [5000], 200, False),
