@@ -550,14 +550,18 @@ __device__ __forceinline__ void combine_tile(const AttnArgs& a, float* out, floa
 // two give the same bits)
 constexpr int kFewSplits = 8;
 
-// At most kFewSplits splits: one thread per accumulator word of a 16-head tile (4 heads x 1
-// channel) requests its partials at once; the tile's (max, sum) pairs come through LDS in one
-// coalesced load (one per thread), so a thread is one round trip plus one barrier. Grid: (words /
-// 256, 16-head tiles, sequences).
+// Exactly NS <= kFewSplits splits: one thread per accumulator word of a 16-head tile (4 heads x 1
+// channel) requests its NS partials at once (a compile-time count, so no load sits behind a branch
+// and waits for the one before); the tile's (max, sum) pairs come through LDS in one coalesced load
+// (one per thread), so a thread is one round trip plus one barrier. Grid: (words / 256, 16-head
+// tiles, sequences).
+template <int NS>
 __global__ __launch_bounds__(kAttnThreads) void combine_few_kernel(AttnArgs a, float* out, float* lse) {
-  __shared__ float2 sml[kFewSplits][16];
+  static_assert(NS >= 1 && NS <= kFewSplits, "splits");
+  __shared__ float2 sml[NS][16];
   const int b = blockIdx.z, hg = blockIdx.y;
-  const int D = a.D, ns = a.n_splits, H = a.H;
+  const int D = a.D, H = a.H;
+  constexpr int ns = NS;
   const int words = (D / 16) * 64;
   const int wpos = min((int)(blockIdx.x * kAttnThreads + threadIdx.x), words - 1);
   const int j = wpos >> 6, lane = wpos & 63, g = lane >> 4, c = lane & 15;
@@ -565,10 +569,9 @@ __global__ __launch_bounds__(kAttnThreads) void combine_few_kernel(AttnArgs a, f
   const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o);
   const int64_t stride = (int64_t)a.head_tiles * 4 * words;    // one split, in f32x4
   const int64_t base = (((int64_t)b * ns * a.head_tiles + tile) * 4 + quarter) * words + wpos;
-  f32x4 v[kFewSplits];
+  f32x4 v[NS];
 #pragma unroll
-  for (int sp = 0; sp < kFewSplits; ++sp)
-    if (sp < ns) v[sp] = po[base + sp * stride];
+  for (int sp = 0; sp < NS; ++sp) v[sp] = po[base + sp * stride];
   if ((int)threadIdx.x < ns * 16) {
     const int sp = threadIdx.x >> 4, h = min(16 * hg + (int)(threadIdx.x & 15), H - 1);
     sml[sp][threadIdx.x & 15] = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * ns + sp) * H + h) * 2);
@@ -579,17 +582,15 @@ __global__ __launch_bounds__(kAttnThreads) void combine_few_kernel(AttnArgs a, f
   for (int r = 0; r < 4; ++r) {
     float M = -INFINITY;
 #pragma unroll
-    for (int sp = 0; sp < kFewSplits; ++sp)
-      if (sp < ns) M = fmaxf(M, sml[sp][4 * g + r].x);
+    for (int sp = 0; sp < NS; ++sp) M = fmaxf(M, sml[sp][4 * g + r].x);
     float L = 0.f, acc = 0.f;
 #pragma unroll
-    for (int sp = 0; sp < kFewSplits; ++sp)
-      if (sp < ns) {
-        const float2 ml = sml[sp][4 * g + r];
-        const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
-        L += wgt * ml.y;
-        acc = fmaf(wgt, v[sp][r], acc);
-      }
+    for (int sp = 0; sp < NS; ++sp) {
+      const float2 ml = sml[sp][4 * g + r];
+      const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      L += wgt * ml.y;
+      acc = fmaf(wgt, v[sp][r], acc);
+    }
     const int h = 16 * hg + 4 * g + r;
     if (h < H) {
       out[((int64_t)b * H + h) * D + 16 * j + c] = (L > 0.f) ? acc / L : 0.f;
@@ -613,7 +614,17 @@ inline void launch_combine(const AttnArgs& a, int32_t batch, int32_t n_heads, in
   if (a.n_splits <= kFewSplits) {
     const dim3 grid((unsigned)((words + kAttnThreads - 1) / kAttnThreads), (unsigned)((n_heads + 15) / 16),
                     (unsigned)batch);
-    hipLaunchKernelGGL(combine_few_kernel, grid, dim3(kAttnThreads), 0, s, a, out, lse);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kAttnThreads), 0, s, a, out, lse); };
+    switch (a.n_splits) {
+      case 1: go(combine_few_kernel<1>); break;
+      case 2: go(combine_few_kernel<2>); break;
+      case 3: go(combine_few_kernel<3>); break;
+      case 4: go(combine_few_kernel<4>); break;
+      case 5: go(combine_few_kernel<5>); break;
+      case 6: go(combine_few_kernel<6>); break;
+      case 7: go(combine_few_kernel<7>); break;
+      default: go(combine_few_kernel<8>); break;
+    }
     return;
   }
   const int words_per_block = kAttnThreads / kCombineLanes;
