@@ -673,6 +673,9 @@ constexpr int kSparseBlocks = CHS_SPARSE_BLOCKS;  // selected (C4) and fp32 spli
 #endif
 constexpr int kDenseBlocks = CHS_DENSE_BLOCKS;   // dense split workgroups aimed at per call
 constexpr int kWideSparseBlocks = 256;        // selected attention goes wide past this many 16-head workgroups
+// Selected (C4) splits of the 64-head kernel aimed at per call: at 64 sequences of 200K tokens (640
+// slots each) 192 gives 3 splits of 256 slots: step 186.9 us, against 188.6 (256), 188.2 (128) and 196 (384).
+constexpr int kWideTopkBlocks = 192;
 constexpr int kWideMaxSelected = 2048;        // most selected entries one wide split stages in LDS
 
 // Dense bf16 (or FP8) attention over many heads (every compressed entry, no top-k) uses one
@@ -706,7 +709,7 @@ inline SplitPlan plan_for(int64_t max_slots, int64_t blocks_per_split, int64_t t
 //     and it aims at kDenseBlocks workgroups;
 //   - selected (C4) bf16 attention with more than 48 heads at d = 512 once its 16-head workgroups
 //     would outnumber the CUs (many sequences): each split's rows are then read once for 64 heads
-//     instead of once per 16-head tile.
+//     instead of once per 16-head tile; it aims at kWideTopkBlocks workgroups.
 // Otherwise bf16 runs one workgroup per 16-head tile over 32-key chunks, aiming at kSparseBlocks (at
 // 64 sequences of a C4 layer 1024 measured better than 512 and 2048; at batch 1 the chunk count caps
 // the splits first), and fp32 one per head over 256-key chunks. FP8 calls take the bf16 plan.
@@ -722,7 +725,7 @@ inline SplitPlan plan_splits(chs_dtype dt, int32_t batch, int32_t H, int32_t d, 
   if (dt != CHS_BF16) return plan_for(max_slots, (int64_t)batch * H, kSparseBlocks, kAttnThreads);
   const SplitPlan narrow = plan_for(max_slots, (int64_t)batch * tiles16, kSparseBlocks, kKeysPerChunk);
   if (d == 512 && H > 48 && (int64_t)narrow.n_splits * batch * tiles16 > kWideSparseBlocks) {
-    SplitPlan p = plan_for(max_slots, (int64_t)batch * tiles64, kDenseBlocks, 64);
+    SplitPlan p = plan_for(max_slots, (int64_t)batch * tiles64, kWideTopkBlocks, 64);
     if (p.kps <= kWideMaxSelected) {
       p.wide = true;
       return p;

@@ -61,7 +61,8 @@ def _rows(rng, n, d, dtype):
 
 @pytest.mark.parametrize("dtype,n,d", [("bf16", 257, 128), ("bf16", 64, 512), ("bf16", 33, 8), ("bf16", 17, 136),
                                        ("bf16", 9, 4096), ("f32", 100, 64), ("f32", 21, 520), ("f32", 5, 1024),
-                                       ("bf16", 4000, 64)])
+                                       ("bf16", 4000, 64), ("bf16", 70, 256), ("f32", 77, 256), ("bf16", 45, 512),
+                                       ("f32", 3, 128)])
 def test_quantize_bit_exact(rng, dtype, n, d):
     print(f"case: quantize_e4m3 {dtype} n={n} d={d}", flush=True)
     x = _rows(rng, n, d, dtype)
