@@ -642,7 +642,7 @@ def run_components(torch, chs, synth, W, dev, comps, per_call_us, graph_us, wl, 
 
 def other_workloads(torch, chs, synth, W, dev, comps, per_call_us, graph_us):
     bf = torch.bfloat16
-    # ---- workload 2: 131,072 tokens, batch 1, C4
+    # ---- c4_128k_bf16: 131,072 tokens, batch 1, C4
     wl2 = W.workload(2)
     L2 = wl2.layers[0]
     log(f"components: {wl2.name}")
@@ -688,7 +688,7 @@ def other_workloads(torch, chs, synth, W, dev, comps, per_call_us, graph_us):
     del sets2, inp, comp2
     torch.cuda.empty_cache()
 
-    # ---- workload 3: 4 x 1,048,576 tokens, C128 (m = 128): the prefill compression and the dense step
+    # ---- c128_1m_bs4_bf16: 4 x 1,048,576 tokens, C128 (m = 128): the prefill compression and the dense step
     wl3 = W.workload(3)
     L3 = wl3.layers[0]
     log(f"components: {wl3.name}")
@@ -725,7 +725,7 @@ def other_workloads(torch, chs, synth, W, dev, comps, per_call_us, graph_us):
     del pools, qs, inp, comp3
     torch.cuda.empty_cache()
 
-    # ---- workload 5: 64 sequences of 200,000 +-5% tokens; a C4 layer (m = 4) and a C128 layer (m = 128)
+    # ---- 64 sequences of 200,000 +-5% tokens; a C4 layer (m = 4) and a C128 layer (m = 128)
     wl5 = W.workload(5)
     for L5 in wl5.layers:
         log(f"components: {wl5.name} {L5.kind}")

@@ -150,7 +150,7 @@ def _run_topk(score_rows, k, reps=2):
     return outs[0]
 
 
-def test_topk_cfg4_rows_exact():
+def test_topk_262144_score_rows_exact():
     from synth import workloads as W
     wl = W.workload(4)
     for variant in ("normal", "dup10", "tie64"):

@@ -176,7 +176,7 @@ def test_workload4_standalone_topk():
     cu = torch.tensor([0, n], dtype=torch.int64, device=dev())
     ws = chs.index_topk_workspace(1, n, 512, dev())
     for v, s in rows.items():
-        print(f"case: workload 4 standalone top-k ({v})", flush=True)
+        print(f"case: c4_1m_bf16 standalone top-k ({v})", flush=True)
         got = chs.topk_from_scores(torch.from_numpy(s).to(dev()), cu, 512, n, ws).cpu().numpy()[0]
         assert np.array_equal(got, oracle.topk(s, 512)), v
     # The 64-row batch the benchmark times.
