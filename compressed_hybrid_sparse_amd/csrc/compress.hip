@@ -42,7 +42,7 @@ __device__ __forceinline__ void store_entry(const float* o, int cpr, int64_t row
     uint32_t w[N / 4];
     e4m3_pack<N>(o, am, w);
     if (store) {
-      e4m3_store<N>(codes + row * d + col, w);
+      e4m3_store<N, true>(codes + row * d + col, w);
       if (col == 0) scales[row] = sc;
     }
   } else if (store) {

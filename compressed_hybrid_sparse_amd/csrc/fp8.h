@@ -45,11 +45,20 @@ __device__ __forceinline__ void e4m3_pack(const float* v, float amax, uint32_t* 
   }
 }
 
-// Stores the N codes of e4m3_pack (N / 4 words) at p, which is N-byte aligned.
-template <int N>
+// Stores the N codes of e4m3_pack (N / 4 words) at p, which is N-byte aligned. NT: non-temporal,
+// for a pass that streams its inputs (the compressor: 430 -> 408 us at 1M tokens; the row
+// quantiser measured 26.4 us plain against 26.9 us non-temporal, so it stores plainly).
+template <int N, bool NT = false>
 __device__ __forceinline__ void e4m3_store(uint8_t* p, const uint32_t* w) {
-  if (N == 8) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
-  else *reinterpret_cast<uint32_t*>(p) = w[0];
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if (N == 8) {
+    const u32x2 v{w[0], w[1]};
+    if (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+    else *reinterpret_cast<u32x2*>(p) = v;
+  } else {
+    if (NT) __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
+    else *reinterpret_cast<uint32_t*>(p) = w[0];
+  }
 }
 
 }  // namespace
