@@ -44,7 +44,8 @@ def _grid():
 
 def _rows(rng, n, d, dtype):
     x = rng.standard_normal((n, d)) * np.exp2(rng.uniform(-20, 20, (n, 1)))
-    x[1] = 0.0                                                  # a zero row: scale 0, codes 0
+    if n > 1:
+        x[1] = 0.0                                              # a zero row: scale 0, codes 0
     if n > 3:
         # Ties: a row whose maximum is 448 * 2^k has the exact scale 2^k, so values placed on E4M3
         # midpoints (and in the subnormal range) stay there after the division.
@@ -62,7 +63,7 @@ def _rows(rng, n, d, dtype):
 @pytest.mark.parametrize("dtype,n,d", [("bf16", 257, 128), ("bf16", 64, 512), ("bf16", 33, 8), ("bf16", 17, 136),
                                        ("bf16", 9, 4096), ("f32", 100, 64), ("f32", 21, 520), ("f32", 5, 1024),
                                        ("bf16", 4000, 64), ("bf16", 70, 256), ("f32", 77, 256), ("bf16", 45, 512),
-                                       ("f32", 3, 128)])
+                                       ("f32", 3, 128), ("bf16", 1, 64), ("f32", 1, 512), ("bf16", 256, 64)])
 def test_quantize_bit_exact(rng, dtype, n, d):
     print(f"case: quantize_e4m3 {dtype} n={n} d={d}", flush=True)
     x = _rows(rng, n, d, dtype)
