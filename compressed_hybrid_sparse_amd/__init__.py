@@ -27,7 +27,7 @@ EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compr
            "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
            "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged",
            "chs_decode_step_workspace_size", "chs_decode_step", "chs_index_scores", "chs_decode_step_noalloc",
-           "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8")
+           "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8", "chs_decode_step_fp8")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -92,6 +92,8 @@ def lib():
                                       _i64, _p, _p, _p, _p, _p, _sz, _p]
         L.chs_decode_step_noalloc.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                                               _p, _i64, _p, _p, _p, _p, _p]
+        L.chs_decode_step_fp8.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
+                                          _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _sz, _p]
         L.chs_quantize_e4m3.argtypes = [ctypes.c_int, _i64, _i32, _p, _p, _p, _p]
         L.chs_compress_fp8.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_append_fp8.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -101,6 +103,7 @@ def lib():
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_index_scores", "chs_decode_step_noalloc",
+                   "chs_decode_step_fp8",
                    "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8",
                    "chs_decode_step", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
@@ -565,6 +568,63 @@ def decode_step(q_idx, w, k_idx, q, swa_kv, swa_len, comp_kv, cu_comp, k: int, s
                                  _ptr(k_idx), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(cu_comp),
                                  int(max_comp), _ptr(scores), _ptr(topk), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel(), _stream()), "chs_decode_step")
+    return topk, out, lse, scores
+
+
+def decode_step_fp8(q_idx, w, k_codes, k_scale, q, swa_codes, swa_scale, swa_len, comp_codes, comp_scale, cu_comp,
+                    k: int, scale=None, max_comp=None, scores=None, workspace=None, topk=None, out=None, lse=None):
+    """The C4 decode step over FP8 storage in one call (chs_decode_step_fp8): index_topk_fp8 then
+    decode_attn_fp8, with bit-identical results. q_idx: [B, Hi, dim] bf16; w: [B, Hi] fp32;
+    k_codes: [G, dim] uint8 (or float8_e4m3fn) with k_scale [G] fp32; q: [B, H, d] bf16;
+    swa_codes: [B, W, d] with swa_scale [B, W]; swa_len: [B] int32; comp_codes: [G, d] with
+    comp_scale [G]; cu_comp: [B+1] int64. Returns (topk, out, lse, scores or None)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 2)
+    k_codes = k_codes.view(torch.uint8) if k_codes.dtype != torch.uint8 else k_codes
+    swa_codes = swa_codes.view(torch.uint8) if swa_codes.dtype != torch.uint8 else swa_codes
+    comp_codes = comp_codes.view(torch.uint8) if comp_codes.dtype != torch.uint8 else comp_codes
+    _need(k_codes, "k_codes", torch.uint8, 2)
+    _need(k_scale, "k_scale", torch.float32, 1)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(swa_codes, "swa_codes", torch.uint8, 3)
+    _need(swa_scale, "swa_scale", torch.float32, 2)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_codes, "comp_codes", torch.uint8, 2)
+    _need(comp_scale, "comp_scale", torch.float32, 1)
+    _need(cu_comp, "cu_comp", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_codes.shape[1]
+    _attn_shapes(q, swa_codes, swa_len, comp_codes, cu_comp)
+    if swa_codes.shape[0] != B or cu_comp.numel() != B + 1:
+        raise ValueError(f"swa_codes must have {B} windows and cu_comp {B + 1} entries")
+    if q_idx.shape[0] != B or k_codes.shape[1] != q_idx.shape[2]:
+        raise ValueError("q_idx must be [B, Hi, dim] and k_codes [G, dim]")
+    _shape(w, q_idx.shape[:2], "w")
+    _shape(swa_scale, (B, W), "swa_scale")
+    if k_scale.numel() != k_codes.shape[0] or comp_scale.numel() != comp_codes.shape[0]:
+        raise ValueError("k_scale and comp_scale must hold one scale per row")
+    max_comp, total = _cu_sizes(cu_comp, max_comp)
+    if scale is None:
+        scale = d ** -0.5
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 1)
+    if total is not None:
+        _rows(comp_codes, total, "comp_codes")
+        _rows(k_codes, total, "k_codes")
+        if scores is not None:
+            _rows(scores, total, "scores")
+    if workspace is None:
+        workspace = decode_step_workspace(B, H, d, W, k, max_comp, q.device)
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=q.device)
+    out, lse = _attn_outputs(q, out, lse)
+    _need(topk, "topk", torch.int32, 2)
+    _shape(topk, (B, k), "topk")
+    _check(lib().chs_decode_step_fp8(B, H, d, W, k, float(scale), q_idx.shape[1], q_idx.shape[2], _ptr(q_idx),
+                                     _ptr(w), _ptr(k_codes), _ptr(k_scale), _ptr(q), _ptr(swa_codes),
+                                     _ptr(swa_scale), _ptr(swa_len), _ptr(comp_codes), _ptr(comp_scale),
+                                     _ptr(cu_comp), int(max_comp), _ptr(scores), _ptr(topk), _ptr(out), _ptr(lse),
+                                     _ptr(workspace), workspace.numel(), _stream()), "chs_decode_step_fp8")
     return topk, out, lse, scores
 
 

@@ -1448,12 +1448,14 @@ extern "C" chs_status chs_index_scores(chs_dtype dtype, int32_t batch, int32_t n
   return topk_first(dtype, batch, &a, lpc, static_cast<hipStream_t>(stream)) == CHS_OK ? CHS_OK : CHS_ERR_LAUNCH;
 }
 
-extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
-                                         const void* q_idx, const float* w, const void* k_idx,
-                                         const float* k_scale, const int64_t* cu_cand, int64_t max_cand,
-                                         float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
-                                         void* stream) {
-  using namespace chs;
+namespace chs {
+namespace {
+
+// Validates chs_index_topk_fp8's arguments, lays out the selection's workspace and fills *a.
+chs_status topk_fp8_setup(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k, const void* q_idx,
+                          const float* w, const void* k_idx, const float* k_scale, const int64_t* cu_cand,
+                          int64_t max_cand, float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                          Args* a) {
   if (batch < 1 || batch > 65535 || k < 1 || k > kMaxK || max_cand < 0 || max_cand >= (1LL << 31) ||
       n_heads < 1 || n_heads > 16 || head_dim < 16 || head_dim > 512 || head_dim % 16 != 0)
     return CHS_ERR_SHAPE;
@@ -1462,23 +1464,42 @@ extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t
   Workspace ws;
   const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
-  Args a;
-  a.q = q_idx; a.w = w; a.keys = k_idx; a.cu = cu_cand; a.max_cand = max_cand;
-  a.nh = n_heads; a.nvec = head_dim / 16; a.k = k; a.scores = scores; a.ws = ws; a.kscale = k_scale;
-  a.gs = kGroup;
-  a.pt = nullptr; a.cand_len = nullptr; a.pt_stride = 0; a.shift = 0; a.pool_pages = 0;
+  a->q = q_idx; a->w = w; a->keys = k_idx; a->cu = cu_cand; a->max_cand = max_cand;
+  a->nh = n_heads; a->nvec = head_dim / 16; a->k = k; a->scores = scores; a->ws = ws; a->kscale = k_scale;
+  a->gs = kGroup;
+  a->pt = nullptr; a->cand_len = nullptr; a->pt_stride = 0; a->shift = 0; a->pool_pages = 0;
+  return CHS_OK;
+}
+
+// The first kernel of the FP8 selection: scores and group statistics over E4M3 keys. Sets a->gs.
+chs_status topk_fp8_first(int32_t batch, int32_t head_dim, Args* a, hipStream_t s) {
+  if (a->max_cand == 0) return CHS_OK;
   int lpc = 2;
-  while (lpc < a.nvec) lpc *= 2;                        // one 16-byte key vector per lane
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (max_cand > 0) {
-    if (!launch_scores_mfma<uint8_t>(batch, head_dim, &a, s)) {
-      const int rw = kPasses * (64 / lpc);
-      a.gs = std::min(rw, kGroup);
-      const dim3 grid((unsigned)((max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
-      launch_scores<uint8_t>(grid, s, a, lpc);
-    }
-    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  while (lpc < a->nvec) lpc *= 2;                       // one 16-byte key vector per lane
+  if (!launch_scores_mfma<uint8_t>(batch, head_dim, a, s)) {
+    const int rw = kPasses * (64 / lpc);
+    a->gs = std::min(rw, kGroup);
+    const dim3 grid((unsigned)((a->max_cand + 4 * rw - 1) / (4 * rw)), (unsigned)batch);
+    launch_scores<uint8_t>(grid, s, *a, lpc);
   }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                                         const void* q_idx, const float* w, const void* k_idx,
+                                         const float* k_scale, const int64_t* cu_cand, int64_t max_cand,
+                                         float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  using namespace chs;
+  Args a;
+  const chs_status st = topk_fp8_setup(batch, n_heads, head_dim, k, q_idx, w, k_idx, k_scale, cu_cand, max_cand,
+                                       scores, topk, workspace, workspace_bytes, &a);
+  if (st != CHS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (topk_fp8_first(batch, head_dim, &a, s) != CHS_OK) return CHS_ERR_LAUNCH;
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, a, topk);
   return launch_status();
 }
@@ -1565,7 +1586,8 @@ namespace {
 // TILES 16-head tiles per workgroup: 1 (four waves attend, the others store the top-k row and end)
 // or 4 (all sixteen waves attend 64 heads, so a split's selection runs once, not once per head
 // tile). The split plan and the arithmetic are the same either way, so the results are too.
-template <int D, int TILES>
+// FP8: the entries and window rows are E4M3 codes with per-row scales (the FP8 split body).
+template <int D, int TILES, bool FP8 = false>
 __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::AttnArgs aa, int32_t* topk) {
   union alignas(16) StepShared {
     CollectShared c;
@@ -1587,7 +1609,7 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
     // All 16 waves attend the split for 64 heads; the top-k row is stored afterwards (a store before
     // the gathers would hold the wait counter they use).
     attn::NoHook none;
-    attn::attn_split_sm<D, 4, attn::NoHook, false, false>(aa, sm, b, split, 4 * z, threadIdx.x, sh.at, none, sel);
+    attn::attn_split_sm<D, 4, attn::NoHook, FP8, false>(aa, sm, b, split, 4 * z, threadIdx.x, sh.at, none, sel);
     if (selects && z == 0 && s_begin <= sm.nswa)
       for (int i = threadIdx.x; i < aa.k; i += kCThreads) topk[(int64_t)b * aa.k + i] = sel[i];
   } else {
@@ -1600,7 +1622,7 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
       return;
     }
     attn::NoHook none;
-    attn::attn_split_sm<D, 1, attn::NoHook, false, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
+    attn::attn_split_sm<D, 1, attn::NoHook, FP8, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
   }
 }
 
@@ -1625,28 +1647,40 @@ extern "C" size_t chs_decode_step_workspace_size(int32_t batch, int32_t n_heads,
 namespace chs {
 namespace {
 
+// The row scales of an FP8 step (chs_decode_step_fp8); all NULL for bf16 storage.
+struct Fp8Scales {
+  const float* keys;   // [cu_comp[batch]] index-key row scales
+  const float* swa;    // [batch, window] window row scales
+  const float* comp;   // [cu_comp[batch]] entry row scales
+  bool on() const { return keys != nullptr; }
+};
+
 chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, float scale,
                             int32_t idx_heads, int32_t idx_dim, const void* q_idx, const float* w, const void* k_idx,
                             const void* q, const void* swa_kv, const int32_t* swa_len, const void* comp_kv,
                             const int64_t* cu_comp, int64_t max_comp, float* scores, int32_t* topk, float* out,
-                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                            const Fp8Scales& f8 = Fp8Scales{nullptr, nullptr, nullptr}) {
   chs_status st = attn::check_args(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_kv, swa_len, comp_kv,
                                    cu_comp, topk, max_comp, out);
   if (st != CHS_OK) return st;
   if (k < 1) return CHS_ERR_SHAPE;
   if (!q_idx || !topk || !workspace) return CHS_ERR_NULL;
+  if (f8.on() && ((window > 0 && !f8.swa) || !f8.comp)) return CHS_ERR_NULL;
   size_t attn_off = 0;
   const size_t need = step_ws(batch, n_heads, d, window, k, max_comp, &attn_off);
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
   Args ia;
   int lpc = 2;
-  st = topk_setup(CHS_BF16, batch, idx_heads, idx_dim, k, q_idx, w, k_idx, cu_comp, max_comp, scores, topk,
-                  workspace, attn_off, &ia, &lpc);
+  st = f8.on() ? topk_fp8_setup(batch, idx_heads, idx_dim, k, q_idx, w, k_idx, f8.keys, cu_comp, max_comp, scores,
+                                topk, workspace, attn_off, &ia)
+               : topk_setup(CHS_BF16, batch, idx_heads, idx_dim, k, q_idx, w, k_idx, cu_comp, max_comp, scores, topk,
+                            workspace, attn_off, &ia, &lpc);
   if (st != CHS_OK) return st;
   const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, d, window, k, max_comp);
   attn::AttnArgs a;
   a.q = q; a.swa = swa_kv; a.swa_len = swa_len; a.comp = comp_kv; a.cu_comp = cu_comp; a.topk = topk;
-  a.swa_scale = nullptr; a.comp_scale = nullptr;
+  a.swa_scale = f8.swa; a.comp_scale = f8.comp;
   a.pg = attn::Paging{nullptr, 0, nullptr, nullptr, 0, 0, 0};
   a.H = n_heads; a.D = d; a.W = window; a.k = k; a.max_comp = max_comp;
   a.scale_log2 = scale * kLog2e;
@@ -1654,8 +1688,9 @@ chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t w
   a.head_tiles = (n_heads + 63) / 64;
   attn::ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace) + attn_off);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (topk_first(CHS_BF16, batch, &ia, lpc, s) != CHS_OK) return CHS_ERR_LAUNCH;
-  if (p.wide) {
+  if ((f8.on() ? topk_fp8_first(batch, idx_dim, &ia, s) : topk_first(CHS_BF16, batch, &ia, lpc, s)) != CHS_OK)
+    return CHS_ERR_LAUNCH;
+  if (p.wide && !f8.on()) {
     // Many sequences at d = 512: the attention's splits run in the 64-head kernel, which stages each
     // split's entries from the top-k list, so the selection runs once per sequence into that list
     // and the attention is chs_decode_attn's own launch (the results are the two calls', trivially).
@@ -1671,11 +1706,22 @@ chs_status decode_step_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t w
   const bool wide = (int64_t)p.n_splits * batch * ((n_heads + 15) / 16) > 256;
   const dim3 grid(p.n_splits, batch, wide ? (n_heads + 63) / 64 : (n_heads + 15) / 16);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kCThreads), 0, s, ia, a, topk); };
-  switch (d) {
-    case 64: wide ? go(collect_attn_kernel<64, 4>) : go(collect_attn_kernel<64, 1>); break;
-    case 128: wide ? go(collect_attn_kernel<128, 4>) : go(collect_attn_kernel<128, 1>); break;
-    case 256: wide ? go(collect_attn_kernel<256, 4>) : go(collect_attn_kernel<256, 1>); break;
-    default: wide ? go(collect_attn_kernel<512, 4>) : go(collect_attn_kernel<512, 1>); break;
+  if (f8.on()) {
+    // FP8 storage: the split body of chs_decode_attn_fp8 (16-head tiles also at many sequences, where the
+    // wide plan's longer splits take several chunks), so the results are that call's.
+    switch (d) {
+      case 64: wide ? go(collect_attn_kernel<64, 4, true>) : go(collect_attn_kernel<64, 1, true>); break;
+      case 128: wide ? go(collect_attn_kernel<128, 4, true>) : go(collect_attn_kernel<128, 1, true>); break;
+      case 256: wide ? go(collect_attn_kernel<256, 4, true>) : go(collect_attn_kernel<256, 1, true>); break;
+      default: wide ? go(collect_attn_kernel<512, 4, true>) : go(collect_attn_kernel<512, 1, true>); break;
+    }
+  } else {
+    switch (d) {
+      case 64: wide ? go(collect_attn_kernel<64, 4>) : go(collect_attn_kernel<64, 1>); break;
+      case 128: wide ? go(collect_attn_kernel<128, 4>) : go(collect_attn_kernel<128, 1>); break;
+      case 256: wide ? go(collect_attn_kernel<256, 4>) : go(collect_attn_kernel<256, 1>); break;
+      default: wide ? go(collect_attn_kernel<512, 4>) : go(collect_attn_kernel<512, 1>); break;
+    }
   }
   if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
   attn::launch_combine(a, batch, n_heads, d, out, lse, s);
@@ -1718,6 +1764,19 @@ extern "C" chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d,
   return chs::decode_step_impl(batch, n_heads, d, window, k, scale, idx_heads, idx_dim, q_idx, w, k_idx, q, swa_kv,
                                swa_len, comp_kv, cu_comp, max_comp, scores, topk, out, lse, workspace,
                                workspace_bytes, stream);
+}
+
+extern "C" chs_status chs_decode_step_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                          float scale, int32_t idx_heads, int32_t idx_dim, const void* q_idx,
+                                          const float* w, const void* k_codes, const float* k_scale, const void* q,
+                                          const void* swa_codes, const float* swa_scale, const int32_t* swa_len,
+                                          const void* comp_codes, const float* comp_scale, const int64_t* cu_comp,
+                                          int64_t max_comp, float* scores, int32_t* topk, float* out, float* lse,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_scale) return CHS_ERR_NULL;
+  return chs::decode_step_impl(batch, n_heads, d, window, k, scale, idx_heads, idx_dim, q_idx, w, k_codes, q,
+                               swa_codes, swa_len, comp_codes, cu_comp, max_comp, scores, topk, out, lse, workspace,
+                               workspace_bytes, stream, chs::Fp8Scales{k_scale, swa_scale, comp_scale});
 }
 
 extern "C" chs_status chs_decode_step_noalloc(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,

@@ -355,6 +355,30 @@ chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d, int32_t wi
                            int32_t* topk, float* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- chs_decode_step_fp8: the C4 decode step over FP8 storage in one call ------------------------
+ * Source: as chs_decode_step, with "SGLang 如何为 DeepSeek V4 打造「Day-0」推理加速", 4.3 部署配置建议
+ * (an fp8 KV cache) and "DeepSeek-V4 本地部署，SGLang 把活做絕了", V4 到底改了啥 (attention kept in
+ * FP8), in the reading of chs_index_topk_fp8 and chs_decode_attn_fp8 (OCP E4M3 codes, one fp32
+ * scale per row).
+ * Computes exactly chs_index_topk_fp8(batch, idx_heads, idx_dim, k, q_idx, w, k_codes, k_scale,
+ * cu_comp, max_comp, scores, topk, ...) followed by chs_decode_attn_fp8(batch, n_heads, d, window, k,
+ * scale, q, swa_codes, swa_scale, swa_len, comp_codes, comp_scale, cu_comp, topk, max_comp, out, lse,
+ * ...): scores, topk, out and lse are bit-identical to those two calls, in three launches instead
+ * of four (the selection's second kernel runs inside the attention's split kernel).
+ * k_codes  : [cu_comp[batch], idx_dim] E4M3 codes; k_scale: [cu_comp[batch]] fp32 (>= 0, finite).
+ * swa_codes: [batch, window, d] E4M3; swa_scale: [batch, window] fp32 (may be NULL when window = 0).
+ * comp_codes: [cu_comp[batch], d] E4M3; comp_scale: [cu_comp[batch]] fp32.
+ * q_idx, w, q, swa_len, cu_comp, scores, topk, out, lse and the ranges: as chs_decode_step (idx_dim
+ * a multiple of 16 in [16, 512]). A NULL scale array returns CHS_ERR_NULL before any launch.
+ * workspace: chs_decode_step_workspace_size(batch, n_heads, d, window, k, max_comp) bytes. */
+chs_status chs_decode_step_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, float scale,
+                               int32_t idx_heads, int32_t idx_dim, const void* q_idx, const float* w,
+                               const void* k_codes, const float* k_scale, const void* q, const void* swa_codes,
+                               const float* swa_scale, const int32_t* swa_len, const void* comp_codes,
+                               const float* comp_scale, const int64_t* cu_comp, int64_t max_comp, float* scores,
+                               int32_t* topk, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* ---- chs_decode_step_noalloc: chs_decode_step for callers that cannot allocate ------------------
  * For callers that cannot call hipMalloc or pass a workspace: code under HIP graph capture that must
  * not allocate, tight serving loops, harnesses that forbid allocation. Computes exactly what

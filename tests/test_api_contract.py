@@ -334,6 +334,26 @@ def test_decode_step_validation(kw, code):
     assert step(**kw) == code
 
 
+def step8(batch=1, H=64, d=512, W=128, k=512, scale=0.04, nh=4, dI=128, qi=FAKE, w=FAKE, ki=FAKE, ks=FAKE, q=FAKE,
+          swa=FAKE, ss=FAKE, sl=FAKE, comp=FAKE, cs=FAKE, cu=FAKE, maxc=1000, sc=FAKE, tk=FAKE, out=FAKE, lse=FAKE,
+          ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_decode_step_workspace_size(batch, H, d, W, k, maxc)
+    return L.chs_decode_step_fp8(batch, H, d, W, k, ctypes.c_float(scale), nh, dI, qi, w, ki, ks, q, swa, ss, sl, comp,
+                                 cs, cu, maxc, sc, tk, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(H=0), SHAPE), (dict(d=96), SHAPE), (dict(k=0), SHAPE), (dict(k=2049), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(nh=17), SHAPE), (dict(dI=24), SHAPE), (dict(dI=1024), SHAPE),
+    (dict(qi=None), NULL), (dict(ki=None), NULL), (dict(ks=None), NULL), (dict(ss=None), NULL), (dict(cs=None), NULL),
+    (dict(q=None), NULL), (dict(comp=None), NULL), (dict(tk=None), NULL), (dict(ws=None), NULL), (dict(wsb=8), WS),
+])
+def test_decode_step_fp8_validation(kw, code):
+    assert step8(**kw) == code
+
+
 def test_decode_step_workspace_covers_both_calls():
     L = chs.lib()
     for batch, H, d, W, k, G in [(1, 64, 512, 128, 512, 262144), (64, 64, 512, 128, 512, 50000), (2, 8, 64, 128, 64, 256)]:

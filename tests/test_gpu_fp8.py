@@ -153,3 +153,36 @@ def test_fp8_attention_matches_oracle(H, d, W, swa_lens, G_list, k, dense):
         o_ref, l_ref = oracle.attend_fp8(qf[b], codes, scales, d ** -0.5)
         assert_bf16_path(og[b], o_ref, f"fp8 attn b={b}")
         assert_lse(lg[b], l_ref, f"fp8 lse b={b}", 1e-3)
+
+
+@pytest.mark.parametrize("B,H,d,W,swa,G_list,Hi,dI,k", [
+    (1, 64, 512, 128, [128], [20000], 4, 128, 512),                               # one sequence, 16-head workgroups
+    (24, 72, 512, 128, [128, 77, 0, 5] * 6, [1500 + 41 * i for i in range(24)], 4, 128, 64),   # 64-head workgroups
+    (3, 16, 128, 64, [64, 10, 64], [300, 0, 2000], 2, 64, 32),                   # small heads, an empty sequence
+])
+def test_fp8_step_matches_the_two_calls(B, H, d, W, swa, G_list, Hi, dI, k):
+    # chs_decode_step_fp8 against chs_index_topk_fp8 followed by chs_decode_attn_fp8 on the same inputs:
+    # scores, top-k, out and lse bit for bit (the two calls are checked against the oracle above).
+    print(f"case: fp8 step B={B} H={H} d={d} G={sum(G_list)} k={k}", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(11)
+    G = int(sum(G_list))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(G_list)]), dtype=torch.int64, device=dev())
+    kc, ks = chs.quantize_e4m3(torch.randn(G, dI, generator=g, device=dev()).bfloat16())
+    cc, cs = chs.quantize_e4m3(torch.randn(G, d, generator=g, device=dev()).bfloat16())
+    sc, ss = chs.quantize_e4m3(torch.randn(B * W, d, generator=g, device=dev()).bfloat16())
+    sc, ss = sc.view(B, W, d), ss.view(B, W)
+    qi = torch.randn(B, Hi, dI, generator=g, device=dev()).bfloat16()
+    w = torch.rand(B, Hi, generator=g, device=dev())
+    q = torch.randn(B, H, d, generator=g, device=dev()).bfloat16()
+    sl = torch.tensor(swa, dtype=torch.int32, device=dev())
+    mx = max(G_list)
+    s1 = torch.empty(G, dtype=torch.float32, device=dev())
+    s2 = torch.empty(G, dtype=torch.float32, device=dev())
+    tk1, _ = chs.index_topk_fp8(qi, w, kc, ks, cu, k, mx, s1)
+    o1, l1 = chs.decode_attn_fp8(q, sc, ss, sl, cc, cs, cu, tk1, None, mx)
+    tk2, o2, l2, _ = chs.decode_step_fp8(qi, w, kc, ks, q, sc, ss, sl, cc, cs, cu, k, None, mx, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2), "scores differ"
+    assert torch.equal(tk1, tk2), "top-k differs"
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)), "out differs"
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "lse differs"
