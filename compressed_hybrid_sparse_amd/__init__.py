@@ -27,7 +27,8 @@ EXPORTS = ("chs_version", "chs_status_string", "chs_workspace_clear", "chs_compr
            "chs_decode_attn_paged", "chs_append_paged", "chs_index_topk_paged", "chs_gather_selected",
            "chs_append_multi", "chs_index_topk_fp8_paged", "chs_decode_attn_fp8_paged",
            "chs_decode_step_workspace_size", "chs_decode_step", "chs_index_scores", "chs_decode_step_noalloc",
-           "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8", "chs_decode_step_fp8")
+           "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8", "chs_decode_step_fp8",
+           "chs_decode_step_paged")
 
 _lib = None
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -94,6 +95,9 @@ def lib():
                                               _p, _i64, _p, _p, _p, _p, _p]
         L.chs_decode_step_fp8.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                                           _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _sz, _p]
+        L.chs_decode_step_paged.argtypes = [_i32, _i32, _i32, _i32, _i32, _f, _i32, _i32, _p, _p, _p, _p, _p, _p,
+                                            _i64, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p, _p, _p, _p, _p, _sz,
+                                            _p]
         L.chs_quantize_e4m3.argtypes = [ctypes.c_int, _i64, _i32, _p, _p, _p, _p]
         L.chs_compress_fp8.argtypes = [ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.chs_append_fp8.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -103,7 +107,7 @@ def lib():
         L.chs_index_topk_paged.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p,
                                            _i64, _p, _p, _p, _sz, _p]
         for fn in ("chs_workspace_clear", "chs_compress", "chs_index_topk", "chs_index_scores", "chs_decode_step_noalloc",
-                   "chs_decode_step_fp8",
+                   "chs_decode_step_fp8", "chs_decode_step_paged",
                    "chs_quantize_e4m3", "chs_compress_fp8", "chs_append_fp8",
                    "chs_decode_step", "chs_decode_attn", "chs_index_topk_fp8",
                    "chs_decode_attn_fp8", "chs_append", "chs_decode_attn_paged", "chs_append_paged",
@@ -856,6 +860,57 @@ def index_topk_paged(q_idx, w, key_pool, page_size: int, page_table, cand_len, k
                                       _ptr(cand_len), int(max_cand), _ptr(scores), _ptr(out), _ptr(workspace),
                                       workspace.numel(), _stream()), "chs_index_topk_paged")
     return out, scores
+
+
+def decode_step_paged(q_idx, w, key_pool, q, swa_pool, swa_page, swa_len, comp_pool, page_size: int, page_table,
+                      comp_len, k: int, max_comp: int, scale=None, scores=None, workspace=None, topk=None, out=None,
+                      lse=None):
+    """The C4 decode step over paged pools in one call (chs_decode_step_paged): index_topk_paged then
+    decode_attn_paged with one page table for the key pool and the entry pool, bit-identical results.
+    q_idx: [B, Hi, dim] bf16; w: [B, Hi] fp32; key_pool: [pool_rows, dim] bf16; q: [B, H, d] bf16;
+    swa_pool: [swa_pages, W, d]; swa_page, swa_len: [B] int32; comp_pool: [pool_rows, d];
+    page_table: [B, pt_stride] int32; comp_len: [B] int64; scores: [B, max_comp] fp32 or None.
+    Returns (topk [B, k] int32, out [B, H, d] fp32, lse [B, H] fp32, scores)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(key_pool, "key_pool", torch.bfloat16, 2)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(swa_pool, "swa_pool", torch.bfloat16, 3)
+    _need(swa_page, "swa_page", torch.int32, 1)
+    _need(swa_len, "swa_len", torch.int32, 1)
+    _need(comp_pool, "comp_pool", torch.bfloat16, 2)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(comp_len, "comp_len", torch.int64, 1)
+    B, H, d = q.shape
+    W = swa_pool.shape[1]
+    Bi, nh, dim = q_idx.shape
+    _attn_shapes(q, swa_pool, swa_len, comp_pool, comp_len)
+    _shape(swa_page, (B,), "swa_page")
+    _shape(comp_len, (B,), "comp_len")
+    _shape(w, (B, nh), "w")
+    if Bi != B or key_pool.shape[1] != dim or page_table.shape[0] != B:
+        raise ValueError("q_idx must be [B, Hi, dim], key_pool [rows, dim] and page_table [B, pt_stride]")
+    if key_pool.shape[0] != comp_pool.shape[0]:
+        raise ValueError("key_pool and comp_pool must hold the same number of rows (one page table serves both)")
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 2)
+        _shape(scores, (B, max_comp), "scores")
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = decode_step_workspace(B, H, d, W, k, max_comp, q.device)
+    if topk is None:
+        topk = torch.empty(B, k, dtype=torch.int32, device=q.device)
+    _need(topk, "topk", torch.int32, 2)
+    _shape(topk, (B, k), "topk")
+    out, lse = _attn_outputs(q, out, lse)
+    _check(lib().chs_decode_step_paged(B, H, d, W, k, float(scale), nh, dim, _ptr(q_idx), _ptr(w), _ptr(key_pool),
+                                       _ptr(q), _ptr(swa_pool), _ptr(swa_page), swa_pool.shape[0], _ptr(swa_len),
+                                       _ptr(comp_pool), comp_pool.shape[0] // page_size, page_size, _ptr(page_table),
+                                       page_table.shape[1], _ptr(comp_len), int(max_comp), _ptr(scores), _ptr(topk),
+                                       _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()),
+           "chs_decode_step_paged")
+    return topk, out, lse, scores
 
 
 # ---------------------------------------------------------------- working-set gather

@@ -1504,13 +1504,15 @@ extern "C" chs_status chs_index_topk_fp8(int32_t batch, int32_t n_heads, int32_t
   return launch_status();
 }
 
-extern "C" chs_status chs_index_topk_paged(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
-                                           int32_t k, const void* q_idx, const float* w, const void* key_pool,
-                                           int64_t pool_pages, int32_t page_size, const int32_t* page_table,
-                                           int32_t pt_stride, const int64_t* cand_len, int64_t max_cand,
-                                           float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
-                                           void* stream) {
-  using namespace chs;
+namespace chs {
+namespace {
+
+// Validates chs_index_topk_paged's arguments, lays out the selection's workspace and fills *a.
+chs_status topk_paged_setup(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim, int32_t k,
+                            const void* q_idx, const float* w, const void* key_pool, int64_t pool_pages,
+                            int32_t page_size, const int32_t* page_table, int32_t pt_stride, const int64_t* cand_len,
+                            int64_t max_cand, float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                            Args* a) {
   if (!dtype_ok(dtype)) return CHS_ERR_DTYPE;
   if (batch < 1 || batch > 65535 || k < 1 || k > kMaxK || max_cand < 0 || max_cand >= (1LL << 31) ||
       n_heads < 1 || n_heads > 16 || head_dim < 8 || head_dim > 512 || page_size < 64 || page_size > 65536 ||
@@ -1522,12 +1524,29 @@ extern "C" chs_status chs_index_topk_paged(chs_dtype dtype, int32_t batch, int32
   Workspace ws;
   const size_t need = ws_layout(batch, max_cand, &ws, static_cast<char*>(workspace));
   if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  a->q = q_idx; a->w = w; a->keys = key_pool; a->cu = nullptr; a->max_cand = max_cand;
+  a->nh = n_heads; a->nvec = head_dim / 8; a->k = k; a->scores = scores; a->ws = ws; a->kscale = nullptr;
+  a->gs = kGroup;
+  a->pt = page_table; a->cand_len = cand_len; a->pt_stride = pt_stride; a->shift = __builtin_ctz((unsigned)page_size);
+  a->pool_pages = pool_pages;
+  return CHS_OK;
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" chs_status chs_index_topk_paged(chs_dtype dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
+                                           int32_t k, const void* q_idx, const float* w, const void* key_pool,
+                                           int64_t pool_pages, int32_t page_size, const int32_t* page_table,
+                                           int32_t pt_stride, const int64_t* cand_len, int64_t max_cand,
+                                           float* scores, int32_t* topk, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  using namespace chs;
   Args a;
-  a.q = q_idx; a.w = w; a.keys = key_pool; a.cu = nullptr; a.max_cand = max_cand;
-  a.nh = n_heads; a.nvec = head_dim / 8; a.k = k; a.scores = scores; a.ws = ws; a.kscale = nullptr;
-  a.gs = kGroup;
-  a.pt = page_table; a.cand_len = cand_len; a.pt_stride = pt_stride; a.shift = __builtin_ctz((unsigned)page_size);
-  a.pool_pages = pool_pages;
+  const chs_status st = topk_paged_setup(dtype, batch, n_heads, head_dim, k, q_idx, w, key_pool, pool_pages,
+                                         page_size, page_table, pt_stride, cand_len, max_cand, scores, topk,
+                                         workspace, workspace_bytes, &a);
+  if (st != CHS_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_cand > 0) {
     launch_scores_mfma<uint16_t>(batch, head_dim, &a, s);
@@ -1587,7 +1606,8 @@ namespace {
 // or 4 (all sixteen waves attend 64 heads, so a split's selection runs once, not once per head
 // tile). The split plan and the arithmetic are the same either way, so the results are too.
 // FP8: the entries and window rows are E4M3 codes with per-row scales (the FP8 split body).
-template <int D, int TILES, bool FP8 = false>
+// PAGED: the window and the entries come through the page tables of aa.pg (the paged split body).
+template <int D, int TILES, bool FP8 = false, bool PAGED = false>
 __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::AttnArgs aa, int32_t* topk) {
   union alignas(16) StepShared {
     CollectShared c;
@@ -1609,7 +1629,7 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
     // All 16 waves attend the split for 64 heads; the top-k row is stored afterwards (a store before
     // the gathers would hold the wait counter they use).
     attn::NoHook none;
-    attn::attn_split_sm<D, 4, attn::NoHook, FP8, false>(aa, sm, b, split, 4 * z, threadIdx.x, sh.at, none, sel);
+    attn::attn_split_sm<D, 4, attn::NoHook, FP8, PAGED>(aa, sm, b, split, 4 * z, threadIdx.x, sh.at, none, sel);
     if (selects && z == 0 && s_begin <= sm.nswa)
       for (int i = threadIdx.x; i < aa.k; i += kCThreads) topk[(int64_t)b * aa.k + i] = sel[i];
   } else {
@@ -1622,7 +1642,7 @@ __global__ __launch_bounds__(kCThreads) void collect_attn_kernel(Args ia, attn::
       return;
     }
     attn::NoHook none;
-    attn::attn_split_sm<D, 1, attn::NoHook, FP8, false>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
+    attn::attn_split_sm<D, 1, attn::NoHook, FP8, PAGED>(aa, sm, b, split, z, threadIdx.x, sh.at, none, sel);
   }
 }
 
@@ -1764,6 +1784,93 @@ extern "C" chs_status chs_decode_step(int32_t batch, int32_t n_heads, int32_t d,
   return chs::decode_step_impl(batch, n_heads, d, window, k, scale, idx_heads, idx_dim, q_idx, w, k_idx, q, swa_kv,
                                swa_len, comp_kv, cu_comp, max_comp, scores, topk, out, lse, workspace,
                                workspace_bytes, stream);
+}
+
+namespace chs {
+namespace {
+
+chs_status decode_step_paged_impl(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, float scale,
+                                  int32_t idx_heads, int32_t idx_dim, const void* q_idx, const float* w,
+                                  const void* key_pool, const void* q, const void* swa_pool, const int32_t* swa_page,
+                                  int64_t swa_pages, const int32_t* swa_len, const void* comp_pool,
+                                  int64_t pool_pages, int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                                  const int64_t* comp_len, int64_t max_comp, float* scores, int32_t* topk, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes, hipStream_t s) {
+  // The shared checks null-test their cu argument; here the per-sequence counts take its place.
+  chs_status st = attn::check_args(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_pool, swa_len, comp_pool,
+                                   comp_len, topk, max_comp, out);
+  if (st != CHS_OK) return st;
+  if (k < 1) return CHS_ERR_SHAPE;
+  if (!q_idx || !workspace || (window > 0 && !swa_page)) return CHS_ERR_NULL;
+  if (window > 0 && swa_pages < 1) return CHS_ERR_SHAPE;
+  size_t attn_off = 0;
+  const size_t need = step_ws(batch, n_heads, d, window, k, max_comp, &attn_off);
+  if (workspace_bytes < need) return CHS_ERR_WORKSPACE;
+  Args ia;
+  st = topk_paged_setup(CHS_BF16, batch, idx_heads, idx_dim, k, q_idx, w, key_pool, pool_pages, page_size,
+                        page_table, pt_stride, comp_len, max_comp, scores, topk, workspace, attn_off, &ia);
+  if (st != CHS_OK) return st;
+  const attn::SplitPlan p = attn::plan_splits(CHS_BF16, batch, n_heads, d, window, k, max_comp);
+  attn::AttnArgs a;
+  a.q = q; a.swa = swa_pool; a.swa_len = swa_len; a.comp = comp_pool; a.cu_comp = nullptr; a.topk = topk;
+  a.swa_scale = nullptr; a.comp_scale = nullptr;
+  a.pg = attn::Paging{};
+  a.pg.swa_page = window > 0 ? swa_page : nullptr;
+  a.pg.swa_pages = swa_pages;
+  a.pg.pt = page_table;
+  a.pg.comp_len = comp_len;
+  a.pg.pt_stride = pt_stride;
+  a.pg.shift = __builtin_ctz((unsigned)page_size);
+  a.pg.pool_pages = pool_pages;
+  a.H = n_heads; a.D = d; a.W = window; a.k = k; a.max_comp = max_comp;
+  a.scale_log2 = scale * kLog2e;
+  a.n_splits = p.n_splits; a.kps = p.kps;
+  a.head_tiles = (n_heads + 63) / 64;
+  attn::ws_bytes(CHS_BF16, batch, n_heads, d, p, &a.part_o, &a.part_ml, static_cast<char*>(workspace) + attn_off);
+  if (max_comp > 0) {
+    launch_scores_mfma<uint16_t>(batch, idx_dim, &ia, s);
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  }
+  if (p.wide) {
+    // Many sequences at d = 512: as chs_decode_step, the selection once per sequence, then the paged
+    // attention call's own 64-head launch.
+    hipLaunchKernelGGL(collect_kernel, dim3((unsigned)batch), dim3(kCThreads), 0, s, ia, topk);
+    if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+    return chs_decode_attn_paged(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_pool, swa_page, swa_pages,
+                                 swa_len, comp_pool, pool_pages, page_size, page_table, pt_stride, comp_len, topk,
+                                 max_comp, out, lse, static_cast<char*>(workspace) + attn_off,
+                                 workspace_bytes - attn_off, s);
+  }
+  const bool wide = (int64_t)p.n_splits * batch * ((n_heads + 15) / 16) > 256;
+  const dim3 grid(p.n_splits, batch, wide ? (n_heads + 63) / 64 : (n_heads + 15) / 16);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kCThreads), 0, s, ia, a, topk); };
+  switch (d) {
+    case 64: wide ? go(collect_attn_kernel<64, 4, false, true>) : go(collect_attn_kernel<64, 1, false, true>); break;
+    case 128: wide ? go(collect_attn_kernel<128, 4, false, true>) : go(collect_attn_kernel<128, 1, false, true>); break;
+    case 256: wide ? go(collect_attn_kernel<256, 4, false, true>) : go(collect_attn_kernel<256, 1, false, true>); break;
+    default: wide ? go(collect_attn_kernel<512, 4, false, true>) : go(collect_attn_kernel<512, 1, false, true>); break;
+  }
+  if (launch_status() != CHS_OK) return CHS_ERR_LAUNCH;
+  attn::launch_combine(a, batch, n_heads, d, out, lse, s);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace chs
+
+extern "C" chs_status chs_decode_step_paged(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,
+                                            float scale, int32_t idx_heads, int32_t idx_dim, const void* q_idx,
+                                            const float* w, const void* key_pool, const void* q,
+                                            const void* swa_pool, const int32_t* swa_page, int64_t swa_pages,
+                                            const int32_t* swa_len, const void* comp_pool, int64_t pool_pages,
+                                            int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                                            const int64_t* comp_len, int64_t max_comp, float* scores, int32_t* topk,
+                                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  return chs::decode_step_paged_impl(batch, n_heads, d, window, k, scale, idx_heads, idx_dim, q_idx, w, key_pool, q,
+                                     swa_pool, swa_page, swa_pages, swa_len, comp_pool, pool_pages, page_size,
+                                     page_table, pt_stride, comp_len, max_comp, scores, topk, out, lse, workspace,
+                                     workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" chs_status chs_decode_step_fp8(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k,

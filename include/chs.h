@@ -431,6 +431,23 @@ chs_status chs_decode_attn_paged(chs_dtype dtype, int32_t batch, int32_t n_heads
                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* chs_decode_step_paged: chs_decode_step over the paged pools, addressed as above: computes exactly
+ * chs_index_topk_paged(CHS_BF16, batch, idx_heads, idx_dim, k, q_idx, w, key_pool, pool_pages, page_size,
+ * page_table, pt_stride, comp_len, max_comp, scores, topk, ...) followed by
+ * chs_decode_attn_paged(CHS_BF16, batch, n_heads, d, window, k, scale, q, swa_pool, swa_page, swa_pages,
+ * swa_len, comp_pool, pool_pages, page_size, page_table, pt_stride, comp_len, topk, max_comp, out, lse,
+ * ...), one page table serving the index-key pool and the entry pool (the same entry numbering):
+ * scores, topk, out and lse are bit-identical to those two calls, in three launches instead of four.
+ * Ranges: those of the two calls (bf16; idx_dim 64, 128 or 256; page_size a power of two of at
+ * least 64). workspace: chs_decode_step_workspace_size(batch, n_heads, d, window, k, max_comp) bytes. */
+chs_status chs_decode_step_paged(int32_t batch, int32_t n_heads, int32_t d, int32_t window, int32_t k, float scale,
+                                 int32_t idx_heads, int32_t idx_dim, const void* q_idx, const float* w,
+                                 const void* key_pool, const void* q, const void* swa_pool, const int32_t* swa_page,
+                                 int64_t swa_pages, const int32_t* swa_len, const void* comp_pool, int64_t pool_pages,
+                                 int32_t page_size, const int32_t* page_table, int32_t pt_stride,
+                                 const int64_t* comp_len, int64_t max_comp, float* scores, int32_t* topk, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* chs_index_topk_paged: chs_index_topk with the index keys in a paged pool, addressed as above
  * (candidate j of sequence b at pool row page_table[b * pt_stride + j / page_size] * page_size +
  * j mod page_size; cand_len[b] candidates, capped at max_cand and pt_stride * page_size). scores, if

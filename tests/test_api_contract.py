@@ -354,6 +354,27 @@ def test_decode_step_fp8_validation(kw, code):
     assert step8(**kw) == code
 
 
+def stepp(batch=1, H=64, d=512, W=128, k=512, scale=0.04, nh=4, dI=128, qi=FAKE, w=FAKE, kp=FAKE, q=FAKE, swa=FAKE,
+          sp=FAKE, swa_pages=4, sl=FAKE, comp=FAKE, pool_pages=16, P=64, pt=FAKE, pts=16, cl=FAKE, maxc=1000,
+          sc=FAKE, tk=FAKE, out=FAKE, lse=FAKE, ws=FAKE, wsb=None):
+    L = chs.lib()
+    if wsb is None:
+        wsb = L.chs_decode_step_workspace_size(batch, H, d, W, k, maxc)
+    return L.chs_decode_step_paged(batch, H, d, W, k, ctypes.c_float(scale), nh, dI, qi, w, kp, q, swa, sp, swa_pages,
+                                   sl, comp, pool_pages, P, pt, pts, cl, maxc, sc, tk, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(H=0), SHAPE), (dict(d=96), SHAPE), (dict(k=0), SHAPE), (dict(k=2049), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(nh=17), SHAPE), (dict(P=48), SHAPE), (dict(P=32), SHAPE), (dict(pts=0), SHAPE),
+    (dict(pool_pages=0), SHAPE), (dict(swa_pages=0), SHAPE), (dict(dI=96), UNSUP), (dict(qi=None), NULL),
+    (dict(kp=None), NULL), (dict(sp=None), NULL), (dict(pt=None), NULL), (dict(cl=None), NULL), (dict(q=None), NULL),
+    (dict(tk=None), NULL), (dict(ws=None), NULL), (dict(wsb=8), WS),
+])
+def test_decode_step_paged_validation(kw, code):
+    assert stepp(**kw) == code
+
+
 def test_decode_step_workspace_covers_both_calls():
     L = chs.lib()
     for batch, H, d, W, k, G in [(1, 64, 512, 128, 512, 262144), (64, 64, 512, 128, 512, 50000), (2, 8, 64, 128, 64, 256)]:

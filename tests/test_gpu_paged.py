@@ -447,3 +447,62 @@ def test_paged_fp8_attention_equals_contiguous_and_oracle(H, d, W, P, G_list, k,
     o_ref, l_ref = oracle.attend_fp8(q[b].float().cpu().numpy(), codes, scales, d ** -0.5)
     assert_bf16_path(op[b].cpu().numpy(), o_ref, "paged fp8 attention")
     assert_lse(lp[b].cpu().numpy(), l_ref, "paged fp8 lse", 1e-3)
+
+
+@pytest.mark.parametrize("B,H,d,W,P,G_list,Hi,dI,k", [
+    (3, 64, 512, 128, 64, [3000, 0, 700], 4, 128, 512),                          # 16-head fused workgroups
+    (24, 72, 512, 128, 64, [400 + 37 * i for i in range(24)], 4, 128, 64),       # many sequences: the 64-head kernel
+    (2, 16, 128, 32, 128, [900, 2500], 2, 64, 40),
+])
+def test_paged_step_matches_the_two_calls_and_the_contiguous_step(B, H, d, W, P, G_list, Hi, dI, k):
+    # chs_decode_step_paged against chs_index_topk_paged + chs_decode_attn_paged (one page table for the
+    # key pool and the entry pool) and against chs_decode_step on the same rows stored contiguously:
+    # scores, top-k, out and lse bit for bit.
+    print(f"case: paged step B={B} H={H} d={d} P={P} G={sum(G_list)} k={k}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    gen = np.random.default_rng(9)
+    G = int(sum(G_list))
+    keys = torch.randn(G, dI, generator=g, device="cuda").bfloat16()
+    comp = torch.randn(G, d, generator=g, device="cuda").bfloat16()
+    need = [(n + P - 1) // P for n in G_list]
+    stride = max(1, max(need))
+    pages = torch.from_numpy(gen.permutation(sum(need) + 2).astype(np.int64)).cuda()
+    pt = torch.full((B, stride), -1, dtype=torch.int32, device="cuda")
+    kpool = torch.zeros((sum(need) + 2) * P, dI, dtype=torch.bfloat16, device="cuda")
+    cpool = torch.zeros((sum(need) + 2) * P, d, dtype=torch.bfloat16, device="cuda")
+    c0, p0 = 0, 0
+    for b, n in enumerate(G_list):
+        for i in range(need[b]):
+            pg = int(pages[p0 + i])
+            pt[b, i] = pg
+            lo, hi = i * P, min(n, (i + 1) * P)
+            kpool[pg * P:pg * P + hi - lo] = keys[c0 + lo:c0 + hi]
+            cpool[pg * P:pg * P + hi - lo] = comp[c0 + lo:c0 + hi]
+        c0 += n
+        p0 += need[b]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(G_list)]), dtype=torch.int64, device="cuda")
+    clen = torch.tensor(G_list, dtype=torch.int64, device="cuda")
+    swa_pages = B + 3
+    swa_page = torch.from_numpy(gen.permutation(swa_pages)[:B].astype(np.int32)).cuda()
+    swa_pool = torch.randn(swa_pages, W, d, generator=g, device="cuda").bfloat16()
+    swa = swa_pool[swa_page.long()].contiguous()
+    sl = torch.tensor([W, W // 2, 0, 7][:B] + [W] * max(0, B - 4), dtype=torch.int32, device="cuda")
+    qi = torch.randn(B, Hi, dI, generator=g, device="cuda").bfloat16()
+    w = torch.rand(B, Hi, generator=g, device="cuda")
+    q = torch.randn(B, H, d, generator=g, device="cuda").bfloat16()
+    mx = max(G_list)
+    s1 = torch.empty(B, mx, dtype=torch.float32, device="cuda")
+    s2 = torch.empty(B, mx, dtype=torch.float32, device="cuda")
+    tk1, _ = chs.index_topk_paged(qi, w, kpool, P, pt, clen, k, mx, s1)
+    o1, l1 = chs.decode_attn_paged(q, swa_pool, swa_page, sl, cpool, P, pt, clen, tk1, None, mx)
+    tk2, o2, l2, _ = chs.decode_step_paged(qi, w, kpool, q, swa_pool, swa_page, sl, cpool, P, pt, clen, k, mx,
+                                           None, s2)
+    tk3, o3, l3, _ = chs.decode_step(qi, w, keys, q, swa, sl, comp, cu, k, None, mx)
+    torch.cuda.synchronize()
+    for b, n in enumerate(G_list):
+        assert torch.equal(s1[b, :n], s2[b, :n]), f"scores differ in sequence {b}"
+    assert torch.equal(tk1, tk2) and torch.equal(tk2, tk3), "top-k differs"
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)), "out differs from the two paged calls"
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "lse differs from the two paged calls"
+    assert torch.equal(o2.view(torch.int32), o3.view(torch.int32)), "out differs from the contiguous step"
+    assert torch.equal(l2.view(torch.int32), l3.view(torch.int32)), "lse differs from the contiguous step"
