@@ -107,6 +107,21 @@ __device__ __forceinline__ void lds_row_dma(const uint16_t* src, uint16_t* dst) 
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds));
 }
 
+// v combined with lane l ^ 16's (lane l ^ 32's) value by op: gfx950's row swaps (v_permlane16_swap,
+// v_permlane32_swap) in place of an LDS-pipe lane permute. With both operands v, the swap leaves each
+// lane its own value in one result and its partner's in the other (in an order that depends on the
+// row), so a commutative op gives the same bits as the permute.
+template <typename Op>
+__device__ __forceinline__ float xor16(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // A workgroup barrier for LDS data only: this wave's LDS operations are complete, then every wave
 // meets. __syncthreads() would also wait for the row DMAs still in flight (they write LDS), which
 // must stay in flight across the chunk.
@@ -255,8 +270,8 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
         x[4 * n + r] = valid ? sacc[n][r] * a.scale_log2 : -INFINITY;
         cm = fmaxf(cm, x[4 * n + r]);
       }
-    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const auto mx = [](float p, float q) { return fmaxf(p, q); };
+    cm = xor32(xor16(cm, mx), mx);
     if (g4 == 0) cmax[kh][hq] = cm;
     lds_barrier();
     const float mn = fmaxf(m_run, fmaxf(cm, cmax[kh ^ 1][hq]));
@@ -328,8 +343,8 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
 
   // Partial result: running max (base 2) and sum per head, O in the 16-head-tile layout of the
   // combine ([16-channel tile][lane 16 g + c][4]: head 4 g + r of the tile, channel 16 j + c).
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  const auto add = [](float p, float q) { return p + q; };
+  l_run = xor32(xor16(l_run, add), add);
   if (kh == 1 && g4 == 0) lpart[hq] = l_run;
   __syncthreads();
   const int64_t pslot = (int64_t)b * a.n_splits + split;
