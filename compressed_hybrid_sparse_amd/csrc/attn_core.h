@@ -664,14 +664,8 @@ struct SplitPlan {
 };
 
 constexpr int kDenseThreads = 1024;   // dense split workgroup: 16 waves, four 16-head tiles
-#ifndef CHS_SPARSE_BLOCKS
-#define CHS_SPARSE_BLOCKS 1024
-#endif
-constexpr int kSparseBlocks = CHS_SPARSE_BLOCKS;  // selected (C4) and fp32 split workgroups aimed at per call
-#ifndef CHS_DENSE_BLOCKS
-#define CHS_DENSE_BLOCKS 256
-#endif
-constexpr int kDenseBlocks = CHS_DENSE_BLOCKS;   // dense split workgroups aimed at per call
+constexpr int kSparseBlocks = 1024;   // selected (C4) and fp32 split workgroups aimed at per call
+constexpr int kDenseBlocks = 256;     // dense split workgroups aimed at per call
 constexpr int kWideSparseBlocks = 256;        // selected attention goes wide past this many 16-head workgroups
 // Selected (C4) splits of the 64-head kernel aimed at per call: at 64 sequences of 200K tokens (640
 // slots each) 192 gives 3 splits of 256 slots: step 186.9 us, against 188.6 (256), 188.2 (128) and 196 (384).
