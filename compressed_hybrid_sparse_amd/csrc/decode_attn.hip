@@ -27,6 +27,7 @@
 // plain VALU kernel with the same split and merge (it has to meet an fp32 tolerance that bf16
 // MFMA operands cannot).
 #include "attn_core.h"
+#include <type_traits>
 
 namespace chs {
 namespace {
@@ -65,47 +66,55 @@ __global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- dense bf16, d = 512
 // Every compressed entry attended by many heads is a skinny GEMM pair per sequence (64 heads x
-// 512 channels against thousands of keys). What bounds it on gfx950 is how often each K element
-// has to reach the MFMA units from LDS, and how much of the LDS and MFMA latency the waves of a CU
-// can hide, not the HBM bytes. This kernel runs one workgroup of 8 waves (two per SIMD) per 64
-// heads and split:
-//   - Key rows go from HBM straight into LDS (global_load_lds_dwordx4: one 1 KB row per
-//     instruction, the LDS row pitch padded by 32 bytes), double-buffered, so the next chunk of 64
-//     keys is in flight during the current one without holding registers.
-//   - Q K^T is computed as S^T = K Q^T (v_mfma_f32_16x16x32_bf16): K (16 keys x 32 channels) is
-//     the A operand read from LDS, Q^T the B operand kept in registers for the whole split. Wave w
-//     takes heads 16 (w & 3) .. +15 and keys 32 (w >> 2) .. +31 of the chunk; the two key halves
-//     of a head tile agree on the chunk's maximum through LDS.
-//   - The S^T accumulator holds, in each lane, 4 consecutive keys of one head: P goes to LDS as
-//     [head][key] with 8-byte stores and comes back as the A operand of P V with 16-byte loads.
-//   - P V (v_mfma_f32_32x32x16_bf16) is split by channels: wave w owns O for all 64 heads and
-//     channels 64 w .. +63, so V is read from LDS once per chunk; its B operand comes from the
-//     transposing LDS load (4 keys of one channel per read).
-// Per 64-key chunk (64 KB of keys) the LDS sees 64 KB of row writes, 256 KB of K reads, 64 KB of V
-// reads and about 80 KB of P and softmax exchange, with three barriers; each wave runs 32 MFMAs
-// of each kind. The partial results use the layout of the 16-head-tile kernels, so the same combine
-// merges them.
-constexpr int kD512Threads = 512;             // 8 waves
-constexpr int kD512Chunk = 64;                // keys per chunk
-// bf16 elements per LDS key row: padded by 32 bytes. Against 16 bytes of padding this cut the C128 step
-// from 27.96 to 26.96 us (4 x 8,320 keys) and from 50.0 to 48.6 us (64 sequences); 48 and 64 bytes
-// measured 27.7 / 52.2 and 27.6 / 48.8 us.
-constexpr int kD512Pitch = 512 + 16;
+// 512 channels against thousands of keys). One workgroup of 12 waves (three per SIMD) runs one
+// split for 64 heads as a two-stage pipeline over chunks of 32 keys:
+//   - waves 0-3 (producers) compute S^T = K Q^T for their 16 heads over the whole chunk
+//     (v_mfma_f32_16x16x32_bf16, K from LDS as the A operand, Q^T held in registers), then the
+//     online softmax: each producer holds all of its heads' keys, so no other wave takes part; P
+//     (rounded to bf16) and the per-head rescale factor go to LDS, and the producers request the
+//     rows of the chunk two ahead, one every two MFMA steps;
+//   - waves 4-11 (consumers) hold O for all 64 heads, 64 channels each, and in the next phase
+//     rescale it and add P V for the chunk (v_mfma_f32_32x32x16_bf16, V = K read back with the
+//     transposing LDS load), every fragment requested before the first MFMA.
+// In phase t the producers work on chunk t while the consumers work on chunk t - 1, so each SIMD
+// has a wave in Q K^T or the softmax beside two in P V, and the softmax's VALU work overlaps the
+// consumers' MFMAs. One barrier per phase, against three per 64-key chunk when every wave did both
+// stages (C128 at 4 x 8,320 keys 26.9 -> 24.9 us, at 64 sequences 48 -> 43-45 us). The reference
+// maximum of a head moves only when a chunk exceeds it by more than kD512Slack (base 2), so most
+// phases leave every rescale factor exactly 1 and the consumers skip the rescale (P stays below
+// 2^8, well inside bf16 and the fp32 sums). Key rows go from HBM straight into LDS
+// (global_load_lds_dwordx4, one 1 KB row per instruction, the row pitch padded by 32 bytes) into
+// four buffers: a chunk is read in two phases and requested two phases ahead.
+// Per 32-key chunk (32 KB of keys) the LDS sees 32 KB of row writes, 128 KB of K reads (each
+// producer reads the chunk for its 16 heads), 32 KB of transposing V reads and 32 KB of P reads;
+// per SIMD the producer and the two consumers issue 512 cycles of MFMA each way. The partial
+// results use the layout of the 16-head-tile kernels, so the same merge applies. Measured and not
+// kept: 8 waves (four consumers of 128 channels; 0.4 us slower at 4 x 8,320 keys), K fragments
+// requested 7 or 15 steps ahead instead of 3, row pitches padded by 16, 48 or 64 bytes.
+constexpr int kD512Threads = 768;             // 12 waves
+constexpr int kD512Chunk = 32;                // keys per phase
+constexpr int kD512Bufs = 4;                  // key row buffers
+constexpr int kD512Pitch = 512 + 16;          // bf16 elements per LDS key row
 constexpr int kD512PPitch = kD512Chunk + 8;   // bf16 elements per LDS row of P
+constexpr float kD512Slack = 8.f;             // base-2 logits a chunk may exceed the reference maximum by
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // One row by DMA into LDS: lane l's 16 bytes at src (its own address) land at dst + 16 l, dst the
 // same in every lane (it goes into M0). Written as an instruction of its own rather than through the
 // compiler builtin: the builtin lets the compiler track the LDS write, and it then waits for every
-// DMA in flight before LDS reads it cannot tell apart from the destination (the P V operand loads),
-// which would empty the prefetch each chunk. The instruction writes no register; the caller waits
-// for it (vmcnt) before reading the rows, and never reads or writes the destination rows meanwhile
-// (so the compiler may move other LDS accesses across it).
+// DMA in flight before LDS reads it cannot tell apart from the destination, which would empty the
+// prefetch each phase. The instruction writes no register; the kernel waits for it (vmcnt) before
+// the rows are read, and never reads or writes the destination rows meanwhile.
 __device__ __forceinline__ void lds_row_dma(const uint16_t* src, uint16_t* dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst);
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds));
 }
+
+// Waits until at most N of this wave's vector memory operations are outstanding (they complete in
+// order, so the older row DMAs have landed).
+template <int N>
+__device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // v combined with lane l ^ 16's (lane l ^ 32's) value by op: gfx950's row swaps (v_permlane16_swap,
 // v_permlane32_swap) in place of an LDS-pipe lane permute. With both operands v, the swap leaves each
@@ -124,8 +133,15 @@ __device__ __forceinline__ float xor32(float v, Op op) {
 
 // A workgroup barrier for LDS data only: this wave's LDS operations are complete, then every wave
 // meets. __syncthreads() would also wait for the row DMAs still in flight (they write LDS), which
-// must stay in flight across the chunk.
+// must stay in flight across phases.
 __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A page-table entry at an index that is the same in every lane, read through the scalar unit: the
+// wait for it is on the scalar/LDS counter, not behind the row DMAs in flight.
+__device__ __forceinline__ int64_t page_entry(const int32_t* pt, int64_t idx) {
+  const __attribute__((address_space(4))) int32_t* p = (const __attribute__((address_space(4))) int32_t*)pt;
+  return p[idx];
+}
 
 // PAGED: entries through the page table (an entry whose page is outside the pool is skipped) and
 // the window through the sequence's window page, as in the other split kernels.
@@ -134,23 +150,20 @@ __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkm
 // skipped.
 template <bool PAGED, bool TOPK>
 __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a) {
-  constexpr int D = 512, KC = kD512Chunk, KP = kD512Pitch, PP = kD512PPitch;
-  __shared__ __attribute__((aligned(16))) uint16_t kt0[KC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t kt1[KC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t pb[64 * PP];
-  __shared__ float cmax[2][64];                              // [key half][head]: the chunk's maxima
-  __shared__ __attribute__((aligned(16))) float alph[64];   // the chunk's rescale factor per head
-  __shared__ float lpart[64];                                // key half 1's running sums at the end
-  __shared__ uint8_t rowok[2][KC];                           // PAGED, TOPK: which rows of each buffer hold a key
-  __shared__ int32_t selrow[TOPK ? kWideMaxSelected : 1];    // TOPK: the split's selected entries
+  constexpr int D = 512, KC = kD512Chunk, NB = kD512Bufs, KP = kD512Pitch, PP = kD512PPitch;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[NB][KC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t pb[2][64 * PP];
+  __shared__ __attribute__((aligned(16))) float alph[2][64];   // [chunk & 1][head]: rescale factor
+  __shared__ uint8_t rowok[NB][KC];                            // PAGED, TOPK: which rows of each buffer hold a key
+  __shared__ int32_t selrow[TOPK ? kWideMaxSelected : 1];      // TOPK: the split's selected entries
 
   const int b = blockIdx.y, split = blockIdx.x, zg = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ht = wave & 3, kh = wave >> 2;        // Q K^T: head tile, key half
+  const int wl = wave & 3;                        // producer: head tile
   const int l32 = lane & 31, lh = lane >> 5;      // 32 x 32 operand layout (P V)
   const int c16 = lane & 15, g4 = lane >> 4;      // 16 x 16 operand layout (Q K^T)
-  const int hq = 16 * ht + c16;                   // this lane's head in Q K^T and the softmax
+  const int hq = 16 * wl + c16;                   // producer: this lane's head
   const SlotMap sm(a, b);
   const int32_t s_begin = split * a.kps;
   const int32_t s_end = min(s_begin + a.kps, sm.nslots());
@@ -158,9 +171,9 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
   const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
 
-  // Row 8 w + i of the chunk at slot s0 into buffer bi, by DMA (lane l brings bytes 16 l .. + 15).
-  // The source is chosen without branches (the row addresses formed, one kept by mask), so a run of
-  // these stays one basic block. Slots that hold no key read the query buffer instead.
+  // Row r = 8 w + i of chunk c into buffer c % NB, by DMA (lane l brings bytes 16 l .. + 15), issued
+  // by producer w. Every value that picks the row is the same in all lanes. Slots that hold no key
+  // read the query buffer instead (the row is then masked).
   const uint64_t swa_a = (uint64_t)(uintptr_t)(swa + sm.swa_row0 * D);
   const uint64_t comp_a = (uint64_t)(uintptr_t)(comp + (sm.comp0 - sm.nswa) * D);
   const uint64_t safe_a = (uint64_t)(uintptr_t)a.q;
@@ -172,9 +185,10 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
     for (int i = threadIdx.x; i < nsel; i += kD512Threads) selrow[i] = tk[j0 + i];
     __syncthreads();
   }
-  auto issue_row = [&](uint16_t* buf, int bi, int32_t s0, int i) {
+  auto issue_row = [&](int c, int i) {
+    const int bi = c & (NB - 1);
     const int r = 8 * wave + i;
-    const int32_t s = s0 + r;
+    const int32_t s = s_begin + c * KC + r;
     const uint64_t in_w = 0ull - (uint64_t)(s < sm.nswa);
     bool ok = s < s_end;
     uint64_t comp_row = comp_a + (uint64_t)(int64_t)s * (D * 2);
@@ -183,13 +197,13 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
       // paged, its page.
       int64_t j = (int64_t)s - sm.nswa;
       if (TOPK) {
-        const int32_t e = selrow[min(max((int32_t)j - j0, 0), max(nsel - 1, 0))];
+        const int32_t e = __builtin_amdgcn_readfirstlane(selrow[min(max((int32_t)j - j0, 0), max(nsel - 1, 0))]);
         ok = ok && (s < sm.nswa || (e >= 0 && e < sm.G));
         j = e;
       }
       j = min(max(j, (int64_t)0), sm.G > 0 ? sm.G - 1 : (int64_t)0);
       if (PAGED) {
-        const int64_t pg = a.pg.pt[(int64_t)b * a.pg.pt_stride + (j >> a.pg.shift)];
+        const int64_t pg = page_entry(a.pg.pt, (int64_t)b * a.pg.pt_stride + (j >> a.pg.shift));
         const bool pok = pg >= 0 && pg < a.pg.pool_pages;
         ok = ok && (s < sm.nswa || pok);
         comp_row = (uint64_t)(uintptr_t)(comp + (((pok ? pg : 0) << a.pg.shift) | (j & ((1 << a.pg.shift) - 1))) * D);
@@ -202,172 +216,219 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
     const uint64_t row = (PAGED || TOPK) ? (((swa_a + (uint64_t)(int64_t)s * (D * 2)) & in_w) | (comp_row & ~in_w))
                                          : ((swa_a & in_w) | (comp_a & ~in_w)) + (uint64_t)(int64_t)s * (D * 2);
     const uint64_t src = (safe_a & past) | (row & ~past);
-    lds_row_dma(reinterpret_cast<const uint16_t*>(src) + 8 * lane, buf + r * KP);
+    lds_row_dma(reinterpret_cast<const uint16_t*>(src) + 8 * lane, &kt[bi][r * KP]);
   };
-  if (nchunks > 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) issue_row(kt0, 0, s_begin, i);
-  }
 
-  // The 64 query rows come in once per workgroup, by DMA into kt1 (free until chunk 1 is requested,
-  // after the first barrier of the loop). Q^T (B operand): lane (head hq, channel group g4) holds
-  // channels 32 t + 8 g4 .. +7 of k-step t. Heads past H read head H - 1; their rows are never
-  // combined.
-  bf16x8 qf[D / 32];
-  {
+  // The 64 query rows by DMA (waves 0-7, 8 rows each) into buffers 2 and 3, free until chunk 2 is
+  // requested in phase 0; then the producers request chunks 0 and 1. Heads past H read head H - 1;
+  // their rows are never combined.
+  if (wave < 8) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int h = min(64 * zg + 8 * wave + i, a.H - 1);
-      lds_row_dma(static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + h) * D + 8 * lane, kt1 + (8 * wave + i) * KP);
+      const int hl = 8 * wave + i;
+      const int h = min(64 * zg + hl, a.H - 1);
+      lds_row_dma(static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + h) * D + 8 * lane, &kt[2 + (hl >> 5)][(hl & 31) * KP]);
     }
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint16_t* qrow = kt1 + hq * KP + 8 * g4;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * t));
   }
-  f32x16 o[2][2];                        // [head tile 32 hp][channel tile 64 w + 32 ct]
+  if (wave < 4) {
 #pragma unroll
-  for (int hp = 0; hp < 2; ++hp)
+    for (int c = 0; c < 2; ++c) {
+      if (c < nchunks) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) o[hp][ct] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;  // head hq; l_run over this lane's keys
+        for (int i = 0; i < 8; ++i) issue_row(c, i);
+      }
+    }
+    if (nchunks > 1) wait_vm<16>(); else if (nchunks > 0) wait_vm<8>(); else wait_vm<0>();
+  } else {
+    wait_vm<0>();
+  }
+  lds_barrier();                         // every wave's query rows landed
 
-  auto chunk = [&](const uint16_t* cur, uint16_t* nxt, int cb, int c) {
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's rows of chunk c landed
-    __syncthreads();                                      // every wave's rows; chunk c - 1 is done
-    const int32_t s0 = s_begin + c * KC;
-    if (c + 1 < nchunks) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) issue_row(nxt, cb ^ 1, s0 + KC, i);
+  // The top of phase t: a producer's rows of chunk t have landed (chunk t + 1's may still be in
+  // flight), and every wave is done with phase t - 1, so the producers may request chunk t + 2 into
+  // the buffer chunk t - 2 used.
+  auto phase_top = [&](int t) {
+    if (wave < 4) {
+      if (t + 1 < nchunks) wait_vm<8>(); else wait_vm<0>();
     }
-    // S^T for keys 32 kh .. +31 (two 16-key tiles) and heads 16 ht .. +15. The K fragments of
-    // step t + 1 are read while step t's MFMAs run.
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const uint16_t* krow = cur + (32 * kh + c16) * KP + 8 * g4;
-    bf16x8 kf[2][2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) kf[0][n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * n * KP));
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      if (t + 1 < D / 32) {
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          kf[(t + 1) & 1][n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * n * KP + 32 * (t + 1)));
-      }
-#pragma unroll
-      for (int n = 0; n < 2; ++n) sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t & 1][n], qf[t], sacc[n], 0, 0, 0);
-    }
-    // Register r of tile n of lane (c16, g4) holds key 32 kh + 16 n + 4 g4 + r of head hq.
-    float x[8];
-    float cm = -INFINITY;
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = 32 * kh + 16 * n + 4 * g4 + r;
-        const bool valid = (PAGED || TOPK) ? rowok[cb][kr] != 0 : s0 + kr < s_end;
-        x[4 * n + r] = valid ? sacc[n][r] * a.scale_log2 : -INFINITY;
-        cm = fmaxf(cm, x[4 * n + r]);
-      }
-    const auto mx = [](float p, float q) { return fmaxf(p, q); };
-    cm = xor32(xor16(cm, mx), mx);
-    if (g4 == 0) cmax[kh][hq] = cm;
     lds_barrier();
-    const float mn = fmaxf(m_run, fmaxf(cm, cmax[kh ^ 1][hq]));
-    const bool none = (mn == -INFINITY);
-    const float alpha = none ? 1.f : fast_exp2(m_run - mn);
-    float psum = 0.f;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      uint32_t w2[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        // Rounded to bf16 here so the running sum matches what the MFMA multiplies.
-        const uint32_t lo = none ? 0u : f32_to_bf16(fast_exp2(x[4 * n + 2 * e] - mn));
-        const uint32_t hi = none ? 0u : f32_to_bf16(fast_exp2(x[4 * n + 2 * e + 1] - mn));
-        psum += bf16_to_f32((uint16_t)lo) + bf16_to_f32((uint16_t)hi);
-        w2[e] = lo | (hi << 16);
-      }
-      *reinterpret_cast<uint2*>(&pb[hq * PP + 32 * kh + 16 * n + 4 * g4]) = make_uint2(w2[0], w2[1]);
-    }
-    l_run = l_run * alpha + psum;
-    m_run = mn;
-    if (kh == 0 && g4 == 0) alph[hq] = alpha;
-    lds_barrier();
-    // O (all 64 heads, channels 64 w .. +63) rescaled, then O += P V over the chunk's 64 keys.
-#pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-      float al[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&alph[32 * hp + 8 * q4 + 4 * lh]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) al[4 * q4 + e] = v[e];
-      }
-      // Skipped when none of the tile's heads raised its maximum this chunk (alpha exactly 1), the
-      // usual case once the running maxima settle.
-      bool moved = false;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) moved |= al[r] != 1.f;
-      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[hp][ct][r] *= al[r];
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < KC / 16; ++kk) {
-      bf16x8 pa[2];
-#pragma unroll
-      for (int hp = 0; hp < 2; ++hp)
-        pa[hp] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pb[(32 * hp + l32) * PP + 16 * kk + 8 * lh]));
-      // Lane (channel l32, key group lh): keys 16 kk + 8 lh .. +7 of its channel, as two
-      // transposing reads of 4 keys each.
-      const uint16_t* vrow = cur + (16 * kk + 8 * (g4 >> 1) + (c16 >> 2)) * KP + 64 * wave + 16 * (g4 & 1) + 4 * (c16 & 3);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 32 * ct));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 4 * KP + 32 * ct));
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-        for (int hp = 0; hp < 2; ++hp) o[hp][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hp], vb, o[hp][ct], 0, 0, 0);
-      }
-    }
   };
-  for (int c = 0; c < nchunks; c += 2) {
-    chunk(kt0, kt1, 0, c);
-    if (c + 1 < nchunks) chunk(kt1, kt0, 1, c + 1);
-  }
-
-  // Partial result: running max (base 2) and sum per head, O in the 16-head-tile layout of the
-  // combine ([16-channel tile][lane 16 g + c][4]: head 4 g + r of the tile, channel 16 j + c).
-  const auto add = [](float p, float q) { return p + q; };
-  l_run = xor32(xor16(l_run, add), add);
-  if (kh == 1 && g4 == 0) lpart[hq] = l_run;
-  __syncthreads();
   const int64_t pslot = (int64_t)b * a.n_splits + split;
-  if (kh == 0 && g4 == 0) {
-    const int h = 64 * zg + hq;
-    if (h < a.H) {
-      a.part_ml[(pslot * a.H + h) * 2] = m_run;
-      a.part_ml[(pslot * a.H + h) * 2 + 1] = l_run + lpart[hq];
+
+  if (wave < 4) {
+    // ---- producer: Q K^T and the online softmax for heads 16 wl .. +15 (this lane: head hq).
+    // Q^T (B operand): lane (head hq, channel group g4) holds channels 32 t + 8 g4 .. +7 of k-step t.
+    bf16x8 qf[D / 32];
+    {
+      const uint16_t* qrow = &kt[2 + (hq >> 5)][(hq & 31) * KP + 8 * g4];
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * t));
     }
-  }
-  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (pslot * a.head_tiles * 4 + 4 * zg) * (D / 16) * 64;
+    float m_run = -INFINITY, l_run = 0.f;  // head hq; l_run over this lane's keys
+    for (int t = 0; t <= nchunks; ++t) {
+      phase_top(t);
+      if (t == nchunks) break;
+      const int bi = t & (NB - 1);
+      const int32_t s0 = s_begin + t * KC;
+      // S^T for the chunk's 32 keys (two 16-key tiles); the K fragments of step u + PD are read
+      // while step u's MFMAs run. Chunk t + 2's rows are requested one every two steps (when there is
+      // such a chunk), so the address unit takes them while the MFMAs run instead of holding up the
+      // wave.
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      const uint16_t* krow = &kt[bi][c16 * KP + 8 * g4];
+      constexpr int PD = 3;                // K-fragment steps requested ahead
+      bf16x8 kf[PD + 1][2];
+      auto qk = [&](auto with_rows) {
+        constexpr bool ROWS = decltype(with_rows)::value;
 #pragma unroll
-  for (int hp = 0; hp < 2; ++hp)
+        for (int p = 0; p < PD; ++p)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+          for (int n = 0; n < 2; ++n) kf[p][n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * n * KP + 32 * p));
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int h0 = 32 * hp + 8 * q4 + 4 * lh;           // local head of register 4 q4
-        const int ch = 64 * wave + 32 * ct + l32;
-        const int64_t idx = (int64_t)(h0 >> 4) * (D / 16) * 64 + (ch >> 4) * 64 + 16 * ((h0 & 15) >> 2) + (ch & 15);
-        const f32x4 v = {o[hp][ct][4 * q4], o[hp][ct][4 * q4 + 1], o[hp][ct][4 * q4 + 2], o[hp][ct][4 * q4 + 3]};
-        __builtin_nontemporal_store(v, &po[idx]);
+        for (int u = 0; u < D / 32; ++u) {
+          if (ROWS && u % 2 == 0) issue_row(t + 2, u / 2);
+          if (u + PD < D / 32) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+              kf[(u + PD) % (PD + 1)][n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * n * KP + 32 * (u + PD)));
+          }
+#pragma unroll
+          for (int n = 0; n < 2; ++n) sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u % (PD + 1)][n], qf[u], sacc[n], 0, 0, 0);
+        }
+        // Keep the reads PD steps ahead of the MFMAs (the scheduler would otherwise pull each read
+        // down to just before its use).
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
+#pragma unroll
+        for (int u = 0; u < D / 32; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (u + PD < D / 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      };
+      if (t + 2 < nchunks) qk(std::true_type{}); else qk(std::false_type{});
+      // Register r of tile n of lane (c16, g4) holds key 16 n + 4 g4 + r of head hq.
+      float x[8];
+      float cm = -INFINITY;
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kr = 16 * n + 4 * g4 + r;
+          const bool valid = (PAGED || TOPK) ? rowok[bi][kr] != 0 : s0 + kr < s_end;
+          x[4 * n + r] = valid ? sacc[n][r] * a.scale_log2 : -INFINITY;
+          cm = fmaxf(cm, x[4 * n + r]);
+        }
+      const auto mx = [](float p, float q) { return fmaxf(p, q); };
+      cm = xor32(xor16(cm, mx), mx);
+      // The reference maximum moves only when the chunk exceeds it by more than 2^8 (or on the first
+      // keys): P stays at most 256, and most chunks leave alpha exactly 1, so the consumers skip the
+      // rescale.
+      const float mn = (cm > m_run + kD512Slack || m_run == -INFINITY) ? cm : m_run;
+      const bool none = (mn == -INFINITY);
+      const float alpha = none ? 1.f : fast_exp2(m_run - mn);
+      float psum = 0.f;
+      uint16_t* pw = &pb[t & 1][hq * PP + 4 * g4];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        uint32_t w2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          // Rounded to bf16 here so the running sum matches what the MFMA multiplies.
+          const uint32_t lo = none ? 0u : f32_to_bf16(fast_exp2(x[4 * n + 2 * e] - mn));
+          const uint32_t hi = none ? 0u : f32_to_bf16(fast_exp2(x[4 * n + 2 * e + 1] - mn));
+          psum += bf16_to_f32((uint16_t)lo) + bf16_to_f32((uint16_t)hi);
+          w2[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint2*>(pw + 16 * n) = make_uint2(w2[0], w2[1]);
       }
+      l_run = l_run * alpha + psum;
+      m_run = mn;
+      if (g4 == 0) alph[t & 1][hq] = alpha;
+    }
+    // Running max (base 2) and sum per head.
+    const auto add = [](float p, float q) { return p + q; };
+    l_run = xor32(xor16(l_run, add), add);
+    const int h = 64 * zg + hq;
+    if (g4 == 0 && h < a.H) {
+      a.part_ml[(pslot * a.H + h) * 2] = m_run;
+      a.part_ml[(pslot * a.H + h) * 2 + 1] = l_run;
+    }
+  } else {
+    // ---- consumer: O for all 64 heads and channels 64 cw .. +63, [head tile 32 hp][channel tile
+    // 64 cw + 32 ct].
+    const int cw = wave - 4;
+    f32x16 o[2][2];
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) o[hp][ct] = f32x16{};
+    for (int t = 0; t <= nchunks; ++t) {
+      phase_top(t);
+      if (t == 0) continue;
+      const int c = t - 1;                 // the chunk the producers finished in phase t - 1
+      const uint16_t* cur = kt[c & (NB - 1)];
+      const uint16_t* pcur = pb[c & 1];
+      // O rescaled by the chunk's factors; skipped when none of a 32-head tile's heads raised its
+      // maximum (alpha exactly 1), the usual case once the running maxima settle.
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {
+        float al[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&alph[c & 1][32 * hp + 8 * q4 + 4 * lh]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) al[4 * q4 + e] = v[e];
+        }
+        bool moved = false;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) moved |= al[r] != 1.f;
+        if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[hp][ct][r] *= al[r];
+        }
+      }
+      // Every P and V fragment of the chunk is requested first, then the 16 MFMAs run.
+      bf16x8 pa[KC / 16][2], vb[KC / 16][2];
+#pragma unroll
+      for (int kk = 0; kk < KC / 16; ++kk) {
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+          pa[kk][hp] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pcur[(32 * hp + l32) * PP + 16 * kk + 8 * lh]));
+        // Lane (channel l32, key group lh): keys 16 kk + 8 lh .. +7 of its channel, as two
+        // transposing reads of 4 keys each.
+        const uint16_t* vrow = cur + (16 * kk + 8 * (g4 >> 1) + (c16 >> 2)) * KP + 64 * cw + 16 * (g4 & 1) + 4 * (c16 & 3);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 32 * ct));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vrow + 4 * KP + 32 * ct));
+          vb[kk][ct] = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KC / 16; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+          for (int hp = 0; hp < 2; ++hp) o[hp][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk][hp], vb[kk][ct], o[hp][ct], 0, 0, 0);
+        }
+    }
+    // Unnormalised O in the 16-head-tile layout of the merge ([16-channel tile][lane 16 g + c][4]:
+    // head 4 g + r of the tile, channel 16 j + c).
+    f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (pslot * a.head_tiles * 4 + 4 * zg) * (D / 16) * 64;
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int h0 = 32 * hp + 8 * q4 + 4 * lh;           // local head of register 4 q4
+          const int ch = 64 * cw + 32 * ct + l32;
+          const int64_t idx = (int64_t)(h0 >> 4) * (D / 16) * 64 + (ch >> 4) * 64 + 16 * ((h0 & 15) >> 2) + (ch & 15);
+          const f32x4 v = {o[hp][ct][4 * q4], o[hp][ct][4 * q4 + 1], o[hp][ct][4 * q4 + 2], o[hp][ct][4 * q4 + 3]};
+          __builtin_nontemporal_store(v, &po[idx]);
+        }
+  }
 }
 
 template <bool FP8, bool PAGED>
@@ -708,3 +769,4 @@ extern "C" chs_status chs_decode_attn_fp8_paged(int32_t batch, int32_t n_heads, 
                          comp_scale_pool, nullptr, pg, topk, max_comp, out, lse, workspace, workspace_bytes,
                          static_cast<hipStream_t>(stream));
 }
+
