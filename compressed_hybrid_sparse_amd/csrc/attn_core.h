@@ -475,21 +475,48 @@ __device__ __forceinline__ void combine_tile(const AttnArgs& a, float* out, floa
   const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o);
   const int64_t stride = (int64_t)a.head_tiles * 4 * (D / 16) * 64;   // one split, in f32x4
   const int64_t base = (((int64_t)b * ns * a.head_tiles + tile) * 4 + wave) * (D / 16) * 64 + wpos;
-  // This lane's first splits (sq, sq + 4, ...) are requested before anything else, so they
-  // arrive while the split weights are computed.
+  // The 16 heads' (max, sum) pairs of every split come through LDS in one coalesced pass; then
+  // head hl = tid / 16 is handled by the 16 lanes of one DPP row, each lane a strided subset of
+  // the splits, and the head's maximum and weighted sum are row reductions. Up to 64 splits the
+  // pairs (at most 4 per thread, at clamped positions so no load sits behind a branch) are
+  // requested first: loads complete in order, so the weights then wait only for them while this
+  // lane's partials (splits sq, sq + 4, ..., requested next) are still arriving. Before, with the
+  // partials requested first, the weights waited for all of them (the 44-split merge at 4 x 1M
+  // tokens 8.0 -> 7.6 us together with the exact load count in launch_combine).
+  const int nh = min(16, a.H - 16 * hg);
+  const int nml = ns * nh;
+  constexpr int kMl = (16 * MAXS + kAttnThreads - 1) / kAttnThreads;
+  constexpr bool kMlFirst = kMl <= 4;
+  float2 mlv[kMlFirst ? kMl : 1];
+  if constexpr (kMlFirst) {
+#pragma unroll
+    for (int i = 0; i < kMl; ++i) {
+      const int e = min(tid + i * kAttnThreads, nml - 1);
+      const int sp = e / nh, hl = e - sp * nh;
+      mlv[i] = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * ns + sp) * a.H + 16 * hg + hl) * 2);
+    }
+  }
   constexpr int kBatch = KB;
   f32x4 v[kBatch];
 #pragma unroll
   for (int q = 0; q < kBatch; ++q) v[q] = po[base + (int64_t)min(sq + kCombineLanes * q, ns - 1) * stride];
-  // The 16 heads' (max, sum) pairs of every split come through LDS in one coalesced pass; then
-  // head hl = tid / 16 is handled by the 16 lanes of one DPP row, each lane a strided subset of
-  // the splits, and the head's maximum and weighted sum are row reductions.
-  const int nh = min(16, a.H - 16 * hg);
-  for (int e = tid; e < ns * nh; e += kAttnThreads) {
-    const int sp = e / nh, hl = e - sp * nh;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * ns + sp) * a.H + 16 * hg + hl) * 2);
-    wts[hl][sp] = ml.x;
-    lpart[hl][sp] = ml.y;
+  if constexpr (kMlFirst) {
+#pragma unroll
+    for (int i = 0; i < kMl; ++i) {
+      const int e = tid + i * kAttnThreads;
+      if (e < nml) {
+        const int sp = e / nh, hl = e - sp * nh;
+        wts[hl][sp] = mlv[i].x;
+        lpart[hl][sp] = mlv[i].y;
+      }
+    }
+  } else {
+    for (int e = tid; e < nml; e += kAttnThreads) {
+      const int sp = e / nh, hl = e - sp * nh;
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * ns + sp) * a.H + 16 * hg + hl) * 2);
+      wts[hl][sp] = ml.x;
+      lpart[hl][sp] = ml.y;
+    }
   }
   __syncthreads();
   {
@@ -630,12 +657,20 @@ inline void launch_combine(const AttnArgs& a, int32_t batch, int32_t n_heads, in
   const int words_per_block = kAttnThreads / kCombineLanes;
   const dim3 grid((unsigned)((words + words_per_block - 1) / words_per_block), (unsigned)((n_heads + 15) / 16),
                   (unsigned)batch);
-  if (a.n_splits <= 4 * 8)
-    hipLaunchKernelGGL((combine_tile_kernel<8, 64>), grid, dim3(kAttnThreads), 0, s, a, out, lse);
-  else if (a.n_splits <= 64)
-    hipLaunchKernelGGL((combine_tile_kernel<16, 64>), grid, dim3(kAttnThreads), 0, s, a, out, lse);
-  else
-    hipLaunchKernelGGL((combine_tile_kernel<16, kCombineSplits>), grid, dim3(kAttnThreads), 0, s, a, out, lse);
+  // Each lane requests KB partials at once; up to 64 splits KB is the smallest listed count that
+  // covers the splits (20 -> 5, 44 -> 11), since a load past the last split repeats it and costs
+  // address-unit time (KB = 16 at 44 splits requested 45% more than needed).
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kAttnThreads), 0, s, a, out, lse); };
+  const int per_lane = (a.n_splits + kCombineLanes - 1) / kCombineLanes;
+  if (per_lane <= 3) go(combine_tile_kernel<3, 64>);
+  else if (per_lane <= 4) go(combine_tile_kernel<4, 64>);
+  else if (per_lane <= 5) go(combine_tile_kernel<5, 64>);
+  else if (per_lane <= 6) go(combine_tile_kernel<6, 64>);
+  else if (per_lane <= 8) go(combine_tile_kernel<8, 64>);
+  else if (per_lane <= 11) go(combine_tile_kernel<11, 64>);
+  else if (per_lane <= 12) go(combine_tile_kernel<12, 64>);
+  else if (per_lane <= 16) go(combine_tile_kernel<16, 64>);
+  else go(combine_tile_kernel<16, kCombineSplits>);
 }
 
 // Host checks of chs_decode_attn's arguments (all but the workspace).
