@@ -185,9 +185,18 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
     for (int i = threadIdx.x; i < nsel; i += kD512Threads) selrow[i] = tk[j0 + i];
     __syncthreads();
   }
-  auto issue_row = [&](int c, int i) {
+  // Who requests the rows: the producers, 8 rows each, spread over their Q K^T steps; in the
+  // selected form the consumers, 4 each, between their P V MFMAs. A selected entry is a random row
+  // of a large buffer, and each request then holds its wave up about 0.2 us (at 64 sequences of
+  // 50,000 entries a producer that requested 8 per phase took 2.1 us instead of 0.8); spread over
+  // the eight consumers, a phase took 1.7-1.9 us instead of 2.1-2.3.
+  constexpr bool kConsumerRows = TOPK;
+  constexpr int kRowsPerWave = kConsumerRows ? 4 : 8;
+  const bool issuer = kConsumerRows ? wave >= 4 : wave < 4;
+  const int iw = kConsumerRows ? wave - 4 : wave;
+  auto row_src = [&](int c, int i) -> uint64_t {
     const int bi = c & (NB - 1);
-    const int r = 8 * wave + i;
+    const int r = kRowsPerWave * iw + i;
     const int32_t s = s_begin + c * KC + r;
     const uint64_t in_w = 0ull - (uint64_t)(s < sm.nswa);
     bool ok = s < s_end;
@@ -215,9 +224,12 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
     const uint64_t past = 0ull - (uint64_t)(!ok);
     const uint64_t row = (PAGED || TOPK) ? (((swa_a + (uint64_t)(int64_t)s * (D * 2)) & in_w) | (comp_row & ~in_w))
                                          : ((swa_a & in_w) | (comp_a & ~in_w)) + (uint64_t)(int64_t)s * (D * 2);
-    const uint64_t src = (safe_a & past) | (row & ~past);
-    lds_row_dma(reinterpret_cast<const uint16_t*>(src) + 8 * lane, &kt[bi][r * KP]);
+    return (safe_a & past) | (row & ~past);
   };
+  auto row_dma = [&](int c, int i, uint64_t src) {
+    lds_row_dma(reinterpret_cast<const uint16_t*>(src) + 8 * lane, &kt[c & (NB - 1)][(kRowsPerWave * iw + i) * KP]);
+  };
+  auto issue_row = [&](int c, int i) { row_dma(c, i, row_src(c, i)); };
 
   // The 64 query rows by DMA (waves 0-7, 8 rows each) into buffers 2 and 3, free until chunk 2 is
   // requested in phase 0; then the producers request chunks 0 and 1. Heads past H read head H - 1;
@@ -230,15 +242,15 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
       lds_row_dma(static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + h) * D + 8 * lane, &kt[2 + (hl >> 5)][(hl & 31) * KP]);
     }
   }
-  if (wave < 4) {
+  if (issuer) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       if (c < nchunks) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) issue_row(c, i);
+        for (int i = 0; i < kRowsPerWave; ++i) issue_row(c, i);
       }
     }
-    if (nchunks > 1) wait_vm<16>(); else if (nchunks > 0) wait_vm<8>(); else wait_vm<0>();
+    if (nchunks > 1) wait_vm<2 * kRowsPerWave>(); else if (nchunks > 0) wait_vm<kRowsPerWave>(); else wait_vm<0>();
   } else {
     wait_vm<0>();
   }
@@ -248,8 +260,8 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   // flight), and every wave is done with phase t - 1, so the producers may request chunk t + 2 into
   // the buffer chunk t - 2 used.
   auto phase_top = [&](int t) {
-    if (wave < 4) {
-      if (t + 1 < nchunks) wait_vm<8>(); else wait_vm<0>();
+    if (issuer) {
+      if (t + 1 < nchunks) wait_vm<kRowsPerWave>(); else wait_vm<0>();
     }
     lds_barrier();
   };
@@ -280,13 +292,20 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
       bf16x8 kf[PD + 1][2];
       auto qk = [&](auto with_rows) {
         constexpr bool ROWS = decltype(with_rows)::value;
+        // The rows' sources first: a selected entry or a page-table entry is an LDS or scalar read,
+        // whose wait (in order) would otherwise also wait for the K fragments in flight.
+        uint64_t src[ROWS ? 8 : 1];
+        if (ROWS) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) src[i] = row_src(t + 2, i);
+        }
 #pragma unroll
         for (int p = 0; p < PD; ++p)
 #pragma unroll
           for (int n = 0; n < 2; ++n) kf[p][n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * n * KP + 32 * p));
 #pragma unroll
         for (int u = 0; u < D / 32; ++u) {
-          if (ROWS && u % 2 == 0) issue_row(t + 2, u / 2);
+          if (ROWS && u % 2 == 0) row_dma(t + 2, u / 2, src[u / 2]);
           if (u + PD < D / 32) {
 #pragma unroll
             for (int n = 0; n < 2; ++n)
@@ -304,7 +323,7 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
           if (u + PD < D / 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       };
-      if (t + 2 < nchunks) qk(std::true_type{}); else qk(std::false_type{});
+      if (!kConsumerRows && t + 2 < nchunks) qk(std::true_type{}); else qk(std::false_type{});
       // Register r of tile n of lane (c16, g4) holds key 16 n + 4 g4 + r of head hq.
       float x[8];
       float cm = -INFINITY;
@@ -363,7 +382,19 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
       for (int ct = 0; ct < 2; ++ct) o[hp][ct] = f32x16{};
     for (int t = 0; t <= nchunks; ++t) {
       phase_top(t);
-      if (t == 0) continue;
+      const bool req = kConsumerRows && t + 2 < nchunks;   // chunk t + 2 is requested this phase
+      uint64_t src[kConsumerRows ? kRowsPerWave : 1];
+      if (req) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) src[i] = row_src(t + 2, i);
+      }
+      if (t == 0) {
+        if (req) {
+#pragma unroll
+          for (int i = 0; i < kRowsPerWave; ++i) row_dma(t + 2, i, src[i]);
+        }
+        continue;
+      }
       const int c = t - 1;                 // the chunk the producers finished in phase t - 1
       const uint16_t* cur = kt[c & (NB - 1)];
       const uint16_t* pcur = pb[c & 1];
@@ -411,6 +442,7 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
         for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
           for (int hp = 0; hp < 2; ++hp) o[hp][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk][hp], vb[kk][ct], o[hp][ct], 0, 0, 0);
+          if (req) row_dma(t + 2, 2 * kk + ct, src[2 * kk + ct]);
         }
     }
     // Unnormalised O in the 16-head-tile layout of the merge ([16-channel tile][lane 16 g + c][4]:
