@@ -186,15 +186,23 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
     __syncthreads();
   }
   // Who requests the rows: the producers, 8 rows each, spread over their Q K^T steps; in the
-  // selected form the consumers, 4 each, between their P V MFMAs. A selected entry is a random row
-  // of a large buffer, and each request then holds its wave up about 0.2 us (at 64 sequences of
-  // 50,000 entries a producer that requested 8 per phase took 2.1 us instead of 0.8); spread over
-  // the eight consumers, a phase took 1.7-1.9 us instead of 2.1-2.3.
+  // selected form the consumers, 4 each, between their P V MFMAs. A selected row costs its wave an
+  // LDS round trip for the entry and the request (at 64 sequences of 50,000 entries a producer that
+  // requested 8 per phase took 2.1 us instead of 0.8, whether the entries were scattered or
+  // consecutive); spread over the eight consumers, with one LDS read for a wave's entries, the
+  // kernel went from 24.1 to 21.6 us.
   constexpr bool kConsumerRows = TOPK;
   constexpr int kRowsPerWave = kConsumerRows ? 4 : 8;
   const bool issuer = kConsumerRows ? wave >= 4 : wave < 4;
   const int iw = kConsumerRows ? wave - 4 : wave;
-  auto row_src = [&](int c, int i) -> uint64_t {
+  // TOPK: the selected entries of this wave's rows of chunk c, lane i holding row i's, from one LDS
+  // read (each row then takes its own with a lane read, instead of an LDS round trip per row).
+  auto sel_entries = [&](int c) -> int32_t {
+    if (!TOPK) return 0;
+    const int32_t s = s_begin + c * KC + kRowsPerWave * iw + (lane < kRowsPerWave ? lane : 0);
+    return selrow[min(max(s - sm.nswa - j0, 0), max(nsel - 1, 0))];
+  };
+  auto row_src = [&](int c, int i, int32_t sel) -> uint64_t {
     const int bi = c & (NB - 1);
     const int r = kRowsPerWave * iw + i;
     const int32_t s = s_begin + c * KC + r;
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
       // paged, its page.
       int64_t j = (int64_t)s - sm.nswa;
       if (TOPK) {
-        const int32_t e = __builtin_amdgcn_readfirstlane(selrow[min(max((int32_t)j - j0, 0), max(nsel - 1, 0))]);
+        const int32_t e = __builtin_amdgcn_readlane(sel, i);
         ok = ok && (s < sm.nswa || (e >= 0 && e < sm.G));
         j = e;
       }
@@ -229,7 +237,11 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   auto row_dma = [&](int c, int i, uint64_t src) {
     lds_row_dma(reinterpret_cast<const uint16_t*>(src) + 8 * lane, &kt[c & (NB - 1)][(kRowsPerWave * iw + i) * KP]);
   };
-  auto issue_row = [&](int c, int i) { row_dma(c, i, row_src(c, i)); };
+  auto issue_rows = [&](int c) {
+    const int32_t sel = sel_entries(c);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) row_dma(c, i, row_src(c, i, sel));
+  };
 
   // The 64 query rows by DMA (waves 0-7, 8 rows each) into buffers 2 and 3, free until chunk 2 is
   // requested in phase 0; then the producers request chunks 0 and 1. Heads past H read head H - 1;
@@ -245,10 +257,7 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   if (issuer) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      if (c < nchunks) {
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) issue_row(c, i);
-      }
+      if (c < nchunks) issue_rows(c);
     }
     if (nchunks > 1) wait_vm<2 * kRowsPerWave>(); else if (nchunks > 0) wait_vm<kRowsPerWave>(); else wait_vm<0>();
   } else {
@@ -296,8 +305,9 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
         // whose wait (in order) would otherwise also wait for the K fragments in flight.
         uint64_t src[ROWS ? 8 : 1];
         if (ROWS) {
+          const int32_t sel = sel_entries(t + 2);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) src[i] = row_src(t + 2, i);
+          for (int i = 0; i < 8; ++i) src[i] = row_src(t + 2, i, sel);
         }
 #pragma unroll
         for (int p = 0; p < PD; ++p)
@@ -385,8 +395,9 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
       const bool req = kConsumerRows && t + 2 < nchunks;   // chunk t + 2 is requested this phase
       uint64_t src[kConsumerRows ? kRowsPerWave : 1];
       if (req) {
+        const int32_t sel = sel_entries(t + 2);
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) src[i] = row_src(t + 2, i);
+        for (int i = 0; i < kRowsPerWave; ++i) src[i] = row_src(t + 2, i, sel);
       }
       if (t == 0) {
         if (req) {
