@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(AttnArgs a) {
 //     (v_mfma_f32_16x16x32_bf16, K from LDS as the A operand, Q^T held in registers), then the
 //     online softmax: each producer holds all of its heads' keys, so no other wave takes part; P
 //     (rounded to bf16) and the per-head rescale factor go to LDS, and the producers request the
-//     rows of the chunk two ahead, one every two MFMA steps;
+//     rows of the chunk two ahead, one every two MFMA steps (in the selected form the consumers do);
 //   - waves 4-11 (consumers) hold O for all 64 heads, 64 channels each, and in the next phase
 //     rescale it and add P V for the chunk (v_mfma_f32_32x32x16_bf16, V = K read back with the
 //     transposing LDS load), every fragment requested before the first MFMA.
@@ -171,9 +171,9 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   const uint16_t* swa = static_cast<const uint16_t*>(a.swa);
   const uint16_t* comp = static_cast<const uint16_t*>(a.comp);
 
-  // Row r = 8 w + i of chunk c into buffer c % NB, by DMA (lane l brings bytes 16 l .. + 15), issued
-  // by producer w. Every value that picks the row is the same in all lanes. Slots that hold no key
-  // read the query buffer instead (the row is then masked).
+  // Row r of chunk c into buffer c % NB, by DMA (lane l brings bytes 16 l .. + 15): requesting wave
+  // iw (below) takes rows kRowsPerWave iw .. + kRowsPerWave - 1. Every value that picks a row is the
+  // same in all lanes. Slots that hold no key read the query buffer instead (the row is then masked).
   const uint64_t swa_a = (uint64_t)(uintptr_t)(swa + sm.swa_row0 * D);
   const uint64_t comp_a = (uint64_t)(uintptr_t)(comp + (sm.comp0 - sm.nswa) * D);
   const uint64_t safe_a = (uint64_t)(uintptr_t)a.q;
@@ -244,8 +244,8 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   };
 
   // The 64 query rows by DMA (waves 0-7, 8 rows each) into buffers 2 and 3, free until chunk 2 is
-  // requested in phase 0; then the producers request chunks 0 and 1. Heads past H read head H - 1;
-  // their rows are never combined.
+  // requested in phase 0; then the requesting waves request chunks 0 and 1. Heads past H read head
+  // H - 1; their rows are never combined.
   if (wave < 8) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -265,9 +265,9 @@ __global__ __launch_bounds__(kD512Threads) void attn_dense512_kernel(AttnArgs a)
   }
   lds_barrier();                         // every wave's query rows landed
 
-  // The top of phase t: a producer's rows of chunk t have landed (chunk t + 1's may still be in
-  // flight), and every wave is done with phase t - 1, so the producers may request chunk t + 2 into
-  // the buffer chunk t - 2 used.
+  // The top of phase t: a requesting wave's rows of chunk t have landed (chunk t + 1's may still be
+  // in flight), and every wave is done with phase t - 1, so chunk t + 2 may be requested into the
+  // buffer chunk t - 2 used.
   auto phase_top = [&](int t) {
     if (issuer) {
       if (t + 1 < nchunks) wait_vm<kRowsPerWave>(); else wait_vm<0>();
