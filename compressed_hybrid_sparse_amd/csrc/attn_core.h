@@ -700,7 +700,12 @@ struct SplitPlan {
 
 constexpr int kDenseThreads = 1024;   // dense split workgroup: 16 waves, four 16-head tiles
 constexpr int kSparseBlocks = 1024;   // selected (C4) and fp32 split workgroups aimed at per call
-constexpr int kDenseBlocks = 256;     // dense split workgroups aimed at per call
+// Dense split workgroups aimed at per call, fewer than the CUs: each split writes 128 KiB of fp32 partials
+// per 64 heads, which the merge reads back. 192 against 256 (graph replays, the two builds interleaved):
+// 64 sequences of ~1,570 keys 42.0-42.3 against 42.4-43.3 us (3 splits instead of 4), 8 sequences of 6,000
+// keys 27.1-27.5 against 29.0-29.2 us, 16 of 4,096 keys 32.3-32.4 against 32.4-33.3 us; 32 sequences of
+// 3,000 keys 39.0-39.4 against 38.6-39.1 us (6 splits instead of 8); 4 sequences the same plan.
+constexpr int kDenseBlocks = 192;
 constexpr int kWideSparseBlocks = 256;        // selected attention goes wide past this many 16-head workgroups
 // Selected (C4) splits of the 64-head kernel aimed at per call: at 64 sequences of 200K tokens (640
 // slots each) 192 gives 3 splits of 256 slots: step 186.9 us, against 188.6 (256), 188.2 (128) and 196 (384).
