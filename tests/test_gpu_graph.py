@@ -147,3 +147,29 @@ def test_graph_replays_per_token_step_bitwise(paged):
                     "lse"):
             assert torch.equal(A[key], Bst[key]), f"token {t}: {key} differs between eager and replay"
     assert A["n"].item() == n0 + steps
+
+
+@pytest.mark.parametrize("words", [1, 255, 256, 1000003, 5_000_000])
+def test_workspace_clear_eager_and_in_graph(words):
+    # chs_workspace_clear zero-fills exactly `bytes` bytes with a kernel (one 4-byte word per
+    # element), so it can sit in a captured graph; words past the range keep their values. The
+    # graph replays after eager writes of fresh garbage, with eager work between replays.
+    print(f"case: workspace clear, {words} words", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(words)
+    buf = torch.randint(1, 1 << 30, (words + 64,), generator=g, dtype=torch.int32, device=dev())
+    tail = buf[words:].clone()
+    chs.workspace_clear(buf[:words])
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(buf[:words])) == 0
+    assert torch.equal(buf[words:], tail)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chs.workspace_clear(buf[:words])
+    for r in range(3):
+        buf[:words].copy_(torch.randint(1, 1 << 30, (words,), generator=g, dtype=torch.int32, device=dev()))
+        torch.cuda.synchronize()
+        _eager_noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(buf[:words])) == 0, f"replay {r}"
+        assert torch.equal(buf[words:], tail), f"replay {r}: past the range"
