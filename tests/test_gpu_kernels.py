@@ -328,6 +328,16 @@ def test_attn_dense_bf16_many_heads(rng, H, d):
     _attn_case(rng, "bf16", 2, H, d, 128, [128, 50], [4000, 700], 0, True)
 
 
+@pytest.mark.parametrize("B,L", [(1, 8192), (2, 5000), (6, 6000), (8, 6000), (12, 4000), (4, 8704)])
+def test_attn_dense512_split_counts(rng, B, L):
+    # Dense d = 512 over 64 heads at batch sizes whose split plans reach every many-split merge form:
+    # 130 and 81 splits (the merge sized to 512 splits), 32, 24, 13 and 46 splits (8, 6, 4 and 12
+    # partial loads per lane). Sequence lengths vary around L, windows are ragged.
+    print(f"case: attn dense d=512 B={B} L={L}", flush=True)
+    G = [L - 37 * i for i in range(B)]
+    _attn_case(rng, "bf16", B, 64, 512, 128, [(128, 100, 0, 31)[i % 4] for i in range(B)], G, 0, True)
+
+
 def test_attn_f32(rng):
     print("case: attn f32", flush=True)
     _attn_case(rng, "f32", 2, 8, 64, 128, [128, 30], [256, 300], 64, False, n_bad=3)
